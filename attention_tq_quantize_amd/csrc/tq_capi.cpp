@@ -1,0 +1,369 @@
+// C ABI: argument validation, error reporting, quantizer handles.
+// What each call computes is documented in include/tq.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+static thread_local std::string g_last_error;
+
+tq_status set_error(tq_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+tq_status check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TQ_OK;
+  std::string m = std::string(what) + ": " + hipGetErrorString(e);
+  if (e == hipErrorOutOfMemory) return set_error(TQ_ERR_NO_MEMORY, m);
+  return set_error(TQ_ERR_DEVICE, m);
+}
+
+namespace {
+
+std::string fmt(const char* f, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, f);
+  vsnprintf(buf, sizeof buf, f, ap);
+  va_end(ap);
+  return buf;
+}
+
+bool gpu_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
+uint16_t bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(r >> 16);
+}
+
+float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// MFMA fragments of a d x d matrix M for v_mfma_f32_16x16x32_bf16, as used by
+// the quantize kernel: for output tile q, k-step ks and lane l = m + 16 g, the
+// eight bf16 values M[row][col + i], row = (d/4)(m/4) + 4q + (m%4),
+// col = (d/4) g + 8 ks. Stored [hilo][q][ks][lane][8]; hi = bf16(M),
+// lo = bf16(M - hi).
+void build_fragments(int d, const double* M, uint16_t* out) {
+  const int nq = d / 16, nk = d / 32;
+  const size_t per = (size_t)nq * nk * 64 * 8;
+  for (int q = 0; q < nq; ++q)
+    for (int ks = 0; ks < nk; ++ks)
+      for (int l = 0; l < 64; ++l)
+        for (int i = 0; i < 8; ++i) {
+          const int m = l % 16, g = l / 16;
+          const int row = (d / 4) * (m / 4) + 4 * q + (m % 4);
+          const int col = (d / 4) * g + 8 * ks + i;
+          const float v = (float)M[(size_t)row * d + col];
+          const uint16_t hi = bf16_rne(v);
+          const uint16_t lo = bf16_rne(v - bf16_to_f32(hi));
+          const size_t off = (((size_t)q * nk + ks) * 64 + l) * 8 + i;
+          out[off] = hi;
+          out[per + off] = lo;
+        }
+}
+
+}  // namespace
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+const char* tq_status_string(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARG: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported";
+    case TQ_ERR_NO_MEMORY: return "out of memory";
+    case TQ_ERR_DEVICE: return "device error";
+    case TQ_ERR_WORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+const char* tq_last_error_message(void) { return g_last_error.c_str(); }
+
+int tq_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+tq_status tq_codebook_build(int d, int bits, float* centroids, float* thresholds,
+                            double* cost_per_coord) {
+  if (d < 3 || d > 4096) return set_error(TQ_ERR_INVALID_ARG, fmt("codebook: d=%d outside [3, 4096]", d));
+  if (bits < 0 || bits > 8) return set_error(TQ_ERR_INVALID_ARG, fmt("codebook: bits=%d outside [0, 8]", bits));
+  if (!centroids) return set_error(TQ_ERR_INVALID_ARG, "codebook: centroids is NULL");
+  const Codebook* cb = nullptr;
+  tq_status st = get_codebook(d, bits, &cb);
+  if (st != TQ_OK) return st;
+  const int K = 1 << bits;
+  std::memcpy(centroids, cb->centroids, sizeof(float) * K);
+  if (thresholds && K > 1) std::memcpy(thresholds, cb->thresholds, sizeof(float) * (K - 1));
+  if (cost_per_coord) *cost_per_coord = cb->cost;
+  g_last_error.clear();
+  return TQ_OK;
+}
+
+tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double* pi,
+                              const double* s, tq_quantizer** out) {
+  if (!out) return set_error(TQ_ERR_INVALID_ARG, "create: out is NULL");
+  *out = nullptr;
+  if (!gpu_dim(d)) return set_error(TQ_ERR_UNSUPPORTED, fmt("create: d=%d (supported: 64, 128, 256)", d));
+  if (bits < 1 || bits > kMaxBits) return set_error(TQ_ERR_UNSUPPORTED, fmt("create: bits=%d (supported: 1..4)", bits));
+  if (variant != TQ_MSE && variant != TQ_PROD) return set_error(TQ_ERR_INVALID_ARG, "create: unknown variant");
+  if (!pi) return set_error(TQ_ERR_INVALID_ARG, "create: pi is NULL");
+  if (variant == TQ_PROD && !s) return set_error(TQ_ERR_INVALID_ARG, "create: prod needs the QJL matrix s");
+  // Pi must be orthogonal (rows orthonormal) for Q^-1 = Pi^T to invert the rotation.
+  double worst = 0.0;
+  for (int i = 0; i < d; ++i)
+    for (int j = i; j < d; ++j) {
+      double acc = 0.0;
+      for (int k = 0; k < d; ++k) acc += pi[(size_t)i * d + k] * pi[(size_t)j * d + k];
+      if (!std::isfinite(acc)) return set_error(TQ_ERR_INVALID_ARG, "create: pi is not finite");
+      worst = std::fmax(worst, std::fabs(acc - (i == j ? 1.0 : 0.0)));
+    }
+  if (worst > 1e-6) return set_error(TQ_ERR_INVALID_ARG, fmt("create: pi is not orthogonal (max |Pi Pi^T - I| = %.3g)", worst));
+  if (variant == TQ_PROD)
+    for (size_t i = 0; i < (size_t)d * d; ++i)
+      if (!std::isfinite(s[i])) return set_error(TQ_ERR_INVALID_ARG, "create: s is not finite");
+
+  tq_quantizer* q = new (std::nothrow) tq_quantizer();
+  if (!q) return set_error(TQ_ERR_NO_MEMORY, "create: out of host memory");
+  q->d = d;
+  q->bits = bits;
+  q->variant = variant;
+  q->planes = variant == TQ_PROD ? bits - 1 : bits;
+  const Codebook* cb = nullptr;
+  tq_status st = get_codebook(d, q->planes, &cb);
+  if (st != TQ_OK) {
+    delete q;
+    return st;
+  }
+  q->cb = *cb;
+  tq_status hs = check_hip(hipGetDevice(&q->device), "create: hipGetDevice");
+  if (hs != TQ_OK) {
+    delete q;
+    return hs;
+  }
+
+  const size_t dd = (size_t)d * d;
+  const size_t frag_bytes = 2 * dd * sizeof(uint16_t);  // hi + lo
+  const bool prod = variant == TQ_PROD;
+  const size_t total = frag_bytes * (prod ? 2 : 1) + dd * sizeof(float) * (prod ? 2 : 1);
+  std::vector<unsigned char> host(total);
+  size_t off = 0;
+  build_fragments(d, pi, (uint16_t*)(host.data() + off));
+  const size_t off_pi_frag = off;
+  off += frag_bytes;
+  size_t off_sp_frag = 0;
+  if (prod) {
+    // S' = S Pi^T, folded in fp64, so that S r = S' (Pi u - y~): the residual never
+    // leaves the rotated space.
+    std::vector<double> sp(dd, 0.0);
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) {
+        double acc = 0.0;
+        for (int k = 0; k < d; ++k) acc += s[(size_t)i * d + k] * pi[(size_t)j * d + k];
+        sp[(size_t)i * d + j] = acc;
+      }
+    build_fragments(d, sp.data(), (uint16_t*)(host.data() + off));
+    off_sp_frag = off;
+    off += frag_bytes;
+  }
+  const size_t off_pi32 = off;
+  for (size_t i = 0; i < dd; ++i) ((float*)(host.data() + off))[i] = (float)pi[i];
+  off += dd * sizeof(float);
+  size_t off_s32 = 0;
+  if (prod) {
+    off_s32 = off;
+    for (size_t i = 0; i < dd; ++i) ((float*)(host.data() + off))[i] = (float)s[i];
+    off += dd * sizeof(float);
+  }
+  hs = check_hip(hipMalloc(&q->dev_block, total), "create: hipMalloc");
+  if (hs != TQ_OK) {
+    delete q;
+    return hs;
+  }
+  hs = check_hip(hipMemcpy(q->dev_block, host.data(), total, hipMemcpyHostToDevice), "create: hipMemcpy");
+  if (hs != TQ_OK) {
+    (void)hipFree(q->dev_block);
+    delete q;
+    return hs;
+  }
+  unsigned char* base = (unsigned char*)q->dev_block;
+  q->pi_frag = (const uint16_t*)(base + off_pi_frag);
+  q->sp_frag = prod ? (const uint16_t*)(base + off_sp_frag) : nullptr;
+  q->pi32 = (const float*)(base + off_pi32);
+  q->s32 = prod ? (const float*)(base + off_s32) : nullptr;
+  *out = q;
+  g_last_error.clear();
+  return TQ_OK;
+}
+
+tq_status tq_quantizer_destroy(tq_quantizer* q) {
+  if (!q) return set_error(TQ_ERR_INVALID_ARG, "destroy: handle is NULL");
+  tq_status st = TQ_OK;
+  if (q->dev_block) st = check_hip(hipFree(q->dev_block), "destroy: hipFree");
+  delete q;
+  return st;
+}
+
+tq_status tq_quantizer_info(const tq_quantizer* q, int* d, int* bits, tq_variant* variant,
+                            int* code_planes) {
+  if (!q) return set_error(TQ_ERR_INVALID_ARG, "info: handle is NULL");
+  if (d) *d = q->d;
+  if (bits) *bits = q->bits;
+  if (variant) *variant = q->variant;
+  if (code_planes) *code_planes = q->planes;
+  return TQ_OK;
+}
+
+tq_status tq_quantize(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group,
+                      const void* x, tq_dtype x_dtype, tq_layout layout, uint8_t* codes,
+                      uint8_t* signs, float* norms, float* rnorms, float* rot_dbg,
+                      float* proj_dbg, void* stream) {
+  if (!qz) return set_error(TQ_ERR_INVALID_ARG, "quantize: qz is NULL");
+  if (n_groups < 1) return set_error(TQ_ERR_INVALID_ARG, fmt("quantize: n_groups=%d < 1", n_groups));
+  if (n_per_group < 0) return set_error(TQ_ERR_INVALID_ARG, "quantize: n_per_group < 0");
+  const tq_quantizer* q0 = qz[0];
+  if (!q0) return set_error(TQ_ERR_INVALID_ARG, "quantize: qz[0] is NULL");
+  for (int g = 1; g < n_groups; ++g) {
+    if (!qz[g]) return set_error(TQ_ERR_INVALID_ARG, fmt("quantize: qz[%d] is NULL", g));
+    if (qz[g]->d != q0->d || qz[g]->bits != q0->bits || qz[g]->variant != q0->variant)
+      return set_error(TQ_ERR_INVALID_ARG, "quantize: handles differ in (d, bits, variant)");
+  }
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return set_error(TQ_ERR_INVALID_ARG, "quantize: unknown dtype");
+  if (layout != TQ_LAYOUT_VECTOR && layout != TQ_LAYOUT_BLOCK32) return set_error(TQ_ERR_INVALID_ARG, "quantize: unknown layout");
+  if (layout == TQ_LAYOUT_BLOCK32) {
+    if (q0->variant != TQ_MSE) return set_error(TQ_ERR_UNSUPPORTED, "quantize: BLOCK32 layout is for mse quantizers");
+    if (n_per_group % kBlock) return set_error(TQ_ERR_INVALID_ARG, "quantize: BLOCK32 needs n_per_group % 32 == 0");
+  }
+  const bool prod = q0->variant == TQ_PROD;
+  if (n_per_group == 0) return TQ_OK;
+  if (!x) return set_error(TQ_ERR_INVALID_ARG, "quantize: x is NULL");
+  if (q0->planes > 0 && !codes) return set_error(TQ_ERR_INVALID_ARG, "quantize: codes is NULL");
+  if (!norms) return set_error(TQ_ERR_INVALID_ARG, "quantize: norms is NULL");
+  if (prod && (!signs || !rnorms)) return set_error(TQ_ERR_INVALID_ARG, "quantize: prod needs signs and rnorms");
+  if (!prod && proj_dbg) return set_error(TQ_ERR_INVALID_ARG, "quantize: proj_dbg is only for prod");
+  if ((double)n_groups * (double)n_per_group > 4.0e9) return set_error(TQ_ERR_UNSUPPORTED, "quantize: more than 4e9 vectors");
+  QuantizeLaunch a{qz, n_groups, n_per_group, x, x_dtype, layout, codes, signs, norms, rnorms, rot_dbg, proj_dbg};
+  return launch_quantize(a, (hipStream_t)stream);
+}
+
+tq_status tq_quantize_mse(const tq_quantizer* q, const void* x, tq_dtype x_dtype, int64_t n,
+                          uint8_t* codes, float* norms, float* rot_dbg, void* stream) {
+  if (!q) return set_error(TQ_ERR_INVALID_ARG, "quantize_mse: handle is NULL");
+  if (q->variant != TQ_MSE) return set_error(TQ_ERR_INVALID_ARG, "quantize_mse: handle is not TQ_MSE");
+  return tq_quantize(&q, 1, n, x, x_dtype, TQ_LAYOUT_VECTOR, codes, nullptr, norms, nullptr, rot_dbg,
+                     nullptr, stream);
+}
+
+tq_status tq_quantize_prod(const tq_quantizer* q, const void* x, tq_dtype x_dtype, int64_t n,
+                           uint8_t* codes, uint8_t* signs, float* norms, float* rnorms,
+                           float* rot_dbg, float* proj_dbg, void* stream) {
+  if (!q) return set_error(TQ_ERR_INVALID_ARG, "quantize_prod: handle is NULL");
+  if (q->variant != TQ_PROD) return set_error(TQ_ERR_INVALID_ARG, "quantize_prod: handle is not TQ_PROD");
+  return tq_quantize(&q, 1, n, x, x_dtype, TQ_LAYOUT_VECTOR, codes, signs, norms, rnorms, rot_dbg,
+                     proj_dbg, stream);
+}
+
+tq_status tq_dequantize(const tq_quantizer* q, tq_layout layout, const uint8_t* codes,
+                        const uint8_t* signs, const float* norms, const float* rnorms, int64_t n,
+                        float* x_out, void* stream) {
+  if (!q) return set_error(TQ_ERR_INVALID_ARG, "dequantize: handle is NULL");
+  if (n < 0) return set_error(TQ_ERR_INVALID_ARG, "dequantize: n < 0");
+  if (layout != TQ_LAYOUT_VECTOR && layout != TQ_LAYOUT_BLOCK32) return set_error(TQ_ERR_INVALID_ARG, "dequantize: unknown layout");
+  if (layout == TQ_LAYOUT_BLOCK32) {
+    if (q->variant != TQ_MSE) return set_error(TQ_ERR_UNSUPPORTED, "dequantize: BLOCK32 layout is for mse quantizers");
+    if (n % kBlock) return set_error(TQ_ERR_INVALID_ARG, "dequantize: BLOCK32 needs n % 32 == 0");
+  }
+  if (n == 0) return TQ_OK;
+  if ((q->planes > 0 && !codes) || !norms || !x_out) return set_error(TQ_ERR_INVALID_ARG, "dequantize: NULL buffer");
+  if (q->variant == TQ_PROD && (!signs || !rnorms)) return set_error(TQ_ERR_INVALID_ARG, "dequantize: prod needs signs and rnorms");
+  if (n > (int64_t)1 << 31) return set_error(TQ_ERR_UNSUPPORTED, "dequantize: n > 2^31");
+  return launch_dequantize(q, layout, codes, signs, norms, rnorms, n, x_out, (hipStream_t)stream);
+}
+
+tq_status tq_inner_products(const tq_quantizer* q, const float* y, int64_t m, const uint8_t* codes,
+                            const uint8_t* signs, const float* norms, const float* rnorms, int64_t n,
+                            float* out, void* stream) {
+  if (!q) return set_error(TQ_ERR_INVALID_ARG, "inner_products: handle is NULL");
+  if (m < 0 || n < 0) return set_error(TQ_ERR_INVALID_ARG, "inner_products: negative size");
+  if (m == 0 || n == 0) return TQ_OK;
+  if (!y || (q->planes > 0 && !codes) || !norms || !out) return set_error(TQ_ERR_INVALID_ARG, "inner_products: NULL buffer");
+  if (q->variant == TQ_PROD && (!signs || !rnorms)) return set_error(TQ_ERR_INVALID_ARG, "inner_products: prod needs signs and rnorms");
+  if (m > 65535 || n > (int64_t)1 << 31) return set_error(TQ_ERR_UNSUPPORTED, "inner_products: m > 65535 or n > 2^31");
+  return launch_inner_products(q, y, m, codes, signs, norms, rnorms, n, out, (hipStream_t)stream);
+}
+
+static tq_status check_decode(const tq_attn_shape* s, const tq_packed_kv* k, const tq_packed_kv* v,
+                              DecodePlan* plan) {
+  if (!s || !k || !v) return set_error(TQ_ERR_INVALID_ARG, "decode: NULL shape or cache");
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1)
+    return set_error(TQ_ERR_INVALID_ARG, "decode: batch and head counts must be >= 1");
+  if (s->n_kv_heads > kMaxKvHeads) return set_error(TQ_ERR_UNSUPPORTED, fmt("decode: n_kv_heads > %d", kMaxKvHeads));
+  if (s->n_q_heads % s->n_kv_heads) return set_error(TQ_ERR_INVALID_ARG, "decode: n_q_heads % n_kv_heads != 0");
+  const int group = s->n_q_heads / s->n_kv_heads;
+  if (group > 8 && group % 8) return set_error(TQ_ERR_UNSUPPORTED, "decode: group size > 8 must be a multiple of 8");
+  if (s->max_ctx < 32 || s->max_ctx % 32) return set_error(TQ_ERR_INVALID_ARG, "decode: max_ctx must be a positive multiple of 32");
+  if (s->max_ctx > ((int64_t)1 << 30)) return set_error(TQ_ERR_UNSUPPORTED, "decode: max_ctx > 2^30");
+  if (!k->qz || !v->qz) return set_error(TQ_ERR_INVALID_ARG, "decode: quantizer arrays are NULL");
+  const tq_quantizer* k0 = k->qz[0];
+  const tq_quantizer* v0 = v->qz[0];
+  if (!k0 || !v0) return set_error(TQ_ERR_INVALID_ARG, "decode: NULL quantizer handle");
+  if (k0->d != s->head_dim || v0->d != s->head_dim) return set_error(TQ_ERR_INVALID_ARG, "decode: head_dim differs from the quantizers' d");
+  for (int h = 0; h < s->n_kv_heads; ++h) {
+    const tq_quantizer* kh = k->qz[h];
+    const tq_quantizer* vh = v->qz[h];
+    if (!kh || !vh) return set_error(TQ_ERR_INVALID_ARG, fmt("decode: NULL handle for kv head %d", h));
+    if (kh->d != k0->d || kh->bits != k0->bits || kh->variant != k0->variant)
+      return set_error(TQ_ERR_INVALID_ARG, "decode: key handles differ in (d, bits, variant)");
+    if (vh->d != v0->d || vh->bits != v0->bits || vh->variant != v0->variant)
+      return set_error(TQ_ERR_INVALID_ARG, "decode: value handles differ in (d, bits, variant)");
+  }
+  if (v0->variant != TQ_MSE) return set_error(TQ_ERR_UNSUPPORTED, "decode: values must use TQ_MSE quantizers");
+  if ((k0->planes > 0 && !k->codes) || !k->norms) return set_error(TQ_ERR_INVALID_ARG, "decode: key cache buffers are NULL");
+  if (k0->variant == TQ_PROD && (!k->signs || !k->rnorms)) return set_error(TQ_ERR_INVALID_ARG, "decode: prod keys need signs and rnorms");
+  if (!v->codes || !v->norms) return set_error(TQ_ERR_INVALID_ARG, "decode: value cache buffers are NULL");
+  return plan_decode(s, k0, v0, plan);
+}
+
+tq_status tq_decode_workspace_size(const tq_attn_shape* shape, const tq_packed_kv* k,
+                                   const tq_packed_kv* v, size_t* bytes) {
+  if (!bytes) return set_error(TQ_ERR_INVALID_ARG, "decode_workspace_size: bytes is NULL");
+  DecodePlan p;
+  tq_status st = check_decode(shape, k, v, &p);
+  if (st != TQ_OK) return st;
+  *bytes = p.total_bytes;
+  return TQ_OK;
+}
+
+tq_status tq_decode_attention(const tq_attn_shape* shape, const void* q, const tq_packed_kv* k,
+                              const tq_packed_kv* v, const int32_t* ctx_lens, float scale,
+                              float* out, float* scores_dbg, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  DecodePlan p;
+  tq_status st = check_decode(shape, k, v, &p);
+  if (st != TQ_OK) return st;
+  if (!q || !ctx_lens || !out) return set_error(TQ_ERR_INVALID_ARG, "decode: q, ctx_lens or out is NULL");
+  if (!std::isfinite(scale)) return set_error(TQ_ERR_INVALID_ARG, "decode: scale is not finite");
+  if (!workspace || ws_bytes < p.total_bytes)
+    return set_error(TQ_ERR_WORKSPACE, fmt("decode: workspace needs %zu bytes, got %zu", p.total_bytes, workspace ? ws_bytes : (size_t)0));
+  return launch_decode(p, q, k, v, ctx_lens, scale, out, scores_dbg, workspace, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// Device helpers shared by the kernel translation units (header-only, internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kMaxGroupsPerLaunch = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// lazy online-softmax rescale: keep the running max until a chunk exceeds it by this much
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ unsigned bf16_bits(float v) {
+  return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)v);
+}
+__device__ __forceinline__ float bf16_val(unsigned h) { return __uint_as_float(h << 16); }
+
+// hi (lo = false) or lo (lo = true) bf16 part of v; hi + lo carries 16 significant bits
+__device__ __forceinline__ unsigned bf16_part(float v, bool lo) {
+  const unsigned hi = bf16_bits(v);
+  return lo ? bf16_bits(v - bf16_val(hi)) : hi;
+}
+__device__ __forceinline__ unsigned pack2(unsigned lo_half, unsigned hi_half) {
+  return (lo_half & 0xFFFFu) | (hi_half << 16);
+}
+
+// Operand bits: slot pair k of a word lands on bit 10+k of each 16-bit half (the
+// low exponent bits of an fp16), so a set bit reads as 2^((1 << k) - 15).
+__device__ __forceinline__ unsigned slot_mask(int k) { return (0x0400u << k) | (0x04000000u << k); }
+// word w rotated so that bits 4r+k and 16+4r+k sit on bits 10+k and 26+k
+__device__ __forceinline__ unsigned rot_for(unsigned w, int r) {
+  return __builtin_amdgcn_alignbit(w, w, (unsigned)((4 * r - 10) & 31));
+}
+__device__ __forceinline__ u32x4 bit_operand(unsigned w, int r) {
+  const unsigned x = rot_for(w, r);
+  u32x4 o;
+  o.x = x & slot_mask(0);
+  o.y = x & slot_mask(1);
+  o.z = x & slot_mask(2);
+  o.w = x & slot_mask(3);
+  return o;
+}
+
+// odd-size subsets of P bit planes, in increasing mask order (matches the host's Walsh list)
+__host__ __device__ constexpr int n_walsh(int P) { return P <= 0 ? 0 : (1 << (P - 1)); }
+__host__ __device__ constexpr int walsh_mask(int P, int s) {
+  int seen = 0;
+  for (int m = 1; m < (1 << P); ++m) {
+    int pc = 0;
+    for (int b = 0; b < P; ++b) pc += (m >> b) & 1;
+    if (pc & 1) {
+      if (seen == s) return m;
+      ++seen;
+    }
+  }
+  return 0;
+}
+
+// Plane bits of the nearest-centroid index of y, by binary search over the
+// float32 thresholds (t_i = largest float32 not above the midpoint of centroids
+// i and i+1; y > t_i <=> strictly nearer centroid i+1; ties go low).
+template <int P>
+__device__ __forceinline__ void search_bits(float y, const float* T, bool* bit) {
+  if constexpr (P == 1) {
+    bit[0] = y > T[0];
+  } else if constexpr (P == 2) {
+    bit[1] = y > T[1];
+    bit[0] = y > (bit[1] ? T[2] : T[0]);
+  } else if constexpr (P == 3) {
+    bit[2] = y > T[3];
+    bit[1] = y > (bit[2] ? T[5] : T[1]);
+    const float a = bit[2] ? T[4] : T[0];
+    const float b = bit[2] ? T[6] : T[2];
+    bit[0] = y > (bit[1] ? b : a);
+  } else if constexpr (P == 4) {
+    bit[3] = y > T[7];
+    bit[2] = y > (bit[3] ? T[11] : T[3]);
+    const float a1 = bit[3] ? T[9] : T[1];
+    const float b1 = bit[3] ? T[13] : T[5];
+    bit[1] = y > (bit[2] ? b1 : a1);
+    const float c0 = bit[3] ? T[8] : T[0];
+    const float c1 = bit[3] ? T[10] : T[2];
+    const float c2 = bit[3] ? T[12] : T[4];
+    const float c3 = bit[3] ? T[14] : T[6];
+    const float lo = bit[1] ? c1 : c0;
+    const float hi = bit[1] ? c3 : c2;
+    bit[0] = y > (bit[2] ? hi : lo);
+  }
+}
+
+template <int P>
+__device__ __forceinline__ float centroid_of(const bool* bit, const float* C) {
+  if constexpr (P == 0) {
+    return 0.0f;
+  } else if constexpr (P == 1) {
+    return bit[0] ? C[1] : C[0];
+  } else if constexpr (P == 2) {
+    const float a = bit[0] ? C[1] : C[0];
+    const float b = bit[0] ? C[3] : C[2];
+    return bit[1] ? b : a;
+  } else {
+    int idx = 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) idx |= (bit[p] ? 1 : 0) << p;
+    float v = C[0];
+#pragma unroll
+    for (int i = 1; i < (1 << P); ++i) v = idx == i ? C[i] : v;
+    return v;
+  }
+}
+
+// ------------------------------- dispatch helpers -------------------------------
+template <typename F>
+tq_status dispatch_dim(int d, F&& f) {
+  switch (d) {
+    case 64: return f(std::integral_constant<int, 64>{});
+    case 128: return f(std::integral_constant<int, 128>{});
+    case 256: return f(std::integral_constant<int, 256>{});
+  }
+  return set_error(TQ_ERR_UNSUPPORTED, "unsupported head dimension");
+}
+template <typename F>
+tq_status dispatch_planes(int p, F&& f) {
+  switch (p) {
+    case 0: return f(std::integral_constant<int, 0>{});
+    case 1: return f(std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 3: return f(std::integral_constant<int, 3>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+  }
+  return set_error(TQ_ERR_UNSUPPORTED, "unsupported plane count");
+}
+template <typename F>
+tq_status dispatch_bool(bool v, F&& f) {
+  return v ? f(std::true_type{}) : f(std::false_type{});
+}
+
+tq_status launch_check(const char* what) { return check_hip(hipGetLastError(), what); }
+
+int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
+}  // namespace
+}  // namespace tq

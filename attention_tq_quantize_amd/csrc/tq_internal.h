@@ -1,0 +1,100 @@
+// Internal declarations shared by the C ABI (tq_capi.cpp) and the kernels
+// (tq_kernels.hip). Not installed; the public surface is include/tq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kMaxBits = 4;       // GPU path: b in [1, 4]
+constexpr int kMaxWalsh = 8;      // odd-size subsets of up to 4 bit planes
+constexpr int kMaxKvHeads = 64;   // per-head pointers travel as kernel arguments
+constexpr int kBlock = 32;        // vectors per BLOCK32 block
+
+
+// A codebook for one (d, planes) pair plus its odd Walsh expansion:
+//   c[idx] = sum_s walsh_coef[s] * prod_{i in walsh_mask[s]} (2 bit_i(idx) - 1)
+struct Codebook {
+  int d = 0, planes = 0;
+  float centroids[256] = {0};   // 2^planes used; planes <= 8 on the host
+  float thresholds[255] = {0};
+  double cost = 0.0;
+  int n_walsh = 0;
+  int walsh_mask[kMaxWalsh] = {0};
+  float walsh_coef[kMaxWalsh] = {0};
+};
+
+}  // namespace tq
+
+struct tq_quantizer {
+  int d = 0;
+  int bits = 0;
+  int planes = 0;           // MSE-stage planes: bits (mse) or bits - 1 (prod)
+  tq_variant variant = TQ_MSE;
+  int device = 0;
+  tq::Codebook cb;          // codebook of the MSE stage (planes bits)
+  // Device tables, one allocation:
+  //   pi_frag / sp_frag: bf16 hi/lo MFMA fragments of Pi and S' = S Pi^T,
+  //                      ordered [hilo][mtile][kstep][lane][8]
+  //   pi32 / s32       : float32 row-major copies of Pi and S
+  void* dev_block = nullptr;
+  const uint16_t* pi_frag = nullptr;
+  const uint16_t* sp_frag = nullptr;
+  const float* pi32 = nullptr;
+  const float* s32 = nullptr;
+};
+
+namespace tq {
+
+tq_status set_error(tq_status s, const std::string& msg);
+tq_status check_hip(hipError_t e, const char* what);
+
+// Host-side codebook (cached per (d, planes); thread-safe).
+tq_status get_codebook(int d, int planes, const Codebook** out);
+
+// ---- launchers (tq_kernels.hip); arguments already validated ----
+struct QuantizeLaunch {
+  const tq_quantizer* const* qz;
+  int n_groups;
+  int64_t n_per_group;
+  const void* x;
+  tq_dtype x_dtype;
+  tq_layout layout;
+  uint8_t* codes;
+  uint8_t* signs;
+  float* norms;
+  float* rnorms;
+  float* rot_dbg;
+  float* proj_dbg;
+};
+tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream);
+
+tq_status launch_dequantize(const tq_quantizer* q, tq_layout layout, const uint8_t* codes,
+                            const uint8_t* signs, const float* norms, const float* rnorms,
+                            int64_t n, float* x_out, hipStream_t stream);
+
+tq_status launch_inner_products(const tq_quantizer* q, const float* y, int64_t m,
+                                const uint8_t* codes, const uint8_t* signs, const float* norms,
+                                const float* rnorms, int64_t n, float* out, hipStream_t stream);
+
+struct DecodePlan {
+  int batch, n_q_heads, n_kv_heads, d, group, chunk_heads, n_chunks;
+  int64_t max_ctx;
+  int n_splits;             // waves per (batch, kv head, head chunk)
+  int64_t split_tokens;     // tokens per split (multiple of 32)
+  size_t frag_bytes, const_bytes, partial_bytes, total_bytes;
+  int k_planes, k_walsh, k_words, v_bits, v_walsh;
+  bool k_qjl;
+};
+tq_status plan_decode(const tq_attn_shape* s, const tq_quantizer* k0, const tq_quantizer* v0,
+                      DecodePlan* plan);
+tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* k,
+                        const tq_packed_kv* v, const int32_t* ctx_lens, float scale, float* out,
+                        float* scores_dbg, void* workspace, hipStream_t stream);
+
+}  // namespace tq

@@ -1,0 +1,238 @@
+/*
+ * tq.h - C ABI of the TurboQuant KV-cache quantizer and quantized-KV decode
+ * attention for AMD MI355X (gfx950).
+ *
+ * Sources for what each call computes (cited as [NIK] / [NAH]):
+ *   [NIK] S. Nikolenko, "Eternal mathematics of TurboQuant: how to compress the
+ *         KV cache down to the Shannon limit" (blog.sergeynikolenko.ru), a
+ *         walkthrough of Zandieh et al. 2025, "TurboQuant: Online Vector
+ *         Quantization with Near-optimal Distortion Rate".
+ *   [NAH] "What exactly TurboQuant showed" (nahornyi.ai): the full prod
+ *         variant needs a custom attention kernel.
+ *
+ * Conventions
+ *   - Every call returns a tq_status. Nothing aborts and no C++ exception
+ *     crosses this boundary. On failure a thread-local message is available
+ *     from tq_last_error_message().
+ *   - Arguments are validated synchronously, before any launch. Kernel faults
+ *     are asynchronous and surface at the caller's stream synchronization.
+ *   - "device" pointers are HIP device memory owned by the caller; "host"
+ *     pointers are ordinary host memory owned by the caller. The library owns
+ *     only quantizer handles and the device tables inside them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream). All
+ *     device work of a call is enqueued on that stream; no call synchronizes.
+ *   - Supported on the GPU: head dimension d in {64, 128, 256}, bit width
+ *     b in [1, 4]. tq_codebook_build accepts 3 <= d <= 4096, 0 <= b <= 8.
+ *
+ * Bit layouts (the pages fix only that Q maps R^d to {0,1}^(b d); these are
+ * this library's contract):
+ *   VECTOR layout, per vector: `planes` bit planes of d bits. Plane p holds bit
+ *     p of every centroid index; coordinate j of plane p is bit (j % 8) of
+ *     byte p*d/8 + j/8. A record is planes*d/8 bytes; records are contiguous.
+ *     QJL signs use the same layout with one plane (bit = 1 <=> S r >= 0).
+ *   BLOCK32 layout (used for the value cache read by decode attention):
+ *     vectors are grouped in blocks of 32; a block is 4*planes*d bytes. For
+ *     plane p, group g in 0..3 and word w in 0..d/4-1, the little-endian
+ *     32-bit word at byte ((p*4 + g)*(d/4) + w)*4 of the block holds, at bit
+ *     4r+k (r, k in 0..3), plane-p bit of coordinate 4w+r of block vector
+ *     4g+k, and at bit 16+4r+k the same for block vector 16+4g+k.
+ *   Centroid indices ascend with centroid value; the codebook is symmetric,
+ *   so the top plane is the sign of the rotated coordinate.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shapes   */
+  TQ_ERR_UNSUPPORTED = 2, /* valid request this build does not implement         */
+  TQ_ERR_NO_MEMORY = 3,   /* host or device allocation failed                    */
+  TQ_ERR_DEVICE = 4,      /* a HIP call or kernel launch failed                  */
+  TQ_ERR_WORKSPACE = 5    /* workspace pointer null or smaller than required     */
+} tq_status;
+
+typedef enum { TQ_MSE = 0, TQ_PROD = 1 } tq_variant;
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+typedef enum { TQ_LAYOUT_VECTOR = 0, TQ_LAYOUT_BLOCK32 = 1 } tq_layout;
+
+/* Opaque quantizer: (d, b, variant, Pi, S) plus device tables. Immutable after
+ * creation, so one handle may be used from many streams and threads at once. */
+typedef struct tq_quantizer tq_quantizer;
+
+const char* tq_status_string(tq_status s);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* tq_last_error_message(void);
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int tq_version(void);
+
+/*
+ * Lloyd-Max codebook for one rotated coordinate.
+ * [NIK] "Step 1: random rotation", Lemma on the coordinate density
+ *   f_X(x) = Gamma(d/2) / (sqrt(pi) Gamma((d-1)/2)) (1 - x^2)^((d-3)/2);
+ * [NIK] "Step 2: optimal scalar quantization (Lloyd-Max)": 2^b centroids
+ *   minimizing C(f_X, b); the codebook depends only on (d, b), no data.
+ * Host only, deterministic. Outputs (host, caller-owned):
+ *   centroids  [2^bits] float32, ascending (the fp64 solution rounded to nearest)
+ *   thresholds [2^bits - 1] float32 (nullable): t_i = the largest float32 not
+ *              above the exact midpoint of centroids i and i+1, so that for any
+ *              float32 y, (y > t_i) <=> y is strictly nearer centroid i+1, and
+ *              a tie goes to the lower index.
+ *   cost_per_coord (nullable): C(f_X, b) in fp64; d * C is D_mse (Theorem 1).
+ * bits == 0 gives the single centroid {0} (the MSE stage of prod with b = 1).
+ */
+tq_status tq_codebook_build(int d, int bits, float* centroids, float* thresholds,
+                            double* cost_per_coord);
+
+/*
+ * Create a quantizer.
+ * [NIK] "Step 0: normalization", "Step 1: random rotation", "Step 2";
+ * for TQ_PROD also [NIK] "QJL: a one-bit method" and "TurboQuant proper":
+ * b-1 bit MSE stage, then sign(S r) and |r| of the residual.
+ *   d, bits   : head dimension and total bits per coordinate (prod: b-1 for the
+ *               MSE stage plus 1 QJL bit).
+ *   pi        : host, float64 [d][d] row-major, orthogonal (y = Pi u).
+ *   s         : host, float64 [d][d] row-major Gaussian QJL matrix; required
+ *               iff variant == TQ_PROD, ignored otherwise. It must be drawn
+ *               independently of pi ([NIK] "What the community did", item 3).
+ *   out       : receives the handle. The matrices are copied; the caller may
+ *               free them after the call.
+ * Allocates device memory on the current HIP device; the handle may be used
+ * only on that device.
+ */
+tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double* pi,
+                              const double* s, tq_quantizer** out);
+/* Frees the handle. The caller must first synchronize work that uses it. */
+tq_status tq_quantizer_destroy(tq_quantizer* q);
+/* Shape queries (any pointer may be NULL). code_planes = b for mse, b-1 for
+ * prod; a VECTOR record has code_planes*d/8 code bytes and, for prod, d/8
+ * sign bytes. */
+tq_status tq_quantizer_info(const tq_quantizer* q, int* d, int* bits, tq_variant* variant,
+                            int* code_planes);
+
+/*
+ * Q (quantize), grouped: vector i of group g (i < n_per_group) is
+ * x[g*n_per_group + i] and uses quantizer qz[g]. All handles must share
+ * (d, bits, variant). One launch covers all groups.
+ *   qz          : host array [n_groups] of handles.
+ *   x           : device [n_groups*n_per_group][d], float32 or bfloat16.
+ *   layout      : TQ_LAYOUT_VECTOR, or TQ_LAYOUT_BLOCK32 (TQ_MSE only, and
+ *                 n_per_group % 32 == 0; blocks never straddle groups).
+ *   codes       : device, code_planes*d/8 bytes per vector (may be NULL when
+ *                 code_planes == 0).
+ *   signs       : device [n][d/8] (TQ_PROD only; NULL for TQ_MSE).
+ *   norms       : device float32 [n]: |x|_2 rounded to float32.
+ *   rnorms      : device float32 [n]: |r|_2 of the unit-vector residual (prod).
+ *   rot_dbg     : device float32 [n][d] or NULL: the rotated unit vector
+ *                 y = Pi x / |x| exactly as the kernel compared it.
+ *   proj_dbg    : device float32 [n][d] or NULL (prod): the projection S r
+ *                 whose signs were stored.
+ * A zero vector gets norm 0, rnorm 0 and all code and sign bits 0.
+ */
+tq_status tq_quantize(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group,
+                      const void* x, tq_dtype x_dtype, tq_layout layout, uint8_t* codes,
+                      uint8_t* signs, float* norms, float* rnorms, float* rot_dbg,
+                      float* proj_dbg, void* stream);
+
+/* Q_mse for n vectors with one quantizer, VECTOR layout ([NIK] Theorem 1's map
+ * Q_mse : R^d -> {0,1}^(b d)). Same argument meanings as tq_quantize. */
+tq_status tq_quantize_mse(const tq_quantizer* q, const void* x, tq_dtype x_dtype, int64_t n,
+                          uint8_t* codes, float* norms, float* rot_dbg, void* stream);
+
+/* Q_prod for n vectors, VECTOR layout ([NIK] Theorem 2's map
+ * Q_prod : S^(d-1) -> [2^(b-1)]^d x {-1,1}^d x R, applied to x/|x| with |x| kept). */
+tq_status tq_quantize_prod(const tq_quantizer* q, const void* x, tq_dtype x_dtype, int64_t n,
+                           uint8_t* codes, uint8_t* signs, float* norms, float* rnorms,
+                           float* rot_dbg, float* proj_dbg, void* stream);
+
+/*
+ * Q^-1 (dequantize) of n vectors:
+ *   mse : x~ = |x| * Pi^T c[idx]                          ([NIK] "Step 2")
+ *   prod: x~ = |x| * (Pi^T c[idx] + |r| sqrt(pi/2)/d S^T z) ([NIK] "QJL",
+ *         "TurboQuant proper")
+ * layout BLOCK32 requires n % 32 == 0 (mse only). x_out: device float32 [n][d].
+ * signs / rnorms are ignored (may be NULL) for TQ_MSE.
+ */
+tq_status tq_dequantize(const tq_quantizer* q, tq_layout layout, const uint8_t* codes,
+                        const uint8_t* signs, const float* norms, const float* rnorms,
+                        int64_t n, float* x_out, void* stream);
+
+/*
+ * Inner products <y_i, x~_j> of m float32 queries with n packed vectors
+ * (VECTOR layout), computed from the codes without materializing x~
+ * ([NIK] problem statement, D_prod; used for D_prod and vector search).
+ *   y   : device float32 [m][d];  out : device float32 [m][n].
+ */
+tq_status tq_inner_products(const tq_quantizer* q, const float* y, int64_t m,
+                            const uint8_t* codes, const uint8_t* signs, const float* norms,
+                            const float* rnorms, int64_t n, float* out, void* stream);
+
+/*
+ * Decode attention over a packed KV cache ([NIK] problem statement: the new
+ * token's query is scored against every cached key and the values are
+ * averaged with the softmax weights; [NAH]: prod keys need a dedicated
+ * attention kernel). For each batch b and query head h with KV head
+ * g = floor(h * n_kv_heads / n_q_heads):
+ *   s_t = scale * <q[b,h], k~_t>,  t < ctx_lens[b]
+ *   out[b,h] = sum_t softmax(s)_t v~_t
+ * where k~, v~ are the dequantized key and value of token t. The kernel never
+ * materializes them: keys are scored in rotated space (Pi_K q and S_K q) and
+ * values are accumulated in rotated space and rotated back once.
+ *
+ * Cache layout (caller-owned device memory), with G = batch*n_kv_heads groups
+ * indexed b*n_kv_heads + g and T = max_ctx (a multiple of 32):
+ *   keys  : codes [G][T][code_planes*d/8] VECTOR layout (may be NULL if
+ *           code_planes == 0); signs [G][T][d/8] (prod keys, else NULL);
+ *           norms [G][T]; rnorms [G][T] (prod keys, else NULL).
+ *   values: TQ_MSE quantizers only; codes [G][T/32][4*bits*d] BLOCK32 layout;
+ *           norms [G][T]; signs and rnorms NULL.
+ *   qz    : host array [n_kv_heads] of handles per tensor; all key handles
+ *           share (d, bits, variant), all value handles share (d, bits).
+ *   q     : device bfloat16 [batch][n_q_heads][d].
+ *   ctx_lens : device int32 [batch]; values are clamped to [0, max_ctx]; a
+ *           sequence with no tokens gets an all-zero output.
+ *   out   : device float32 [batch][n_q_heads][d].
+ *   scores_dbg : device float32 [batch][n_q_heads][max_ctx] or NULL: s_t for
+ *           t < ctx_len (other entries untouched).
+ *   workspace : device scratch of at least tq_decode_workspace_size() bytes,
+ *           used only during the call's stream work. Concurrent calls need
+ *           separate workspaces.
+ * n_q_heads must be a multiple of n_kv_heads, with a group size of at most 8
+ * or a multiple of 8. Results are deterministic for a fixed shape (fixed
+ * split schedule, no floating-point atomics).
+ */
+typedef struct {
+  int batch;
+  int n_q_heads;
+  int n_kv_heads;
+  int head_dim;
+  int64_t max_ctx;
+} tq_attn_shape;
+
+typedef struct {
+  const tq_quantizer* const* qz;
+  const uint8_t* codes;
+  const uint8_t* signs;
+  const float* norms;
+  const float* rnorms;
+} tq_packed_kv;
+
+tq_status tq_decode_workspace_size(const tq_attn_shape* shape, const tq_packed_kv* k,
+                                   const tq_packed_kv* v, size_t* bytes);
+
+tq_status tq_decode_attention(const tq_attn_shape* shape, const void* q, const tq_packed_kv* k,
+                              const tq_packed_kv* v, const int32_t* ctx_lens, float scale,
+                              float* out, float* scores_dbg, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -7,6 +7,7 @@ library.
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 from scipy import special
@@ -113,7 +114,9 @@ def codebook(d: int, bits: int) -> np.ndarray:
 
 def nearest_index(y, centroids) -> np.ndarray:
     """[NIK] "Step 2": for every coordinate, the index of the nearest centroid.
-    Ties go to the lower index (argmin returns the first minimum)."""
+    Ties go to the lower index. Distances are compared exactly: where the fp64
+    distances of the two best candidates are within rounding of each other,
+    they are recomputed in rational arithmetic."""
     y = np.asarray(y, dtype=np.float64)
     c = np.asarray(centroids, dtype=np.float64)
     out = np.empty(y.shape, dtype=np.int64)
@@ -121,8 +124,17 @@ def nearest_index(y, centroids) -> np.ndarray:
     flat_o = out.reshape(-1)
     step = 1 << 20
     for s in range(0, flat_y.size, step):
-        dist = np.abs(flat_y[s:s + step, None] - c[None, :])
-        flat_o[s:s + step] = np.argmin(dist, axis=1)
+        ys = flat_y[s:s + step]
+        dist = np.abs(ys[:, None] - c[None, :])
+        best = np.argmin(dist, axis=1)
+        flat_o[s:s + step] = best
+        if c.size > 1:
+            part = np.partition(dist, 1, axis=1)
+            near = np.nonzero(part[:, 1] - part[:, 0] <= 1e-12 * (np.abs(ys) + np.max(np.abs(c))))[0]
+            for i in near:
+                yi = Fraction(float(ys[i]))
+                exact = [abs(yi - Fraction(float(ci))) for ci in c]
+                flat_o[s + i] = min(range(c.size), key=lambda k: (exact[k], k))
     return out
 
 
@@ -332,6 +344,8 @@ def decode_attention(q, kcache, vcache, ctx_lens, scale, *, return_scores=False)
     cv = codebook(d, vcache["bits"])
     for b in range(B):
         T = int(ctx_lens[b])
+        if T == 0:
+            continue  # no cached token: no attention mass, the output is defined as 0
         for h in range(Hkv):
             Kt = _dequant_k(kcache, b, h, T, ck)
             Vt = _dequant_v(vcache, b, h, T, cv)

@@ -1,0 +1,65 @@
+"""Shared helpers for the GPU parity tests: quantizers from seeded matrices,
+caches packed by the oracle, and comparisons in the documented tolerances."""
+import math
+
+import numpy as np
+
+import oracle as O
+import tq_synth as syn
+
+RTOL, ATOL = 1e-3, 1e-4          # scores and attention outputs
+TIE_BAND = 1e-5                   # codes may flip only this close to a threshold
+MAX_FLIP_RATE = 1e-4
+
+
+def matrices(d, config, tensor, head, prod):
+    Pi = syn.rotation(d, config, tensor, head)
+    S = syn.gaussian_matrix(d, config, tensor, head) if prod else None
+    return Pi, S
+
+
+def quantizer(tq, d, bits, variant, config, tensor, head):
+    Pi, S = matrices(d, config, tensor, head, variant == "prod")
+    return tq.Quantizer(d, bits, variant, Pi, S), Pi, S
+
+
+def oracle_cache_slice(x, d, bits, variant, Pi, S, layout):
+    """Quantize float vectors x [T, d] with the oracle; return numpy arrays in the
+    library's layouts plus the dequantized vectors."""
+    planes = bits - 1 if variant == "prod" else bits
+    cb = O.codebook(d, planes)
+    if variant == "prod":
+        r = O.quantize_prod(x, Pi, S, cb)
+        xt = O.dequantize_prod(r["idx"], r["signs"], r["norms"], r["rnorms"], Pi, S, cb)
+    else:
+        r = O.quantize_mse(x, Pi, cb)
+        xt = O.dequantize_mse(r["idx"], r["norms"], Pi, cb)
+    out = {"norms": r["norms"], "xt": xt, "idx": r["idx"]}
+    if planes > 0:
+        out["codes"] = (O.pack_block_layout(r["idx"], planes) if layout == "block32"
+                        else O.pack_vector_layout(r["idx"], planes))
+    if variant == "prod":
+        out["signs"] = O.pack_bits(r["signs"])
+        out["rnorms"] = r["rnorms"]
+    return out
+
+
+def allclose_report(got, want, rtol=RTOL, atol=ATOL):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    err = np.abs(got - want)
+    bad = err > atol + rtol * np.abs(want)
+    return int(bad.sum()), float(err.max()) if err.size else 0.0
+
+
+def near_threshold(y, centroids, band=TIE_BAND):
+    mids = (centroids[:-1] + centroids[1:]) / 2
+    if mids.size == 0:
+        return np.zeros_like(y, dtype=bool)
+    return np.min(np.abs(np.asarray(y)[..., None] - mids), axis=-1) <= band
+
+
+def ulp_diff_f32(a, b):
+    a = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(a - b)

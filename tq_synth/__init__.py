@@ -131,3 +131,27 @@ def ragged_lengths(batch: int, max_ctx: int, config: int, minimum: int = 1) -> n
         lens[0] = max_ctx
         lens[1] = minimum
     return lens.astype(np.int32)
+
+
+def kv_vectors_device(G: int, n: int, d: int, config: int, tensor: int, device, *,
+                      outliers: int = 4, outlier_scale: float = 10.0, lognormal_sigma: float = 0.0,
+                      seed_offset: int = 0):
+    """Bulk synthetic head vectors drawn on the GPU with torch's seeded generator,
+    bf16 tensor [G, n, d]. Same distribution as ``kv_vectors`` (N(0,1), fixed
+    outlier channels x10 per group, optional per-vector LogNormal scale) but a
+    different random stream: used to fill large caches whose values are never
+    compared element by element with the oracle."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(ROOT_SEED * 1000 + config * 100 + tensor * 10 + seed_offset)
+    out = torch.empty((G, n, d), dtype=torch.bfloat16, device=device)
+    for gi in range(G):
+        v = torch.randn((n, d), generator=gen, device=device, dtype=torch.float32)
+        if lognormal_sigma > 0:
+            s = torch.exp(lognormal_sigma * torch.randn((n,), generator=gen, device=device))
+            v *= s[:, None]
+        if outliers:
+            ch = torch.from_numpy(outlier_channels(d, config, tensor, gi, outliers)).to(device)
+            v[:, ch] *= outlier_scale
+        out[gi] = v.to(torch.bfloat16)
+    return out
