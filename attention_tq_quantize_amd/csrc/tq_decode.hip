@@ -31,6 +31,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <string>
 
 #include "tq_device.h"
 
@@ -105,131 +107,129 @@ struct KWords {
 // [32,48) 2^-E_mse, [48,64) 2^-E_qjl, one value per MFMA row.
 constexpr int kConstsPerUnit = 64;
 
+// One workgroup of D threads per (batch, query head): thread j computes
+// q'_j = (Pi_K q)_j and q''_j = (S_K q)_j, then the workgroup writes this head's
+// two MFMA rows (hi, lo) of every score-operand fragment and of the constants.
+// The workgroup of the chunk's first head also zero-fills unused rows.
 template <int D, int PK, bool QJL>
-__global__ __launch_bounds__(kThreads) void decode_prep_kernel(DecPrepParams prm) {
+__global__ __launch_bounds__(D) void decode_prep_kernel(DecPrepParams prm) {
   using KW = KWords<D, PK, QJL>;
-  __shared__ float qs[8][D], qp[8][D], qq[8][D];
-  __shared__ float red[2][8][kThreads / 8];
-  __shared__ int em_s[8], eq_s[8];
-  const int bhc = blockIdx.x;
-  const int chunk = bhc % prm.n_chunks;
-  const int bh = bhc / prm.n_chunks;
-  const int b = bh / prm.Hkv, hkv = bh % prm.Hkv;
-  const int hq0 = hkv * prm.group + chunk * prm.chunk_heads;
-  for (int e = threadIdx.x; e < 8 * D; e += kThreads) {
-    const int h = e / D, j = e % D;
-    float v = 0.f;
-    if (h < prm.chunk_heads) v = bf16_val(prm.q[((int64_t)b * prm.Hq + hq0 + h) * D + j]);
-    qs[h][j] = v;
+  __shared__ float qs[D], qp[D], qq[D];
+  __shared__ float red[4][D / 64];
+  const int bhq = blockIdx.x;
+  const int b = bhq / prm.Hq, hq = bhq % prm.Hq;
+  const int hkv = hq / prm.group;
+  const int in_group = hq % prm.group;
+  const int chunk = in_group / prm.chunk_heads, h = in_group % prm.chunk_heads;
+  const int bhc = (b * prm.Hkv + hkv) * prm.n_chunks + chunk;
+  const int j = threadIdx.x;
+  qs[j] = bf16_val(prm.q[(int64_t)bhq * D + j]);
+  __syncthreads();
+  const float4* prow = (const float4*)(prm.pk[hkv] + (int64_t)j * D);
+  const float4* srow = QJL ? (const float4*)(prm.sk[hkv] + (int64_t)j * D) : nullptr;
+  float a0 = 0.f, a1 = 0.f, c0 = 0.f, c1 = 0.f;
+#pragma unroll 4
+  for (int k = 0; k < D / 4; k += 2) {
+    const float4 p0 = prow[k], p1 = prow[k + 1];
+    a0 += p0.x * qs[4 * k] + p0.y * qs[4 * k + 1] + p0.z * qs[4 * k + 2] + p0.w * qs[4 * k + 3];
+    a1 += p1.x * qs[4 * k + 4] + p1.y * qs[4 * k + 5] + p1.z * qs[4 * k + 6] + p1.w * qs[4 * k + 7];
+    if constexpr (QJL) {
+      const float4 s0 = srow[k], s1 = srow[k + 1];
+      c0 += s0.x * qs[4 * k] + s0.y * qs[4 * k + 1] + s0.z * qs[4 * k + 2] + s0.w * qs[4 * k + 3];
+      c1 += s1.x * qs[4 * k + 4] + s1.y * qs[4 * k + 5] + s1.z * qs[4 * k + 6] + s1.w * qs[4 * k + 7];
+    }
+  }
+  const float vp = a0 + a1, vq = c0 + c1;
+  qp[j] = vp;
+  qq[j] = vq;
+  // per-head sums and maxima (wave reductions, then across the D/64 waves)
+  float s_p = vp, s_q = vq, m_p = fabsf(vp), m_q = fabsf(vq);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    s_p += __shfl_xor(s_p, o);
+    s_q += __shfl_xor(s_q, o);
+    m_p = fmaxf(m_p, __shfl_xor(m_p, o));
+    m_q = fmaxf(m_q, __shfl_xor(m_q, o));
+  }
+  if ((j & 63) == 0) {
+    red[0][j / 64] = s_p;
+    red[1][j / 64] = s_q;
+    red[2][j / 64] = m_p;
+    red[3][j / 64] = m_q;
   }
   __syncthreads();
-  const float* P = prm.pk[hkv];
-  const float* S = prm.sk[hkv];
-  for (int e = threadIdx.x; e < 8 * D; e += kThreads) {
-    const int h = e / D, j = e % D;
-    float a = 0.f, c = 0.f;
-    if (h < prm.chunk_heads) {
-      for (int k = 0; k < D; ++k) {
-        a += P[j * D + k] * qs[h][k];
-        if constexpr (QJL) c += S[j * D + k] * qs[h][k];
-      }
-    }
-    qp[h][j] = a;
-    qq[h][j] = c;
+  float sum_p = 0.f, sum_q = 0.f, max_p = 0.f, max_q = 0.f;
+#pragma unroll
+  for (int w = 0; w < D / 64; ++w) {
+    sum_p += red[0][w];
+    sum_q += red[1][w];
+    max_p = fmaxf(max_p, red[2][w]);
+    max_q = fmaxf(max_q, red[3][w]);
   }
-  __syncthreads();
-  // per-head max |q'| and |q''|: 32 threads per head
-  {
-    const int h = threadIdx.x / 32, t = threadIdx.x % 32;
-    float mp = 0.f, mq = 0.f;
-    for (int j = t; j < D; j += 32) {
-      mp = fmaxf(mp, fabsf(qp[h][j]));
-      mq = fmaxf(mq, fabsf(qq[h][j]));
-    }
-    red[0][h][t] = mp;
-    red[1][h][t] = mq;
+  float amax = 0.f, asum = 0.f;
+  for (int s = 0; s < KW::WK; ++s) {
+    amax = fmaxf(amax, fabsf(prm.kcoef[s]));
+    asum += prm.kcoef[s];
   }
-  __syncthreads();
-  if (threadIdx.x < 8) {
-    const int h = threadIdx.x;
-    float mp = 0.f, mq = 0.f;
-    for (int t = 0; t < 32; ++t) {
-      mp = fmaxf(mp, red[0][h][t]);
-      mq = fmaxf(mq, red[1][h][t]);
-    }
-    float amax = 0.f;
-    for (int s = 0; s < KW::WK; ++s) amax = fmaxf(amax, fabsf(prm.kcoef[s]));
-    em_s[h] = range_exp(2.f * amax * mp * prm.scale_log2e);
-    eq_s[h] = range_exp(2.f * prm.kappa * mq * prm.scale_log2e);
+  const int em = range_exp(2.f * amax * max_p * prm.scale_log2e);
+  const int eq = range_exp(2.f * prm.kappa * max_q * prm.scale_log2e);
+  float* cst = prm.consts + (int64_t)bhc * kConstsPerUnit;
+  if (j < 2) {
+    const int row = 2 * h + j;
+    cst[row] = j == 0 ? -asum * sum_p * prm.scale_log2e * ldexpf(1.0f, em) : 0.f;
+    cst[16 + row] = j == 0 ? (QJL ? -prm.kappa * sum_q * prm.scale_log2e * ldexpf(1.0f, eq) : 0.f) : 0.f;
+    cst[32 + row] = ldexpf(1.0f, -em);
+    cst[48 + row] = ldexpf(1.0f, -eq);
   }
-  __syncthreads();
-  // constants: hi rows carry -(sum_s a_s sum_j q'_j) and -kappa sum_j q''_j, x scale log2e 2^E
-  if (threadIdx.x < 64) {
-    const int which = threadIdx.x / 16, row = threadIdx.x % 16, h = row / 2;
-    float v = 0.f;
-    if (h < prm.chunk_heads) {
-      const int E = (which == 0 || which == 2) ? em_s[h] : eq_s[h];
-      if (which < 2) {
-        if ((row & 1) == 0) {
-          float sq = 0.f;
-          for (int j = 0; j < D; ++j) sq += which == 0 ? qp[h][j] : qq[h][j];
-          float coef = 0.f;
-          if (which == 0) {
-            for (int s = 0; s < KW::WK; ++s) coef += prm.kcoef[s];
-          } else {
-            coef = QJL ? prm.kappa : 0.f;
-          }
-          v = -coef * sq * prm.scale_log2e * ldexpf(1.0f, E);
-        }
-      } else {
-        v = ldexpf(1.0f, -E);
-      }
-    } else if (which >= 2) {
-      v = 1.0f;
-    }
-    prm.consts[bhc * kConstsPerUnit + which * 16 + row] = v;
+  if (h == 0 && prm.chunk_heads < 8 && j >= 2 * prm.chunk_heads && j < 16) {
+    cst[j] = 0.f;
+    cst[16 + j] = 0.f;
+    cst[32 + j] = 1.f;
+    cst[48 + j] = 1.f;
   }
-  // operand fragments
-  for (int e = threadIdx.x; e < KW::NF * 64; e += kThreads) {
-    const int f = e / 64, lane = e % 64;
+  // fragment elements of this head's rows: (fragment f, lane group g, hi/lo) per thread
+  for (int e = j; e < KW::NF * 4 * 2; e += D) {
+    const int f = e / 8, g = (e / 2) % 4, lo = e % 2;
     const int W = f / 4, r = f % 4;
-    const int row = lane % 16, g = lane / 16, h = row / 2;
-    const bool lo = row & 1;
+    const int lane = 16 * g + 2 * h + lo;
     unsigned hv[8];
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int k = it / 2, half = it % 2;
       const int beta = 16 * half + 4 * r + k;  // bit of the lane's word
       float val = 0.f;
-      int E = 0;
-      if (h < prm.chunk_heads) {
-        if (W < KW::NWM) {
-          int s, j;
-          if constexpr (D >= 128) {
-            s = W / (D / 128);
-            j = g * (D / 4) + 32 * (W % (D / 128)) + beta;
-          } else {
-            s = 2 * W + half;
-            j = g * (D / 4) + (beta % 16);
-          }
-          if (s < KW::WK) val = 2.f * prm.kcoef[s] * qp[h][j];
-          E = em_s[h];
+      int E;
+      if (W < KW::NWM) {
+        int s, jj;
+        if constexpr (D >= 128) {
+          s = W / (D / 128);
+          jj = g * (D / 4) + 32 * (W % (D / 128)) + beta;
         } else {
-          const int Wq = W - KW::NWM;
-          if constexpr (D >= 128) {
-            const int j = g * (D / 4) + 32 * Wq + beta;
-            val = 2.f * prm.kappa * qq[h][j];
-          } else {
-            if (half == 0) val = 2.f * prm.kappa * qq[h][g * (D / 4) + beta];
-          }
-          E = eq_s[h];
+          s = 2 * W + half;
+          jj = g * (D / 4) + (beta % 16);
         }
-        val *= prm.scale_log2e * ldexpf(1.0f, E - slot_exp16(k));
+        if (s < KW::WK) val = 2.f * prm.kcoef[s] * qp[jj];
+        E = em;
+      } else {
+        const int Wq = W - KW::NWM;
+        if constexpr (D >= 128) {
+          val = 2.f * prm.kappa * qq[g * (D / 4) + 32 * Wq + beta];
+        } else {
+          if (half == 0) val = 2.f * prm.kappa * qq[g * (D / 4) + beta];
+        }
+        E = eq;
       }
+      val *= prm.scale_log2e * ldexpf(1.0f, E - slot_exp16(k));
       hv[it] = f16_part(val, lo);
     }
     prm.frag[((int64_t)bhc * KW::NF + f) * 64 + lane] =
         u32x4{pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]), pack2(hv[6], hv[7])};
+  }
+  if (h == 0 && prm.chunk_heads < 8) {
+    for (int e = j; e < KW::NF * 64; e += D) {
+      const int lane = e % 64, row = lane % 16;
+      if (row >= 2 * prm.chunk_heads) prm.frag[(int64_t)bhc * KW::NF * 64 + e] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
 }
 
@@ -264,22 +264,43 @@ __device__ __forceinline__ unsigned load_plane_chunk(const uint8_t* rec, int p, 
   }
 }
 
-template <int D, int PK, bool QJL, int VB, bool FOLD, bool SCORES>
-__global__ __launch_bounds__(kThreads) void decode_main_kernel(DecMainParams prm) {
+// lanes l and l ^ 1 exchange a value (DPP quad permutation [1, 0, 3, 2])
+__device__ __forceinline__ float swap_pair(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+}
+// two fp16 bit patterns (in the low 16 bits of each argument) packed into one dword
+__device__ __forceinline__ unsigned pack_f16x2(unsigned lo_half, unsigned hi_half) {
+  return __builtin_amdgcn_perm(hi_half, lo_half, 0x05040100u);
+}
+
+template <int D, int PK, bool QJL, int VB, bool FOLD, bool SCORES, bool PREFETCH>
+__global__ __launch_bounds__(kThreads, FOLD ? 2 : 1) void decode_main_kernel(DecMainParams prm) {
   using KW = KWords<D, PK, QJL>;
   constexpr int WV = n_walsh(VB);
   constexpr int NT = D / 16;   // value N-tiles (16 coordinates each)
   constexpr int VWL = D / 64;  // value words per lane per plane
   constexpr int NACC = FOLD ? 1 : WV;
+  constexpr int NAF = FOLD ? WV : 1;
   constexpr int KREC = PK * D / 8;
-  constexpr bool KF_REG = KW::NF <= 24;  // keep the score operands in registers
+  constexpr int SREC = D / 8;
+  constexpr int VBLK = 4 * VB * D;  // bytes of one 32-token value block
+  constexpr int WPP = D >= 128 ? D / 128 : 1;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int bhc = blockIdx.y;
   const int chunk = bhc % prm.n_chunks;
   const int bh = bhc / prm.n_chunks;
   const int b = bh / prm.Hkv, hkv = bh % prm.Hkv;
+  // score operands of this (batch, kv head, chunk), shared by the workgroup's waves
+  __shared__ u32x4 kf_lds[KW::NF * 64];
+  {
+    const u32x4* src = prm.frag + (int64_t)bhc * KW::NF * 64;
+    for (int i = threadIdx.x; i < KW::NF * 64; i += kThreads) kf_lds[i] = src[i];
+  }
+  __syncthreads();
+  auto kfrag = [&](int f) -> u32x4 { return kf_lds[f * 64 + lane]; };
   const int split = blockIdx.x * 4 + wave;
   if (split >= prm.n_splits) return;
   int64_t ctx = prm.ctx_lens[b];
@@ -288,163 +309,119 @@ __global__ __launch_bounds__(kThreads) void decode_main_kernel(DecMainParams prm
   const int64_t t1 = min(t0 + prm.split_tokens, ctx);
   const int hq0 = hkv * prm.group + chunk * prm.chunk_heads;
 
-  const u32x4* kfg = prm.frag + (int64_t)bhc * KW::NF * 64 + lane;
-  u32x4 kf[KF_REG ? KW::NF : 1];
-  if constexpr (KF_REG) {
-#pragma unroll
-    for (int f = 0; f < KW::NF; ++f) kf[f] = kfg[f * 64];
-  }
-  auto kfrag = [&](int f) -> u32x4 {
-    if constexpr (KF_REG) return kf[f];
-    else return kfg[f * 64];
-  };
   const float* cst = prm.consts + bhc * kConstsPerUnit;
   const float cm0 = cst[r16], cq0 = cst[16 + r16];
   const float ism = cst[32 + r16], isq = cst[48 + r16];
 
+  // wave-uniform bases of this split; per-lane 32-bit offsets below
   const int64_t grp = (int64_t)b * prm.Hkv + hkv;
-  const uint8_t* kc = prm.kcodes + grp * prm.max_ctx * KREC;
-  const uint8_t* ksg = QJL ? prm.ksigns + grp * prm.max_ctx * (D / 8) : nullptr;
-  const float* kn = prm.knorms + grp * prm.max_ctx;
-  const float* kr = QJL ? prm.krnorms + grp * prm.max_ctx : nullptr;
-  const uint8_t* vc = prm.vcodes + grp * (prm.max_ctx / 32) * (int64_t)(4 * VB * D);
-  const float* vn = prm.vnorms + grp * prm.max_ctx;
+  const int64_t tok0 = grp * prm.max_ctx + t0;
+  const uint8_t* kc = prm.kcodes + tok0 * KREC;
+  const uint8_t* ksg = QJL ? prm.ksigns + tok0 * SREC : nullptr;
+  const float* kn = prm.knorms + tok0;
+  const float* kr = QJL ? prm.krnorms + tok0 : nullptr;
+  const float* vn = prm.vnorms + tok0;
+  const uint8_t* vc = prm.vcodes + (grp * (prm.max_ctx / 32) + t0 / 32) * (int64_t)VBLK;
+  const unsigned k_off = (unsigned)(r16 * KREC + g * (D / 32));
+  const unsigned s_off = (unsigned)(r16 * SREC + g * (D / 32));
+  const unsigned n_off = (unsigned)(4 * g);
+  const unsigned v_off = (unsigned)((g * (D / 4) + VWL * r16) * 4);
   const bool lo_row = r16 & 1;
 
   float m_run = -INFINITY, l_acc = 0.f, w_acc = 0.f;
   int ev = 64;  // value accumulator exponent of this row (64 = unset)
+  float wsc[NAF][4];  // per-slot weight multipliers: coefficient (fold) * 2^(ev - e_k)
+#pragma unroll
+  for (int a = 0; a < NAF; ++a)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wsc[a][k] = 0.f;
   f32x4 acc[NACC][NT];
 #pragma unroll
   for (int a = 0; a < NACC; ++a)
 #pragma unroll
     for (int q = 0; q < NT; ++q) acc[a][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t tc = t0; tc < t1; tc += 32) {
-    // ---------------- scores: two tiles of 16 tokens ----------------
-    f32x4 cm[2], cq[2];
+  // Raw cache data of one 32-token chunk for this lane.
+  struct Chunk {
+    unsigned kpl[2][PK > 0 ? PK : 1][WPP];
+    unsigned ksg[2][KW::NWQ > 0 ? KW::NWQ : 1];
+    float4 nk[2], gm[2], nv[2];
+    unsigned vp[VB][VWL];
+  };
+  auto load_chunk = [&](unsigned rel, Chunk& c) {  // rel = chunk start - t0 (multiple of 32)
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      const int64_t tok = tc + 16 * tile + r16;  // always < max_ctx (32-aligned chunks)
-      cm[tile] = f32x4{cm0, cm0, cm0, cm0};
-      cq[tile] = f32x4{cq0, cq0, cq0, cq0};
+      const unsigned tt = rel + 16 * tile;
       if constexpr (PK > 0) {
-        const uint8_t* rec = kc + tok * KREC;
-        constexpr int WPP = D >= 128 ? D / 128 : 1;
-        unsigned pl[PK][WPP];
 #pragma unroll
         for (int p = 0; p < PK; ++p)
 #pragma unroll
-          for (int w = 0; w < WPP; ++w) pl[p][w] = load_plane_chunk<D, PK>(rec, p, g, w);
-#pragma unroll
-        for (int W = 0; W < KW::NWM; ++W) {
-          unsigned word;
-          if constexpr (D >= 128) {
-            const int s = W / (D / 128), w = W % (D / 128);
-            const int mask = walsh_mask(PK, s);
-            word = 0u;
-#pragma unroll
-            for (int p = 0; p < PK; ++p)
-              if (mask >> p & 1) word ^= pl[p][w];
-          } else {
-            unsigned lo16 = 0u, hi16 = 0u;
-            const int s0 = 2 * W, s1 = 2 * W + 1;
-            const int m0 = walsh_mask(PK, s0);
-            const int m1 = s1 < KW::WK ? walsh_mask(PK, s1) : 0;
-#pragma unroll
-            for (int p = 0; p < PK; ++p) {
-              if (m0 >> p & 1) lo16 ^= pl[p][0];
-              if (m1 >> p & 1) hi16 ^= pl[p][0];
-            }
-            word = (lo16 & 0xFFFFu) | (hi16 << 16);
+          for (int w = 0; w < WPP; ++w) {
+            const unsigned o = tt * KREC + k_off + p * (D / 8) + 4 * w;
+            if constexpr (D >= 128) c.kpl[tile][p][w] = *(const unsigned*)(kc + o);
+            else c.kpl[tile][p][w] = *(const unsigned short*)(kc + o);
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) cm[tile] = mfma16(bit_operand(word, r), kfrag(4 * W + r), cm[tile]);
-        }
       }
       if constexpr (QJL) {
-        const uint8_t* srec = ksg + tok * (D / 8);
 #pragma unroll
         for (int Wq = 0; Wq < KW::NWQ; ++Wq) {
-          unsigned word;
-          if constexpr (D >= 128) word = *(const unsigned*)(srec + g * (D / 32) + 4 * Wq);
-          else word = *(const unsigned short*)(srec + g * (D / 32));
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            cq[tile] = mfma16(bit_operand(word, r), kfrag(4 * (KW::NWM + Wq) + r), cq[tile]);
+          const unsigned o = tt * SREC + s_off + 4 * Wq;
+          if constexpr (D >= 128) c.ksg[tile][Wq] = *(const unsigned*)(ksg + o);
+          else c.ksg[tile][Wq] = *(const unsigned short*)(ksg + o);
         }
       }
+      c.nk[tile] = *(const float4*)(kn + tt + n_off);
+      if constexpr (QJL) c.gm[tile] = *(const float4*)(kr + tt + n_off);
+      else c.gm[tile] = float4{0.f, 0.f, 0.f, 0.f};
+      c.nv[tile] = *(const float4*)(vn + tt + n_off);
     }
-    // this lane: row r16 (head r16/2, hi or lo part), tokens tc + 16 tile + 4g + i
-    float s2[2][4];
+    const uint8_t* vblk = vc + (size_t)(rel / 32) * VBLK;
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      const int64_t tb = tc + 16 * tile + 4 * g;
-      const float4 nk = *(const float4*)(kn + tb);
-      float4 gm = float4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (QJL) gm = *(const float4*)(kr + tb);
-      const float nkv[4] = {nk.x, nk.y, nk.z, nk.w};
-      const float gmv[4] = {gm.x, gm.y, gm.z, gm.w};
-      const float cmv[4] = {cm[tile].x, cm[tile].y, cm[tile].z, cm[tile].w};
-      const float cqv[4] = {cq[tile].x, cq[tile].y, cq[tile].z, cq[tile].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // hi row + lo row of the same head live in lanes r16 and r16 ^ 1
-        float sc = (cmv[i] + __shfl_xor(cmv[i], 1)) * ism;
-        if constexpr (QJL) sc += gmv[i] * (cqv[i] + __shfl_xor(cqv[i], 1)) * isq;
-        const float v = nkv[i] * sc;
-        s2[tile][i] = (tb + i < t1) ? v : -INFINITY;
-      }
-      if constexpr (SCORES) {
-        const int h = r16 >> 1;
-        if (!lo_row && h < prm.chunk_heads) {
-          float* dst = prm.scores_dbg + ((int64_t)b * prm.Hq + hq0 + h) * prm.max_ctx;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (tb + i < t1) dst[tb + i] = s2[tile][i] * kLn2;
-        }
+    for (int p = 0; p < VB; ++p) {
+      const uint8_t* src = vblk + p * (4 * (D / 4) * 4) + v_off;
+      if constexpr (VWL == 1) {
+        c.vp[p][0] = *(const unsigned*)src;
+      } else if constexpr (VWL == 2) {
+        const uint2 t = *(const uint2*)src;
+        c.vp[p][0] = t.x;
+        c.vp[p][1] = t.y;
+      } else {
+        const uint4 t = *(const uint4*)src;
+        c.vp[p][0] = t.x;
+        c.vp[p][1] = t.y;
+        c.vp[p][2] = t.z;
+        c.vp[p][3] = t.w;
       }
     }
-    // ---------------- online softmax ----------------
-    float cmax = s2[0][0];
+  };
+
+  const unsigned n_rel = (unsigned)(t1 > t0 ? t1 - t0 : 0);
+  // The hot loop touches the value accumulators only with MFMAs. When a chunk
+  // needs the running max raised (online softmax) or the value exponent lowered,
+  // the loop exits before accumulating that chunk; the accumulators are rescaled
+  // out here and the chunk is processed again.
+  unsigned rel = 0;
+  float pend_cmax = -INFINITY, pend_wmax = 0.f;
+  int pend = 0;  // 1: raise the max to pend_cmax; 2: lower the exponent for pend_wmax
+  while (true) {
+    if (pend) {
+      float f = 1.0f;
+      if (pend == 1) {
+        const float m_new = fmaxf(m_run, pend_cmax);
+        f = exp2f(m_run - m_new);
+        l_acc *= f;
+        w_acc *= f;
+        m_run = m_new;
+      } else {
+        const int e_need = range_exp(pend_wmax);
+        const int ev_new = e_need < ev ? e_need : ev;
+        f = ldexpf(1.0f, ev_new - ev);
+        ev = ev_new;
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile)
+        for (int a = 0; a < NAF; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, s2[tile][i]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    float alpha = 1.0f;
-    if (__any(cmax > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, cmax);
-      alpha = exp2f(m_run - m_new);
-      l_acc *= alpha;
-      w_acc *= alpha;
-      m_run = m_new;
-    }
-    float wv[2][4];
-    float wmax = 0.f;
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      const int64_t tb = tc + 16 * tile + 4 * g;
-      const float4 nv = *(const float4*)(vn + tb);
-      const float nvv[4] = {nv.x, nv.y, nv.z, nv.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(s2[tile][i] - m_run);
-        l_acc += p;
-        const float w = p > 0.f ? p * nvv[i] : 0.f;
-        w_acc += w;
-        wv[tile][i] = w;
-        wmax = fmaxf(wmax, w);
+          for (int k = 0; k < 4; ++k) wsc[a][k] = (FOLD ? prm.vcoef[a] : 1.0f) * ldexpf(1.0f, ev - slot_exp16(k));
       }
-    }
-    wmax = fmaxf(wmax, __shfl_xor(wmax, 16));
-    wmax = fmaxf(wmax, __shfl_xor(wmax, 32));
-    // keep w 2^(ev + 14) below 2^14: lower the row exponent when a chunk brings larger weights
-    const int e_need = range_exp(wmax);
-    const bool lower = wmax > 0.f && e_need < ev;
-    if (__any(lower || alpha != 1.0f)) {
-      const int ev_new = lower ? e_need : ev;
-      const float f = alpha * ldexpf(1.0f, ev_new - ev);
       float fr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) fr[i] = __shfl(f, 4 * g + i);
@@ -457,59 +434,169 @@ __global__ __launch_bounds__(kThreads) void decode_main_kernel(DecMainParams prm
           acc[a][q].z *= fr[2];
           acc[a][q].w *= fr[3];
         }
-      ev = ev_new;
+      pend = 0;
     }
-    // ---------------- values ----------------
-    float sc_v[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) sc_v[k] = ldexpf(1.0f, ev - slot_exp16(k));
-    u32x4 af[FOLD ? WV : 1];
-#pragma unroll
-    for (int a = 0; a < (FOLD ? WV : 1); ++a) {
-      const float cf = FOLD ? prm.vcoef[a] : 1.0f;
-      unsigned d4[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const unsigned h0 = f16_part(wv[0][k] * cf * sc_v[k], lo_row);
-        const unsigned h1 = f16_part(wv[1][k] * cf * sc_v[k], lo_row);
-        d4[k] = pack2(h0, h1);
+    if (rel >= n_rel) break;
+    Chunk cur, nxt;
+    load_chunk(rel, cur);
+    for (; rel < n_rel; rel += 32) {
+      if constexpr (PREFETCH) {
+        if (rel + 32 < n_rel) load_chunk(rel + 32, nxt);
       }
-      af[a] = u32x4{d4[0], d4[1], d4[2], d4[3]};
-    }
-    const uint8_t* vblk = vc + (tc / 32) * (int64_t)(4 * VB * D);
-    unsigned vp[VB][VWL];
+      // ---------------- scores: two tiles of 16 tokens ----------------
+      f32x4 cm[2], cq[2];
 #pragma unroll
-    for (int p = 0; p < VB; ++p) {
-      const uint8_t* src = vblk + ((p * 4 + g) * (D / 4) + VWL * r16) * 4;
-      if constexpr (VWL == 1) {
-        vp[p][0] = *(const unsigned*)src;
-      } else if constexpr (VWL == 2) {
-        const uint2 t = *(const uint2*)src;
-        vp[p][0] = t.x;
-        vp[p][1] = t.y;
-      } else {
-        const uint4 t = *(const uint4*)src;
-        vp[p][0] = t.x;
-        vp[p][1] = t.y;
-        vp[p][2] = t.z;
-        vp[p][3] = t.w;
+      for (int tile = 0; tile < 2; ++tile) {
+        cm[tile] = f32x4{cm0, cm0, cm0, cm0};
+        cq[tile] = f32x4{cq0, cq0, cq0, cq0};
       }
-    }
+      if constexpr (PK > 0) {
 #pragma unroll
-    for (int s = 0; s < WV; ++s) {
-      const int mask = walsh_mask(VB, s);
+        for (int W = 0; W < KW::NWM; ++W) {
+          unsigned word[2];
 #pragma unroll
-      for (int w = 0; w < VWL; ++w) {
-        unsigned word = 0u;
+          for (int tile = 0; tile < 2; ++tile) {
+            if constexpr (D >= 128) {
+              const int s = W / (D / 128), w = W % (D / 128);
+              const int mask = walsh_mask(PK, s);
+              word[tile] = 0u;
 #pragma unroll
-        for (int p = 0; p < VB; ++p)
-          if (mask >> p & 1) word ^= vp[p][w];
+              for (int p = 0; p < PK; ++p)
+                if (mask >> p & 1) word[tile] ^= cur.kpl[tile][p][w];
+            } else {
+              unsigned lo16 = 0u, hi16 = 0u;
+              const int s0 = 2 * W, s1 = 2 * W + 1;
+              const int m0 = walsh_mask(PK, s0);
+              const int m1 = s1 < KW::WK ? walsh_mask(PK, s1) : 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = 4 * w + r;
-          acc[FOLD ? 0 : s][q] = mfma16(af[FOLD ? s : 0], bit_operand(word, r), acc[FOLD ? 0 : s][q]);
+              for (int p = 0; p < PK; ++p) {
+                if (m0 >> p & 1) lo16 ^= cur.kpl[tile][p][0];
+                if (m1 >> p & 1) hi16 ^= cur.kpl[tile][p][0];
+              }
+              word[tile] = (lo16 & 0xFFFFu) | (hi16 << 16);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const u32x4 bf = kfrag(4 * W + r);
+            cm[0] = mfma16(bit_operand(word[0], r), bf, cm[0]);
+            cm[1] = mfma16(bit_operand(word[1], r), bf, cm[1]);
+          }
         }
       }
+      if constexpr (QJL) {
+#pragma unroll
+        for (int Wq = 0; Wq < KW::NWQ; ++Wq) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const u32x4 bf = kfrag(4 * (KW::NWM + Wq) + r);
+            cq[0] = mfma16(bit_operand(cur.ksg[0][Wq], r), bf, cq[0]);
+            cq[1] = mfma16(bit_operand(cur.ksg[1][Wq], r), bf, cq[1]);
+          }
+        }
+      }
+      // this lane: row r16 (head r16/2, hi or lo part), tokens rel + 16 tile + 4g + i
+      const bool full = rel + 32 <= n_rel;
+      float s2[2][4];
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        const float nkv[4] = {cur.nk[tile].x, cur.nk[tile].y, cur.nk[tile].z, cur.nk[tile].w};
+        const float gmv[4] = {cur.gm[tile].x, cur.gm[tile].y, cur.gm[tile].z, cur.gm[tile].w};
+        const float cmv[4] = {cm[tile].x, cm[tile].y, cm[tile].z, cm[tile].w};
+        const float cqv[4] = {cq[tile].x, cq[tile].y, cq[tile].z, cq[tile].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // hi row + lo row of the same head live in lanes r16 and r16 ^ 1
+          float sc = (cmv[i] + swap_pair(cmv[i])) * ism;
+          if constexpr (QJL) sc += gmv[i] * (cqv[i] + swap_pair(cqv[i])) * isq;
+          s2[tile][i] = nkv[i] * sc;
+        }
+        if (!full) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (rel + 16 * tile + 4 * g + i >= n_rel) s2[tile][i] = -INFINITY;
+        }
+      }
+      // ---------------- online softmax ----------------
+      float cmax = fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), fmaxf(s2[0][2], s2[0][3])),
+                         fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      if (__any(cmax > m_run + kRescaleSlack)) {
+        pend = 1;
+        pend_cmax = cmax;
+        break;
+      }
+      float wv[2][4];
+      float psum = 0.f, wsum = 0.f, wmax = 0.f;
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        const float nvv[4] = {cur.nv[tile].x, cur.nv[tile].y, cur.nv[tile].z, cur.nv[tile].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(s2[tile][i] - m_run);
+          psum += p;
+          float w = p * nvv[i];
+          if (!full) w = p > 0.f ? w : 0.f;  // masked tokens may hold garbage norms
+          wsum += w;
+          wv[tile][i] = w;
+          wmax = fmaxf(wmax, w);
+        }
+      }
+      wmax = fmaxf(wmax, __shfl_xor(wmax, 16));
+      wmax = fmaxf(wmax, __shfl_xor(wmax, 32));
+      // keep w 2^(ev + 14) below 2^14: lower the row exponent when a chunk brings larger weights
+      if (__any(wmax > 0.f && range_exp(wmax) < ev)) {
+        pend = 2;
+        pend_wmax = wmax;
+        break;
+      }
+      l_acc += psum;
+      w_acc += wsum;
+      if constexpr (SCORES) {
+        const int h = r16 >> 1;
+        if (!lo_row && h < prm.chunk_heads) {
+          float* dst = prm.scores_dbg + ((int64_t)b * prm.Hq + hq0 + h) * prm.max_ctx + t0;
+#pragma unroll
+          for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const unsigned tt = rel + 16 * tile + 4 * g + i;
+              if (tt < n_rel) dst[tt] = s2[tile][i] * kLn2;
+            }
+        }
+      }
+      // ---------------- values ----------------
+      u32x4 af[NAF];
+#pragma unroll
+      for (int a = 0; a < NAF; ++a) {
+        unsigned d4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const unsigned h0 = f16_part(wv[0][k] * wsc[a][k], lo_row);
+          const unsigned h1 = f16_part(wv[1][k] * wsc[a][k], lo_row);
+          d4[k] = pack_f16x2(h0, h1);
+        }
+        af[a] = u32x4{d4[0], d4[1], d4[2], d4[3]};
+      }
+#pragma unroll
+      for (int s = 0; s < WV; ++s) {
+        const int mask = walsh_mask(VB, s);
+#pragma unroll
+        for (int w = 0; w < VWL; ++w) {
+          unsigned word = 0u;
+#pragma unroll
+          for (int p = 0; p < VB; ++p)
+            if (mask >> p & 1) word ^= cur.vp[p][w];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int q = 4 * w + r;
+            acc[FOLD ? 0 : s][q] = mfma16(af[FOLD ? s : 0], bit_operand(word, r), acc[FOLD ? 0 : s][q]);
+          }
+        }
+      }
+      if constexpr (PREFETCH) cur = nxt;
+      else if (rel + 32 < n_rel) load_chunk(rel + 32, cur);
     }
   }
 
@@ -565,17 +652,21 @@ struct DecCombineParams {
   int n_splits, Hq, group;
 };
 
+// One workgroup per (batch, query head): weights 2^(m_s - M) / L of every
+// split, the merged rotated-space accumulator, then out = Pi_V^T acc.
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecCombineParams prm) {
+  extern __shared__ float wsplit[];  // [n_splits]
   __shared__ float red[kThreads];
+  __shared__ float part[kThreads / D][D];
   __shared__ float o[D];
-  __shared__ float M_s, L_s;
   const int64_t bhq = blockIdx.x;
   const int hq = (int)(bhq % prm.Hq);
   const int hkv = hq / prm.group;
-  const float* ml = prm.part_ml + bhq * prm.n_splits * 2;
+  const int ns = prm.n_splits;
+  const float* ml = prm.part_ml + bhq * ns * 2;
   float mx = -INFINITY;
-  for (int s = threadIdx.x; s < prm.n_splits; s += kThreads)
+  for (int s = threadIdx.x; s < ns; s += kThreads)
     if (ml[2 * s + 1] > 0.f) mx = fmaxf(mx, ml[2 * s]);
   red[threadIdx.x] = mx;
   __syncthreads();
@@ -583,37 +674,61 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecCombinePara
     if (threadIdx.x < st) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + st]);
     __syncthreads();
   }
-  if (threadIdx.x == 0) M_s = red[0];
+  const float M = red[0];
   __syncthreads();
-  const float M = M_s;
   float lsum = 0.f;
-  for (int s = threadIdx.x; s < prm.n_splits; s += kThreads)
-    if (ml[2 * s + 1] > 0.f) lsum += exp2f(ml[2 * s] - M) * ml[2 * s + 1];
+  for (int s = threadIdx.x; s < ns; s += kThreads) {
+    const float l = ml[2 * s + 1];
+    const float wgt = l > 0.f ? exp2f(ml[2 * s] - M) : 0.f;
+    wsplit[s] = wgt;
+    lsum += wgt * l;
+  }
   red[threadIdx.x] = lsum;
   __syncthreads();
   for (int st = kThreads / 2; st > 0; st >>= 1) {
     if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
     __syncthreads();
   }
-  if (threadIdx.x == 0) L_s = red[0];
+  const float L = red[0];
+  const float invL = L > 0.f ? 1.0f / L : 0.f;
+  // merged accumulator: thread (j, phase) sums splits phase, phase + P, ...
+  constexpr int P = kThreads / D;
+  const int j = threadIdx.x % D, ph = threadIdx.x / D;
+  const float* acc = prm.part_acc + bhq * (int64_t)ns * D + j;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int s = ph;
+  for (; s + 3 * P < ns; s += 4 * P) {
+    a0 += wsplit[s] * acc[(int64_t)s * D];
+    a1 += wsplit[s + P] * acc[(int64_t)(s + P) * D];
+    a2 += wsplit[s + 2 * P] * acc[(int64_t)(s + 2 * P) * D];
+    a3 += wsplit[s + 3 * P] * acc[(int64_t)(s + 3 * P) * D];
+  }
+  for (; s < ns; s += P) a0 += wsplit[s] * acc[(int64_t)s * D];
+  part[ph][j] = (a0 + a1) + (a2 + a3);
   __syncthreads();
-  const float L = L_s;
-  for (int j = threadIdx.x; j < D; j += kThreads) {
-    float a = 0.f;
-    if (L > 0.f) {
-      for (int s = 0; s < prm.n_splits; ++s) {
-        if (ml[2 * s + 1] > 0.f) a += exp2f(ml[2 * s] - M) * prm.part_acc[(bhq * prm.n_splits + s) * D + j];
-      }
-      a /= L;
-    }
-    o[j] = a;
+  if (threadIdx.x < D) {
+    float t = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) t += part[p][threadIdx.x];
+    o[threadIdx.x] = t * invL;
   }
   __syncthreads();
-  const float* P = prm.pv[hkv];
-  for (int j = threadIdx.x; j < D; j += kThreads) {
-    float a = 0.f;
-    for (int i = 0; i < D; ++i) a += P[i * D + j] * o[i];
-    prm.out[bhq * D + j] = a;
+  // out[j] = sum_i Pi_V[i][j] o[i]
+  const float* Pv = prm.pv[hkv];
+  float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+  for (int i = ph * 4; i < D; i += 4 * P) {
+    b0 += Pv[(int64_t)i * D + j] * o[i];
+    b1 += Pv[(int64_t)(i + 1) * D + j] * o[i + 1];
+    b2 += Pv[(int64_t)(i + 2) * D + j] * o[i + 2];
+    b3 += Pv[(int64_t)(i + 3) * D + j] * o[i + 3];
+  }
+  part[ph][j] = (b0 + b1) + (b2 + b3);
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float t = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) t += part[p][threadIdx.x];
+    prm.out[bhq * D + threadIdx.x] = t;
   }
 }
 
@@ -644,6 +759,7 @@ tq_status plan_decode(const tq_attn_shape* s, const tq_quantizer* k0, const tq_q
   int64_t ns = (target + units - 1) / units;
   const int64_t max_splits = (p->max_ctx + 255) / 256;
   if (ns > max_splits) ns = max_splits;
+  if (ns > 4096) ns = 4096;  // the combine keeps one weight per split in LDS
   if (ns < 1) ns = 1;
   int64_t st = (p->max_ctx + ns - 1) / ns;
   st = (st + 31) / 32 * 32;
@@ -725,7 +841,17 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
   cp.Hq = p.n_q_heads;
   cp.group = p.group;
 
-  const bool fold = (size_t)p.v_walsh * (p.d / 16) * 4 > 128;  // per-plane accumulators must fit in 128 regs
+  // Value accumulators: one folded set (two waves per SIMD; measured faster on
+  // MI355X) or one set per Walsh plane (fewer VALU ops, one wave per SIMD).
+  // TQ_DECODE_VARIANT selects explicitly: "fold" / "planes", optionally ",prefetch".
+  bool fold = true;
+  bool prefetch = false;
+  if (const char* env = std::getenv("TQ_DECODE_VARIANT")) {
+    const std::string v(env);
+    if (v.find("fold") != std::string::npos) fold = true;
+    if (v.find("planes") != std::string::npos && (size_t)p.v_walsh * (p.d / 16) * 4 <= 128) fold = false;
+    prefetch = v.find("prefetch") != std::string::npos;
+  }
   return dispatch_dim(p.d, [&](auto DC) -> tq_status {
     constexpr int D = decltype(DC)::value;
     return dispatch_planes(p.k_planes, [&](auto KPC) -> tq_status {
@@ -735,7 +861,7 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
         if constexpr ((!QJL && PK == 0) || (QJL && PK > 3)) {
           return set_error(TQ_ERR_UNSUPPORTED, "decode: unsupported key quantizer");
         } else {
-          hipLaunchKernelGGL((decode_prep_kernel<D, PK, QJL>), dim3(units), dim3(kThreads), 0, stream, pp);
+          hipLaunchKernelGGL((decode_prep_kernel<D, PK, QJL>), dim3((unsigned)(p.batch * p.n_q_heads)), dim3(D), 0, stream, pp);
           tq_status st = launch_check("decode: prep launch");
           if (st != TQ_OK) return st;
           st = dispatch_planes(p.v_bits, [&](auto VBC) -> tq_status {
@@ -751,18 +877,21 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
                 } else {
                   return dispatch_bool(scores_dbg != nullptr, [&](auto SC) -> tq_status {
                     constexpr bool SCORES = decltype(SC)::value;
-                    dim3 grid((unsigned)((p.n_splits + 3) / 4), (unsigned)units);
-                    hipLaunchKernelGGL((decode_main_kernel<D, PK, QJL, VB, FOLD, SCORES>), grid, dim3(kThreads), 0,
-                                       stream, mp);
-                    return launch_check("decode: main launch");
+                    return dispatch_bool(prefetch, [&](auto PF) -> tq_status {
+                      constexpr bool PREF = decltype(PF)::value;
+                      dim3 grid((unsigned)((p.n_splits + 3) / 4), (unsigned)units);
+                      hipLaunchKernelGGL((decode_main_kernel<D, PK, QJL, VB, FOLD, SCORES, PREF>), grid, dim3(kThreads),
+                                         0, stream, mp);
+                      return launch_check("decode: main launch");
+                    });
                   });
                 }
               });
             }
           });
           if (st != TQ_OK) return st;
-          hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(p.batch * p.n_q_heads)), dim3(kThreads), 0,
-                             stream, cp);
+          hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(p.batch * p.n_q_heads)), dim3(kThreads),
+                             (size_t)p.n_splits * sizeof(float), stream, cp);
           return launch_check("decode: combine launch");
         }
       });

@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the TurboQuant hot path on one MI355X.
+
+One step = one pass over every stage of the path on synthetic inputs:
+  1. quantize one layer's KV: 8 KV heads x 32768 tokens, head_dim 128, bf16,
+     TurboQuant_mse b=3 (keys -> vector layout, values -> 32-vector block
+     layout), 524,288 vectors;
+  2. decode attention over a resident packed cache: batch 8, 64 query / 8 KV
+     heads, head_dim 128, context 131072, keys TurboQuant_prod b=3, values
+     TurboQuant_mse b=3, one query token per sequence.
+The decode streams 906 MB, more than the 256 MB Infinity Cache, so each step's
+quantize inputs are not cache-resident when it starts.
+
+Printed: one JSON line. `value` is the step's algorithmic HBM bytes (quantize
+in + codes + norms; decode 108 B per token and KV head) per second. Per-stage
+throughput, the decode kernel's roofline and the fp64 oracle's CPU rate on a
+bounded sample are attached.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "quantize Mvec/s (d=128,b=3) + decode-attention GB/s over packed KV, % roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU timing")
+    ap.add_argument("--traffic", type=str, default=None,
+                    help="counter summary with the measured HBM bytes per decode launch (default: profiles/)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy 1 GiB device to device 3 times (scale reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def build_workloads(tq, syn, torch, dev):
+    import numpy as np
+    d = 128
+    # ---- layer quantize (8 heads x 32768 tokens, mse b=3) ----
+    H, T2 = 8, 32768
+    qk2 = [tq.Quantizer(d, 3, "mse", syn.rotation(d, syn.CFG_LAYER_QUANT, syn.T_K, h)) for h in range(H)]
+    qv2 = [tq.Quantizer(d, 3, "mse", syn.rotation(d, syn.CFG_LAYER_QUANT, syn.T_V, h)) for h in range(H)]
+    xk2 = syn.kv_vectors_device(H, T2, d, syn.CFG_LAYER_QUANT, syn.T_K, dev)
+    xv2 = syn.kv_vectors_device(H, T2, d, syn.CFG_LAYER_QUANT, syn.T_V, dev)
+    out_k2 = {"codes": torch.empty((H, T2 * 48), dtype=torch.uint8, device=dev),
+              "norms": torch.empty((H, T2), dtype=torch.float32, device=dev)}
+    out_v2 = {"codes": torch.empty((H, T2 * 48), dtype=torch.uint8, device=dev),
+              "norms": torch.empty((H, T2), dtype=torch.float32, device=dev)}
+    # ---- decode cache (B=8, 64/8 heads, ctx 131072) ----
+    B, Hq, Hkv, T3 = 8, 64, 8, 131072
+    kq3 = [tq.Quantizer(d, 3, "prod", syn.rotation(d, syn.CFG_DECODE_128K, syn.T_K, h),
+                        syn.gaussian_matrix(d, syn.CFG_DECODE_128K, syn.T_K, h)) for h in range(Hkv)]
+    vq3 = [tq.Quantizer(d, 3, "mse", syn.rotation(d, syn.CFG_DECODE_128K, syn.T_V, h)) for h in range(Hkv)]
+    kcodes = torch.empty((B, Hkv, T3, 32), dtype=torch.uint8, device=dev)
+    ksigns = torch.empty((B, Hkv, T3, 16), dtype=torch.uint8, device=dev)
+    knorms = torch.empty((B, Hkv, T3), dtype=torch.float32, device=dev)
+    krn = torch.empty((B, Hkv, T3), dtype=torch.float32, device=dev)
+    vcodes = torch.empty((B, Hkv, T3 // 32, 4 * 3 * d), dtype=torch.uint8, device=dev)
+    vnorms = torch.empty((B, Hkv, T3), dtype=torch.float32, device=dev)
+    for b in range(B):
+        xk = syn.kv_vectors_device(Hkv, T3, d, syn.CFG_DECODE_128K, syn.T_K, dev, seed_offset=b)
+        tq.quantize(kq3, xk, layout="vector", out={"codes": kcodes[b].view(Hkv, -1), "signs": ksigns[b],
+                                                   "norms": knorms[b], "rnorms": krn[b]})
+        del xk
+        xv = syn.kv_vectors_device(Hkv, T3, d, syn.CFG_DECODE_128K, syn.T_V, dev, seed_offset=b)
+        tq.quantize(vq3, xv, layout="block32", out={"codes": vcodes[b].view(Hkv, -1), "norms": vnorms[b]})
+        del xv
+    torch.cuda.synchronize()
+    kcache = tq.KVCache(kq3, knorms, kcodes, ksigns, krn)
+    vcache = tq.KVCache(vq3, vnorms, vcodes)
+    q = torch.from_numpy(syn.decode_queries(B, Hq, d, syn.CFG_DECODE_128K)).to(dev).to(torch.bfloat16)
+    lens = torch.full((B,), T3, dtype=torch.int32, device=dev)
+    ws = torch.empty(tq.decode_workspace_size(B, Hq, Hkv, d, T3, kcache, vcache), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    # a prod quantize of the layer's keys, timed on its own (residual + QJL stage)
+    qp2 = [tq.Quantizer(d, 3, "prod", syn.rotation(d, syn.CFG_LAYER_QUANT, syn.T_K, h),
+                        syn.gaussian_matrix(d, syn.CFG_LAYER_QUANT, syn.T_K, h)) for h in range(H)]
+    out_p2 = {"codes": torch.empty((H, T2 * 32), dtype=torch.uint8, device=dev),
+              "signs": torch.empty((H, T2, 16), dtype=torch.uint8, device=dev),
+              "norms": torch.empty((H, T2), dtype=torch.float32, device=dev),
+              "rnorms": torch.empty((H, T2), dtype=torch.float32, device=dev)}
+    return dict(d=d, H=H, T2=T2, qk2=qk2, qv2=qv2, xk2=xk2, xv2=xv2, out_k2=out_k2, out_v2=out_v2,
+                B=B, Hq=Hq, Hkv=Hkv, T3=T3, kcache=kcache, vcache=vcache, q=q, lens=lens, ws=ws, out=out,
+                qp2=qp2, out_p2=out_p2)
+
+
+def decode_traffic(path=None):
+    """HBM bytes per decode main-kernel launch measured with rocprofv3 FETCH_SIZE /
+    WRITE_SIZE (scaled by a 1 GiB copy), read from the committed counter summary.
+    None when the decode source changed since the counters were taken."""
+    import hashlib
+    path = path or os.path.join(ROOT, "profiles", "decode_attention_b8_ctx128k_hbm_counters.md")
+    src = os.path.join(ROOT, "attention_tq_quantize_amd", "csrc", "tq_decode.hip")
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0].strip() in ("decode_bytes_per_launch", "decode_source_sha256_16"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    now = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if fields.get("decode_source_sha256_16") != now or "decode_bytes_per_launch" not in fields:
+        return None
+    return int(fields["decode_bytes_per_launch"])
+
+
+def cpu_baseline(syn):
+    """The fp64 oracle on a bounded sample of the same workload, host cores."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    d = 128
+    nq = 262144
+    x = syn.kv_vectors(nq, d, syn.CFG_LAYER_QUANT, syn.T_K, 0, 0)
+    Pi = syn.rotation(d, syn.CFG_LAYER_QUANT, syn.T_K, 0)
+    cb = O.codebook(d, 3)
+    t0 = time.perf_counter()
+    r = O.quantize_mse(x, Pi, cb)
+    O.pack_vector_layout(r["idx"], 3)
+    tq_s = time.perf_counter() - t0
+    # decode sample: one (batch, kv head) group, 8 query heads, T tokens
+    T = 131072
+    Pk, Sk = syn.rotation(d, syn.CFG_DECODE_128K, syn.T_K, 0), syn.gaussian_matrix(d, syn.CFG_DECODE_128K, syn.T_K, 0)
+    Pv = syn.rotation(d, syn.CFG_DECODE_128K, syn.T_V, 0)
+    xk = syn.kv_vectors(T, d, syn.CFG_DECODE_128K, syn.T_K, 0, 0)
+    xv = syn.kv_vectors(T, d, syn.CFG_DECODE_128K, syn.T_V, 0, 0)
+    ck, cv = O.codebook(d, 2), O.codebook(d, 3)
+    rk = O.quantize_prod(xk, Pk, Sk, ck)
+    rv = O.quantize_mse(xv, Pv, cv)
+    kc = {"variant": "prod", "bits": 3, "d": d, "max_ctx": T, "Pi": Pk[None], "S": Sk[None],
+          "codes": O.pack_vector_layout(rk["idx"], 2)[None, None], "signs": O.pack_bits(rk["signs"])[None, None],
+          "norms": rk["norms"][None, None], "rnorms": rk["rnorms"][None, None]}
+    vc = {"variant": "mse", "bits": 3, "d": d, "max_ctx": T, "Pi": Pv[None],
+          "codes": O.pack_block_layout(rv["idx"], 3).reshape(1, 1, T // 32, -1), "norms": rv["norms"][None, None]}
+    q = syn.decode_queries(1, 8, d, syn.CFG_DECODE_128K)
+    t0 = time.perf_counter()
+    O.decode_attention(q, kc, vc, np.array([T]), 1 / math.sqrt(d))
+    td_s = time.perf_counter() - t0
+    qbytes = nq * (256 + 48 + 4)
+    dbytes = T * 108
+    return {"value": round((qbytes + dbytes) / (tq_s + td_s) / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"fp64 oracle: quantize_mse of {nq} bf16 vectors (d=128, b=3; {tq_s:.2f} s) + decode "
+                       f"attention of one (batch, kv head) group, 8 query heads over {T} tokens "
+                       f"(prod-3 keys, mse-3 values; {td_s:.2f} s); same algorithmic-byte accounting"),
+            "quantize_mvec_s": round(nq / tq_s / 1e6, 5), "decode_gb_s": round(dbytes / td_s / 1e9, 5)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every box here has one GPU).",
+              file=sys.stderr)
+        return 2
+    import torch
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 1 << 30, "copies": 3}))
+        return 0
+    import attention_tq_quantize_amd as tq
+    import tq_synth as syn
+    tq.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("building workloads", file=sys.stderr, flush=True)
+    w = build_workloads(tq, syn, torch, dev)
+
+    def quantize_layer():
+        tq.quantize(w["qk2"], w["xk2"], layout="vector", out=w["out_k2"])
+        tq.quantize(w["qv2"], w["xv2"], layout="block32", out=w["out_v2"])
+
+    def decode():
+        tq.decode_attention(w["q"], w["kcache"], w["vcache"], w["lens"], 1 / math.sqrt(w["d"]), max_ctx=w["T3"],
+                            out=w["out"], workspace=w["ws"])
+
+    for _ in range(args.warmup):
+        quantize_layer()
+        decode()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for k in range(K):
+        ev[k][0].record()
+        quantize_layer()
+        ev[k][1].record()
+        decode()
+        ev[k][2].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    q_ms = sorted(ev[k][0].elapsed_time(ev[k][1]) for k in range(K))
+    d_ms = sorted(ev[k][1].elapsed_time(ev[k][2]) for k in range(K))
+    q_avg = sum(q_ms) / K
+    d_avg = sum(d_ms) / K
+    n_vec = 2 * w["H"] * w["T2"]
+    q_bytes = n_vec * (256 + 48 + 4)
+    d_bytes = w["B"] * w["Hkv"] * w["T3"] * 108
+    ms_per_step = total_ms / K
+    value = (q_bytes + d_bytes) / (ms_per_step * 1e-3) / 1e9
+
+    # residual + QJL stage on its own: prod quantize of the layer's keys
+    for _ in range(3):
+        tq.quantize(w["qp2"], w["xk2"], layout="vector", out=w["out_p2"])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        tq.quantize(w["qp2"], w["xk2"], layout="vector", out=w["out_p2"])
+    e1.record()
+    torch.cuda.synchronize()
+    p_ms = e0.elapsed_time(e1) / 10
+    p_vec = w["H"] * w["T2"]
+
+    traffic = decode_traffic(args.traffic)
+    d_gbs = d_bytes / (d_avg * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in; bf16/f16 hi+lo MFMA operands, f32 accumulate",
+        "data": "synthetic (seeded N(0,1) KV with 4 outlier channels x10 per head, bf16; Haar rotations; Gaussian S)",
+        "config": {"workload": "layer KV quantize (8 heads x 32768 tokens, d=128, mse b=3) + decode attention "
+                               "(B=8, 64/8 heads, d=128, ctx 131072, keys prod b=3, values mse b=3)",
+                   "quantize_vectors": n_vec, "decode_tokens_x_kv_heads": w["B"] * w["Hkv"] * w["T3"]},
+        "components": {
+            "quantize_mvec_s": round(n_vec / (q_avg * 1e-3) / 1e6, 1),
+            "quantize_gb_s": round(q_bytes / (q_avg * 1e-3) / 1e9, 1),
+            "quantize_ms": round(q_avg, 4),
+            "quantize_frac_hbm": round(q_bytes / (q_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "decode_gb_s": round(d_gbs, 1),
+            "decode_ms": round(d_avg, 4),
+            "decode_ms_p10_p90": [round(d_ms[K // 10], 4), round(d_ms[(9 * K) // 10 - 1 if K >= 10 else -1], 4)],
+            "quantize_prod_mvec_s": round(p_vec / (p_ms * 1e-3) / 1e6, 1),
+            "quantize_prod_gb_s": round(p_vec * (256 + 32 + 16 + 8) / (p_ms * 1e-3) / 1e9, 1),
+            "wall_s_timed_region": round(wall, 3),
+        },
+        "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(d_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode attention call (prep + split main loop + combine), "
+                               f"{d_bytes} algorithmic bytes per launch"},
+    }
+    if not args.no_cpu_baseline:
+        print("timing the oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(syn)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

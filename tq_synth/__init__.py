@@ -10,7 +10,7 @@ Random draws that the method itself makes are produced here and passed to both
 sides as plain inputs:
   * the rotation matrix Pi: a Haar-random orthogonal matrix, taken as the Q
     factor of a QR decomposition of an i.i.d. Gaussian matrix with the signs of
-    R's diagonal folded into Q (the pages: "Vechnaya matematika TurboQuant",
+    R's diagonal folded into Q (the page "Eternal mathematics of TurboQuant",
     section "Step 1: random rotation");
   * the QJL matrix S: i.i.d. N(0, 1) entries, drawn from a seed stream that is
     independent of Pi's (same page, sections "QJL" and the community note on
