@@ -171,8 +171,9 @@ __global__ __launch_bounds__(D) void decode_prep_kernel(DecPrepParams prm) {
     amax = fmaxf(amax, fabsf(prm.kcoef[s]));
     asum += prm.kcoef[s];
   }
-  const int em = range_exp(2.f * amax * max_p * prm.scale_log2e);
-  const int eq = range_exp(2.f * prm.kappa * max_q * prm.scale_log2e);
+  // one exponent for both score parts: the main loop scales their sum once
+  const int em = range_exp(fmaxf(2.f * amax * max_p, QJL ? 2.f * prm.kappa * max_q : 0.f) * prm.scale_log2e);
+  const int eq = em;
   float* cst = prm.consts + (int64_t)bhc * kConstsPerUnit;
   if (j < 2) {
     const int row = 2 * h + j;
@@ -250,37 +251,117 @@ struct DecMainParams {
   int64_t split_tokens;
   int n_splits;
   int Hq, Hkv, group, chunk_heads, n_chunks;
-  float vcoef[kMaxWalsh];
-  float vcoef_sum;
+  float vrho[kMaxWalsh];   // per value subset: a_s / a_lead of its set (1 for leads)
+  float vlead[kMaxWalsh];  // per set: the lead subset's coefficient
+  float vcoef_sum;         // sum of all value subset coefficients
 };
-
-template <int D, int PK>
-__device__ __forceinline__ unsigned load_plane_chunk(const uint8_t* rec, int p, int g, int w) {
-  // D/4 bits of plane p for coordinate quarter g; word w of them (D = 64: 16 bits)
-  if constexpr (D >= 128) {
-    return *(const unsigned*)(rec + p * (D / 8) + g * (D / 32) + 4 * w);
-  } else {
-    return *(const unsigned short*)(rec + p * (D / 8) + g * (D / 32));
-  }
-}
 
 // lanes l and l ^ 1 exchange a value (DPP quad permutation [1, 0, 3, 2])
 __device__ __forceinline__ float swap_pair(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
 }
-// two fp16 bit patterns (in the low 16 bits of each argument) packed into one dword
-__device__ __forceinline__ unsigned pack_f16x2(unsigned lo_half, unsigned hi_half) {
-  return __builtin_amdgcn_perm(hi_half, lo_half, 0x05040100u);
+// two floats to fp16 (round toward zero) packed into one dword, a in the low half
+__device__ __forceinline__ unsigned pack_rtz(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 
-template <int D, int PK, bool QJL, int VB, bool FOLD, bool SCORES, bool PREFETCH>
-__global__ __launch_bounds__(kThreads, FOLD ? 2 : 1) void decode_main_kernel(DecMainParams prm) {
+// max of three floats as one v_max3_f32 (fmaxf chains pick up NaN
+// canonicalisations in IEEE mode); the inputs are ordinary VALU results
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max8f(const float (&v)[2][4]) {
+  return max3f(max3f(v[0][0], v[0][1], v[0][2]), max3f(v[0][3], v[1][0], v[1][1]), max3f(v[1][2], v[1][3], v[1][3]));
+}
+// max of non-negative floats through their bit patterns (same order as the values)
+__device__ __forceinline__ unsigned max8_nonneg_bits(const float (&v)[2][4]) {
+  unsigned m = 0u;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, __float_as_uint(v[t][i]));
+  return m;
+}
+
+// Buffer resources: a wave-uniform base in SGPRs plus a 32-bit lane offset keeps
+// the hot loop free of 64-bit VGPR address arithmetic (raw buffer, 32-bit data).
+typedef __amdgpu_buffer_rsrc_t buf_t;
+__device__ __forceinline__ buf_t make_buf(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ unsigned ld32(buf_t r, unsigned voff, unsigned soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint2 ld64(buf_t r, unsigned voff, unsigned soff) {
+  typedef unsigned u2 __attribute__((ext_vector_type(2)));
+  const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return uint2{v.x, v.y};
+}
+__device__ __forceinline__ uint4 ld128(buf_t r, unsigned voff, unsigned soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return uint4{v.x, v.y, v.z, v.w};
+}
+
+// Value accumulator sets. The odd Walsh subsets of the VB value planes are
+// split into NSET sets; set j accumulates sum_t w_t (bits of its lead subset)
+// plus, for its other subsets s, sum_t (w_t rho_s)(bits of s) with
+// rho_s = a_s / a_lead <= 1. The lead of set j is the single top plane
+// {VB-1-j} (the largest coefficients of a symmetric Lloyd-Max codebook); with
+// NSET = 2^(VB-1) every subset is its own lead.
+__host__ __device__ constexpr int value_sets(int D, int VB) {
+  // at most 64 accumulator registers (D/4 per set), and single-plane leads
+  const int wv = n_walsh(VB);
+  int n = 64 / (D / 4);
+  if (n >= wv) return wv;
+  if (n > VB) n = VB;
+  return n < 1 ? 1 : n;
+}
+__host__ __device__ constexpr bool walsh_is_lead(int VB, int NSET, int s) {
+  if (NSET == n_walsh(VB)) return true;
+  for (int j = 0; j < NSET; ++j)
+    if (walsh_mask(VB, s) == (1 << (VB - 1 - j))) return true;
+  return false;
+}
+__host__ __device__ constexpr int walsh_set(int VB, int NSET, int s) {
+  if (NSET == n_walsh(VB)) return s;
+  for (int j = 0; j < NSET; ++j)
+    if (walsh_mask(VB, s) == (1 << (VB - 1 - j))) return j;
+  int k = 0;
+  for (int t = 0; t < s; ++t)
+    if (!walsh_is_lead(VB, NSET, t)) ++k;
+  return k % NSET;
+}
+
+// Largest value-weight operand the loop accepts before it lowers the row's
+// value exponent (fp16 holds up to 65504; the weights are kept below 2^14).
+constexpr float kWeightOperandMax = 32768.0f;
+// "value exponent not chosen yet"
+constexpr int kEvUnset = 40;
+
+// Main loop. One wave per (batch, kv head, head chunk, context split); 32
+// tokens (two 16-token tiles) per iteration.
+//
+// Scores: C[token][row] over 16 rows = 8 query heads x (hi, lo) fp16 parts of
+// the score operands; lane (r, g) holds tokens 16t + 4g + i of row r, and the
+// hi and lo lanes of a head (r, r ^ 1) add their parts with one DPP exchange.
+//
+// Values: A[row][token] holds the hi (even rows) or lo (odd rows) fp16 part of
+// the weight w = p * |v| times 2^(ev - e_k), where e_k is the value of a set
+// bit in slot k = i of the value bit operand (the K order of the value cache
+// block layout puts token 16t + 4g + k in slot k). The factor is folded into
+// the exp2 argument, so the weights need no extra multiply. The value subsets
+// accumulate in NSET sets (see value_sets); each set's lead coefficient and
+// the 0/1-to-sign correction are applied once, after the loop.
+template <int D, int PK, bool QJL, int VB, int NSET, bool SCORES>
+__global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams prm) {
   using KW = KWords<D, PK, QJL>;
   constexpr int WV = n_walsh(VB);
   constexpr int NT = D / 16;   // value N-tiles (16 coordinates each)
   constexpr int VWL = D / 64;  // value words per lane per plane
-  constexpr int NACC = FOLD ? 1 : WV;
-  constexpr int NAF = FOLD ? WV : 1;
+  constexpr int NACC = NSET;
+  static_assert(NSET == WV || NSET <= VB, "accumulator sets need single-plane leads");
   constexpr int KREC = PK * D / 8;
   constexpr int SREC = D / 8;
   constexpr int VBLK = 4 * VB * D;  // bytes of one 32-token value block
@@ -295,6 +376,8 @@ __global__ __launch_bounds__(kThreads, FOLD ? 2 : 1) void decode_main_kernel(Dec
   const int b = bh / prm.Hkv, hkv = bh % prm.Hkv;
   // score operands of this (batch, kv head, chunk), shared by the workgroup's waves
   __shared__ u32x4 kf_lds[KW::NF * 64];
+  // per wave: the norms of the chunk in flight, [0, 32) |k|, [32, 64) |r|, [64, 96) |v|
+  __shared__ float4 nrm_lds[kThreads / 64][24];
   {
     const u32x4* src = prm.frag + (int64_t)bhc * KW::NF * 64;
     for (int i = threadIdx.x; i < KW::NF * 64; i += kThreads) kf_lds[i] = src[i];
@@ -311,116 +394,303 @@ __global__ __launch_bounds__(kThreads, FOLD ? 2 : 1) void decode_main_kernel(Dec
 
   const float* cst = prm.consts + bhc * kConstsPerUnit;
   const float cm0 = cst[r16], cq0 = cst[16 + r16];
-  const float ism = cst[32 + r16], isq = cst[48 + r16];
+  const float isc = cst[32 + r16];  // 2^-E of this row's score operands
 
-  // wave-uniform bases of this split; per-lane 32-bit offsets below
+  // buffer resources over this split's part of each cache array; per-lane 32-bit offsets
   const int64_t grp = (int64_t)b * prm.Hkv + hkv;
   const int64_t tok0 = grp * prm.max_ctx + t0;
-  const uint8_t* kc = prm.kcodes + tok0 * KREC;
-  const uint8_t* ksg = QJL ? prm.ksigns + tok0 * SREC : nullptr;
-  const float* kn = prm.knorms + tok0;
-  const float* kr = QJL ? prm.krnorms + tok0 : nullptr;
-  const float* vn = prm.vnorms + tok0;
-  const uint8_t* vc = prm.vcodes + (grp * (prm.max_ctx / 32) + t0 / 32) * (int64_t)VBLK;
+  const unsigned span = (unsigned)((t1 > t0 ? t1 - t0 : 0) + 31) & ~31u;  // tokens read by this split
+  const buf_t rk = make_buf(prm.kcodes + tok0 * KREC, span * KREC);
+  const buf_t rs = make_buf(QJL ? prm.ksigns + tok0 * SREC : prm.kcodes, QJL ? span * SREC : 0u);
+  const buf_t rn = make_buf(prm.knorms + tok0, span * 4);
+  const buf_t rr = make_buf(QJL ? prm.krnorms + tok0 : prm.knorms, QJL ? span * 4 : 0u);
+  const buf_t rvn = make_buf(prm.vnorms + tok0, span * 4);
+  const buf_t rv = make_buf(prm.vcodes + (grp * (prm.max_ctx / 32) + t0 / 32) * (int64_t)VBLK, (span / 32) * VBLK);
   const unsigned k_off = (unsigned)(r16 * KREC + g * (D / 32));
   const unsigned s_off = (unsigned)(r16 * SREC + g * (D / 32));
-  const unsigned n_off = (unsigned)(4 * g);
   const unsigned v_off = (unsigned)((g * (D / 4) + VWL * r16) * 4);
   const bool lo_row = r16 & 1;
+  const unsigned lo_mask = lo_row ? 0xFFFFE000u : 0u;  // w - (w & mask): the lo part on odd rows
 
-  float m_run = -INFINITY, l_acc = 0.f, w_acc = 0.f;
-  int ev = 64;  // value accumulator exponent of this row (64 = unset)
-  float wsc[NAF][4];  // per-slot weight multipliers: coefficient (fold) * 2^(ev - e_k)
+  float m_run = -INFINITY;  // running max of this row's scores (log2 units)
+  float m_thr = -INFINITY;  // (m_run + slack) 2^E: raise the max above this raw score
+  int ev = kEvUnset;        // value exponent of this row
+  float mk[4];              // m_run - (ev - e_k): exp2(s - mk[k]) = p * 2^(ev - e_k)
+  float lsum[4];            // per slot: sum of p * 2^(ev - e_k)
 #pragma unroll
-  for (int a = 0; a < NAF; ++a)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) wsc[a][k] = 0.f;
+  for (int k = 0; k < 4; ++k) {
+    mk[k] = -INFINITY;
+    lsum[k] = 0.f;
+  }
   f32x4 acc[NACC][NT];
 #pragma unroll
   for (int a = 0; a < NACC; ++a)
 #pragma unroll
     for (int q = 0; q < NT; ++q) acc[a][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 wacc = {0.f, 0.f, 0.f, 0.f};  // sum of w 2^ev per row (every column)
+  const u32x4 ones = {slot_mask(0), slot_mask(1), slot_mask(2), slot_mask(3)};
 
-  // Raw cache data of one 32-token chunk for this lane.
+  // Raw cache data of one 32-token chunk for this lane: its key and value bit
+  // words, and one norm (lanes 0..31: |k| of token lane, 32..63: |r|; nb: |v|)
+  // that goes through LDS to the lanes that use it.
   struct Chunk {
     unsigned kpl[2][PK > 0 ? PK : 1][WPP];
     unsigned ksg[2][KW::NWQ > 0 ? KW::NWQ : 1];
-    float4 nk[2], gm[2], nv[2];
     unsigned vp[VB][VWL];
+    float na, nb;
   };
+  const unsigned ln4 = (unsigned)(lane & 31) * 4;
   auto load_chunk = [&](unsigned rel, Chunk& c) {  // rel = chunk start - t0 (multiple of 32)
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      const unsigned tt = rel + 16 * tile;
       if constexpr (PK > 0) {
 #pragma unroll
         for (int p = 0; p < PK; ++p)
 #pragma unroll
           for (int w = 0; w < WPP; ++w) {
-            const unsigned o = tt * KREC + k_off + p * (D / 8) + 4 * w;
-            if constexpr (D >= 128) c.kpl[tile][p][w] = *(const unsigned*)(kc + o);
-            else c.kpl[tile][p][w] = *(const unsigned short*)(kc + o);
+            const unsigned o = k_off + 16 * tile * KREC + p * (D / 8) + 4 * w;
+            const unsigned x = ld32(rk, o & ~3u, rel * KREC);
+            c.kpl[tile][p][w] = (D >= 128) ? x : ((o & 2u) ? (x >> 16) : (x & 0xFFFFu));
           }
       }
       if constexpr (QJL) {
 #pragma unroll
         for (int Wq = 0; Wq < KW::NWQ; ++Wq) {
-          const unsigned o = tt * SREC + s_off + 4 * Wq;
-          if constexpr (D >= 128) c.ksg[tile][Wq] = *(const unsigned*)(ksg + o);
-          else c.ksg[tile][Wq] = *(const unsigned short*)(ksg + o);
+          const unsigned o = s_off + 16 * tile * SREC + 4 * Wq;
+          const unsigned x = ld32(rs, o & ~3u, rel * SREC);
+          c.ksg[tile][Wq] = (D >= 128) ? x : ((o & 2u) ? (x >> 16) : (x & 0xFFFFu));
         }
       }
-      c.nk[tile] = *(const float4*)(kn + tt + n_off);
-      if constexpr (QJL) c.gm[tile] = *(const float4*)(kr + tt + n_off);
-      else c.gm[tile] = float4{0.f, 0.f, 0.f, 0.f};
-      c.nv[tile] = *(const float4*)(vn + tt + n_off);
     }
-    const uint8_t* vblk = vc + (size_t)(rel / 32) * VBLK;
 #pragma unroll
     for (int p = 0; p < VB; ++p) {
-      const uint8_t* src = vblk + p * (4 * (D / 4) * 4) + v_off;
+      const unsigned o = p * (4 * (D / 4) * 4) + v_off;
+      const unsigned so = (rel / 32) * VBLK;
       if constexpr (VWL == 1) {
-        c.vp[p][0] = *(const unsigned*)src;
+        c.vp[p][0] = ld32(rv, o, so);
       } else if constexpr (VWL == 2) {
-        const uint2 t = *(const uint2*)src;
+        const uint2 t = ld64(rv, o, so);
         c.vp[p][0] = t.x;
         c.vp[p][1] = t.y;
       } else {
-        const uint4 t = *(const uint4*)src;
+        const uint4 t = ld128(rv, o, so);
         c.vp[p][0] = t.x;
         c.vp[p][1] = t.y;
         c.vp[p][2] = t.z;
         c.vp[p][3] = t.w;
       }
     }
+    if (lane < 32) {
+      c.na = __uint_as_float(ld32(rn, ln4, rel * 4));
+      c.nb = __uint_as_float(ld32(rvn, ln4, rel * 4));
+    } else {
+      c.na = QJL ? __uint_as_float(ld32(rr, ln4, rel * 4)) : 0.f;
+      c.nb = 0.f;
+    }
   };
 
   const unsigned n_rel = (unsigned)(t1 > t0 ? t1 - t0 : 0);
-  // The hot loop touches the value accumulators only with MFMAs. When a chunk
-  // needs the running max raised (online softmax) or the value exponent lowered,
-  // the loop exits before accumulating that chunk; the accumulators are rescaled
-  // out here and the chunk is processed again.
+  int pend = 0;           // 1: raise the running max; 2: lower the value exponent
+  float pend_val = 0.f;   // lane maximum that triggered it
+
+  // One chunk: 0 = accumulated, otherwise the pend code (nothing accumulated).
+  auto step = [&](unsigned rel, const Chunk& cur, auto mask_c) -> int {
+    constexpr bool MASK = decltype(mask_c)::value;  // the chunk runs past the context
+    {
+      float* nl = (float*)nrm_lds[wave];
+      nl[lane] = cur.na;
+      if (lane < 32) nl[64 + lane] = cur.nb;
+    }
+    // ---------------- scores: two tiles of 16 tokens ----------------
+    f32x4 cm[2], cq[2];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      cm[tile] = f32x4{cm0, cm0, cm0, cm0};
+      cq[tile] = f32x4{cq0, cq0, cq0, cq0};
+    }
+    // key words of fragment group W (one Walsh subset / the sign plane) for both tiles
+    auto key_words = [&](int W, unsigned (&word)[2]) {
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        if (W >= KW::NWM) {
+          if constexpr (QJL) word[tile] = cur.ksg[tile][W - KW::NWM];
+        } else if constexpr (PK > 0) {
+          if constexpr (D >= 128) {
+            const int s = W / (D / 128), w = W % (D / 128);
+            const int mask = walsh_mask(PK, s);
+            word[tile] = 0u;
+#pragma unroll
+            for (int p = 0; p < PK; ++p)
+              if (mask >> p & 1) word[tile] ^= cur.kpl[tile][p][w];
+          } else {
+            unsigned lo16 = 0u, hi16 = 0u;
+            const int s0 = 2 * W, s1 = 2 * W + 1;
+            const int m0 = walsh_mask(PK, s0);
+            const int m1 = s1 < KW::WK ? walsh_mask(PK, s1) : 0;
+#pragma unroll
+            for (int p = 0; p < PK; ++p) {
+              if (m0 >> p & 1) lo16 ^= cur.kpl[tile][p][0];
+              if (m1 >> p & 1) hi16 ^= cur.kpl[tile][p][0];
+            }
+            word[tile] = (lo16 & 0xFFFFu) | (hi16 << 16);
+          }
+        }
+      }
+    };
+    // fragments are read from LDS one step ahead of their MFMAs
+    u32x4 bf_next = kfrag(0);
+#pragma unroll
+    for (int W = 0; W < KW::NW; ++W) {
+      unsigned word[2];
+      key_words(W, word);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int f = 4 * W + r;
+        const u32x4 bf = bf_next;
+        if (f + 1 < KW::NF) bf_next = kfrag(f + 1);
+        if (W < KW::NWM) {
+          cm[0] = mfma16(bit_operand(word[0], r), bf, cm[0]);
+          cm[1] = mfma16(bit_operand(word[1], r), bf, cm[1]);
+        } else {
+          cq[0] = mfma16(bit_operand(word[0], r), bf, cq[0]);
+          cq[1] = mfma16(bit_operand(word[1], r), bf, cq[1]);
+        }
+        // keep the bit operands next to their MFMAs (hoisting them all costs registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // this lane: row r16 (head r16/2, hi or lo part), tokens rel + 16 tile + 4g + i;
+    // raw scores sr = score 2^E (the row's operand exponent is applied in the exp2 argument)
+    float sr[2][4];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      const float4 nk4 = nrm_lds[wave][4 * tile + g];
+      const float4 gm4 = QJL ? nrm_lds[wave][8 + 4 * tile + g] : float4{0.f, 0.f, 0.f, 0.f};
+      const float nkv[4] = {nk4.x, nk4.y, nk4.z, nk4.w};
+      const float gmv[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
+      const float cmv[4] = {cm[tile].x, cm[tile].y, cm[tile].z, cm[tile].w};
+      const float cqv[4] = {cq[tile].x, cq[tile].y, cq[tile].z, cq[tile].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // hi row + lo row of the same head live in lanes r16 and r16 ^ 1
+        float sc = cmv[i] + swap_pair(cmv[i]);
+        if constexpr (QJL) sc = fmaf(gmv[i], cqv[i] + swap_pair(cqv[i]), sc);
+        sr[tile][i] = nkv[i] * sc;
+      }
+      if constexpr (MASK) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (rel + 16 * tile + 4 * g + i >= n_rel) sr[tile][i] = -INFINITY;
+      }
+    }
+    // ---------------- online softmax: lane-local checks, no cross-lane work ----------------
+    const float mx = max8f(sr);
+    if (__builtin_expect(__any(mx > m_thr), 0)) {
+      pend_val = mx * isc;
+      return 1;
+    }
+    float wv[2][4], pk[2][4];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      const float4 nv4 = nrm_lds[wave][16 + 4 * tile + g];
+      const float nvv[4] = {nv4.x, nv4.y, nv4.z, nv4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pk[tile][i] = __builtin_amdgcn_exp2f(fmaf(sr[tile][i], isc, -mk[i]));  // p 2^(ev - e_i)
+        float w = pk[tile][i] * nvv[i];
+        if constexpr (MASK) w = pk[tile][i] > 0.f ? w : 0.f;  // masked tokens may hold garbage norms
+        wv[tile][i] = w;
+      }
+    }
+    const unsigned wm = max8_nonneg_bits(wv);
+    if (__builtin_expect(__any(wm >= __float_as_uint(kWeightOperandMax)), 0)) {
+      // largest unscaled weight of this lane: wv 2^(e_k - ev)
+      float u = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u = fmaxf(u, fmaxf(wv[0][i], wv[1][i]) * ldexpf(1.0f, slot_exp16(i) - ev));
+      pend_val = u;
+      return 2;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lsum[i] += pk[0][i] + pk[1][i];
+    if constexpr (SCORES) {
+      const int h = r16 >> 1;
+      if (!lo_row && h < prm.chunk_heads) {
+        float* dst = prm.scores_dbg + ((int64_t)b * prm.Hq + hq0 + h) * prm.max_ctx + t0;
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const unsigned tt = rel + 16 * tile + 4 * g + i;
+            if (tt < n_rel) dst[tt] = sr[tile][i] * isc * kLn2;
+          }
+      }
+    }
+    // ---------------- values ----------------
+    // A operand for weights x: the hi (even rows) or lo (odd rows) fp16 part
+    auto a_operand = [&](float rho, bool scaled) -> u32x4 {
+      unsigned d4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x0 = scaled ? wv[0][k] * rho : wv[0][k];
+        const float x1 = scaled ? wv[1][k] * rho : wv[1][k];
+        const float y0 = x0 - __uint_as_float(__float_as_uint(x0) & lo_mask);
+        const float y1 = x1 - __uint_as_float(__float_as_uint(x1) & lo_mask);
+        d4[k] = pack_rtz(y0, y1);
+      }
+      return u32x4{d4[0], d4[1], d4[2], d4[3]};
+    };
+    const u32x4 a_lead = a_operand(1.0f, false);
+#pragma unroll
+    for (int s = 0; s < WV; ++s) {
+      const int mask = walsh_mask(VB, s);
+      const bool lead = walsh_is_lead(VB, NSET, s);
+      const int set = walsh_set(VB, NSET, s);
+      const u32x4 af = lead ? a_lead : a_operand(prm.vrho[s], true);
+#pragma unroll
+      for (int w = 0; w < VWL; ++w) {
+        unsigned word = 0u;
+#pragma unroll
+        for (int p = 0; p < VB; ++p)
+          if (mask >> p & 1) word ^= cur.vp[p][w];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = 4 * w + r;
+          acc[set][q] = mfma16(af, bit_operand(word, r), acc[set][q]);
+          if (r & 1) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    wacc = mfma16(a_lead, ones, wacc);
+    return 0;
+  };
+
+  // The hot loop touches the accumulators only with MFMAs. When a chunk needs
+  // the running max raised or the value exponent lowered, it is not
+  // accumulated: the state is rescaled here and the chunk runs again.
   unsigned rel = 0;
-  float pend_cmax = -INFINITY, pend_wmax = 0.f;
-  int pend = 0;  // 1: raise the max to pend_cmax; 2: lower the exponent for pend_wmax
   while (true) {
     if (pend) {
+      // row-wide maximum of the lane values (lanes 16 apart hold the same row)
+      float v = pend_val;
+      v = fmaxf(v, __shfl_xor(v, 16));
+      v = fmaxf(v, __shfl_xor(v, 32));
       float f = 1.0f;
       if (pend == 1) {
-        const float m_new = fmaxf(m_run, pend_cmax);
-        f = exp2f(m_run - m_new);
-        l_acc *= f;
-        w_acc *= f;
+        const float m_new = fmaxf(m_run, v);
+        f = exp2f(m_run - m_new);  // 0 on the first chunk (m_run = -inf); the state is still zero
         m_run = m_new;
       } else {
-        const int e_need = range_exp(pend_wmax);
+        const int e_need = range_exp(v);  // v: the row's largest weight in this chunk
         const int ev_new = e_need < ev ? e_need : ev;
         f = ldexpf(1.0f, ev_new - ev);
         ev = ev_new;
+      }
+      m_thr = (m_run + kRescaleSlack) / isc;
 #pragma unroll
-        for (int a = 0; a < NAF; ++a)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) wsc[a][k] = (FOLD ? prm.vcoef[a] : 1.0f) * ldexpf(1.0f, ev - slot_exp16(k));
+      for (int k = 0; k < 4; ++k) {
+        mk[k] = m_run - (float)(ev - slot_exp16(k));
+        lsum[k] *= f;
       }
       float fr[4];
 #pragma unroll
@@ -434,209 +704,72 @@ __global__ __launch_bounds__(kThreads, FOLD ? 2 : 1) void decode_main_kernel(Dec
           acc[a][q].z *= fr[2];
           acc[a][q].w *= fr[3];
         }
+      wacc.x *= fr[0];
+      wacc.y *= fr[1];
+      wacc.z *= fr[2];
+      wacc.w *= fr[3];
       pend = 0;
     }
     if (rel >= n_rel) break;
-    Chunk cur, nxt;
-    load_chunk(rel, cur);
-    for (; rel < n_rel; rel += 32) {
-      if constexpr (PREFETCH) {
-        if (rel + 32 < n_rel) load_chunk(rel + 32, nxt);
-      }
-      // ---------------- scores: two tiles of 16 tokens ----------------
-      f32x4 cm[2], cq[2];
-#pragma unroll
-      for (int tile = 0; tile < 2; ++tile) {
-        cm[tile] = f32x4{cm0, cm0, cm0, cm0};
-        cq[tile] = f32x4{cq0, cq0, cq0, cq0};
-      }
-      if constexpr (PK > 0) {
-#pragma unroll
-        for (int W = 0; W < KW::NWM; ++W) {
-          unsigned word[2];
-#pragma unroll
-          for (int tile = 0; tile < 2; ++tile) {
-            if constexpr (D >= 128) {
-              const int s = W / (D / 128), w = W % (D / 128);
-              const int mask = walsh_mask(PK, s);
-              word[tile] = 0u;
-#pragma unroll
-              for (int p = 0; p < PK; ++p)
-                if (mask >> p & 1) word[tile] ^= cur.kpl[tile][p][w];
-            } else {
-              unsigned lo16 = 0u, hi16 = 0u;
-              const int s0 = 2 * W, s1 = 2 * W + 1;
-              const int m0 = walsh_mask(PK, s0);
-              const int m1 = s1 < KW::WK ? walsh_mask(PK, s1) : 0;
-#pragma unroll
-              for (int p = 0; p < PK; ++p) {
-                if (m0 >> p & 1) lo16 ^= cur.kpl[tile][p][0];
-                if (m1 >> p & 1) hi16 ^= cur.kpl[tile][p][0];
-              }
-              word[tile] = (lo16 & 0xFFFFu) | (hi16 << 16);
-            }
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const u32x4 bf = kfrag(4 * W + r);
-            cm[0] = mfma16(bit_operand(word[0], r), bf, cm[0]);
-            cm[1] = mfma16(bit_operand(word[1], r), bf, cm[1]);
-          }
-        }
-      }
-      if constexpr (QJL) {
-#pragma unroll
-        for (int Wq = 0; Wq < KW::NWQ; ++Wq) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const u32x4 bf = kfrag(4 * (KW::NWM + Wq) + r);
-            cq[0] = mfma16(bit_operand(cur.ksg[0][Wq], r), bf, cq[0]);
-            cq[1] = mfma16(bit_operand(cur.ksg[1][Wq], r), bf, cq[1]);
-          }
-        }
-      }
-      // this lane: row r16 (head r16/2, hi or lo part), tokens rel + 16 tile + 4g + i
-      const bool full = rel + 32 <= n_rel;
-      float s2[2][4];
-#pragma unroll
-      for (int tile = 0; tile < 2; ++tile) {
-        const float nkv[4] = {cur.nk[tile].x, cur.nk[tile].y, cur.nk[tile].z, cur.nk[tile].w};
-        const float gmv[4] = {cur.gm[tile].x, cur.gm[tile].y, cur.gm[tile].z, cur.gm[tile].w};
-        const float cmv[4] = {cm[tile].x, cm[tile].y, cm[tile].z, cm[tile].w};
-        const float cqv[4] = {cq[tile].x, cq[tile].y, cq[tile].z, cq[tile].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // hi row + lo row of the same head live in lanes r16 and r16 ^ 1
-          float sc = (cmv[i] + swap_pair(cmv[i])) * ism;
-          if constexpr (QJL) sc += gmv[i] * (cqv[i] + swap_pair(cqv[i])) * isq;
-          s2[tile][i] = nkv[i] * sc;
-        }
-        if (!full) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (rel + 16 * tile + 4 * g + i >= n_rel) s2[tile][i] = -INFINITY;
-        }
-      }
-      // ---------------- online softmax ----------------
-      float cmax = fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), fmaxf(s2[0][2], s2[0][3])),
-                         fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      if (__any(cmax > m_run + kRescaleSlack)) {
-        pend = 1;
-        pend_cmax = cmax;
+    // ping-pong buffers: the next chunk loads while this one computes
+    const unsigned n_full = n_rel & ~31u;  // chunks that lie inside the context
+    Chunk ca, cb;
+    load_chunk(rel, ca);
+    while (rel < n_full) {
+      if (rel + 32 < n_rel) load_chunk(rel + 32, cb);
+      pend = step(rel, ca, std::false_type{});
+      if (pend) break;
+      rel += 32;
+      if (rel >= n_full) {
+        ca = cb;  // the tail chunk, if any
         break;
       }
-      float wv[2][4];
-      float psum = 0.f, wsum = 0.f, wmax = 0.f;
-#pragma unroll
-      for (int tile = 0; tile < 2; ++tile) {
-        const float nvv[4] = {cur.nv[tile].x, cur.nv[tile].y, cur.nv[tile].z, cur.nv[tile].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s2[tile][i] - m_run);
-          psum += p;
-          float w = p * nvv[i];
-          if (!full) w = p > 0.f ? w : 0.f;  // masked tokens may hold garbage norms
-          wsum += w;
-          wv[tile][i] = w;
-          wmax = fmaxf(wmax, w);
-        }
-      }
-      wmax = fmaxf(wmax, __shfl_xor(wmax, 16));
-      wmax = fmaxf(wmax, __shfl_xor(wmax, 32));
-      // keep w 2^(ev + 14) below 2^14: lower the row exponent when a chunk brings larger weights
-      if (__any(wmax > 0.f && range_exp(wmax) < ev)) {
-        pend = 2;
-        pend_wmax = wmax;
-        break;
-      }
-      l_acc += psum;
-      w_acc += wsum;
-      if constexpr (SCORES) {
-        const int h = r16 >> 1;
-        if (!lo_row && h < prm.chunk_heads) {
-          float* dst = prm.scores_dbg + ((int64_t)b * prm.Hq + hq0 + h) * prm.max_ctx + t0;
-#pragma unroll
-          for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const unsigned tt = rel + 16 * tile + 4 * g + i;
-              if (tt < n_rel) dst[tt] = s2[tile][i] * kLn2;
-            }
-        }
-      }
-      // ---------------- values ----------------
-      u32x4 af[NAF];
-#pragma unroll
-      for (int a = 0; a < NAF; ++a) {
-        unsigned d4[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const unsigned h0 = f16_part(wv[0][k] * wsc[a][k], lo_row);
-          const unsigned h1 = f16_part(wv[1][k] * wsc[a][k], lo_row);
-          d4[k] = pack_f16x2(h0, h1);
-        }
-        af[a] = u32x4{d4[0], d4[1], d4[2], d4[3]};
-      }
-#pragma unroll
-      for (int s = 0; s < WV; ++s) {
-        const int mask = walsh_mask(VB, s);
-#pragma unroll
-        for (int w = 0; w < VWL; ++w) {
-          unsigned word = 0u;
-#pragma unroll
-          for (int p = 0; p < VB; ++p)
-            if (mask >> p & 1) word ^= cur.vp[p][w];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int q = 4 * w + r;
-            acc[FOLD ? 0 : s][q] = mfma16(af[FOLD ? s : 0], bit_operand(word, r), acc[FOLD ? 0 : s][q]);
-          }
-        }
-      }
-      if constexpr (PREFETCH) cur = nxt;
-      else if (rel + 32 < n_rel) load_chunk(rel + 32, cur);
+      if (rel + 32 < n_rel) load_chunk(rel + 32, ca);
+      pend = step(rel, cb, std::false_type{});
+      if (pend) break;
+      rel += 32;
+    }
+    if (!pend && rel < n_rel) {
+      pend = step(rel, ca, std::true_type{});
+      if (!pend) rel += 32;
     }
   }
 
   // ---------------- write this split's partial state ----------------
+  // softmax denominator of this row: sum_k lsum[k] 2^(e_k - ev), over the 4 lane groups
+  float l_acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) l_acc += lsum[k] * ldexpf(1.0f, slot_exp16(k) - ev);
   l_acc += __shfl_xor(l_acc, 16);
   l_acc += __shfl_xor(l_acc, 32);
-  w_acc += __shfl_xor(w_acc, 16);
-  w_acc += __shfl_xor(w_acc, 32);
   const int64_t hq_base = (int64_t)b * prm.Hq + hq0;
   if (g == 0 && !lo_row && (r16 >> 1) < prm.chunk_heads) {
     float* ml = prm.part_ml + ((hq_base + (r16 >> 1)) * prm.n_splits + split) * 2;
     ml[0] = m_run;
     ml[1] = l_acc;
   }
+  // sum of w 2^ev per head, in the value lanes' row order (rows 4g .. 4g+3)
+  const float wt[2] = {wacc.x + wacc.y, wacc.z + wacc.w};
   // value lanes: coordinate lane r16 (coords (D/16) r16 + q), rows 4g .. 4g+3 = heads 2g, 2g+1 (hi, lo)
-  const float w_h0 = __shfl(w_acc, 4 * g);
-  const float w_h1 = __shfl(w_acc, 4 * g + 2);
   const int ev_h0 = __shfl(ev, 4 * g);
   const int ev_h1 = __shfl(ev, 4 * g + 2);
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     const int h = 2 * g + hh;
     if (h >= prm.chunk_heads) continue;
-    const float wh = hh ? w_h1 : w_h0;
-    const float unscale = 2.f * ldexpf(1.0f, -(hh ? ev_h1 : ev_h0));
+    const float unscale = ldexpf(1.0f, -(hh ? ev_h1 : ev_h0));
+    const float wh = wt[hh];
     float outv[NT];
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
-      float v = 0.f;
-      if constexpr (FOLD) {
-        const float c2 = hh ? (acc[0][q].z + acc[0][q].w) : (acc[0][q].x + acc[0][q].y);
-        v = unscale * c2 - wh * prm.vcoef_sum;
-      } else {
+      // sum_t w_t c[idx_t] = sum_s a_s (2 sum_t w_t bit_s - sum_t w_t)
+      float v = -wh * prm.vcoef_sum;
 #pragma unroll
-        for (int s = 0; s < WV; ++s) {
-          const float c2 = hh ? (acc[s][q].z + acc[s][q].w) : (acc[s][q].x + acc[s][q].y);
-          v += prm.vcoef[s] * (unscale * c2 - wh);
-        }
+      for (int j = 0; j < NSET; ++j) {
+        const float c2 = hh ? (acc[j][q].z + acc[j][q].w) : (acc[j][q].x + acc[j][q].y);
+        v = fmaf(2.f * prm.vlead[j], c2, v);
       }
-      outv[q] = v;
+      outv[q] = v * unscale;
     }
     float* dst = prm.part_acc + ((hq_base + h) * prm.n_splits + split) * D + (D / 16) * r16;
 #pragma unroll
@@ -825,12 +958,21 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
   mp.group = p.group;
   mp.chunk_heads = p.chunk_heads;
   mp.n_chunks = p.n_chunks;
+  // value subsets: sets, leads and ratios (a_s / a_lead must not exceed 1)
+  const int vb = v0->bits;
+  const int nset = value_sets(p.d, vb);
   float csum = 0.f;
-  for (int s = 0; s < v0->cb.n_walsh; ++s) {
-    mp.vcoef[s] = v0->cb.walsh_coef[s];
-    csum += v0->cb.walsh_coef[s];
-  }
+  for (int s = 0; s < v0->cb.n_walsh; ++s) csum += v0->cb.walsh_coef[s];
   mp.vcoef_sum = csum;
+  for (int s = 0; s < v0->cb.n_walsh; ++s) {
+    if (walsh_is_lead(vb, nset, s)) mp.vlead[walsh_set(vb, nset, s)] = v0->cb.walsh_coef[s];
+  }
+  for (int s = 0; s < v0->cb.n_walsh; ++s) {
+    const float lead = mp.vlead[walsh_set(vb, nset, s)];
+    const float rho = walsh_is_lead(vb, nset, s) ? 1.0f : v0->cb.walsh_coef[s] / lead;
+    if (!(std::fabs(rho) <= 1.0f)) return set_error(TQ_ERR_UNSUPPORTED, "decode: value codebook coefficients out of order");
+    mp.vrho[s] = rho;
+  }
 
   DecCombineParams cp{};
   cp.part_acc = part_acc;
@@ -841,17 +983,6 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
   cp.Hq = p.n_q_heads;
   cp.group = p.group;
 
-  // Value accumulators: one folded set (two waves per SIMD; measured faster on
-  // MI355X) or one set per Walsh plane (fewer VALU ops, one wave per SIMD).
-  // TQ_DECODE_VARIANT selects explicitly: "fold" / "planes", optionally ",prefetch".
-  bool fold = true;
-  bool prefetch = false;
-  if (const char* env = std::getenv("TQ_DECODE_VARIANT")) {
-    const std::string v(env);
-    if (v.find("fold") != std::string::npos) fold = true;
-    if (v.find("planes") != std::string::npos && (size_t)p.v_walsh * (p.d / 16) * 4 <= 128) fold = false;
-    prefetch = v.find("prefetch") != std::string::npos;
-  }
   return dispatch_dim(p.d, [&](auto DC) -> tq_status {
     constexpr int D = decltype(DC)::value;
     return dispatch_planes(p.k_planes, [&](auto KPC) -> tq_status {
@@ -869,23 +1000,13 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
             if constexpr (VB == 0) {
               return set_error(TQ_ERR_UNSUPPORTED, "decode: value bits");
             } else {
-              return dispatch_bool(fold, [&](auto FC) -> tq_status {
-                constexpr bool FOLD = decltype(FC)::value;
-                constexpr bool fits = (n_walsh(VB) * (D / 16) * 4 <= 128);
-                if constexpr (!FOLD && !fits) {
-                  return set_error(TQ_ERR_UNSUPPORTED, "decode: accumulator mode");
-                } else {
-                  return dispatch_bool(scores_dbg != nullptr, [&](auto SC) -> tq_status {
-                    constexpr bool SCORES = decltype(SC)::value;
-                    return dispatch_bool(prefetch, [&](auto PF) -> tq_status {
-                      constexpr bool PREF = decltype(PF)::value;
-                      dim3 grid((unsigned)((p.n_splits + 3) / 4), (unsigned)units);
-                      hipLaunchKernelGGL((decode_main_kernel<D, PK, QJL, VB, FOLD, SCORES, PREF>), grid, dim3(kThreads),
-                                         0, stream, mp);
-                      return launch_check("decode: main launch");
-                    });
-                  });
-                }
+              constexpr int NSET = value_sets(D, VB);
+              return dispatch_bool(scores_dbg != nullptr, [&](auto SC) -> tq_status {
+                constexpr bool SCORES = decltype(SC)::value;
+                dim3 grid((unsigned)((p.n_splits + 3) / 4), (unsigned)units);
+                hipLaunchKernelGGL((decode_main_kernel<D, PK, QJL, VB, NSET, SCORES>), grid, dim3(kThreads), 0, stream,
+                                   mp);
+                return launch_check("decode: main launch");
               });
             }
           });
