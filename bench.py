@@ -126,7 +126,7 @@ def cpu_baseline(syn):
     except Exception:
         cores = os.cpu_count() or 1
     d = 128
-    nq = 262144
+    nq = 1 << 20
     x = syn.kv_vectors(nq, d, syn.CFG_LAYER_QUANT, syn.T_K, 0, 0)
     Pi = syn.rotation(d, syn.CFG_LAYER_QUANT, syn.T_K, 0)
     cb = O.codebook(d, 3)
@@ -134,30 +134,34 @@ def cpu_baseline(syn):
     r = O.quantize_mse(x, Pi, cb)
     O.pack_vector_layout(r["idx"], 3)
     tq_s = time.perf_counter() - t0
-    # decode sample: one (batch, kv head) group, 8 query heads, T tokens
-    T = 131072
-    Pk, Sk = syn.rotation(d, syn.CFG_DECODE_128K, syn.T_K, 0), syn.gaussian_matrix(d, syn.CFG_DECODE_128K, syn.T_K, 0)
-    Pv = syn.rotation(d, syn.CFG_DECODE_128K, syn.T_V, 0)
-    xk = syn.kv_vectors(T, d, syn.CFG_DECODE_128K, syn.T_K, 0, 0)
-    xv = syn.kv_vectors(T, d, syn.CFG_DECODE_128K, syn.T_V, 0, 0)
-    ck, cv = O.codebook(d, 2), O.codebook(d, 3)
-    rk = O.quantize_prod(xk, Pk, Sk, ck)
-    rv = O.quantize_mse(xv, Pv, cv)
-    kc = {"variant": "prod", "bits": 3, "d": d, "max_ctx": T, "Pi": Pk[None], "S": Sk[None],
-          "codes": O.pack_vector_layout(rk["idx"], 2)[None, None], "signs": O.pack_bits(rk["signs"])[None, None],
-          "norms": rk["norms"][None, None], "rnorms": rk["rnorms"][None, None]}
-    vc = {"variant": "mse", "bits": 3, "d": d, "max_ctx": T, "Pi": Pv[None],
-          "codes": O.pack_block_layout(rv["idx"], 3).reshape(1, 1, T // 32, -1), "norms": rv["norms"][None, None]}
-    q = syn.decode_queries(1, 8, d, syn.CFG_DECODE_128K)
-    t0 = time.perf_counter()
-    O.decode_attention(q, kc, vc, np.array([T]), 1 / math.sqrt(d))
-    td_s = time.perf_counter() - t0
+    del x, r
+    # decode sample: two (batch, kv head) groups, 8 query heads each, T tokens
+    T, n_groups = 131072, 2
+    td_s = 0.0
+    for h in range(n_groups):
+        Pk = syn.rotation(d, syn.CFG_DECODE_128K, syn.T_K, h)
+        Sk = syn.gaussian_matrix(d, syn.CFG_DECODE_128K, syn.T_K, h)
+        Pv = syn.rotation(d, syn.CFG_DECODE_128K, syn.T_V, h)
+        xk = syn.kv_vectors(T, d, syn.CFG_DECODE_128K, syn.T_K, 0, h)
+        xv = syn.kv_vectors(T, d, syn.CFG_DECODE_128K, syn.T_V, 0, h)
+        ck, cv = O.codebook(d, 2), O.codebook(d, 3)
+        rk = O.quantize_prod(xk, Pk, Sk, ck)
+        rv = O.quantize_mse(xv, Pv, cv)
+        kc = {"variant": "prod", "bits": 3, "d": d, "max_ctx": T, "Pi": Pk[None], "S": Sk[None],
+              "codes": O.pack_vector_layout(rk["idx"], 2)[None, None], "signs": O.pack_bits(rk["signs"])[None, None],
+              "norms": rk["norms"][None, None], "rnorms": rk["rnorms"][None, None]}
+        vc = {"variant": "mse", "bits": 3, "d": d, "max_ctx": T, "Pi": Pv[None],
+              "codes": O.pack_block_layout(rv["idx"], 3).reshape(1, 1, T // 32, -1), "norms": rv["norms"][None, None]}
+        q = syn.decode_queries(1, 64, d, syn.CFG_DECODE_128K)[:, 8 * h:8 * (h + 1)]
+        t0 = time.perf_counter()
+        O.decode_attention(q, kc, vc, np.array([T]), 1 / math.sqrt(d))
+        td_s += time.perf_counter() - t0
     qbytes = nq * (256 + 48 + 4)
-    dbytes = T * 108
+    dbytes = n_groups * T * 108
     return {"value": round((qbytes + dbytes) / (tq_s + td_s) / 1e9, 4), "unit": "GB/s", "cores": int(cores),
             "kind": "oracle",
             "sample": (f"fp64 oracle: quantize_mse of {nq} bf16 vectors (d=128, b=3; {tq_s:.2f} s) + decode "
-                       f"attention of one (batch, kv head) group, 8 query heads over {T} tokens "
+                       f"attention of {n_groups} (batch, kv head) groups, 8 query heads each over {T} tokens "
                        f"(prod-3 keys, mse-3 values; {td_s:.2f} s); same algorithmic-byte accounting"),
             "quantize_mvec_s": round(nq / tq_s / 1e6, 5), "decode_gb_s": round(dbytes / td_s / 1e9, 5)}
 
@@ -165,7 +169,7 @@ def cpu_baseline(syn):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every box here has one GPU).",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the path is measured on a single GPU.",
               file=sys.stderr)
         return 2
     import torch

@@ -52,7 +52,7 @@ extern "C" {
 typedef enum {
   TQ_OK = 0,
   TQ_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shapes   */
-  TQ_ERR_UNSUPPORTED = 2, /* valid request this build does not implement         */
+  TQ_ERR_UNSUPPORTED = 2, /* valid request this library does not implement       */
   TQ_ERR_NO_MEMORY = 3,   /* host or device allocation failed                    */
   TQ_ERR_DEVICE = 4,      /* a HIP call or kernel launch failed                  */
   TQ_ERR_WORKSPACE = 5    /* workspace pointer null or smaller than required     */

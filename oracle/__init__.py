@@ -14,7 +14,7 @@ eye against the source pages. Citations name the page and its section:
          walkthrough of Zandieh et al. 2025.
   [NAH]  "What exactly TurboQuant showed" (nahornyi.ai news note).
 
-Readings the pages leave open (each also listed in the design doc):
+Readings the pages leave open:
   * The codebook is stored as float32: the fp64 Lloyd-Max centroids rounded to
     nearest. "Nearest centroid" means nearest among those stored values, ties
     to the lower index.

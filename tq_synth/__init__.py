@@ -23,7 +23,7 @@ import numpy as np
 ROOT_SEED = 20260401
 
 # roles
-ROLE_PI, ROLE_S, ROLE_DATA, ROLE_QUERY, ROLE_OUTLIER, ROLE_SCALE, ROLE_CTX = 0, 1, 2, 3, 4, 5, 6
+ROLE_PI, ROLE_S, ROLE_DATA, ROLE_QUERY, ROLE_OUTLIER, ROLE_SCALE, ROLE_CTX, ROLE_PACKED = 0, 1, 2, 3, 4, 5, 6, 7
 # tensors
 T_K, T_V, T_Q = 0, 1, 2
 
@@ -154,4 +154,23 @@ def kv_vectors_device(G: int, n: int, d: int, config: int, tensor: int, device, 
             ch = torch.from_numpy(outlier_channels(d, config, tensor, gi, outliers)).to(device)
             v[:, ch] *= outlier_scale
         out[gi] = v.to(torch.bfloat16)
+    return out
+
+
+def random_packed_group(T: int, d: int, key_code_bytes: int, value_block_bytes: int, config: int,
+                        batch: int, head: int, *, lognormal_sigma: float = 0.0, norm_base: float = 22.9):
+    """Packed cache arrays of one (batch, kv head) made of seeded random bits:
+    key codes [T, key_code_bytes], key sign bytes [T, d/8], value blocks
+    [T/32, value_block_bytes] (uint8, uniform), key and value norms
+    ``norm_base`` times a LogNormal(0, sigma) per token, residual norms uniform in
+    [0.25, 0.45] (float32). Any bits form a valid packed cache; the norm scales
+    follow the synthetic vectors (N(0,1) with 4 channels x10 has |x| ~ 22.9 at d=128)."""
+    g = rng(config, ROLE_PACKED, 0, batch, head)
+    out = {"kcodes": g.integers(0, 256, (T, key_code_bytes), dtype=np.uint8),
+           "ksigns": g.integers(0, 256, (T, d // 8), dtype=np.uint8),
+           "vcodes": g.integers(0, 256, (T // 32, value_block_bytes), dtype=np.uint8)}
+    for k in ("knorms", "vnorms"):
+        s = np.exp(lognormal_sigma * g.standard_normal(T)) if lognormal_sigma > 0 else np.ones(T)
+        out[k] = (norm_base * s * (1.0 + 0.05 * g.standard_normal(T))).astype(np.float32)
+    out["krnorms"] = g.uniform(0.25, 0.45, T).astype(np.float32)
     return out
