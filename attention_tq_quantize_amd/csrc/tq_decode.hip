@@ -66,8 +66,10 @@ __device__ __forceinline__ unsigned f16_part(float v, bool lo) {
   const unsigned hi = f16_bits(v);
   return lo ? f16_bits(v - f16_val(hi)) : hi;
 }
-// fp16 value of an operand bit in slot pair k: exponent bit k set, 2^((1 << k) - 15)
-__host__ __device__ constexpr int slot_exp16(int k) { return (1 << k) - 15; }
+// Value operands: a set bit of the value bit operand in slot k (token 4g + k of
+// a lane's group) is 2^(k - 16) = 2^(vslot_exp(k) - 2); the weight of that token
+// carries 2^(ev - vslot_exp(k)), so every product is w 2^(ev - 2).
+__host__ __device__ constexpr int vslot_exp(int k) { return k - 14; }
 // exponent E such that |w| <= wmax keeps |w| 2^(E + 14) < 2^14 (the largest
 // compensation is 2^14), so every scaled weight and its lo part stay normal fp16
 // down to about 2^-10 of the largest weight
@@ -104,7 +106,8 @@ struct KWords {
 };
 
 // consts per (batch, kv head, chunk): [0,16) mse init, [16,32) qjl init,
-// [32,48) 2^-E_mse, [48,64) 2^-E_qjl, one value per MFMA row.
+// [32,48) 2^(10-E_mse), [48,64) 2^(10-E_qjl) (raw scores are score x 2^(E-10)),
+// one value per MFMA row.
 constexpr int kConstsPerUnit = 64;
 
 // One workgroup of D threads per (batch, query head): thread j computes
@@ -177,10 +180,10 @@ __global__ __launch_bounds__(D) void decode_prep_kernel(DecPrepParams prm) {
   float* cst = prm.consts + (int64_t)bhc * kConstsPerUnit;
   if (j < 2) {
     const int row = 2 * h + j;
-    cst[row] = j == 0 ? -asum * sum_p * prm.scale_log2e * ldexpf(1.0f, em) : 0.f;
-    cst[16 + row] = j == 0 ? (QJL ? -prm.kappa * sum_q * prm.scale_log2e * ldexpf(1.0f, eq) : 0.f) : 0.f;
-    cst[32 + row] = ldexpf(1.0f, -em);
-    cst[48 + row] = ldexpf(1.0f, -eq);
+    cst[row] = j == 0 ? -asum * sum_p * prm.scale_log2e * ldexpf(1.0f, em - 10) : 0.f;
+    cst[16 + row] = j == 0 ? (QJL ? -prm.kappa * sum_q * prm.scale_log2e * ldexpf(1.0f, eq - 10) : 0.f) : 0.f;
+    cst[32 + row] = ldexpf(1.0f, 10 - em);
+    cst[48 + row] = ldexpf(1.0f, 10 - eq);
   }
   if (h == 0 && prm.chunk_heads < 8 && j >= 2 * prm.chunk_heads && j < 16) {
     cst[j] = 0.f;
@@ -220,7 +223,8 @@ __global__ __launch_bounds__(D) void decode_prep_kernel(DecPrepParams prm) {
         }
         E = eq;
       }
-      val *= prm.scale_log2e * ldexpf(1.0f, E - slot_exp16(k));
+      // the lane's bit reads as 2^(operand_pos(k) - 24); raw scores come out x 2^(E - 10)
+      val *= prm.scale_log2e * ldexpf(1.0f, E + 14 - operand_pos(k));
       hv[it] = f16_part(val, lo);
     }
     prm.frag[((int64_t)bhc * KW::NF + f) * 64 + lane] =
@@ -263,6 +267,21 @@ __device__ __forceinline__ float swap_pair(float x) {
 // two floats to fp16 (round toward zero) packed into one dword, a in the low half
 __device__ __forceinline__ unsigned pack_rtz(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// fp16 hi (nsel = -0) or lo (nsel = -1) parts of x0 and x1 packed in one dword:
+// h = RNE_f16(x); the result is RNE_f16(x + nsel * h). x - h is exact in fp32,
+// so hi + lo carries 22 significant bits. The inputs are ordinary VALU results.
+__device__ __forceinline__ unsigned split_pair(float x0, float x1, float nsel) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector((f2){x0, x1}, h2));
+  unsigned r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %1, %2, %4 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(r)
+      : "v"(h), "v"(nsel), "v"(x0), "v"(x1));
+  return r;
 }
 
 // max of three floats as one v_max3_f32 (fmaxf chains pick up NaN
@@ -348,12 +367,13 @@ constexpr int kEvUnset = 40;
 // hi and lo lanes of a head (r, r ^ 1) add their parts with one DPP exchange.
 //
 // Values: A[row][token] holds the hi (even rows) or lo (odd rows) fp16 part of
-// the weight w = p * |v| times 2^(ev - e_k), where e_k is the value of a set
-// bit in slot k = i of the value bit operand (the K order of the value cache
-// block layout puts token 16t + 4g + k in slot k). The factor is folded into
-// the exp2 argument, so the weights need no extra multiply. The value subsets
-// accumulate in NSET sets (see value_sets); each set's lead coefficient and
-// the 0/1-to-sign correction are applied once, after the loop.
+// the weight w = p * |v| times 2^(ev - e_k), e_k = vslot_exp(k), for the token
+// in slot k = i of the value bit operand (the K order of the value cache block
+// layout puts token 16t + 4g + k in slot k; its bit reads as 2^(k - 16), and
+// the leftover 2^-2 is removed after the loop). The factor is
+// folded into the exp2 argument, so the weights need no extra multiply. The
+// value subsets accumulate in NSET sets (see value_sets); each set's lead
+// coefficient and the 0/1-to-sign correction are applied once, after the loop.
 template <int D, int PK, bool QJL, int VB, int NSET, bool SCORES>
 __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams prm) {
   using KW = KWords<D, PK, QJL>;
@@ -410,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   const unsigned s_off = (unsigned)(r16 * SREC + g * (D / 32));
   const unsigned v_off = (unsigned)((g * (D / 4) + VWL * r16) * 4);
   const bool lo_row = r16 & 1;
-  const unsigned lo_mask = lo_row ? 0xFFFFE000u : 0u;  // w - (w & mask): the lo part on odd rows
+  const float nsel = lo_row ? -1.0f : -0.0f;  // x + nsel * hi(x): the lo part on odd rows
 
   float m_run = -INFINITY;  // running max of this row's scores (log2 units)
   float m_thr = -INFINITY;  // (m_run + slack) 2^E: raise the max above this raw score
@@ -428,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
 #pragma unroll
     for (int q = 0; q < NT; ++q) acc[a][q] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 wacc = {0.f, 0.f, 0.f, 0.f};  // sum of w 2^ev per row (every column)
-  const u32x4 ones = {slot_mask(0), slot_mask(1), slot_mask(2), slot_mask(3)};
+  const u32x4 ones = {pos_mask(8), pos_mask(9), pos_mask(10), pos_mask(11)};  // slot k: 2^(k - 16)
 
   // Raw cache data of one 32-token chunk for this lane: its key and value bit
   // words, and one norm (lanes 0..31: |k| of token lane, 32..63: |r|; nb: |v|)
@@ -607,7 +627,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
       // largest unscaled weight of this lane: wv 2^(e_k - ev)
       float u = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u = fmaxf(u, fmaxf(wv[0][i], wv[1][i]) * ldexpf(1.0f, slot_exp16(i) - ev));
+      for (int i = 0; i < 4; ++i) u = fmaxf(u, fmaxf(wv[0][i], wv[1][i]) * ldexpf(1.0f, vslot_exp(i) - ev));
       pend_val = u;
       return 2;
     }
@@ -631,13 +651,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
     auto a_operand = [&](float rho, bool scaled) -> u32x4 {
       unsigned d4[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x0 = scaled ? wv[0][k] * rho : wv[0][k];
-        const float x1 = scaled ? wv[1][k] * rho : wv[1][k];
-        const float y0 = x0 - __uint_as_float(__float_as_uint(x0) & lo_mask);
-        const float y1 = x1 - __uint_as_float(__float_as_uint(x1) & lo_mask);
-        d4[k] = pack_rtz(y0, y1);
-      }
+      for (int k = 0; k < 4; ++k)
+        d4[k] = split_pair(scaled ? wv[0][k] * rho : wv[0][k], scaled ? wv[1][k] * rho : wv[1][k], nsel);
       return u32x4{d4[0], d4[1], d4[2], d4[3]};
     };
     const u32x4 a_lead = a_operand(1.0f, false);
@@ -689,7 +704,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
       m_thr = (m_run + kRescaleSlack) / isc;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        mk[k] = m_run - (float)(ev - slot_exp16(k));
+        mk[k] = m_run - (float)(ev - vslot_exp(k));
         lsum[k] *= f;
       }
       float fr[4];
@@ -739,7 +754,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   // softmax denominator of this row: sum_k lsum[k] 2^(e_k - ev), over the 4 lane groups
   float l_acc = 0.f;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) l_acc += lsum[k] * ldexpf(1.0f, slot_exp16(k) - ev);
+  for (int k = 0; k < 4; ++k) l_acc += lsum[k] * ldexpf(1.0f, vslot_exp(k) - ev);
   l_acc += __shfl_xor(l_acc, 16);
   l_acc += __shfl_xor(l_acc, 32);
   const int64_t hq_base = (int64_t)b * prm.Hq + hq0;
@@ -758,7 +773,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
     const int h = 2 * g + hh;
     if (h >= prm.chunk_heads) continue;
     const float unscale = ldexpf(1.0f, -(hh ? ev_h1 : ev_h0));
-    const float wh = wt[hh];
+    const float wh = wt[hh] * 4.0f;  // the ones operand reads 2^(k - 16) against 2^(14 - k)
     float outv[NT];
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
@@ -766,7 +781,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
       float v = -wh * prm.vcoef_sum;
 #pragma unroll
       for (int j = 0; j < NSET; ++j) {
-        const float c2 = hh ? (acc[j][q].z + acc[j][q].w) : (acc[j][q].x + acc[j][q].y);
+        const float c2 = (hh ? (acc[j][q].z + acc[j][q].w) : (acc[j][q].x + acc[j][q].y)) * 4.0f;
         v = fmaf(2.f * prm.vlead[j], c2, v);
       }
       outv[q] = v * unscale;

@@ -43,21 +43,19 @@ __device__ __forceinline__ unsigned pack2(unsigned lo_half, unsigned hi_half) {
   return (lo_half & 0xFFFFu) | (hi_half << 16);
 }
 
-// Operand bits: slot pair k of a word lands on bit 10+k of each 16-bit half (the
-// low exponent bits of an fp16), so a set bit reads as 2^((1 << k) - 15).
-__device__ __forceinline__ unsigned slot_mask(int k) { return (0x0400u << k) | (0x04000000u << k); }
-// word w rotated so that bits 4r+k and 16+4r+k sit on bits 10+k and 26+k
-__device__ __forceinline__ unsigned rot_for(unsigned w, int r) {
-  return __builtin_amdgcn_alignbit(w, w, (unsigned)((4 * r - 10) & 31));
-}
+// Operand bits. Bit 4r+k of a word (and bit 16+4r+k) becomes an fp16 element of
+// an MFMA operand: the word is shifted so that nibble r sits on bits 8-11 of each
+// half (nibble 2 already does), and masked. An fp16 half whose only set bit is
+// bit 8+k has the value 2^(k - 16) (bits 8 and 9 are subnormals, 10 and 11 the
+// two lowest exponent values), so the element is the bit times 2^(k - 16). The
+// matrix cores keep full product precision for these positions; bits further
+// down (deeper subnormals) lose low product bits in the sum. The other operand
+// carries the compensating powers of two.
+__host__ __device__ constexpr int operand_pos(int k) { return 8 + k; }
+__device__ __forceinline__ unsigned pos_mask(int p) { return (1u << p) | (1u << (16 + p)); }
 __device__ __forceinline__ u32x4 bit_operand(unsigned w, int r) {
-  const unsigned x = rot_for(w, r);
-  u32x4 o;
-  o.x = x & slot_mask(0);
-  o.y = x & slot_mask(1);
-  o.z = x & slot_mask(2);
-  o.w = x & slot_mask(3);
-  return o;
+  const unsigned x = r == 0 ? (w << 8) : r == 1 ? (w << 4) : r == 2 ? w : (w >> 4);
+  return u32x4{x & pos_mask(8), x & pos_mask(9), x & pos_mask(10), x & pos_mask(11)};
 }
 
 // odd-size subsets of P bit planes, in increasing mask order (matches the host's Walsh list)
