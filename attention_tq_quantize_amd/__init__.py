@@ -24,7 +24,7 @@ TQ_LAYOUT_VECTOR, TQ_LAYOUT_BLOCK32 = 0, 1
 
 EXPORTS = [
     "tq_status_string", "tq_last_error_message", "tq_version", "tq_codebook_build",
-    "tq_quantizer_create", "tq_quantizer_destroy", "tq_quantizer_info", "tq_quantize",
+    "tq_quantizer_create", "tq_quantizer_create_wht", "tq_quantizer_destroy", "tq_quantizer_info", "tq_quantize",
     "tq_quantize_mse", "tq_quantize_prod", "tq_dequantize", "tq_inner_products",
     "tq_decode_workspace_size", "tq_decode_attention",
 ]
@@ -67,6 +67,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tq_version.restype = _I
     lib.tq_codebook_build.argtypes = [_I, _I, _VP, _VP, _VP]
     lib.tq_quantizer_create.argtypes = [_I, _I, _I, _VP, _VP, ctypes.POINTER(_VP)]
+    lib.tq_quantizer_create_wht.argtypes = [_I, _I, _I, _VP, _VP, ctypes.POINTER(_VP)]
     lib.tq_quantizer_destroy.argtypes = [_VP]
     lib.tq_quantizer_info.argtypes = [_VP, _VP, _VP, _VP, _VP]
     lib.tq_quantize.argtypes = [_VP, _I, _I64, _VP, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
@@ -130,6 +131,22 @@ class Quantizer:
                "tq_quantizer_create")
         self.handle = h
         self.planes = bits - 1 if variant == "prod" else bits
+
+    @classmethod
+    def wht(cls, d: int, bits: int, variant: str, signs: np.ndarray, s: Optional[np.ndarray] = None) -> "Quantizer":
+        """Quantizer with the randomized Walsh-Hadamard rotation H diag(signs) / sqrt(d)."""
+        lib = load()
+        self = cls.__new__(cls)
+        self.d, self.bits, self.variant = int(d), int(bits), variant
+        v = TQ_PROD if variant == "prod" else TQ_MSE
+        sg = np.ascontiguousarray(signs, dtype=np.float64)
+        s64 = None if s is None else np.ascontiguousarray(s, dtype=np.float64)
+        h = ctypes.c_void_p()
+        _check(lib.tq_quantizer_create_wht(d, bits, v, sg.ctypes.data, None if s64 is None else s64.ctypes.data,
+                                           ctypes.byref(h)), "tq_quantizer_create_wht")
+        self.handle = h
+        self.planes = bits - 1 if variant == "prod" else bits
+        return self
 
     def close(self):
         if getattr(self, "handle", None) is not None and self.handle.value:

@@ -214,6 +214,32 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
   return TQ_OK;
 }
 
+tq_status tq_quantizer_create_wht(int d, int bits, tq_variant variant, const double* signs,
+                                  const double* s, tq_quantizer** out) {
+  if (!out) return set_error(TQ_ERR_INVALID_ARG, "create_wht: out is NULL");
+  *out = nullptr;
+  if (!signs) return set_error(TQ_ERR_INVALID_ARG, "create_wht: signs is NULL");
+  if (!gpu_dim(d)) return set_error(TQ_ERR_UNSUPPORTED, fmt("create_wht: d=%d (supported: 64, 128, 256)", d));
+  for (int j = 0; j < d; ++j)
+    if (signs[j] != 1.0 && signs[j] != -1.0)
+      return set_error(TQ_ERR_INVALID_ARG, fmt("create_wht: signs[%d] is not +-1", j));
+  // Sylvester doubling: H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]
+  std::vector<double> h((size_t)d * d, 0.0);
+  h[0] = 1.0;
+  for (int n = 1; n < d; n *= 2)
+    for (int i = 0; i < n; ++i)
+      for (int j = 0; j < n; ++j) {
+        const double v = h[(size_t)i * d + j];
+        h[(size_t)i * d + j + n] = v;
+        h[(size_t)(i + n) * d + j] = v;
+        h[(size_t)(i + n) * d + j + n] = -v;
+      }
+  const double inv = 1.0 / std::sqrt((double)d);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) h[(size_t)i * d + j] *= signs[j] * inv;
+  return tq_quantizer_create(d, bits, variant, h.data(), s, out);
+}
+
 tq_status tq_quantizer_destroy(tq_quantizer* q) {
   if (!q) return set_error(TQ_ERR_INVALID_ARG, "destroy: handle is NULL");
   tq_status st = TQ_OK;

@@ -108,6 +108,21 @@ tq_status tq_codebook_build(int d, int bits, float* centroids, float* thresholds
  */
 tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double* pi,
                               const double* s, tq_quantizer** out);
+/*
+ * Same as tq_quantizer_create with a randomized Walsh-Hadamard rotation,
+ * Pi = H diag(signs) / sqrt(d), H the Sylvester-Hadamard matrix of order d
+ * (H[i][j] = (-1)^popcount(i & j)): the structured rotation the page's
+ * community section ([NIK] "What the community did", item 3) reports as the
+ * best MSE-stage transform, with the QJL matrix s drawn independently.
+ *   signs : host, float64 [d], every entry exactly +1 or -1 (the random
+ *           diagonal); copied.
+ *   s     : as for tq_quantizer_create (required iff variant == TQ_PROD).
+ * Errors: TQ_ERR_INVALID_ARG for a NULL pointer or a sign that is not +-1;
+ * the other checks and the device tables are those of tq_quantizer_create
+ * (the rotation is applied as a dense matrix by the same kernels).
+ */
+tq_status tq_quantizer_create_wht(int d, int bits, tq_variant variant, const double* signs,
+                                  const double* s, tq_quantizer** out);
 /* Frees the handle. The caller must first synchronize work that uses it. */
 tq_status tq_quantizer_destroy(tq_quantizer* q);
 /* Shape queries (any pointer may be NULL). code_planes = b for mse, b-1 for

@@ -17,7 +17,7 @@ __all__ = [
     "nearest_index", "quantize_mse", "quantize_prod", "dequantize_mse", "dequantize_prod",
     "qjl", "qjl_inverse", "pack_vector_layout", "unpack_vector_layout", "pack_bits",
     "unpack_bits", "pack_block_layout", "unpack_block_layout", "attention",
-    "decode_attention", "inner_products", "QJL_SCALE",
+    "decode_attention", "inner_products", "QJL_SCALE", "hadamard", "wht_rotation",
 ]
 
 
@@ -136,6 +136,33 @@ def nearest_index(y, centroids) -> np.ndarray:
                 exact = [abs(yi - Fraction(float(ci))) for ci in c]
                 flat_o[s + i] = min(range(c.size), key=lambda k: (exact[k], k))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Randomized Walsh-Hadamard rotation: [NIK] "What the community did", item 3
+# (a Walsh-Hadamard transform for the MSE stage, with a random transform for
+# QJL drawn independently). Pi = H D / sqrt(d), H the Sylvester-Hadamard
+# matrix of order d (a power of two), D a random +-1 diagonal.
+# ---------------------------------------------------------------------------
+
+def hadamard(d: int) -> np.ndarray:
+    """Sylvester-Hadamard matrix, closed form H[i, j] = (-1)^popcount(i & j)."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    i = np.arange(d)
+    parity = np.zeros((d, d), dtype=np.int64)
+    m = i[:, None] & i[None, :]
+    while np.any(m):
+        parity ^= m & 1
+        m = m >> 1
+    return np.where(parity == 1, -1.0, 1.0)
+
+
+def wht_rotation(signs) -> np.ndarray:
+    """Pi = H diag(signs) / sqrt(d): orthogonal, y = Pi u."""
+    signs = np.asarray(signs, dtype=np.float64)
+    d = signs.size
+    return hadamard(d) * signs[None, :] / math.sqrt(d)
 
 
 # ---------------------------------------------------------------------------

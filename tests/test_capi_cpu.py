@@ -116,3 +116,17 @@ def test_argument_errors(lib):
     assert lib.tq_decode_attention(None, None, None, None, None, ctypes.c_float(1.0), None, None, None, 0,
                                    None) == tq.TQ_ERR_INVALID_ARG
     assert lib.tq_status_string(tq.TQ_ERR_WORKSPACE) == b"workspace too small"
+
+
+def test_wht_argument_errors(lib):
+    h = ctypes.c_void_p()
+    ok = np.ones(128)
+    assert lib.tq_quantizer_create_wht(128, 3, tq.TQ_MSE, None, None, ctypes.byref(h)) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_quantizer_create_wht(128, 3, tq.TQ_MSE, ok.ctypes.data, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_quantizer_create_wht(96, 3, tq.TQ_MSE, ok.ctypes.data, None, ctypes.byref(h)) == tq.TQ_ERR_UNSUPPORTED
+    bad = np.ones(128)
+    bad[5] = 0.5
+    assert lib.tq_quantizer_create_wht(128, 3, tq.TQ_MSE, bad.ctypes.data, None, ctypes.byref(h)) == tq.TQ_ERR_INVALID_ARG
+    assert b"signs[5]" in lib.tq_last_error_message()
+    # the rotation it builds is checked by the dense constructor: prod without s is refused there
+    assert lib.tq_quantizer_create_wht(128, 3, tq.TQ_PROD, ok.ctypes.data, None, ctypes.byref(h)) == tq.TQ_ERR_INVALID_ARG

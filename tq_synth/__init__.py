@@ -23,7 +23,8 @@ import numpy as np
 ROOT_SEED = 20260401
 
 # roles
-ROLE_PI, ROLE_S, ROLE_DATA, ROLE_QUERY, ROLE_OUTLIER, ROLE_SCALE, ROLE_CTX, ROLE_PACKED = 0, 1, 2, 3, 4, 5, 6, 7
+ROLE_PI, ROLE_S, ROLE_DATA, ROLE_QUERY, ROLE_OUTLIER, ROLE_SCALE, ROLE_CTX, ROLE_PACKED, ROLE_WHT = (
+    0, 1, 2, 3, 4, 5, 6, 7, 8)
 # tensors
 T_K, T_V, T_Q = 0, 1, 2
 
@@ -62,6 +63,12 @@ def rotation(d: int, config: int, tensor: int = 0, head: int = 0) -> np.ndarray:
     s = np.sign(np.diag(r))
     s[s == 0] = 1.0
     return np.ascontiguousarray(q * s[None, :])
+
+
+def wht_signs(d: int, config: int, tensor: int = 0, head: int = 0) -> np.ndarray:
+    """Random +-1 diagonal of a randomized Walsh-Hadamard rotation (float64 [d]),
+    from its own seed stream (independent of Pi and S)."""
+    return rng(config, ROLE_WHT, tensor, 0, head).integers(0, 2, d).astype(np.float64) * 2.0 - 1.0
 
 
 def gaussian_matrix(d: int, config: int, tensor: int = 0, head: int = 0) -> np.ndarray:
