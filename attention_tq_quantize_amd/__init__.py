@@ -26,7 +26,8 @@ EXPORTS = [
     "tq_status_string", "tq_last_error_message", "tq_version", "tq_codebook_build",
     "tq_quantizer_create", "tq_quantizer_create_wht", "tq_quantizer_destroy", "tq_quantizer_info", "tq_quantize",
     "tq_quantize_mse", "tq_quantize_prod", "tq_dequantize", "tq_inner_products",
-    "tq_decode_workspace_size", "tq_decode_attention",
+    "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_append_workspace_size",
+    "tq_decode_append_attention",
 ]
 
 
@@ -79,6 +80,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                              ctypes.POINTER(PackedKV), ctypes.POINTER(ctypes.c_size_t)]
     lib.tq_decode_attention.argtypes = [ctypes.POINTER(AttnShape), _VP, ctypes.POINTER(PackedKV),
                                         ctypes.POINTER(PackedKV), _VP, _F, _VP, _VP, _VP, ctypes.c_size_t, _VP]
+    lib.tq_decode_append_workspace_size.argtypes = [ctypes.POINTER(AttnShape), ctypes.POINTER(PackedKV),
+                                                    ctypes.POINTER(PackedKV), ctypes.POINTER(ctypes.c_size_t)]
+    lib.tq_decode_append_attention.argtypes = [ctypes.POINTER(AttnShape), _VP, _VP, _VP, _I,
+                                               ctypes.POINTER(PackedKV), ctypes.POINTER(PackedKV), _VP, _F, _VP,
+                                               _VP, ctypes.c_size_t, _VP]
     for name in EXPORTS:
         if name not in ("tq_status_string", "tq_last_error_message", "tq_version"):
             getattr(lib, name).restype = _I
@@ -309,4 +315,47 @@ def decode_attention(q, kcache: KVCache, vcache: KVCache, ctx_lens, scale: Optio
     _check(lib.tq_decode_attention(ctypes.byref(shape), _ptr(q.contiguous()), ctypes.byref(kp), ctypes.byref(vp),
                                    _ptr(ctx_lens), float(scale), _ptr(out), _ptr(scores), _ptr(workspace),
                                    workspace.numel(), _stream(stream)), "tq_decode_attention")
+    return out
+
+
+def decode_append_workspace_size(batch, n_q_heads, n_kv_heads, d, max_ctx, kcache: KVCache,
+                                 vcache: KVCache) -> int:
+    lib = load()
+    shape = AttnShape(batch, n_q_heads, n_kv_heads, d, max_ctx)
+    kp, ka = kcache.packed()
+    vp, va = vcache.packed()
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.tq_decode_append_workspace_size(ctypes.byref(shape), ctypes.byref(kp), ctypes.byref(vp),
+                                               ctypes.byref(nbytes)), "tq_decode_append_workspace_size")
+    return nbytes.value
+
+
+def decode_append_attention(q, k_new, v_new, kcache: KVCache, vcache: KVCache, ctx_lens,
+                            scale: Optional[float] = None, max_ctx: Optional[int] = None, out=None,
+                            workspace=None, stream=None):
+    """Quantize k_new / v_new ([B, Hkv, d], float32 or bfloat16) into the caches at
+    token ctx_lens[b], then attend ctx_lens[b] + 1 tokens. ctx_lens is not advanced."""
+    import torch
+    lib = load()
+    B, Hq, d = q.shape
+    Hkv = len(kcache.qz)
+    T = int(max_ctx if max_ctx is not None else kcache.norms.shape[-1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    assert tuple(k_new.shape) == (B, Hkv, d) and tuple(v_new.shape) == (B, Hkv, d)
+    if k_new.dtype != v_new.dtype or k_new.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("k_new and v_new must share a float32 or bfloat16 dtype")
+    dt = TQ_BF16 if k_new.dtype == torch.bfloat16 else TQ_F32
+    shape = AttnShape(B, Hq, Hkv, d, T)
+    kp, ka = kcache.packed()
+    vp, va = vcache.packed()
+    if workspace is None:
+        nbytes = decode_append_workspace_size(B, Hq, Hkv, d, T, kcache, vcache)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check(lib.tq_decode_append_attention(ctypes.byref(shape), _ptr(q.contiguous()), _ptr(k_new.contiguous()),
+                                          _ptr(v_new.contiguous()), dt, ctypes.byref(kp), ctypes.byref(vp),
+                                          _ptr(ctx_lens), float(scale), _ptr(out), _ptr(workspace),
+                                          workspace.numel(), _stream(stream)), "tq_decode_append_attention")
     return out

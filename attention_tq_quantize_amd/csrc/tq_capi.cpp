@@ -392,4 +392,93 @@ tq_status tq_decode_attention(const tq_attn_shape* shape, const void* q, const t
   return launch_decode(p, q, k, v, ctx_lens, scale, out, scores_dbg, workspace, (hipStream_t)stream);
 }
 
+// Append workspace: [decode workspace][attended lengths][staged key and value records]
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+struct AppendLayout {
+  size_t lens, k_codes, k_signs, k_norms, k_rnorms, v_codes, v_norms, total;
+};
+static AppendLayout append_layout(const DecodePlan& p) {
+  const size_t G = (size_t)p.batch * p.n_kv_heads, d = (size_t)p.d;
+  AppendLayout L;
+  size_t o = align256(p.total_bytes);
+  L.lens = o;     o = align256(o + sizeof(int32_t) * p.batch);
+  L.k_codes = o;  o = align256(o + G * (size_t)(p.k_planes > 0 ? p.k_planes : 1) * d / 8);
+  L.k_signs = o;  o = align256(o + G * d / 8);
+  L.k_norms = o;  o = align256(o + G * 4);
+  L.k_rnorms = o; o = align256(o + G * 4);
+  L.v_codes = o;  o = align256(o + G * (size_t)p.v_bits * d / 8);
+  L.v_norms = o;  o = align256(o + G * 4);
+  L.total = o;
+  return L;
+}
+
+tq_status tq_decode_append_workspace_size(const tq_attn_shape* shape, const tq_packed_kv* k,
+                                          const tq_packed_kv* v, size_t* bytes) {
+  if (!bytes) return set_error(TQ_ERR_INVALID_ARG, "decode_append_workspace_size: bytes is NULL");
+  DecodePlan p;
+  tq_status st = check_decode(shape, k, v, &p);
+  if (st != TQ_OK) return st;
+  *bytes = append_layout(p).total;
+  return TQ_OK;
+}
+
+tq_status tq_decode_append_attention(const tq_attn_shape* shape, const void* q, const void* k_new,
+                                     const void* v_new, tq_dtype kv_dtype, const tq_packed_kv* k,
+                                     const tq_packed_kv* v, const int32_t* ctx_lens, float scale,
+                                     float* out, void* workspace, size_t ws_bytes, void* stream) {
+  DecodePlan p;
+  tq_status st = check_decode(shape, k, v, &p);
+  if (st != TQ_OK) return st;
+  if (!q || !ctx_lens || !out) return set_error(TQ_ERR_INVALID_ARG, "decode_append: q, ctx_lens or out is NULL");
+  if (!k_new || !v_new) return set_error(TQ_ERR_INVALID_ARG, "decode_append: k_new or v_new is NULL");
+  if (kv_dtype != TQ_F32 && kv_dtype != TQ_BF16) return set_error(TQ_ERR_INVALID_ARG, "decode_append: unknown kv_dtype");
+  if (!std::isfinite(scale)) return set_error(TQ_ERR_INVALID_ARG, "decode_append: scale is not finite");
+  const AppendLayout L = append_layout(p);
+  if (!workspace || ws_bytes < L.total)
+    return set_error(TQ_ERR_WORKSPACE, fmt("decode_append: workspace needs %zu bytes, got %zu", L.total, workspace ? ws_bytes : (size_t)0));
+  hipStream_t hs = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int G = p.batch * p.n_kv_heads;
+  std::vector<const tq_quantizer*> kq(G), vq(G);
+  for (int g = 0; g < G; ++g) {
+    kq[g] = k->qz[g % p.n_kv_heads];
+    vq[g] = v->qz[g % p.n_kv_heads];
+  }
+  const bool kprod = kq[0]->variant == TQ_PROD;
+  QuantizeLaunch qk{kq.data(), G, 1, k_new, kv_dtype, TQ_LAYOUT_VECTOR,
+                    p.k_planes > 0 ? (uint8_t*)(ws + L.k_codes) : nullptr, kprod ? (uint8_t*)(ws + L.k_signs) : nullptr,
+                    (float*)(ws + L.k_norms), kprod ? (float*)(ws + L.k_rnorms) : nullptr, nullptr, nullptr};
+  st = launch_quantize(qk, hs);
+  if (st != TQ_OK) return st;
+  QuantizeLaunch qv{vq.data(), G, 1, v_new, kv_dtype, TQ_LAYOUT_VECTOR, (uint8_t*)(ws + L.v_codes), nullptr,
+                    (float*)(ws + L.v_norms), nullptr, nullptr, nullptr};
+  st = launch_quantize(qv, hs);
+  if (st != TQ_OK) return st;
+  AppendScatter a;
+  a.ctx_lens = ctx_lens;
+  a.lens_out = (int32_t*)(ws + L.lens);
+  a.batch = p.batch;
+  a.n_kv_heads = p.n_kv_heads;
+  a.d = p.d;
+  a.k_planes = p.k_planes;
+  a.v_bits = p.v_bits;
+  a.max_ctx = p.max_ctx;
+  a.k_prod = kprod;
+  a.sk_codes = (const uint8_t*)(ws + L.k_codes);
+  a.sk_signs = (const uint8_t*)(ws + L.k_signs);
+  a.sk_norms = (const float*)(ws + L.k_norms);
+  a.sk_rnorms = (const float*)(ws + L.k_rnorms);
+  a.sv_codes = (const uint8_t*)(ws + L.v_codes);
+  a.sv_norms = (const float*)(ws + L.v_norms);
+  a.k_codes = const_cast<uint8_t*>(k->codes);
+  a.k_signs = const_cast<uint8_t*>(k->signs);
+  a.k_norms = const_cast<float*>(k->norms);
+  a.k_rnorms = const_cast<float*>(k->rnorms);
+  a.v_codes = const_cast<uint8_t*>(v->codes);
+  a.v_norms = const_cast<float*>(v->norms);
+  st = launch_append_scatter(a, hs);
+  if (st != TQ_OK) return st;
+  return launch_decode(p, q, k, v, (const int32_t*)(ws + L.lens), scale, out, nullptr, workspace, hs);
+}
+
 }  // extern "C"

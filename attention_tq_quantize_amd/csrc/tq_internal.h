@@ -97,4 +97,28 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
                         const tq_packed_kv* v, const int32_t* ctx_lens, float scale, float* out,
                         float* scores_dbg, void* workspace, hipStream_t stream);
 
+// Decode-step append (tq_append.hip): staged vector-layout records of the new
+// token per (batch, kv head) into the caches at ctx_lens[b]; lens_out[b] gets
+// the attended length.
+struct AppendScatter {
+  const int32_t* ctx_lens;
+  int32_t* lens_out;
+  int batch, n_kv_heads, d, k_planes, v_bits;
+  int64_t max_ctx;
+  bool k_prod;
+  const uint8_t* sk_codes;
+  const uint8_t* sk_signs;
+  const float* sk_norms;
+  const float* sk_rnorms;
+  const uint8_t* sv_codes;
+  const float* sv_norms;
+  uint8_t* k_codes;
+  uint8_t* k_signs;
+  float* k_norms;
+  float* k_rnorms;
+  uint8_t* v_codes;
+  float* v_norms;
+};
+tq_status launch_append_scatter(const AppendScatter& a, hipStream_t stream);
+
 }  // namespace tq

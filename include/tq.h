@@ -246,6 +246,36 @@ tq_status tq_decode_attention(const tq_attn_shape* shape, const void* q, const t
                               float* out, float* scores_dbg, void* workspace, size_t ws_bytes,
                               void* stream);
 
+/*
+ * Decode step with append: the online use of the quantizer ([NIK] "Step 0" to
+ * "Step 2": vector in, code out, nothing to train; for prod keys also "TurboQuant
+ * proper") followed by the attention step that reads the cache ([NAH]: the prod
+ * variant needs its own attention kernel). For every (b, h) the new key k_new[b][h]
+ * is quantized with k->qz[h] and the new value v_new[b][h] with v->qz[h]; both are
+ * written into the packed caches at token ctx_lens[b] (keys: vector layout record;
+ * values: slot ctx_lens[b] % 32 of its BLOCK32 block, the other 31 slots kept),
+ * and the query then attends ctx_lens[b] + 1 tokens, as tq_decode_attention.
+ *   q             : device bf16 [B][Hq][d].
+ *   k_new, v_new  : device [B][Hkv][d], float32 or bfloat16 (kv_dtype).
+ *   k, v          : the caches as for tq_decode_attention; their code, sign and
+ *                   norm buffers are WRITTEN at token ctx_lens[b] (device memory
+ *                   owned by the caller; the const in tq_packed_kv is cast away).
+ *   ctx_lens      : device int32 [B], tokens already cached; read, not advanced
+ *                   (the caller adds 1 after the call). A sequence with
+ *                   ctx_lens[b] >= max_ctx is not appended and attends max_ctx
+ *                   tokens.
+ *   workspace     : device, at least tq_decode_append_workspace_size() bytes.
+ * Same validation and errors as tq_decode_attention, plus TQ_ERR_INVALID_ARG
+ * for NULL k_new / v_new or an unknown kv_dtype. Four launches on `stream`
+ * (key quantize, value quantize, scatter, attention); no host synchronization.
+ */
+tq_status tq_decode_append_workspace_size(const tq_attn_shape* shape, const tq_packed_kv* k,
+                                          const tq_packed_kv* v, size_t* bytes);
+tq_status tq_decode_append_attention(const tq_attn_shape* shape, const void* q, const void* k_new,
+                                     const void* v_new, tq_dtype kv_dtype, const tq_packed_kv* k,
+                                     const tq_packed_kv* v, const int32_t* ctx_lens, float scale,
+                                     float* out, void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -130,3 +130,13 @@ def test_wht_argument_errors(lib):
     assert b"signs[5]" in lib.tq_last_error_message()
     # the rotation it builds is checked by the dense constructor: prod without s is refused there
     assert lib.tq_quantizer_create_wht(128, 3, tq.TQ_PROD, ok.ctypes.data, None, ctypes.byref(h)) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_append_argument_errors(lib):
+    assert lib.tq_decode_append_attention(None, None, None, None, 1, None, None, None, ctypes.c_float(1.0), None,
+                                          None, 0, None) == tq.TQ_ERR_INVALID_ARG
+    nb = ctypes.c_size_t(0)
+    shape = tq.AttnShape(1, 8, 1, 128, 100)
+    kv = tq.PackedKV(None, None, None, None, None)
+    assert lib.tq_decode_append_workspace_size(ctypes.byref(shape), ctypes.byref(kv), ctypes.byref(kv),
+                                               ctypes.byref(nb)) == tq.TQ_ERR_INVALID_ARG
