@@ -163,17 +163,18 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
   const size_t dd = (size_t)d * d;
   const size_t frag_bytes = 2 * dd * sizeof(uint16_t);  // hi + lo
   const bool prod = variant == TQ_PROD;
-  const size_t total = frag_bytes * (prod ? 2 : 1) + dd * sizeof(float) * (prod ? 2 : 1);
+  const size_t total = frag_bytes * (prod ? 2 : 1) + dd * sizeof(float) * (prod ? 3 : 1);
   std::vector<unsigned char> host(total);
   size_t off = 0;
   build_fragments(d, pi, (uint16_t*)(host.data() + off));
   const size_t off_pi_frag = off;
   off += frag_bytes;
   size_t off_sp_frag = 0;
+  std::vector<double> sp;
   if (prod) {
     // S' = S Pi^T, folded in fp64, so that S r = S' (Pi u - y~): the residual never
     // leaves the rotated space.
-    std::vector<double> sp(dd, 0.0);
+    sp.assign(dd, 0.0);
     for (int i = 0; i < d; ++i)
       for (int j = 0; j < d; ++j) {
         double acc = 0.0;
@@ -187,10 +188,13 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
   const size_t off_pi32 = off;
   for (size_t i = 0; i < dd; ++i) ((float*)(host.data() + off))[i] = (float)pi[i];
   off += dd * sizeof(float);
-  size_t off_s32 = 0;
+  size_t off_s32 = 0, off_sp32 = 0;
   if (prod) {
     off_s32 = off;
     for (size_t i = 0; i < dd; ++i) ((float*)(host.data() + off))[i] = (float)s[i];
+    off += dd * sizeof(float);
+    off_sp32 = off;
+    for (size_t i = 0; i < dd; ++i) ((float*)(host.data() + off))[i] = (float)sp[i];
     off += dd * sizeof(float);
   }
   hs = check_hip(hipMalloc(&q->dev_block, total), "create: hipMalloc");
@@ -209,6 +213,7 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
   q->sp_frag = prod ? (const uint16_t*)(base + off_sp_frag) : nullptr;
   q->pi32 = (const float*)(base + off_pi32);
   q->s32 = prod ? (const float*)(base + off_s32) : nullptr;
+  q->sp32 = prod ? (const float*)(base + off_sp32) : nullptr;
   *out = q;
   g_last_error.clear();
   return TQ_OK;
@@ -392,24 +397,10 @@ tq_status tq_decode_attention(const tq_attn_shape* shape, const void* q, const t
   return launch_decode(p, q, k, v, ctx_lens, scale, out, scores_dbg, workspace, (hipStream_t)stream);
 }
 
-// Append workspace: [decode workspace][attended lengths][staged key and value records]
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-struct AppendLayout {
-  size_t lens, k_codes, k_signs, k_norms, k_rnorms, v_codes, v_norms, total;
-};
-static AppendLayout append_layout(const DecodePlan& p) {
-  const size_t G = (size_t)p.batch * p.n_kv_heads, d = (size_t)p.d;
-  AppendLayout L;
-  size_t o = align256(p.total_bytes);
-  L.lens = o;     o = align256(o + sizeof(int32_t) * p.batch);
-  L.k_codes = o;  o = align256(o + G * (size_t)(p.k_planes > 0 ? p.k_planes : 1) * d / 8);
-  L.k_signs = o;  o = align256(o + G * d / 8);
-  L.k_norms = o;  o = align256(o + G * 4);
-  L.k_rnorms = o; o = align256(o + G * 4);
-  L.v_codes = o;  o = align256(o + G * (size_t)p.v_bits * d / 8);
-  L.v_norms = o;  o = align256(o + G * 4);
-  L.total = o;
-  return L;
+// Append workspace: the decode workspace, then the attended lengths [B]
+static size_t append_workspace(const DecodePlan& p) {
+  const size_t o = (p.total_bytes + 255) & ~(size_t)255;
+  return o + (((size_t)p.batch * sizeof(int32_t) + 255) & ~(size_t)255);
 }
 
 tq_status tq_decode_append_workspace_size(const tq_attn_shape* shape, const tq_packed_kv* k,
@@ -418,7 +409,7 @@ tq_status tq_decode_append_workspace_size(const tq_attn_shape* shape, const tq_p
   DecodePlan p;
   tq_status st = check_decode(shape, k, v, &p);
   if (st != TQ_OK) return st;
-  *bytes = append_layout(p).total;
+  *bytes = append_workspace(p);
   return TQ_OK;
 }
 
@@ -433,52 +424,32 @@ tq_status tq_decode_append_attention(const tq_attn_shape* shape, const void* q, 
   if (!k_new || !v_new) return set_error(TQ_ERR_INVALID_ARG, "decode_append: k_new or v_new is NULL");
   if (kv_dtype != TQ_F32 && kv_dtype != TQ_BF16) return set_error(TQ_ERR_INVALID_ARG, "decode_append: unknown kv_dtype");
   if (!std::isfinite(scale)) return set_error(TQ_ERR_INVALID_ARG, "decode_append: scale is not finite");
-  const AppendLayout L = append_layout(p);
-  if (!workspace || ws_bytes < L.total)
-    return set_error(TQ_ERR_WORKSPACE, fmt("decode_append: workspace needs %zu bytes, got %zu", L.total, workspace ? ws_bytes : (size_t)0));
+  const size_t need = append_workspace(p);
+  if (!workspace || ws_bytes < need)
+    return set_error(TQ_ERR_WORKSPACE, fmt("decode_append: workspace needs %zu bytes, got %zu", need, workspace ? ws_bytes : (size_t)0));
   hipStream_t hs = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  const int G = p.batch * p.n_kv_heads;
-  std::vector<const tq_quantizer*> kq(G), vq(G);
-  for (int g = 0; g < G; ++g) {
-    kq[g] = k->qz[g % p.n_kv_heads];
-    vq[g] = v->qz[g % p.n_kv_heads];
-  }
-  const bool kprod = kq[0]->variant == TQ_PROD;
-  QuantizeLaunch qk{kq.data(), G, 1, k_new, kv_dtype, TQ_LAYOUT_VECTOR,
-                    p.k_planes > 0 ? (uint8_t*)(ws + L.k_codes) : nullptr, kprod ? (uint8_t*)(ws + L.k_signs) : nullptr,
-                    (float*)(ws + L.k_norms), kprod ? (float*)(ws + L.k_rnorms) : nullptr, nullptr, nullptr};
-  st = launch_quantize(qk, hs);
-  if (st != TQ_OK) return st;
-  QuantizeLaunch qv{vq.data(), G, 1, v_new, kv_dtype, TQ_LAYOUT_VECTOR, (uint8_t*)(ws + L.v_codes), nullptr,
-                    (float*)(ws + L.v_norms), nullptr, nullptr, nullptr};
-  st = launch_quantize(qv, hs);
-  if (st != TQ_OK) return st;
-  AppendScatter a;
+  int32_t* lens1 = (int32_t*)((char*)workspace + ((p.total_bytes + 255) & ~(size_t)255));
+  AppendLaunch a;
   a.ctx_lens = ctx_lens;
-  a.lens_out = (int32_t*)(ws + L.lens);
+  a.lens_out = lens1;
   a.batch = p.batch;
   a.n_kv_heads = p.n_kv_heads;
   a.d = p.d;
-  a.k_planes = p.k_planes;
-  a.v_bits = p.v_bits;
   a.max_ctx = p.max_ctx;
-  a.k_prod = kprod;
-  a.sk_codes = (const uint8_t*)(ws + L.k_codes);
-  a.sk_signs = (const uint8_t*)(ws + L.k_signs);
-  a.sk_norms = (const float*)(ws + L.k_norms);
-  a.sk_rnorms = (const float*)(ws + L.k_rnorms);
-  a.sv_codes = (const uint8_t*)(ws + L.v_codes);
-  a.sv_norms = (const float*)(ws + L.v_norms);
+  a.kq = k->qz;
+  a.vq = v->qz;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.x_dtype = kv_dtype;
   a.k_codes = const_cast<uint8_t*>(k->codes);
   a.k_signs = const_cast<uint8_t*>(k->signs);
   a.k_norms = const_cast<float*>(k->norms);
   a.k_rnorms = const_cast<float*>(k->rnorms);
   a.v_codes = const_cast<uint8_t*>(v->codes);
   a.v_norms = const_cast<float*>(v->norms);
-  st = launch_append_scatter(a, hs);
+  st = launch_append(a, hs);
   if (st != TQ_OK) return st;
-  return launch_decode(p, q, k, v, (const int32_t*)(ws + L.lens), scale, out, nullptr, workspace, hs);
+  return launch_decode(p, q, k, v, lens1, scale, out, nullptr, workspace, hs);
 }
 
 }  // extern "C"

@@ -41,12 +41,13 @@ struct tq_quantizer {
   // Device tables, one allocation:
   //   pi_frag / sp_frag: bf16 hi/lo MFMA fragments of Pi and S' = S Pi^T,
   //                      ordered [hilo][mtile][kstep][lane][8]
-  //   pi32 / s32       : float32 row-major copies of Pi and S
+  //   pi32 / s32 / sp32: float32 row-major copies of Pi, S and S' = S Pi^T
   void* dev_block = nullptr;
   const uint16_t* pi_frag = nullptr;
   const uint16_t* sp_frag = nullptr;
   const float* pi32 = nullptr;
   const float* s32 = nullptr;
+  const float* sp32 = nullptr;
 };
 
 namespace tq {
@@ -97,21 +98,19 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
                         const tq_packed_kv* v, const int32_t* ctx_lens, float scale, float* out,
                         float* scores_dbg, void* workspace, hipStream_t stream);
 
-// Decode-step append (tq_append.hip): staged vector-layout records of the new
-// token per (batch, kv head) into the caches at ctx_lens[b]; lens_out[b] gets
-// the attended length.
-struct AppendScatter {
+// Decode-step append (tq_append.hip): quantize the new key and value of every
+// (batch, kv head) and write them into the caches at ctx_lens[b]; lens_out[b]
+// gets the attended length.
+struct AppendLaunch {
   const int32_t* ctx_lens;
   int32_t* lens_out;
-  int batch, n_kv_heads, d, k_planes, v_bits;
+  int batch, n_kv_heads, d;
   int64_t max_ctx;
-  bool k_prod;
-  const uint8_t* sk_codes;
-  const uint8_t* sk_signs;
-  const float* sk_norms;
-  const float* sk_rnorms;
-  const uint8_t* sv_codes;
-  const float* sv_norms;
+  const tq_quantizer* const* kq;  // [n_kv_heads]
+  const tq_quantizer* const* vq;
+  const void* k_new;
+  const void* v_new;
+  tq_dtype x_dtype;
   uint8_t* k_codes;
   uint8_t* k_signs;
   float* k_norms;
@@ -119,6 +118,6 @@ struct AppendScatter {
   uint8_t* v_codes;
   float* v_norms;
 };
-tq_status launch_append_scatter(const AppendScatter& a, hipStream_t stream);
+tq_status launch_append(const AppendLaunch& a, hipStream_t stream);
 
 }  // namespace tq

@@ -172,6 +172,7 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the path is measured on a single GPU.",
               file=sys.stderr)
         return 2
+    import numpy as np
     import torch
     if args.calibrate_copy:
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
@@ -241,6 +242,30 @@ def main():
     p_ms = e0.elapsed_time(e1) / 10
     p_vec = w["H"] * w["T2"]
 
+    # decode step with append: the new token's key and value are quantized into the
+    # caches at position ctx - 1 of every sequence, then ctx tokens are attended
+    knew = torch.from_numpy(np.stack([syn.kv_vectors(w["Hkv"], w["d"], syn.CFG_DECODE_128K, syn.T_K, b, 99)
+                                      for b in range(w["B"])])).to(dev).to(torch.bfloat16)
+    vnew = torch.from_numpy(np.stack([syn.kv_vectors(w["Hkv"], w["d"], syn.CFG_DECODE_128K, syn.T_V, b, 99)
+                                      for b in range(w["B"])])).to(dev).to(torch.bfloat16)
+    lens_app = torch.full((w["B"],), w["T3"] - 1, dtype=torch.int32, device=dev)
+    ws_app = torch.empty(tq.decode_append_workspace_size(w["B"], w["Hq"], w["Hkv"], w["d"], w["T3"], w["kcache"],
+                                                         w["vcache"]), dtype=torch.uint8, device=dev)
+
+    def decode_append():
+        tq.decode_append_attention(w["q"], knew, vnew, w["kcache"], w["vcache"], lens_app, 1 / math.sqrt(w["d"]),
+                                   max_ctx=w["T3"], out=w["out"], workspace=ws_app)
+
+    for _ in range(3):
+        decode_append()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        decode_append()
+    e1.record()
+    torch.cuda.synchronize()
+    a_ms = e0.elapsed_time(e1) / 10
+
     traffic = decode_traffic(args.traffic)
     d_gbs = d_bytes / (d_avg * 1e-3) / 1e9
     result = {
@@ -269,6 +294,7 @@ def main():
             "decode_ms_p10_p90": [round(d_ms[K // 10], 4), round(d_ms[(9 * K) // 10 - 1 if K >= 10 else -1], 4)],
             "quantize_prod_mvec_s": round(p_vec / (p_ms * 1e-3) / 1e6, 1),
             "quantize_prod_gb_s": round(p_vec * (256 + 32 + 16 + 8) / (p_ms * 1e-3) / 1e9, 1),
+            "decode_append_ms": round(a_ms, 4),
             "wall_s_timed_region": round(wall, 3),
         },
         "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

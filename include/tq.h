@@ -266,8 +266,11 @@ tq_status tq_decode_attention(const tq_attn_shape* shape, const void* q, const t
  *                   tokens.
  *   workspace     : device, at least tq_decode_append_workspace_size() bytes.
  * Same validation and errors as tq_decode_attention, plus TQ_ERR_INVALID_ARG
- * for NULL k_new / v_new or an unknown kv_dtype. Four launches on `stream`
- * (key quantize, value quantize, scatter, attention); no host synchronization.
+ * for NULL k_new / v_new or an unknown kv_dtype. Two steps on `stream` (one
+ * workgroup per (b, h) quantizes and writes both records, then the attention);
+ * no host synchronization. Records equal those of tq_quantize except where a
+ * rotated coordinate lies within rounding of a decision threshold (the append
+ * rotates in fp32 instead of split-bf16 matrix cores).
  */
 tq_status tq_decode_append_workspace_size(const tq_attn_shape* shape, const tq_packed_kv* k,
                                           const tq_packed_kv* v, size_t* bytes);
