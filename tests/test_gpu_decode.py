@@ -70,6 +70,10 @@ CASES = [
     (1, 16, 2, 256, 96, 3, "prod", 3, [90]),
     (1, 8, 2, 64, 96, 4, "prod", 4, [70]),
     (1, 8, 1, 256, 64, 4, "mse", 2, [64]),
+    # GQA group sizes 1 and 2, and the largest number of KV heads (64)
+    (2, 4, 4, 128, 64, 3, "prod", 3, [64, 50]),
+    (1, 32, 16, 128, 96, 2, "mse", 3, [77]),
+    (1, 64, 64, 64, 32, 3, "prod", 2, [29]),
 ]
 
 
