@@ -1,24 +1,13 @@
-// HIP kernels for gfx950 (CDNA4, wave64) and their launchers.
+// Dequantize and inner-product kernels for gfx950 (CDNA4, wave64) and their
+// launchers: the reference-speed library calls Q^-1 and <y, x~> on packed codes.
 //
 // What is computed follows [NIK] = S. Nikolenko, "Eternal mathematics of
-// TurboQuant" (blog.sergeynikolenko.ru): "Step 0: normalization", "Step 1:
-// random rotation", "Step 2: optimal scalar quantization (Lloyd-Max)", "QJL:
-// a one-bit method", "TurboQuant proper"; and [NAH] = "What exactly TurboQuant
-// showed" (nahornyi.ai): prod keys need a dedicated attention kernel.
-//
-// Matrix-core building block: v_mfma_f32_16x16x32_bf16. For C = A*B + C with
-// A 16x32, B 32x16 and lane l = r + 16*g (r in 0..15, g in 0..3):
-//   A: lane l holds A[r][8g .. 8g+7];  B: lane l holds B[8g .. 8g+7][r];
-//   C: lane l holds C[4g .. 4g+3][r].
-// fp32 accuracy for the dense rotations comes from splitting each operand into
-// bf16 hi + lo parts (16 significant bits) and accumulating in fp32.
-//
-// Bit operands. A packed bit becomes a bf16 MFMA operand without unpacking:
-// rotate the 32-bit word so that the wanted bit lands on exponent bit 4+k of a
-// bf16 half and mask everything else; the half is then 0 or the exact power of
-// two 2^(2^(4+k) - 127). The other operand carries the compensating factor
-// 2^(E - e_k), so every product is exactly (weight * bit * 2^E). One rotate plus
-// four ANDs turn a word into one MFMA operand (8 bits).
+// TurboQuant" (blog.sergeynikolenko.ru): "Step 2: optimal scalar quantization
+// (Lloyd-Max)" (x~ = |x| Pi^T c[idx]), "QJL: a one-bit method" (the
+// sqrt(pi/2)/d S^T z reconstruction) and "TurboQuant proper" (their sum for
+// prod). Both kernels are plain fp32 VALU code over the quantizer's fp32 copies
+// of Pi and S: they are not on the decode hot path, which reads the codes with
+// matrix cores directly.
 #include <hip/hip_runtime.h>
 
 #include <cmath>

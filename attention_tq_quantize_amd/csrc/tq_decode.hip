@@ -15,12 +15,14 @@
 // weights, so every MFMA row is used and weights carry 22 significant bits.
 //
 // Bit operands. A packed cache bit becomes an fp16 MFMA operand without
-// unpacking: rotate the 32-bit word so the wanted bit lands on exponent bit k
-// of an fp16 half (bit position 10+k or 26+k) and mask everything else; the
-// half is then 0 or the exact power of two 2^(2^k - 15). The weight operand
-// carries the compensating power of two, so each product is exactly
+// unpacking: shift the 32-bit word so the wanted nibble lands on bits 8-11 of
+// each fp16 half and mask one bit per element (bit_operand); the half is then
+// 0 or the exact power of two 2^(k - 16) for slot k. The other operand carries
+// the compensating power of two, so each product is exactly
 // weight * bit * 2^E for a per-row exponent E chosen to keep the weights in
-// fp16 range. One rotate plus four ANDs make one MFMA operand (8 bits).
+// fp16 range. One shift (none for the third nibble) plus four ANDs make one
+// MFMA operand (8 bits). Positions 8-11 keep the matrix cores' products exact
+// in their sums; deeper subnormal positions would lose low product bits.
 //
 // Both contractions use 0/1 bits. With sigma = 2 bit - 1 and the odd Walsh
 // expansion of the symmetric codebook, c[idx] = sum_s a_s prod_{i in s} sigma_i,
