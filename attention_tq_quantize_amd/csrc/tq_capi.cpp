@@ -40,6 +40,9 @@ std::string fmt(const char* f, ...) {
 }
 
 bool gpu_dim(int d) { return d == 64 || d == 128 || d == 256; }
+// head dimensions of the vector-search path (quantize in the vector layout and
+// inner products only): multiples of 64 above 256, up to 4096
+bool large_dim(int d) { return d > 256 && d <= 4096 && d % 64 == 0; }
 
 uint16_t bf16_rne(float f) {
   uint32_t u;
@@ -122,20 +125,49 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
                               const double* s, tq_quantizer** out) {
   if (!out) return set_error(TQ_ERR_INVALID_ARG, "create: out is NULL");
   *out = nullptr;
-  if (!gpu_dim(d)) return set_error(TQ_ERR_UNSUPPORTED, fmt("create: d=%d (supported: 64, 128, 256)", d));
+  const bool large = large_dim(d);
+  if (!gpu_dim(d) && !large)
+    return set_error(TQ_ERR_UNSUPPORTED, fmt("create: d=%d (supported: 64, 128, 256; multiples of 64 up to 4096 for quantize and inner products)", d));
   if (bits < 1 || bits > kMaxBits) return set_error(TQ_ERR_UNSUPPORTED, fmt("create: bits=%d (supported: 1..4)", bits));
   if (variant != TQ_MSE && variant != TQ_PROD) return set_error(TQ_ERR_INVALID_ARG, "create: unknown variant");
   if (!pi) return set_error(TQ_ERR_INVALID_ARG, "create: pi is NULL");
   if (variant == TQ_PROD && !s) return set_error(TQ_ERR_INVALID_ARG, "create: prod needs the QJL matrix s");
   // Pi must be orthogonal (rows orthonormal) for Q^-1 = Pi^T to invert the rotation.
   double worst = 0.0;
-  for (int i = 0; i < d; ++i)
-    for (int j = i; j < d; ++j) {
-      double acc = 0.0;
-      for (int k = 0; k < d; ++k) acc += pi[(size_t)i * d + k] * pi[(size_t)j * d + k];
-      if (!std::isfinite(acc)) return set_error(TQ_ERR_INVALID_ARG, "create: pi is not finite");
-      worst = std::fmax(worst, std::fabs(acc - (i == j ? 1.0 : 0.0)));
+  for (size_t i = 0; i < (size_t)d * d; ++i)
+    if (!std::isfinite(pi[i])) return set_error(TQ_ERR_INVALID_ARG, "create: pi is not finite");
+  if (!large) {
+    for (int i = 0; i < d; ++i)
+      for (int j = i; j < d; ++j) {
+        double acc = 0.0;
+        for (int k = 0; k < d; ++k) acc += pi[(size_t)i * d + k] * pi[(size_t)j * d + k];
+        worst = std::fmax(worst, std::fabs(acc - (i == j ? 1.0 : 0.0)));
+      }
+  } else {
+    // O(d^2) check instead of the O(d^3) Gram matrix: Pi^T Pi v = v for a few
+    // fixed pseudo-random v (a matrix that is not orthogonal fails it for almost any v)
+    std::vector<double> v(d), w(d), z(d);
+    uint32_t st = 12345u;
+    for (int rep = 0; rep < 4; ++rep) {
+      for (int j = 0; j < d; ++j) {
+        st = st * 1664525u + 1013904223u;
+        v[j] = (double)(st >> 8) / 16777216.0 - 0.5;
+      }
+      for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int k = 0; k < d; ++k) acc += pi[(size_t)i * d + k] * v[k];
+        w[i] = acc;
+      }
+      double nv = 0.0;
+      for (int j = 0; j < d; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += pi[(size_t)i * d + j] * w[i];
+        z[j] = acc;
+        nv = std::fmax(nv, std::fabs(v[j]));
+      }
+      for (int j = 0; j < d; ++j) worst = std::fmax(worst, std::fabs(z[j] - v[j]) / nv);
     }
+  }
   if (worst > 1e-6) return set_error(TQ_ERR_INVALID_ARG, fmt("create: pi is not orthogonal (max |Pi Pi^T - I| = %.3g)", worst));
   if (variant == TQ_PROD)
     for (size_t i = 0; i < (size_t)d * d; ++i)
@@ -161,17 +193,19 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
   }
 
   const size_t dd = (size_t)d * d;
-  const size_t frag_bytes = 2 * dd * sizeof(uint16_t);  // hi + lo
+  // large d: fp32 Pi and S only (the MFMA fragments and S' = S Pi^T serve the
+  // d <= 256 kernels; the O(d^3) fold would dominate creation time)
+  const size_t frag_bytes = large ? 0 : 2 * dd * sizeof(uint16_t);  // hi + lo
   const bool prod = variant == TQ_PROD;
-  const size_t total = frag_bytes * (prod ? 2 : 1) + dd * sizeof(float) * (prod ? 3 : 1);
+  const size_t total = frag_bytes * (prod ? 2 : 1) + dd * sizeof(float) * (prod ? (large ? 2 : 3) : 1);
   std::vector<unsigned char> host(total);
   size_t off = 0;
-  build_fragments(d, pi, (uint16_t*)(host.data() + off));
+  if (!large) build_fragments(d, pi, (uint16_t*)(host.data() + off));
   const size_t off_pi_frag = off;
   off += frag_bytes;
   size_t off_sp_frag = 0;
   std::vector<double> sp;
-  if (prod) {
+  if (prod && !large) {
     // S' = S Pi^T, folded in fp64, so that S r = S' (Pi u - y~): the residual never
     // leaves the rotated space.
     sp.assign(dd, 0.0);
@@ -193,9 +227,11 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
     off_s32 = off;
     for (size_t i = 0; i < dd; ++i) ((float*)(host.data() + off))[i] = (float)s[i];
     off += dd * sizeof(float);
-    off_sp32 = off;
-    for (size_t i = 0; i < dd; ++i) ((float*)(host.data() + off))[i] = (float)sp[i];
-    off += dd * sizeof(float);
+    if (!large) {
+      off_sp32 = off;
+      for (size_t i = 0; i < dd; ++i) ((float*)(host.data() + off))[i] = (float)sp[i];
+      off += dd * sizeof(float);
+    }
   }
   hs = check_hip(hipMalloc(&q->dev_block, total), "create: hipMalloc");
   if (hs != TQ_OK) {
@@ -209,11 +245,11 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
     return hs;
   }
   unsigned char* base = (unsigned char*)q->dev_block;
-  q->pi_frag = (const uint16_t*)(base + off_pi_frag);
-  q->sp_frag = prod ? (const uint16_t*)(base + off_sp_frag) : nullptr;
+  q->pi_frag = large ? nullptr : (const uint16_t*)(base + off_pi_frag);
+  q->sp_frag = prod && !large ? (const uint16_t*)(base + off_sp_frag) : nullptr;
   q->pi32 = (const float*)(base + off_pi32);
   q->s32 = prod ? (const float*)(base + off_s32) : nullptr;
-  q->sp32 = prod ? (const float*)(base + off_sp32) : nullptr;
+  q->sp32 = prod && !large ? (const float*)(base + off_sp32) : nullptr;
   *out = q;
   g_last_error.clear();
   return TQ_OK;
@@ -224,7 +260,8 @@ tq_status tq_quantizer_create_wht(int d, int bits, tq_variant variant, const dou
   if (!out) return set_error(TQ_ERR_INVALID_ARG, "create_wht: out is NULL");
   *out = nullptr;
   if (!signs) return set_error(TQ_ERR_INVALID_ARG, "create_wht: signs is NULL");
-  if (!gpu_dim(d)) return set_error(TQ_ERR_UNSUPPORTED, fmt("create_wht: d=%d (supported: 64, 128, 256)", d));
+  if (!gpu_dim(d) && !(large_dim(d) && (d & (d - 1)) == 0))
+    return set_error(TQ_ERR_UNSUPPORTED, fmt("create_wht: d=%d (a supported power of two)", d));
   for (int j = 0; j < d; ++j)
     if (signs[j] != 1.0 && signs[j] != -1.0)
       return set_error(TQ_ERR_INVALID_ARG, fmt("create_wht: signs[%d] is not +-1", j));
@@ -292,6 +329,7 @@ tq_status tq_quantize(const tq_quantizer* const* qz, int n_groups, int64_t n_per
   if (!prod && proj_dbg) return set_error(TQ_ERR_INVALID_ARG, "quantize: proj_dbg is only for prod");
   if ((double)n_groups * (double)n_per_group > 4.0e9) return set_error(TQ_ERR_UNSUPPORTED, "quantize: more than 4e9 vectors");
   QuantizeLaunch a{qz, n_groups, n_per_group, x, x_dtype, layout, codes, signs, norms, rnorms, rot_dbg, proj_dbg};
+  if (large_dim(q0->d)) return launch_quantize_large(a, (hipStream_t)stream);
   return launch_quantize(a, (hipStream_t)stream);
 }
 
@@ -317,6 +355,7 @@ tq_status tq_dequantize(const tq_quantizer* q, tq_layout layout, const uint8_t* 
                         float* x_out, void* stream) {
   if (!q) return set_error(TQ_ERR_INVALID_ARG, "dequantize: handle is NULL");
   if (n < 0) return set_error(TQ_ERR_INVALID_ARG, "dequantize: n < 0");
+  if (large_dim(q->d)) return set_error(TQ_ERR_UNSUPPORTED, "dequantize: d > 256 (quantize and inner products only)");
   if (layout != TQ_LAYOUT_VECTOR && layout != TQ_LAYOUT_BLOCK32) return set_error(TQ_ERR_INVALID_ARG, "dequantize: unknown layout");
   if (layout == TQ_LAYOUT_BLOCK32) {
     if (q->variant != TQ_MSE) return set_error(TQ_ERR_UNSUPPORTED, "dequantize: BLOCK32 layout is for mse quantizers");
@@ -338,6 +377,8 @@ tq_status tq_inner_products(const tq_quantizer* q, const float* y, int64_t m, co
   if (!y || (q->planes > 0 && !codes) || !norms || !out) return set_error(TQ_ERR_INVALID_ARG, "inner_products: NULL buffer");
   if (q->variant == TQ_PROD && (!signs || !rnorms)) return set_error(TQ_ERR_INVALID_ARG, "inner_products: prod needs signs and rnorms");
   if (m > 65535 || n > (int64_t)1 << 31) return set_error(TQ_ERR_UNSUPPORTED, "inner_products: m > 65535 or n > 2^31");
+  if (large_dim(q->d))
+    return launch_inner_products_large(q, y, m, codes, signs, norms, rnorms, n, out, (hipStream_t)stream);
   return launch_inner_products(q, y, m, codes, signs, norms, rnorms, n, out, (hipStream_t)stream);
 }
 

@@ -74,6 +74,11 @@ struct QuantizeLaunch {
   float* proj_dbg;
 };
 tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream);
+// d > 256 (tq_large.hip): vector layout only
+tq_status launch_quantize_large(const QuantizeLaunch& a, hipStream_t stream);
+tq_status launch_inner_products_large(const tq_quantizer* q, const float* y, int64_t m,
+                                      const uint8_t* codes, const uint8_t* signs, const float* norms,
+                                      const float* rnorms, int64_t n, float* out, hipStream_t stream);
 
 tq_status launch_dequantize(const tq_quantizer* q, tq_layout layout, const uint8_t* codes,
                             const uint8_t* signs, const float* norms, const float* rnorms,

@@ -166,6 +166,47 @@ def cpu_baseline(syn):
             "quantize_mvec_s": round(nq / tq_s / 1e6, 5), "decode_gb_s": round(dbytes / td_s / 1e9, 5)}
 
 
+def vector_search(tq, syn, torch, dev, n=100000, m=16, bits=3):
+    """Vector-search workload: index n synthetic Gaussian embeddings with
+    TurboQuant_prod (b = 3) at d = 1536 and 3072, then score m queries against
+    the packed database with tq_inner_products."""
+    import numpy as np
+    out = {}
+    for d in (1536, 3072):
+        qz = tq.Quantizer(d, bits, "prod", syn.rotation(d, syn.CFG_SWEEP, syn.T_K, 500 + d),
+                          syn.gaussian_matrix(d, syn.CFG_SWEEP, syn.T_K, 500 + d))
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(syn.ROOT_SEED + d)
+        x = torch.randn((n, d), generator=gen, device=dev, dtype=torch.float32)
+        y = torch.randn((m, d), generator=gen, device=dev, dtype=torch.float32)
+        rec = tq.quantize_prod(qz, x)  # warm-up and the database
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        rec = tq.quantize_prod(qz, x)
+        e1.record()
+        torch.cuda.synchronize()
+        index_ms = e0.elapsed_time(e1)
+        del x
+        args = (qz, y, rec["codes"], rec["norms"], rec["signs"], rec["rnorms"])
+        for _ in range(3):
+            tq.inner_products(*args)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            tq.inner_products(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        score_ms = e0.elapsed_time(e1) / 10
+        rec_bytes = (bits - 1) * d // 8 + d // 8 + 8
+        out[f"d{d}"] = {"database": n, "queries": m, "variant": f"prod b={bits}",
+                        "index_ms": round(index_ms, 3), "index_mvec_s": round(n / (index_ms * 1e-3) / 1e6, 2),
+                        "score_ms": round(score_ms, 3), "pairs_per_s": round(m * n / (score_ms * 1e-3), 1),
+                        "score_record_gb_s": round(m * n * rec_bytes / (score_ms * 1e-3) / 1e9, 1)}
+        del rec, qz
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -266,6 +307,8 @@ def main():
     torch.cuda.synchronize()
     a_ms = e0.elapsed_time(e1) / 10
 
+    vsearch = vector_search(tq, syn, torch, dev)
+
     traffic = decode_traffic(args.traffic)
     d_gbs = d_bytes / (d_avg * 1e-3) / 1e9
     result = {
@@ -295,6 +338,7 @@ def main():
             "quantize_prod_mvec_s": round(p_vec / (p_ms * 1e-3) / 1e6, 1),
             "quantize_prod_gb_s": round(p_vec * (256 + 32 + 16 + 8) / (p_ms * 1e-3) / 1e9, 1),
             "decode_append_ms": round(a_ms, 4),
+            "vector_search": vsearch,
             "wall_s_timed_region": round(wall, 3),
         },
         "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

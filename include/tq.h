@@ -96,7 +96,12 @@ tq_status tq_codebook_build(int d, int bits, float* centroids, float* thresholds
  * for TQ_PROD also [NIK] "QJL: a one-bit method" and "TurboQuant proper":
  * b-1 bit MSE stage, then sign(S r) and |r| of the residual.
  *   d, bits   : head dimension and total bits per coordinate (prod: b-1 for the
- *               MSE stage plus 1 QJL bit).
+ *               MSE stage plus 1 QJL bit). d in {64, 128, 256} for every call;
+ *               d a multiple of 64 in (256, 4096] (vector search, [NIK]
+ *               "Experiments": d = 1536, 3072) for tq_quantize in the VECTOR
+ *               layout and tq_inner_products only (others return
+ *               TQ_ERR_UNSUPPORTED). Orthogonality is checked exactly for
+ *               d <= 256 and on four fixed pseudo-random vectors above.
  *   pi        : host, float64 [d][d] row-major, orthogonal (y = Pi u).
  *   s         : host, float64 [d][d] row-major Gaussian QJL matrix; required
  *               iff variant == TQ_PROD, ignored otherwise. It must be drawn

@@ -1,0 +1,125 @@
+"""Vector-search scoring at large head dimensions ([NIK] "Experiments":
+nearest neighbours with d = 1536 and 3072), against the fp64 oracle:
+
+* quantize at d = 512, 1536, 3072 (mse and prod): norms within 2 ulp, rotated
+  coordinates within 2e-5 of fp64, codes and QJL signs bit-exact when the
+  oracle's rule is fed the kernel's own rotated coordinates / projections,
+  and flips against the full fp64 path only within the 1e-5 band;
+* inner products <y, x~> straight from an oracle-packed database, within
+  1e-4 of the largest |<y, x~>|;
+* D_prod measured from the GPU's inner products for prod b = 3 at d = 1536:
+  E (<y,x> - <y,x~>)^2 d / (|x|^2 |y|^2) = (pi/2 - 1/d) d C(f_X, 2) for y
+  independent of x (within 10 %).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import tq_synth as syn
+from tq_testlib import MAX_FLIP_RATE, TIE_BAND, near_threshold, ulp_diff_f32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _mats(d, prod, head=0):
+    Pi = syn.rotation(d, syn.CFG_TEST, syn.T_K, 100 + head)
+    S = syn.gaussian_matrix(d, syn.CFG_TEST, syn.T_K, 100 + head) if prod else None
+    return Pi, S
+
+
+@pytest.mark.parametrize("d,variant,bits", [(512, "mse", 2), (1536, "mse", 3), (1536, "prod", 3), (3072, "prod", 2)])
+def test_large_d_quantize_parity(gpu_lib, d, variant, bits):
+    tq = gpu_lib
+    n = 300
+    print(f"large-d quantize d={d} {variant} b={bits} n={n}", flush=True)
+    Pi, S = _mats(d, variant == "prod")
+    q = tq.Quantizer(d, bits, variant, Pi, S)
+    x = syn.gaussian_queries(n, d, syn.CFG_TEST, batch=d)  # Gaussian embeddings, fp32
+    x[7] = 0.0
+    xd = torch.from_numpy(x).to(DEV)
+    r = tq.quantize_prod(q, xd, rot_dbg=True, proj_dbg=True) if variant == "prod" else tq.quantize_mse(q, xd, rot_dbg=True)
+    torch.cuda.synchronize()
+    planes = q.planes
+    cb = O.codebook(d, planes)
+    ref = O.quantize_prod(x, Pi, S, cb) if variant == "prod" else O.quantize_mse(x, Pi, cb)
+    valid = ref["nu"] > 0
+    assert ulp_diff_f32(r["norms"].cpu().numpy(), ref["nu"].astype(np.float32)).max() <= 2
+    rot = r["rot"].cpu().numpy()
+    assert np.abs(rot[valid] - ref["y"][valid]).max() < 2e-5
+    if planes > 0:
+        codes = r["codes"].cpu().numpy()
+        fed = O.nearest_index(rot.astype(np.float64), cb)
+        fed[~valid] = 0
+        assert np.array_equal(codes, O.pack_vector_layout(fed, planes))
+        idx = O.unpack_vector_layout(codes, planes, d)
+        flips = idx[valid] != ref["idx"][valid]
+        assert flips.mean() < MAX_FLIP_RATE
+        if flips.any():
+            assert np.all(near_threshold(ref["y"][valid][flips], cb, TIE_BAND))
+    if variant == "prod":
+        proj = r["proj"].cpu().numpy()
+        fed = proj >= 0
+        fed[~valid] = False
+        assert np.array_equal(r["signs"].cpu().numpy(), O.pack_bits(fed))
+        rn = r["rnorms"].cpu().numpy()
+        assert rn[7] == 0
+        same = valid & np.all(O.unpack_vector_layout(r["codes"].cpu().numpy(), planes, d) == ref["idx"], axis=1)
+        assert np.allclose(rn[same], ref["gamma"][same], rtol=2e-5, atol=2e-7)
+
+
+def _oracle_database(d, variant, bits, n, head):
+    Pi, S = _mats(d, variant == "prod", head)
+    x = syn.gaussian_queries(n, d, syn.CFG_TEST, batch=1000 + head)
+    planes = bits - 1 if variant == "prod" else bits
+    cb = O.codebook(d, planes)
+    if variant == "prod":
+        r = O.quantize_prod(x, Pi, S, cb)
+        xt = O.dequantize_prod(r["idx"], r["signs"], r["norms"], r["rnorms"], Pi, S, cb)
+    else:
+        r = O.quantize_mse(x, Pi, cb)
+        xt = O.dequantize_mse(r["idx"], r["norms"], Pi, cb)
+    db = {"norms": r["norms"], "codes": O.pack_vector_layout(r["idx"], planes) if planes else None}
+    if variant == "prod":
+        db["signs"] = O.pack_bits(r["signs"])
+        db["rnorms"] = r["rnorms"]
+    return Pi, S, x, xt, db
+
+
+@pytest.mark.parametrize("d,variant,bits,n", [(1536, "prod", 3, 3000), (1536, "mse", 2, 3000), (3072, "prod", 2, 1200),
+                                              (768, "prod", 1, 1000)])
+def test_large_d_inner_products_parity(gpu_lib, d, variant, bits, n):
+    tq = gpu_lib
+    m = 4
+    print(f"large-d inner products d={d} {variant} b={bits} n={n} m={m}", flush=True)
+    Pi, S, x, xt, db = _oracle_database(d, variant, bits, n, 1)
+    q = tq.Quantizer(d, bits, variant, Pi, S)
+    y = syn.gaussian_queries(m, d, syn.CFG_TEST, batch=5000 + d)
+    dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    got = tq.inner_products(q, dev(y), dev(db["codes"]), dev(db["norms"]), dev(db.get("signs")),
+                            dev(db.get("rnorms"))).cpu().numpy()
+    want = O.inner_products(y, xt)
+    err = np.abs(got - want).max()
+    assert err <= 1e-4 * np.abs(want).max(), (err, np.abs(want).max())
+
+
+def test_vector_search_dprod(gpu_lib):
+    tq = gpu_lib
+    d, bits, n, m = 1536, 3, 4000, 8
+    print(f"D_prod d={d} prod b={bits} n={n} m={m}", flush=True)
+    Pi, S, x, xt, db = _oracle_database(d, "prod", bits, n, 2)
+    q = tq.Quantizer(d, bits, "prod", Pi, S)
+    y = syn.gaussian_queries(m, d, syn.CFG_TEST, batch=6000)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    got = tq.inner_products(q, dev(y), dev(db["codes"]), dev(db["norms"]), dev(db["signs"]), dev(db["rnorms"]))
+    got = got.cpu().numpy().astype(np.float64)
+    true = y.astype(np.float64) @ x.astype(np.float64).T
+    nx = np.sum(x.astype(np.float64) ** 2, axis=1)
+    ny = np.sum(y.astype(np.float64) ** 2, axis=1)
+    dprod = np.mean((true - got) ** 2 * d / (ny[:, None] * nx[None, :]))
+    _, _, cost = tq.codebook_build(d, bits - 1)
+    want = (math.pi / 2 - 1 / d) * d * cost
+    assert abs(dprod - want) < 0.1 * want, (dprod, want)
