@@ -154,14 +154,16 @@ tq_status dispatch_bool(bool v, F&& f) {
 
 tq_status launch_check(const char* what) { return check_hip(hipGetLastError(), what); }
 
+// compute units of the current device, queried once (thread-safe static init;
+// a process here drives one GPU model)
 int device_cus() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
+  static const int cus = [] {
+    int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  }
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    return n;
+  }();
   return cus;
 }
 
