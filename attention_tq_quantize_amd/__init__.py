@@ -27,7 +27,7 @@ EXPORTS = [
     "tq_quantizer_create", "tq_quantizer_create_wht", "tq_quantizer_destroy", "tq_quantizer_info", "tq_quantize",
     "tq_quantize_mse", "tq_quantize_prod", "tq_dequantize", "tq_inner_products",
     "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_append_workspace_size",
-    "tq_decode_append_attention",
+    "tq_decode_append_attention", "tq_search_workspace_size", "tq_search_scores",
 ]
 
 
@@ -76,6 +76,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tq_quantize_prod.argtypes = [_VP, _VP, _I, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
     lib.tq_dequantize.argtypes = [_VP, _I, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
     lib.tq_inner_products.argtypes = [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
+    lib.tq_search_workspace_size.argtypes = [_VP, _I64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.tq_search_scores.argtypes = [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _VP]
     lib.tq_decode_workspace_size.argtypes = [ctypes.POINTER(AttnShape), ctypes.POINTER(PackedKV),
                                              ctypes.POINTER(PackedKV), ctypes.POINTER(ctypes.c_size_t)]
     lib.tq_decode_attention.argtypes = [ctypes.POINTER(AttnShape), _VP, ctypes.POINTER(PackedKV),
@@ -264,6 +266,28 @@ def inner_products(q: Quantizer, y, codes, norms, signs=None, rnorms=None, strea
     _check(lib.tq_inner_products(q.handle, _ptr(y.contiguous()), m, _ptr(codes) if q.planes else None,
                                  _ptr(signs), _ptr(norms), _ptr(rnorms), n, _ptr(out), _stream(stream)),
            "tq_inner_products")
+    return out
+
+
+def search_workspace_size(q: Quantizer, m: int) -> int:
+    lib = load()
+    nb = ctypes.c_size_t(0)
+    _check(lib.tq_search_workspace_size(q.handle, m, ctypes.byref(nb)), "tq_search_workspace_size")
+    return nb.value
+
+
+def search_scores(q: Quantizer, y, codes, norms, signs=None, rnorms=None, workspace=None, stream=None):
+    """<y_i, x~_j> on the matrix cores (tq_search_scores); workspace: a uint8 device
+    tensor of at least search_workspace_size(q, m) bytes (allocated when None)."""
+    import torch
+    lib = load()
+    m, n = y.shape[0], norms.numel()
+    out = torch.empty((m, n), dtype=torch.float32, device=y.device)
+    if workspace is None:
+        workspace = torch.empty(max(search_workspace_size(q, m), 1), dtype=torch.uint8, device=y.device)
+    _check(lib.tq_search_scores(q.handle, _ptr(y.contiguous()), m, _ptr(codes) if q.planes else None,
+                                _ptr(signs), _ptr(norms), _ptr(rnorms), n, _ptr(out), _ptr(workspace),
+                                workspace.numel(), _stream(stream)), "tq_search_scores")
     return out
 
 

@@ -127,7 +127,7 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
   *out = nullptr;
   const bool large = large_dim(d);
   if (!gpu_dim(d) && !large)
-    return set_error(TQ_ERR_UNSUPPORTED, fmt("create: d=%d (supported: 64, 128, 256; multiples of 64 up to 4096 for quantize and inner products)", d));
+    return set_error(TQ_ERR_UNSUPPORTED, fmt("create: d=%d (supported: 64, 128, 256; multiples of 64 in (256, 4096] for quantize, inner products and search)", d));
   if (bits < 1 || bits > kMaxBits) return set_error(TQ_ERR_UNSUPPORTED, fmt("create: bits=%d (supported: 1..4)", bits));
   if (variant != TQ_MSE && variant != TQ_PROD) return set_error(TQ_ERR_INVALID_ARG, "create: unknown variant");
   if (!pi) return set_error(TQ_ERR_INVALID_ARG, "create: pi is NULL");
@@ -380,6 +380,35 @@ tq_status tq_inner_products(const tq_quantizer* q, const float* y, int64_t m, co
   if (large_dim(q->d))
     return launch_inner_products_large(q, y, m, codes, signs, norms, rnorms, n, out, (hipStream_t)stream);
   return launch_inner_products(q, y, m, codes, signs, norms, rnorms, n, out, (hipStream_t)stream);
+}
+
+tq_status tq_search_workspace_size(const tq_quantizer* q, int64_t m, size_t* bytes) {
+  if (!q || !bytes) return set_error(TQ_ERR_INVALID_ARG, "search_workspace_size: NULL argument");
+  if (m < 0) return set_error(TQ_ERR_INVALID_ARG, "search_workspace_size: negative m");
+  SearchPlan pl;
+  tq_status st = search_plan(q, m, &pl);
+  if (st != TQ_OK) return st;
+  *bytes = pl.total;
+  return TQ_OK;
+}
+
+tq_status tq_search_scores(const tq_quantizer* q, const float* y, int64_t m, const uint8_t* codes,
+                           const uint8_t* signs, const float* norms, const float* rnorms, int64_t n, float* out,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  if (!q) return set_error(TQ_ERR_INVALID_ARG, "search: handle is NULL");
+  if (m < 0 || n < 0) return set_error(TQ_ERR_INVALID_ARG, "search: negative size");
+  SearchPlan pl;
+  tq_status st = search_plan(q, m, &pl);
+  if (st != TQ_OK) return st;
+  if (m == 0 || n == 0) return TQ_OK;
+  if (!y || (q->planes > 0 && !codes) || !norms || !out) return set_error(TQ_ERR_INVALID_ARG, "search: NULL buffer");
+  if (q->variant == TQ_PROD && (!signs || !rnorms)) return set_error(TQ_ERR_INVALID_ARG, "search: prod needs signs and rnorms");
+  if ((uintptr_t)y & 15) return set_error(TQ_ERR_INVALID_ARG, "search: y must be 16-byte aligned");
+  if (m > 65535 || n > (int64_t)1 << 31) return set_error(TQ_ERR_UNSUPPORTED, "search: m > 65535 or n > 2^31");
+  const size_t need = pl.total;
+  if (!workspace || ws_bytes < need)
+    return set_error(TQ_ERR_WORKSPACE, fmt("search: workspace needs %zu bytes, got %zu", need, workspace ? ws_bytes : (size_t)0));
+  return launch_search(q, y, m, codes, signs, norms, rnorms, n, out, workspace, (hipStream_t)stream);
 }
 
 static tq_status check_decode(const tq_attn_shape* s, const tq_packed_kv* k, const tq_packed_kv* v,

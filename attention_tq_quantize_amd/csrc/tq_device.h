@@ -126,6 +126,60 @@ __device__ __forceinline__ float centroid_of(const bool* bit, const float* C) {
   }
 }
 
+
+// ---- fp16 matrix-core helpers shared by the decode and vector-search kernels ----
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                0, 0, 0);
+}
+__device__ __forceinline__ unsigned f16_bits(float v) {
+  return (unsigned)__builtin_bit_cast(unsigned short, (_Float16)v);
+}
+__device__ __forceinline__ float f16_val(unsigned h) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
+}
+// hi (lo = false) or lo (lo = true) fp16 part of v; hi + lo carries 22 significant bits
+__device__ __forceinline__ unsigned f16_part(float v, bool lo) {
+  const unsigned hi = f16_bits(v);
+  return lo ? f16_bits(v - f16_val(hi)) : hi;
+}
+
+// exponent E such that |w| <= wmax keeps |w| 2^(E + 14) < 2^14 (the largest
+// compensation is 2^14), so every scaled weight and its lo part stay normal fp16
+// down to about 2^-10 of the largest weight
+__device__ __forceinline__ int range_exp(float wmax) {
+  if (!(wmax > 0.f)) return 0;
+  int e;
+  frexpf(wmax, &e);  // wmax < 2^e
+  return -e;
+}
+
+// lanes l and l ^ 1 exchange a value (DPP quad permutation [1, 0, 3, 2])
+__device__ __forceinline__ float swap_pair(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+}
+
+// Buffer resources: a wave-uniform base in SGPRs plus a 32-bit lane offset keeps
+// the hot loop free of 64-bit VGPR address arithmetic (raw buffer, 32-bit data).
+typedef __amdgpu_buffer_rsrc_t buf_t;
+__device__ __forceinline__ buf_t make_buf(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ unsigned ld32(buf_t r, unsigned voff, unsigned soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint2 ld64(buf_t r, unsigned voff, unsigned soff) {
+  typedef unsigned u2 __attribute__((ext_vector_type(2)));
+  const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return uint2{v.x, v.y};
+}
+__device__ __forceinline__ uint4 ld128(buf_t r, unsigned voff, unsigned soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return uint4{v.x, v.y, v.z, v.w};
+}
+
 // ------------------------------- dispatch helpers -------------------------------
 template <typename F>
 tq_status dispatch_dim(int d, F&& f) {

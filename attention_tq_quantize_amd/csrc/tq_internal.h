@@ -76,6 +76,16 @@ struct QuantizeLaunch {
 tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream);
 // d > 256 (tq_large.hip): vector layout only
 tq_status launch_quantize_large(const QuantizeLaunch& a, hipStream_t stream);
+// MFMA scoring of a packed database (tq_large.hip). Workspace: fragments
+// [groups][nf][64] u32x4, constants [groups][48] f32, Pi y and S y [groups*8][d] f32.
+struct SearchPlan {
+  int nf = 0;  // fragments per query group
+  size_t frag_off = 0, const_off = 0, qp_off = 0, qq_off = 0, total = 0;
+};
+tq_status search_plan(const tq_quantizer* q, int64_t m, SearchPlan* plan);
+tq_status launch_search(const tq_quantizer* q, const float* y, int64_t m, const uint8_t* codes,
+                        const uint8_t* signs, const float* norms, const float* rnorms, int64_t n, float* out,
+                        void* workspace, hipStream_t stream);
 tq_status launch_inner_products_large(const tq_quantizer* q, const float* y, int64_t m,
                                       const uint8_t* codes, const uint8_t* signs, const float* norms,
                                       const float* rnorms, int64_t n, float* out, hipStream_t stream);

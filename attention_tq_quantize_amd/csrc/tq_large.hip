@@ -232,7 +232,422 @@ __global__ __launch_bounds__(kThreads) void inner_products_large_kernel(LargeIpP
   }
 }
 
+
+// ===========================================================================
+// Scoring on the matrix cores (tq_search_scores): the key-side contraction of
+// the decode kernel applied to a database. For a group of 8 queries the 16
+// MFMA columns hold each query's rotated vector (hi, lo fp16 parts, one
+// exponent per query); the records' bit planes are the other operand (shifted
+// onto fp16 bits 8-11 and masked, bit_operand). With sigma = 2 bit - 1 and the
+// odd Walsh expansion c[idx] = sum_s a_s prod_{i in s} sigma_i, a product over
+// an odd subset being 2 xor(bits) - 1,
+//   <y, x~> = |x| (sum_s 2 a_s <Pi y, xor_s> - (sum_s a_s) sum_j (Pi y)_j
+//                  + |r| sqrt(pi/2)/d (2 <S y, z> - sum_j (S y)_j)),
+// so a record is scored with (odd subsets + 1 sign plane) x d/32 MFMAs per
+// 16 records and 16 columns, without unpacking.
+// Coordinates: 32-bit word u of a plane holds coordinates 32u .. 32u+31 (LSB
+// first); lane quarter g reads the words u = 4w + g, w < d/128, so the four
+// quarters of a record read 16 contiguous bytes. Within the word, bit
+// 16 half + 4 r + k is MFMA k-slot 2k + half of step r.
+// Fragments: [query group][4 W + r][64 lanes] u32x4, W = s (d/128) + w for
+// Walsh subset s (then the sign words, s = number of subsets).
+// ===========================================================================
+constexpr int kSearchConsts = 48;     // per query group: [0,16) mse init, [16,32) qjl init, [32,48) 2^(10-E)
+constexpr int kSearchMaxFragKB = 144;  // LDS for one coordinate slice's fragments
+constexpr int kSearchThreads = 512;
+
+constexpr int kProjRows = 16;  // rows of Pi (or S) per projection workgroup
+
+struct SearchProjParams {
+  const float* y;
+  int64_t m;
+  int d;
+  const float* pi;
+  const float* s;
+  float* qp;  // [groups * 8][d]: Pi y
+  float* qq;  // [groups * 8][d]: S y
+};
+
+// grid (d / kProjRows, query groups, 1 + qjl): rows [i0, i0 + kProjRows) of Pi
+// (z = 0) or S (z = 1) times the group's 8 queries, so each matrix is read once
+// per query group, spread over the chip
+__global__ __launch_bounds__(kThreads) void search_project_kernel(SearchProjParams prm) {
+  extern __shared__ float4 ylds[];  // [8][d / 4]
+  const int d = prm.d, d4 = d / 4;
+  const int64_t qg = blockIdx.y;
+  const int nq = (int)min((int64_t)8, prm.m - 8 * qg);
+  for (int e = threadIdx.x; e < 8 * d4; e += kThreads) {
+    const int h = e / d4, j = e % d4;
+    ylds[e] = h < nq ? ((const float4*)(prm.y + (qg * 8 + h) * d))[j] : float4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+  const float* M = blockIdx.z ? prm.s : prm.pi;
+  float* out = blockIdx.z ? prm.qq : prm.qp;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int ri = wave; ri < kProjRows; ri += kThreads / 64) {
+    const int i = blockIdx.x * kProjRows + ri;
+    const float4* row = (const float4*)(M + (int64_t)i * d);
+    float acc[8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) acc[h] = 0.f;
+    for (int j = lane; j < d4; j += 64) {
+      const float4 pv = row[j];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const float4 yv = ylds[h * d4 + j];
+        acc[h] = fmaf(pv.x, yv.x, fmaf(pv.y, yv.y, fmaf(pv.z, yv.z, fmaf(pv.w, yv.w, acc[h]))));
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) acc[h] += __shfl_xor(acc[h], o);
+      if (lane == h && h < nq) out[(qg * 8 + h) * d + i] = acc[h];
+    }
+  }
+}
+
+struct SearchPrepParams {
+  int64_t m;
+  int d, wk, wpp;
+  bool qjl;
+  const float* qp;
+  const float* qq;
+  u32x4* frag;
+  float* consts;
+  int nf;
+  float kappa;
+  float kcoef[8];
+};
+
+// one workgroup per query: from q' = Pi y and q'' = S y, the query's fragment columns and constants
+__global__ __launch_bounds__(kThreads) void search_prep_kernel(SearchPrepParams prm) {
+  extern __shared__ float lds[];  // qp[d], qq[d]
+  __shared__ float red[4][kThreads / 64];
+  const int d = prm.d;
+  float* qp = lds;
+  float* qq = lds + d;
+  const int64_t qi = blockIdx.x;
+  const int64_t qg = qi / 8;
+  const int h = (int)(qi % 8);
+  const int nq = (int)min((int64_t)8, prm.m - 8 * qg);
+  for (int j = threadIdx.x; j < d; j += kThreads) {
+    qp[j] = prm.qp[qi * d + j];
+    if (prm.qjl) qq[j] = prm.qq[qi * d + j];
+  }
+  __syncthreads();
+  float sp = 0.f, sq = 0.f, mp = 0.f, mq = 0.f;
+  for (int j = threadIdx.x; j < d; j += kThreads) {
+    sp += qp[j];
+    mp = fmaxf(mp, fabsf(qp[j]));
+    if (prm.qjl) {
+      sq += qq[j];
+      mq = fmaxf(mq, fabsf(qq[j]));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    sp += __shfl_xor(sp, o);
+    sq += __shfl_xor(sq, o);
+    mp = fmaxf(mp, __shfl_xor(mp, o));
+    mq = fmaxf(mq, __shfl_xor(mq, o));
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][wave] = sp;
+    red[1][wave] = sq;
+    red[2][wave] = mp;
+    red[3][wave] = mq;
+  }
+  __syncthreads();
+  float sum_p = 0.f, sum_q = 0.f, max_p = 0.f, max_q = 0.f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    sum_p += red[0][w];
+    sum_q += red[1][w];
+    max_p = fmaxf(max_p, red[2][w]);
+    max_q = fmaxf(max_q, red[3][w]);
+  }
+  float amax = 0.f, asum = 0.f;
+  for (int s = 0; s < prm.wk; ++s) {
+    amax = fmaxf(amax, fabsf(prm.kcoef[s]));
+    asum += prm.kcoef[s];
+  }
+  // one exponent for both terms: every fragment entry |v| 2^E < 1
+  const int E = range_exp(fmaxf(2.f * amax * max_p, prm.qjl ? 2.f * prm.kappa * max_q : 0.f));
+  float* cst = prm.consts + qg * kSearchConsts;
+  if (threadIdx.x < 2) {
+    const int row = 2 * h + threadIdx.x;  // hi column carries the constant, lo column 0
+    cst[row] = threadIdx.x == 0 ? -asum * sum_p * ldexpf(1.0f, E - 10) : 0.f;
+    cst[16 + row] = threadIdx.x == 0 && prm.qjl ? -prm.kappa * sum_q * ldexpf(1.0f, E - 10) : 0.f;
+    cst[32 + row] = ldexpf(1.0f, 10 - E);
+  }
+  // the group's first query also fills the columns of absent queries (partial last group)
+  if (h == 0 && nq < 8 && threadIdx.x >= 2 * nq && threadIdx.x < 16) {
+    cst[threadIdx.x] = 0.f;
+    cst[16 + threadIdx.x] = 0.f;
+    cst[32 + threadIdx.x] = 1.f;
+  }
+  const int nwm = prm.wk * prm.wpp;
+  u32x4* frag = prm.frag + qg * (int64_t)prm.nf * 64;
+  for (int e = threadIdx.x; e < prm.nf * 8; e += kThreads) {
+    const int f = e / 8, g = (e / 2) % 4, lo = e % 2;
+    const int W = f / 4, r = f % 4;
+    const int lane = 16 * g + 2 * h + lo;
+    unsigned hv[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int k = it / 2, half = it % 2;
+      const int beta = 16 * half + 4 * r + k;  // bit of the lane's word
+      float val;
+      if (W < nwm) {
+        const int sub = W / prm.wpp, w = W % prm.wpp;
+        val = 2.f * prm.kcoef[sub] * qp[32 * (4 * w + g) + beta];
+      } else {
+        const int w = W - nwm;
+        val = 2.f * prm.kappa * qq[32 * (4 * w + g) + beta];
+      }
+      // the bit reads as 2^(operand_pos(k) - 24); raw scores come out x 2^(E - 10)
+      val *= ldexpf(1.0f, E + 14 - operand_pos(k));
+      hv[it] = f16_part(val, lo);
+    }
+    frag[(int64_t)f * 64 + lane] =
+        u32x4{pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]), pack2(hv[6], hv[7])};
+  }
+  if (h == 0 && nq < 8)
+    for (int e = threadIdx.x; e < prm.nf * 64; e += kThreads)
+      if ((e % 16) >= 2 * nq) frag[e] = u32x4{0u, 0u, 0u, 0u};
+}
+
+struct SearchParams {
+  const u32x4* frag;
+  const float* consts;
+  const uint8_t* codes;
+  const uint8_t* signs;
+  const float* norms;
+  const float* rnorms;
+  float* out;
+  int64_t n, m;
+  int d, wpp, nf;
+  int w0, ws;  // this launch scores word groups [w0, w0 + ws) of every record
+  bool first;  // first slice: starts from the constants and writes (later slices add)
+};
+
+// Persistent workgroups of 8 waves; the slice's fragments sit in LDS; a wave
+// scores 32 records (two 16-record tiles) per step for one group of 8 queries.
+template <int PK, bool QJL>
+__global__ __launch_bounds__(kSearchThreads, 1) void search_score_kernel(SearchParams prm) {
+  extern __shared__ u32x4 sfrag[];
+  constexpr int WK = n_walsh(PK);
+  constexpr int NS = WK + (QJL ? 1 : 0);  // operand kinds per word: Walsh subsets, then signs
+  constexpr int NW = kSearchThreads / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t qg = blockIdx.y;
+  const int d = prm.d, wpp = prm.wpp, w0 = prm.w0, ws = prm.ws;
+  {
+    // local fragment 4 (s ws + w - w0) + r <- global 4 (s wpp + w) + r
+    const u32x4* src = prm.frag + qg * (int64_t)prm.nf * 64;
+    for (int e = threadIdx.x; e < NS * ws * 4 * 64; e += kSearchThreads) {
+      const int fl = e / 64, ln = e % 64;
+      const int Wl = fl / 4, r = fl % 4;
+      const int W = (Wl / ws) * wpp + w0 + Wl % ws;
+      sfrag[e] = src[(int64_t)(4 * W + r) * 64 + ln];
+    }
+  }
+  __syncthreads();
+  const float* cst = prm.consts + qg * kSearchConsts;
+  const float cm0 = prm.first ? cst[r16] : 0.f;
+  const float cq0 = prm.first ? cst[16 + r16] : 0.f;
+  const float isc = cst[32 + r16];
+  const int nq = (int)min((int64_t)8, prm.m - 8 * qg);
+  const int h = r16 >> 1;
+  const bool writer = !(r16 & 1) && h < nq;
+  const int plane_bytes = d / 8;
+  const int64_t n = prm.n;
+  const int64_t steps = (n + 31) / 32;
+  for (int64_t step = (int64_t)blockIdx.x * NW + wave; step < steps; step += (int64_t)gridDim.x * NW) {
+    const int64_t v0 = step * 32;
+    f32x4 cm[2], cq[2];
+    const uint8_t* crec[2];
+    const uint8_t* srec[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      cm[t] = f32x4{cm0, cm0, cm0, cm0};
+      cq[t] = f32x4{cq0, cq0, cq0, cq0};
+      const int64_t v = min(v0 + 16 * t + r16, n - 1);  // rows past the end repeat the last record
+      crec[t] = prm.codes + v * (PK * plane_bytes) + 4 * g;
+      srec[t] = QJL ? prm.signs + v * plane_bytes + 4 * g : nullptr;
+    }
+    for (int wl = 0; wl < ws; ++wl) {
+      const int off = 16 * (w0 + wl);
+      unsigned pw[2][PK > 0 ? PK : 1], sw[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int p = 0; p < PK; ++p) pw[t][p] = *(const unsigned*)(crec[t] + p * plane_bytes + off);
+        if constexpr (QJL) sw[t] = *(const unsigned*)(srec[t] + off);
+      }
+#pragma unroll
+      for (int sub = 0; sub < NS; ++sub) {
+        unsigned word[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          if (sub < WK) {
+            unsigned x = 0u;
+#pragma unroll
+            for (int p = 0; p < PK; ++p)
+              if (walsh_mask(PK, sub) >> p & 1) x ^= pw[t][p];
+            word[t] = x;
+          } else {
+            word[t] = sw[t];
+          }
+        }
+        const u32x4* fb = sfrag + 4 * (sub * ws + wl) * 64 + lane;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const u32x4 bf = fb[r * 64];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            if (sub < WK)
+              cm[t] = mfma16(bit_operand(word[t], r), bf, cm[t]);
+            else
+              cq[t] = mfma16(bit_operand(word[t], r), bf, cq[t]);
+          }
+        }
+      }
+    }
+    // lane (column r16, quarter g) holds rows 4 g + i: records v0 + 16 t + 4 g + i
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float cmv[4] = {cm[t].x, cm[t].y, cm[t].z, cm[t].w};
+      const float cqv[4] = {cq[t].x, cq[t].y, cq[t].z, cq[t].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = cmv[i] + swap_pair(cmv[i]);  // hi + lo columns
+        const float b = QJL ? cqv[i] + swap_pair(cqv[i]) : 0.f;
+        const int64_t v = v0 + 16 * t + 4 * g + i;
+        if (writer && v < n) {
+          const float gam = QJL ? prm.rnorms[v] : 0.f;
+          const float sc = prm.norms[v] * fmaf(gam, b, a) * isc;
+          float* o = prm.out + (qg * 8 + h) * n + v;
+          *o = prm.first ? sc : *o + sc;
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
+
+tq_status search_plan(const tq_quantizer* q, int64_t m, SearchPlan* pl) {
+  const int d = q->d;
+  if (d % 128 || d < 128 || d > 4096) return set_error(TQ_ERR_UNSUPPORTED, "search: d must be a multiple of 128 in [128, 4096]");
+  const bool qjl = q->variant == TQ_PROD;
+  const int pk = q->planes;
+  if (pk > 4 || (!qjl && pk == 0)) return set_error(TQ_ERR_UNSUPPORTED, "search: planes");
+  const int wk = pk > 0 ? 1 << (pk - 1) : 0;
+  const int wpp = d / 128;
+  pl->nf = 4 * (wk + (qjl ? 1 : 0)) * wpp;
+  const size_t groups = (size_t)((m + 7) / 8);
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  pl->frag_off = 0;
+  pl->const_off = up(groups * (size_t)pl->nf * 64 * sizeof(u32x4));
+  pl->qp_off = pl->const_off + up(groups * kSearchConsts * sizeof(float));
+  pl->qq_off = pl->qp_off + up(groups * 8 * (size_t)d * sizeof(float));
+  pl->total = pl->qq_off + (qjl ? up(groups * 8 * (size_t)d * sizeof(float)) : 0);
+  return TQ_OK;
+}
+
+tq_status launch_search(const tq_quantizer* q, const float* y, int64_t m, const uint8_t* codes, const uint8_t* signs,
+                        const float* norms, const float* rnorms, int64_t n, float* out, void* workspace,
+                        hipStream_t stream) {
+  SearchPlan pl;
+  tq_status st = search_plan(q, m, &pl);
+  if (st != TQ_OK) return st;
+  const int d = q->d, pk = q->planes, wpp = d / 128, nf = pl.nf;
+  const bool qjl = q->variant == TQ_PROD;
+  const int wk = pk > 0 ? 1 << (pk - 1) : 0;
+  char* base = (char*)workspace;
+  u32x4* frag = (u32x4*)(base + pl.frag_off);
+  float* consts = (float*)(base + pl.const_off);
+  float* qp = (float*)(base + pl.qp_off);
+  float* qq = qjl ? (float*)(base + pl.qq_off) : nullptr;
+  const int64_t groups = (m + 7) / 8;
+  {
+    SearchProjParams pj{y, m, d, q->pi32, q->s32, qp, qq};
+    const size_t lds = (size_t)8 * d * sizeof(float);
+    hipError_t e = hipFuncSetAttribute((const void*)search_project_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return check_hip(e, "search: set LDS size");
+    hipLaunchKernelGGL(search_project_kernel, dim3((unsigned)(d / kProjRows), (unsigned)groups, qjl ? 2u : 1u),
+                       dim3(kThreads), lds, stream, pj);
+    st = launch_check("search: projection launch");
+    if (st != TQ_OK) return st;
+  }
+  SearchPrepParams pp{};
+  pp.m = m;
+  pp.d = d;
+  pp.wk = wk;
+  pp.wpp = wpp;
+  pp.qjl = qjl;
+  pp.qp = qp;
+  pp.qq = qq;
+  pp.frag = frag;
+  pp.consts = consts;
+  pp.nf = nf;
+  pp.kappa = (float)(std::sqrt(M_PI / 2.0) / d);
+  for (int s = 0; s < wk; ++s) pp.kcoef[s] = q->cb.walsh_coef[s];
+  hipLaunchKernelGGL(search_prep_kernel, dim3((unsigned)m), dim3(kThreads), (size_t)2 * d * sizeof(float), stream, pp);
+  st = launch_check("search: prep launch");
+  if (st != TQ_OK) return st;
+  // coordinate slices whose fragments fit the LDS budget
+  const int per_word = 4 * (wk + (qjl ? 1 : 0));  // fragments per word index
+  int ws = (kSearchMaxFragKB * 1024) / (per_word * 64 * (int)sizeof(u32x4));
+  if (ws > wpp) ws = wpp;
+  if (ws < 1) return set_error(TQ_ERR_UNSUPPORTED, "search: fragments exceed the LDS budget");
+  SearchParams sp{};
+  sp.frag = frag;
+  sp.consts = consts;
+  sp.codes = codes;
+  sp.signs = signs;
+  sp.norms = norms;
+  sp.rnorms = rnorms;
+  sp.out = out;
+  sp.n = n;
+  sp.m = m;
+  sp.d = d;
+  sp.wpp = wpp;
+  sp.nf = nf;
+  const int64_t steps = (n + 31) / 32;
+  int64_t gx = (device_cus() + groups - 1) / groups;
+  const int64_t cap = (steps + kSearchThreads / 64 - 1) / (kSearchThreads / 64);
+  if (gx > cap) gx = cap;
+  if (gx < 1) gx = 1;
+  for (int w0 = 0; w0 < wpp; w0 += ws) {
+    sp.w0 = w0;
+    sp.ws = min(ws, wpp - w0);
+    sp.first = w0 == 0;
+    const size_t lds = (size_t)per_word * sp.ws * 64 * sizeof(u32x4);
+    st = dispatch_planes(pk, [&](auto PC) -> tq_status {
+      constexpr int PK = decltype(PC)::value;
+      return dispatch_bool(qjl, [&](auto QC) -> tq_status {
+        constexpr bool QJL = decltype(QC)::value;
+        if constexpr (!QJL && PK == 0) {
+          return set_error(TQ_ERR_UNSUPPORTED, "search: planes");
+        } else {
+          auto kern = search_score_kernel<PK, QJL>;
+          hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+          if (e != hipSuccess) return check_hip(e, "search: set LDS size");
+          hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)groups), dim3(kSearchThreads), lds, stream, sp);
+          return launch_check("search: score launch");
+        }
+      });
+    });
+    if (st != TQ_OK) return st;
+  }
+  return TQ_OK;
+}
 
 tq_status launch_quantize_large(const QuantizeLaunch& a, hipStream_t stream) {
   const tq_quantizer* q0 = a.qz[0];

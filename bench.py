@@ -169,7 +169,8 @@ def cpu_baseline(syn):
 def vector_search(tq, syn, torch, dev, n=100000, m=16, bits=3):
     """Vector-search workload: index n synthetic Gaussian embeddings with
     TurboQuant_prod (b = 3) at d = 1536 and 3072, then score m queries against
-    the packed database with tq_inner_products."""
+    the packed database with tq_inner_products (fp32 vector units) and with
+    tq_search_scores (matrix cores)."""
     import numpy as np
     out = {}
     for d in (1536, 3072):
@@ -198,11 +199,23 @@ def vector_search(tq, syn, torch, dev, n=100000, m=16, bits=3):
         e1.record()
         torch.cuda.synchronize()
         score_ms = e0.elapsed_time(e1) / 10
+        ws = torch.empty(tq.search_workspace_size(qz, m), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            tq.search_scores(*args, workspace=ws)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            tq.search_scores(*args, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        mfma_ms = e0.elapsed_time(e1) / 10
         rec_bytes = (bits - 1) * d // 8 + d // 8 + 8
         out[f"d{d}"] = {"database": n, "queries": m, "variant": f"prod b={bits}",
                         "index_ms": round(index_ms, 3), "index_mvec_s": round(n / (index_ms * 1e-3) / 1e6, 2),
                         "score_ms": round(score_ms, 3), "pairs_per_s": round(m * n / (score_ms * 1e-3), 1),
-                        "score_record_gb_s": round(m * n * rec_bytes / (score_ms * 1e-3) / 1e9, 1)}
+                        "score_record_gb_s": round(m * n * rec_bytes / (score_ms * 1e-3) / 1e9, 1),
+                        "mfma_score_ms": round(mfma_ms, 3), "mfma_pairs_per_s": round(m * n / (mfma_ms * 1e-3), 1),
+                        "mfma_database_gb_s": round(n * rec_bytes / (mfma_ms * 1e-3) / 1e9, 1)}
         del rec, qz
     return out
 

@@ -99,8 +99,8 @@ tq_status tq_codebook_build(int d, int bits, float* centroids, float* thresholds
  *               MSE stage plus 1 QJL bit). d in {64, 128, 256} for every call;
  *               d a multiple of 64 in (256, 4096] (vector search, [NIK]
  *               "Experiments": d = 1536, 3072) for tq_quantize in the VECTOR
- *               layout and tq_inner_products only (others return
- *               TQ_ERR_UNSUPPORTED). Orthogonality is checked exactly for
+ *               layout, tq_inner_products and tq_search_scores (d a multiple
+ *               of 128 there) only (others return TQ_ERR_UNSUPPORTED). Orthogonality is checked exactly for
  *               d <= 256 and on four fixed pseudo-random vectors above.
  *   pi        : host, float64 [d][d] row-major, orthogonal (y = Pi u).
  *   s         : host, float64 [d][d] row-major Gaussian QJL matrix; required
@@ -192,6 +192,28 @@ tq_status tq_dequantize(const tq_quantizer* q, tq_layout layout, const uint8_t* 
 tq_status tq_inner_products(const tq_quantizer* q, const float* y, int64_t m,
                             const uint8_t* codes, const uint8_t* signs, const float* norms,
                             const float* rnorms, int64_t n, float* out, void* stream);
+
+/*
+ * Vector-search scoring on the matrix cores: the same inner products
+ * <y_i, x~_j> as tq_inner_products ([NIK] "Experiments": nearest-neighbour
+ * search over quantized embeddings), from a VECTOR-layout database, computed
+ * as MFMA contractions of the queries' rotated (and, for prod, S-projected)
+ * vectors with the records' bit planes, through the odd Walsh expansion of the
+ * symmetric codebook. Supports d a multiple of 128 in [128, 4096] and up to 4
+ * MSE-stage planes; other quantizers return TQ_ERR_UNSUPPORTED.
+ *   y, m, codes, signs, norms, rnorms, n, out : as for tq_inner_products
+ *               (out: device float32 [m][n], overwritten); y 16-byte aligned.
+ *   workspace : device scratch of at least tq_search_workspace_size(q, m)
+ *               bytes (per-query operands); concurrent calls need separate
+ *               workspaces.
+ * Errors: TQ_ERR_INVALID_ARG (NULL handle or buffer, negative size, y not
+ * 16-byte aligned), TQ_ERR_WORKSPACE (workspace missing or too small), TQ_ERR_UNSUPPORTED
+ * (d, planes, m > 65535 or n > 2^31). m == 0 or n == 0 is a no-op.
+ */
+tq_status tq_search_workspace_size(const tq_quantizer* q, int64_t m, size_t* bytes);
+tq_status tq_search_scores(const tq_quantizer* q, const float* y, int64_t m, const uint8_t* codes,
+                           const uint8_t* signs, const float* norms, const float* rnorms, int64_t n,
+                           float* out, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Decode attention over a packed KV cache ([NIK] problem statement: the new

@@ -140,3 +140,9 @@ def test_append_argument_errors(lib):
     kv = tq.PackedKV(None, None, None, None, None)
     assert lib.tq_decode_append_workspace_size(ctypes.byref(shape), ctypes.byref(kv), ctypes.byref(kv),
                                                ctypes.byref(nb)) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_search_argument_errors(lib):
+    nb = ctypes.c_size_t(0)
+    assert lib.tq_search_workspace_size(None, 8, ctypes.byref(nb)) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_search_scores(None, None, 1, None, None, None, None, 1, None, None, 0, None) == tq.TQ_ERR_INVALID_ARG
