@@ -250,6 +250,15 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
   q->pi32 = (const float*)(base + off_pi32);
   q->s32 = prod ? (const float*)(base + off_s32) : nullptr;
   q->sp32 = prod && !large ? (const float*)(base + off_sp32) : nullptr;
+  if (large) {
+    hs = build_large_tables(q);
+    if (hs != TQ_OK) {
+      if (q->lq_block) (void)hipFree(q->lq_block);
+      (void)hipFree(q->dev_block);
+      delete q;
+      return hs;
+    }
+  }
   *out = q;
   g_last_error.clear();
   return TQ_OK;
@@ -286,6 +295,10 @@ tq_status tq_quantizer_destroy(tq_quantizer* q) {
   if (!q) return set_error(TQ_ERR_INVALID_ARG, "destroy: handle is NULL");
   tq_status st = TQ_OK;
   if (q->dev_block) st = check_hip(hipFree(q->dev_block), "destroy: hipFree");
+  if (q->lq_block) {
+    tq_status s2 = check_hip(hipFree(q->lq_block), "destroy: hipFree");
+    if (st == TQ_OK) st = s2;
+  }
   delete q;
   return st;
 }

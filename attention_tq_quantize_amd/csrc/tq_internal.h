@@ -48,6 +48,11 @@ struct tq_quantizer {
   const float* pi32 = nullptr;
   const float* s32 = nullptr;
   const float* sp32 = nullptr;
+  // d a multiple of 128 above 256: fragment-ordered bf16 hi/lo Pi and S' = S Pi^T
+  // for the GEMM quantize kernels (own allocation)
+  void* lq_block = nullptr;
+  const void* lq_pi = nullptr;
+  const void* lq_sp = nullptr;
 };
 
 namespace tq {
@@ -76,6 +81,9 @@ struct QuantizeLaunch {
 tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream);
 // d > 256 (tq_large.hip): vector layout only
 tq_status launch_quantize_large(const QuantizeLaunch& a, hipStream_t stream);
+// d a multiple of 128 in (256, 4096]: the GEMM quantize tables, built at creation
+bool lq_supported(int d);
+tq_status build_large_tables(tq_quantizer* q);
 // MFMA scoring of a packed database (tq_large.hip). Workspace: fragments
 // [groups][nf][64] u32x4, constants [groups][48] f32, Pi y and S y [groups*8][d] f32.
 struct SearchPlan {

@@ -649,9 +649,405 @@ tq_status launch_search(const tq_quantizer* q, const float* y, int64_t m, const 
   return TQ_OK;
 }
 
+namespace {
+
+// ===========================================================================
+// Quantize on the matrix cores for d a multiple of 128 (the indexing half of
+// vector search). The rotation y = Pi u over a batch of vectors is a dense
+// GEMM: a workgroup computes 128 coordinates x 256 vectors, Pi (and S' = S
+// Pi^T for the QJL stage) as bf16 hi/lo fragments, fp32 inputs split into
+// bf16 hi/lo when staged through LDS (hi*hi + lo*hi + hi*lo, ~16 significant
+// bits per operand, fp32 accumulation). The matrix rows are ordered so that
+// lane quarter g of the MFMA output owns coordinates 32 g .. 32 g + 31 of
+// the block: every plane's 32-bit word is built in one lane's registers.
+// The norm is accumulated in fp64 while the input is staged. prod runs a
+// second GEMM, p = S' e, over the fp32 residuals e = y - c[idx] of the first
+// (stream-ordered scratch); its staging accumulates |e|^2.
+// ===========================================================================
+constexpr int kLqCoords = 128;                           // coordinates per workgroup
+constexpr int kLqWaves = 4;
+constexpr int kLqTiles = 4;                              // 16-vector tiles per wave
+constexpr int kLqVecs = kLqWaves * kLqTiles * 16;        // vectors per workgroup (256)
+constexpr int kLqThreads = kLqWaves * 64;
+constexpr int kLqMatFrag = 8 * 2 * 64;                   // u32x4 per k-step of a coordinate block (16 KB)
+constexpr int kLqVecFrag = kLqVecs / 16 * 2 * 64;        // u32x4 per k-step of a vector block (32 KB)
+static_assert(kLqVecs == kLqThreads, "one staged vector per thread");
+
+struct LqParams {
+  const void* x;          // MODE 0: inputs; MODE 1: residuals (fp32)
+  int64_t xg0, xgs, xoff; // input row of vector v of group grp: (grp + xg0) * xgs + v - xoff
+  int64_t n_per_group;    // outputs: row (group_base + grp) * n_per_group + v
+  int64_t group_base;
+  int64_t v_begin, v_end; // vectors of this launch, in every group
+  int d;
+  float* resid;           // MODE 0 prod: residual out, row grp * cap + v - v_begin
+  int64_t cap;
+  uint8_t* codes;
+  uint8_t* signs;
+  float* norms;
+  float* rnorms;
+  float* rot_dbg;
+  float* proj_dbg;
+  float thr[15];
+  float cen[16];
+  const u32x4* mat[kMaxGroupsPerLaunch];  // fragment-ordered Pi (MODE 0) or S' (MODE 1)
+};
+
+__device__ __forceinline__ float opaque_f(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+template <int P, int MODE, bool XF32, bool PROD>
+__global__ __launch_bounds__(kLqThreads, 2) void lq_kernel(LqParams prm) {
+  extern __shared__ u32x4 lq_lds[];  // matrix fragments [kLqMatFrag], vector fragments [kLqVecFrag]
+  __shared__ float vsc[kLqVecs];     // per staged vector: 1/|x| (MODE 0) or |e| (MODE 1)
+  constexpr int XB = XF32 ? 4 : 2;   // input bytes per element
+  constexpr int XR = XF32 ? 8 : 4;   // u32x4 per 32 staged elements
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int d = prm.d, NKS = d / 32, NCB = d / kLqCoords;
+  // XCD-aware order: consecutive workgroup ids go to different XCDs, so give each
+  // XCD a contiguous range of (vector block, coordinate block) pairs with the
+  // coordinate block fastest: the blocks of one vector block share its inputs in L2
+  const int64_t total = (int64_t)gridDim.x, total8 = total & ~(int64_t)7;
+  int64_t L = blockIdx.x;
+  if (L < total8) L = (L & 7) * (total8 >> 3) + (L >> 3);
+  const int cb = (int)(L % NCB);
+  const int64_t v0 = prm.v_begin + (L / NCB) * kLqVecs;
+  const int grp = blockIdx.y;
+  // staging: thread tid brings in vector v0 + tid (clamped to the last one)
+  const int64_t sv = min(v0 + tid, prm.v_end - 1);
+  const uint8_t* xsrc = (const uint8_t*)prm.x + ((grp + prm.xg0) * prm.xgs + sv - prm.xoff) * (int64_t)d * XB;
+  const u32x4* msrc = prm.mat[grp] + (int64_t)cb * NKS * kLqMatFrag;
+  u32x4* ldsm = lq_lds;
+  u32x4* ldsx = lq_lds + kLqMatFrag;
+  const int tv = tid >> 4, rv = tid & 15;  // the staged vector's tile and row
+  u32x4 xr[XR], mr[kLqMatFrag / kLqThreads];
+  auto gload = [&](int ks) {
+    const u32x4* xs = (const u32x4*)(xsrc + (int64_t)ks * 32 * XB);
+#pragma unroll
+    for (int j = 0; j < XR; ++j) xr[j] = xs[j];
+    const u32x4* ms = msrc + (int64_t)ks * kLqMatFrag;
+#pragma unroll
+    for (int j = 0; j < kLqMatFrag / kLqThreads; ++j) mr[j] = ms[tid + kLqThreads * j];
+  };
+  double ss = 0.0;
+  auto lstore = [&]() {
+#pragma unroll
+    for (int j = 0; j < kLqMatFrag / kLqThreads; ++j) ldsm[tid + kLqThreads * j] = mr[j];
+#pragma unroll
+    for (int sg = 0; sg < 4; ++sg) {  // 8 elements of K segment sg -> lane 16 sg + rv
+      if constexpr (XF32) {
+        const u32x4 u0 = xr[2 * sg], u1 = xr[2 * sg + 1];
+        const float f[8] = {__uint_as_float(u0.x), __uint_as_float(u0.y), __uint_as_float(u0.z), __uint_as_float(u0.w),
+                            __uint_as_float(u1.x), __uint_as_float(u1.y), __uint_as_float(u1.z), __uint_as_float(u1.w)};
+        unsigned h[8], l[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          h[e] = bf16_part(f[e], false);
+          l[e] = bf16_part(f[e], true);
+          ss = fma((double)f[e], (double)f[e], ss);
+        }
+        ldsx[(tv * 2) * 64 + 16 * sg + rv] = u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+        ldsx[(tv * 2 + 1) * 64 + 16 * sg + rv] = u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
+      } else {
+        const u32x4 v = xr[sg];
+        const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = bf16_val(w[e] & 0xFFFFu), b = bf16_val(w[e] >> 16);
+          ss = fma((double)a, (double)a, ss);
+          ss = fma((double)b, (double)b, ss);
+        }
+        ldsx[(tv * 2) * 64 + 16 * sg + rv] = v;
+      }
+    }
+  };
+  f32x4 acc[8][kLqTiles];
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+#pragma unroll
+    for (int t = 0; t < kLqTiles; ++t) acc[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gload(0);
+  for (int ks = 0; ks < NKS; ++ks) {
+    __syncthreads();  // the previous step's fragments are consumed
+    lstore();
+    __syncthreads();
+    gload(min(ks + 1, NKS - 1));  // next step in flight during this step's MFMAs
+    u32x4 xh[kLqTiles], xl[kLqTiles];
+#pragma unroll
+    for (int t = 0; t < kLqTiles; ++t) {
+      xh[t] = ldsx[((wave * kLqTiles + t) * 2) * 64 + lane];
+      if constexpr (XF32) xl[t] = ldsx[((wave * kLqTiles + t) * 2 + 1) * 64 + lane];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const u32x4 ph = ldsm[(q * 2) * 64 + lane], pl = ldsm[(q * 2 + 1) * 64 + lane];
+#pragma unroll
+      for (int t = 0; t < kLqTiles; ++t) {
+        acc[q][t] = mfma(ph, xh[t], acc[q][t]);
+        acc[q][t] = mfma(pl, xh[t], acc[q][t]);
+        if constexpr (XF32) acc[q][t] = mfma(ph, xl[t], acc[q][t]);
+      }
+    }
+  }
+  // per-vector scale from the staging thread's sum of squares
+  {
+    const double nrm = sqrt(ss);
+    const int64_t v = v0 + tid;
+    const int64_t orow = (prm.group_base + grp) * prm.n_per_group + v;
+    if constexpr (MODE == 0) {
+      vsc[tid] = nrm > 0.0 ? (float)(1.0 / nrm) : 0.f;
+      if (cb == 0 && v < prm.v_end) prm.norms[orow] = (float)nrm;
+    } else {
+      vsc[tid] = (float)nrm;
+      if (cb == 0 && v < prm.v_end) prm.rnorms[orow] = prm.norms[orow] > 0.f ? (float)nrm : 0.f;
+    }
+  }
+  __syncthreads();
+  constexpr int NT = P > 0 ? (1 << P) - 1 : 1;
+  float thr[NT], cen[1 << (P > 0 ? P : 0)];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) thr[i] = opaque_f(prm.thr[i]);
+#pragma unroll
+  for (int i = 0; i < (1 << (P > 0 ? P : 0)); ++i) cen[i] = opaque_f(prm.cen[i]);
+  const int c0 = kLqCoords * cb + 32 * g;  // this lane's 32 coordinates
+#pragma unroll
+  for (int t = 0; t < kLqTiles; ++t) {
+    const int vl = wave * (16 * kLqTiles) + 16 * t + r16;
+    const int64_t v = v0 + vl;
+    if (v >= prm.v_end) continue;
+    const int64_t orow = (prm.group_base + grp) * prm.n_per_group + v;
+    if constexpr (MODE == 0) {
+      const float inv = vsc[vl];
+      const bool valid = inv > 0.f;
+      unsigned w[P > 0 ? P : 1];
+#pragma unroll
+      for (int p = 0; p < P; ++p) w[p] = 0u;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float y[4] = {acc[q][t].x * inv, acc[q][t].y * inv, acc[q][t].z * inv, acc[q][t].w * inv};
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bool b[P > 0 ? P : 1];
+          if constexpr (P > 0) {
+            search_bits<P>(y[i], thr, b);
+#pragma unroll
+            for (int p = 0; p < P; ++p) w[p] |= (b[p] ? 1u : 0u) << (4 * q + i);
+          }
+          if constexpr (PROD) e[i] = valid ? y[i] - centroid_of<P>(b, cen) : 0.f;
+        }
+        if (prm.rot_dbg) *(float4*)(prm.rot_dbg + orow * d + c0 + 4 * q) = float4{y[0], y[1], y[2], y[3]};
+        if constexpr (PROD)
+          *(float4*)(prm.resid + ((int64_t)grp * prm.cap + v - prm.v_begin) * d + c0 + 4 * q) = float4{e[0], e[1], e[2], e[3]};
+      }
+      if constexpr (P > 0) {
+        uint8_t* rec = prm.codes + orow * (int64_t)(P * d / 8) + c0 / 8;
+#pragma unroll
+        for (int p = 0; p < P; ++p) *(unsigned*)(rec + p * (d / 8)) = valid ? w[p] : 0u;
+      }
+    } else {
+      const bool valid = prm.norms[orow] > 0.f;
+      unsigned w = 0u;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x4 pv = acc[q][t];
+        w |= (pv.x >= 0.f ? 1u : 0u) << (4 * q);
+        w |= (pv.y >= 0.f ? 1u : 0u) << (4 * q + 1);
+        w |= (pv.z >= 0.f ? 1u : 0u) << (4 * q + 2);
+        w |= (pv.w >= 0.f ? 1u : 0u) << (4 * q + 3);
+        if (prm.proj_dbg) *(float4*)(prm.proj_dbg + orow * d + c0 + 4 * q) = float4{pv.x, pv.y, pv.z, pv.w};
+      }
+      *(unsigned*)(prm.signs + orow * (int64_t)(d / 8) + c0 / 8) = valid ? w : 0u;
+    }
+  }
+}
+
+// ---- tables of the GEMM path, built once per quantizer ----
+// C = A B^T for d x d fp32 matrices (S' = S Pi^T), 64 x 64 output per workgroup
+__global__ __launch_bounds__(256) void abt_kernel(const float* __restrict__ A, const float* __restrict__ B, float* C, int d) {
+  __shared__ float As[64][33], Bs[64][33];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int j0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
+  float acc[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[u][v] = 0.f;
+  for (int i0 = 0; i0 < d; i0 += 32) {
+    for (int e = threadIdx.x; e < 64 * 32; e += 256) {
+      const int r = e >> 5, c = e & 31;
+      As[r][c] = A[(int64_t)(j0 + r) * d + i0 + c];
+      Bs[r][c] = B[(int64_t)(k0 + r) * d + i0 + c];
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int c = 0; c < 32; ++c) {
+      float a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = As[ty + 16 * u][c];
+        b[u] = Bs[tx + 16 * u][c];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a[u], b[v], acc[u][v]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) C[(int64_t)(j0 + ty + 16 * u) * d + k0 + tx + 16 * v] = acc[u][v];
+}
+
+// Fragment order of a d x d fp32 matrix M for lq_kernel: entry
+// ((cb * d/32 + ks) * 8 + q) * 2 + hl) * 64 + lane, lane = r + 16 g, holds
+// M[128 cb + 32 (r / 4) + 4 q + r % 4][32 ks + 8 g .. + 7] as bf16 (hl = 0 hi, 1 lo).
+__global__ __launch_bounds__(256) void frag_order_kernel(const float* __restrict__ M, u32x4* out, int d) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)d * d / 4) return;
+  const int lane = (int)(e & 63), hl = (int)((e >> 6) & 1), q = (int)((e >> 7) & 7);
+  const int64_t rest = e >> 10;
+  const int nks = d / 32;
+  const int ks = (int)(rest % nks), cb = (int)(rest / nks);
+  const int r = lane & 15, g = lane >> 4;
+  const int row = kLqCoords * cb + 32 * (r >> 2) + 4 * q + (r & 3);
+  const float* src = M + (int64_t)row * d + 32 * ks + 8 * g;
+  unsigned h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = bf16_part(src[i], hl == 1);
+  out[e] = u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+}
+
+}  // namespace
+
+bool lq_supported(int d) { return d > 256 && d <= 4096 && d % kLqCoords == 0; }
+
+tq_status build_large_tables(tq_quantizer* q) {
+  const int d = q->d;
+  if (!lq_supported(d)) return TQ_OK;
+  const size_t mat = (size_t)d * d * sizeof(u32x4) / 4;  // d^2 / 4 u32x4 = hi + lo bf16
+  const bool prod = q->variant == TQ_PROD;
+  tq_status st = check_hip(hipMalloc(&q->lq_block, mat * (prod ? 2 : 1)), "create: hipMalloc (GEMM tables)");
+  if (st != TQ_OK) return st;
+  u32x4* pif = (u32x4*)q->lq_block;
+  const unsigned nb = (unsigned)(((int64_t)d * d / 4 + 255) / 256);
+  hipLaunchKernelGGL(frag_order_kernel, dim3(nb), dim3(256), 0, nullptr, q->pi32, pif, d);
+  st = launch_check("create: fragment order");
+  if (st == TQ_OK && prod) {
+    float* sp = nullptr;
+    st = check_hip(hipMalloc(&sp, (size_t)d * d * sizeof(float)), "create: hipMalloc (S')");
+    if (st == TQ_OK) {
+      hipLaunchKernelGGL(abt_kernel, dim3(d / 64, d / 64), dim3(256), 0, nullptr, q->s32, q->pi32, sp, d);
+      st = launch_check("create: S' = S Pi^T");
+      if (st == TQ_OK) {
+        hipLaunchKernelGGL(frag_order_kernel, dim3(nb), dim3(256), 0, nullptr, sp, pif + mat / sizeof(u32x4), d);
+        st = launch_check("create: fragment order (S')");
+      }
+      if (st == TQ_OK) st = check_hip(hipDeviceSynchronize(), "create: GEMM tables");
+      tq_status fs = check_hip(hipFree(sp), "create: hipFree (S')");
+      if (st == TQ_OK) st = fs;
+    }
+  } else if (st == TQ_OK) {
+    st = check_hip(hipDeviceSynchronize(), "create: GEMM tables");
+  }
+  if (st == TQ_OK) {
+    q->lq_pi = pif;
+    q->lq_sp = prod ? pif + mat / sizeof(u32x4) : nullptr;
+  }
+  return st;
+}
+
+static tq_status launch_lq(const QuantizeLaunch& a, hipStream_t stream) {
+  const tq_quantizer* q0 = a.qz[0];
+  const int d = q0->d, P = q0->planes;
+  const bool prod = q0->variant == TQ_PROD;
+  const bool xf32 = a.x_dtype == TQ_F32;
+  const int64_t n = a.n_per_group;
+  for (int g0 = 0; g0 < a.n_groups; g0 += kMaxGroupsPerLaunch) {
+    const int ng = min(kMaxGroupsPerLaunch, a.n_groups - g0);
+    // prod: stream-ordered scratch for the fp32 residuals, at most 1 GiB per chunk of vectors
+    int64_t cap = n;
+    float* resid = nullptr;
+    if (prod) {
+      const int64_t lim = ((int64_t)1 << 30) / ((int64_t)ng * d * 4);
+      cap = min(n, max((int64_t)kLqVecs, lim / kLqVecs * kLqVecs));
+      tq_status st = check_hip(hipMallocAsync((void**)&resid, (size_t)ng * cap * d * sizeof(float), stream),
+                               "quantize: hipMallocAsync (residual scratch)");
+      if (st != TQ_OK) return st;
+    }
+    tq_status st = TQ_OK;
+    for (int64_t vb = 0; vb < n && st == TQ_OK; vb += cap) {
+      LqParams prm{};
+      prm.x = a.x;
+      prm.xg0 = g0;
+      prm.xgs = n;
+      prm.xoff = 0;
+      prm.n_per_group = n;
+      prm.group_base = g0;
+      prm.v_begin = vb;
+      prm.v_end = min(n, vb + cap);
+      prm.d = d;
+      prm.resid = resid;
+      prm.cap = cap;
+      prm.codes = a.codes;
+      prm.signs = a.signs;
+      prm.norms = a.norms;
+      prm.rnorms = a.rnorms;
+      prm.rot_dbg = a.rot_dbg;
+      prm.proj_dbg = a.proj_dbg;
+      const int K = 1 << P;
+      for (int i = 0; i + 1 < K; ++i) prm.thr[i] = q0->cb.thresholds[i];
+      for (int i = 0; i < K; ++i) prm.cen[i] = q0->cb.centroids[i];
+      for (int g = 0; g < ng; ++g) prm.mat[g] = (const u32x4*)a.qz[g0 + g]->lq_pi;
+      const int64_t nvb = (prm.v_end - vb + kLqVecs - 1) / kLqVecs;
+      const dim3 grid((unsigned)(nvb * (d / kLqCoords)), (unsigned)ng);
+      const size_t lds = (size_t)(kLqMatFrag + kLqVecFrag) * sizeof(u32x4);
+      st = dispatch_planes(P, [&](auto PC) -> tq_status {
+        constexpr int PP = decltype(PC)::value;
+        return dispatch_bool(xf32, [&](auto XC) -> tq_status {
+          constexpr bool XF = decltype(XC)::value;
+          return dispatch_bool(prod, [&](auto RC) -> tq_status {
+            constexpr bool PR = decltype(RC)::value;
+            if constexpr (!PR && PP == 0) {
+              return set_error(TQ_ERR_UNSUPPORTED, "quantize: planes");
+            } else {
+              hipLaunchKernelGGL((lq_kernel<PP, 0, XF, PR>), grid, dim3(kLqThreads), lds, stream, prm);
+              return launch_check("quantize (GEMM): rotation launch");
+            }
+          });
+        });
+      });
+      if (st != TQ_OK || !prod) continue;
+      LqParams p2 = prm;
+      p2.x = resid;
+      p2.xg0 = 0;
+      p2.xgs = cap;
+      p2.xoff = vb;
+      for (int g = 0; g < ng; ++g) p2.mat[g] = (const u32x4*)a.qz[g0 + g]->lq_sp;
+      hipLaunchKernelGGL((lq_kernel<0, 1, true, true>), grid, dim3(kLqThreads), lds, stream, p2);
+      st = launch_check("quantize (GEMM): QJL launch");
+    }
+    if (resid) {
+      tq_status fs = check_hip(hipFreeAsync(resid, stream), "quantize: hipFreeAsync (residual scratch)");
+      if (st == TQ_OK) st = fs;
+    }
+    if (st != TQ_OK) return st;
+  }
+  return TQ_OK;
+}
+
 tq_status launch_quantize_large(const QuantizeLaunch& a, hipStream_t stream) {
   const tq_quantizer* q0 = a.qz[0];
   const int d = q0->d;
+  bool gemm = a.layout == TQ_LAYOUT_VECTOR;
+  for (int g = 0; g < a.n_groups && gemm; ++g) gemm = a.qz[g]->lq_pi != nullptr;
+  if (gemm) return launch_lq(a, stream);
   if (a.layout != TQ_LAYOUT_VECTOR) return set_error(TQ_ERR_UNSUPPORTED, "quantize: d > 256 supports the vector layout only");
   const int vb = d <= 2048 ? 8 : 4;
   const size_t lds = ((size_t)2 * vb * d + 3 * vb) * sizeof(float);
