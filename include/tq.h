@@ -154,6 +154,11 @@ tq_status tq_quantizer_info(const tq_quantizer* q, int* d, int* bits, tq_variant
  *   proj_dbg    : device float32 [n][d] or NULL (prod): the projection S r
  *                 whose signs were stored.
  * A zero vector gets norm 0, rnorm 0 and all code and sign bits 0.
+ * x must be 16-byte aligned. For TQ_PROD at d a multiple of 128 above 256 the
+ * call takes stream-ordered scratch for the residuals (hipMallocAsync /
+ * hipFreeAsync on the caller's stream, at most 1 GiB, vectors processed in
+ * chunks that fit); every other configuration allocates nothing.
+ * Errors: TQ_ERR_NO_MEMORY or TQ_ERR_DEVICE if that scratch cannot be had.
  */
 tq_status tq_quantize(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group,
                       const void* x, tq_dtype x_dtype, tq_layout layout, uint8_t* codes,
