@@ -18,6 +18,7 @@ __all__ = [
     "qjl", "qjl_inverse", "pack_vector_layout", "unpack_vector_layout", "pack_bits",
     "unpack_bits", "pack_block_layout", "unpack_block_layout", "attention",
     "decode_attention", "inner_products", "QJL_SCALE", "hadamard", "wht_rotation",
+    "quantize_split", "dequantize_split",
 ]
 
 
@@ -256,6 +257,42 @@ def dequantize_prod(idx, signs, norms, rnorms, Pi, S, centroids_bm1):
 def inner_products(yq, x_tilde):
     """<y_i, x~_j> for every query i and vector j."""
     return np.asarray(yq, dtype=np.float64) @ np.asarray(x_tilde, dtype=np.float64).T
+
+
+# ---------------------------------------------------------------------------
+# Outlier-channel split: [NIK] "Experiments" (KV cache): outlier channels and
+# the other channels go through separate TurboQuant instances with different
+# bit widths. Part p takes the sub-vector x[:, channels_p] and is plain
+# TurboQuant in d_p = len(channels_p) dimensions, with its own rotation, norm,
+# codebook and (prod) QJL matrix. A part is a dict with keys "channels",
+# "variant" ("mse" or "prod"), "Pi", "S" (prod) and "centroids" (the d_p-dim
+# codebook of b_p bits for mse, b_p - 1 bits for prod).
+# ---------------------------------------------------------------------------
+
+def quantize_split(x, parts):
+    """Per-part results of quantize_mse / quantize_prod on x[:, channels_p]."""
+    x = np.asarray(x, dtype=np.float64)
+    res = []
+    for p in parts:
+        sub = x[:, np.asarray(p["channels"], dtype=np.int64)]
+        if p["variant"] == "prod":
+            res.append(quantize_prod(sub, p["Pi"], p["S"], p["centroids"]))
+        else:
+            res.append(quantize_mse(sub, p["Pi"], p["centroids"]))
+    return res
+
+
+def dequantize_split(results, parts, dim: int):
+    """x~ [n, dim]: each part's dequantized sub-vector at its channels, 0 at channels no part keeps."""
+    n = len(results[0]["norms"])
+    xt = np.zeros((n, dim))
+    for r, p in zip(results, parts):
+        if p["variant"] == "prod":
+            sub = dequantize_prod(r["idx"], r["signs"], r["norms"], r["rnorms"], p["Pi"], p["S"], p["centroids"])
+        else:
+            sub = dequantize_mse(r["idx"], r["norms"], p["Pi"], p["centroids"])
+        xt[:, np.asarray(p["channels"], dtype=np.int64)] = sub
+    return xt
 
 
 # ---------------------------------------------------------------------------
