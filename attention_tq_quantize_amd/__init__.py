@@ -27,7 +27,8 @@ EXPORTS = [
     "tq_quantizer_create", "tq_quantizer_create_wht", "tq_quantizer_destroy", "tq_quantizer_info", "tq_quantize",
     "tq_quantize_mse", "tq_quantize_prod", "tq_dequantize", "tq_inner_products",
     "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_append_workspace_size",
-    "tq_decode_append_attention", "tq_search_workspace_size", "tq_search_scores",
+    "tq_decode_append_attention", "tq_search_workspace_size", "tq_search_scores", "tq_quantize_split",
+    "tq_inner_products_split",
 ]
 
 
@@ -45,6 +46,11 @@ class AttnShape(ctypes.Structure):
 class PackedKV(ctypes.Structure):
     _fields_ = [("qz", ctypes.POINTER(ctypes.c_void_p)), ("codes", ctypes.c_void_p),
                 ("signs", ctypes.c_void_p), ("norms", ctypes.c_void_p), ("rnorms", ctypes.c_void_p)]
+
+
+class Records(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("signs", ctypes.c_void_p), ("norms", ctypes.c_void_p),
+                ("rnorms", ctypes.c_void_p), ("rot_dbg", ctypes.c_void_p), ("proj_dbg", ctypes.c_void_p)]
 
 
 _lib = None
@@ -76,6 +82,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tq_quantize_prod.argtypes = [_VP, _VP, _I, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
     lib.tq_dequantize.argtypes = [_VP, _I, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
     lib.tq_inner_products.argtypes = [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
+    lib.tq_quantize_split.argtypes = [_VP, _I, _VP, _I, _VP, _I, _I64, ctypes.POINTER(Records), _VP]
+    lib.tq_inner_products_split.argtypes = [_VP, _I, _VP, _I, _VP, _I64, ctypes.POINTER(Records), _I64, _VP, _VP]
     lib.tq_search_workspace_size.argtypes = [_VP, _I64, ctypes.POINTER(ctypes.c_size_t)]
     lib.tq_search_scores.argtypes = [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _VP]
     lib.tq_decode_workspace_size.argtypes = [ctypes.POINTER(AttnShape), ctypes.POINTER(PackedKV),
@@ -266,6 +274,64 @@ def inner_products(q: Quantizer, y, codes, norms, signs=None, rnorms=None, strea
     _check(lib.tq_inner_products(q.handle, _ptr(y.contiguous()), m, _ptr(codes) if q.planes else None,
                                  _ptr(signs), _ptr(norms), _ptr(rnorms), n, _ptr(out), _stream(stream)),
            "tq_inner_products")
+    return out
+
+
+def _split_args(qs, channels):
+    import numpy as np
+    ch = np.ascontiguousarray(np.concatenate([np.asarray(c, dtype=np.int32).ravel() for c in channels]), dtype=np.int32)
+    for q, c in zip(qs, channels):
+        assert len(c) == q.d, "each part's channel list must have its quantizer's d entries"
+    return ch
+
+
+def _records(rs):
+    arr = (Records * len(rs))()
+    for i, r in enumerate(rs):
+        arr[i] = Records(_ptr(r.get("codes")), _ptr(r.get("signs")), _ptr(r["norms"]), _ptr(r.get("rnorms")),
+                         _ptr(r.get("rot")), _ptr(r.get("proj")))
+    return arr
+
+
+def quantize_split(qs: Sequence[Quantizer], channels, x, rot_dbg: bool = False, proj_dbg: bool = False,
+                   stream=None) -> list:
+    """Outlier-channel split (tq_quantize_split): part p quantizes x[:, channels[p]] with qs[p].
+    x: [n, dim] float32 or bfloat16 CUDA tensor; returns one record dict per part."""
+    import torch
+    lib = load()
+    x = x.contiguous()
+    n, dim = x.shape
+    dt = TQ_BF16 if x.dtype == torch.bfloat16 else TQ_F32
+    ch = _split_args(qs, channels)
+    outs = []
+    for q in qs:
+        o = {"norms": torch.empty(n, dtype=torch.float32, device=x.device)}
+        if q.planes > 0:
+            o["codes"] = torch.empty((n, q.code_bytes), dtype=torch.uint8, device=x.device)
+        if q.variant == "prod":
+            o["signs"] = torch.empty((n, q.d // 8), dtype=torch.uint8, device=x.device)
+            o["rnorms"] = torch.empty(n, dtype=torch.float32, device=x.device)
+            if proj_dbg:
+                o["proj"] = torch.empty((n, q.d), dtype=torch.float32, device=x.device)
+        if rot_dbg:
+            o["rot"] = torch.empty((n, q.d), dtype=torch.float32, device=x.device)
+        outs.append(o)
+    _check(lib.tq_quantize_split(_handles(qs), len(qs), ch.ctypes.data, dim, _ptr(x), dt, n, _records(outs),
+                                 _stream(stream)), "tq_quantize_split")
+    return outs
+
+
+def inner_products_split(qs: Sequence[Quantizer], channels, y, recs, stream=None):
+    """sum over parts of <y restricted to part p, x~_p> (tq_inner_products_split); y: [m, dim] float32."""
+    import torch
+    lib = load()
+    y = y.contiguous()
+    m, dim = y.shape
+    n = recs[0]["norms"].numel()
+    ch = _split_args(qs, channels)
+    out = torch.empty((m, n), dtype=torch.float32, device=y.device)
+    _check(lib.tq_inner_products_split(_handles(qs), len(qs), ch.ctypes.data, dim, _ptr(y), m, _records(recs), n,
+                                       _ptr(out), _stream(stream)), "tq_inner_products_split")
     return out
 
 

@@ -40,9 +40,11 @@ std::string fmt(const char* f, ...) {
 }
 
 bool gpu_dim(int d) { return d == 64 || d == 128 || d == 256; }
-// head dimensions of the vector-search path (quantize in the vector layout and
-// inner products only): multiples of 64 above 256, up to 4096
-bool large_dim(int d) { return d > 256 && d <= 4096 && d % 64 == 0; }
+// head dimensions served by the generic kernels (quantize in the vector layout,
+// inner products, channel splits): multiples of 32 up to 4096 other than 64,
+// 128 and 256 (vector search at d = 1536 / 3072, the 32 / 96 channel parts of
+// an outlier split)
+bool large_dim(int d) { return d >= 32 && d <= 4096 && d % 32 == 0 && !gpu_dim(d); }
 
 uint16_t bf16_rne(float f) {
   uint32_t u;
@@ -127,7 +129,7 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
   *out = nullptr;
   const bool large = large_dim(d);
   if (!gpu_dim(d) && !large)
-    return set_error(TQ_ERR_UNSUPPORTED, fmt("create: d=%d (supported: 64, 128, 256; multiples of 64 in (256, 4096] for quantize, inner products and search)", d));
+    return set_error(TQ_ERR_UNSUPPORTED, fmt("create: d=%d (supported: 64, 128, 256; other multiples of 32 up to 4096 for quantize, inner products, search and channel splits)", d));
   if (bits < 1 || bits > kMaxBits) return set_error(TQ_ERR_UNSUPPORTED, fmt("create: bits=%d (supported: 1..4)", bits));
   if (variant != TQ_MSE && variant != TQ_PROD) return set_error(TQ_ERR_INVALID_ARG, "create: unknown variant");
   if (!pi) return set_error(TQ_ERR_INVALID_ARG, "create: pi is NULL");
@@ -422,6 +424,87 @@ tq_status tq_search_scores(const tq_quantizer* q, const float* y, int64_t m, con
   if (!workspace || ws_bytes < need)
     return set_error(TQ_ERR_WORKSPACE, fmt("search: workspace needs %zu bytes, got %zu", need, workspace ? ws_bytes : (size_t)0));
   return launch_search(q, y, m, codes, signs, norms, rnorms, n, out, workspace, (hipStream_t)stream);
+}
+
+// ---- outlier-channel split ([NIK] "Experiments": separate quantizers for outlier and ordinary channels) ----
+static tq_status check_split(const tq_quantizer* const* qz, int n_parts, const int32_t* channels, int dim,
+                             std::vector<uint16_t>* chan, std::vector<int>* off) {
+  if (!qz || !channels) return set_error(TQ_ERR_INVALID_ARG, "split: qz or channels is NULL");
+  if (n_parts < 1 || n_parts > 8) return set_error(TQ_ERR_INVALID_ARG, "split: n_parts outside [1, 8]");
+  if (dim < 1 || dim > kSplitMaxDim) return set_error(TQ_ERR_UNSUPPORTED, fmt("split: dim=%d outside [1, %d]", dim, kSplitMaxDim));
+  int total = 0;
+  off->assign(n_parts + 1, 0);
+  for (int p = 0; p < n_parts; ++p) {
+    if (!qz[p]) return set_error(TQ_ERR_INVALID_ARG, fmt("split: part %d handle is NULL", p));
+    if (qz[p]->planes > 4) return set_error(TQ_ERR_UNSUPPORTED, "split: planes");
+    total += qz[p]->d;
+    (*off)[p + 1] = total;
+  }
+  if (total > dim) return set_error(TQ_ERR_INVALID_ARG, fmt("split: parts cover %d channels, the rows have %d", total, dim));
+  std::vector<char> seen(dim, 0);
+  chan->resize(total);
+  for (int j = 0; j < total; ++j) {
+    const int c = channels[j];
+    if (c < 0 || c >= dim) return set_error(TQ_ERR_INVALID_ARG, fmt("split: channels[%d]=%d outside [0, %d)", j, c, dim));
+    if (seen[c]) return set_error(TQ_ERR_INVALID_ARG, fmt("split: channel %d listed twice", c));
+    seen[c] = 1;
+    (*chan)[j] = (uint16_t)c;
+  }
+  return TQ_OK;
+}
+
+tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, const int32_t* channels, int dim,
+                            const void* x, tq_dtype x_dtype, int64_t n, const tq_records* out, void* stream) {
+  std::vector<uint16_t> chan;
+  std::vector<int> off;
+  tq_status st = check_split(qz, n_parts, channels, dim, &chan, &off);
+  if (st != TQ_OK) return st;
+  if (!out) return set_error(TQ_ERR_INVALID_ARG, "split: out is NULL");
+  if (n < 0) return set_error(TQ_ERR_INVALID_ARG, "split: negative n");
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return set_error(TQ_ERR_INVALID_ARG, "split: x_dtype");
+  if (n == 0) return TQ_OK;
+  if (!x) return set_error(TQ_ERR_INVALID_ARG, "split: x is NULL");
+  if (n > (int64_t)1 << 31) return set_error(TQ_ERR_UNSUPPORTED, "split: n > 2^31");
+  for (int p = 0; p < n_parts; ++p) {
+    const tq_records& r = out[p];
+    const bool prod = qz[p]->variant == TQ_PROD;
+    if (!r.norms || (qz[p]->planes > 0 && !r.codes) || (prod && (!r.signs || !r.rnorms)))
+      return set_error(TQ_ERR_INVALID_ARG, fmt("split: part %d output buffer is NULL", p));
+  }
+  for (int p = 0; p < n_parts; ++p) {
+    const tq_records& r = out[p];
+    const tq_quantizer* one[1] = {qz[p]};
+    QuantizeLaunch a{one, 1, n, x, x_dtype, TQ_LAYOUT_VECTOR, r.codes, r.signs, r.norms, r.rnorms, r.rot_dbg, r.proj_dbg};
+    st = launch_quantize_fp32(a, chan.data() + off[p], dim, (hipStream_t)stream);
+    if (st != TQ_OK) return st;
+  }
+  return TQ_OK;
+}
+
+tq_status tq_inner_products_split(const tq_quantizer* const* qz, int n_parts, const int32_t* channels, int dim,
+                                  const float* y, int64_t m, const tq_records* recs, int64_t n, float* out,
+                                  void* stream) {
+  std::vector<uint16_t> chan;
+  std::vector<int> off;
+  tq_status st = check_split(qz, n_parts, channels, dim, &chan, &off);
+  if (st != TQ_OK) return st;
+  if (m < 0 || n < 0) return set_error(TQ_ERR_INVALID_ARG, "split inner products: negative size");
+  if (m == 0 || n == 0) return TQ_OK;
+  if (!y || !recs || !out) return set_error(TQ_ERR_INVALID_ARG, "split inner products: NULL buffer");
+  if (m > 65535 || n > (int64_t)1 << 31) return set_error(TQ_ERR_UNSUPPORTED, "split inner products: m > 65535 or n > 2^31");
+  for (int p = 0; p < n_parts; ++p) {
+    const tq_records& r = recs[p];
+    const bool prod = qz[p]->variant == TQ_PROD;
+    if (!r.norms || (qz[p]->planes > 0 && !r.codes) || (prod && (!r.signs || !r.rnorms)))
+      return set_error(TQ_ERR_INVALID_ARG, fmt("split inner products: part %d record buffer is NULL", p));
+  }
+  for (int p = 0; p < n_parts; ++p) {
+    const tq_records& r = recs[p];
+    st = launch_inner_products_fp32(qz[p], y, dim, chan.data() + off[p], p > 0, m, r.codes, r.signs, r.norms, r.rnorms,
+                                    n, out, (hipStream_t)stream);
+    if (st != TQ_OK) return st;
+  }
+  return TQ_OK;
 }
 
 static tq_status check_decode(const tq_attn_shape* s, const tq_packed_kv* k, const tq_packed_kv* v,

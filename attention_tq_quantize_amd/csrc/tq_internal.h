@@ -81,6 +81,14 @@ struct QuantizeLaunch {
 tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream);
 // d > 256 (tq_large.hip): vector layout only
 tq_status launch_quantize_large(const QuantizeLaunch& a, hipStream_t stream);
+// fp32 kernels for any d (multiple of 32): optional channel map (quantized
+// coordinate j reads input channel chan[j] of a row of x_stride elements)
+tq_status launch_quantize_fp32(const QuantizeLaunch& a, const uint16_t* chan, int64_t x_stride, hipStream_t stream);
+tq_status launch_inner_products_fp32(const tq_quantizer* q, const float* y, int64_t y_stride, const uint16_t* chan,
+                                     bool accumulate, int64_t m, const uint8_t* codes, const uint8_t* signs,
+                                     const float* norms, const float* rnorms, int64_t n, float* out,
+                                     hipStream_t stream);
+constexpr int kSplitMaxDim = 512;  // widest input row of a channel split
 // d a multiple of 128 in (256, 4096]: the GEMM quantize tables, built at creation
 bool lq_supported(int d);
 tq_status build_large_tables(tq_quantizer* q);

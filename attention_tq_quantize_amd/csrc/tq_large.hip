@@ -16,8 +16,13 @@
 namespace tq {
 namespace {
 
+constexpr int kMaxSplitDim = 512;  // channel maps travel in the kernel arguments
+
 struct LargeQuantParams {
   const void* x;
+  int64_t x_stride;       // elements per input row (d, or the full width of a channel split)
+  bool chan_map;          // coordinate j of the quantized vector is input channel chan[j]
+  uint16_t chan[kMaxSplitDim];
   int64_t n_per_group;
   int d, planes, vb;
   bool prod, x_bf16;
@@ -98,7 +103,8 @@ __global__ __launch_bounds__(kThreads) void quantize_large_kernel(LargeQuantPara
     if (v < nv) {
       const int64_t row = gbase + v0 + v;
       for (int j = lane; j < d; j += 64) {
-        const float xv = prm.x_bf16 ? bf16_val(((const uint16_t*)prm.x)[row * d + j]) : ((const float*)prm.x)[row * d + j];
+        const int64_t src = row * prm.x_stride + (prm.chan_map ? prm.chan[j] : j);
+        const float xv = prm.x_bf16 ? bf16_val(((const uint16_t*)prm.x)[src]) : ((const float*)prm.x)[src];
         A[(size_t)v * d + j] = xv;
         acc = fma((double)xv, (double)xv, acc);
       }
@@ -180,6 +186,10 @@ __global__ __launch_bounds__(kThreads) void quantize_large_kernel(LargeQuantPara
 // thread then walks whole records, 8 coordinates per code byte.
 struct LargeIpParams {
   const float* y;
+  int64_t y_stride;       // elements per query row
+  bool chan_map;          // coordinate j of the query is its channel chan[j]
+  bool accumulate;        // add into out (the parts of a channel split)
+  uint16_t chan[kMaxSplitDim];
   const uint8_t* codes;
   const uint8_t* signs;
   const float* norms;
@@ -203,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void inner_products_large_kernel(LargeIpP
   float* yp = lds + d;
   float* ys = lds + 2 * d;
   const int64_t qi = blockIdx.y;
-  for (int j = threadIdx.x; j < d; j += kThreads) yq[j] = prm.y[qi * d + j];
+  for (int j = threadIdx.x; j < d; j += kThreads) yq[j] = prm.y[qi * prm.y_stride + (prm.chan_map ? prm.chan[j] : j)];
   __syncthreads();
   rows_times<1>(prm.pi, yq, yp, d, 1);
   if (prm.prod) rows_times<1>(prm.s, yq, ys, d, 1);
@@ -228,7 +238,8 @@ __global__ __launch_bounds__(kThreads) void inner_products_large_kernel(LargeIpP
     }
     float r = a;
     if (prm.prod) r = fmaf(prm.rnorms[v] * prm.kappa, b, r);
-    prm.out[qi * prm.n + v] = prm.norms[v] * r;
+    float* o = prm.out + qi * prm.n + v;
+    *o = prm.accumulate ? *o + prm.norms[v] * r : prm.norms[v] * r;
   }
 }
 
@@ -1049,12 +1060,22 @@ tq_status launch_quantize_large(const QuantizeLaunch& a, hipStream_t stream) {
   for (int g = 0; g < a.n_groups && gemm; ++g) gemm = a.qz[g]->lq_pi != nullptr;
   if (gemm) return launch_lq(a, stream);
   if (a.layout != TQ_LAYOUT_VECTOR) return set_error(TQ_ERR_UNSUPPORTED, "quantize: d > 256 supports the vector layout only");
+  return launch_quantize_fp32(a, nullptr, d, stream);
+}
+
+tq_status launch_quantize_fp32(const QuantizeLaunch& a, const uint16_t* chan, int64_t x_stride, hipStream_t stream) {
+  const tq_quantizer* q0 = a.qz[0];
+  const int d = q0->d;
   const int vb = d <= 2048 ? 8 : 4;
   const size_t lds = ((size_t)2 * vb * d + 3 * vb) * sizeof(float);
   for (int g0 = 0; g0 < a.n_groups; g0 += kMaxGroupsPerLaunch) {
     const int ng = min(kMaxGroupsPerLaunch, a.n_groups - g0);
     LargeQuantParams prm{};
     prm.x = a.x;
+    prm.x_stride = x_stride;
+    prm.chan_map = chan != nullptr;
+    if (chan)
+      for (int j = 0; j < d; ++j) prm.chan[j] = chan[j];
     prm.n_per_group = a.n_per_group;
     prm.d = d;
     prm.planes = q0->planes;
@@ -1096,8 +1117,20 @@ tq_status launch_quantize_large(const QuantizeLaunch& a, hipStream_t stream) {
 tq_status launch_inner_products_large(const tq_quantizer* q, const float* y, int64_t m, const uint8_t* codes,
                                       const uint8_t* signs, const float* norms, const float* rnorms, int64_t n,
                                       float* out, hipStream_t stream) {
+  return launch_inner_products_fp32(q, y, q->d, nullptr, false, m, codes, signs, norms, rnorms, n, out, stream);
+}
+
+tq_status launch_inner_products_fp32(const tq_quantizer* q, const float* y, int64_t y_stride, const uint16_t* chan,
+                                     bool accumulate, int64_t m, const uint8_t* codes, const uint8_t* signs,
+                                     const float* norms, const float* rnorms, int64_t n, float* out,
+                                     hipStream_t stream) {
   LargeIpParams prm{};
   prm.y = y;
+  prm.y_stride = y_stride;
+  prm.chan_map = chan != nullptr;
+  prm.accumulate = accumulate;
+  if (chan)
+    for (int j = 0; j < q->d; ++j) prm.chan[j] = chan[j];
   prm.codes = codes;
   prm.signs = signs;
   prm.norms = norms;

@@ -220,6 +220,41 @@ def vector_search(tq, syn, torch, dev, n=100000, m=16, bits=3):
     return out
 
 
+def outlier_split(tq, syn, torch, dev, w):
+    """Outlier-channel mixed precision on the layer's KV (8 heads x 32768 tokens,
+    d = 128): per head, the 32 channels of largest RMS at 3 bits and the other 96
+    at 2 bits (2.25 bits per channel), keys TurboQuant_prod, values TurboQuant_mse,
+    through tq_quantize_split (two parts per call, one call per head and tensor)."""
+    H, T2, d = w["H"], w["T2"], w["d"]
+    calls = []
+    for t, xs, var in ((syn.T_K, w["xk2"], "prod"), (syn.T_V, w["xv2"], "mse")):
+        for h in range(H):
+            x = xs[h]
+            rms = x.float().pow(2).mean(dim=0)
+            order = torch.argsort(rms, descending=True, stable=True).cpu().numpy()
+            chans = [order[:32], order[32:]]
+            qs = []
+            for i, (c, bits) in enumerate(zip(chans, (3, 2))):
+                dp = len(c)
+                S = syn.gaussian_matrix(dp, syn.CFG_LAYER_QUANT, t, 100 + 2 * h + i) if var == "prod" else None
+                qs.append(tq.Quantizer(dp, bits, var, syn.rotation(dp, syn.CFG_LAYER_QUANT, t, 100 + 2 * h + i), S))
+            calls.append((qs, chans, x))
+    run = lambda: [tq.quantize_split(qs, chans, x) for qs, chans, x in calls]
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    nvec = 2 * H * T2
+    return {"split": "32 ch x 3 b + 96 ch x 2 b (2.25 bits/channel), keys prod, values mse", "vectors": nvec,
+            "ms": round(ms, 3), "mvec_s": round(nvec / (ms * 1e-3) / 1e6, 1),
+            "input_gb_s": round(nvec * d * 2 / (ms * 1e-3) / 1e9, 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -321,6 +356,7 @@ def main():
     a_ms = e0.elapsed_time(e1) / 10
 
     vsearch = vector_search(tq, syn, torch, dev)
+    split = outlier_split(tq, syn, torch, dev, w)
 
     traffic = decode_traffic(args.traffic)
     d_gbs = d_bytes / (d_avg * 1e-3) / 1e9
@@ -352,6 +388,7 @@ def main():
             "quantize_prod_gb_s": round(p_vec * (256 + 32 + 16 + 8) / (p_ms * 1e-3) / 1e9, 1),
             "decode_append_ms": round(a_ms, 4),
             "vector_search": vsearch,
+            "outlier_split": split,
             "wall_s_timed_region": round(wall, 3),
         },
         "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

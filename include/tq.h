@@ -97,10 +97,12 @@ tq_status tq_codebook_build(int d, int bits, float* centroids, float* thresholds
  * b-1 bit MSE stage, then sign(S r) and |r| of the residual.
  *   d, bits   : head dimension and total bits per coordinate (prod: b-1 for the
  *               MSE stage plus 1 QJL bit). d in {64, 128, 256} for every call;
- *               d a multiple of 64 in (256, 4096] (vector search, [NIK]
- *               "Experiments": d = 1536, 3072) for tq_quantize in the VECTOR
- *               layout, tq_inner_products and tq_search_scores (d a multiple
- *               of 128 there) only (others return TQ_ERR_UNSUPPORTED). Orthogonality is checked exactly for
+ *               any other multiple of 32 up to 4096 (vector search, [NIK]
+ *               "Experiments": d = 1536, 3072; the parts of an outlier
+ *               split, e.g. 32 and 96) for tq_quantize in the VECTOR layout,
+ *               tq_inner_products, the split calls and tq_search_scores (d a
+ *               multiple of 128 there) only (others return
+ *               TQ_ERR_UNSUPPORTED). Orthogonality is checked exactly for
  *               d <= 256 and on four fixed pseudo-random vectors above.
  *   pi        : host, float64 [d][d] row-major, orthogonal (y = Pi u).
  *   s         : host, float64 [d][d] row-major Gaussian QJL matrix; required
@@ -197,6 +199,53 @@ tq_status tq_dequantize(const tq_quantizer* q, tq_layout layout, const uint8_t* 
 tq_status tq_inner_products(const tq_quantizer* q, const float* y, int64_t m,
                             const uint8_t* codes, const uint8_t* signs, const float* norms,
                             const float* rnorms, int64_t n, float* out, void* stream);
+
+/*
+ * Outlier-channel mixed precision ([NIK] "Experiments", KV cache: outlier
+ * channels get more bits than the others, e.g. 32 channels at 3 bits and 96
+ * at 2 bits of a 128-channel head): the channels of each input row are split
+ * into parts and part p is quantized by its own quantizer qz[p] (its own
+ * rotation, norm, codebook and, for prod, QJL matrix) in the VECTOR layout.
+ * The rule that picks the outlier channels is not given by the pages; the
+ * caller passes the channel lists.
+ *   qz       : host array [n_parts] of handles, 1 <= n_parts <= 8, any
+ *              variant and bit width each (d_p = the handle's d, at most 4
+ *              MSE-stage planes).
+ *   channels : host int32 [d_0 + ... + d_{P-1}]: part p takes the input
+ *              channels channels[off_p .. off_p + d_p), off_p = d_0 + .. +
+ *              d_{p-1}, in that order (coordinate j of the part is channel
+ *              channels[off_p + j]). Every entry in [0, dim), none repeated;
+ *              channels left out are dropped. Copied.
+ *   dim      : channels per input row, at most 512.
+ *   x        : device [n][dim], float32 or bfloat16.
+ *   out      : host array [n_parts] of device record buffers, as for
+ *              tq_quantize with d = d_p (rot_dbg / proj_dbg may be NULL).
+ * One launch per part on the caller's stream; the kernels are the generic
+ * fp32 ones (any d_p a multiple of 32). Allocates nothing.
+ * Errors: TQ_ERR_INVALID_ARG (NULL pointers, a channel out of range or
+ * repeated, more channels than dim), TQ_ERR_UNSUPPORTED (dim > 512, n > 2^31).
+ */
+typedef struct {
+  uint8_t* codes;   /* code_planes*d/8 bytes per vector (NULL when code_planes == 0) */
+  uint8_t* signs;   /* prod: [n][d/8] */
+  float* norms;     /* [n] */
+  float* rnorms;    /* prod: [n] */
+  float* rot_dbg;   /* optional [n][d] */
+  float* proj_dbg;  /* optional [n][d] (prod) */
+} tq_records;
+tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, const int32_t* channels, int dim,
+                            const void* x, tq_dtype x_dtype, int64_t n, const tq_records* out,
+                            void* stream);
+/*
+ * Inner products of m float32 queries y [m][dim] with n split records:
+ *   out[i][j] = sum_p <y_i restricted to part p's channels, x~_p,j>
+ * the estimate of <y_i, x_j> over the kept channels (each part as in
+ * tq_inner_products). recs is read only; out: device float32 [m][n].
+ * Errors as for tq_quantize_split, plus m > 65535.
+ */
+tq_status tq_inner_products_split(const tq_quantizer* const* qz, int n_parts, const int32_t* channels,
+                                  int dim, const float* y, int64_t m, const tq_records* recs, int64_t n,
+                                  float* out, void* stream);
 
 /*
  * Vector-search scoring on the matrix cores: the same inner products

@@ -146,3 +146,9 @@ def test_search_argument_errors(lib):
     nb = ctypes.c_size_t(0)
     assert lib.tq_search_workspace_size(None, 8, ctypes.byref(nb)) == tq.TQ_ERR_INVALID_ARG
     assert lib.tq_search_scores(None, None, 1, None, None, None, None, 1, None, None, 0, None) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_split_argument_errors(lib):
+    ch = (ctypes.c_int32 * 4)(0, 1, 2, 3)
+    assert lib.tq_quantize_split(None, 1, ch, 4, None, 0, 1, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_inner_products_split(None, 1, ch, 4, None, 1, None, 1, None, None) == tq.TQ_ERR_INVALID_ARG

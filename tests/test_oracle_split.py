@@ -102,9 +102,9 @@ def test_split_prod_unbiased_with_closed_form_variance():
     ch = np.random.default_rng(9).permutation(dim)
     parts = [_part(ch[:32], "prod", 3, 6), _part(ch[32:], "prod", 2, 7)]
     x = np.random.default_rng(10).standard_normal((n, dim))
-    y = np.random.default_rng(11).standard_normal((4, dim))
+    y = np.random.default_rng(11).standard_normal((32, dim))  # one S per part: average over query directions
     xt = O.dequantize_split(O.quantize_split(x, parts), parts, dim)
-    err = O.inner_products(y, xt) - O.inner_products(y, x)  # [4, n]
+    err = O.inner_products(y, xt) - O.inner_products(y, x)  # [32, n]
     assert abs(err.mean()) < 4 * err.std() / math.sqrt(err.size)
     want = 0.0
     for p, b in zip(parts, (3, 2)):
