@@ -1,14 +1,17 @@
-// Quantize and inner products for large head dimensions (vector search,
-// d = 512 .. 4096, multiples of 64): [NIK] "Step 0: normalization", "Step 1:
-// random rotation", "Step 2: optimal scalar quantization", "QJL: a one-bit
-// method" and "TurboQuant proper"; the vector-search workload of [NIK]
-// "Experiments" (nearest neighbours at d = 1536 and 3072).
+// Quantize, inner products and scoring for the head dimensions outside the
+// d = 64 / 128 / 256 kernels: vector search (d = 1536, 3072; [NIK]
+// "Experiments", nearest neighbours) and the parts of an outlier-channel split
+// (d = 32, 96; [NIK] "Experiments", KV cache), following [NIK] "Step 0:
+// normalization", "Step 1: random rotation", "Step 2: optimal scalar
+// quantization", "QJL: a one-bit method" and "TurboQuant proper".
 //
-// At these sizes the rotation no longer fits the LDS-staged MFMA fragments of
-// the d <= 256 kernels, so both kernels are plain fp32 code over the
-// quantizer's fp32 Pi and S: a workgroup quantizes VB vectors at once, reading
-// each row of Pi (and S) once for all VB vectors (VB dot products per matrix
-// element fetched), with the vectors in LDS. The norm is accumulated in fp64.
+// Three families of kernels live here:
+// * generic fp32 kernels for any d that is a multiple of 32 (with an optional
+//   channel map for splits): a workgroup quantizes VB vectors at once, reading
+//   each row of Pi (and S) once for all VB vectors, with the vectors in LDS;
+//   the norm is accumulated in fp64;
+// * the matrix-core GEMM quantize for d a multiple of 128 above 256;
+// * the matrix-core scoring of a packed database (tq_search_scores).
 #include <hip/hip_runtime.h>
 
 #include "tq_device.h"
