@@ -40,6 +40,7 @@ std::string fmt(const char* f, ...) {
 }
 
 bool gpu_dim(int d) { return d == 64 || d == 128 || d == 256; }
+bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
 // head dimensions served by the generic kernels (quantize in the vector layout,
 // inner products, channel splits): multiples of 32 up to 4096 other than 64,
 // 128 and 256 (vector search at d = 1536 / 3072, the 32 / 96 channel parts of
@@ -343,6 +344,10 @@ tq_status tq_quantize(const tq_quantizer* const* qz, int n_groups, int64_t n_per
   if (prod && (!signs || !rnorms)) return set_error(TQ_ERR_INVALID_ARG, "quantize: prod needs signs and rnorms");
   if (!prod && proj_dbg) return set_error(TQ_ERR_INVALID_ARG, "quantize: proj_dbg is only for prod");
   if ((double)n_groups * (double)n_per_group > 4.0e9) return set_error(TQ_ERR_UNSUPPORTED, "quantize: more than 4e9 vectors");
+  // the kernels load x in 16-byte vectors, store code and sign words and float4 debug rows
+  if (misaligned(x, 16) || misaligned(codes, 4) || misaligned(signs, 4) || misaligned(rot_dbg, 16) ||
+      misaligned(proj_dbg, 16))
+    return set_error(TQ_ERR_INVALID_ARG, "quantize: x, rot_dbg and proj_dbg must be 16-byte aligned, codes and signs 4-byte aligned");
   QuantizeLaunch a{qz, n_groups, n_per_group, x, x_dtype, layout, codes, signs, norms, rnorms, rot_dbg, proj_dbg};
   if (large_dim(q0->d)) return launch_quantize_large(a, (hipStream_t)stream);
   return launch_quantize(a, (hipStream_t)stream);
@@ -418,7 +423,8 @@ tq_status tq_search_scores(const tq_quantizer* q, const float* y, int64_t m, con
   if (m == 0 || n == 0) return TQ_OK;
   if (!y || (q->planes > 0 && !codes) || !norms || !out) return set_error(TQ_ERR_INVALID_ARG, "search: NULL buffer");
   if (q->variant == TQ_PROD && (!signs || !rnorms)) return set_error(TQ_ERR_INVALID_ARG, "search: prod needs signs and rnorms");
-  if ((uintptr_t)y & 15) return set_error(TQ_ERR_INVALID_ARG, "search: y must be 16-byte aligned");
+  if (misaligned(y, 16) || misaligned(codes, 4) || misaligned(signs, 4))
+    return set_error(TQ_ERR_INVALID_ARG, "search: y must be 16-byte aligned, codes and signs 4-byte aligned");
   if (m > 65535 || n > (int64_t)1 << 31) return set_error(TQ_ERR_UNSUPPORTED, "search: m > 65535 or n > 2^31");
   const size_t need = pl.total;
   if (!workspace || ws_bytes < need)
@@ -470,6 +476,8 @@ tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, const in
     const bool prod = qz[p]->variant == TQ_PROD;
     if (!r.norms || (qz[p]->planes > 0 && !r.codes) || (prod && (!r.signs || !r.rnorms)))
       return set_error(TQ_ERR_INVALID_ARG, fmt("split: part %d output buffer is NULL", p));
+    if (misaligned(r.codes, 4) || misaligned(r.signs, 4))
+      return set_error(TQ_ERR_INVALID_ARG, fmt("split: part %d codes and signs must be 4-byte aligned", p));
   }
   for (int p = 0; p < n_parts; ++p) {
     const tq_records& r = out[p];

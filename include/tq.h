@@ -156,7 +156,8 @@ tq_status tq_quantizer_info(const tq_quantizer* q, int* d, int* bits, tq_variant
  *   proj_dbg    : device float32 [n][d] or NULL (prod): the projection S r
  *                 whose signs were stored.
  * A zero vector gets norm 0, rnorm 0 and all code and sign bits 0.
- * x must be 16-byte aligned. For TQ_PROD at d a multiple of 128 above 256 the
+ * x, rot_dbg and proj_dbg must be 16-byte aligned, codes and signs 4-byte
+ * aligned (TQ_ERR_INVALID_ARG otherwise). For TQ_PROD at d a multiple of 128 above 256 the
  * call takes stream-ordered scratch for the residuals (hipMallocAsync /
  * hipFreeAsync on the caller's stream, at most 1 GiB, vectors processed in
  * chunks that fit); every other configuration allocates nothing.
@@ -219,7 +220,8 @@ tq_status tq_inner_products(const tq_quantizer* q, const float* y, int64_t m,
  *   dim      : channels per input row, at most 512.
  *   x        : device [n][dim], float32 or bfloat16.
  *   out      : host array [n_parts] of device record buffers, as for
- *              tq_quantize with d = d_p (rot_dbg / proj_dbg may be NULL).
+ *              tq_quantize with d = d_p (rot_dbg / proj_dbg may be NULL;
+ *              codes and signs 4-byte aligned).
  * One launch per part on the caller's stream; the kernels are the generic
  * fp32 ones (any d_p a multiple of 32). Allocates nothing.
  * Errors: TQ_ERR_INVALID_ARG (NULL pointers, a channel out of range or
@@ -256,12 +258,13 @@ tq_status tq_inner_products_split(const tq_quantizer* const* qz, int n_parts, co
  * symmetric codebook. Supports d a multiple of 128 in [128, 4096] and up to 4
  * MSE-stage planes; other quantizers return TQ_ERR_UNSUPPORTED.
  *   y, m, codes, signs, norms, rnorms, n, out : as for tq_inner_products
- *               (out: device float32 [m][n], overwritten); y 16-byte aligned.
+ *               (out: device float32 [m][n], overwritten); y 16-byte aligned,
+ *               codes and signs 4-byte aligned.
  *   workspace : device scratch of at least tq_search_workspace_size(q, m)
  *               bytes (per-query operands); concurrent calls need separate
  *               workspaces.
- * Errors: TQ_ERR_INVALID_ARG (NULL handle or buffer, negative size, y not
- * 16-byte aligned), TQ_ERR_WORKSPACE (workspace missing or too small), TQ_ERR_UNSUPPORTED
+ * Errors: TQ_ERR_INVALID_ARG (NULL handle or buffer, negative size, a
+ * misaligned buffer), TQ_ERR_WORKSPACE (workspace missing or too small), TQ_ERR_UNSUPPORTED
  * (d, planes, m > 65535 or n > 2^31). m == 0 or n == 0 is a no-op.
  */
 tq_status tq_search_workspace_size(const tq_quantizer* q, int64_t m, size_t* bytes);

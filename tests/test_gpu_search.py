@@ -108,3 +108,23 @@ def test_search_scores_unsupported_dims(gpu_lib):
         q = tq.Quantizer(d, 3, "mse", syn.rotation(d, syn.CFG_TEST, syn.T_K, 1))
         nb = ctypes.c_size_t(0)
         assert lib.tq_search_workspace_size(q.handle, 8, ctypes.byref(nb)) == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_misaligned_buffers_are_refused(gpu_lib):
+    """The kernels load x and y in 16-byte vectors and code / sign words in 4
+    bytes: misaligned buffers are refused with TQ_ERR_INVALID_ARG."""
+    tq = gpu_lib
+    d = 128
+    q = tq.Quantizer(d, 3, "prod", syn.rotation(d, syn.CFG_TEST, syn.T_K, 5), syn.gaussian_matrix(d, syn.CFG_TEST, syn.T_K, 5))
+    flat = torch.zeros(4 * d + 1, dtype=torch.bfloat16, device=DEV)
+    x = flat[1:].view(4, d)  # 2-byte offset
+    with pytest.raises(tq.TQError) as e:
+        tq.quantize_prod(q, x)
+    assert e.value.status == tq.TQ_ERR_INVALID_ARG
+    yflat = torch.zeros(8 * d + 1, dtype=torch.float32, device=DEV)
+    y = yflat[1:].view(8, d)
+    r = tq.quantize_prod(q, torch.zeros((4, d), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(tq.TQError) as e:
+        tq.search_scores(q, y, r["codes"], r["norms"], r["signs"], r["rnorms"])
+    assert e.value.status == tq.TQ_ERR_INVALID_ARG
+    torch.cuda.synchronize()
