@@ -135,8 +135,8 @@ def cpu_baseline(syn):
     O.pack_vector_layout(r["idx"], 3)
     tq_s = time.perf_counter() - t0
     del x, r
-    # decode sample: two (batch, kv head) groups, 8 query heads each, T tokens
-    T, n_groups = 131072, 2
+    # decode sample: six (batch, kv head) groups, 8 query heads each, T tokens
+    T, n_groups = 131072, 6
     td_s = 0.0
     for h in range(n_groups):
         Pk = syn.rotation(d, syn.CFG_DECODE_128K, syn.T_K, h)
