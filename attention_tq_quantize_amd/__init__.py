@@ -24,7 +24,8 @@ TQ_LAYOUT_VECTOR, TQ_LAYOUT_BLOCK32 = 0, 1
 
 EXPORTS = [
     "tq_status_string", "tq_last_error_message", "tq_version", "tq_codebook_build",
-    "tq_quantizer_create", "tq_quantizer_create_wht", "tq_quantizer_destroy", "tq_quantizer_info", "tq_quantize",
+    "tq_quantizer_create", "tq_quantizer_create_wht", "tq_quantizer_destroy", "tq_quantizer_info",
+    "tq_quantizer_sizes", "tq_quantize",
     "tq_quantize_mse", "tq_quantize_prod", "tq_dequantize", "tq_inner_products",
     "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_append_workspace_size",
     "tq_decode_append_attention", "tq_search_workspace_size", "tq_search_scores", "tq_quantize_split",
@@ -78,8 +79,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tq_quantizer_destroy.argtypes = [_VP]
     lib.tq_quantizer_info.argtypes = [_VP, _VP, _VP, _VP, _VP]
     lib.tq_quantize.argtypes = [_VP, _I, _I64, _VP, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
-    lib.tq_quantize_mse.argtypes = [_VP, _VP, _I, _I64, _VP, _VP, _VP, _VP]
-    lib.tq_quantize_prod.argtypes = [_VP, _VP, _I, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+    lib.tq_quantize_mse.argtypes = [_VP, _VP, _I, _I64, _I64, _VP, _VP, _VP, _VP]
+    lib.tq_quantize_prod.argtypes = [_VP, _VP, _I, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+    lib.tq_quantizer_sizes.argtypes = [_VP, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
     lib.tq_dequantize.argtypes = [_VP, _I, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
     lib.tq_inner_products.argtypes = [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
     lib.tq_quantize_split.argtypes = [_VP, _I, _VP, _I, _VP, _I, _I64, ctypes.POINTER(Records), _VP]
@@ -219,17 +221,25 @@ def quantize(qs: Sequence[Quantizer], x, layout: str = "vector", rot_dbg: bool =
     return o
 
 
+def _rows(x):
+    """x [n, d] with unit column stride read in place (its row stride passed on), else a contiguous copy."""
+    if x.dim() == 2 and x.stride(1) == 1 and x.stride(0) >= x.shape[1]:
+        return x, x.stride(0)
+    x = x.contiguous()
+    return x, x.shape[-1]
+
+
 def quantize_mse(q: Quantizer, x, rot_dbg: bool = False, stream=None) -> dict:
     import torch
     lib = load()
     n = x.shape[0]
-    x = x.contiguous()
+    x, stride = _rows(x)
     dt = TQ_BF16 if x.dtype == torch.bfloat16 else TQ_F32
     o = {"codes": torch.empty((n, q.code_bytes), dtype=torch.uint8, device=x.device),
          "norms": torch.empty(n, dtype=torch.float32, device=x.device)}
     if rot_dbg:
         o["rot"] = torch.empty((n, q.d), dtype=torch.float32, device=x.device)
-    _check(lib.tq_quantize_mse(q.handle, _ptr(x), dt, n, _ptr(o["codes"]), _ptr(o["norms"]),
+    _check(lib.tq_quantize_mse(q.handle, _ptr(x), dt, n, stride, _ptr(o["codes"]), _ptr(o["norms"]),
                                _ptr(o.get("rot")), _stream(stream)), "tq_quantize_mse")
     return o
 
@@ -238,7 +248,7 @@ def quantize_prod(q: Quantizer, x, rot_dbg: bool = False, proj_dbg: bool = False
     import torch
     lib = load()
     n = x.shape[0]
-    x = x.contiguous()
+    x, stride = _rows(x)
     dt = TQ_BF16 if x.dtype == torch.bfloat16 else TQ_F32
     dev = x.device
     o = {"codes": torch.empty((n, max(q.code_bytes, 1)), dtype=torch.uint8, device=dev),
@@ -249,7 +259,7 @@ def quantize_prod(q: Quantizer, x, rot_dbg: bool = False, proj_dbg: bool = False
         o["rot"] = torch.empty((n, q.d), dtype=torch.float32, device=dev)
     if proj_dbg:
         o["proj"] = torch.empty((n, q.d), dtype=torch.float32, device=dev)
-    _check(lib.tq_quantize_prod(q.handle, _ptr(x), dt, n, _ptr(o["codes"]) if q.planes else None,
+    _check(lib.tq_quantize_prod(q.handle, _ptr(x), dt, n, stride, _ptr(o["codes"]) if q.planes else None,
                                 _ptr(o["signs"]), _ptr(o["norms"]), _ptr(o["rnorms"]), _ptr(o.get("rot")),
                                 _ptr(o.get("proj")), _stream(stream)), "tq_quantize_prod")
     return o

@@ -306,6 +306,13 @@ tq_status tq_quantizer_destroy(tq_quantizer* q) {
   return st;
 }
 
+tq_status tq_quantizer_sizes(const tq_quantizer* q, size_t* code_bytes, size_t* sign_bytes) {
+  if (!q) return set_error(TQ_ERR_INVALID_ARG, "sizes: handle is NULL");
+  if (code_bytes) *code_bytes = (size_t)q->planes * q->d / 8;
+  if (sign_bytes) *sign_bytes = q->variant == TQ_PROD ? (size_t)q->d / 8 : 0;
+  return TQ_OK;
+}
+
 tq_status tq_quantizer_info(const tq_quantizer* q, int* d, int* bits, tq_variant* variant,
                             int* code_planes) {
   if (!q) return set_error(TQ_ERR_INVALID_ARG, "info: handle is NULL");
@@ -316,10 +323,10 @@ tq_status tq_quantizer_info(const tq_quantizer* q, int* d, int* bits, tq_variant
   return TQ_OK;
 }
 
-tq_status tq_quantize(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group,
-                      const void* x, tq_dtype x_dtype, tq_layout layout, uint8_t* codes,
-                      uint8_t* signs, float* norms, float* rnorms, float* rot_dbg,
-                      float* proj_dbg, void* stream) {
+static tq_status quantize_impl(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group,
+                               const void* x, int64_t x_stride, tq_dtype x_dtype, tq_layout layout,
+                               uint8_t* codes, uint8_t* signs, float* norms, float* rnorms, float* rot_dbg,
+                               float* proj_dbg, void* stream) {
   if (!qz) return set_error(TQ_ERR_INVALID_ARG, "quantize: qz is NULL");
   if (n_groups < 1) return set_error(TQ_ERR_INVALID_ARG, fmt("quantize: n_groups=%d < 1", n_groups));
   if (n_per_group < 0) return set_error(TQ_ERR_INVALID_ARG, "quantize: n_per_group < 0");
@@ -331,6 +338,9 @@ tq_status tq_quantize(const tq_quantizer* const* qz, int n_groups, int64_t n_per
       return set_error(TQ_ERR_INVALID_ARG, "quantize: handles differ in (d, bits, variant)");
   }
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return set_error(TQ_ERR_INVALID_ARG, "quantize: unknown dtype");
+  if (x_stride < q0->d) return set_error(TQ_ERR_INVALID_ARG, fmt("quantize: x_stride=%lld < d=%d", (long long)x_stride, q0->d));
+  if ((x_stride * (x_dtype == TQ_F32 ? 4 : 2)) % 16)
+    return set_error(TQ_ERR_INVALID_ARG, "quantize: x_stride must be a multiple of 16 bytes");
   if (layout != TQ_LAYOUT_VECTOR && layout != TQ_LAYOUT_BLOCK32) return set_error(TQ_ERR_INVALID_ARG, "quantize: unknown layout");
   if (layout == TQ_LAYOUT_BLOCK32) {
     if (q0->variant != TQ_MSE) return set_error(TQ_ERR_UNSUPPORTED, "quantize: BLOCK32 layout is for mse quantizers");
@@ -348,26 +358,35 @@ tq_status tq_quantize(const tq_quantizer* const* qz, int n_groups, int64_t n_per
   if (misaligned(x, 16) || misaligned(codes, 4) || misaligned(signs, 4) || misaligned(rot_dbg, 16) ||
       misaligned(proj_dbg, 16))
     return set_error(TQ_ERR_INVALID_ARG, "quantize: x, rot_dbg and proj_dbg must be 16-byte aligned, codes and signs 4-byte aligned");
-  QuantizeLaunch a{qz, n_groups, n_per_group, x, x_dtype, layout, codes, signs, norms, rnorms, rot_dbg, proj_dbg};
+  QuantizeLaunch a{qz, n_groups, n_per_group, x, x_stride, x_dtype, layout, codes, signs, norms, rnorms, rot_dbg, proj_dbg};
   if (large_dim(q0->d)) return launch_quantize_large(a, (hipStream_t)stream);
   return launch_quantize(a, (hipStream_t)stream);
 }
 
-tq_status tq_quantize_mse(const tq_quantizer* q, const void* x, tq_dtype x_dtype, int64_t n,
+tq_status tq_quantize(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group,
+                      const void* x, tq_dtype x_dtype, tq_layout layout, uint8_t* codes,
+                      uint8_t* signs, float* norms, float* rnorms, float* rot_dbg,
+                      float* proj_dbg, void* stream) {
+  if (!qz || !qz[0]) return set_error(TQ_ERR_INVALID_ARG, "quantize: qz is NULL");
+  return quantize_impl(qz, n_groups, n_per_group, x, qz[0]->d, x_dtype, layout, codes, signs, norms, rnorms,
+                       rot_dbg, proj_dbg, stream);
+}
+
+tq_status tq_quantize_mse(const tq_quantizer* q, const void* x, tq_dtype x_dtype, int64_t n, int64_t x_stride,
                           uint8_t* codes, float* norms, float* rot_dbg, void* stream) {
   if (!q) return set_error(TQ_ERR_INVALID_ARG, "quantize_mse: handle is NULL");
   if (q->variant != TQ_MSE) return set_error(TQ_ERR_INVALID_ARG, "quantize_mse: handle is not TQ_MSE");
-  return tq_quantize(&q, 1, n, x, x_dtype, TQ_LAYOUT_VECTOR, codes, nullptr, norms, nullptr, rot_dbg,
-                     nullptr, stream);
+  return quantize_impl(&q, 1, n, x, x_stride, x_dtype, TQ_LAYOUT_VECTOR, codes, nullptr, norms, nullptr, rot_dbg,
+                       nullptr, stream);
 }
 
-tq_status tq_quantize_prod(const tq_quantizer* q, const void* x, tq_dtype x_dtype, int64_t n,
+tq_status tq_quantize_prod(const tq_quantizer* q, const void* x, tq_dtype x_dtype, int64_t n, int64_t x_stride,
                            uint8_t* codes, uint8_t* signs, float* norms, float* rnorms,
                            float* rot_dbg, float* proj_dbg, void* stream) {
   if (!q) return set_error(TQ_ERR_INVALID_ARG, "quantize_prod: handle is NULL");
   if (q->variant != TQ_PROD) return set_error(TQ_ERR_INVALID_ARG, "quantize_prod: handle is not TQ_PROD");
-  return tq_quantize(&q, 1, n, x, x_dtype, TQ_LAYOUT_VECTOR, codes, signs, norms, rnorms, rot_dbg,
-                     proj_dbg, stream);
+  return quantize_impl(&q, 1, n, x, x_stride, x_dtype, TQ_LAYOUT_VECTOR, codes, signs, norms, rnorms, rot_dbg,
+                       proj_dbg, stream);
 }
 
 tq_status tq_dequantize(const tq_quantizer* q, tq_layout layout, const uint8_t* codes,
@@ -482,7 +501,7 @@ tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, const in
   for (int p = 0; p < n_parts; ++p) {
     const tq_records& r = out[p];
     const tq_quantizer* one[1] = {qz[p]};
-    QuantizeLaunch a{one, 1, n, x, x_dtype, TQ_LAYOUT_VECTOR, r.codes, r.signs, r.norms, r.rnorms, r.rot_dbg, r.proj_dbg};
+    QuantizeLaunch a{one, 1, n, x, dim, x_dtype, TQ_LAYOUT_VECTOR, r.codes, r.signs, r.norms, r.rnorms, r.rot_dbg, r.proj_dbg};
     st = launch_quantize_fp32(a, chan.data() + off[p], dim, (hipStream_t)stream);
     if (st != TQ_OK) return st;
   }

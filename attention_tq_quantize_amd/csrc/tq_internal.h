@@ -69,6 +69,7 @@ struct QuantizeLaunch {
   int n_groups;
   int64_t n_per_group;
   const void* x;
+  int64_t x_stride;  // elements from one input vector to the next (>= d)
   tq_dtype x_dtype;
   tq_layout layout;
   uint8_t* codes;

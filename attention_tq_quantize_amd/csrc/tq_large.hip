@@ -690,6 +690,7 @@ static_assert(kLqVecs == kLqThreads, "one staged vector per thread");
 struct LqParams {
   const void* x;          // MODE 0: inputs; MODE 1: residuals (fp32)
   int64_t xg0, xgs, xoff; // input row of vector v of group grp: (grp + xg0) * xgs + v - xoff
+  int64_t x_stride;       // elements from one input row to the next
   int64_t n_per_group;    // outputs: row (group_base + grp) * n_per_group + v
   int64_t group_base;
   int64_t v_begin, v_end; // vectors of this launch, in every group
@@ -733,7 +734,7 @@ __global__ __launch_bounds__(kLqThreads, 2) void lq_kernel(LqParams prm) {
   const int grp = blockIdx.y;
   // staging: thread tid brings in vector v0 + tid (clamped to the last one)
   const int64_t sv = min(v0 + tid, prm.v_end - 1);
-  const uint8_t* xsrc = (const uint8_t*)prm.x + ((grp + prm.xg0) * prm.xgs + sv - prm.xoff) * (int64_t)d * XB;
+  const uint8_t* xsrc = (const uint8_t*)prm.x + ((grp + prm.xg0) * prm.xgs + sv - prm.xoff) * prm.x_stride * XB;
   const u32x4* msrc = prm.mat[grp] + (int64_t)cb * NKS * kLqMatFrag;
   u32x4* ldsm = lq_lds;
   u32x4* ldsx = lq_lds + kLqMatFrag;
@@ -1002,6 +1003,7 @@ static tq_status launch_lq(const QuantizeLaunch& a, hipStream_t stream) {
       prm.xg0 = g0;
       prm.xgs = n;
       prm.xoff = 0;
+      prm.x_stride = a.x_stride;
       prm.n_per_group = n;
       prm.group_base = g0;
       prm.v_begin = vb;
@@ -1043,6 +1045,7 @@ static tq_status launch_lq(const QuantizeLaunch& a, hipStream_t stream) {
       p2.xg0 = 0;
       p2.xgs = cap;
       p2.xoff = vb;
+      p2.x_stride = d;
       for (int g = 0; g < ng; ++g) p2.mat[g] = (const u32x4*)a.qz[g0 + g]->lq_sp;
       hipLaunchKernelGGL((lq_kernel<0, 1, true, true>), grid, dim3(kLqThreads), lds, stream, p2);
       st = launch_check("quantize (GEMM): QJL launch");
@@ -1063,7 +1066,7 @@ tq_status launch_quantize_large(const QuantizeLaunch& a, hipStream_t stream) {
   for (int g = 0; g < a.n_groups && gemm; ++g) gemm = a.qz[g]->lq_pi != nullptr;
   if (gemm) return launch_lq(a, stream);
   if (a.layout != TQ_LAYOUT_VECTOR) return set_error(TQ_ERR_UNSUPPORTED, "quantize: d > 256 supports the vector layout only");
-  return launch_quantize_fp32(a, nullptr, d, stream);
+  return launch_quantize_fp32(a, nullptr, a.x_stride, stream);
 }
 
 tq_status launch_quantize_fp32(const QuantizeLaunch& a, const uint16_t* chan, int64_t x_stride, hipStream_t stream) {

@@ -42,6 +42,7 @@ constexpr int kQThreads = 64 * kQWaves;
 
 struct QuantParams {
   const void* x;
+  int64_t x_row_bytes;    // bytes from one input vector to the next
   int64_t n_per_group;
   int n_groups;
   int64_t group_base;     // first group of this launch (vectors index from it)
@@ -76,9 +77,10 @@ struct XTile {
 // lane's row relative to it, clamped by the caller to an existing row (rows
 // past the end are read again and never stored).
 template <int D, bool XF32>
-__device__ __forceinline__ void load_tile(const uint8_t* base, unsigned rel, int g, XTile<D, XF32>& t) {
+__device__ __forceinline__ void load_tile(const uint8_t* base, unsigned rel, int64_t row_bytes, int g,
+                                          XTile<D, XF32>& t) {
   constexpr int ROW = D * (XF32 ? 4 : 2);
-  const u32x4* src = (const u32x4*)(base + rel * ROW + g * (ROW / 4));
+  const u32x4* src = (const u32x4*)(base + (int64_t)rel * row_bytes + g * (ROW / 4));
 #pragma unroll
   for (int i = 0; i < XTile<D, XF32>::NR; ++i) t.raw[i] = src[i];
 }
@@ -257,15 +259,15 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD)) void quantize
   int64_t step = (int64_t)blockIdx.x * kQWaves + wave;
 
   XTile<D, XF32> cur[T], nxt[T];
-  constexpr int XROW = D * (XF32 ? 4 : 2);
+  const int64_t xrow = prm.x_row_bytes;
   auto load_step = [&](int64_t s, XTile<D, XF32>(&dst)[T]) {
     const int64_t vb = s * 16 * T;  // first vector of step s
-    const uint8_t* base = (const uint8_t*)prm.x + (gbase + vb) * XROW;
+    const uint8_t* base = (const uint8_t*)prm.x + (gbase + vb) * xrow;
     const int64_t left = n - 1 - vb;  // last existing row, relative
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int rel = 16 * t + r16;
-      load_tile<D, XF32>(base, (unsigned)(rel < left ? rel : left), g, dst[t]);
+      load_tile<D, XF32>(base, (unsigned)(rel < left ? rel : left), xrow, g, dst[t]);
     }
   };
   if (step < steps) load_step(step, cur);  // in flight while the fragments are staged
@@ -569,6 +571,7 @@ tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream) {
     const int ng = a.n_groups - g0 < kMaxGroupsPerLaunch ? a.n_groups - g0 : kMaxGroupsPerLaunch;
     QuantParams prm{};
     prm.x = a.x;
+    prm.x_row_bytes = a.x_stride * (xf32 ? 4 : 2);
     prm.n_per_group = a.n_per_group;
     prm.n_groups = ng;
     prm.group_base = g0;

@@ -137,6 +137,11 @@ tq_status tq_quantizer_destroy(tq_quantizer* q);
  * sign bytes. */
 tq_status tq_quantizer_info(const tq_quantizer* q, int* d, int* bits, tq_variant* variant,
                             int* code_planes);
+/* Record sizes of one vector in the VECTOR layout ([NIK] "Step 2": b bits per
+ * coordinate; "TurboQuant proper": b-1 code bits plus one sign bit for prod):
+ * code_bytes = code_planes*d/8, sign_bytes = d/8 for TQ_PROD, 0 for TQ_MSE.
+ * Either pointer may be NULL. Errors: TQ_ERR_INVALID_ARG for a NULL handle. */
+tq_status tq_quantizer_sizes(const tq_quantizer* q, size_t* code_bytes, size_t* sign_bytes);
 
 /*
  * Q (quantize), grouped: vector i of group g (i < n_per_group) is
@@ -169,13 +174,18 @@ tq_status tq_quantize(const tq_quantizer* const* qz, int n_groups, int64_t n_per
                       float* proj_dbg, void* stream);
 
 /* Q_mse for n vectors with one quantizer, VECTOR layout ([NIK] Theorem 1's map
- * Q_mse : R^d -> {0,1}^(b d)). Same argument meanings as tq_quantize. */
+ * Q_mse : R^d -> {0,1}^(b d)). Same argument meanings as tq_quantize, except:
+ *   x_stride : elements from one input vector to the next (>= d; x_stride
+ *              times the element size a multiple of 16 bytes), so one head's
+ *              slice of a [n][heads*d] projection is read in place. */
 tq_status tq_quantize_mse(const tq_quantizer* q, const void* x, tq_dtype x_dtype, int64_t n,
-                          uint8_t* codes, float* norms, float* rot_dbg, void* stream);
+                          int64_t x_stride, uint8_t* codes, float* norms, float* rot_dbg, void* stream);
 
 /* Q_prod for n vectors, VECTOR layout ([NIK] Theorem 2's map
- * Q_prod : S^(d-1) -> [2^(b-1)]^d x {-1,1}^d x R, applied to x/|x| with |x| kept). */
+ * Q_prod : S^(d-1) -> [2^(b-1)]^d x {-1,1}^d x R, applied to x/|x| with |x| kept).
+ * x_stride as for tq_quantize_mse. */
 tq_status tq_quantize_prod(const tq_quantizer* q, const void* x, tq_dtype x_dtype, int64_t n,
+                           int64_t x_stride,
                            uint8_t* codes, uint8_t* signs, float* norms, float* rnorms,
                            float* rot_dbg, float* proj_dbg, void* stream);
 
