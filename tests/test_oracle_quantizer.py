@@ -150,6 +150,32 @@ def test_mse_distortion_is_data_oblivious(bits):
         assert abs(dots.mean() - (1 - D)) < 4 * se2 + 1e-12
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_requantize_is_idempotent(d):
+    """Q(Q^-1(Q(x))) = Q(x) for mse ([NIK] "Step 2": dequantize is the centroid
+    lookup then Pi^T). Re-quantizing sees y' = c[idx] / |c[idx]|, each centroid
+    scaled by s = 1/|c[idx]|. The symmetric codebook keeps every centroid in its
+    own cell (mids[i-1], mids[i]] exactly for s in (s_lo, s_hi), computed from the
+    codebook; when every observed s lies there the indices must come back
+    unchanged. A transposed Pi in either direction or a wrong centroid lookup
+    breaks it."""
+    Pi = syn.rotation(d, syn.CFG_TEST, syn.T_K, 3)
+    x = np.random.default_rng(1).standard_normal((2000, d))
+    for bits in (1, 2, 3, 4):
+        c = O.codebook(d, bits)
+        mids = (c[:-1] + c[1:]) / 2  # cell i is (mids[i-1], mids[i]]
+        pos = c > 0  # by symmetry the negative half mirrors it
+        s_hi = np.min(mids[pos[:-1]] / c[:-1][pos[:-1]]) if pos[:-1].any() else np.inf
+        inner = pos[1:] & (mids > 0)
+        s_lo = np.max(mids[inner] / c[1:][inner]) if inner.any() else 0.0
+        r = O.quantize_mse(x, Pi, c)
+        scale = 1.0 / np.linalg.norm(c[r["idx"]], axis=1)
+        assert scale.min() > s_lo and scale.max() < s_hi, (bits, s_lo, s_hi, scale.min(), scale.max())
+        xt = O.dequantize_mse(r["idx"], r["norms"], Pi, c)
+        assert np.array_equal(O.quantize_mse(xt, Pi, c)["idx"], r["idx"])
+        assert not np.array_equal(O.quantize_mse(xt, Pi.T, c)["idx"], r["idx"])
+
+
 def test_qjl_unbiased_and_variance():
     """QJL lemma: E <y, Q^-1(Q(x))> = <y, x>, Var = (pi/2 |y|^2 - <x,y>^2)/d <= pi/(2d) |y|^2."""
     d, trials = 32, 10000
