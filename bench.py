@@ -220,6 +220,52 @@ def vector_search(tq, syn, torch, dev, n=100000, m=16, bits=3):
     return out
 
 
+def decode_1m(tq, syn, torch, dev, reps=20):
+    """Decode attention at 1M context: B=1, 64/8 heads, d=128, T=1,048,576, keys
+    TurboQuant_prod b=3, values TurboQuant_mse b=3, KV vectors with a per-token
+    LogNormal(0, 0.5) scale; the same 905,969,664 algorithmic bytes per call as
+    the 128K batch, in one sequence (split-context over 1M tokens)."""
+    d, Hq, Hkv, T = 128, 64, 8, 1 << 20
+    kq = [tq.Quantizer(d, 3, "prod", syn.rotation(d, syn.CFG_DECODE_1M, syn.T_K, h),
+                       syn.gaussian_matrix(d, syn.CFG_DECODE_1M, syn.T_K, h)) for h in range(Hkv)]
+    vq = [tq.Quantizer(d, 3, "mse", syn.rotation(d, syn.CFG_DECODE_1M, syn.T_V, h)) for h in range(Hkv)]
+    kcodes = torch.empty((1, Hkv, T, 32), dtype=torch.uint8, device=dev)
+    ksigns = torch.empty((1, Hkv, T, 16), dtype=torch.uint8, device=dev)
+    knorms = torch.empty((1, Hkv, T), dtype=torch.float32, device=dev)
+    krn = torch.empty((1, Hkv, T), dtype=torch.float32, device=dev)
+    vcodes = torch.empty((1, Hkv, T // 32, 4 * 3 * d), dtype=torch.uint8, device=dev)
+    vnorms = torch.empty((1, Hkv, T), dtype=torch.float32, device=dev)
+    xk = syn.kv_vectors_device(Hkv, T, d, syn.CFG_DECODE_1M, syn.T_K, dev, lognormal_sigma=0.5)
+    tq.quantize(kq, xk, layout="vector", out={"codes": kcodes[0].view(Hkv, -1), "signs": ksigns[0],
+                                              "norms": knorms[0], "rnorms": krn[0]})
+    del xk
+    xv = syn.kv_vectors_device(Hkv, T, d, syn.CFG_DECODE_1M, syn.T_V, dev, lognormal_sigma=0.5)
+    tq.quantize(vq, xv, layout="block32", out={"codes": vcodes[0].view(Hkv, -1), "norms": vnorms[0]})
+    del xv
+    kcache = tq.KVCache(kq, knorms, kcodes, ksigns, krn)
+    vcache = tq.KVCache(vq, vnorms, vcodes)
+    q = torch.from_numpy(syn.decode_queries(1, Hq, d, syn.CFG_DECODE_1M)).to(dev).to(torch.bfloat16)
+    lens = torch.full((1,), T, dtype=torch.int32, device=dev)
+    ws = torch.empty(tq.decode_workspace_size(1, Hq, Hkv, d, T, kcache, vcache), dtype=torch.uint8, device=dev)
+    out = torch.empty((1, Hq, d), dtype=torch.float32, device=dev)
+    run = lambda: tq.decode_attention(q, kcache, vcache, lens, 1 / math.sqrt(d), max_ctx=T, out=out, workspace=ws)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    avg = sum(ms) / reps
+    nbytes = Hkv * T * 108
+    return {"workload": "decode B=1, 64/8 heads, d=128, ctx 1048576, keys prod b=3, values mse b=3",
+            "ms": round(avg, 4), "ms_p10_p90": [round(ms[reps // 10], 4), round(ms[(9 * reps) // 10], 4)],
+            "gb_s": round(nbytes / (avg * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def outlier_split(tq, syn, torch, dev, w):
     """Outlier-channel mixed precision on the layer's KV (8 heads x 32768 tokens,
     d = 128): per head, the 32 channels of largest RMS at 3 bits and the other 96
@@ -357,6 +403,7 @@ def main():
 
     vsearch = vector_search(tq, syn, torch, dev)
     split = outlier_split(tq, syn, torch, dev, w)
+    dec1m = decode_1m(tq, syn, torch, dev)
 
     traffic = decode_traffic(args.traffic)
     d_gbs = d_bytes / (d_avg * 1e-3) / 1e9
@@ -389,6 +436,7 @@ def main():
             "decode_append_ms": round(a_ms, 4),
             "vector_search": vsearch,
             "outlier_split": split,
+            "decode_1m": dec1m,
             "wall_s_timed_region": round(wall, 3),
         },
         "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
