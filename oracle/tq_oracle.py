@@ -18,7 +18,7 @@ __all__ = [
     "qjl", "qjl_inverse", "pack_vector_layout", "unpack_vector_layout", "pack_bits",
     "unpack_bits", "pack_block_layout", "unpack_block_layout", "attention",
     "decode_attention", "inner_products", "QJL_SCALE", "hadamard", "wht_rotation",
-    "quantize_split", "dequantize_split",
+    "quantize_split", "dequantize_split", "decode_attention_split",
 ]
 
 
@@ -293,6 +293,29 @@ def dequantize_split(results, parts, dim: int):
             sub = dequantize_mse(r["idx"], r["norms"], p["Pi"], p["centroids"])
         xt[:, np.asarray(p["channels"], dtype=np.int64)] = sub
     return xt
+
+
+def decode_attention_split(q, keys, values, ctx_lens, scale, dim: int):
+    """Decode attention over split caches: keys[b][g] and values[b][g] are
+    (per-part results over the cached tokens, parts) as quantize_split returns
+    them for KV head g of batch b. Every query head h of KV head g = h // (Hq/Hkv)
+    attends the first ctx_lens[b] tokens of the dequantized caches (channels no
+    part keeps are 0); an empty context gives 0."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, _ = q.shape
+    Hkv = len(keys[0])
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, dim))
+    for b in range(B):
+        n = int(ctx_lens[b])
+        if n == 0:
+            continue
+        for g in range(Hkv):
+            K = dequantize_split(*keys[b][g], dim)[:n]
+            V = dequantize_split(*values[b][g], dim)[:n]
+            for h in range(G):
+                out[b, g * G + h] = attention(q[b, g * G + h], K, V, scale)[0]
+    return out
 
 
 # ---------------------------------------------------------------------------

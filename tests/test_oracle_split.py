@@ -115,3 +115,45 @@ def test_split_prod_unbiased_with_closed_form_variance():
         want = want + (math.pi / 2 - 1 / dp) * dp * _cost(dp, b - 1) * yy * xx / dp
     ratio = np.mean(err ** 2) / np.mean(want)
     assert abs(ratio - 1) < 0.06, ratio
+
+
+def test_split_decode_with_one_full_part_is_plain_decode():
+    """One key part and one value part holding every channel in order reduce the
+    split decode to the plain decode over the same records."""
+    B, Hq, Hkv, d, T = 2, 4, 2, 32, 40
+    lens = np.array([40, 0])
+    ch = np.arange(d)
+    kc = {"variant": "prod", "bits": 3, "d": d, "max_ctx": T, "Pi": [], "S": [],
+          "codes": np.zeros((B, Hkv, T, 2 * d // 8), np.uint8), "signs": np.zeros((B, Hkv, T, d // 8), np.uint8),
+          "norms": np.zeros((B, Hkv, T), np.float32), "rnorms": np.zeros((B, Hkv, T), np.float32)}
+    vc = {"variant": "mse", "bits": 3, "d": d, "max_ctx": T, "Pi": [],
+          "codes": np.zeros((B, Hkv, T // 32 if T % 32 == 0 else 0, 4 * 3 * d), np.uint8),
+          "norms": np.zeros((B, Hkv, T), np.float32)}
+    keys = [[None] * Hkv for _ in range(B)]
+    values = [[None] * Hkv for _ in range(B)]
+    kparts = [_part(ch, "prod", 3, 30 + g) for g in range(Hkv)]
+    vparts = [_part(ch, "mse", 3, 40 + g) for g in range(Hkv)]
+    Tp = 64  # block layout needs whole 32-token blocks: pad the value records
+    vc["codes"] = np.zeros((B, Hkv, Tp // 32, 4 * 3 * d), np.uint8)
+    for b in range(B):
+        for g in range(Hkv):
+            x = syn.kv_vectors(Tp, d, syn.CFG_TEST, syn.T_K, b, g)
+            xv = syn.kv_vectors(Tp, d, syn.CFG_TEST, syn.T_V, b, g)
+            rk = O.quantize_split(x[:T], [kparts[g]])
+            rv = O.quantize_split(xv, [vparts[g]])
+            keys[b][g] = (rk, [kparts[g]])
+            values[b][g] = ([{k: (v[:T] if hasattr(v, "__len__") else v) for k, v in rv[0].items()}], [vparts[g]])
+            kc["codes"][b, g] = O.pack_vector_layout(rk[0]["idx"], 2)
+            kc["signs"][b, g] = O.pack_bits(rk[0]["signs"])
+            kc["norms"][b, g] = rk[0]["norms"]
+            kc["rnorms"][b, g] = rk[0]["rnorms"]
+            vc["codes"][b, g] = O.pack_block_layout(rv[0]["idx"], 3).reshape(Tp // 32, -1)
+            vc["norms"][b, g] = rv[0]["norms"][:T]
+    kc["Pi"] = np.stack([p["Pi"] for p in kparts])
+    kc["S"] = np.stack([p["S"] for p in kparts])
+    vc["Pi"] = np.stack([p["Pi"] for p in vparts])
+    q = syn.decode_queries(B, Hq, d, syn.CFG_TEST)
+    got = O.decode_attention_split(q, keys, values, lens, 0.2, d)
+    want = O.decode_attention(q, kc, vc, lens, 0.2)
+    assert np.abs(got - want).max() < 1e-12
+    assert np.all(got[1] == 0)
