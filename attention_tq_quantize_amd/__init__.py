@@ -29,7 +29,7 @@ EXPORTS = [
     "tq_quantize_mse", "tq_quantize_prod", "tq_dequantize", "tq_inner_products",
     "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_append_workspace_size",
     "tq_decode_append_attention", "tq_search_workspace_size", "tq_search_scores", "tq_quantize_split",
-    "tq_inner_products_split",
+    "tq_inner_products_split", "tq_decode_split_workspace_size", "tq_decode_attention_split",
 ]
 
 
@@ -52,6 +52,11 @@ class PackedKV(ctypes.Structure):
 class Records(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("signs", ctypes.c_void_p), ("norms", ctypes.c_void_p),
                 ("rnorms", ctypes.c_void_p), ("rot_dbg", ctypes.c_void_p), ("proj_dbg", ctypes.c_void_p)]
+
+
+class SplitCache(ctypes.Structure):
+    _fields_ = [("n_parts", ctypes.c_int), ("qz", ctypes.POINTER(ctypes.c_void_p)),
+                ("channels", ctypes.c_void_p), ("rec", ctypes.c_void_p)]
 
 
 _lib = None
@@ -86,6 +91,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tq_inner_products.argtypes = [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
     lib.tq_quantize_split.argtypes = [_VP, _I, _VP, _I, _VP, _I, _I64, ctypes.POINTER(Records), _VP]
     lib.tq_inner_products_split.argtypes = [_VP, _I, _VP, _I, _VP, _I64, ctypes.POINTER(Records), _I64, _VP, _VP]
+    lib.tq_decode_split_workspace_size.argtypes = [ctypes.POINTER(AttnShape), ctypes.POINTER(SplitCache),
+                                                   ctypes.POINTER(SplitCache), ctypes.POINTER(ctypes.c_size_t)]
+    lib.tq_decode_attention_split.argtypes = [ctypes.POINTER(AttnShape), _VP, ctypes.POINTER(SplitCache),
+                                              ctypes.POINTER(SplitCache), _VP, _F, _VP, _VP, ctypes.c_size_t, _VP]
     lib.tq_search_workspace_size.argtypes = [_VP, _I64, ctypes.POINTER(ctypes.c_size_t)]
     lib.tq_search_scores.argtypes = [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _VP]
     lib.tq_decode_workspace_size.argtypes = [ctypes.POINTER(AttnShape), ctypes.POINTER(PackedKV),
@@ -415,6 +424,64 @@ def decode_attention(q, kcache: KVCache, vcache: KVCache, ctx_lens, scale: Optio
     _check(lib.tq_decode_attention(ctypes.byref(shape), _ptr(q.contiguous()), ctypes.byref(kp), ctypes.byref(vp),
                                    _ptr(ctx_lens), float(scale), _ptr(out), _ptr(scores), _ptr(workspace),
                                    workspace.numel(), _stream(stream)), "tq_decode_attention")
+    return out
+
+
+@dataclass
+class SplitKV:
+    """One side (keys or values) of a split cache: parts[p] = (quantizers per KV head,
+    channel list, records dict of device tensors [B, Hkv, T, ...] / [B, Hkv, T])."""
+    parts: Sequence[tuple]
+
+    def packed(self, n_kv_heads):
+        import numpy as np
+        P = len(self.parts)
+        qz = (ctypes.c_void_p * (P * n_kv_heads))()
+        for p, (qs, _, _) in enumerate(self.parts):
+            assert len(qs) == n_kv_heads
+            for g, q in enumerate(qs):
+                qz[p * n_kv_heads + g] = q.handle.value
+        ch = np.ascontiguousarray(np.concatenate([np.asarray(c, dtype=np.int32).ravel() for _, c, _ in self.parts]),
+                                  dtype=np.int32)
+        recs = _records([r for _, _, r in self.parts])
+        sc = SplitCache(P, qz, ch.ctypes.data, ctypes.cast(recs, ctypes.c_void_p))
+        return sc, (qz, ch, recs)  # keep the arrays alive for the call
+
+
+def decode_split_workspace_size(batch, n_q_heads, n_kv_heads, dim, max_ctx, k: SplitKV, v: SplitKV) -> int:
+    lib = load()
+    shape = AttnShape(batch, n_q_heads, n_kv_heads, dim, max_ctx)
+    kc, ka = k.packed(n_kv_heads)
+    vc, va = v.packed(n_kv_heads)
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.tq_decode_split_workspace_size(ctypes.byref(shape), ctypes.byref(kc), ctypes.byref(vc),
+                                              ctypes.byref(nbytes)), "tq_decode_split_workspace_size")
+    return nbytes.value
+
+
+def decode_attention_split(q, k: SplitKV, v: SplitKV, ctx_lens, scale: Optional[float] = None,
+                           max_ctx: Optional[int] = None, out=None, workspace=None, stream=None):
+    """Decode attention over outlier-split caches (tq_decode_attention_split).
+    q: [B, Hq, dim] bfloat16; ctx_lens: int32 [B] (device). Returns out [B, Hq, dim] float32."""
+    import torch
+    lib = load()
+    B, Hq, dim = q.shape
+    Hkv = len(k.parts[0][0])
+    T = int(max_ctx if max_ctx is not None else k.parts[0][2]["norms"].shape[-1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(dim)
+    shape = AttnShape(B, Hq, Hkv, dim, T)
+    kc, ka = k.packed(Hkv)
+    vc, va = v.packed(Hkv)
+    if workspace is None:
+        workspace = torch.empty(max(decode_split_workspace_size(B, Hq, Hkv, dim, T, k, v), 1), dtype=torch.uint8,
+                                device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, dim), dtype=torch.float32, device=q.device)
+    _check(lib.tq_decode_attention_split(ctypes.byref(shape), _ptr(q.contiguous()), ctypes.byref(kc),
+                                         ctypes.byref(vc), _ptr(ctx_lens), float(scale), _ptr(out),
+                                         _ptr(workspace), workspace.numel(), _stream(stream)),
+           "tq_decode_attention_split")
     return out
 
 

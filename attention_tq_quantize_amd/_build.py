@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
-SOURCES = ["tq_capi.cpp", "tq_codebook.cpp", "tq_quantize.hip", "tq_aux.hip", "tq_decode.hip", "tq_append.hip", "tq_large.hip"]
+SOURCES = ["tq_capi.cpp", "tq_codebook.cpp", "tq_quantize.hip", "tq_aux.hip", "tq_decode.hip", "tq_append.hip", "tq_large.hip", "tq_split_decode.hip"]
 OBJDIR = os.path.join(os.path.dirname(HERE), "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -534,6 +534,127 @@ tq_status tq_inner_products_split(const tq_quantizer* const* qz, int n_parts, co
   return TQ_OK;
 }
 
+// ---- decode attention over split caches ----
+struct SplitPlan {
+  int n_splits = 1;
+  int64_t split_tokens = 0;
+  int dk = 0, dv = 0;
+  size_t bytes = 0;
+};
+
+static tq_status check_split_side(const tq_split_cache* c, const tq_attn_shape* s, bool values, SplitSide* side,
+                                  int* total) {
+  const char* what = values ? "split decode (values)" : "split decode (keys)";
+  if (!c || !c->qz || !c->channels || !c->rec) return set_error(TQ_ERR_INVALID_ARG, fmt("%s: NULL cache description", what));
+  if (c->n_parts < 1 || c->n_parts > kSplitMaxParts)
+    return set_error(TQ_ERR_UNSUPPORTED, fmt("%s: n_parts outside [1, %d]", what, kSplitMaxParts));
+  side->n_parts = c->n_parts;
+  side->qz = c->qz;
+  side->channels = c->channels;
+  int off = 0;
+  for (int p = 0; p < c->n_parts; ++p) {
+    const tq_quantizer* q0 = c->qz[p * s->n_kv_heads];
+    if (!q0) return set_error(TQ_ERR_INVALID_ARG, fmt("%s: part %d handle is NULL", what, p));
+    for (int g = 1; g < s->n_kv_heads; ++g) {
+      const tq_quantizer* qg = c->qz[p * s->n_kv_heads + g];
+      if (!qg || qg->d != q0->d || qg->bits != q0->bits || qg->variant != q0->variant)
+        return set_error(TQ_ERR_INVALID_ARG, fmt("%s: part %d handles differ across KV heads", what, p));
+    }
+    if (q0->d % 32) return set_error(TQ_ERR_UNSUPPORTED, fmt("%s: part %d dimension %d is not a multiple of 32", what, p, q0->d));
+    if (q0->planes > 4) return set_error(TQ_ERR_UNSUPPORTED, fmt("%s: part %d planes", what, p));
+    if (values && q0->variant != TQ_MSE) return set_error(TQ_ERR_UNSUPPORTED, fmt("%s: value parts must be mse", what));
+    const tq_records& r = c->rec[p];
+    const bool qjl = q0->variant == TQ_PROD;
+    if (!r.norms || (q0->planes > 0 && !r.codes) || (qjl && (!r.signs || !r.rnorms)))
+      return set_error(TQ_ERR_INVALID_ARG, fmt("%s: part %d record buffer is NULL", what, p));
+    if (misaligned(r.codes, 4) || misaligned(r.signs, 4))
+      return set_error(TQ_ERR_INVALID_ARG, fmt("%s: part %d codes and signs must be 4-byte aligned", what, p));
+    side->codes[p] = r.codes;
+    side->signs[p] = r.signs;
+    side->norms[p] = r.norms;
+    side->rnorms[p] = r.rnorms;
+    off += q0->d;
+  }
+  if (off > s->head_dim) return set_error(TQ_ERR_INVALID_ARG, fmt("%s: parts cover %d channels of %d", what, off, s->head_dim));
+  std::vector<char> seen(s->head_dim, 0);
+  for (int j = 0; j < off; ++j) {
+    const int ch = c->channels[j];
+    if (ch < 0 || ch >= s->head_dim) return set_error(TQ_ERR_INVALID_ARG, fmt("%s: channels[%d]=%d out of range", what, j, ch));
+    if (seen[ch]) return set_error(TQ_ERR_INVALID_ARG, fmt("%s: channel %d listed twice", what, ch));
+    seen[ch] = 1;
+  }
+  *total = off;
+  return TQ_OK;
+}
+
+static tq_status plan_split_decode(const tq_attn_shape* s, const tq_split_cache* k, const tq_split_cache* v,
+                                   SplitDecodeLaunch* L, SplitPlan* plan) {
+  if (!s) return set_error(TQ_ERR_INVALID_ARG, "split decode: shape is NULL");
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->max_ctx < 1)
+    return set_error(TQ_ERR_INVALID_ARG, "split decode: empty shape");
+  if (s->n_kv_heads > kSplitMaxKv) return set_error(TQ_ERR_UNSUPPORTED, fmt("split decode: more than %d KV heads", kSplitMaxKv));
+  if (s->n_q_heads % s->n_kv_heads || s->n_q_heads / s->n_kv_heads > kSplitMaxGroup)
+    return set_error(TQ_ERR_UNSUPPORTED, fmt("split decode: query heads per KV head must divide and be at most %d", kSplitMaxGroup));
+  if (s->head_dim < 16 || s->head_dim > kSplitMaxDecodeDim)
+    return set_error(TQ_ERR_UNSUPPORTED, fmt("split decode: head_dim outside [16, %d]", kSplitMaxDecodeDim));
+  if (s->max_ctx > ((int64_t)1 << 31)) return set_error(TQ_ERR_UNSUPPORTED, "split decode: max_ctx > 2^31");
+  tq_status st = check_split_side(k, s, false, &L->k, &plan->dk);
+  if (st != TQ_OK) return st;
+  st = check_split_side(v, s, true, &L->v, &plan->dv);
+  if (st != TQ_OK) return st;
+  // about 1024 workgroups, splits of at least 256 tokens
+  const int64_t bg = (int64_t)s->batch * s->n_kv_heads;
+  int64_t ns = (1024 + bg - 1) / bg;
+  const int64_t blocks = (s->max_ctx + 255) / 256;
+  if (ns > blocks) ns = blocks;
+  if (ns < 1) ns = 1;
+  int64_t per = (s->max_ctx + ns - 1) / ns;
+  per = (per + 255) / 256 * 256;
+  ns = (s->max_ctx + per - 1) / per;
+  if (ns > 65535) return set_error(TQ_ERR_UNSUPPORTED, "split decode: too many splits");
+  plan->n_splits = (int)ns;
+  plan->split_tokens = per;
+  plan->bytes = (size_t)s->batch * s->n_q_heads * ns * (plan->dv + 2) * sizeof(float);
+  L->B = s->batch;
+  L->Hq = s->n_q_heads;
+  L->Hkv = s->n_kv_heads;
+  L->dim = s->head_dim;
+  L->max_ctx = s->max_ctx;
+  L->n_splits = plan->n_splits;
+  L->split_tokens = per;
+  return TQ_OK;
+}
+
+tq_status tq_decode_split_workspace_size(const tq_attn_shape* shape, const tq_split_cache* k, const tq_split_cache* v,
+                                         size_t* bytes) {
+  if (!bytes) return set_error(TQ_ERR_INVALID_ARG, "split decode workspace: bytes is NULL");
+  SplitDecodeLaunch L{};
+  SplitPlan plan;
+  tq_status st = plan_split_decode(shape, k, v, &L, &plan);
+  if (st != TQ_OK) return st;
+  *bytes = plan.bytes;
+  return TQ_OK;
+}
+
+tq_status tq_decode_attention_split(const tq_attn_shape* shape, const void* q, const tq_split_cache* k,
+                                    const tq_split_cache* v, const int32_t* ctx_lens, float scale, float* out,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  SplitDecodeLaunch L{};
+  SplitPlan plan;
+  tq_status st = plan_split_decode(shape, k, v, &L, &plan);
+  if (st != TQ_OK) return st;
+  if (!q || !ctx_lens || !out) return set_error(TQ_ERR_INVALID_ARG, "split decode: q, ctx_lens or out is NULL");
+  if (!std::isfinite(scale)) return set_error(TQ_ERR_INVALID_ARG, "split decode: scale is not finite");
+  if (!workspace || ws_bytes < plan.bytes)
+    return set_error(TQ_ERR_WORKSPACE, fmt("split decode: workspace needs %zu bytes, got %zu", plan.bytes, workspace ? ws_bytes : (size_t)0));
+  L.q = q;
+  L.lens = ctx_lens;
+  L.scale = scale;
+  L.out = out;
+  L.workspace = workspace;
+  return launch_split_decode(L, (hipStream_t)stream);
+}
+
 static tq_status check_decode(const tq_attn_shape* s, const tq_packed_kv* k, const tq_packed_kv* v,
                               DecodePlan* plan) {
   if (!s || !k || !v) return set_error(TQ_ERR_INVALID_ARG, "decode: NULL shape or cache");

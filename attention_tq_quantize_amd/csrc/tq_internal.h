@@ -90,6 +90,33 @@ tq_status launch_inner_products_fp32(const tq_quantizer* q, const float* y, int6
                                      const float* norms, const float* rnorms, int64_t n, float* out,
                                      hipStream_t stream);
 constexpr int kSplitMaxDim = 512;  // widest input row of a channel split
+// decode attention over split caches (tq_split_decode.hip)
+constexpr int kSplitMaxParts = 4;
+constexpr int kSplitMaxKv = 8;
+constexpr int kSplitMaxGroup = 8;
+constexpr int kSplitMaxDecodeDim = 256;
+struct SplitSide {
+  int n_parts;
+  const tq_quantizer* const* qz;  // [n_parts][Hkv]
+  const int32_t* channels;        // host, concatenated part lists
+  const uint8_t* codes[kSplitMaxParts];
+  const uint8_t* signs[kSplitMaxParts];
+  const float* norms[kSplitMaxParts];
+  const float* rnorms[kSplitMaxParts];
+};
+struct SplitDecodeLaunch {
+  int B, Hq, Hkv, dim;
+  int64_t max_ctx;
+  const void* q;
+  const int32_t* lens;
+  float scale;
+  float* out;
+  void* workspace;
+  int n_splits;
+  int64_t split_tokens;
+  SplitSide k, v;
+};
+tq_status launch_split_decode(const SplitDecodeLaunch& L, hipStream_t stream);
 // d a multiple of 128 in (256, 4096]: the GEMM quantize tables, built at creation
 bool lq_supported(int d);
 tq_status build_large_tables(tq_quantizer* q);

@@ -266,6 +266,65 @@ def decode_1m(tq, syn, torch, dev, reps=20):
             "gb_s": round(nbytes / (avg * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def outlier_split_decode(tq, syn, torch, dev, reps=10):
+    """Decode attention over an outlier-split cache at the 128K batch shape (B=8,
+    64/8 heads, d=128, ctx 131072): keys TurboQuant_prod with the 32 largest-RMS
+    channels at 3 bits and the other 96 at 2, values TurboQuant_mse with the same
+    bit split (96 B per (token, KV head) against 108 B for the uniform 3-bit cache);
+    tq_decode_attention_split (generic fp32 kernels)."""
+    B, Hq, Hkv, d, T = 8, 64, 8, 128, 131072
+    sides = []
+    for tensor, var in ((syn.T_K, "prod"), (syn.T_V, "mse")):
+        qs_p = [[], []]
+        chans_p = [None, None]
+        sample = syn.kv_vectors_device(Hkv, 4096, d, syn.CFG_DECODE_128K, tensor, dev, seed_offset=0)
+        order = torch.argsort(sample[0].float().pow(2).mean(dim=0), descending=True, stable=True).cpu().numpy()
+        chans_p = [order[:32], order[32:]]
+        for p, bits in enumerate((3, 2)):
+            dp = len(chans_p[p])
+            for g in range(Hkv):
+                S = syn.gaussian_matrix(dp, syn.CFG_DECODE_128K, tensor, 300 + 10 * p + g) if var == "prod" else None
+                qs_p[p].append(tq.Quantizer(dp, bits, var, syn.rotation(dp, syn.CFG_DECODE_128K, tensor, 300 + 10 * p + g), S))
+        recs = []
+        for p in range(2):
+            q0 = qs_p[p][0]
+            r = {"norms": torch.empty((B, Hkv, T), dtype=torch.float32, device=dev),
+                 "codes": torch.empty((B, Hkv, T, q0.code_bytes), dtype=torch.uint8, device=dev)}
+            if var == "prod":
+                r["signs"] = torch.empty((B, Hkv, T, q0.d // 8), dtype=torch.uint8, device=dev)
+                r["rnorms"] = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+            recs.append(r)
+        for b in range(B):
+            x = syn.kv_vectors_device(Hkv, T, d, syn.CFG_DECODE_128K, tensor, dev, seed_offset=b)
+            for g in range(Hkv):
+                got = tq.quantize_split([qs_p[0][g], qs_p[1][g]], chans_p, x[g])
+                for p in range(2):
+                    for key, val in got[p].items():
+                        recs[p][key][b, g].copy_(val.view(recs[p][key][b, g].shape))
+            del x
+        sides.append(tq.SplitKV([(qs_p[p], chans_p[p], recs[p]) for p in range(2)]))
+    k, v = sides
+    q = torch.from_numpy(syn.decode_queries(B, Hq, d, syn.CFG_DECODE_128K)).to(dev).to(torch.bfloat16)
+    lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+    ws = torch.empty(tq.decode_split_workspace_size(B, Hq, Hkv, d, T, k, v), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    run = lambda: tq.decode_attention_split(q, k, v, lens, 1 / math.sqrt(d), out=out, workspace=ws)
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = B * Hkv * T * 96
+    return {"workload": "split decode B=8, 64/8 heads, d=128, ctx 131072; K prod 32 ch x 3 b + 96 ch x 2 b, "
+                        "V mse 32 ch x 3 b + 96 ch x 2 b", "bytes_per_token_head": 96, "ms": round(ms, 3),
+            "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def outlier_split(tq, syn, torch, dev, w):
     """Outlier-channel mixed precision on the layer's KV (8 heads x 32768 tokens,
     d = 128): per head, the 32 channels of largest RMS at 3 bits and the other 96
@@ -404,6 +463,7 @@ def main():
     vsearch = vector_search(tq, syn, torch, dev)
     split = outlier_split(tq, syn, torch, dev, w)
     dec1m = decode_1m(tq, syn, torch, dev)
+    split_dec = outlier_split_decode(tq, syn, torch, dev)
 
     traffic = decode_traffic(args.traffic)
     d_gbs = d_bytes / (d_avg * 1e-3) / 1e9
@@ -437,6 +497,7 @@ def main():
             "vector_search": vsearch,
             "outlier_split": split,
             "decode_1m": dec1m,
+            "outlier_split_decode": split_dec,
             "wall_s_timed_region": round(wall, 3),
         },
         "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

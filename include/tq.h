@@ -373,6 +373,45 @@ tq_status tq_decode_append_attention(const tq_attn_shape* shape, const void* q, 
                                      const tq_packed_kv* v, const int32_t* ctx_lens, float scale,
                                      float* out, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Decode attention over KV caches quantized with an outlier-channel split
+ * ([NIK] "Experiments", KV cache: outlier channels at more bits; the same
+ * attention as tq_decode_attention, scores and outputs over the channels the
+ * parts keep). Each side (keys, values) is a split of the head's channels into
+ * parts, part p quantized per KV head in the VECTOR layout (records
+ * [B][n_kv_heads][max_ctx], as tq_quantize_split writes them per head):
+ *   s_t = scale * sum_p <q restricted to key part p's channels, k~_{p,t}>
+ *   out[b,h] = sum_{t < ctx_lens[b]} softmax(s)_t v~_t, each value part written
+ *   to its channels (channels no value part keeps are 0; ctx_lens[b] <= 0 gives
+ *   0, lengths above max_ctx attend max_ctx tokens).
+ *   qz       : host [n_parts * n_kv_heads]; part p of KV head g is
+ *              qz[p * n_kv_heads + g]; the handles of one part share (d, bits,
+ *              variant); d a multiple of 32; keys mse or prod, values mse;
+ *              codes and signs 4-byte aligned.
+ *   channels : host int32, the parts' channel lists concatenated (entries in
+ *              [0, head_dim), none repeated).
+ *   rec      : host [n_parts]; rec[p] holds part p's device arrays.
+ * head_dim = the full channel count (at most 256), at most 8 KV heads and 8
+ * query heads per KV head. q: device bf16 [B][n_q_heads][head_dim];
+ * out: device float32 [B][n_q_heads][head_dim]; workspace: at least
+ * tq_decode_split_workspace_size() bytes (per-split softmax partials).
+ * Generic fp32 kernels, split context with a log-sum-exp combine
+ * (deterministic). Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED (limits
+ * above), TQ_ERR_WORKSPACE.
+ */
+typedef struct {
+  int n_parts;
+  const tq_quantizer* const* qz;
+  const int32_t* channels;
+  const tq_records* rec;
+} tq_split_cache;
+tq_status tq_decode_split_workspace_size(const tq_attn_shape* shape, const tq_split_cache* k,
+                                         const tq_split_cache* v, size_t* bytes);
+tq_status tq_decode_attention_split(const tq_attn_shape* shape, const void* q, const tq_split_cache* k,
+                                    const tq_split_cache* v, const int32_t* ctx_lens, float scale,
+                                    float* out, void* workspace, size_t ws_bytes, void* stream);
+
+
 #ifdef __cplusplus
 }
 #endif
