@@ -602,14 +602,14 @@ static tq_status plan_split_decode(const tq_attn_shape* s, const tq_split_cache*
   if (st != TQ_OK) return st;
   st = check_split_side(v, s, true, &L->v, &plan->dv);
   if (st != TQ_OK) return st;
-  // about 1024 workgroups, splits of at least 256 tokens
+  // one wave per context split, about 4096 waves (16 per CU), splits a multiple of 32 tokens
   const int64_t bg = (int64_t)s->batch * s->n_kv_heads;
-  int64_t ns = (1024 + bg - 1) / bg;
-  const int64_t blocks = (s->max_ctx + 255) / 256;
-  if (ns > blocks) ns = blocks;
+  int64_t ns = (4096 + bg - 1) / bg;
+  const int64_t chunks = (s->max_ctx + 31) / 32;
+  if (ns > chunks) ns = chunks;
   if (ns < 1) ns = 1;
   int64_t per = (s->max_ctx + ns - 1) / ns;
-  per = (per + 255) / 256 * 256;
+  per = (per + 31) / 32 * 32;
   ns = (s->max_ctx + per - 1) / per;
   if (ns > 65535) return set_error(TQ_ERR_UNSUPPORTED, "split decode: too many splits");
   plan->n_splits = (int)ns;

@@ -7,19 +7,30 @@
 //   out = sum_t softmax(s)_t v~_t, each value part written back to its channels
 // (channels no value part keeps come out 0).
 //
-// Generic fp32 code for part dimensions that are multiples of 32 (the 32 / 96
-// split of a 128-channel head): a workgroup takes one (batch, KV head, token
-// split) and all query heads of the group. Each block of 256 tokens first
-// copies every part's records (contiguous per part) into LDS with coalesced
-// 32-bit loads; threads then read their token's bits from LDS. The query parts are rotated into
-// each part's basis once per workgroup (q' = Pi_p q_p, q'' = S_p q_p, scale and
-// the QJL factor folded in), so a score is a sum over code bits with no
-// inverse rotation; values are accumulated in each part's rotated basis and
-// rotated back once, in the combine. Tokens go in blocks of 256, one per
-// thread, with an online softmax per block; the value sum stages 16
-// dequantized coordinates of the block's tokens in LDS at a time, token-major
-// so both the weights and the values are read four tokens per access. Splits are
-// merged by log-sum-exp in a second kernel (deterministic, no atomics).
+// Matrix-core design for part dimensions that are multiples of 32 (the 32 / 96
+// split of a 128-channel head). A workgroup of 4 waves takes one (batch, KV
+// head) and 4 context splits, one per wave. The workgroup first rotates the
+// query parts into each key part's basis (q' = scale Pi_p q_p, q'' = scale
+// sqrt(pi/2)/d_p S_p q_p), scales each head by a power of two and stores them as
+// fp16 hi/lo MFMA fragments (rows = 8 heads x {hi, lo}, K = 32 coordinates).
+// Then every wave walks its split in chunks of 32 tokens:
+//  * the chunk's records of every part are copied straight from HBM into the
+//    wave's LDS staging buffer (global_load_lds, double-buffered: the next
+//    chunk is in flight while this one is computed);
+//  * scores: per key part and 32-coordinate step, each lane decodes 8
+//    coordinates of one token into exact fp16 hi/lo centroid pairs (a 16-entry
+//    LDS table per part) and the QJL signs into +-1, and the matrix cores form
+//    <q', c~> and <q'', z> for 16 tokens x 8 heads per instruction;
+//  * an online softmax per head over the chunk (16-lane reductions);
+//  * values: the probabilities times each value part's norms become the fp16
+//    hi/lo weight operand (rows = 8 heads x {hi, lo}, K = 32 tokens), each lane
+//    decodes one coordinate of 8 tokens into the centroid operand, and the
+//    matrix cores accumulate 16 coordinates x 8 heads per instruction in the
+//    part's rotated basis (a running power-of-two exponent per part keeps the
+//    weights in fp16 range).
+// Splits are merged by log-sum-exp in a second kernel that also rotates each
+// value part back (Pi_p^T) and scatters it to its channels (deterministic, no
+// atomics).
 #include <hip/hip_runtime.h>
 
 #include "tq_device.h"
@@ -27,254 +38,377 @@
 namespace tq {
 namespace {
 
-constexpr int kSdBlock = 256;  // tokens per block = threads per workgroup
-constexpr int kSdChunk = 16;   // value coordinates staged per pass
-static_assert(kSdBlock == 2 * kSplitMaxGroup * kSdChunk, "two threads per (head, coordinate) pair in the value sum");
+constexpr int kSmWaves = 4;                 // waves per workgroup, one context split each
+constexpr int kSmThreads = 64 * kSmWaves;
+constexpr int kSmChunk = 32;                // tokens per step
+constexpr int kSmMaxSeg = 6 * kSplitMaxParts;
+constexpr int kSmTabWords = 2 * kSplitMaxParts * 16 + 4;  // key tables, value tables, QJL sign pairs
+constexpr int kSmEvUnset = -1000;
 
-struct SdPart {
-  int d, planes, off;  // part dimension, MSE-stage planes, offset in the concatenated channel list
-  int lds_codes, lds_signs;  // 32-bit word offsets of the part's staged records in dynamic LDS
-  bool qjl;
-  const uint8_t* codes;  // [B][Hkv][T][planes*d/8]
-  const uint8_t* signs;  // [B][Hkv][T][d/8] (qjl)
-  const float* norms;    // [B][Hkv][T]
-  const float* rnorms;   // [B][Hkv][T] (qjl)
-  float cen[16];
-  float kappa;  // sqrt(pi/2) / d
+struct SmPart {
+  int d, planes, off, qjl;
+  int rec;                                   // code bytes per token: planes * d / 8
+  int st_codes, st_signs, st_norms, st_rnorms;  // byte offsets in a staging buffer
+  float kappa;                               // sqrt(pi/2) / d
+  unsigned tab[16];                          // centroid i as fp16 hi | lo << 16
   const float* pi[kSplitMaxKv];
   const float* s[kSplitMaxKv];
 };
 
-struct SdParams {
-  int Hq, Hkv, G, dim, nk, nv, dk, dv, n_splits;
+struct SmSeg {  // one per-token array of one part: elem bytes per token, [B * Hkv][T][elem]
+  const uint8_t* base;
+  int elem, lds;
+};
+
+struct SmParams {
+  int Hq, Hkv, G, dim, nk, nv, dk, dv, n_splits, n_seg;
   int64_t T, split_tokens;
   const uint16_t* q;  // bf16 [B][Hq][dim]
   const int32_t* lens;
   float scale;
   float* part;  // [B][Hq][n_splits][dv + 2]
   float* out;   // [B][Hq][dim]
+  int stage_bytes, tab_off, wave_off, wave_bytes;  // LDS layout (bytes); fragments at 0
   uint8_t kchan[kSplitMaxDecodeDim], vchan[kSplitMaxDecodeDim];
-  SdPart kp[kSplitMaxParts], vp[kSplitMaxParts];
+  uint8_t vword_part[kSplitMaxDecodeDim / 32];  // value part of each 32-coordinate word
+  SmPart kp[kSplitMaxParts], vp[kSplitMaxParts];
+  SmSeg seg[kSmMaxSeg];
 };
 
-// plane bytes jb of a record (coordinates 8 jb .. 8 jb + 7)
-__device__ __forceinline__ void plane_bytes(const uint8_t* rec, int planes, int d, int jb, unsigned* pb) {
-#pragma unroll
-  for (int pl = 0; pl < 4; ++pl) pb[pl] = pl < planes ? rec[pl * (d / 8) + jb] : 0u;
-}
-__device__ __forceinline__ int bit_index(const unsigned* pb, int bit) {
-  return (int)(((pb[0] >> bit) & 1u) | (((pb[1] >> bit) & 1u) << 1) | (((pb[2] >> bit) & 1u) << 2) |
-               (((pb[3] >> bit) & 1u) << 3));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__device__ __forceinline__ unsigned lds_u32(const uint8_t* p) { return *(const unsigned*)p; }
+
+// index of coordinate e in plane words w (bit e of each plane, plane 0 lowest)
+__device__ __forceinline__ unsigned code_index(const unsigned (&w)[4], int e, int planes) {
+  unsigned i = __builtin_amdgcn_ubfe(w[0], e, 1);
+  if (planes > 1) i |= __builtin_amdgcn_ubfe(w[1], e, 1) << 1;
+  if (planes > 2) i |= __builtin_amdgcn_ubfe(w[2], e, 1) << 2;
+  if (planes > 3) i |= __builtin_amdgcn_ubfe(w[3], e, 1) << 3;
+  return i;
 }
 
-__device__ float block_reduce(float v, bool is_max, float* red) {
+// fp16 operands of eight table entries (hi | lo << 16): the hi parts and the lo parts
+__device__ __forceinline__ void entry_operands(const unsigned (&e)[8], u32x4& hi, u32x4& lo) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float u = __shfl_xor(v, o);
-    v = is_max ? fmaxf(v, u) : v + u;
+  for (int v = 0; v < 4; ++v) {
+    hi[v] = __builtin_amdgcn_perm(e[2 * v + 1], e[2 * v], 0x05040100u);
+    lo[v] = __builtin_amdgcn_perm(e[2 * v + 1], e[2 * v], 0x07060302u);
   }
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
+}
+
+__device__ __forceinline__ float group16_max(float v) {
 #pragma unroll
-  for (int w = 1; w < kSdBlock / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
-  return r;
+  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float group16_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
-// the records of up to 256 consecutive tokens of one part: nt * bytes contiguous
-// bytes (a multiple of 4) copied to LDS with coalesced 32-bit loads
-__device__ __forceinline__ void stage(const uint8_t* src, uint32_t* dst, int nt, int bytes) {
-  const uint32_t* s = (const uint32_t*)src;
-  for (int e = threadIdx.x; e < nt * bytes / 4; e += kSdBlock) dst[e] = s[e];
-}
-
-__global__ __launch_bounds__(kSdBlock) void split_decode_kernel(SdParams prm) {
-  extern __shared__ uint32_t rec_lds[];  // staged key and value records of the current block
-  __shared__ float qk[kSplitMaxGroup][kSplitMaxDecodeDim];  // q' per head, key parts' bases
-  __shared__ float qs[kSplitMaxGroup][kSplitMaxDecodeDim];  // q'' per head (QJL parts)
-  __shared__ float acc[kSplitMaxGroup][kSplitMaxDecodeDim];  // value sums, value parts' bases
-  __shared__ float wts[kSplitMaxGroup][kSdBlock];            // block scores, then weights
-  __shared__ float vt[kSdChunk][kSdBlock];                   // dequantized value coordinates, [coordinate][token]
-  __shared__ float vhalf[kSplitMaxGroup * kSdChunk];           // second half of the token sum
-  __shared__ float mrow[kSplitMaxGroup], lrow[kSplitMaxGroup], resc[kSplitMaxGroup];
-  __shared__ float red[kSdBlock / 64];
-  __shared__ float cenk[kSplitMaxParts][16], cenv[kSplitMaxParts][16];
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x / prm.Hkv, g = blockIdx.x % prm.Hkv, split = blockIdx.y;
-  if (tid < kSplitMaxParts * 16) {
-    cenk[tid / 16][tid % 16] = prm.kp[tid / 16].cen[tid % 16];
-    cenv[tid / 16][tid % 16] = prm.vp[tid / 16].cen[tid % 16];
-  }
+template <int NW>  // 32-coordinate words of the value vector, at most
+__global__ __launch_bounds__(kSmThreads) void split_main_kernel(SmParams prm) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int sexp[2][kSplitMaxGroup];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int bgi = blockIdx.y;
+  const int b = bgi / prm.Hkv, g = bgi % prm.Hkv;
   const int G = prm.G;
-  const int64_t len = min(max((int64_t)prm.lens[b], (int64_t)0), prm.T);  // lengths beyond the cache attend all of it
-  const int64_t t0 = (int64_t)split * prm.split_tokens;
-  const int64_t t1 = min(len, t0 + prm.split_tokens);
-  const int64_t bg = (int64_t)b * prm.Hkv + g;
+  u32x4* frag = (u32x4*)lds;  // [dk / 32][{mse, qjl}][64 lanes]
+  unsigned* tabs = (unsigned*)(lds + prm.tab_off);
 
-  // ---- query parts in the key parts' bases (acc is scratch for the raw queries) ----
-  for (int e = tid; e < G * prm.dim; e += kSdBlock) {
+  // ---- tables: key parts, value parts, QJL sign pairs ----
+  if (tid < kSplitMaxParts * 16) {
+    tabs[tid] = prm.kp[tid / 16].tab[tid % 16];
+    tabs[kSplitMaxParts * 16 + tid] = prm.vp[tid / 16].tab[tid % 16];
+  }
+  if (tid < 4) tabs[2 * kSplitMaxParts * 16 + tid] = ((tid & 1) ? 0x3C00u : 0xBC00u) | (((tid & 2) ? 0x3C00u : 0xBC00u) << 16);
+
+  // ---- query parts in the key parts' bases (scratch aliases the staging buffers) ----
+  float* qraw = (float*)(lds + prm.wave_off);  // [G][dim]
+  float* qr = qraw + G * prm.dim;              // [G][dk]  q'
+  float* qs = qr + G * prm.dk;                 // [G][dk]  q''
+  for (int e = tid; e < G * prm.dim; e += kSmThreads) {
     const int h = e / prm.dim, j = e % prm.dim;
-    acc[h][j] = __uint_as_float((unsigned)prm.q[((int64_t)b * prm.Hq + g * G + h) * prm.dim + j] << 16);
+    qraw[e] = __uint_as_float((unsigned)prm.q[((int64_t)b * prm.Hq + g * G + h) * prm.dim + j] << 16);
   }
   __syncthreads();
   for (int p = 0; p < prm.nk; ++p) {
-    const SdPart& P = prm.kp[p];
-    for (int e = tid; e < G * P.d; e += kSdBlock) {
+    const SmPart& P = prm.kp[p];
+    for (int e = tid; e < G * P.d; e += kSmThreads) {
       const int h = e / P.d, i = e % P.d;
       const float* prow = P.pi[g] + (int64_t)i * P.d;
       const float* srow = P.qjl ? P.s[g] + (int64_t)i * P.d : nullptr;
       float a = 0.f, c = 0.f;
       for (int j = 0; j < P.d; ++j) {
-        const float qv = acc[h][prm.kchan[P.off + j]];
+        const float qv = qraw[h * prm.dim + prm.kchan[P.off + j]];
         a = fmaf(prow[j], qv, a);
         if (P.qjl) c = fmaf(srow[j], qv, c);
       }
-      qk[h][P.off + i] = prm.scale * a;
-      qs[h][P.off + i] = P.qjl ? prm.scale * P.kappa * c : 0.f;
+      qr[h * prm.dk + P.off + i] = prm.scale * a;
+      qs[h * prm.dk + P.off + i] = P.qjl ? prm.scale * P.kappa * c : 0.f;
     }
   }
   __syncthreads();
-  for (int e = tid; e < G * prm.dv; e += kSdBlock) acc[e / prm.dv][e % prm.dv] = 0.f;
-  if (tid < G) {
-    mrow[tid] = -INFINITY;
-    lrow[tid] = 0.f;
+  if (tid < 2 * kSplitMaxGroup) {  // power-of-two scale per (kind, head): |x| 2^S < 2^14
+    const int kind = tid / kSplitMaxGroup, h = tid % kSplitMaxGroup;
+    const float* src = kind ? qs : qr;
+    float mx = 0.f;
+    if (h < G)
+      for (int j = 0; j < prm.dk; ++j) mx = fmaxf(mx, fabsf(src[h * prm.dk + j]));
+    int e = 0;
+    frexpf(mx, &e);  // mx < 2^e
+    sexp[kind][h] = mx > 0.f ? min(14 - e, 100) : 0;
+  }
+  __syncthreads();
+  for (int f = tid; f < (prm.dk / 32) * 2 * 64; f += kSmThreads) {
+    const int ks = f / 128, kind = (f / 64) & 1, ln = f % 64;
+    const int row = ln % 16, h = row >> 1, kb = ks * 32 + 8 * (ln / 16);
+    const bool lo = row & 1;
+    const float* src = kind ? qs : qr;
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x0 = 0.f, x1 = 0.f;
+      if (h < G) {
+        x0 = ldexpf(src[h * prm.dk + kb + 2 * e], sexp[kind][h]);
+        x1 = ldexpf(src[h * prm.dk + kb + 2 * e + 1], sexp[kind][h]);
+      }
+      v[e] = f16_part(x0, lo) | (f16_part(x1, lo) << 16);
+    }
+    frag[f] = v;
   }
   __syncthreads();
 
-  for (int64_t tb = t0; tb < t1; tb += kSdBlock) {
-    const int64_t t = tb + tid;
-    const bool valid = t < t1;
-    {
-      const int nt = (int)min((int64_t)kSdBlock, t1 - tb);
-      const int64_t r0 = bg * prm.T + tb;
-      for (int p = 0; p < prm.nk; ++p) {
-        const SdPart& P = prm.kp[p];
-        if (P.planes) stage(P.codes + r0 * (P.planes * P.d / 8), rec_lds + P.lds_codes, nt, P.planes * P.d / 8);
-        if (P.qjl) stage(P.signs + r0 * (P.d / 8), rec_lds + P.lds_signs, nt, P.d / 8);
+  // ---- one context split per wave; no workgroup barriers from here on ----
+  const int split = blockIdx.x * kSmWaves + wave;
+  if (split >= prm.n_splits) return;
+  const int64_t len = min(max((int64_t)prm.lens[b], (int64_t)0), prm.T);  // lengths beyond the cache attend all of it
+  const int64_t t0 = (int64_t)split * prm.split_tokens;
+  const int64_t t1 = min(len, t0 + prm.split_tokens);
+  uint8_t* wbase = lds + prm.wave_off + wave * prm.wave_bytes;
+  float* wts = (float*)(wbase + 2 * prm.stage_bytes);  // [8 heads][32 tokens] probabilities
+  int* evs = (int*)(wts + kSplitMaxGroup * kSmChunk);  // per value part: weight exponent
+  float* fix = (float*)(evs + kSplitMaxParts);          // per value part: accumulator rescale
+  if (lane < kSplitMaxParts) evs[lane] = kSmEvUnset;
+  const int hA = 2 * g4, hB = 2 * g4 + 1;  // this lane's heads in every C tile
+  const float imA = hA < G ? ldexpf(1.f, -sexp[0][hA]) : 0.f, imB = hB < G ? ldexpf(1.f, -sexp[0][hB]) : 0.f;
+  const float iqA = hA < G ? ldexpf(1.f, -sexp[1][hA]) : 0.f, iqB = hB < G ? ldexpf(1.f, -sexp[1][hB]) : 0.f;
+  const unsigned* ztab = tabs + 2 * kSplitMaxParts * 16;
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4 acc[2 * NW];
+#pragma unroll
+  for (int t = 0; t < 2 * NW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // copy the records of tokens [c0, c0 + 32) into a staging buffer; tokens at or
+  // beyond t1 read copies of the last valid dword (finite, masked later)
+  auto issue = [&](int64_t c0, uint8_t* dst) {
+    const int nvalid = (int)min((int64_t)kSmChunk, t1 - c0);
+    for (int si = 0; si < prm.n_seg; ++si) {
+      const SmSeg S = prm.seg[si];
+      const int wpt = S.elem >> 2;
+      const int nd = kSmChunk * wpt, nvd = nvalid * wpt;
+      const unsigned* src = (const unsigned*)(S.base + ((int64_t)bgi * prm.T + c0) * S.elem);
+      for (int e0 = 0; e0 < nd; e0 += 64) {
+        const int e = e0 + lane;
+        if (e < nd)
+          __builtin_amdgcn_global_load_lds((void*)(src + min(e, nvd - 1)), (lds_ptr)(dst + S.lds + 4 * e0), 4, 0, 0);
       }
-      for (int p = 0; p < prm.nv; ++p) {
-        const SdPart& P = prm.vp[p];
-        stage(P.codes + r0 * (P.planes * P.d / 8), rec_lds + P.lds_codes, nt, P.planes * P.d / 8);
-      }
-      __syncthreads();
     }
-    // ---- scores of this thread's token for every head of the group ----
-    float sc[kSplitMaxGroup];
+  };
+
+  if (t0 < t1) issue(t0, wbase);
+  int it = 0;
+  for (int64_t c0 = t0; c0 < t1; c0 += kSmChunk, ++it) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this chunk's records are in LDS
+    asm volatile("" ::: "memory");
+    const uint8_t* sb = wbase + (it & 1) * prm.stage_bytes;
+    if (c0 + kSmChunk < t1) issue(c0 + kSmChunk, wbase + ((it + 1) & 1) * prm.stage_bytes);
+    const int nvalid = (int)min((int64_t)kSmChunk, t1 - c0);
+
+    // ---------------- scores: 2 tiles of 16 tokens x this lane's 2 heads ----------------
+    float sv[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    for (int p = 0; p < prm.nk; ++p) {
+      const SmPart& P = prm.kp[p];
+      const int planes = P.planes, dq = P.d >> 3, rec = P.rec;
+      const uint8_t* kc = sb + P.st_codes;
+      const uint8_t* ksg = sb + P.st_signs;
+      const unsigned* tk = tabs + 16 * p;
+      f32x4 am[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      f32x4 aq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      for (int ks = 0; ks < (P.d >> 5); ++ks) {
+        const int kg = (P.off >> 5) + ks;
+        const u32x4 fm = frag[(2 * kg) * 64 + lane];
+        const u32x4 fq = frag[(2 * kg + 1) * 64 + lane];
 #pragma unroll
-    for (int h = 0; h < kSplitMaxGroup; ++h) sc[h] = 0.f;
-    if (valid) {
-      for (int p = 0; p < prm.nk; ++p) {
-        const SdPart& P = prm.kp[p];
-        const int64_t r = bg * prm.T + t;
-        const uint8_t* rec = (const uint8_t*)(rec_lds + P.lds_codes) + tid * (P.planes * P.d / 8);
-        const uint8_t* sg = (const uint8_t*)(rec_lds + P.lds_signs) + tid * (P.d / 8);
-        float a[kSplitMaxGroup], c[kSplitMaxGroup];
+        for (int tile = 0; tile < 2; ++tile) {
+          const int tok = 16 * tile + r16;
+          if (planes > 0) {
+            unsigned w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int h = 0; h < kSplitMaxGroup; ++h) a[h] = c[h] = 0.f;
-        for (int jb = 0; jb < P.d / 8; ++jb) {
-          // 8 coordinates per byte: centroid values, then float4 broadcasts of q' (q'')
-          unsigned pb[4];
-          plane_bytes(rec, P.planes, P.d, jb, pb);
-          float cv[8];
+            for (int pl = 0; pl < 4; ++pl)
+              if (pl < planes) w[pl] = lds_u32(kc + tok * rec + pl * dq + 4 * ks) >> (8 * g4);
+            unsigned en[8];
 #pragma unroll
-          for (int bit = 0; bit < 8; ++bit) cv[bit] = cenk[p][bit_index(pb, bit)];
-          const int j0 = P.off + 8 * jb;
-#pragma unroll
-          for (int h = 0; h < kSplitMaxGroup; ++h)
-            if (h < G) {
-              const float4 u0 = *(const float4*)&qk[h][j0], u1 = *(const float4*)&qk[h][j0 + 4];
-              a[h] = fmaf(u0.x, cv[0], fmaf(u0.y, cv[1], fmaf(u0.z, cv[2], fmaf(u0.w, cv[3], a[h]))));
-              a[h] = fmaf(u1.x, cv[4], fmaf(u1.y, cv[5], fmaf(u1.z, cv[6], fmaf(u1.w, cv[7], a[h]))));
-            }
+            for (int e = 0; e < 8; ++e) en[e] = tk[code_index(w, e, planes)];
+            u32x4 bh, bl;
+            entry_operands(en, bh, bl);
+            am[tile] = mfma16(fm, bh, am[tile]);
+            am[tile] = mfma16(fm, bl, am[tile]);
+          }
           if (P.qjl) {
-            const unsigned zb = sg[jb];
-            float z[8];
+            const unsigned z = lds_u32(ksg + tok * dq + 4 * ks) >> (8 * g4);
+            u32x4 bz;
 #pragma unroll
-            for (int bit = 0; bit < 8; ++bit) z[bit] = ((zb >> bit) & 1u) ? 1.f : -1.f;
-#pragma unroll
-            for (int h = 0; h < kSplitMaxGroup; ++h)
-              if (h < G) {
-                const float4 u0 = *(const float4*)&qs[h][j0], u1 = *(const float4*)&qs[h][j0 + 4];
-                c[h] = fmaf(u0.x, z[0], fmaf(u0.y, z[1], fmaf(u0.z, z[2], fmaf(u0.w, z[3], c[h]))));
-                c[h] = fmaf(u1.x, z[4], fmaf(u1.y, z[5], fmaf(u1.z, z[6], fmaf(u1.w, z[7], c[h]))));
-              }
+            for (int v = 0; v < 4; ++v) bz[v] = ztab[(z >> (2 * v)) & 3u];
+            aq[tile] = mfma16(fq, bz, aq[tile]);
           }
         }
-        const float nu = P.norms[r], gam = P.qjl ? P.rnorms[r] : 0.f;
+      }
+      const float* kn = (const float*)(sb + P.st_norms);
+      const float* kr = (const float*)(sb + P.st_rnorms);
 #pragma unroll
-        for (int h = 0; h < kSplitMaxGroup; ++h) sc[h] = fmaf(nu, fmaf(gam, c[h], a[h]), sc[h]);
+      for (int tile = 0; tile < 2; ++tile) {
+        const int tok = 16 * tile + r16;
+        const float nu = kn[tok], ga = P.qjl ? kr[tok] : 0.f;
+        // |k| (<q', c~> + gamma <q'', z>): the residual norm gamma is relative to the unit vector
+        sv[tile][0] += nu * fmaf(ga * iqA, aq[tile][0] + aq[tile][1], imA * (am[tile][0] + am[tile][1]));
+        sv[tile][1] += nu * fmaf(ga * iqB, aq[tile][2] + aq[tile][3], imB * (am[tile][2] + am[tile][3]));
       }
     }
-    // ---- online softmax over the block ----
+
+    // ---------------- online softmax per head over the chunk ----------------
+    float alpha[2];
 #pragma unroll
-    for (int h = 0; h < kSplitMaxGroup; ++h) {
-      if (h >= G) break;  // uniform: every thread leaves together
-      const float bmax = block_reduce(valid ? sc[h] : -INFINITY, true, red);
-      const float mnew = fmaxf(mrow[h], bmax);
-      const float w = valid ? __expf(sc[h] - mnew) : 0.f;
-      wts[h][tid] = w;
-      const float bsum = block_reduce(w, false, red);
-      if (tid == 0) {
-        resc[h] = __expf(mrow[h] - mnew);  // 0 on the first block (mrow = -inf)
-        lrow[h] = lrow[h] * resc[h] + bsum;
-        mrow[h] = mnew;
-      }
+    for (int hh = 0; hh < 2; ++hh) {
+      const float s0 = r16 < nvalid ? sv[0][hh] : -INFINITY;
+      const float s1 = 16 + r16 < nvalid ? sv[1][hh] : -INFINITY;
+      const float mn = fmaxf(m_run[hh], group16_max(fmaxf(s0, s1)));  // finite: the chunk has a valid token
+      alpha[hh] = __expf(m_run[hh] - mn);
+      const float p0 = __expf(s0 - mn), p1 = __expf(s1 - mn);
+      l_run[hh] = l_run[hh] * alpha[hh] + p0 + p1;
+      m_run[hh] = mn;
+      wts[(2 * g4 + hh) * kSmChunk + r16] = p0;
+      wts[(2 * g4 + hh) * kSmChunk + 16 + r16] = p1;
     }
-    __syncthreads();
-    for (int e = tid; e < G * prm.dv; e += kSdBlock) acc[e / prm.dv][e % prm.dv] *= resc[e / prm.dv];
-    // ---- values: acc[h][j] += sum_t w[h][t] * nu_t * c[idx_{t,j}], 16 coordinates at a time ----
+    // value weight exponents: weights p |v| 2^-ev stay below 2^14
+    bool refit = false;
     for (int p = 0; p < prm.nv; ++p) {
-      const SdPart& P = prm.vp[p];
-      const int64_t r = bg * prm.T + t;
-      for (int c0 = 0; c0 < P.d; c0 += kSdChunk) {
-        __syncthreads();  // vt of the previous pass consumed; acc rescale done
-        if (valid) {
-          const uint8_t* rec = (const uint8_t*)(rec_lds + P.lds_codes) + tid * (P.planes * P.d / 8);
-          const float nu = P.norms[r];
+      const SmPart& P = prm.vp[p];
+      float nmx = lane < kSmChunk ? ((const float*)(sb + P.st_norms))[lane] : 0.f;
 #pragma unroll
-          for (int half = 0; half < kSdChunk / 8; ++half) {
-            unsigned pb[4];
-            plane_bytes(rec, P.planes, P.d, c0 / 8 + half, pb);
+      for (int o = 1; o < 64; o <<= 1) nmx = fmaxf(nmx, __shfl_xor(nmx, o));
+      int e = 0;
+      frexpf(nmx, &e);
+      const int need = nmx > 0.f ? max(e - 14, -100) : kSmEvUnset;
+      const int ev = evs[p];
+      float f = 1.f;
+      if (need > ev) {
+        if (ev != kSmEvUnset) f = ldexpf(1.f, ev - need);
+        refit = true;
+        __builtin_amdgcn_wave_barrier();
+        if (lane == 0) evs[p] = need;
+      }
+      if (lane == 0) fix[p] = f;
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    if (refit || __ballot(alpha[0] != 1.f || alpha[1] != 1.f)) {
 #pragma unroll
-            for (int bit = 0; bit < 8; ++bit) vt[8 * half + bit][tid] = nu * cenv[p][bit_index(pb, bit)];
+      for (int np = 0; np < NW; ++np) {
+        if (32 * np < prm.dv) {
+          const float f = fix[prm.vword_part[np]];
+          const float fa = alpha[0] * f, fb = alpha[1] * f;
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            acc[2 * np + hf][0] *= fa;
+            acc[2 * np + hf][1] *= fa;
+            acc[2 * np + hf][2] *= fb;
+            acc[2 * np + hf][3] *= fb;
           }
-        } else {
-#pragma unroll
-          for (int k = 0; k < kSdChunk; ++k) vt[k][tid] = 0.f;
         }
-        __syncthreads();
-        // pair (h, k) sums its token half; the two halves are added in a fixed order
-        const int pair = tid % (kSplitMaxGroup * kSdChunk), th = tid / (kSplitMaxGroup * kSdChunk);
-        const int h = pair / kSdChunk, k = pair % kSdChunk;
-        float sum = 0.f;
-        if (h < G) {
-          const float4* wv = (const float4*)&wts[h][th * (kSdBlock / 2)];
-          const float4* vv = (const float4*)&vt[k][th * (kSdBlock / 2)];
-          for (int i = 0; i < kSdBlock / 8; ++i) {
-            const float4 a4 = wv[i], b4 = vv[i];
-            sum = fmaf(a4.x, b4.x, fmaf(a4.y, b4.y, fmaf(a4.z, b4.z, fmaf(a4.w, b4.w, sum))));
-          }
-          if (th == 1) vhalf[pair] = sum;
-        }
-        __syncthreads();
-        if (th == 0 && h < G) acc[h][P.off + c0 + k] += sum + vhalf[pair];
       }
     }
-    __syncthreads();
+
+    // ---------------- values: 16 coordinates x 8 heads per instruction ----------------
+    u32x4 aw = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int np = 0; np < NW; ++np) {
+      if (32 * np < prm.dv) {
+        const int p = prm.vword_part[np];
+        const SmPart& P = prm.vp[p];
+        const int wd = np - (P.off >> 5);
+        if (wd == 0) {  // first word of this part: its weight operand
+          const int ev = evs[p];
+          const float wsc = ev == kSmEvUnset ? 0.f : ldexpf(1.f, -ev);
+          const float4* wr = (const float4*)(wts + (r16 >> 1) * kSmChunk + 8 * g4);
+          const float4* nr = (const float4*)(sb + P.st_norms + 4 * 8 * g4);
+          const float4 wa = wr[0], wb = wr[1], na = nr[0], nb = nr[1];
+          const float x[8] = {wa.x * na.x * wsc, wa.y * na.y * wsc, wa.z * na.z * wsc, wa.w * na.w * wsc,
+                              wb.x * nb.x * wsc, wb.y * nb.y * wsc, wb.z * nb.z * wsc, wb.w * nb.w * wsc};
+          const bool lo = r16 & 1;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) aw[v] = f16_part(x[2 * v], lo) | (f16_part(x[2 * v + 1], lo) << 16);
+        }
+        const int planes = P.planes, dq = P.d >> 3, rec = P.rec;
+        const uint8_t* vc = sb + P.st_codes + 4 * wd;
+        const unsigned* tv = tabs + kSplitMaxParts * 16 + 16 * p;
+        unsigned w[8][4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int pl = 0; pl < 4; ++pl) w[e][pl] = pl < planes ? lds_u32(vc + (8 * g4 + e) * rec + pl * dq) : 0u;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int bit = 16 * hf + r16;
+          unsigned en[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) en[e] = tv[code_index(w[e], bit, planes)];
+          u32x4 bh, bl;
+          entry_operands(en, bh, bl);
+          acc[2 * np + hf] = mfma16(aw, bh, acc[2 * np + hf]);
+          acc[2 * np + hf] = mfma16(aw, bl, acc[2 * np + hf]);
+        }
+      }
+    }
   }
+
   // ---- partials: acc[dv], m, l per head ----
-  for (int e = tid; e < G * (prm.dv + 2); e += kSdBlock) {
-    const int h = e / (prm.dv + 2), j = e % (prm.dv + 2);
-    const float v = j < prm.dv ? acc[h][j] : (j == prm.dv ? mrow[h] : lrow[h]);
-    prm.part[(((int64_t)b * prm.Hq + g * G + h) * prm.n_splits + split) * (prm.dv + 2) + j] = v;
+  const float lA = group16_sum(l_run[0]), lB = group16_sum(l_run[1]);
+  const int64_t rowA = (((int64_t)b * prm.Hq + g * G + hA) * prm.n_splits + split) * (prm.dv + 2);
+  const int64_t rowB = (((int64_t)b * prm.Hq + g * G + hB) * prm.n_splits + split) * (prm.dv + 2);
+#pragma unroll
+  for (int np = 0; np < NW; ++np) {
+    if (32 * np < prm.dv) {
+      const int ev = evs[prm.vword_part[np]];
+      const float sc = ev == kSmEvUnset ? 0.f : ldexpf(1.f, ev);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int j = 32 * np + 16 * hf + r16;
+        if (hA < G) prm.part[rowA + j] = (acc[2 * np + hf][0] + acc[2 * np + hf][1]) * sc;
+        if (hB < G) prm.part[rowB + j] = (acc[2 * np + hf][2] + acc[2 * np + hf][3]) * sc;
+      }
+    }
+  }
+  if (r16 == 0) {
+    if (hA < G) {
+      prm.part[rowA + prm.dv] = m_run[0];
+      prm.part[rowA + prm.dv + 1] = lA;
+    }
+    if (hB < G) {
+      prm.part[rowB + prm.dv] = m_run[1];
+      prm.part[rowB + prm.dv + 1] = lB;
+    }
   }
 }
 
 // one workgroup per (batch, query head): log-sum-exp merge of the splits, then
 // each value part rotated back (Pi_p^T) and written to its channels
-__global__ __launch_bounds__(kSdBlock) void split_combine_kernel(SdParams prm) {
+__global__ __launch_bounds__(kSmThreads) void split_combine_kernel(SmParams prm) {
   __shared__ float a[kSplitMaxDecodeDim];
   __shared__ float ml[2];
   const int tid = threadIdx.x;
@@ -294,7 +428,7 @@ __global__ __launch_bounds__(kSdBlock) void split_combine_kernel(SdParams prm) {
   }
   __syncthreads();
   const float M = ml[0], L = ml[1];
-  for (int j = tid; j < prm.dv; j += kSdBlock) {
+  for (int j = tid; j < prm.dv; j += kSmThreads) {
     float v = 0.f;
     if (L > 0.f) {
       for (int s = 0; s < prm.n_splits; ++s) {
@@ -307,11 +441,11 @@ __global__ __launch_bounds__(kSdBlock) void split_combine_kernel(SdParams prm) {
   }
   __syncthreads();
   float* o = prm.out + bh * prm.dim;
-  for (int j = tid; j < prm.dim; j += kSdBlock) o[j] = 0.f;  // channels no value part keeps
+  for (int j = tid; j < prm.dim; j += kSmThreads) o[j] = 0.f;  // channels no value part keeps
   __syncthreads();
   for (int p = 0; p < prm.nv; ++p) {
-    const SdPart& P = prm.vp[p];
-    for (int j = tid; j < P.d; j += kSdBlock) {
+    const SmPart& P = prm.vp[p];
+    for (int j = tid; j < P.d; j += kSmThreads) {
       float v = 0.f;
       for (int i = 0; i < P.d; ++i) v = fmaf(P.pi[g][(int64_t)i * P.d + j], a[P.off + i], v);
       o[prm.vchan[P.off + j]] = v;
@@ -322,7 +456,7 @@ __global__ __launch_bounds__(kSdBlock) void split_combine_kernel(SdParams prm) {
 }  // namespace
 
 tq_status launch_split_decode(const SplitDecodeLaunch& L, hipStream_t stream) {
-  SdParams prm{};
+  SmParams prm{};
   prm.Hq = L.Hq;
   prm.Hkv = L.Hkv;
   prm.G = L.Hq / L.Hkv;
@@ -335,34 +469,46 @@ tq_status launch_split_decode(const SplitDecodeLaunch& L, hipStream_t stream) {
   prm.part = (float*)L.workspace;
   prm.n_splits = L.n_splits;
   prm.split_tokens = L.split_tokens;
-  int lds_words = 0;  // dynamic LDS: every part's records of one 256-token block
+  // staging buffer of one wave: every part's per-token arrays for 32 tokens, 16-byte aligned
+  int st = 0;
+  auto add_seg = [&](const void* base, int elem) -> int {
+    const int at = st;
+    prm.seg[prm.n_seg++] = SmSeg{(const uint8_t*)base, elem, at};
+    st += (kSmChunk * elem + 15) / 16 * 16;
+    return at;
+  };
   for (int side = 0; side < 2; ++side) {
     const SplitSide& S = side == 0 ? L.k : L.v;
-    SdPart* dst = side == 0 ? prm.kp : prm.vp;
+    SmPart* dst = side == 0 ? prm.kp : prm.vp;
     uint8_t* chan = side == 0 ? prm.kchan : prm.vchan;
     int off = 0;
     for (int p = 0; p < S.n_parts; ++p) {
       const tq_quantizer* q0 = S.qz[p * L.Hkv];
-      SdPart& P = dst[p];
+      SmPart& P = dst[p];
       P.d = q0->d;
       P.planes = q0->planes;
       P.off = off;
-      P.qjl = q0->variant == TQ_PROD;
-      P.lds_codes = lds_words;
-      lds_words += kSdBlock * (P.planes * P.d / 8) / 4;
-      P.lds_signs = lds_words;
-      if (side == 0 && P.qjl) lds_words += kSdBlock * (P.d / 8) / 4;
-      P.codes = S.codes[p];
-      P.signs = S.signs[p];
-      P.norms = S.norms[p];
-      P.rnorms = S.rnorms[p];
-      for (int i = 0; i < (1 << q0->planes); ++i) P.cen[i] = q0->cb.centroids[i];
+      P.qjl = side == 0 && q0->variant == TQ_PROD;
+      P.rec = P.planes * P.d / 8;
+      if (P.planes > 0) P.st_codes = add_seg(S.codes[p], P.rec);
+      if (P.qjl) P.st_signs = add_seg(S.signs[p], P.d / 8);
+      P.st_norms = add_seg(S.norms[p], 4);
+      if (P.qjl) P.st_rnorms = add_seg(S.rnorms[p], 4);
+      for (int i = 0; i < (1 << q0->planes) && i < 16; ++i) {
+        const float c = q0->cb.centroids[i];
+        const _Float16 hi = (_Float16)c;
+        const _Float16 lo = (_Float16)(c - (float)hi);
+        P.tab[i] = (unsigned)__builtin_bit_cast(unsigned short, hi) |
+                   ((unsigned)__builtin_bit_cast(unsigned short, lo) << 16);
+      }
       P.kappa = (float)(std::sqrt(M_PI / 2.0) / q0->d);
       for (int g = 0; g < L.Hkv; ++g) {
         P.pi[g] = S.qz[p * L.Hkv + g]->pi32;
         P.s[g] = S.qz[p * L.Hkv + g]->s32;
       }
       for (int j = 0; j < P.d; ++j) chan[off + j] = (uint8_t)S.channels[off + j];
+      if (side == 1)
+        for (int w = off / 32; w < (off + P.d) / 32; ++w) prm.vword_part[w] = (uint8_t)p;
       off += P.d;
     }
     if (side == 0) {
@@ -373,14 +519,24 @@ tq_status launch_split_decode(const SplitDecodeLaunch& L, hipStream_t stream) {
       prm.dv = off;
     }
   }
-  const size_t lds = (size_t)lds_words * 4;
-  hipError_t e = hipFuncSetAttribute((const void*)split_decode_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  prm.stage_bytes = st;
+  prm.tab_off = (prm.dk / 32) * 2 * 64 * 16;
+  prm.wave_off = prm.tab_off + (kSmTabWords * 4 + 15) / 16 * 16;
+  // per wave: two staging buffers, probabilities [8][32], exponents and rescale factors
+  prm.wave_bytes = 2 * st + kSplitMaxGroup * kSmChunk * 4 + 2 * kSplitMaxParts * 4;
+  prm.wave_bytes = (prm.wave_bytes + 15) / 16 * 16;
+  const size_t prep = (size_t)prm.G * (prm.dim + 2 * prm.dk) * 4;
+  const size_t waves = (size_t)kSmWaves * prm.wave_bytes;
+  const size_t lds = prm.wave_off + (prep > waves ? prep : waves);
+  if (lds > 160 * 1024) return set_error(TQ_ERR_UNSUPPORTED, "split decode: parts need more LDS than a workgroup has");
+  const dim3 grid((unsigned)((L.n_splits + kSmWaves - 1) / kSmWaves), (unsigned)(L.B * L.Hkv));
+  auto kern = prm.dv <= 128 ? split_main_kernel<4> : split_main_kernel<8>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return check_hip(e, "split decode: set LDS size");
-  hipLaunchKernelGGL(split_decode_kernel, dim3((unsigned)(L.B * L.Hkv), (unsigned)L.n_splits), dim3(kSdBlock), lds,
-                     stream, prm);
-  tq_status st = launch_check("split decode: main launch");
-  if (st != TQ_OK) return st;
-  hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)(L.B * L.Hq)), dim3(kSdBlock), 0, stream, prm);
+  hipLaunchKernelGGL(kern, grid, dim3(kSmThreads), lds, stream, prm);
+  tq_status st2 = launch_check("split decode: main launch");
+  if (st2 != TQ_OK) return st2;
+  hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)(L.B * L.Hq)), dim3(kSmThreads), 0, stream, prm);
   return launch_check("split decode: combine launch");
 }
 

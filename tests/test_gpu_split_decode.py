@@ -88,6 +88,11 @@ CASES = [
      [(64, "prod", 3), (32, "mse", 2)], [(32, "mse", 4), (64, "mse", 2)]),
     ("gqa1_d64", 3, 4, 4, 64, 40, [40, 1, 17],
      [(32, "mse", 2), (32, "prod", 2)], [(32, "mse", 3), (32, "mse", 1)]),
+    # 8 KV heads at batch 1: 512 context splits of 64 tokens, so every split runs
+    # two chunks of 32 (the second one's records in flight during the first) and
+    # the last split ends in a partial chunk
+    ("multi_chunk_splits", 1, 64, 8, 128, 20000, [19999],
+     [(32, "prod", 3), (96, "prod", 2)], [(32, "mse", 3), (96, "mse", 2)]),
 ]
 
 
