@@ -33,6 +33,8 @@
 // atomics).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "tq_device.h"
 
 namespace tq {
@@ -79,12 +81,12 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 __device__ __forceinline__ unsigned lds_u32(const uint8_t* p) { return *(const unsigned*)p; }
 
-// index of coordinate e in plane words w (bit e of each plane, plane 0 lowest)
-__device__ __forceinline__ unsigned code_index(const unsigned (&w)[4], int e, int planes) {
+// index of coordinate e in the PL plane words w (bit e of each plane, plane 0 lowest)
+template <int PL>
+__device__ __forceinline__ unsigned code_index(const unsigned* w, int e) {
   unsigned i = __builtin_amdgcn_ubfe(w[0], e, 1);
-  if (planes > 1) i |= __builtin_amdgcn_ubfe(w[1], e, 1) << 1;
-  if (planes > 2) i |= __builtin_amdgcn_ubfe(w[2], e, 1) << 2;
-  if (planes > 3) i |= __builtin_amdgcn_ubfe(w[3], e, 1) << 3;
+#pragma unroll
+  for (int pl = 1; pl < PL; ++pl) i |= __builtin_amdgcn_ubfe(w[pl], e, 1) << pl;
   return i;
 }
 
@@ -109,7 +111,7 @@ __device__ __forceinline__ float group16_sum(float v) {
 }
 
 template <int NW>  // 32-coordinate words of the value vector, at most
-__global__ __launch_bounds__(kSmThreads) void split_main_kernel(SmParams prm) {
+__global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(4))) void split_main_kernel(SmParams prm) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int sexp[2][kSplitMaxGroup];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -232,35 +234,35 @@ __global__ __launch_bounds__(kSmThreads) void split_main_kernel(SmParams prm) {
 
     // ---------------- scores: 2 tiles of 16 tokens x this lane's 2 heads ----------------
     float sv[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-    for (int p = 0; p < prm.nk; ++p) {
-      const SmPart& P = prm.kp[p];
-      const int planes = P.planes, dq = P.d >> 3, rec = P.rec;
+    // one key part with PL planes (QJ: QJL signs); am / aq: <q', c~> and <q'', z> per tile
+    auto key_part = [&](auto PLc, auto QJc, const SmPart& P, int p) {
+      constexpr int PL = decltype(PLc)::value;
+      constexpr bool QJ = decltype(QJc)::value;
+      const int dq = P.d >> 3, rec = P.rec, kg0 = P.off >> 5, nks = P.d >> 5;
       const uint8_t* kc = sb + P.st_codes;
       const uint8_t* ksg = sb + P.st_signs;
       const unsigned* tk = tabs + 16 * p;
       f32x4 am[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       f32x4 aq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      for (int ks = 0; ks < (P.d >> 5); ++ks) {
-        const int kg = (P.off >> 5) + ks;
-        const u32x4 fm = frag[(2 * kg) * 64 + lane];
-        const u32x4 fq = frag[(2 * kg + 1) * 64 + lane];
+      for (int ks = 0; ks < nks; ++ks) {
+        const u32x4 fm = frag[(2 * (kg0 + ks)) * 64 + lane];
+        const u32x4 fq = frag[(2 * (kg0 + ks) + 1) * 64 + lane];
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) {
           const int tok = 16 * tile + r16;
-          if (planes > 0) {
-            unsigned w[4] = {0u, 0u, 0u, 0u};
+          if constexpr (PL > 0) {
+            unsigned w[PL];
 #pragma unroll
-            for (int pl = 0; pl < 4; ++pl)
-              if (pl < planes) w[pl] = lds_u32(kc + tok * rec + pl * dq + 4 * ks) >> (8 * g4);
+            for (int pl = 0; pl < PL; ++pl) w[pl] = lds_u32(kc + tok * rec + pl * dq + 4 * ks) >> (8 * g4);
             unsigned en[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) en[e] = tk[code_index(w, e, planes)];
+            for (int e = 0; e < 8; ++e) en[e] = tk[code_index<PL>(w, e)];
             u32x4 bh, bl;
             entry_operands(en, bh, bl);
             am[tile] = mfma16(fm, bh, am[tile]);
             am[tile] = mfma16(fm, bl, am[tile]);
           }
-          if (P.qjl) {
+          if constexpr (QJ) {
             const unsigned z = lds_u32(ksg + tok * dq + 4 * ks) >> (8 * g4);
             u32x4 bz;
 #pragma unroll
@@ -274,10 +276,31 @@ __global__ __launch_bounds__(kSmThreads) void split_main_kernel(SmParams prm) {
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile) {
         const int tok = 16 * tile + r16;
-        const float nu = kn[tok], ga = P.qjl ? kr[tok] : 0.f;
+        const float nu = kn[tok], ga = QJ ? kr[tok] : 0.f;
         // |k| (<q', c~> + gamma <q'', z>): the residual norm gamma is relative to the unit vector
         sv[tile][0] += nu * fmaf(ga * iqA, aq[tile][0] + aq[tile][1], imA * (am[tile][0] + am[tile][1]));
         sv[tile][1] += nu * fmaf(ga * iqB, aq[tile][2] + aq[tile][3], imB * (am[tile][2] + am[tile][3]));
+      }
+    };
+    for (int p = 0; p < prm.nk; ++p) {
+      const SmPart& P = prm.kp[p];
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;
+      using I4 = std::integral_constant<int, 4>;
+      using T_ = std::true_type;
+      using F_ = std::false_type;
+      switch (P.planes * 2 + (P.qjl ? 1 : 0)) {
+        case 1: key_part(I0{}, T_{}, P, p); break;
+        case 2: key_part(I1{}, F_{}, P, p); break;
+        case 3: key_part(I1{}, T_{}, P, p); break;
+        case 4: key_part(I2{}, F_{}, P, p); break;
+        case 5: key_part(I2{}, T_{}, P, p); break;
+        case 6: key_part(I3{}, F_{}, P, p); break;
+        case 7: key_part(I3{}, T_{}, P, p); break;
+        case 8: key_part(I4{}, F_{}, P, p); break;
+        default: break;
       }
     }
 
@@ -354,24 +377,35 @@ __global__ __launch_bounds__(kSmThreads) void split_main_kernel(SmParams prm) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) aw[v] = f16_part(x[2 * v], lo) | (f16_part(x[2 * v + 1], lo) << 16);
         }
-        const int planes = P.planes, dq = P.d >> 3, rec = P.rec;
-        const uint8_t* vc = sb + P.st_codes + 4 * wd;
-        const unsigned* tv = tabs + kSplitMaxParts * 16 + 16 * p;
-        unsigned w[8][4];
+        // one 32-coordinate word of a value part with PL planes: two tiles of 16 coordinates
+        auto value_word = [&](auto PLc) {
+          constexpr int PL = decltype(PLc)::value;
+          const int dq = P.d >> 3, rec = P.rec;
+          const uint8_t* vc = sb + P.st_codes + 4 * wd;
+          const unsigned* tv = tabs + kSplitMaxParts * 16 + 16 * p;
+          unsigned w[8][PL];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+          for (int e = 0; e < 8; ++e)
 #pragma unroll
-          for (int pl = 0; pl < 4; ++pl) w[e][pl] = pl < planes ? lds_u32(vc + (8 * g4 + e) * rec + pl * dq) : 0u;
+            for (int pl = 0; pl < PL; ++pl) w[e][pl] = lds_u32(vc + (8 * g4 + e) * rec + pl * dq);
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int bit = 16 * hf + r16;
-          unsigned en[8];
+          for (int hf = 0; hf < 2; ++hf) {
+            const int bit = 16 * hf + r16;
+            unsigned en[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) en[e] = tv[code_index(w[e], bit, planes)];
-          u32x4 bh, bl;
-          entry_operands(en, bh, bl);
-          acc[2 * np + hf] = mfma16(aw, bh, acc[2 * np + hf]);
-          acc[2 * np + hf] = mfma16(aw, bl, acc[2 * np + hf]);
+            for (int e = 0; e < 8; ++e) en[e] = tv[code_index<PL>(w[e], bit)];
+            u32x4 bh, bl;
+            entry_operands(en, bh, bl);
+            acc[2 * np + hf] = mfma16(aw, bh, acc[2 * np + hf]);
+            acc[2 * np + hf] = mfma16(aw, bl, acc[2 * np + hf]);
+          }
+        };
+        switch (P.planes) {
+          case 1: value_word(std::integral_constant<int, 1>{}); break;
+          case 2: value_word(std::integral_constant<int, 2>{}); break;
+          case 3: value_word(std::integral_constant<int, 3>{}); break;
+          case 4: value_word(std::integral_constant<int, 4>{}); break;
+          default: break;
         }
       }
     }
