@@ -602,9 +602,15 @@ static tq_status plan_split_decode(const tq_attn_shape* s, const tq_split_cache*
   if (st != TQ_OK) return st;
   st = check_split_side(v, s, true, &L->v, &plan->dv);
   if (st != TQ_OK) return st;
-  // one wave per context split, about 4096 waves (16 per CU), splits a multiple of 32 tokens
+  L->B = s->batch;
+  L->Hq = s->n_q_heads;
+  L->Hkv = s->n_kv_heads;
+  L->dim = s->head_dim;
+  L->max_ctx = s->max_ctx;
+  // one wave per context split, as many splits as waves fit on the device at
+  // once (a single round), splits a multiple of 32 tokens
   const int64_t bg = (int64_t)s->batch * s->n_kv_heads;
-  int64_t ns = (4096 + bg - 1) / bg;
+  int64_t ns = split_decode_resident_waves(*L) / bg;
   const int64_t chunks = (s->max_ctx + 31) / 32;
   if (ns > chunks) ns = chunks;
   if (ns < 1) ns = 1;
@@ -615,11 +621,6 @@ static tq_status plan_split_decode(const tq_attn_shape* s, const tq_split_cache*
   plan->n_splits = (int)ns;
   plan->split_tokens = per;
   plan->bytes = (size_t)s->batch * s->n_q_heads * ns * (plan->dv + 2) * sizeof(float);
-  L->B = s->batch;
-  L->Hq = s->n_q_heads;
-  L->Hkv = s->n_kv_heads;
-  L->dim = s->head_dim;
-  L->max_ctx = s->max_ctx;
   L->n_splits = plan->n_splits;
   L->split_tokens = per;
   return TQ_OK;

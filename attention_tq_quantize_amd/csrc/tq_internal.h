@@ -117,6 +117,9 @@ struct SplitDecodeLaunch {
   SplitSide k, v;
 };
 tq_status launch_split_decode(const SplitDecodeLaunch& L, hipStream_t stream);
+// waves of the split decode kernel resident on the current device at once (one
+// context split per wave; a fixed estimate when the device cannot be queried)
+int split_decode_resident_waves(const SplitDecodeLaunch& L);
 // d a multiple of 128 in (256, 4096]: the GEMM quantize tables, built at creation
 bool lq_supported(int d);
 tq_status build_large_tables(tq_quantizer* q);

@@ -44,13 +44,13 @@ constexpr int kSmWaves = 4;                 // waves per workgroup, one context 
 constexpr int kSmThreads = 64 * kSmWaves;
 constexpr int kSmChunk = 32;                // tokens per step
 constexpr int kSmMaxSeg = 6 * kSplitMaxParts;
-constexpr int kSmTabWords = 2 * kSplitMaxParts * 16 + 4;  // key tables, value tables, QJL sign pairs
 constexpr int kSmEvUnset = -1000;
 
 struct SmPart {
   int d, planes, off, qjl;
   int rec;                                   // code bytes per token: planes * d / 8
   int st_codes, st_signs, st_norms, st_rnorms;  // byte offsets in a staging buffer
+  int ptab;                                  // byte offset of its pair table from the tables' start
   float kappa;                               // sqrt(pi/2) / d
   unsigned tab[16];                          // centroid i as fp16 hi | lo << 16
   const float* pi[kSplitMaxKv];
@@ -81,23 +81,20 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 __device__ __forceinline__ unsigned lds_u32(const uint8_t* p) { return *(const unsigned*)p; }
 
-// index of coordinate e in the PL plane words w (bit e of each plane, plane 0 lowest)
-template <int PL>
-__device__ __forceinline__ unsigned code_index(const unsigned* w, int e) {
-  unsigned i = __builtin_amdgcn_ubfe(w[0], e, 1);
-#pragma unroll
-  for (int pl = 1; pl < PL; ++pl) i |= __builtin_amdgcn_ubfe(w[pl], e, 1) << pl;
-  return i;
+// w >> off (off a VGPR) masked to W bits, as one v_bfe_u32: plain ALU, the
+// compiler otherwise splits constant-offset extracts into a shift and a mask
+template <int W>
+__device__ __forceinline__ unsigned bfe(unsigned w, unsigned off) {
+  unsigned r;
+  asm("v_bfe_u32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "v"(off), "n"(W));
+  return r;
 }
 
-// fp16 operands of eight table entries (hi | lo << 16): the hi parts and the lo parts
-__device__ __forceinline__ void entry_operands(const unsigned (&e)[8], u32x4& hi, u32x4& lo) {
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    hi[v] = __builtin_amdgcn_perm(e[2 * v + 1], e[2 * v], 0x05040100u);
-    lo[v] = __builtin_amdgcn_perm(e[2 * v + 1], e[2 * v], 0x07060302u);
-  }
-}
+// Pair tables: entry (a, b) of a part with PL planes, a and b the code indices of
+// two coordinates, holds their centroids as fp16 (hi_a | hi_b << 16, lo_a | lo_b
+// << 16), i.e. one dword of each MFMA operand. The entry index interleaves the
+// planes: bits 2 pl and 2 pl + 1 are plane pl of a and of b.
+__device__ __forceinline__ unsigned pair_entries(int PL) { return 1u << (2 * PL); }
 
 __device__ __forceinline__ float group16_max(float v) {
 #pragma unroll
@@ -111,10 +108,13 @@ __device__ __forceinline__ float group16_sum(float v) {
 }
 
 template <int NW>  // 32-coordinate words of the value vector, at most
-__global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(4))) void split_main_kernel(SmParams prm) {
+__global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3))) void split_main_kernel(SmParams prm) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int sexp[2][kSplitMaxGroup];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __align__(16) float wts_s[kSmWaves][kSplitMaxGroup * kSmChunk];
+  __shared__ int evs_s[kSmWaves][kSplitMaxParts];
+  __shared__ float fix_s[kSmWaves][kSplitMaxParts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
   const int bgi = blockIdx.y;
   const int b = bgi / prm.Hkv, g = bgi % prm.Hkv;
@@ -122,12 +122,24 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(4)))
   u32x4* frag = (u32x4*)lds;  // [dk / 32][{mse, qjl}][64 lanes]
   unsigned* tabs = (unsigned*)(lds + prm.tab_off);
 
-  // ---- tables: key parts, value parts, QJL sign pairs ----
-  if (tid < kSplitMaxParts * 16) {
-    tabs[tid] = prm.kp[tid / 16].tab[tid % 16];
-    tabs[kSplitMaxParts * 16 + tid] = prm.vp[tid / 16].tab[tid % 16];
+  // ---- tables: QJL sign pairs (+-1 fp16), then a pair table per key and value part ----
+  if (tid < 4) tabs[tid] = ((tid & 1) ? 0x3C00u : 0xBC00u) | (((tid & 2) ? 0x3C00u : 0xBC00u) << 16);
+  for (int side = 0; side < 2; ++side) {
+    const int np = side ? prm.nv : prm.nk;
+    for (int p = 0; p < np; ++p) {
+      const SmPart& P = side ? prm.vp[p] : prm.kp[p];
+      uint2* pt = (uint2*)(lds + prm.tab_off + P.ptab);
+      for (int e = tid; e < (int)pair_entries(P.planes); e += kSmThreads) {
+        unsigned ia = 0, ib = 0;
+        for (int pl = 0; pl < P.planes; ++pl) {
+          ia |= ((e >> (2 * pl)) & 1) << pl;
+          ib |= ((e >> (2 * pl + 1)) & 1) << pl;
+        }
+        const unsigned ta = P.tab[ia], tb = P.tab[ib];
+        pt[e] = uint2{(ta & 0xFFFFu) | (tb << 16), (ta >> 16) | (tb & 0xFFFF0000u)};
+      }
+    }
   }
-  if (tid < 4) tabs[2 * kSplitMaxParts * 16 + tid] = ((tid & 1) ? 0x3C00u : 0xBC00u) | (((tid & 2) ? 0x3C00u : 0xBC00u) << 16);
 
   // ---- query parts in the key parts' bases (scratch aliases the staging buffers) ----
   float* qraw = (float*)(lds + prm.wave_off);  // [G][dim]
@@ -192,14 +204,16 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(4)))
   const int64_t t0 = (int64_t)split * prm.split_tokens;
   const int64_t t1 = min(len, t0 + prm.split_tokens);
   uint8_t* wbase = lds + prm.wave_off + wave * prm.wave_bytes;
-  float* wts = (float*)(wbase + 2 * prm.stage_bytes);  // [8 heads][32 tokens] probabilities
-  int* evs = (int*)(wts + kSplitMaxGroup * kSmChunk);  // per value part: weight exponent
-  float* fix = (float*)(evs + kSplitMaxParts);          // per value part: accumulator rescale
+  // in their own LDS arrays, apart from the staging buffers the direct loads write
+  float* wts = wts_s[wave];  // [8 heads][32 tokens] probabilities
+  int* evs = evs_s[wave];    // per value part: weight exponent
+  float* fix = fix_s[wave];  // per value part: accumulator rescale
   if (lane < kSplitMaxParts) evs[lane] = kSmEvUnset;
   const int hA = 2 * g4, hB = 2 * g4 + 1;  // this lane's heads in every C tile
   const float imA = hA < G ? ldexpf(1.f, -sexp[0][hA]) : 0.f, imB = hB < G ? ldexpf(1.f, -sexp[0][hB]) : 0.f;
   const float iqA = hA < G ? ldexpf(1.f, -sexp[1][hA]) : 0.f, iqB = hB < G ? ldexpf(1.f, -sexp[1][hB]) : 0.f;
-  const unsigned* ztab = tabs + 2 * kSplitMaxParts * 16;
+  const unsigned* ztab = tabs;
+  const unsigned offv[4] = {8u * g4, 8u * g4 + 2, 8u * g4 + 4, 8u * g4 + 6};  // bit offsets of this lane's coordinate pairs
 
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   f32x4 acc[2 * NW];
@@ -241,7 +255,7 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(4)))
       const int dq = P.d >> 3, rec = P.rec, kg0 = P.off >> 5, nks = P.d >> 5;
       const uint8_t* kc = sb + P.st_codes;
       const uint8_t* ksg = sb + P.st_signs;
-      const unsigned* tk = tabs + 16 * p;
+      const uint2* tk = (const uint2*)(lds + prm.tab_off + P.ptab);
       f32x4 am[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       f32x4 aq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       for (int ks = 0; ks < nks; ++ks) {
@@ -253,20 +267,25 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(4)))
           if constexpr (PL > 0) {
             unsigned w[PL];
 #pragma unroll
-            for (int pl = 0; pl < PL; ++pl) w[pl] = lds_u32(kc + tok * rec + pl * dq + 4 * ks) >> (8 * g4);
-            unsigned en[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) en[e] = tk[code_index<PL>(w, e)];
+            for (int pl = 0; pl < PL; ++pl) w[pl] = lds_u32(kc + tok * rec + pl * dq + 4 * ks);
             u32x4 bh, bl;
-            entry_operands(en, bh, bl);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {  // coordinates 8 g4 + 2v, + 1 of this step
+              unsigned pi = bfe<2>(w[0], offv[v]);
+#pragma unroll
+              for (int pl = 1; pl < PL; ++pl) pi |= bfe<2>(w[pl], offv[v]) << (2 * pl);
+              const uint2 en = tk[pi];
+              bh[v] = en.x;
+              bl[v] = en.y;
+            }
             am[tile] = mfma16(fm, bh, am[tile]);
             am[tile] = mfma16(fm, bl, am[tile]);
           }
           if constexpr (QJ) {
-            const unsigned z = lds_u32(ksg + tok * dq + 4 * ks) >> (8 * g4);
+            const unsigned z = lds_u32(ksg + tok * dq + 4 * ks);
             u32x4 bz;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) bz[v] = ztab[(z >> (2 * v)) & 3u];
+            for (int v = 0; v < 4; ++v) bz[v] = ztab[bfe<2>(z, offv[v])];
             aq[tile] = mfma16(fq, bz, aq[tile]);
           }
         }
@@ -382,7 +401,7 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(4)))
           constexpr int PL = decltype(PLc)::value;
           const int dq = P.d >> 3, rec = P.rec;
           const uint8_t* vc = sb + P.st_codes + 4 * wd;
-          const unsigned* tv = tabs + kSplitMaxParts * 16 + 16 * p;
+          const uint2* tv = (const uint2*)(lds + prm.tab_off + P.ptab);
           unsigned w[8][PL];
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -390,12 +409,18 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(4)))
             for (int pl = 0; pl < PL; ++pl) w[e][pl] = lds_u32(vc + (8 * g4 + e) * rec + pl * dq);
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            const int bit = 16 * hf + r16;
-            unsigned en[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) en[e] = tv[code_index<PL>(w[e], bit)];
+            const unsigned bit = 16 * hf + r16;
             u32x4 bh, bl;
-            entry_operands(en, bh, bl);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {  // tokens 8 g4 + 2v, + 1
+              unsigned pi = bfe<1>(w[2 * v][0], bit) | (bfe<1>(w[2 * v + 1][0], bit) << 1);
+#pragma unroll
+              for (int pl = 1; pl < PL; ++pl)
+                pi |= (bfe<1>(w[2 * v][pl], bit) | (bfe<1>(w[2 * v + 1][pl], bit) << 1)) << (2 * pl);
+              const uint2 en = tv[pi];
+              bh[v] = en.x;
+              bl[v] = en.y;
+            }
             acc[2 * np + hf] = mfma16(aw, bh, acc[2 * np + hf]);
             acc[2 * np + hf] = mfma16(aw, bl, acc[2 * np + hf]);
           }
@@ -487,10 +512,9 @@ __global__ __launch_bounds__(kSmThreads) void split_combine_kernel(SmParams prm)
   }
 }
 
-}  // namespace
-
-tq_status launch_split_decode(const SplitDecodeLaunch& L, hipStream_t stream) {
-  SmParams prm{};
+// kernel arguments and dynamic LDS bytes of a split decode (lds = 0 when the
+// parts need more LDS than a workgroup has)
+static void build_split_params(const SplitDecodeLaunch& L, SmParams& prm, size_t* lds_out) {
   prm.Hq = L.Hq;
   prm.Hkv = L.Hkv;
   prm.G = L.Hq / L.Hkv;
@@ -555,16 +579,54 @@ tq_status launch_split_decode(const SplitDecodeLaunch& L, hipStream_t stream) {
   }
   prm.stage_bytes = st;
   prm.tab_off = (prm.dk / 32) * 2 * 64 * 16;
-  prm.wave_off = prm.tab_off + (kSmTabWords * 4 + 15) / 16 * 16;
-  // per wave: two staging buffers, probabilities [8][32], exponents and rescale factors
-  prm.wave_bytes = 2 * st + kSplitMaxGroup * kSmChunk * 4 + 2 * kSplitMaxParts * 4;
-  prm.wave_bytes = (prm.wave_bytes + 15) / 16 * 16;
+  int tb = 16;  // QJL sign pairs first
+  for (int p = 0; p < prm.nk; ++p) {
+    prm.kp[p].ptab = tb;
+    tb += 8 << (2 * prm.kp[p].planes);
+  }
+  for (int p = 0; p < prm.nv; ++p) {
+    prm.vp[p].ptab = tb;
+    tb += 8 << (2 * prm.vp[p].planes);
+  }
+  prm.wave_off = prm.tab_off + (tb + 15) / 16 * 16;
+  prm.wave_bytes = 2 * st;  // per wave: two staging buffers
   const size_t prep = (size_t)prm.G * (prm.dim + 2 * prm.dk) * 4;
   const size_t waves = (size_t)kSmWaves * prm.wave_bytes;
   const size_t lds = prm.wave_off + (prep > waves ? prep : waves);
-  if (lds > 160 * 1024) return set_error(TQ_ERR_UNSUPPORTED, "split decode: parts need more LDS than a workgroup has");
+  *lds_out = lds > 160 * 1024 ? 0 : lds;
+}
+
+static void (*split_kernel(int dv))(SmParams) { return dv <= 128 ? split_main_kernel<4> : split_main_kernel<8>; }
+
+}  // namespace
+
+int split_decode_resident_waves(const SplitDecodeLaunch& L) {
+  static thread_local SmParams prm;  // large; host only
+  prm = SmParams{};
+  size_t lds = 0;
+  build_split_params(L, prm, &lds);
+  int fallback = 3 * 4 * 256;  // 3 waves per SIMD on 256 CUs
+  if (lds == 0) return fallback;
+  auto kern = split_kernel(prm.dv);
+  int blocks = 0, dev = 0, cus = 0;
+  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kern, kSmThreads, lds) != hipSuccess ||
+      hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      blocks < 1 || cus < 1) {
+    (void)hipGetLastError();
+    return fallback;
+  }
+  return blocks * kSmWaves * cus;
+}
+
+tq_status launch_split_decode(const SplitDecodeLaunch& L, hipStream_t stream) {
+  static thread_local SmParams prm;
+  prm = SmParams{};
+  size_t lds = 0;
+  build_split_params(L, prm, &lds);
+  if (lds == 0) return set_error(TQ_ERR_UNSUPPORTED, "split decode: parts need more LDS than a workgroup has");
   const dim3 grid((unsigned)((L.n_splits + kSmWaves - 1) / kSmWaves), (unsigned)(L.B * L.Hkv));
-  auto kern = prm.dv <= 128 ? split_main_kernel<4> : split_main_kernel<8>;
+  auto kern = split_kernel(prm.dv);
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return check_hip(e, "split decode: set LDS size");
   hipLaunchKernelGGL(kern, grid, dim3(kSmThreads), lds, stream, prm);
