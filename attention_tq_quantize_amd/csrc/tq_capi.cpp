@@ -620,9 +620,9 @@ static tq_status plan_split_decode(const tq_attn_shape* s, const tq_split_cache*
   if (ns > 65535) return set_error(TQ_ERR_UNSUPPORTED, "split decode: too many splits");
   plan->n_splits = (int)ns;
   plan->split_tokens = per;
-  plan->bytes = (size_t)s->batch * s->n_q_heads * ns * (plan->dv + 2) * sizeof(float);
   L->n_splits = plan->n_splits;
   L->split_tokens = per;
+  plan->bytes = split_decode_workspace_bytes(*L, plan->dk, plan->dv);
   return TQ_OK;
 }
 

@@ -120,6 +120,9 @@ tq_status launch_split_decode(const SplitDecodeLaunch& L, hipStream_t stream);
 // waves of the split decode kernel resident on the current device at once (one
 // context split per wave; a fixed estimate when the device cannot be queried)
 int split_decode_resident_waves(const SplitDecodeLaunch& L);
+// workspace bytes: softmax partials [B][Hq][n_splits][dv + 2], then the score
+// operand fragments and their scales per (batch, KV head)
+size_t split_decode_workspace_bytes(const SplitDecodeLaunch& L, int dk, int dv);
 // d a multiple of 128 in (256, 4096]: the GEMM quantize tables, built at creation
 bool lq_supported(int d);
 tq_status build_large_tables(tq_quantizer* q);

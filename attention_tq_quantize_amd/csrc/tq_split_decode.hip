@@ -70,6 +70,8 @@ struct SmParams {
   float scale;
   float* part;  // [B][Hq][n_splits][dv + 2]
   float* out;   // [B][Hq][dim]
+  u32x4* qfrag;  // [B * Hkv][dk / 32][{mse, qjl}][64 lanes]: score operand fragments
+  int* qexp;     // [B * Hkv][2][8]: their power-of-two scales per (kind, head)
   int stage_bytes, tab_off, wave_off, wave_bytes;  // LDS layout (bytes); fragments at 0
   uint8_t kchan[kSplitMaxDecodeDim], vchan[kSplitMaxDecodeDim];
   uint8_t vword_part[kSplitMaxDecodeDim / 32];  // value part of each 32-coordinate word
@@ -107,6 +109,87 @@ __device__ __forceinline__ float group16_sum(float v) {
   return v;
 }
 
+// One workgroup per (batch, KV head): the query parts rotated into each key
+// part's basis (q' = scale Pi_p q_p, q'' = scale sqrt(pi/2)/d_p S_p q_p, fp32),
+// a power-of-two scale per (kind, head) with |x| 2^S < 2^14, and the fp16 hi/lo
+// MFMA fragments (rows = 8 heads x {hi, lo}, K = 32 coordinates). The matrices
+// are staged through LDS in blocks of rows (padded against bank conflicts).
+constexpr int kPrepRows = 32;
+__global__ __launch_bounds__(kSmThreads) void split_prep_kernel(SmParams prm) {
+  extern __shared__ __align__(16) float sm[];
+  __shared__ int sexp[2][kSplitMaxGroup];
+  const int tid = threadIdx.x;
+  const int bgi = blockIdx.x;
+  const int b = bgi / prm.Hkv, g = bgi % prm.Hkv;
+  const int G = prm.G;
+  float* qraw = sm;                     // [G][dim]
+  float* qr = qraw + G * prm.dim;       // [G][dk]  q'
+  float* qs = qr + G * prm.dk;          // [G][dk]  q''
+  float* mat = qs + G * prm.dk;         // [2][kPrepRows][d + 1] rows of Pi and S
+  for (int e = tid; e < G * prm.dim; e += kSmThreads) {
+    const int h = e / prm.dim, j = e % prm.dim;
+    qraw[e] = __uint_as_float((unsigned)prm.q[((int64_t)b * prm.Hq + g * G + h) * prm.dim + j] << 16);
+  }
+  for (int p = 0; p < prm.nk; ++p) {
+    const SmPart& P = prm.kp[p];
+    const int d = P.d, ld = d + 1;
+    for (int i0 = 0; i0 < d; i0 += kPrepRows) {
+      const int nr = min(kPrepRows, d - i0);
+      __syncthreads();  // previous block consumed (and qraw written)
+      for (int e = tid; e < nr * d; e += kSmThreads) {
+        const int i = e / d, j = e % d;
+        mat[i * ld + j] = P.pi[g][(int64_t)(i0 + i) * d + j];
+        if (P.qjl) mat[kPrepRows * ld + i * ld + j] = P.s[g][(int64_t)(i0 + i) * d + j];
+      }
+      __syncthreads();
+      for (int e = tid; e < G * nr; e += kSmThreads) {
+        const int h = e / nr, i = e % nr;
+        const float* pr = mat + i * ld;
+        const float* sr = mat + kPrepRows * ld + i * ld;
+        float a = 0.f, c = 0.f;
+        for (int j = 0; j < d; ++j) {
+          const float qv = qraw[h * prm.dim + prm.kchan[P.off + j]];
+          a = fmaf(pr[j], qv, a);
+          if (P.qjl) c = fmaf(sr[j], qv, c);
+        }
+        qr[h * prm.dk + P.off + i0 + i] = prm.scale * a;
+        qs[h * prm.dk + P.off + i0 + i] = P.qjl ? prm.scale * P.kappa * c : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 2 * kSplitMaxGroup) {
+    const int kind = tid / kSplitMaxGroup, h = tid % kSplitMaxGroup;
+    const float* src = kind ? qs : qr;
+    float mx = 0.f;
+    if (h < G)
+      for (int j = 0; j < prm.dk; ++j) mx = fmaxf(mx, fabsf(src[h * prm.dk + j]));
+    int e = 0;
+    frexpf(mx, &e);  // mx < 2^e
+    sexp[kind][h] = mx > 0.f ? min(14 - e, 100) : 0;
+    prm.qexp[bgi * 2 * kSplitMaxGroup + tid] = sexp[kind][h];
+  }
+  __syncthreads();
+  u32x4* dst = prm.qfrag + (int64_t)bgi * (prm.dk / 32) * 2 * 64;
+  for (int f = tid; f < (prm.dk / 32) * 2 * 64; f += kSmThreads) {
+    const int ks = f / 128, kind = (f / 64) & 1, ln = f % 64;
+    const int row = ln % 16, h = row >> 1, kb = ks * 32 + 8 * (ln / 16);
+    const bool lo = row & 1;
+    const float* src = kind ? qs : qr;
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x0 = 0.f, x1 = 0.f;
+      if (h < G) {
+        x0 = ldexpf(src[h * prm.dk + kb + 2 * e], sexp[kind][h]);
+        x1 = ldexpf(src[h * prm.dk + kb + 2 * e + 1], sexp[kind][h]);
+      }
+      v[e] = f16_part(x0, lo) | (f16_part(x1, lo) << 16);
+    }
+    dst[f] = v;
+  }
+}
+
 template <int NW>  // 32-coordinate words of the value vector, at most
 __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3))) void split_main_kernel(SmParams prm) {
   extern __shared__ __align__(16) uint8_t lds[];
@@ -141,59 +224,12 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
     }
   }
 
-  // ---- query parts in the key parts' bases (scratch aliases the staging buffers) ----
-  float* qraw = (float*)(lds + prm.wave_off);  // [G][dim]
-  float* qr = qraw + G * prm.dim;              // [G][dk]  q'
-  float* qs = qr + G * prm.dk;                 // [G][dk]  q''
-  for (int e = tid; e < G * prm.dim; e += kSmThreads) {
-    const int h = e / prm.dim, j = e % prm.dim;
-    qraw[e] = __uint_as_float((unsigned)prm.q[((int64_t)b * prm.Hq + g * G + h) * prm.dim + j] << 16);
-  }
-  __syncthreads();
-  for (int p = 0; p < prm.nk; ++p) {
-    const SmPart& P = prm.kp[p];
-    for (int e = tid; e < G * P.d; e += kSmThreads) {
-      const int h = e / P.d, i = e % P.d;
-      const float* prow = P.pi[g] + (int64_t)i * P.d;
-      const float* srow = P.qjl ? P.s[g] + (int64_t)i * P.d : nullptr;
-      float a = 0.f, c = 0.f;
-      for (int j = 0; j < P.d; ++j) {
-        const float qv = qraw[h * prm.dim + prm.kchan[P.off + j]];
-        a = fmaf(prow[j], qv, a);
-        if (P.qjl) c = fmaf(srow[j], qv, c);
-      }
-      qr[h * prm.dk + P.off + i] = prm.scale * a;
-      qs[h * prm.dk + P.off + i] = P.qjl ? prm.scale * P.kappa * c : 0.f;
-    }
-  }
-  __syncthreads();
-  if (tid < 2 * kSplitMaxGroup) {  // power-of-two scale per (kind, head): |x| 2^S < 2^14
-    const int kind = tid / kSplitMaxGroup, h = tid % kSplitMaxGroup;
-    const float* src = kind ? qs : qr;
-    float mx = 0.f;
-    if (h < G)
-      for (int j = 0; j < prm.dk; ++j) mx = fmaxf(mx, fabsf(src[h * prm.dk + j]));
-    int e = 0;
-    frexpf(mx, &e);  // mx < 2^e
-    sexp[kind][h] = mx > 0.f ? min(14 - e, 100) : 0;
-  }
-  __syncthreads();
-  for (int f = tid; f < (prm.dk / 32) * 2 * 64; f += kSmThreads) {
-    const int ks = f / 128, kind = (f / 64) & 1, ln = f % 64;
-    const int row = ln % 16, h = row >> 1, kb = ks * 32 + 8 * (ln / 16);
-    const bool lo = row & 1;
-    const float* src = kind ? qs : qr;
-    u32x4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float x0 = 0.f, x1 = 0.f;
-      if (h < G) {
-        x0 = ldexpf(src[h * prm.dk + kb + 2 * e], sexp[kind][h]);
-        x1 = ldexpf(src[h * prm.dk + kb + 2 * e + 1], sexp[kind][h]);
-      }
-      v[e] = f16_part(x0, lo) | (f16_part(x1, lo) << 16);
-    }
-    frag[f] = v;
+  // ---- score operand fragments of this (batch, KV head), from the prep kernel ----
+  {
+    const int nf = (prm.dk / 32) * 2 * 64;
+    const u32x4* src = prm.qfrag + (int64_t)bgi * nf;
+    for (int f = tid; f < nf; f += kSmThreads) frag[f] = src[f];
+    if (tid < 2 * kSplitMaxGroup) sexp[tid / kSplitMaxGroup][tid % kSplitMaxGroup] = prm.qexp[bgi * 2 * kSplitMaxGroup + tid];
   }
   __syncthreads();
 
@@ -475,21 +511,40 @@ __global__ __launch_bounds__(kSmThreads) void split_combine_kernel(SmParams prm)
   const int hq = (int)(bh % prm.Hq);
   const int g = hq / prm.G;
   const float* src = prm.part + bh * prm.n_splits * (prm.dv + 2);
+  __shared__ float red[kSmWaves];
+  auto block_reduce = [&](float v, bool is_max) -> float {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float u = __shfl_xor(v, o);
+      v = is_max ? fmaxf(v, u) : v + u;
+    }
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int w = 1; w < kSmWaves; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+    return r;
+  };
+  float mloc = -INFINITY;
+  for (int s = tid; s < prm.n_splits; s += kSmThreads) mloc = fmaxf(mloc, src[s * (prm.dv + 2) + prm.dv]);
+  const float Mx = block_reduce(mloc, true);
+  float lloc = 0.f;
+  if (Mx > -INFINITY)
+    for (int s = tid; s < prm.n_splits; s += kSmThreads) {
+      const float ms = src[s * (prm.dv + 2) + prm.dv];
+      if (ms > -INFINITY) lloc += src[s * (prm.dv + 2) + prm.dv + 1] * __expf(ms - Mx);
+    }
+  const float Lx = block_reduce(lloc, false);
   if (tid == 0) {
-    float M = -INFINITY;
-    for (int s = 0; s < prm.n_splits; ++s) M = fmaxf(M, src[s * (prm.dv + 2) + prm.dv]);
-    float L = 0.f;
-    if (M > -INFINITY)
-      for (int s = 0; s < prm.n_splits; ++s)
-        L += src[s * (prm.dv + 2) + prm.dv + 1] * __expf(src[s * (prm.dv + 2) + prm.dv] - M);
-    ml[0] = M;
-    ml[1] = L;
+    ml[0] = Mx;
+    ml[1] = Lx;
   }
   __syncthreads();
   const float M = ml[0], L = ml[1];
   for (int j = tid; j < prm.dv; j += kSmThreads) {
     float v = 0.f;
     if (L > 0.f) {
+#pragma unroll 8
       for (int s = 0; s < prm.n_splits; ++s) {
         const float ms = src[s * (prm.dv + 2) + prm.dv];
         if (ms > -INFINITY) v = fmaf(src[s * (prm.dv + 2) + j], __expf(ms - M), v);
@@ -510,6 +565,10 @@ __global__ __launch_bounds__(kSmThreads) void split_combine_kernel(SmParams prm)
       o[prm.vchan[P.off + j]] = v;
     }
   }
+}
+
+size_t split_part_bytes(int B, int Hq, int n_splits, int dv) {
+  return ((size_t)B * Hq * n_splits * (dv + 2) * sizeof(float) + 255) / 256 * 256;
 }
 
 // kernel arguments and dynamic LDS bytes of a split decode (lds = 0 when the
@@ -590,15 +649,22 @@ static void build_split_params(const SplitDecodeLaunch& L, SmParams& prm, size_t
   }
   prm.wave_off = prm.tab_off + (tb + 15) / 16 * 16;
   prm.wave_bytes = 2 * st;  // per wave: two staging buffers
-  const size_t prep = (size_t)prm.G * (prm.dim + 2 * prm.dk) * 4;
-  const size_t waves = (size_t)kSmWaves * prm.wave_bytes;
-  const size_t lds = prm.wave_off + (prep > waves ? prep : waves);
+  const size_t lds = prm.wave_off + (size_t)kSmWaves * prm.wave_bytes;
   *lds_out = lds > 160 * 1024 ? 0 : lds;
+  // workspace: partials, then the score fragments and their scales per (batch, KV head)
+  const size_t part_bytes = split_part_bytes(L.B, L.Hq, L.n_splits, prm.dv);
+  uint8_t* ws = (uint8_t*)L.workspace;
+  prm.qfrag = ws ? (u32x4*)(ws + part_bytes) : nullptr;
+  prm.qexp = ws ? (int*)(ws + part_bytes + (size_t)L.B * L.Hkv * (prm.dk / 32) * 2 * 64 * 16) : nullptr;
 }
 
 static void (*split_kernel(int dv))(SmParams) { return dv <= 128 ? split_main_kernel<4> : split_main_kernel<8>; }
 
 }  // namespace
+
+size_t split_decode_workspace_bytes(const SplitDecodeLaunch& L, int dk, int dv) {
+  return split_part_bytes(L.B, L.Hq, L.n_splits, dv) + (size_t)L.B * L.Hkv * ((dk / 32) * 2 * 64 * 16 + 2 * kSplitMaxGroup * 4);
+}
 
 int split_decode_resident_waves(const SplitDecodeLaunch& L) {
   static thread_local SmParams prm;  // large; host only
@@ -627,7 +693,15 @@ tq_status launch_split_decode(const SplitDecodeLaunch& L, hipStream_t stream) {
   if (lds == 0) return set_error(TQ_ERR_UNSUPPORTED, "split decode: parts need more LDS than a workgroup has");
   const dim3 grid((unsigned)((L.n_splits + kSmWaves - 1) / kSmWaves), (unsigned)(L.B * L.Hkv));
   auto kern = split_kernel(prm.dv);
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  int dmax = 0;
+  for (int p = 0; p < prm.nk; ++p) dmax = prm.kp[p].d > dmax ? prm.kp[p].d : dmax;
+  const size_t plds = ((size_t)prm.G * (prm.dim + 2 * prm.dk) + 2 * kPrepRows * (dmax + 1)) * sizeof(float);
+  hipError_t e = hipFuncSetAttribute((const void*)split_prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
+  if (e != hipSuccess) return check_hip(e, "split decode: set prep LDS size");
+  hipLaunchKernelGGL(split_prep_kernel, dim3((unsigned)(L.B * L.Hkv)), dim3(kSmThreads), plds, stream, prm);
+  tq_status st0 = launch_check("split decode: prep launch");
+  if (st0 != TQ_OK) return st0;
+  e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return check_hip(e, "split decode: set LDS size");
   hipLaunchKernelGGL(kern, grid, dim3(kSmThreads), lds, stream, prm);
   tq_status st2 = launch_check("split decode: main launch");
