@@ -8,29 +8,31 @@
 // (channels no value part keeps come out 0).
 //
 // Matrix-core design for part dimensions that are multiples of 32 (the 32 / 96
-// split of a 128-channel head). A workgroup of 4 waves takes one (batch, KV
-// head) and 4 context splits, one per wave. The workgroup first rotates the
-// query parts into each key part's basis (q' = scale Pi_p q_p, q'' = scale
-// sqrt(pi/2)/d_p S_p q_p), scales each head by a power of two and stores them as
-// fp16 hi/lo MFMA fragments (rows = 8 heads x {hi, lo}, K = 32 coordinates).
-// Then every wave walks its split in chunks of 32 tokens:
-//  * the chunk's records of every part are copied straight from HBM into the
-//    wave's LDS staging buffer (global_load_lds, double-buffered: the next
-//    chunk is in flight while this one is computed);
-//  * scores: per key part and 32-coordinate step, each lane decodes 8
-//    coordinates of one token into exact fp16 hi/lo centroid pairs (a 16-entry
-//    LDS table per part) and the QJL signs into +-1, and the matrix cores form
-//    <q', c~> and <q'', z> for 16 tokens x 8 heads per instruction;
-//  * an online softmax per head over the chunk (16-lane reductions);
-//  * values: the probabilities times each value part's norms become the fp16
-//    hi/lo weight operand (rows = 8 heads x {hi, lo}, K = 32 tokens), each lane
-//    decodes one coordinate of 8 tokens into the centroid operand, and the
-//    matrix cores accumulate 16 coordinates x 8 heads per instruction in the
-//    part's rotated basis (a running power-of-two exponent per part keeps the
-//    weights in fp16 range).
-// Splits are merged by log-sum-exp in a second kernel that also rotates each
-// value part back (Pi_p^T) and scatters it to its channels (deterministic, no
-// atomics).
+// split of a 128-channel head), in three kernels:
+//  1. prep, one workgroup per (batch, KV head): the query parts rotated into
+//     each key part's basis (q' = scale Pi_p q_p, q'' = scale sqrt(pi/2)/d_p
+//     S_p q_p), a power-of-two scale per head, and the fp16 hi/lo MFMA
+//     fragments (rows = 8 heads x {hi, lo}, K = 32 coordinates), written to the
+//     workspace;
+//  2. main, one wave per context split (as many splits as waves fit on the
+//     device at once). Each wave walks its split in chunks of 32 tokens:
+//      * the chunk's records of every part are copied straight from HBM into
+//        the wave's LDS staging buffer (global_load_lds, double-buffered);
+//      * scores: per key part and 32-coordinate step, each lane turns two
+//        coordinates of one token at a time into exact fp16 hi/lo centroid
+//        operands with one bit-field extract per plane and one read of a pair
+//        table (the QJL signs into +-1 likewise), and the matrix cores form
+//        <q', c~> and <q'', z> for 16 tokens x 8 heads per instruction;
+//      * an online softmax per head over the chunk (16-lane reductions);
+//      * values: the probabilities times each value part's norms become the
+//        fp16 hi/lo weight operand (rows = 8 heads x {hi, lo}, K = 32 tokens),
+//        each lane turns one coordinate of two tokens at a time into the
+//        centroid operand, and the matrix cores accumulate 16 coordinates x 8
+//        heads per instruction in the part's rotated basis (a running
+//        power-of-two exponent per part keeps the weights in fp16 range);
+//  3. combine, one workgroup per (batch, query head): log-sum-exp merge of the
+//     splits, each value part rotated back (Pi_p^T) and scattered to its
+//     channels (deterministic, no atomics).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>

@@ -271,7 +271,7 @@ def outlier_split_decode(tq, syn, torch, dev, reps=10):
     64/8 heads, d=128, ctx 131072): keys TurboQuant_prod with the 32 largest-RMS
     channels at 3 bits and the other 96 at 2, values TurboQuant_mse with the same
     bit split (96 B per (token, KV head) against 108 B for the uniform 3-bit cache);
-    tq_decode_attention_split (generic fp32 kernels)."""
+    tq_decode_attention_split (matrix-core split kernels)."""
     B, Hq, Hkv, d, T = 8, 64, 8, 128, 131072
     sides = []
     for tensor, var in ((syn.T_K, "prod"), (syn.T_V, "mse")):

@@ -394,8 +394,10 @@ tq_status tq_decode_append_attention(const tq_attn_shape* shape, const void* q, 
  * head_dim = the full channel count (at most 256), at most 8 KV heads and 8
  * query heads per KV head. q: device bf16 [B][n_q_heads][head_dim];
  * out: device float32 [B][n_q_heads][head_dim]; workspace: at least
- * tq_decode_split_workspace_size() bytes (per-split softmax partials).
- * Generic fp32 kernels, split context with a log-sum-exp combine
+ * tq_decode_split_workspace_size() bytes (per-split softmax partials and the
+ * rotated query operands; the size depends on the device, which sets the number
+ * of context splits). Scores and value sums run on the matrix cores as exact
+ * fp16 hi/lo products, split context with a log-sum-exp combine
  * (deterministic). Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED (limits
  * above), TQ_ERR_WORKSPACE.
  */
