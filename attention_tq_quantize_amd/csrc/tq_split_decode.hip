@@ -47,6 +47,7 @@ constexpr int kSmThreads = 64 * kSmWaves;
 constexpr int kSmChunk = 32;                // tokens per step
 constexpr int kSmMaxSeg = 6 * kSplitMaxParts;
 constexpr int kSmEvUnset = -1000;
+constexpr int kSmSplitsCached = 1024;  // split weights the combine keeps in LDS
 
 struct SmPart {
   int d, planes, off, qjl;
@@ -75,6 +76,7 @@ struct SmParams {
   u32x4* qfrag;  // [B * Hkv][dk / 32][{mse, qjl}][64 lanes]: score operand fragments
   int* qexp;     // [B * Hkv][2][8]: their power-of-two scales per (kind, head)
   int stage_bytes, tab_off, wave_off, wave_bytes;  // LDS layout (bytes); fragments at 0
+  int prep_rows;  // matrix rows the prep kernel stages per block
   uint8_t kchan[kSplitMaxDecodeDim], vchan[kSplitMaxDecodeDim];
   uint8_t vword_part[kSplitMaxDecodeDim / 32];  // value part of each 32-coordinate word
   SmPart kp[kSplitMaxParts], vp[kSplitMaxParts];
@@ -116,7 +118,6 @@ __device__ __forceinline__ float group16_sum(float v) {
 // a power-of-two scale per (kind, head) with |x| 2^S < 2^14, and the fp16 hi/lo
 // MFMA fragments (rows = 8 heads x {hi, lo}, K = 32 coordinates). The matrices
 // are staged through LDS in blocks of rows (padded against bank conflicts).
-constexpr int kPrepRows = 32;
 __global__ __launch_bounds__(kSmThreads) void split_prep_kernel(SmParams prm) {
   extern __shared__ __align__(16) float sm[];
   __shared__ int sexp[2][kSplitMaxGroup];
@@ -124,35 +125,59 @@ __global__ __launch_bounds__(kSmThreads) void split_prep_kernel(SmParams prm) {
   const int bgi = blockIdx.x;
   const int b = bgi / prm.Hkv, g = bgi % prm.Hkv;
   const int G = prm.G;
-  float* qraw = sm;                     // [G][dim]
-  float* qr = qraw + G * prm.dim;       // [G][dk]  q'
+  float* qraw = sm;                     // [G][dk]: q in the key parts' channel order
+  float* qr = qraw + G * prm.dk;        // [G][dk]  q'
   float* qs = qr + G * prm.dk;          // [G][dk]  q''
-  float* mat = qs + G * prm.dk;         // [2][kPrepRows][d + 1] rows of Pi and S
-  for (int e = tid; e < G * prm.dim; e += kSmThreads) {
-    const int h = e / prm.dim, j = e % prm.dim;
-    qraw[e] = __uint_as_float((unsigned)prm.q[((int64_t)b * prm.Hq + g * G + h) * prm.dim + j] << 16);
+  float* mat = qs + G * prm.dk;         // [2][prep_rows][d + 1] rows of Pi and S
+  for (int e = tid; e < G * prm.dk; e += kSmThreads) {
+    const int h = e / prm.dk, j = e % prm.dk;
+    qraw[e] = __uint_as_float((unsigned)prm.q[((int64_t)b * prm.Hq + g * G + h) * prm.dim + prm.kchan[j]] << 16);
   }
   for (int p = 0; p < prm.nk; ++p) {
     const SmPart& P = prm.kp[p];
     const int d = P.d, ld = d + 1;
-    for (int i0 = 0; i0 < d; i0 += kPrepRows) {
-      const int nr = min(kPrepRows, d - i0);
+    for (int i0 = 0; i0 < d; i0 += prm.prep_rows) {
+      const int nr = min(prm.prep_rows, d - i0);
       __syncthreads();  // previous block consumed (and qraw written)
-      for (int e = tid; e < nr * d; e += kSmThreads) {
-        const int i = e / d, j = e % d;
-        mat[i * ld + j] = P.pi[g][(int64_t)(i0 + i) * d + j];
-        if (P.qjl) mat[kPrepRows * ld + i * ld + j] = P.s[g][(int64_t)(i0 + i) * d + j];
+      {  // eight loads in flight per thread and matrix, then the LDS stores
+        const float* pg = P.pi[g] + (int64_t)i0 * d;
+        const float* sg = P.qjl ? P.s[g] + (int64_t)i0 * d : pg;
+        const int n = nr * d;
+        for (int e0 = tid; e0 < n; e0 += 8 * kSmThreads) {
+          float vp[8], vs[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int e = e0 + u * kSmThreads;
+            vp[u] = e < n ? pg[e] : 0.f;
+            vs[u] = e < n ? sg[e] : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int e = e0 + u * kSmThreads;
+            if (e < n) {
+              const int i = e / d, j = e - i * d;
+              mat[i * ld + j] = vp[u];
+              if (P.qjl) mat[prm.prep_rows * ld + i * ld + j] = vs[u];
+            }
+          }
+        }
       }
       __syncthreads();
       for (int e = tid; e < G * nr; e += kSmThreads) {
         const int h = e / nr, i = e % nr;
         const float* pr = mat + i * ld;
-        const float* sr = mat + kPrepRows * ld + i * ld;
+        const float* sr = mat + prm.prep_rows * ld + i * ld;
         float a = 0.f, c = 0.f;
-        for (int j = 0; j < d; ++j) {
-          const float qv = qraw[h * prm.dim + prm.kchan[P.off + j]];
-          a = fmaf(pr[j], qv, a);
-          if (P.qjl) c = fmaf(sr[j], qv, c);
+        const float* qp = qraw + h * prm.dk + P.off;
+        if (P.qjl) {
+#pragma unroll 8
+          for (int j = 0; j < d; ++j) {
+            a = fmaf(pr[j], qp[j], a);
+            c = fmaf(sr[j], qp[j], c);
+          }
+        } else {
+#pragma unroll 8
+          for (int j = 0; j < d; ++j) a = fmaf(pr[j], qp[j], a);
         }
         qr[h * prm.dk + P.off + i0 + i] = prm.scale * a;
         qs[h * prm.dk + P.off + i0 + i] = P.qjl ? prm.scale * P.kappa * c : 0.f;
@@ -160,16 +185,19 @@ __global__ __launch_bounds__(kSmThreads) void split_prep_kernel(SmParams prm) {
     }
   }
   __syncthreads();
-  if (tid < 2 * kSplitMaxGroup) {
-    const int kind = tid / kSplitMaxGroup, h = tid % kSplitMaxGroup;
+  {  // 16 threads per (kind, head): largest |x|, then its power-of-two scale
+    const int kind = tid / 128, h = (tid / 16) % kSplitMaxGroup, l16 = tid % 16;
     const float* src = kind ? qs : qr;
     float mx = 0.f;
     if (h < G)
-      for (int j = 0; j < prm.dk; ++j) mx = fmaxf(mx, fabsf(src[h * prm.dk + j]));
-    int e = 0;
-    frexpf(mx, &e);  // mx < 2^e
-    sexp[kind][h] = mx > 0.f ? min(14 - e, 100) : 0;
-    prm.qexp[bgi * 2 * kSplitMaxGroup + tid] = sexp[kind][h];
+      for (int j = l16; j < prm.dk; j += 16) mx = fmaxf(mx, fabsf(src[h * prm.dk + j]));
+    mx = group16_max(mx);
+    if (l16 == 0) {
+      int e = 0;
+      frexpf(mx, &e);  // mx < 2^e
+      sexp[kind][h] = mx > 0.f ? min(14 - e, 100) : 0;
+      prm.qexp[bgi * 2 * kSplitMaxGroup + kind * kSplitMaxGroup + h] = sexp[kind][h];
+    }
   }
   __syncthreads();
   u32x4* dst = prm.qfrag + (int64_t)bgi * (prm.dk / 32) * 2 * 64;
@@ -542,16 +570,22 @@ __global__ __launch_bounds__(kSmThreads) void split_combine_kernel(SmParams prm)
     ml[1] = Lx;
   }
   __syncthreads();
-  const float M = ml[0], L = ml[1];
+  const float L = ml[1];
+  // weight of each split, exp(m_s - M) / L (0 for empty splits), then the merged sum
+  __shared__ float sw[kSmSplitsCached];
+  const int nsc = prm.n_splits < kSmSplitsCached ? prm.n_splits : kSmSplitsCached;
+  for (int s = tid; s < nsc; s += kSmThreads) {
+    const float ms = src[s * (prm.dv + 2) + prm.dv];
+    sw[s] = (L > 0.f && ms > -INFINITY) ? __expf(ms - Mx) / L : 0.f;
+  }
+  __syncthreads();
   for (int j = tid; j < prm.dv; j += kSmThreads) {
     float v = 0.f;
-    if (L > 0.f) {
 #pragma unroll 8
-      for (int s = 0; s < prm.n_splits; ++s) {
-        const float ms = src[s * (prm.dv + 2) + prm.dv];
-        if (ms > -INFINITY) v = fmaf(src[s * (prm.dv + 2) + j], __expf(ms - M), v);
-      }
-      v /= L;
+    for (int s = 0; s < nsc; ++s) v = fmaf(src[s * (prm.dv + 2) + j], sw[s], v);
+    for (int s = nsc; s < prm.n_splits; ++s) {
+      const float ms = src[s * (prm.dv + 2) + prm.dv];
+      if (L > 0.f && ms > -INFINITY) v = fmaf(src[s * (prm.dv + 2) + j], __expf(ms - Mx) / L, v);
     }
     a[j] = v;
   }
@@ -563,7 +597,9 @@ __global__ __launch_bounds__(kSmThreads) void split_combine_kernel(SmParams prm)
     const SmPart& P = prm.vp[p];
     for (int j = tid; j < P.d; j += kSmThreads) {
       float v = 0.f;
-      for (int i = 0; i < P.d; ++i) v = fmaf(P.pi[g][(int64_t)i * P.d + j], a[P.off + i], v);
+      const float* pc = P.pi[g] + j;
+#pragma unroll 8
+      for (int i = 0; i < P.d; ++i) v = fmaf(pc[(int64_t)i * P.d], a[P.off + i], v);
       o[prm.vchan[P.off + j]] = v;
     }
   }
@@ -697,7 +733,10 @@ tq_status launch_split_decode(const SplitDecodeLaunch& L, hipStream_t stream) {
   auto kern = split_kernel(prm.dv);
   int dmax = 0;
   for (int p = 0; p < prm.nk; ++p) dmax = prm.kp[p].d > dmax ? prm.kp[p].d : dmax;
-  const size_t plds = ((size_t)prm.G * (prm.dim + 2 * prm.dk) + 2 * kPrepRows * (dmax + 1)) * sizeof(float);
+  // prep LDS: q, q', q'' [G][dk] each, then as many rows of Pi and S as fit (at most 128)
+  const int fit = (int)((160 * 1024 / 4 - (size_t)prm.G * 3 * prm.dk) / (2 * (dmax + 1)));
+  prm.prep_rows = fit < 128 ? fit : 128;
+  const size_t plds = ((size_t)prm.G * 3 * prm.dk + 2 * (size_t)prm.prep_rows * (dmax + 1)) * sizeof(float);
   hipError_t e = hipFuncSetAttribute((const void*)split_prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
   if (e != hipSuccess) return check_hip(e, "split decode: set prep LDS size");
   hipLaunchKernelGGL(split_prep_kernel, dim3((unsigned)(L.B * L.Hkv)), dim3(kSmThreads), plds, stream, prm);
