@@ -4,7 +4,8 @@ more bits) against the oracle's decode_attention_split on oracle-packed
 records: outputs within rtol 1e-3 / atol 1e-4. Cases: the pages' split of a
 128-channel head (32 channels at 3 bits, 96 at 2; prod keys, mse values) with
 GQA 8 and ragged lengths; parts that drop channels, with different channel
-lists for keys and values, and an empty context; GQA 1 at head_dim 64."""
+lists for keys and values, and an empty context; GQA 1 at head_dim 64; every
+plane count of key and value parts; head_dim 256; splits of several chunks."""
 import math
 
 import numpy as np
@@ -88,6 +89,15 @@ CASES = [
      [(64, "prod", 3), (32, "mse", 2)], [(32, "mse", 4), (64, "mse", 2)]),
     ("gqa1_d64", 3, 4, 4, 64, 40, [40, 1, 17],
      [(32, "mse", 2), (32, "prod", 2)], [(32, "mse", 3), (32, "mse", 1)]),
+    # every plane count of the key parts (prod b=1 is signs only, mse b=1 is one
+    # plane, prod b=4 has three planes and signs), four parts per side
+    ("all_key_plane_counts", 2, 8, 2, 128, 150, [150, 61],
+     [(32, "prod", 1), (32, "mse", 1), (32, "mse", 3), (32, "prod", 4)], [(64, "mse", 4), (64, "mse", 1)]),
+    ("mse4_keys_gqa4", 1, 8, 2, 128, 97, [97],
+     [(64, "mse", 4), (64, "prod", 2)], [(96, "mse", 2), (32, "mse", 3)]),
+    # head_dim 256: value vectors longer than 128 coordinates (the wider kernel)
+    ("head_dim_256", 2, 16, 2, 256, 130, [130, 33],
+     [(64, "prod", 3), (192, "prod", 2)], [(64, "mse", 3), (192, "mse", 2)]),
     # 8 KV heads at batch 1: 512 context splits of 64 tokens, so every split runs
     # two chunks of 32 (the second one's records in flight during the first) and
     # the last split ends in a partial chunk
