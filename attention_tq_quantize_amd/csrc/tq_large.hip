@@ -42,45 +42,50 @@ struct LargeQuantParams {
   const float* s[kMaxGroupsPerLaunch];
 };
 
-// out[v][i] = sum_j M[i][j] in[v][j] for the workgroup's nv vectors: thread t
-// takes rows t, t + 256, ...; each row is read once (float4) for all vectors.
-template <int VB>
+// out[v][i] = sum_j M[i][j] in[v][j] for the workgroup's nv vectors. The work
+// items are (row, group of VG vectors), spread over the threads so that small d
+// still uses them all; each item reads its row once (float4) for its vectors.
+template <int VB, int VG = VB>
 __device__ void rows_times(const float* __restrict__ M, const float* in, float* out, int d, int nv) {
-  for (int i = threadIdx.x; i < d; i += kThreads) {
+  static_assert(VB % VG == 0, "vector groups");
+  for (int e = threadIdx.x; e < d * (VB / VG); e += kThreads) {
+    const int i = e % d, g0 = (e / d) * VG;
     const float4* row = (const float4*)(M + (int64_t)i * d);
-    float acc[VB];
+    float acc[VG];
 #pragma unroll
-    for (int v = 0; v < VB; ++v) acc[v] = 0.f;
+    for (int v = 0; v < VG; ++v) acc[v] = 0.f;
     for (int j4 = 0; j4 < d / 4; ++j4) {
       const float4 m = row[j4];
 #pragma unroll
-      for (int v = 0; v < VB; ++v) {
-        const float4 u = ((const float4*)(in + (size_t)v * d))[j4];
+      for (int v = 0; v < VG; ++v) {
+        const float4 u = ((const float4*)(in + (size_t)(g0 + v) * d))[j4];
         acc[v] = fmaf(m.x, u.x, fmaf(m.y, u.y, fmaf(m.z, u.z, fmaf(m.w, u.w, acc[v]))));
       }
     }
 #pragma unroll
-    for (int v = 0; v < VB; ++v)
-      if (v < nv) out[(size_t)v * d + i] = acc[v];
+    for (int v = 0; v < VG; ++v)
+      if (g0 + v < nv) out[(size_t)(g0 + v) * d + i] = acc[v];
   }
 }
 
-// out[v][j] = sum_i M[i][j] in[v][i]: thread t takes columns t, t + 256, ...
-// (consecutive threads read consecutive elements of a row)
-template <int VB>
+// out[v][j] = sum_i M[i][j] in[v][i]: work items (column, group of VG vectors);
+// consecutive threads read consecutive elements of a row
+template <int VB, int VG = VB>
 __device__ void cols_times(const float* __restrict__ M, const float* in, float* out, int d, int nv) {
-  for (int j = threadIdx.x; j < d; j += kThreads) {
-    float acc[VB];
+  static_assert(VB % VG == 0, "vector groups");
+  for (int e = threadIdx.x; e < d * (VB / VG); e += kThreads) {
+    const int j = e % d, g0 = (e / d) * VG;
+    float acc[VG];
 #pragma unroll
-    for (int v = 0; v < VB; ++v) acc[v] = 0.f;
+    for (int v = 0; v < VG; ++v) acc[v] = 0.f;
     for (int i = 0; i < d; ++i) {
       const float m = M[(int64_t)i * d + j];
 #pragma unroll
-      for (int v = 0; v < VB; ++v) acc[v] = fmaf(m, in[(size_t)v * d + i], acc[v]);
+      for (int v = 0; v < VG; ++v) acc[v] = fmaf(m, in[(size_t)(g0 + v) * d + i], acc[v]);
     }
 #pragma unroll
-    for (int v = 0; v < VB; ++v)
-      if (v < nv) out[(size_t)v * d + j] = acc[v];
+    for (int v = 0; v < VG; ++v)
+      if (g0 + v < nv) out[(size_t)(g0 + v) * d + j] = acc[v];
   }
 }
 
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void quantize_large_kernel(LargeQuantPara
   }
   __syncthreads();
   // ---- y = Pi u ----
-  rows_times<VB>(pi, A, Bm, d, VB);
+  rows_times<VB, (VB < 8 ? VB : 8)>(pi, A, Bm, d, VB);
   __syncthreads();
   // ---- nearest centroids, codes, residual ----
   const int K = 1 << prm.planes;
@@ -166,9 +171,9 @@ __global__ __launch_bounds__(kThreads) void quantize_large_kernel(LargeQuantPara
     if (lane == 0) gam_s[v] = inv_s[v] > 0.f ? (float)sqrt(acc) : 0.f;
   }
   __syncthreads();  // the indices in A are no longer needed
-  cols_times<VB>(pi, Bm, A, d, VB);
+  cols_times<VB, (VB < 8 ? VB : 8)>(pi, Bm, A, d, VB);
   __syncthreads();
-  rows_times<VB>(prm.s[grp], A, Bm, d, VB);  // Bm = p
+  rows_times<VB, (VB < 8 ? VB : 8)>(prm.s[grp], A, Bm, d, VB);  // Bm = p
   __syncthreads();
   if (prm.proj_dbg)
     for (int e = threadIdx.x; e < VB * d; e += kThreads)
@@ -1072,7 +1077,9 @@ tq_status launch_quantize_large(const QuantizeLaunch& a, hipStream_t stream) {
 tq_status launch_quantize_fp32(const QuantizeLaunch& a, const uint16_t* chan, int64_t x_stride, hipStream_t stream) {
   const tq_quantizer* q0 = a.qz[0];
   const int d = q0->d;
-  const int vb = d <= 2048 ? 8 : 4;
+  // vectors per workgroup: 32 for d <= 128 (the matrix rows are then read once
+  // per 32 vectors and every thread has work), 8 up to 2048, 4 beyond
+  const int vb = d <= 128 ? 32 : (d <= 2048 ? 8 : 4);
   const size_t lds = ((size_t)2 * vb * d + 3 * vb) * sizeof(float);
   for (int g0 = 0; g0 < a.n_groups; g0 += kMaxGroupsPerLaunch) {
     const int ng = min(kMaxGroupsPerLaunch, a.n_groups - g0);
@@ -1103,7 +1110,12 @@ tq_status launch_quantize_fp32(const QuantizeLaunch& a, const uint16_t* chan, in
       prm.s[g] = a.qz[g0 + g]->s32;
     }
     const dim3 grid((unsigned)((a.n_per_group + vb - 1) / vb), (unsigned)ng);
-    if (vb == 8) {
+    if (vb == 32) {
+      hipError_t e = hipFuncSetAttribute((const void*)quantize_large_kernel<32>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return check_hip(e, "quantize: set LDS size");
+      hipLaunchKernelGGL(quantize_large_kernel<32>, grid, dim3(kThreads), lds, stream, prm);
+    } else if (vb == 8) {
       hipError_t e = hipFuncSetAttribute((const void*)quantize_large_kernel<8>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return check_hip(e, "quantize: set LDS size");
