@@ -105,19 +105,23 @@ __global__ __launch_bounds__(kThreads) void quantize_large_kernel(LargeQuantPara
   const int64_t gbase = (prm.group_base + grp) * n;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* pi = prm.pi[grp];
+  // ---- inputs of all the workgroup's vectors (every load in flight at once) ----
+  for (int e = threadIdx.x; e < VB * d; e += kThreads) {
+    const int v = e / d, j = e - v * d;
+    float xv = 0.f;
+    if (v < nv) {
+      const int64_t src = (gbase + v0 + v) * prm.x_stride + (prm.chan_map ? prm.chan[j] : j);
+      xv = prm.x_bf16 ? bf16_val(((const uint16_t*)prm.x)[src]) : ((const float*)prm.x)[src];
+    }
+    A[e] = xv;
+  }
+  __syncthreads();
   // ---- norms (fp64) and unit vectors ----
   for (int v = wave; v < VB; v += kThreads / 64) {
     double acc = 0.0;
-    if (v < nv) {
-      const int64_t row = gbase + v0 + v;
-      for (int j = lane; j < d; j += 64) {
-        const int64_t src = row * prm.x_stride + (prm.chan_map ? prm.chan[j] : j);
-        const float xv = prm.x_bf16 ? bf16_val(((const uint16_t*)prm.x)[src]) : ((const float*)prm.x)[src];
-        A[(size_t)v * d + j] = xv;
-        acc = fma((double)xv, (double)xv, acc);
-      }
-    } else {
-      for (int j = lane; j < d; j += 64) A[(size_t)v * d + j] = 0.f;
+    for (int j = lane; j < d; j += 64) {
+      const float xv = A[(size_t)v * d + j];
+      acc = fma((double)xv, (double)xv, acc);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
