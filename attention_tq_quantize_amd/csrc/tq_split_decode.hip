@@ -35,7 +35,9 @@
 //     channels (deterministic, no atomics).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "tq_device.h"
 
@@ -712,15 +714,36 @@ int split_decode_resident_waves(const SplitDecodeLaunch& L) {
   int fallback = 3 * 4 * 256;  // 3 waves per SIMD on 256 CUs
   if (lds == 0) return fallback;
   auto kern = split_kernel(prm.dv);
-  int blocks = 0, dev = 0, cus = 0;
-  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kern, kSmThreads, lds) != hipSuccess ||
-      hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      blocks < 1 || cus < 1) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     return fallback;
   }
-  return blocks * kSmWaves * cus;
+  // the answer depends on (device, kernel, LDS bytes) only: remember it
+  struct Entry {
+    int dev;
+    void (*kern)(SmParams);
+    size_t lds;
+    int waves;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> seen;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry& e : seen)
+      if (e.dev == dev && e.kern == kern && e.lds == lds) return e.waves;
+  }
+  int blocks = 0, cus = 0;
+  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kern, kSmThreads, lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || blocks < 1 || cus < 1) {
+    (void)hipGetLastError();
+    return fallback;
+  }
+  const int waves = blocks * kSmWaves * cus;
+  std::lock_guard<std::mutex> lock(mu);
+  if (seen.size() < 64) seen.push_back(Entry{dev, kern, lds, waves});
+  return waves;
 }
 
 tq_status launch_split_decode(const SplitDecodeLaunch& L, hipStream_t stream) {
