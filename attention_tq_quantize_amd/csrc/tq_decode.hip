@@ -759,7 +759,7 @@ struct DecCombineParams {
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecCombineParams prm) {
   extern __shared__ float wsplit[];  // [n_splits]
-  __shared__ float red[kThreads];
+  __shared__ float red[2][kThreads / 64];
   __shared__ float part[kThreads / D][D];
   __shared__ float o[D];
   const int64_t bhq = blockIdx.x;
@@ -767,17 +767,18 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecCombinePara
   const int hkv = hq / prm.group;
   const int ns = prm.n_splits;
   const float* ml = prm.part_ml + bhq * ns * 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // block reductions: within each wave by shuffles, then across the waves
   float mx = -INFINITY;
   for (int s = threadIdx.x; s < ns; s += kThreads)
     if (ml[2 * s + 1] > 0.f) mx = fmaxf(mx, ml[2 * s]);
-  red[threadIdx.x] = mx;
+#pragma unroll
+  for (int o2 = 32; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+  if (lane == 0) red[0][wave] = mx;
   __syncthreads();
-  for (int st = kThreads / 2; st > 0; st >>= 1) {
-    if (threadIdx.x < st) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + st]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
+  float M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, red[0][w]);
   float lsum = 0.f;
   for (int s = threadIdx.x; s < ns; s += kThreads) {
     const float l = ml[2 * s + 1];
@@ -785,28 +786,26 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecCombinePara
     wsplit[s] = wgt;
     lsum += wgt * l;
   }
-  red[threadIdx.x] = lsum;
-  __syncthreads();
-  for (int st = kThreads / 2; st > 0; st >>= 1) {
-    if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
-    __syncthreads();
-  }
-  const float L = red[0];
+#pragma unroll
+  for (int o2 = 32; o2 > 0; o2 >>= 1) lsum += __shfl_xor(lsum, o2);
+  if (lane == 0) red[1][wave] = lsum;
+  __syncthreads();  // also publishes wsplit
+  float L = red[1][0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) L += red[1][w];
   const float invL = L > 0.f ? 1.0f / L : 0.f;
   // merged accumulator: thread (j, phase) sums splits phase, phase + P, ...
   constexpr int P = kThreads / D;
   const int j = threadIdx.x % D, ph = threadIdx.x / D;
   const float* acc = prm.part_acc + bhq * (int64_t)ns * D + j;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // eight loads in flight
   int s = ph;
-  for (; s + 3 * P < ns; s += 4 * P) {
-    a0 += wsplit[s] * acc[(int64_t)s * D];
-    a1 += wsplit[s + P] * acc[(int64_t)(s + P) * D];
-    a2 += wsplit[s + 2 * P] * acc[(int64_t)(s + 2 * P) * D];
-    a3 += wsplit[s + 3 * P] * acc[(int64_t)(s + 3 * P) * D];
+  for (; s + 7 * P < ns; s += 8 * P) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] += wsplit[s + u * P] * acc[(int64_t)(s + u * P) * D];
   }
-  for (; s < ns; s += P) a0 += wsplit[s] * acc[(int64_t)s * D];
-  part[ph][j] = (a0 + a1) + (a2 + a3);
+  for (; s < ns; s += P) a[0] += wsplit[s] * acc[(int64_t)s * D];
+  part[ph][j] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   __syncthreads();
   if (threadIdx.x < D) {
     float t = 0.f;
@@ -817,14 +816,12 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecCombinePara
   __syncthreads();
   // out[j] = sum_i Pi_V[i][j] o[i]
   const float* Pv = prm.pv[hkv];
-  float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
-  for (int i = ph * 4; i < D; i += 4 * P) {
-    b0 += Pv[(int64_t)i * D + j] * o[i];
-    b1 += Pv[(int64_t)(i + 1) * D + j] * o[i + 1];
-    b2 += Pv[(int64_t)(i + 2) * D + j] * o[i + 2];
-    b3 += Pv[(int64_t)(i + 3) * D + j] * o[i + 3];
+  float bq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // eight rows in flight
+  for (int i = ph * 8; i < D; i += 8 * P) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) bq[u] += Pv[(int64_t)(i + u) * D + j] * o[i + u];
   }
-  part[ph][j] = (b0 + b1) + (b2 + b3);
+  part[ph][j] = ((bq[0] + bq[1]) + (bq[2] + bq[3])) + ((bq[4] + bq[5]) + (bq[6] + bq[7]));
   __syncthreads();
   if (threadIdx.x < D) {
     float t = 0.f;
