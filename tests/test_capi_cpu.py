@@ -152,3 +152,26 @@ def test_split_argument_errors(lib):
     ch = (ctypes.c_int32 * 4)(0, 1, 2, 3)
     assert lib.tq_quantize_split(None, 1, ch, 4, None, 0, 1, None, None) == tq.TQ_ERR_INVALID_ARG
     assert lib.tq_inner_products_split(None, 1, ch, 4, None, 1, None, 1, None, None) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_split_decode_argument_errors(lib):
+    """Shape and cache-description checks of the split decode run before any
+    device work: NULL shape, empty or oversize shapes, NULL cache descriptions."""
+    nb = ctypes.c_size_t(0)
+    empty = tq.SplitCache(0, None, None, None)
+    ok_shape = tq.AttnShape(1, 8, 1, 128, 64)
+    assert lib.tq_decode_split_workspace_size(None, ctypes.byref(empty), ctypes.byref(empty),
+                                              ctypes.byref(nb)) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_decode_split_workspace_size(ctypes.byref(ok_shape), ctypes.byref(empty), ctypes.byref(empty),
+                                              None) == tq.TQ_ERR_INVALID_ARG
+    for shape, err in ((tq.AttnShape(0, 8, 1, 128, 64), tq.TQ_ERR_INVALID_ARG),     # empty batch
+                       (tq.AttnShape(1, 18, 9, 128, 64), tq.TQ_ERR_UNSUPPORTED),    # more than 8 KV heads
+                       (tq.AttnShape(1, 18, 1, 128, 64), tq.TQ_ERR_UNSUPPORTED),    # 18 query heads per KV head
+                       (tq.AttnShape(1, 12, 8, 128, 64), tq.TQ_ERR_UNSUPPORTED),    # heads do not divide
+                       (tq.AttnShape(1, 8, 1, 512, 64), tq.TQ_ERR_UNSUPPORTED),     # head_dim above 256
+                       (tq.AttnShape(1, 8, 1, 128, 1 << 32), tq.TQ_ERR_UNSUPPORTED),
+                       (ok_shape, tq.TQ_ERR_INVALID_ARG)):                          # NULL cache description
+        assert lib.tq_decode_split_workspace_size(ctypes.byref(shape), ctypes.byref(empty), ctypes.byref(empty),
+                                                  ctypes.byref(nb)) == err, (shape.n_q_heads, shape.n_kv_heads)
+        assert lib.tq_decode_attention_split(ctypes.byref(shape), None, ctypes.byref(empty), ctypes.byref(empty),
+                                             None, ctypes.c_float(1.0), None, None, 0, None) == err
