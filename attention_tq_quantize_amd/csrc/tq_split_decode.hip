@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
     // ---------------- scores: 2 tiles of 16 tokens x this lane's 2 heads ----------------
     float sv[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
     // one key part with PL planes (QJ: QJL signs); am / aq: <q', c~> and <q'', z> per tile
-    auto key_part = [&](auto PLc, auto QJc, const SmPart& P, int p) {
+    auto key_part = [&](auto PLc, auto QJc, const SmPart& P) {
       constexpr int PL = decltype(PLc)::value;
       constexpr bool QJ = decltype(QJc)::value;
       const int dq = P.d >> 3, rec = P.rec, kg0 = P.off >> 5, nks = P.d >> 5;
@@ -379,14 +379,14 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
       using T_ = std::true_type;
       using F_ = std::false_type;
       switch (P.planes * 2 + (P.qjl ? 1 : 0)) {
-        case 1: key_part(I0{}, T_{}, P, p); break;
-        case 2: key_part(I1{}, F_{}, P, p); break;
-        case 3: key_part(I1{}, T_{}, P, p); break;
-        case 4: key_part(I2{}, F_{}, P, p); break;
-        case 5: key_part(I2{}, T_{}, P, p); break;
-        case 6: key_part(I3{}, F_{}, P, p); break;
-        case 7: key_part(I3{}, T_{}, P, p); break;
-        case 8: key_part(I4{}, F_{}, P, p); break;
+        case 1: key_part(I0{}, T_{}, P); break;
+        case 2: key_part(I1{}, F_{}, P); break;
+        case 3: key_part(I1{}, T_{}, P); break;
+        case 4: key_part(I2{}, F_{}, P); break;
+        case 5: key_part(I2{}, T_{}, P); break;
+        case 6: key_part(I3{}, F_{}, P); break;
+        case 7: key_part(I3{}, T_{}, P); break;
+        case 8: key_part(I4{}, F_{}, P); break;
         default: break;
       }
     }
