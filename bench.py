@@ -266,12 +266,13 @@ def decode_1m(tq, syn, torch, dev, reps=20):
             "gb_s": round(nbytes / (avg * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def outlier_split_decode(tq, syn, torch, dev, reps=10):
+def outlier_split_decode(tq, syn, torch, dev, reps=10, bits=(3, 2)):
     """Decode attention over an outlier-split cache at the 128K batch shape (B=8,
     64/8 heads, d=128, ctx 131072): keys TurboQuant_prod with the 32 largest-RMS
-    channels at 3 bits and the other 96 at 2, values TurboQuant_mse with the same
-    bit split (96 B per (token, KV head) against 108 B for the uniform 3-bit cache);
-    tq_decode_attention_split (matrix-core split kernels)."""
+    channels at bits[0] and the other 96 at bits[1], values TurboQuant_mse with the
+    same bit split (3 + 2 bits: 96 B per (token, KV head) against 108 B for the
+    uniform 3-bit cache; 4 + 3 bits: 128 B); tq_decode_attention_split (matrix-core
+    split kernels)."""
     B, Hq, Hkv, d, T = 8, 64, 8, 128, 131072
     sides = []
     for tensor, var in ((syn.T_K, "prod"), (syn.T_V, "mse")):
@@ -280,11 +281,11 @@ def outlier_split_decode(tq, syn, torch, dev, reps=10):
         sample = syn.kv_vectors_device(Hkv, 4096, d, syn.CFG_DECODE_128K, tensor, dev, seed_offset=0)
         order = torch.argsort(sample[0].float().pow(2).mean(dim=0), descending=True, stable=True).cpu().numpy()
         chans_p = [order[:32], order[32:]]
-        for p, bits in enumerate((3, 2)):
+        for p, pbits in enumerate(bits):
             dp = len(chans_p[p])
             for g in range(Hkv):
                 S = syn.gaussian_matrix(dp, syn.CFG_DECODE_128K, tensor, 300 + 10 * p + g) if var == "prod" else None
-                qs_p[p].append(tq.Quantizer(dp, bits, var, syn.rotation(dp, syn.CFG_DECODE_128K, tensor, 300 + 10 * p + g), S))
+                qs_p[p].append(tq.Quantizer(dp, pbits, var, syn.rotation(dp, syn.CFG_DECODE_128K, tensor, 300 + 10 * p + g), S))
         recs = []
         for p in range(2):
             q0 = qs_p[p][0]
@@ -319,17 +320,22 @@ def outlier_split_decode(tq, syn, torch, dev, reps=10):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    nbytes = B * Hkv * T * 96
-    return {"workload": "split decode B=8, 64/8 heads, d=128, ctx 131072; K prod 32 ch x 3 b + 96 ch x 2 b, "
-                        "V mse 32 ch x 3 b + 96 ch x 2 b", "bytes_per_token_head": 96, "ms": round(ms, 3),
+    # record bytes per (token, KV head): codes and norms of every part, plus signs and residual norms of the keys
+    per = (sum(qs[0].code_bytes + 4 + qs[0].d // 8 + 4 for qs, _, _ in k.parts)
+           + sum(qs[0].code_bytes + 4 for qs, _, _ in v.parts))
+    nbytes = B * Hkv * T * per
+    split = f"32 ch x {bits[0]} b + 96 ch x {bits[1]} b"
+    return {"workload": f"split decode B=8, 64/8 heads, d=128, ctx 131072; K prod {split}, V mse {split}",
+            "bytes_per_token_head": per, "ms": round(ms, 3),
             "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def outlier_split(tq, syn, torch, dev, w):
+def outlier_split(tq, syn, torch, dev, w, bits=(3, 2)):
     """Outlier-channel mixed precision on the layer's KV (8 heads x 32768 tokens,
-    d = 128): per head, the 32 channels of largest RMS at 3 bits and the other 96
-    at 2 bits (2.25 bits per channel), keys TurboQuant_prod, values TurboQuant_mse,
-    through tq_quantize_split (two parts per call, one call per head and tensor)."""
+    d = 128): per head, the 32 channels of largest RMS at bits[0] and the other 96
+    at bits[1] (3 + 2: 2.25 bits per channel; 4 + 3: 3.25), keys TurboQuant_prod,
+    values TurboQuant_mse, through tq_quantize_split (two parts per call, one call
+    per head and tensor)."""
     H, T2, d = w["H"], w["T2"], w["d"]
     calls = []
     for t, xs, var in ((syn.T_K, w["xk2"], "prod"), (syn.T_V, w["xv2"], "mse")):
@@ -339,10 +345,10 @@ def outlier_split(tq, syn, torch, dev, w):
             order = torch.argsort(rms, descending=True, stable=True).cpu().numpy()
             chans = [order[:32], order[32:]]
             qs = []
-            for i, (c, bits) in enumerate(zip(chans, (3, 2))):
+            for i, (c, pbits) in enumerate(zip(chans, bits)):
                 dp = len(c)
                 S = syn.gaussian_matrix(dp, syn.CFG_LAYER_QUANT, t, 100 + 2 * h + i) if var == "prod" else None
-                qs.append(tq.Quantizer(dp, bits, var, syn.rotation(dp, syn.CFG_LAYER_QUANT, t, 100 + 2 * h + i), S))
+                qs.append(tq.Quantizer(dp, pbits, var, syn.rotation(dp, syn.CFG_LAYER_QUANT, t, 100 + 2 * h + i), S))
             calls.append((qs, chans, x))
     run = lambda: [tq.quantize_split(qs, chans, x) for qs, chans, x in calls]
     run()
@@ -355,7 +361,9 @@ def outlier_split(tq, syn, torch, dev, w):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / 3
     nvec = 2 * H * T2
-    return {"split": "32 ch x 3 b + 96 ch x 2 b (2.25 bits/channel), keys prod, values mse", "vectors": nvec,
+    per_ch = (32 * bits[0] + 96 * bits[1]) / 128
+    return {"split": f"32 ch x {bits[0]} b + 96 ch x {bits[1]} b ({per_ch} bits/channel), keys prod, values mse",
+            "vectors": nvec,
             "ms": round(ms, 3), "mvec_s": round(nvec / (ms * 1e-3) / 1e6, 1),
             "input_gb_s": round(nvec * d * 2 / (ms * 1e-3) / 1e9, 1)}
 
@@ -462,8 +470,10 @@ def main():
 
     vsearch = vector_search(tq, syn, torch, dev)
     split = outlier_split(tq, syn, torch, dev, w)
+    split_35 = outlier_split(tq, syn, torch, dev, w, bits=(4, 3))
     dec1m = decode_1m(tq, syn, torch, dev)
     split_dec = outlier_split_decode(tq, syn, torch, dev)
+    split_dec_35 = outlier_split_decode(tq, syn, torch, dev, bits=(4, 3))
 
     traffic = decode_traffic(args.traffic)
     d_gbs = d_bytes / (d_avg * 1e-3) / 1e9
@@ -498,6 +508,8 @@ def main():
             "outlier_split": split,
             "decode_1m": dec1m,
             "outlier_split_decode": split_dec,
+            "outlier_split_3_5": split_35,
+            "outlier_split_decode_3_5": split_dec_35,
             "wall_s_timed_region": round(wall, 3),
         },
         "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

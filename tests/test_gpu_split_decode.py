@@ -89,6 +89,9 @@ CASES = [
      [(64, "prod", 3), (32, "mse", 2)], [(32, "mse", 4), (64, "mse", 2)]),
     ("gqa1_d64", 3, 4, 4, 64, 40, [40, 1, 17],
      [(32, "mse", 2), (32, "prod", 2)], [(32, "mse", 3), (32, "mse", 1)]),
+    # the 3.5-bit setting: 32 channels at 4 bits and 96 at 3 (prod keys, mse values)
+    ("pages_32x4_96x3_gqa8", 2, 16, 2, 128, 257, [257, 100],
+     [(32, "prod", 4), (96, "prod", 3)], [(32, "mse", 4), (96, "mse", 3)]),
     # every plane count of the key parts (prod b=1 is signs only, mse b=1 is one
     # plane, prod b=4 has three planes and signs), four parts per side
     ("all_key_plane_counts", 2, 8, 2, 128, 150, [150, 61],
