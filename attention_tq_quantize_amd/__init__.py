@@ -131,6 +131,80 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocations of a call happen on the stream its kernels run on, so the caching
+    allocator never hands their memory to other work while the kernels still run."""
+    import contextlib
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _float_dtype(x, what: str) -> int:
+    """TQ_F32 / TQ_BF16 for a float32 / bfloat16 tensor; anything else is refused
+    (the kernels would read the buffer with the wrong element size)."""
+    import torch
+    if x.dtype == torch.bfloat16:
+        return TQ_BF16
+    if x.dtype == torch.float32:
+        return TQ_F32
+    raise TypeError(f"{what} must be float32 or bfloat16, got {x.dtype}")
+
+
+def _need_dtype(t, dtype, what: str):
+    if t is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+
+
+def _need_cuda(t, what: str):
+    if t is not None and not t.is_cuda:
+        raise ValueError(f"{what} must be a CUDA tensor")
+
+
+def _need_bytes(t, nbytes: int, what: str):
+    """The kernels index cache arrays by (group, token) with max_ctx as the token
+    stride: the buffer must hold that many bytes, contiguously."""
+    if t is None:
+        raise ValueError(f"{what} is required")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what} holds {have} bytes, the cache shape needs {nbytes}")
+
+
+def _check_decode_args(q, ctx_lens, B, Hkv, d, T, kcache, vcache):
+    """Dtype, device and extent checks of a decode call, before any launch."""
+    import torch
+    _need_dtype(q, torch.bfloat16, "q")
+    _need_dtype(ctx_lens, torch.int32, "ctx_lens")
+    if tuple(ctx_lens.shape) != (B,):
+        raise ValueError(f"ctx_lens must have shape ({B},), got {tuple(ctx_lens.shape)}")
+    if T % 32:
+        raise ValueError("max_ctx must be a multiple of 32")
+    if len(vcache.qz) != Hkv:
+        raise ValueError("keys and values need one quantizer per KV head each")
+    kq, vq = kcache.qz[0], vcache.qz[0]
+    if kq.d != d or vq.d != d:
+        raise ValueError("quantizer head dimension differs from q's")
+    G = B * Hkv
+    for name, t in (("k.norms", kcache.norms), ("v.norms", vcache.norms), ("k.rnorms", kcache.rnorms)):
+        if t is not None:
+            _need_dtype(t, torch.float32, name)
+    for name, t in (("k.codes", kcache.codes), ("k.signs", kcache.signs), ("v.codes", vcache.codes)):
+        if t is not None:
+            _need_dtype(t, torch.uint8, name)
+    _need_bytes(kcache.norms, G * T * 4, "k.norms")
+    _need_bytes(vcache.norms, G * T * 4, "v.norms")
+    if kq.planes > 0:
+        _need_bytes(kcache.codes, G * T * kq.code_bytes, "k.codes")
+    if kq.variant == "prod":
+        _need_bytes(kcache.signs, G * T * (d // 8), "k.signs")
+        _need_bytes(kcache.rnorms, G * T * 4, "k.rnorms")
+    _need_bytes(vcache.codes, G * T * vq.code_bytes, "v.codes")
+    _need_cuda(q, "q")
+    _need_cuda(ctx_lens, "ctx_lens")
+
+
 # ----------------------------------------------------------------------------------------
 def codebook_build(d: int, bits: int):
     """Lloyd-Max codebook for one rotated coordinate: (centroids, thresholds, cost C(f_X, b))."""
@@ -196,22 +270,8 @@ def _handles(qs: Sequence[Quantizer]):
     return arr
 
 
-def quantize(qs: Sequence[Quantizer], x, layout: str = "vector", rot_dbg: bool = False,
-             proj_dbg: bool = False, out: Optional[dict] = None, stream=None) -> dict:
-    """Grouped quantize: x is [G, n, d] (float32 or bfloat16 torch CUDA tensor), group g uses qs[g]."""
+def _alloc_quantize_out(o, q0, G, n, dev, rot_dbg, proj_dbg):
     import torch
-    lib = load()
-    q0 = qs[0]
-    G = len(qs)
-    assert x.dim() == 3 and x.shape[0] == G and x.shape[2] == q0.d, "x must be [n_groups, n, d]"
-    x = x.contiguous()
-    n = x.shape[1]
-    dev = x.device
-    lay = TQ_LAYOUT_BLOCK32 if layout == "block32" else TQ_LAYOUT_VECTOR
-    dt = TQ_BF16 if x.dtype == torch.bfloat16 else TQ_F32
-    if dt == TQ_F32 and x.dtype != torch.float32:
-        raise TypeError("x must be float32 or bfloat16")
-    o = out if out is not None else {}
     if "norms" not in o:
         o["norms"] = torch.empty((G, n), dtype=torch.float32, device=dev)
         if q0.planes > 0:
@@ -223,6 +283,28 @@ def quantize(qs: Sequence[Quantizer], x, layout: str = "vector", rot_dbg: bool =
         o["rot"] = torch.empty((G, n, q0.d), dtype=torch.float32, device=dev)
     if proj_dbg and "proj" not in o:
         o["proj"] = torch.empty((G, n, q0.d), dtype=torch.float32, device=dev)
+
+
+def quantize(qs: Sequence[Quantizer], x, layout: str = "vector", rot_dbg: bool = False,
+             proj_dbg: bool = False, out: Optional[dict] = None, stream=None) -> dict:
+    """Grouped quantize: x is [G, n, d] (float32 or bfloat16 torch CUDA tensor), group g uses qs[g]."""
+    import torch
+    lib = load()
+    q0 = qs[0]
+    G = len(qs)
+    _float_dtype(x, "x")
+    if not (x.dim() == 3 and x.shape[0] == G and x.shape[2] == q0.d):
+        raise ValueError("x must be [n_groups, n, d]")
+    _need_cuda(x, "x")
+    with _on(stream):
+        x = x.contiguous()
+    n = x.shape[1]
+    dev = x.device
+    lay = TQ_LAYOUT_BLOCK32 if layout == "block32" else TQ_LAYOUT_VECTOR
+    dt = _float_dtype(x, "x")
+    o = out if out is not None else {}
+    with _on(stream):
+        _alloc_quantize_out(o, q0, G, n, dev, rot_dbg, proj_dbg)
     hs = _handles(qs)
     _check(lib.tq_quantize(hs, G, n, _ptr(x), dt, lay, _ptr(o.get("codes")), _ptr(o.get("signs")),
                            _ptr(o["norms"]), _ptr(o.get("rnorms")), _ptr(o.get("rot")), _ptr(o.get("proj")),
@@ -238,16 +320,25 @@ def _rows(x):
     return x, x.shape[-1]
 
 
+def _check_rows(q: Quantizer, x):
+    dt = _float_dtype(x, "x")
+    if x.dim() != 2 or x.shape[-1] != q.d:
+        raise ValueError(f"x must be [n, {q.d}], got {tuple(x.shape)}")
+    _need_cuda(x, "x")
+    return dt
+
+
 def quantize_mse(q: Quantizer, x, rot_dbg: bool = False, stream=None) -> dict:
     import torch
     lib = load()
+    dt = _check_rows(q, x)
     n = x.shape[0]
-    x, stride = _rows(x)
-    dt = TQ_BF16 if x.dtype == torch.bfloat16 else TQ_F32
-    o = {"codes": torch.empty((n, q.code_bytes), dtype=torch.uint8, device=x.device),
-         "norms": torch.empty(n, dtype=torch.float32, device=x.device)}
-    if rot_dbg:
-        o["rot"] = torch.empty((n, q.d), dtype=torch.float32, device=x.device)
+    with _on(stream):
+        x, stride = _rows(x)
+        o = {"codes": torch.empty((n, q.code_bytes), dtype=torch.uint8, device=x.device),
+             "norms": torch.empty(n, dtype=torch.float32, device=x.device)}
+        if rot_dbg:
+            o["rot"] = torch.empty((n, q.d), dtype=torch.float32, device=x.device)
     _check(lib.tq_quantize_mse(q.handle, _ptr(x), dt, n, stride, _ptr(o["codes"]), _ptr(o["norms"]),
                                _ptr(o.get("rot")), _stream(stream)), "tq_quantize_mse")
     return o
@@ -256,18 +347,19 @@ def quantize_mse(q: Quantizer, x, rot_dbg: bool = False, stream=None) -> dict:
 def quantize_prod(q: Quantizer, x, rot_dbg: bool = False, proj_dbg: bool = False, stream=None) -> dict:
     import torch
     lib = load()
+    dt = _check_rows(q, x)
     n = x.shape[0]
-    x, stride = _rows(x)
-    dt = TQ_BF16 if x.dtype == torch.bfloat16 else TQ_F32
     dev = x.device
-    o = {"codes": torch.empty((n, max(q.code_bytes, 1)), dtype=torch.uint8, device=dev),
-         "signs": torch.empty((n, q.d // 8), dtype=torch.uint8, device=dev),
-         "norms": torch.empty(n, dtype=torch.float32, device=dev),
-         "rnorms": torch.empty(n, dtype=torch.float32, device=dev)}
-    if rot_dbg:
-        o["rot"] = torch.empty((n, q.d), dtype=torch.float32, device=dev)
-    if proj_dbg:
-        o["proj"] = torch.empty((n, q.d), dtype=torch.float32, device=dev)
+    with _on(stream):
+        x, stride = _rows(x)
+        o = {"codes": torch.empty((n, max(q.code_bytes, 1)), dtype=torch.uint8, device=dev),
+             "signs": torch.empty((n, q.d // 8), dtype=torch.uint8, device=dev),
+             "norms": torch.empty(n, dtype=torch.float32, device=dev),
+             "rnorms": torch.empty(n, dtype=torch.float32, device=dev)}
+        if rot_dbg:
+            o["rot"] = torch.empty((n, q.d), dtype=torch.float32, device=dev)
+        if proj_dbg:
+            o["proj"] = torch.empty((n, q.d), dtype=torch.float32, device=dev)
     _check(lib.tq_quantize_prod(q.handle, _ptr(x), dt, n, stride, _ptr(o["codes"]) if q.planes else None,
                                 _ptr(o["signs"]), _ptr(o["norms"]), _ptr(o["rnorms"]), _ptr(o.get("rot")),
                                 _ptr(o.get("proj")), _stream(stream)), "tq_quantize_prod")
@@ -277,8 +369,13 @@ def quantize_prod(q: Quantizer, x, rot_dbg: bool = False, proj_dbg: bool = False
 def dequantize(q: Quantizer, codes, norms, signs=None, rnorms=None, layout: str = "vector", stream=None):
     import torch
     lib = load()
+    _need_dtype(norms, torch.float32, "norms")
+    _need_dtype(rnorms, torch.float32, "rnorms")
+    _need_dtype(codes, torch.uint8, "codes")
+    _need_dtype(signs, torch.uint8, "signs")
     n = norms.numel()
-    out = torch.empty((n, q.d), dtype=torch.float32, device=norms.device)
+    with _on(stream):
+        out = torch.empty((n, q.d), dtype=torch.float32, device=norms.device)
     lay = TQ_LAYOUT_BLOCK32 if layout == "block32" else TQ_LAYOUT_VECTOR
     _check(lib.tq_dequantize(q.handle, lay, _ptr(codes) if q.planes else None, _ptr(signs), _ptr(norms),
                              _ptr(rnorms), n, _ptr(out), _stream(stream)), "tq_dequantize")
@@ -288,9 +385,15 @@ def dequantize(q: Quantizer, codes, norms, signs=None, rnorms=None, layout: str 
 def inner_products(q: Quantizer, y, codes, norms, signs=None, rnorms=None, stream=None):
     import torch
     lib = load()
+    _need_dtype(y, torch.float32, "y")
+    if y.dim() != 2 or y.shape[1] != q.d:
+        raise ValueError(f"y must be [m, {q.d}]")
+    _need_dtype(norms, torch.float32, "norms")
     m, n = y.shape[0], norms.numel()
-    out = torch.empty((m, n), dtype=torch.float32, device=y.device)
-    _check(lib.tq_inner_products(q.handle, _ptr(y.contiguous()), m, _ptr(codes) if q.planes else None,
+    with _on(stream):
+        y = y.contiguous()
+        out = torch.empty((m, n), dtype=torch.float32, device=y.device)
+    _check(lib.tq_inner_products(q.handle, _ptr(y), m, _ptr(codes) if q.planes else None,
                                  _ptr(signs), _ptr(norms), _ptr(rnorms), n, _ptr(out), _stream(stream)),
            "tq_inner_products")
     return out
@@ -318,23 +421,27 @@ def quantize_split(qs: Sequence[Quantizer], channels, x, rot_dbg: bool = False, 
     x: [n, dim] float32 or bfloat16 CUDA tensor; returns one record dict per part."""
     import torch
     lib = load()
-    x = x.contiguous()
+    dt = _float_dtype(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [n, dim]")
+    _need_cuda(x, "x")
     n, dim = x.shape
-    dt = TQ_BF16 if x.dtype == torch.bfloat16 else TQ_F32
     ch = _split_args(qs, channels)
     outs = []
-    for q in qs:
-        o = {"norms": torch.empty(n, dtype=torch.float32, device=x.device)}
-        if q.planes > 0:
-            o["codes"] = torch.empty((n, q.code_bytes), dtype=torch.uint8, device=x.device)
-        if q.variant == "prod":
-            o["signs"] = torch.empty((n, q.d // 8), dtype=torch.uint8, device=x.device)
-            o["rnorms"] = torch.empty(n, dtype=torch.float32, device=x.device)
-            if proj_dbg:
-                o["proj"] = torch.empty((n, q.d), dtype=torch.float32, device=x.device)
-        if rot_dbg:
-            o["rot"] = torch.empty((n, q.d), dtype=torch.float32, device=x.device)
-        outs.append(o)
+    with _on(stream):
+        x = x.contiguous()
+        for q in qs:
+            o = {"norms": torch.empty(n, dtype=torch.float32, device=x.device)}
+            if q.planes > 0:
+                o["codes"] = torch.empty((n, q.code_bytes), dtype=torch.uint8, device=x.device)
+            if q.variant == "prod":
+                o["signs"] = torch.empty((n, q.d // 8), dtype=torch.uint8, device=x.device)
+                o["rnorms"] = torch.empty(n, dtype=torch.float32, device=x.device)
+                if proj_dbg:
+                    o["proj"] = torch.empty((n, q.d), dtype=torch.float32, device=x.device)
+            if rot_dbg:
+                o["rot"] = torch.empty((n, q.d), dtype=torch.float32, device=x.device)
+            outs.append(o)
     _check(lib.tq_quantize_split(_handles(qs), len(qs), ch.ctypes.data, dim, _ptr(x), dt, n, _records(outs),
                                  _stream(stream)), "tq_quantize_split")
     return outs
@@ -344,11 +451,13 @@ def inner_products_split(qs: Sequence[Quantizer], channels, y, recs, stream=None
     """sum over parts of <y restricted to part p, x~_p> (tq_inner_products_split); y: [m, dim] float32."""
     import torch
     lib = load()
-    y = y.contiguous()
+    _need_dtype(y, torch.float32, "y")
     m, dim = y.shape
     n = recs[0]["norms"].numel()
     ch = _split_args(qs, channels)
-    out = torch.empty((m, n), dtype=torch.float32, device=y.device)
+    with _on(stream):
+        y = y.contiguous()
+        out = torch.empty((m, n), dtype=torch.float32, device=y.device)
     _check(lib.tq_inner_products_split(_handles(qs), len(qs), ch.ctypes.data, dim, _ptr(y), m, _records(recs), n,
                                        _ptr(out), _stream(stream)), "tq_inner_products_split")
     return out
@@ -366,11 +475,16 @@ def search_scores(q: Quantizer, y, codes, norms, signs=None, rnorms=None, worksp
     tensor of at least search_workspace_size(q, m) bytes (allocated when None)."""
     import torch
     lib = load()
+    _need_dtype(y, torch.float32, "y")
+    if y.dim() != 2 or y.shape[1] != q.d:
+        raise ValueError(f"y must be [m, {q.d}]")
     m, n = y.shape[0], norms.numel()
-    out = torch.empty((m, n), dtype=torch.float32, device=y.device)
-    if workspace is None:
-        workspace = torch.empty(max(search_workspace_size(q, m), 1), dtype=torch.uint8, device=y.device)
-    _check(lib.tq_search_scores(q.handle, _ptr(y.contiguous()), m, _ptr(codes) if q.planes else None,
+    with _on(stream):
+        y = y.contiguous()
+        out = torch.empty((m, n), dtype=torch.float32, device=y.device)
+        if workspace is None:
+            workspace = torch.empty(max(search_workspace_size(q, m), 1), dtype=torch.uint8, device=y.device)
+    _check(lib.tq_search_scores(q.handle, _ptr(y), m, _ptr(codes) if q.planes else None,
                                 _ptr(signs), _ptr(norms), _ptr(rnorms), n, _ptr(out), _ptr(workspace),
                                 workspace.numel(), _stream(stream)), "tq_search_scores")
     return out
@@ -413,15 +527,21 @@ def decode_attention(q, kcache: KVCache, vcache: KVCache, ctx_lens, scale: Optio
     T = int(max_ctx if max_ctx is not None else kcache.norms.shape[-1])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _check_decode_args(q, ctx_lens, B, Hkv, d, T, kcache, vcache)
+    if scores is not None:
+        _need_dtype(scores, torch.float32, "scores")
+        _need_bytes(scores, B * Hq * T * 4, "scores")
     shape = AttnShape(B, Hq, Hkv, d, T)
     kp, ka = kcache.packed()
     vp, va = vcache.packed()
-    if workspace is None:
-        nbytes = decode_workspace_size(B, Hq, Hkv, d, T, kcache, vcache)
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
-    _check(lib.tq_decode_attention(ctypes.byref(shape), _ptr(q.contiguous()), ctypes.byref(kp), ctypes.byref(vp),
+    with _on(stream):
+        q = q.contiguous()
+        if workspace is None:
+            nbytes = decode_workspace_size(B, Hq, Hkv, d, T, kcache, vcache)
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check(lib.tq_decode_attention(ctypes.byref(shape), _ptr(q), ctypes.byref(kp), ctypes.byref(vp),
                                    _ptr(ctx_lens), float(scale), _ptr(out), _ptr(scores), _ptr(workspace),
                                    workspace.numel(), _stream(stream)), "tq_decode_attention")
     return out
@@ -470,15 +590,30 @@ def decode_attention_split(q, k: SplitKV, v: SplitKV, ctx_lens, scale: Optional[
     T = int(max_ctx if max_ctx is not None else k.parts[0][2]["norms"].shape[-1])
     if scale is None:
         scale = 1.0 / math.sqrt(dim)
+    _need_dtype(q, torch.bfloat16, "q")
+    _need_dtype(ctx_lens, torch.int32, "ctx_lens")
+    if tuple(ctx_lens.shape) != (B,):
+        raise ValueError(f"ctx_lens must have shape ({B},)")
+    G = B * Hkv
+    for side, name in ((k, "k"), (v, "v")):
+        for p, (qs, _, r) in enumerate(side.parts):
+            _need_bytes(r["norms"], G * T * 4, f"{name}.part{p}.norms")
+            if qs[0].planes > 0:
+                _need_bytes(r["codes"], G * T * qs[0].code_bytes, f"{name}.part{p}.codes")
+            if qs[0].variant == "prod":
+                _need_bytes(r["signs"], G * T * (qs[0].d // 8), f"{name}.part{p}.signs")
+                _need_bytes(r["rnorms"], G * T * 4, f"{name}.part{p}.rnorms")
     shape = AttnShape(B, Hq, Hkv, dim, T)
     kc, ka = k.packed(Hkv)
     vc, va = v.packed(Hkv)
-    if workspace is None:
-        workspace = torch.empty(max(decode_split_workspace_size(B, Hq, Hkv, dim, T, k, v), 1), dtype=torch.uint8,
-                                device=q.device)
-    if out is None:
-        out = torch.empty((B, Hq, dim), dtype=torch.float32, device=q.device)
-    _check(lib.tq_decode_attention_split(ctypes.byref(shape), _ptr(q.contiguous()), ctypes.byref(kc),
+    with _on(stream):
+        q = q.contiguous()
+        if workspace is None:
+            workspace = torch.empty(max(decode_split_workspace_size(B, Hq, Hkv, dim, T, k, v), 1),
+                                    dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty((B, Hq, dim), dtype=torch.float32, device=q.device)
+    _check(lib.tq_decode_attention_split(ctypes.byref(shape), _ptr(q), ctypes.byref(kc),
                                          ctypes.byref(vc), _ptr(ctx_lens), float(scale), _ptr(out),
                                          _ptr(workspace), workspace.numel(), _stream(stream)),
            "tq_decode_attention_split")
@@ -509,20 +644,24 @@ def decode_append_attention(q, k_new, v_new, kcache: KVCache, vcache: KVCache, c
     T = int(max_ctx if max_ctx is not None else kcache.norms.shape[-1])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    assert tuple(k_new.shape) == (B, Hkv, d) and tuple(v_new.shape) == (B, Hkv, d)
+    if tuple(k_new.shape) != (B, Hkv, d) or tuple(v_new.shape) != (B, Hkv, d):
+        raise ValueError(f"k_new and v_new must be [{B}, {Hkv}, {d}]")
     if k_new.dtype != v_new.dtype or k_new.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("k_new and v_new must share a float32 or bfloat16 dtype")
     dt = TQ_BF16 if k_new.dtype == torch.bfloat16 else TQ_F32
+    _check_decode_args(q, ctx_lens, B, Hkv, d, T, kcache, vcache)
     shape = AttnShape(B, Hq, Hkv, d, T)
     kp, ka = kcache.packed()
     vp, va = vcache.packed()
-    if workspace is None:
-        nbytes = decode_append_workspace_size(B, Hq, Hkv, d, T, kcache, vcache)
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
-    _check(lib.tq_decode_append_attention(ctypes.byref(shape), _ptr(q.contiguous()), _ptr(k_new.contiguous()),
-                                          _ptr(v_new.contiguous()), dt, ctypes.byref(kp), ctypes.byref(vp),
+    with _on(stream):
+        q, k_new, v_new = q.contiguous(), k_new.contiguous(), v_new.contiguous()
+        if workspace is None:
+            nbytes = decode_append_workspace_size(B, Hq, Hkv, d, T, kcache, vcache)
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check(lib.tq_decode_append_attention(ctypes.byref(shape), _ptr(q), _ptr(k_new),
+                                          _ptr(v_new), dt, ctypes.byref(kp), ctypes.byref(vp),
                                           _ptr(ctx_lens), float(scale), _ptr(out), _ptr(workspace),
                                           workspace.numel(), _stream(stream)), "tq_decode_append_attention")
     return out

@@ -326,6 +326,7 @@ def outlier_split_decode(tq, syn, torch, dev, reps=10, bits=(3, 2)):
     nbytes = B * Hkv * T * per
     split = f"32 ch x {bits[0]} b + 96 ch x {bits[1]} b"
     return {"workload": f"split decode B=8, 64/8 heads, d=128, ctx 131072; K prod {split}, V mse {split}",
+            "bits_per_channel": (32 * bits[0] + 96 * bits[1]) / 128,
             "bytes_per_token_head": per, "ms": round(ms, 3),
             "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
@@ -508,8 +509,8 @@ def main():
             "outlier_split": split,
             "decode_1m": dec1m,
             "outlier_split_decode": split_dec,
-            "outlier_split_3_5": split_35,
-            "outlier_split_decode_3_5": split_dec_35,
+            "outlier_split_32x4_96x3": split_35,
+            "outlier_split_decode_32x4_96x3": split_dec_35,
             "wall_s_timed_region": round(wall, 3),
         },
         "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
