@@ -42,6 +42,9 @@ def parse():
                     help="counter summary with the measured HBM bytes per decode launch (default: profiles/)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device to device 3 times (scale reference for HBM byte counters)")
+    ap.add_argument("--only", choices=["quantize", "decode"], default=None,
+                    help="profiling runs: build the headline workload, then run only this stage "
+                         "warmup + steps times and print its mean time (no JSON line)")
     return ap.parse_args()
 
 
@@ -400,6 +403,21 @@ def main():
     def decode():
         tq.decode_attention(w["q"], w["kcache"], w["vcache"], w["lens"], 1 / math.sqrt(w["d"]), max_ctx=w["T3"],
                             out=w["out"], workspace=w["ws"])
+
+    if args.only:
+        stage = quantize_layer if args.only == "quantize" else decode
+        for _ in range(args.warmup):
+            stage()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            stage()
+        e1.record()
+        torch.cuda.synchronize()
+        print(f"{args.only}: {e0.elapsed_time(e1) / max(args.steps, 1):.4f} ms per call over {args.steps} calls",
+              flush=True)
+        return 0
 
     for _ in range(args.warmup):
         quantize_layer()
