@@ -54,6 +54,10 @@ class Records(ctypes.Structure):
                 ("rnorms", ctypes.c_void_p), ("rot_dbg", ctypes.c_void_p), ("proj_dbg", ctypes.c_void_p)]
 
 
+class AppendDebug(ctypes.Structure):
+    _fields_ = [("rot", ctypes.c_void_p), ("proj", ctypes.c_void_p)]
+
+
 class SplitCache(ctypes.Structure):
     _fields_ = [("n_parts", ctypes.c_int), ("qz", ctypes.POINTER(ctypes.c_void_p)),
                 ("channels", ctypes.c_void_p), ("rec", ctypes.c_void_p)]
@@ -105,7 +109,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                                     ctypes.POINTER(PackedKV), ctypes.POINTER(ctypes.c_size_t)]
     lib.tq_decode_append_attention.argtypes = [ctypes.POINTER(AttnShape), _VP, _VP, _VP, _I,
                                                ctypes.POINTER(PackedKV), ctypes.POINTER(PackedKV), _VP, _F, _VP,
-                                               _VP, ctypes.c_size_t, _VP]
+                                               ctypes.POINTER(AppendDebug), _VP, ctypes.c_size_t, _VP]
     for name in EXPORTS:
         if name not in ("tq_status_string", "tq_last_error_message", "tq_version"):
             getattr(lib, name).restype = _I
@@ -634,9 +638,11 @@ def decode_append_workspace_size(batch, n_q_heads, n_kv_heads, d, max_ctx, kcach
 
 def decode_append_attention(q, k_new, v_new, kcache: KVCache, vcache: KVCache, ctx_lens,
                             scale: Optional[float] = None, max_ctx: Optional[int] = None, out=None,
-                            workspace=None, stream=None):
+                            workspace=None, stream=None, rot_dbg=None, proj_dbg=None):
     """Quantize k_new / v_new ([B, Hkv, d], float32 or bfloat16) into the caches at
-    token ctx_lens[b], then attend ctx_lens[b] + 1 tokens. ctx_lens is not advanced."""
+    token ctx_lens[b], then attend ctx_lens[b] + 1 tokens. ctx_lens is not advanced.
+    rot_dbg (float32 [B, Hkv, 2, d]) / proj_dbg (float32 [B, Hkv, d]), when given,
+    receive the rotated unit vectors of the new key and value and the key's S r."""
     import torch
     lib = load()
     B, Hq, d = q.shape
@@ -660,8 +666,15 @@ def decode_append_attention(q, k_new, v_new, kcache: KVCache, vcache: KVCache, c
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
         if out is None:
             out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    for name, t, shp in (("rot_dbg", rot_dbg, (B, Hkv, 2, d)), ("proj_dbg", proj_dbg, (B, Hkv, d))):
+        if t is not None:
+            _need_dtype(t, torch.float32, name)
+            if tuple(t.shape) != shp or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {shp} tensor")
+    dbg = AppendDebug(_ptr(rot_dbg), _ptr(proj_dbg))
     _check(lib.tq_decode_append_attention(ctypes.byref(shape), _ptr(q), _ptr(k_new),
                                           _ptr(v_new), dt, ctypes.byref(kp), ctypes.byref(vp),
-                                          _ptr(ctx_lens), float(scale), _ptr(out), _ptr(workspace),
-                                          workspace.numel(), _stream(stream)), "tq_decode_append_attention")
+                                          _ptr(ctx_lens), float(scale), _ptr(out), ctypes.byref(dbg),
+                                          _ptr(workspace), workspace.numel(), _stream(stream)),
+           "tq_decode_append_attention")
     return out

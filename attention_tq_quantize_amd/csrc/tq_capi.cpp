@@ -106,7 +106,7 @@ const char* tq_status_string(tq_status s) {
 
 const char* tq_last_error_message(void) { return g_last_error.c_str(); }
 
-int tq_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+int tq_version(void) { return 2 * 10000 + 0 * 100 + 0; }
 
 tq_status tq_codebook_build(int d, int bits, float* centroids, float* thresholds,
                             double* cost_per_coord) {
@@ -712,11 +712,9 @@ tq_status tq_decode_attention(const tq_attn_shape* shape, const void* q, const t
   return launch_decode(p, q, k, v, ctx_lens, scale, out, scores_dbg, workspace, (hipStream_t)stream);
 }
 
-// Append workspace: the decode workspace, then the attended lengths [B]
-static size_t append_workspace(const DecodePlan& p) {
-  const size_t o = (p.total_bytes + 255) & ~(size_t)255;
-  return o + (((size_t)p.batch * sizeof(int32_t) + 255) & ~(size_t)255);
-}
+// Append workspace: the same as the plain decode's (the new records go straight
+// into the caches; the attended length is formed in the main kernel)
+static size_t append_workspace(const DecodePlan& p) { return p.total_bytes; }
 
 tq_status tq_decode_append_workspace_size(const tq_attn_shape* shape, const tq_packed_kv* k,
                                           const tq_packed_kv* v, size_t* bytes) {
@@ -731,7 +729,8 @@ tq_status tq_decode_append_workspace_size(const tq_attn_shape* shape, const tq_p
 tq_status tq_decode_append_attention(const tq_attn_shape* shape, const void* q, const void* k_new,
                                      const void* v_new, tq_dtype kv_dtype, const tq_packed_kv* k,
                                      const tq_packed_kv* v, const int32_t* ctx_lens, float scale,
-                                     float* out, void* workspace, size_t ws_bytes, void* stream) {
+                                     float* out, const tq_append_debug* dbg, void* workspace,
+                                     size_t ws_bytes, void* stream) {
   DecodePlan p;
   tq_status st = check_decode(shape, k, v, &p);
   if (st != TQ_OK) return st;
@@ -739,32 +738,17 @@ tq_status tq_decode_append_attention(const tq_attn_shape* shape, const void* q, 
   if (!k_new || !v_new) return set_error(TQ_ERR_INVALID_ARG, "decode_append: k_new or v_new is NULL");
   if (kv_dtype != TQ_F32 && kv_dtype != TQ_BF16) return set_error(TQ_ERR_INVALID_ARG, "decode_append: unknown kv_dtype");
   if (!std::isfinite(scale)) return set_error(TQ_ERR_INVALID_ARG, "decode_append: scale is not finite");
+  if (p.d > 256) return set_error(TQ_ERR_UNSUPPORTED, "decode_append: head_dim > 256");
   const size_t need = append_workspace(p);
   if (!workspace || ws_bytes < need)
     return set_error(TQ_ERR_WORKSPACE, fmt("decode_append: workspace needs %zu bytes, got %zu", need, workspace ? ws_bytes : (size_t)0));
-  hipStream_t hs = (hipStream_t)stream;
-  int32_t* lens1 = (int32_t*)((char*)workspace + ((p.total_bytes + 255) & ~(size_t)255));
   AppendLaunch a;
-  a.ctx_lens = ctx_lens;
-  a.lens_out = lens1;
-  a.batch = p.batch;
-  a.n_kv_heads = p.n_kv_heads;
-  a.d = p.d;
-  a.max_ctx = p.max_ctx;
-  a.kq = k->qz;
-  a.vq = v->qz;
   a.k_new = k_new;
   a.v_new = v_new;
   a.x_dtype = kv_dtype;
-  a.k_codes = const_cast<uint8_t*>(k->codes);
-  a.k_signs = const_cast<uint8_t*>(k->signs);
-  a.k_norms = const_cast<float*>(k->norms);
-  a.k_rnorms = const_cast<float*>(k->rnorms);
-  a.v_codes = const_cast<uint8_t*>(v->codes);
-  a.v_norms = const_cast<float*>(v->norms);
-  st = launch_append(a, hs);
-  if (st != TQ_OK) return st;
-  return launch_decode(p, q, k, v, lens1, scale, out, nullptr, workspace, hs);
+  a.rot_dbg = dbg ? dbg->rot : nullptr;
+  a.proj_dbg = dbg ? dbg->proj : nullptr;
+  return launch_decode(p, q, k, v, ctx_lens, scale, out, nullptr, workspace, (hipStream_t)stream, &a);
 }
 
 }  // extern "C"

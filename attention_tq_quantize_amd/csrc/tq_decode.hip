@@ -56,16 +56,46 @@ namespace {
 // carries 2^(ev - vslot_exp(k)), so every product is w 2^(ev - 2).
 __host__ __device__ constexpr int vslot_exp(int k) { return k - 14; }
 
+// Append of the new token (online quantization of one vector per (batch, KV
+// head) and tensor: [NIK] "Step 0" to "Step 2", prod keys also "TurboQuant
+// proper"). The vector is normalized with its norm accumulated in fp64, rotated
+// with the quantizer's fp32 Pi (prod: the residual e = y - c[idx] stays in the
+// rotated basis and is projected with S' = S Pi^T, so S r = S' e), and its
+// record is written at the sequence's current length; the value goes into its
+// slot of the 32-token block (the other slots are kept).
+struct AppendArgs {
+  const int32_t* ctx_lens;
+  int64_t max_ctx;
+  int k_planes, v_bits;
+  bool k_prod, x_bf16;
+  const void* k_new;  // [B][Hkv][d]
+  const void* v_new;
+  const float* k_pi[kMaxKvHeads];
+  const float* k_sp[kMaxKvHeads];
+  const float* v_pi[kMaxKvHeads];
+  float k_thr[15], k_cen[16];
+  float v_thr[15], v_cen[16];
+  uint32_t* k_codes;  // [B][Hkv][max_ctx][k_planes * d / 32]
+  uint32_t* k_signs;  // [B][Hkv][max_ctx][d / 32]
+  float* k_norms;
+  float* k_rnorms;
+  uint32_t* v_codes;  // [B][Hkv][max_ctx / 32][v_bits * d] words (block layout)
+  float* v_norms;
+  float* rot_dbg;   // optional [B][Hkv][2][d]: rotated unit vectors (key, value)
+  float* proj_dbg;  // optional [B][Hkv][d]: S r of the key (prod)
+};
+
 struct DecPrepParams {
   const uint16_t* q;
   const float* pk[kMaxKvHeads];
   const float* sk[kMaxKvHeads];
   u32x4* frag;
   float* consts;
-  int Hq, Hkv, group, chunk_heads, n_chunks;
+  int Hq, Hkv, group, chunk_heads, n_chunks, n_units;
   float scale_log2e;
   float kappa;
   float kcoef[kMaxWalsh];
+  AppendArgs app;  // used by the blocks past n_units (2 per (batch, KV head))
 };
 
 // K-side operand words, for lane group g: the odd Walsh combinations of the
@@ -86,131 +116,278 @@ struct KWords {
 // one value per MFMA row.
 constexpr int kConstsPerUnit = 64;
 
-// One workgroup of D threads per (batch, query head): thread j computes
-// q'_j = (Pi_K q)_j and q''_j = (S_K q)_j, then the workgroup writes this head's
-// two MFMA rows (hi, lo) of every score-operand fragment and of the constants.
-// The workgroup of the chunk's first head also zero-fills unused rows.
-template <int D, int PK, bool QJL>
-__global__ __launch_bounds__(D) void decode_prep_kernel(DecPrepParams prm) {
-  using KW = KWords<D, PK, QJL>;
-  __shared__ float qs[D], qp[D], qq[D];
-  __shared__ float red[4][D / 64];
-  const int bhq = blockIdx.x;
-  const int b = bhq / prm.Hq, hq = bhq % prm.Hq;
-  const int hkv = hq / prm.group;
-  const int in_group = hq % prm.group;
-  const int chunk = in_group / prm.chunk_heads, h = in_group % prm.chunk_heads;
-  const int bhc = (b * prm.Hkv + hkv) * prm.n_chunks + chunk;
-  const int j = threadIdx.x;
-  qs[j] = bf16_val(prm.q[(int64_t)bhq * D + j]);
+template <int NTH>
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  const float4* prow = (const float4*)(prm.pk[hkv] + (int64_t)j * D);
-  const float4* srow = QJL ? (const float4*)(prm.sk[hkv] + (int64_t)j * D) : nullptr;
-  float a0 = 0.f, a1 = 0.f, c0 = 0.f, c1 = 0.f;
-#pragma unroll 4
-  for (int k = 0; k < D / 4; k += 2) {
-    const float4 p0 = prow[k], p1 = prow[k + 1];
-    a0 += p0.x * qs[4 * k] + p0.y * qs[4 * k + 1] + p0.z * qs[4 * k + 2] + p0.w * qs[4 * k + 3];
-    a1 += p1.x * qs[4 * k + 4] + p1.y * qs[4 * k + 5] + p1.z * qs[4 * k + 6] + p1.w * qs[4 * k + 7];
-    if constexpr (QJL) {
-      const float4 s0 = srow[k], s1 = srow[k + 1];
-      c0 += s0.x * qs[4 * k] + s0.y * qs[4 * k + 1] + s0.z * qs[4 * k + 2] + s0.w * qs[4 * k + 3];
-      c1 += s1.x * qs[4 * k + 4] + s1.y * qs[4 * k + 5] + s1.z * qs[4 * k + 6] + s1.w * qs[4 * k + 7];
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < NTH / 64; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// a row of M (D floats, 16-byte aligned) dotted with v (shared memory); groups
+// of up to 16 float4 loads in flight
+template <int D>
+__device__ __forceinline__ float row_dot(const float* __restrict__ row, const float* v) {
+  constexpr int G = D < 64 ? D / 4 : 16;
+  const float4* r4 = (const float4*)row;
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int j0 = 0; j0 < D / 4; j0 += G) {
+    float4 m[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) m[j] = r4[j0 + j];
+#pragma unroll
+    for (int j = 0; j < G; j += 2) {
+      const int c = 4 * (j0 + j);
+      a0 = fmaf(m[j].x, v[c], fmaf(m[j].y, v[c + 1], fmaf(m[j].z, v[c + 2], fmaf(m[j].w, v[c + 3], a0))));
+      a1 = fmaf(m[j + 1].x, v[c + 4], fmaf(m[j + 1].y, v[c + 5], fmaf(m[j + 1].z, v[c + 6], fmaf(m[j + 1].w, v[c + 7], a1))));
     }
   }
-  const float vp = a0 + a1, vq = c0 + c1;
-  qp[j] = vp;
-  qq[j] = vq;
-  // per-head sums and maxima (wave reductions, then across the D/64 waves)
-  float s_p = vp, s_q = vq, m_p = fabsf(vp), m_q = fabsf(vq);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    s_p += __shfl_xor(s_p, o);
-    s_q += __shfl_xor(s_q, o);
-    m_p = fmaxf(m_p, __shfl_xor(m_p, o));
-    m_q = fmaxf(m_q, __shfl_xor(m_q, o));
+  return a0 + a1;
+}
+
+// The append role: one block per (batch, kv head, tensor); thread t < D owns coordinate t.
+template <int D, int NTH>
+__device__ void append_one(const AppendArgs& p, int grp, bool value, int Hkv) {
+  __shared__ float sx[D], se[D], sp[D];
+  __shared__ int sidx[D];
+  __shared__ double red[NTH / 64];
+  const int t = threadIdx.x;
+  const int b = grp / Hkv, h = grp % Hkv;
+  int64_t len = p.ctx_lens[b];
+  len = len < 0 ? 0 : len;
+  if (len >= p.max_ctx) return;  // block-uniform: a full cache is not appended
+  const int64_t slot = (int64_t)grp * p.max_ctx + len;
+  const void* src = (const char*)(value ? p.v_new : p.k_new) + (size_t)grp * D * (p.x_bf16 ? 2 : 4);
+  const float* pi = value ? p.v_pi[h] : p.k_pi[h];
+  const float* spm = (!value && p.k_prod) ? p.k_sp[h] : nullptr;
+  const int planes = value ? p.v_bits : p.k_planes;
+  const float* thr = value ? p.v_thr : p.k_thr;
+  const float* cen = value ? p.v_cen : p.k_cen;
+  float xv = 0.f;
+  if (t < D) xv = p.x_bf16 ? bf16_val(((const uint16_t*)src)[t]) : ((const float*)src)[t];
+  const double nu = sqrt(block_sum_f64<NTH>(t < D ? (double)xv * (double)xv : 0.0, red));
+  const float nu32 = (float)nu;
+  const bool zero = !(nu > 0.0);
+  if (t < D) sx[t] = zero ? 0.f : (float)((double)xv / nu);
+  __syncthreads();
+  float e = 0.f;
+  if (t < D) {
+    const float y = row_dot<D>(pi + (int64_t)t * D, sx);
+    const int K = 1 << planes;
+    int i = 0;
+    for (int k = 0; k + 1 < K; ++k) i += y > thr[k] ? 1 : 0;
+    if (zero) i = 0;
+    sidx[t] = i;
+    e = zero ? 0.f : y - cen[i];
+    se[t] = e;
+    if (p.rot_dbg) p.rot_dbg[((int64_t)grp * 2 + (value ? 1 : 0)) * D + t] = y;
   }
-  if ((j & 63) == 0) {
-    red[0][j / 64] = s_p;
-    red[1][j / 64] = s_q;
-    red[2][j / 64] = m_p;
-    red[3][j / 64] = m_q;
+  float gamma = 0.f;
+  if (spm) {
+    gamma = (float)sqrt(block_sum_f64<NTH>((double)e * (double)e, red));  // also publishes se
+    if (t < D) {
+      const float pr = row_dot<D>(spm + (int64_t)t * D, se);
+      sp[t] = zero ? -1.f : pr;  // zero vector: sign bits 0
+      if (p.proj_dbg) p.proj_dbg[(int64_t)grp * D + t] = pr;
+    }
   }
   __syncthreads();
-  float sum_p = 0.f, sum_q = 0.f, max_p = 0.f, max_q = 0.f;
+  if (!value) {
+    constexpr int wpp = D / 32;  // 32-bit words per plane of a record
+    if (t < p.k_planes * wpp) {
+      const int pl = t / wpp, w = t % wpp;
+      unsigned bits = 0u;
 #pragma unroll
-  for (int w = 0; w < D / 64; ++w) {
-    sum_p += red[0][w];
-    sum_q += red[1][w];
-    max_p = fmaxf(max_p, red[2][w]);
-    max_q = fmaxf(max_q, red[3][w]);
+      for (int c = 0; c < 32; ++c) bits |= (unsigned)((sidx[32 * w + c] >> pl) & 1) << c;
+      p.k_codes[slot * (p.k_planes * wpp) + t] = bits;
+    }
+    if (p.k_prod && t < wpp) {
+      unsigned bits = 0u;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) bits |= (sp[32 * t + c] >= 0.f ? 1u : 0u) << c;
+      p.k_signs[slot * wpp + t] = bits;
+    }
+    if (t == 0) {
+      p.k_norms[slot] = nu32;
+      if (p.k_prod) p.k_rnorms[slot] = gamma;
+    }
+    return;
   }
+  // value: slot len % 32 of its block. Slot v is vector 4g + k (v < 16) or 16 + 4g + k;
+  // plane pl, coordinate 4w + r sits at bit 4r + k (+16) of word (pl*4 + g)*(d/4) + w
+  const int v = (int)(len % 32);
+  const int hi = v >= 16 ? 16 : 0, g = (v % 16) / 4, k = v % 4;
+  const unsigned keep = ~(0x1111u << (k + hi));
+  constexpr int wq = D / 4;
+  uint32_t* blk = p.v_codes + ((int64_t)grp * (p.max_ctx / 32) + len / 32) * (int64_t)(p.v_bits * D);
+  for (int i = t; i < p.v_bits * wq; i += NTH) {
+    const int pl = i / wq, w = i % wq;
+    unsigned bits = 0u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bits |= (unsigned)((sidx[4 * w + r] >> pl) & 1) << (4 * r + k + hi);
+    uint32_t* word = blk + (pl * 4 + g) * wq + w;
+    *word = (*word & keep) | bits;
+  }
+  if (t == 0) p.v_norms[slot] = nu32;
+}
+
+// One launch before the main loop. Blocks [0, n_units): one per (batch, kv
+// head, head chunk): threads 2j and 2j + 1 take the two halves of row j of
+// Pi_K (j < D) or of S_K (j >= D) and dot them with every head of the chunk
+// (each matrix row is read once for all of them, every load of a thread in
+// flight at once); then the block writes the chunk's score-operand fragments
+// (fp16 hi/lo of 2 a_s (Pi_K q)_j and 2 kappa (S_K q)_j with the bit-position
+// powers of two) and the per-row constants. Blocks past n_units (decode with
+// append): the new token's key and value records.
+template <int D, int PK, bool QJL>
+__global__ __launch_bounds__(4 * D) void decode_prep_kernel(DecPrepParams prm) {
+  using KW = KWords<D, PK, QJL>;
+  constexpr int NTH = 4 * D;
+  if ((int)blockIdx.x >= prm.n_units) {
+    const int a = blockIdx.x - prm.n_units;
+    append_one<D, NTH>(prm.app, a >> 1, a & 1, prm.Hkv);
+    return;
+  }
+  __shared__ float qs[8][D], qp[8][D], qq[8][D];
+  __shared__ float stats[8][4];  // per head: sum q', sum q'', max |q'|, max |q''|
+  const int unit = blockIdx.x;
+  const int chunk = unit % prm.n_chunks, bh = unit / prm.n_chunks;
+  const int b = bh / prm.Hkv, hkv = bh % prm.Hkv;
+  const int nh = prm.chunk_heads;
+  const int hq0 = hkv * prm.group + chunk * nh;
+  const int t = threadIdx.x;
+  for (int i = t; i < nh * D; i += NTH) qs[i / D][i % D] = bf16_val(prm.q[((int64_t)b * prm.Hq + hq0 + i / D) * D + i % D]);
+  __syncthreads();
+  {
+    const int mrow = t >> 1, half = t & 1;  // matrix row (Pi_K rows, then S_K rows), half of it
+    const bool s_row = mrow >= D;
+    const int row = mrow % D;
+    constexpr int NV = D / 8;           // float4 loads per half row
+    constexpr int NB = NV < 16 ? NV : 16;  // loads in flight per batch (64 VGPRs)
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (!s_row || QJL) {
+      const float4* m4 = (const float4*)((s_row ? prm.sk[hkv] : prm.pk[hkv]) + (int64_t)row * D) + half * NV;
+#pragma unroll
+      for (int k0 = 0; k0 < NV; k0 += NB) {
+        float4 mv[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) mv[k] = m4[k0 + k];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+          const int c = 4 * (half * NV + k0 + k);
+#pragma unroll
+          for (int h = 0; h < 8; ++h)
+            if (h < nh) a[h] = fmaf(mv[k].x, qs[h][c], fmaf(mv[k].y, qs[h][c + 1], fmaf(mv[k].z, qs[h][c + 2], fmaf(mv[k].w, qs[h][c + 3], a[h]))));
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 8; ++h) a[h] += __shfl_xor(a[h], 1);
+    if (half == 0 && (!s_row || QJL)) {
+      float(*dst)[D] = s_row ? qq : qp;
+#pragma unroll
+      for (int h = 0; h < 8; ++h)
+        if (h < nh) dst[h][row] = a[h];
+    }
+  }
+  __syncthreads();
+  {
+    const int wave = t >> 6, lane = t & 63;
+    for (int h = wave; h < nh; h += NTH / 64) {
+      float s_p = 0.f, s_q = 0.f, m_p = 0.f, m_q = 0.f;
+      for (int j = lane; j < D; j += 64) {
+        s_p += qp[h][j];
+        m_p = fmaxf(m_p, fabsf(qp[h][j]));
+        if (QJL) {
+          s_q += qq[h][j];
+          m_q = fmaxf(m_q, fabsf(qq[h][j]));
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        s_p += __shfl_xor(s_p, o);
+        s_q += __shfl_xor(s_q, o);
+        m_p = fmaxf(m_p, __shfl_xor(m_p, o));
+        m_q = fmaxf(m_q, __shfl_xor(m_q, o));
+      }
+      if (lane == 0) {
+        stats[h][0] = s_p;
+        stats[h][1] = s_q;
+        stats[h][2] = m_p;
+        stats[h][3] = m_q;
+      }
+    }
+  }
+  __syncthreads();
   float amax = 0.f, asum = 0.f;
   for (int s = 0; s < KW::WK; ++s) {
     amax = fmaxf(amax, fabsf(prm.kcoef[s]));
     asum += prm.kcoef[s];
   }
-  // one exponent for both score parts: the main loop scales their sum once
-  const int em = range_exp(fmaxf(2.f * amax * max_p, QJL ? 2.f * prm.kappa * max_q : 0.f) * prm.scale_log2e);
-  const int eq = em;
-  float* cst = prm.consts + (int64_t)bhc * kConstsPerUnit;
-  if (j < 2) {
-    const int row = 2 * h + j;
-    cst[row] = j == 0 ? -asum * sum_p * prm.scale_log2e * ldexpf(1.0f, em - 10) : 0.f;
-    cst[16 + row] = j == 0 ? (QJL ? -prm.kappa * sum_q * prm.scale_log2e * ldexpf(1.0f, eq - 10) : 0.f) : 0.f;
-    cst[32 + row] = ldexpf(1.0f, 10 - em);
-    cst[48 + row] = ldexpf(1.0f, 10 - eq);
+  // one exponent per head for both score parts: the main loop scales their sum once
+  auto head_exp = [&](int h) {
+    return range_exp(fmaxf(2.f * amax * stats[h][2], QJL ? 2.f * prm.kappa * stats[h][3] : 0.f) * prm.scale_log2e);
+  };
+  float* cst = prm.consts + (int64_t)unit * kConstsPerUnit;
+  if (t < 16) {
+    const int h = t >> 1, lo = t & 1;
+    if (h < nh) {
+      const int em = head_exp(h);
+      cst[t] = lo ? 0.f : -asum * stats[h][0] * prm.scale_log2e * ldexpf(1.0f, em - 10);
+      cst[16 + t] = lo ? 0.f : (QJL ? -prm.kappa * stats[h][1] * prm.scale_log2e * ldexpf(1.0f, em - 10) : 0.f);
+      cst[32 + t] = ldexpf(1.0f, 10 - em);
+      cst[48 + t] = ldexpf(1.0f, 10 - em);
+    } else {
+      cst[t] = 0.f;
+      cst[16 + t] = 0.f;
+      cst[32 + t] = 1.f;
+      cst[48 + t] = 1.f;
+    }
   }
-  if (h == 0 && prm.chunk_heads < 8 && j >= 2 * prm.chunk_heads && j < 16) {
-    cst[j] = 0.f;
-    cst[16 + j] = 0.f;
-    cst[32 + j] = 1.f;
-    cst[48 + j] = 1.f;
-  }
-  // fragment elements of this head's rows: (fragment f, lane group g, hi/lo) per thread
-  for (int e = j; e < KW::NF * 4 * 2; e += D) {
-    const int f = e / 8, g = (e / 2) % 4, lo = e % 2;
+  // fragment (f, lane): row r16 = 2 h + lo of the MFMA, K elements 8 g .. 8 g + 7
+  for (int e = t; e < KW::NF * 64; e += NTH) {
+    const int f = e / 64, lane = e % 64;
+    const int g = lane >> 4, r16 = lane & 15, h = r16 >> 1, lo = r16 & 1;
     const int W = f / 4, r = f % 4;
-    const int lane = 16 * g + 2 * h + lo;
     unsigned hv[8];
+    const int E = h < nh ? head_exp(h) : 0;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int k = it / 2, half = it % 2;
       const int beta = 16 * half + 4 * r + k;  // bit of the lane's word
       float val = 0.f;
-      int E;
-      if (W < KW::NWM) {
-        int s, jj;
-        if constexpr (D >= 128) {
-          s = W / (D / 128);
-          jj = g * (D / 4) + 32 * (W % (D / 128)) + beta;
+      if (h < nh) {
+        if (W < KW::NWM) {
+          int s, jj;
+          if constexpr (D >= 128) {
+            s = W / (D / 128);
+            jj = g * (D / 4) + 32 * (W % (D / 128)) + beta;
+          } else {
+            s = 2 * W + half;
+            jj = g * (D / 4) + (beta % 16);
+          }
+          if (s < KW::WK) val = 2.f * prm.kcoef[s] * qp[h][jj];
         } else {
-          s = 2 * W + half;
-          jj = g * (D / 4) + (beta % 16);
+          const int Wq = W - KW::NWM;
+          if constexpr (D >= 128) {
+            val = 2.f * prm.kappa * qq[h][g * (D / 4) + 32 * Wq + beta];
+          } else {
+            if (half == 0) val = 2.f * prm.kappa * qq[h][g * (D / 4) + beta];
+          }
         }
-        if (s < KW::WK) val = 2.f * prm.kcoef[s] * qp[jj];
-        E = em;
-      } else {
-        const int Wq = W - KW::NWM;
-        if constexpr (D >= 128) {
-          val = 2.f * prm.kappa * qq[g * (D / 4) + 32 * Wq + beta];
-        } else {
-          if (half == 0) val = 2.f * prm.kappa * qq[g * (D / 4) + beta];
-        }
-        E = eq;
+        // the lane's bit reads as 2^(operand_pos(k) - 24); raw scores come out x 2^(E - 10)
+        val *= prm.scale_log2e * ldexpf(1.0f, E + 14 - operand_pos(k));
       }
-      // the lane's bit reads as 2^(operand_pos(k) - 24); raw scores come out x 2^(E - 10)
-      val *= prm.scale_log2e * ldexpf(1.0f, E + 14 - operand_pos(k));
       hv[it] = f16_part(val, lo);
     }
-    prm.frag[((int64_t)bhc * KW::NF + f) * 64 + lane] =
+    prm.frag[((int64_t)unit * KW::NF + f) * 64 + lane] =
         u32x4{pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]), pack2(hv[6], hv[7])};
-  }
-  if (h == 0 && prm.chunk_heads < 8) {
-    for (int e = j; e < KW::NF * 64; e += D) {
-      const int lane = e % 64, row = lane % 16;
-      if (row >= 2 * prm.chunk_heads) prm.frag[(int64_t)bhc * KW::NF * 64 + e] = u32x4{0u, 0u, 0u, 0u};
-    }
   }
 }
 
@@ -224,6 +401,7 @@ struct DecMainParams {
   const uint8_t* vcodes;
   const float* vnorms;
   const int* ctx_lens;
+  int len_add;  // 1 when the step appended a token at ctx_lens[b]
   float* part_acc;
   float* part_ml;
   float* scores_dbg;
@@ -316,19 +494,27 @@ constexpr int kEvUnset = 40;
 // Main loop. One wave per (batch, kv head, head chunk, context split); 32
 // tokens (two 16-token tiles) per iteration.
 //
-// Scores: C[token][row] over 16 rows = 8 query heads x (hi, lo) fp16 parts of
-// the score operands; lane (r, g) holds tokens 16t + 4g + i of row r, and the
-// hi and lo lanes of a head (r, r ^ 1) add their parts with one DPP exchange.
+// Scores: C[row][token] over 16 rows = 8 query heads x (hi, lo) fp16 parts of
+// the score operands (the MFMA's A operand, held in registers for the whole
+// split) against the key bit planes (B operand). Lane (n, g) holds rows
+// 4g .. 4g+3 of token n of each tile, i.e. heads 2g and 2g + 1 with both their
+// parts, so a head's score is one add per part and the softmax runs once per
+// (head, token) in the lane that owns the token.
 //
-// Values: A[row][token] holds the hi (even rows) or lo (odd rows) fp16 part of
-// the weight w = p * |v| times 2^(ev - e_k), e_k = vslot_exp(k), for the token
-// in slot k = i of the value bit operand (the K order of the value cache block
-// layout puts token 16t + 4g + k in slot k; its bit reads as 2^(k - 16), and
-// the leftover 2^-2 is removed after the loop). The factor is
-// folded into the exp2 argument, so the weights need no extra multiply. The
-// value subsets accumulate in NSET sets (see value_sets); each set's lead
-// coefficient and the 0/1-to-sign correction are applied once, after the loop.
-template <int D, int PK, bool QJL, int VB, int NSET, bool SCORES>
+// Values: C[row][coord] with A[row][token] = the hi (even rows) or lo (odd rows)
+// fp16 part of the weight w = p * |v| times 2^(ev - e_k), e_k = vslot_exp(k),
+// for the token in slot k of the value bit operand (the K order of the value
+// cache block layout puts token 16t + 4g + k in slot k; its bit reads as
+// 2^(k - 16), and the leftover 2^-2 is removed after the loop). The factor is
+// folded into the exp2 argument. The weights reach the A-operand lanes through
+// a per-wave LDS transpose (each token lane writes its two heads, each row lane
+// reads eight tokens of its head). The value subsets accumulate in NSET sets
+// (see value_sets); each set's lead coefficient and the 0/1-to-sign
+// correction are applied once, after the loop.
+//
+constexpr int kWRow = 40;  // floats per head row of the weight transpose (bank-disjoint writes)
+
+template <int D, int PK, bool QJL, int VB, int NSET>
 __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams prm) {
   using KW = KWords<D, PK, QJL>;
   constexpr int WV = n_walsh(VB);
@@ -340,6 +526,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   constexpr int SREC = D / 8;
   constexpr int VBLK = 4 * VB * D;  // bytes of one 32-token value block
   constexpr int WPP = D >= 128 ? D / 128 : 1;
+  constexpr bool KF_REG = false;  // score fragments in registers (else LDS)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -348,27 +535,39 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   const int chunk = bhc % prm.n_chunks;
   const int bh = bhc / prm.n_chunks;
   const int b = bh / prm.Hkv, hkv = bh % prm.Hkv;
-  // score operands of this (batch, kv head, chunk), shared by the workgroup's waves
-  __shared__ u32x4 kf_lds[KW::NF * 64];
-  // per wave: the norms of the chunk in flight, [0, 32) |k|, [32, 64) |r|, [64, 96) |v|
-  __shared__ float4 nrm_lds[kThreads / 64][24];
-  {
-    const u32x4* src = prm.frag + (int64_t)bhc * KW::NF * 64;
-    for (int i = threadIdx.x; i < KW::NF * 64; i += kThreads) kf_lds[i] = src[i];
+  __shared__ u32x4 kf_lds[KF_REG ? 1 : KW::NF * 64];
+  __shared__ float wt_lds[kThreads / 64][8][kWRow];
+  const u32x4* fsrc = prm.frag + (int64_t)bhc * KW::NF * 64;
+  u32x4 kf[KF_REG ? KW::NF : 1];
+  if constexpr (KF_REG) {
+#pragma unroll
+    for (int f = 0; f < KW::NF; ++f) kf[f] = fsrc[f * 64 + lane];
+  } else {
+    for (int i = threadIdx.x; i < KW::NF * 64; i += kThreads) kf_lds[i] = fsrc[i];
+    __syncthreads();
   }
-  __syncthreads();
-  auto kfrag = [&](int f) -> u32x4 { return kf_lds[f * 64 + lane]; };
+  auto kfrag = [&](int f) -> u32x4 {
+    if constexpr (KF_REG) return kf[f];
+    else return kf_lds[f * 64 + lane];
+  };
   const int split = blockIdx.x * 4 + wave;
   if (split >= prm.n_splits) return;
   int64_t ctx = prm.ctx_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > prm.max_ctx ? prm.max_ctx : ctx);
+  ctx = ctx < 0 ? 0 : ctx + prm.len_add;
+  ctx = ctx > prm.max_ctx ? prm.max_ctx : ctx;
   const int64_t t0 = (int64_t)split * prm.split_tokens;
   const int64_t t1 = min(t0 + prm.split_tokens, ctx);
   const int hq0 = hkv * prm.group + chunk * prm.chunk_heads;
 
+  // constants of this lane's rows 4g .. 4g+3 (heads 2g, 2g + 1; hi and lo parts)
   const float* cst = prm.consts + bhc * kConstsPerUnit;
-  const float cm0 = cst[r16], cq0 = cst[16 + r16];
-  const float isc = cst[32 + r16];  // 2^-E of this row's score operands
+  float cm_init[4], cq_init[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    cm_init[i] = cst[4 * g + i];
+    cq_init[i] = cst[16 + 4 * g + i];
+  }
+  const float isc[2] = {cst[32 + 4 * g], cst[32 + 4 * g + 2]};  // 2^-E of the two heads' score operands
 
   // buffer resources over this split's part of each cache array; per-lane 32-bit offsets
   const int64_t grp = (int64_t)b * prm.Hkv + hkv;
@@ -383,19 +582,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   const unsigned k_off = (unsigned)(r16 * KREC + g * (D / 32));
   const unsigned s_off = (unsigned)(r16 * SREC + g * (D / 32));
   const unsigned v_off = (unsigned)((g * (D / 4) + VWL * r16) * 4);
+  const unsigned n_off = (unsigned)r16 * 4;
   const bool lo_row = r16 & 1;
   const float nsel = lo_row ? -1.0f : -0.0f;  // x + nsel * hi(x): the lo part on odd rows
+  // value slot of this lane's tokens (16 t + r16 sits in slot r16 % 4 of its block group)
+  const float e_slot = (float)vslot_exp(r16 & 3);
 
-  float m_run = -INFINITY;  // running max of this row's scores (log2 units)
-  float m_thr = -INFINITY;  // (m_run + slack) 2^E: raise the max above this raw score
-  int ev = kEvUnset;        // value exponent of this row
-  float mk[4];              // m_run - (ev - e_k): exp2(s - mk[k]) = p * 2^(ev - e_k)
-  float lsum[4];            // per slot: sum of p * 2^(ev - e_k)
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    mk[k] = -INFINITY;
-    lsum[k] = 0.f;
-  }
+  // online softmax state of the lane's two heads (identical across the 16 token lanes of group g)
+  float m_run[2] = {-INFINITY, -INFINITY};  // running max (log2 units)
+  float m_thr[2] = {-INFINITY, -INFINITY};  // (m_run + slack) 2^E: raise the max above this raw score
+  int ev[2] = {kEvUnset, kEvUnset};          // value exponent of the head's rows
+  float mk[2] = {-INFINITY, -INFINITY};      // m_run - (ev - e_slot): exp2(s - mk) = p * 2^(ev - e_slot)
+  float lsum[2] = {0.f, 0.f};                // sum of p * 2^(ev - e_slot) over this lane's tokens
   f32x4 acc[NACC][NT];
 #pragma unroll
   for (int a = 0; a < NACC; ++a)
@@ -405,15 +603,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   const u32x4 ones = {pos_mask(8), pos_mask(9), pos_mask(10), pos_mask(11)};  // slot k: 2^(k - 16)
 
   // Raw cache data of one 32-token chunk for this lane: its key and value bit
-  // words, and one norm (lanes 0..31: |k| of token lane, 32..63: |r|; nb: |v|)
-  // that goes through LDS to the lanes that use it.
+  // words, and the norms of its two tokens (16 t + r16).
   struct Chunk {
     unsigned kpl[2][PK > 0 ? PK : 1][WPP];
     unsigned ksg[2][KW::NWQ > 0 ? KW::NWQ : 1];
     unsigned vp[VB][VWL];
-    float na, nb;
+    float nk[2], gm[2], nv[2];
   };
-  const unsigned ln4 = (unsigned)(lane & 31) * 4;
   auto load_chunk = [&](unsigned rel, Chunk& c) {  // rel = chunk start - t0 (multiple of 32)
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
@@ -435,6 +631,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
           c.ksg[tile][Wq] = (D >= 128) ? x : ((o & 2u) ? (x >> 16) : (x & 0xFFFFu));
         }
       }
+      c.nk[tile] = __uint_as_float(ld32(rn, n_off + 64 * tile, rel * 4));
+      c.gm[tile] = QJL ? __uint_as_float(ld32(rr, n_off + 64 * tile, rel * 4)) : 0.f;
+      c.nv[tile] = __uint_as_float(ld32(rvn, n_off + 64 * tile, rel * 4));
     }
 #pragma unroll
     for (int p = 0; p < VB; ++p) {
@@ -454,33 +653,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
         c.vp[p][3] = t.w;
       }
     }
-    if (lane < 32) {
-      c.na = __uint_as_float(ld32(rn, ln4, rel * 4));
-      c.nb = __uint_as_float(ld32(rvn, ln4, rel * 4));
-    } else {
-      c.na = QJL ? __uint_as_float(ld32(rr, ln4, rel * 4)) : 0.f;
-      c.nb = 0.f;
-    }
   };
 
   const unsigned n_rel = (unsigned)(t1 > t0 ? t1 - t0 : 0);
-  int pend = 0;           // 1: raise the running max; 2: lower the value exponent
-  float pend_val = 0.f;   // lane maximum that triggered it
+  int pend = 0;                       // 1: raise the running max; 2: lower the value exponent
+  float pend_val[2] = {0.f, 0.f};     // lane values per head that triggered it
+  float (*wrow)[kWRow] = wt_lds[wave];
 
   // One chunk: 0 = accumulated, otherwise the pend code (nothing accumulated).
   auto step = [&](unsigned rel, const Chunk& cur, auto mask_c) -> int {
     constexpr bool MASK = decltype(mask_c)::value;  // the chunk runs past the context
-    {
-      float* nl = (float*)nrm_lds[wave];
-      nl[lane] = cur.na;
-      if (lane < 32) nl[64 + lane] = cur.nb;
-    }
     // ---------------- scores: two tiles of 16 tokens ----------------
     f32x4 cm[2], cq[2];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      cm[tile] = f32x4{cm0, cm0, cm0, cm0};
-      cq[tile] = f32x4{cq0, cq0, cq0, cq0};
+      cm[tile] = f32x4{cm_init[0], cm_init[1], cm_init[2], cm_init[3]};
+      cq[tile] = f32x4{cq_init[0], cq_init[1], cq_init[2], cq_init[3]};
     }
     // key words of fragment group W (one Walsh subset / the sign plane) for both tiles
     auto key_words = [&](int W, unsigned (&word)[2]) {
@@ -511,102 +699,97 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
         }
       }
     };
-    // fragments are read from LDS one step ahead of their MFMAs
-    u32x4 bf_next = kfrag(0);
 #pragma unroll
     for (int W = 0; W < KW::NW; ++W) {
       unsigned word[2];
       key_words(W, word);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int f = 4 * W + r;
-        const u32x4 bf = bf_next;
-        if (f + 1 < KW::NF) bf_next = kfrag(f + 1);
-        if (W < KW::NWM) {
-          cm[0] = mfma16(bit_operand(word[0], r), bf, cm[0]);
-          cm[1] = mfma16(bit_operand(word[1], r), bf, cm[1]);
-        } else {
-          cq[0] = mfma16(bit_operand(word[0], r), bf, cq[0]);
-          cq[1] = mfma16(bit_operand(word[1], r), bf, cq[1]);
+        const u32x4 bf = kfrag(4 * W + r);
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+          if (W < KW::NWM) cm[tile] = mfma16(bf, bit_operand(word[tile], r), cm[tile]);
+          else cq[tile] = mfma16(bf, bit_operand(word[tile], r), cq[tile]);
         }
-        // keep the bit operands next to their MFMAs (hoisting them all costs registers)
+        // keep each operand next to its MFMA (hoisting them all costs registers)
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // this lane: row r16 (head r16/2, hi or lo part), tokens rel + 16 tile + 4g + i;
-    // raw scores sr = score 2^E (the row's operand exponent is applied in the exp2 argument)
-    float sr[2][4];
+    // this lane: token 16 t + r16 of the chunk, heads 2g (rows 4g, 4g+1) and 2g + 1 (rows 4g+2, 4g+3);
+    // raw scores sr = score 2^E (the operand exponent is applied in the exp2 argument)
+    float sr[2][2];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      const float4 nk4 = nrm_lds[wave][4 * tile + g];
-      const float4 gm4 = QJL ? nrm_lds[wave][8 + 4 * tile + g] : float4{0.f, 0.f, 0.f, 0.f};
-      const float nkv[4] = {nk4.x, nk4.y, nk4.z, nk4.w};
-      const float gmv[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
       const float cmv[4] = {cm[tile].x, cm[tile].y, cm[tile].z, cm[tile].w};
       const float cqv[4] = {cq[tile].x, cq[tile].y, cq[tile].z, cq[tile].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // hi row + lo row of the same head live in lanes r16 and r16 ^ 1
-        float sc = cmv[i] + swap_pair(cmv[i]);
-        if constexpr (QJL) sc = fmaf(gmv[i], cqv[i] + swap_pair(cqv[i]), sc);
-        sr[tile][i] = nkv[i] * sc;
-      }
-      if constexpr (MASK) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (rel + 16 * tile + 4 * g + i >= n_rel) sr[tile][i] = -INFINITY;
+      for (int hh = 0; hh < 2; ++hh) {
+        float sc = cmv[2 * hh] + cmv[2 * hh + 1];
+        if constexpr (QJL) sc = fmaf(cur.gm[tile], cqv[2 * hh] + cqv[2 * hh + 1], sc);
+        sr[tile][hh] = cur.nk[tile] * sc;
+        if constexpr (MASK) {
+          if (rel + 16 * tile + r16 >= n_rel) sr[tile][hh] = -INFINITY;
+        }
       }
     }
     // ---------------- online softmax: lane-local checks, no cross-lane work ----------------
-    const float mx = max8f(sr);
-    if (__builtin_expect(__any(mx > m_thr), 0)) {
-      pend_val = mx * isc;
+    const float mx0 = fmaxf(sr[0][0], sr[1][0]), mx1 = fmaxf(sr[0][1], sr[1][1]);
+    if (__builtin_expect(__any(mx0 > m_thr[0] || mx1 > m_thr[1]), 0)) {
+      pend_val[0] = mx0 * isc[0];
+      pend_val[1] = mx1 * isc[1];
       return 1;
     }
-    float wv[2][4], pk[2][4];
+    float wv[2][2], pk[2][2];
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      const float4 nv4 = nrm_lds[wave][16 + 4 * tile + g];
-      const float nvv[4] = {nv4.x, nv4.y, nv4.z, nv4.w};
+    for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pk[tile][i] = __builtin_amdgcn_exp2f(fmaf(sr[tile][i], isc, -mk[i]));  // p 2^(ev - e_i)
-        float w = pk[tile][i] * nvv[i];
-        if constexpr (MASK) w = pk[tile][i] > 0.f ? w : 0.f;  // masked tokens may hold garbage norms
-        wv[tile][i] = w;
+      for (int hh = 0; hh < 2; ++hh) {
+        pk[tile][hh] = __builtin_amdgcn_exp2f(fmaf(sr[tile][hh], isc[hh], -mk[hh]));  // p 2^(ev - e_slot)
+        float w = pk[tile][hh] * cur.nv[tile];
+        if constexpr (MASK) w = pk[tile][hh] > 0.f ? w : 0.f;  // masked tokens may hold garbage norms
+        wv[tile][hh] = w;
       }
-    }
-    const unsigned wm = max8_nonneg_bits(wv);
-    if (__builtin_expect(__any(wm >= __float_as_uint(kWeightOperandMax)), 0)) {
-      // largest unscaled weight of this lane: wv 2^(e_k - ev)
-      float u = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) u = fmaxf(u, fmaxf(wv[0][i], wv[1][i]) * ldexpf(1.0f, vslot_exp(i) - ev));
-      pend_val = u;
+    const float wm0 = fmaxf(wv[0][0], wv[1][0]), wm1 = fmaxf(wv[0][1], wv[1][1]);
+    if (__builtin_expect(__any(fmaxf(wm0, wm1) >= kWeightOperandMax), 0)) {
+      // largest unscaled weight of this lane per head: w 2^(e_slot - ev); nothing accumulated
+      pend_val[0] = wm0 * exp2f(e_slot - (float)ev[0]);
+      pend_val[1] = wm1 * exp2f(e_slot - (float)ev[1]);
       return 2;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lsum[i] += pk[0][i] + pk[1][i];
-    if constexpr (SCORES) {
-      const int h = r16 >> 1;
-      if (!lo_row && h < prm.chunk_heads) {
-        float* dst = prm.scores_dbg + ((int64_t)b * prm.Hq + hq0 + h) * prm.max_ctx + t0;
+    for (int hh = 0; hh < 2; ++hh) lsum[hh] += pk[0][hh] + pk[1][hh];
+    if (prm.scores_dbg) {
 #pragma unroll
-        for (int tile = 0; tile < 2; ++tile)
+      for (int hh = 0; hh < 2; ++hh) {
+        const int h = 2 * g + hh;
+        if (h < prm.chunk_heads) {
+          float* dst = prm.scores_dbg + ((int64_t)b * prm.Hq + hq0 + h) * prm.max_ctx + t0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const unsigned tt = rel + 16 * tile + 4 * g + i;
-            if (tt < n_rel) dst[tt] = sr[tile][i] * isc * kLn2;
+          for (int tile = 0; tile < 2; ++tile) {
+            const unsigned tt = rel + 16 * tile + r16;
+            if (tt < n_rel) dst[tt] = sr[tile][hh] * isc[hh] * kLn2;
           }
+        }
       }
     }
+    // ---------------- weights: token lanes -> row lanes through LDS ----------------
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      wrow[2 * g + hh][r16] = wv[0][hh];
+      wrow[2 * g + hh][16 + r16] = wv[1][hh];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const float4 wa = *(const float4*)&wrow[r16 >> 1][4 * g];
+    const float4 wb = *(const float4*)&wrow[r16 >> 1][16 + 4 * g];
+    const float w0[4] = {wa.x, wa.y, wa.z, wa.w};  // tokens 4g + k (slot k)
+    const float w1[4] = {wb.x, wb.y, wb.z, wb.w};  // tokens 16 + 4g + k
     // ---------------- values ----------------
     // A operand for weights x: the hi (even rows) or lo (odd rows) fp16 part
     auto a_operand = [&](float rho, bool scaled) -> u32x4 {
       unsigned d4[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        d4[k] = split_pair(scaled ? wv[0][k] * rho : wv[0][k], scaled ? wv[1][k] * rho : wv[1][k], nsel);
+      for (int k = 0; k < 4; ++k) d4[k] = split_pair(scaled ? w0[k] * rho : w0[k], scaled ? w1[k] * rho : w1[k], nsel);
       return u32x4{d4[0], d4[1], d4[2], d4[3]};
     };
     const u32x4 a_lead = a_operand(1.0f, false);
@@ -640,43 +823,43 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   unsigned rel = 0;
   while (true) {
     if (pend) {
-      // row-wide maximum of the lane values (lanes 16 apart hold the same row)
-      float v = pend_val;
-      v = fmaxf(v, __shfl_xor(v, 16));
-      v = fmaxf(v, __shfl_xor(v, 32));
-      float f = 1.0f;
-      if (pend == 1) {
-        const float m_new = fmaxf(m_run, v);
-        f = exp2f(m_run - m_new);  // 0 on the first chunk (m_run = -inf); the state is still zero
-        m_run = m_new;
-      } else {
-        const int e_need = range_exp(v);  // v: the row's largest weight in this chunk
-        const int ev_new = e_need < ev ? e_need : ev;
-        f = ldexpf(1.0f, ev_new - ev);
-        ev = ev_new;
-      }
-      m_thr = (m_run + kRescaleSlack) / isc;
+      // group-wide maxima over the 16 token lanes of this lane group (heads 2g, 2g + 1)
+      float f[2];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        mk[k] = m_run - (float)(ev - vslot_exp(k));
-        lsum[k] *= f;
-      }
-      float fr[4];
+      for (int hh = 0; hh < 2; ++hh) {
+        float v = pend_val[hh];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fr[i] = __shfl(f, 4 * g + i);
+        for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+        f[hh] = 1.0f;
+        if (pend == 1) {
+          const float m_new = fmaxf(m_run[hh], v);
+          // 0 on the first chunk (m_run = -inf); the state is still zero then
+          if (m_new > -INFINITY) f[hh] = exp2f(m_run[hh] - m_new);
+          m_run[hh] = m_new;
+        } else {
+          const int e_need = range_exp(v);  // v: the head's largest weight in this chunk
+          const int ev_new = e_need < ev[hh] ? e_need : ev[hh];
+          f[hh] = ldexpf(1.0f, ev_new - ev[hh]);
+          ev[hh] = ev_new;
+        }
+        m_thr[hh] = (m_run[hh] + kRescaleSlack) / isc[hh];
+        mk[hh] = m_run[hh] - ((float)ev[hh] - e_slot);
+        lsum[hh] *= f[hh];
+      }
+      // value rows 4g .. 4g+3 of every lane in this group are heads 2g (x, y) and 2g + 1 (z, w)
 #pragma unroll
       for (int a = 0; a < NACC; ++a)
 #pragma unroll
         for (int q = 0; q < NT; ++q) {
-          acc[a][q].x *= fr[0];
-          acc[a][q].y *= fr[1];
-          acc[a][q].z *= fr[2];
-          acc[a][q].w *= fr[3];
+          acc[a][q].x *= f[0];
+          acc[a][q].y *= f[0];
+          acc[a][q].z *= f[1];
+          acc[a][q].w *= f[1];
         }
-      wacc.x *= fr[0];
-      wacc.y *= fr[1];
-      wacc.z *= fr[2];
-      wacc.w *= fr[3];
+      wacc.x *= f[0];
+      wacc.y *= f[0];
+      wacc.z *= f[1];
+      wacc.w *= f[1];
       pend = 0;
     }
     if (rel >= n_rel) break;
@@ -705,28 +888,35 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   }
 
   // ---------------- write this split's partial state ----------------
-  // softmax denominator of this row: sum_k lsum[k] 2^(e_k - ev), over the 4 lane groups
-  float l_acc = 0.f;
+  // softmax denominator per head: sum over the 16 token lanes of lsum 2^(e_slot - ev)
+  float l_acc[2];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) l_acc += lsum[k] * ldexpf(1.0f, vslot_exp(k) - ev);
-  l_acc += __shfl_xor(l_acc, 16);
-  l_acc += __shfl_xor(l_acc, 32);
+  for (int hh = 0; hh < 2; ++hh) {
+    float l = lsum[hh] * exp2f(e_slot - (float)ev[hh]);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) l += __shfl_xor(l, o);
+    l_acc[hh] = l;
+  }
   const int64_t hq_base = (int64_t)b * prm.Hq + hq0;
-  if (g == 0 && !lo_row && (r16 >> 1) < prm.chunk_heads) {
-    float* ml = prm.part_ml + ((hq_base + (r16 >> 1)) * prm.n_splits + split) * 2;
-    ml[0] = m_run;
-    ml[1] = l_acc;
+  if (r16 == 0) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int h = 2 * g + hh;
+      if (h < prm.chunk_heads) {
+        float* ml = prm.part_ml + ((hq_base + h) * prm.n_splits + split) * 2;
+        ml[0] = m_run[hh];
+        ml[1] = l_acc[hh];
+      }
+    }
   }
   // sum of w 2^ev per head, in the value lanes' row order (rows 4g .. 4g+3)
   const float wt[2] = {wacc.x + wacc.y, wacc.z + wacc.w};
   // value lanes: coordinate lane r16 (coords (D/16) r16 + q), rows 4g .. 4g+3 = heads 2g, 2g+1 (hi, lo)
-  const int ev_h0 = __shfl(ev, 4 * g);
-  const int ev_h1 = __shfl(ev, 4 * g + 2);
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     const int h = 2 * g + hh;
     if (h >= prm.chunk_heads) continue;
-    const float unscale = ldexpf(1.0f, -(hh ? ev_h1 : ev_h0));
+    const float unscale = ldexpf(1.0f, -ev[hh]);
     const float wh = wt[hh] * 4.0f;  // the ones operand reads 2^(k - 16) against 2^(14 - k)
     float outv[NT];
 #pragma unroll
@@ -751,26 +941,30 @@ struct DecCombineParams {
   const float* part_ml;
   const float* pv[kMaxKvHeads];
   float* out;
-  int n_splits, Hq, group;
+  int n_splits, Hq, Hkv, group, chunk_heads, n_chunks;
 };
 
-// One workgroup per (batch, query head): weights 2^(m_s - M) / L of every
-// split, the merged rotated-space accumulator, then out = Pi_V^T acc.
+// One block of 512 threads per (batch, query head): the weights 2^(m_s - M) / L
+// of every split (block reductions), the merged rotated-space accumulator
+// (thread (quad, phase) sums phase, phase + P, ... of its four coordinates with
+// 16-byte loads, then the phases are added in LDS), and out = Pi_V^T acc.
+constexpr int kCombineThreads = 512;
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecCombineParams prm) {
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecCombineParams prm) {
   extern __shared__ float wsplit[];  // [n_splits]
-  __shared__ float red[2][kThreads / 64];
-  __shared__ float part[kThreads / D][D];
+  constexpr int NQ = D / 4;                   // coordinate quads
+  constexpr int P = kCombineThreads / NQ;     // split phases
+  __shared__ float4 part[P][NQ];
   __shared__ float o[D];
+  __shared__ float red[2][kCombineThreads / 64];
   const int64_t bhq = blockIdx.x;
   const int hq = (int)(bhq % prm.Hq);
   const int hkv = hq / prm.group;
   const int ns = prm.n_splits;
   const float* ml = prm.part_ml + bhq * ns * 2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // block reductions: within each wave by shuffles, then across the waves
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   float mx = -INFINITY;
-  for (int s = threadIdx.x; s < ns; s += kThreads)
+  for (int s = t; s < ns; s += kCombineThreads)
     if (ml[2 * s + 1] > 0.f) mx = fmaxf(mx, ml[2 * s]);
 #pragma unroll
   for (int o2 = 32; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
@@ -778,13 +972,13 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecCombinePara
   __syncthreads();
   float M = red[0][0];
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, red[0][w]);
+  for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, red[0][w]);
   float lsum = 0.f;
-  for (int s = threadIdx.x; s < ns; s += kThreads) {
+  for (int s = t; s < ns; s += kCombineThreads) {
     const float l = ml[2 * s + 1];
-    const float wgt = l > 0.f ? exp2f(ml[2 * s] - M) : 0.f;
-    wsplit[s] = wgt;
-    lsum += wgt * l;
+    const float w = l > 0.f ? exp2f(ml[2 * s] - M) : 0.f;
+    wsplit[s] = w;
+    lsum += w * l;
   }
 #pragma unroll
   for (int o2 = 32; o2 > 0; o2 >>= 1) lsum += __shfl_xor(lsum, o2);
@@ -792,42 +986,60 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecCombinePara
   __syncthreads();  // also publishes wsplit
   float L = red[1][0];
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) L += red[1][w];
+  for (int w = 1; w < kCombineThreads / 64; ++w) L += red[1][w];
   const float invL = L > 0.f ? 1.0f / L : 0.f;
-  // merged accumulator: thread (j, phase) sums splits phase, phase + P, ...
-  constexpr int P = kThreads / D;
-  const int j = threadIdx.x % D, ph = threadIdx.x / D;
-  const float* acc = prm.part_acc + bhq * (int64_t)ns * D + j;
-  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // eight loads in flight
+  const int quad = t % NQ, ph = t / NQ;
+  const float4* acc = (const float4*)(prm.part_acc + bhq * (int64_t)ns * D) + quad;
+  float4 a[4] = {};
   int s = ph;
-  for (; s + 7 * P < ns; s += 8 * P) {
+  for (; s + 3 * P < ns; s += 4 * P) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) a[u] += wsplit[s + u * P] * acc[(int64_t)(s + u * P) * D];
+    for (int u = 0; u < 4; ++u) {
+      const float w = wsplit[s + u * P];
+      const float4 v = acc[(int64_t)(s + u * P) * NQ];
+      a[u].x = fmaf(w, v.x, a[u].x);
+      a[u].y = fmaf(w, v.y, a[u].y);
+      a[u].z = fmaf(w, v.z, a[u].z);
+      a[u].w = fmaf(w, v.w, a[u].w);
+    }
   }
-  for (; s < ns; s += P) a[0] += wsplit[s] * acc[(int64_t)s * D];
-  part[ph][j] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+  for (; s < ns; s += P) {
+    const float w = wsplit[s];
+    const float4 v = acc[(int64_t)s * NQ];
+    a[0].x = fmaf(w, v.x, a[0].x);
+    a[0].y = fmaf(w, v.y, a[0].y);
+    a[0].z = fmaf(w, v.z, a[0].z);
+    a[0].w = fmaf(w, v.w, a[0].w);
+  }
+  part[ph][quad] = float4{(a[0].x + a[1].x) + (a[2].x + a[3].x), (a[0].y + a[1].y) + (a[2].y + a[3].y),
+                          (a[0].z + a[1].z) + (a[2].z + a[3].z), (a[0].w + a[1].w) + (a[2].w + a[3].w)};
   __syncthreads();
-  if (threadIdx.x < D) {
-    float t = 0.f;
+  if (t < D) {
+    float v = 0.f;
 #pragma unroll
-    for (int p = 0; p < P; ++p) t += part[p][threadIdx.x];
-    o[threadIdx.x] = t * invL;
+    for (int p = 0; p < P; ++p) v += ((const float*)part[p])[t];
+    o[t] = v * invL;
   }
   __syncthreads();
-  // out[j] = sum_i Pi_V[i][j] o[i]
+  // out[i] = sum_j Pi_V[j][i] o[j]: thread (i, phase) sums rows phase, phase + R, ...
+  constexpr int R = kCombineThreads / D;
   const float* Pv = prm.pv[hkv];
-  float bq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // eight rows in flight
-  for (int i = ph * 8; i < D; i += 8 * P) {
+  const int i = t % D, pr = t / D;
+  constexpr int NJ = D / R;  // rows per thread, every load in flight at once
+  float pvv[NJ];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) bq[u] += Pv[(int64_t)(i + u) * D + j] * o[i + u];
-  }
-  part[ph][j] = ((bq[0] + bq[1]) + (bq[2] + bq[3])) + ((bq[4] + bq[5]) + (bq[6] + bq[7]));
+  for (int u = 0; u < NJ; ++u) pvv[u] = Pv[(int64_t)(pr + u * R) * D + i];
+  float b4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < NJ; ++u) b4[u & 3] = fmaf(pvv[u], o[pr + u * R], b4[u & 3]);
+  float* pb = (float*)part;
+  pb[pr * D + i] = (b4[0] + b4[1]) + (b4[2] + b4[3]);
   __syncthreads();
-  if (threadIdx.x < D) {
-    float t = 0.f;
+  if (t < D) {
+    float v = 0.f;
 #pragma unroll
-    for (int p = 0; p < P; ++p) t += part[p][threadIdx.x];
-    prm.out[bhq * D + threadIdx.x] = t;
+    for (int p = 0; p < R; ++p) v += pb[p * D + t];
+    prm.out[bhq * D + t] = v;
   }
 }
 
@@ -875,7 +1087,7 @@ tq_status plan_decode(const tq_attn_shape* s, const tq_quantizer* k0, const tq_q
 
 tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* k, const tq_packed_kv* v,
                         const int32_t* ctx_lens, float scale, float* out, float* scores_dbg,
-                        void* workspace, hipStream_t stream) {
+                        void* workspace, hipStream_t stream, const AppendLaunch* app) {
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
   unsigned char* ws = (unsigned char*)workspace;
   u32x4* frag = (u32x4*)ws;
@@ -899,9 +1111,45 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
   pp.group = p.group;
   pp.chunk_heads = p.chunk_heads;
   pp.n_chunks = p.n_chunks;
+  pp.n_units = units;
   pp.scale_log2e = scale * kLog2e;
   pp.kappa = (float)(std::sqrt(M_PI / 2.0) / p.d);
   for (int s = 0; s < k0->cb.n_walsh; ++s) pp.kcoef[s] = k0->cb.walsh_coef[s];
+  if (app) {
+    AppendArgs& a = pp.app;
+    a.ctx_lens = ctx_lens;
+    a.max_ctx = p.max_ctx;
+    a.k_planes = k0->planes;
+    a.v_bits = v0->bits;
+    a.k_prod = k0->variant == TQ_PROD;
+    a.x_bf16 = app->x_dtype == TQ_BF16;
+    a.k_new = app->k_new;
+    a.v_new = app->v_new;
+    for (int h = 0; h < p.n_kv_heads; ++h) {
+      a.k_pi[h] = k->qz[h]->pi32;
+      a.k_sp[h] = k->qz[h]->sp32;
+      a.v_pi[h] = v->qz[h]->pi32;
+    }
+    const Codebook& kc = k0->cb;
+    const Codebook& vc = v0->cb;
+    for (int i = 0; i < 15; ++i) {
+      a.k_thr[i] = i + 1 < (1 << kc.planes) ? kc.thresholds[i] : 0.f;
+      a.v_thr[i] = i + 1 < (1 << vc.planes) ? vc.thresholds[i] : 0.f;
+    }
+    for (int i = 0; i < 16; ++i) {
+      a.k_cen[i] = i < (1 << kc.planes) ? kc.centroids[i] : 0.f;
+      a.v_cen[i] = i < (1 << vc.planes) ? vc.centroids[i] : 0.f;
+    }
+    a.k_codes = (uint32_t*)const_cast<uint8_t*>(k->codes);
+    a.k_signs = (uint32_t*)const_cast<uint8_t*>(k->signs);
+    a.k_norms = const_cast<float*>(k->norms);
+    a.k_rnorms = const_cast<float*>(k->rnorms);
+    a.v_codes = (uint32_t*)const_cast<uint8_t*>(v->codes);
+    a.v_norms = const_cast<float*>(v->norms);
+    a.rot_dbg = app->rot_dbg;
+    a.proj_dbg = app->proj_dbg;
+  }
+  const int prep_blocks = units + (app ? 2 * p.batch * p.n_kv_heads : 0);
 
   DecMainParams mp{};
   mp.frag = frag;
@@ -913,6 +1161,7 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
   mp.vcodes = v->codes;
   mp.vnorms = v->norms;
   mp.ctx_lens = ctx_lens;
+  mp.len_add = app ? 1 : 0;
   mp.part_acc = part_acc;
   mp.part_ml = part_ml;
   mp.scores_dbg = scores_dbg;
@@ -947,7 +1196,10 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
   cp.out = out;
   cp.n_splits = p.n_splits;
   cp.Hq = p.n_q_heads;
+  cp.Hkv = p.n_kv_heads;
   cp.group = p.group;
+  cp.chunk_heads = p.chunk_heads;
+  cp.n_chunks = p.n_chunks;
 
   return dispatch_dim(p.d, [&](auto DC) -> tq_status {
     constexpr int D = decltype(DC)::value;
@@ -958,7 +1210,7 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
         if constexpr ((!QJL && PK == 0) || (QJL && PK > 3)) {
           return set_error(TQ_ERR_UNSUPPORTED, "decode: unsupported key quantizer");
         } else {
-          hipLaunchKernelGGL((decode_prep_kernel<D, PK, QJL>), dim3((unsigned)(p.batch * p.n_q_heads)), dim3(D), 0, stream, pp);
+          hipLaunchKernelGGL((decode_prep_kernel<D, PK, QJL>), dim3((unsigned)prep_blocks), dim3(4 * D), 0, stream, pp);
           tq_status st = launch_check("decode: prep launch");
           if (st != TQ_OK) return st;
           st = dispatch_planes(p.v_bits, [&](auto VBC) -> tq_status {
@@ -967,18 +1219,14 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
               return set_error(TQ_ERR_UNSUPPORTED, "decode: value bits");
             } else {
               constexpr int NSET = value_sets(D, VB);
-              return dispatch_bool(scores_dbg != nullptr, [&](auto SC) -> tq_status {
-                constexpr bool SCORES = decltype(SC)::value;
-                dim3 grid((unsigned)((p.n_splits + 3) / 4), (unsigned)units);
-                hipLaunchKernelGGL((decode_main_kernel<D, PK, QJL, VB, NSET, SCORES>), grid, dim3(kThreads), 0, stream,
-                                   mp);
-                return launch_check("decode: main launch");
-              });
+              dim3 grid((unsigned)((p.n_splits + 3) / 4), (unsigned)units);
+              hipLaunchKernelGGL((decode_main_kernel<D, PK, QJL, VB, NSET>), grid, dim3(kThreads), 0, stream, mp);
+              return launch_check("decode: main launch");
             }
           });
           if (st != TQ_OK) return st;
-          hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(p.batch * p.n_q_heads)), dim3(kThreads),
-                             (size_t)p.n_splits * sizeof(float), stream, cp);
+          hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(p.batch * p.n_q_heads)),
+                             dim3(kCombineThreads), (size_t)p.n_splits * sizeof(float), stream, cp);
           return launch_check("decode: combine launch");
         }
       });

@@ -159,30 +159,19 @@ struct DecodePlan {
 };
 tq_status plan_decode(const tq_attn_shape* s, const tq_quantizer* k0, const tq_quantizer* v0,
                       DecodePlan* plan);
-tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* k,
-                        const tq_packed_kv* v, const int32_t* ctx_lens, float scale, float* out,
-                        float* scores_dbg, void* workspace, hipStream_t stream);
-
-// Decode-step append (tq_append.hip): quantize the new key and value of every
-// (batch, kv head) and write them into the caches at ctx_lens[b]; lens_out[b]
-// gets the attended length.
+// Decode step with append: the new key and value of every (batch, kv head) are
+// quantized into the caches at ctx_lens[b] by the launch that precedes the main
+// loop, which then attends ctx_lens[b] + 1 tokens (at most max_ctx).
 struct AppendLaunch {
-  const int32_t* ctx_lens;
-  int32_t* lens_out;
-  int batch, n_kv_heads, d;
-  int64_t max_ctx;
-  const tq_quantizer* const* kq;  // [n_kv_heads]
-  const tq_quantizer* const* vq;
   const void* k_new;
   const void* v_new;
   tq_dtype x_dtype;
-  uint8_t* k_codes;
-  uint8_t* k_signs;
-  float* k_norms;
-  float* k_rnorms;
-  uint8_t* v_codes;
-  float* v_norms;
+  float* rot_dbg;   // optional [B][Hkv][2][d]
+  float* proj_dbg;  // optional [B][Hkv][d]
 };
-tq_status launch_append(const AppendLaunch& a, hipStream_t stream);
+tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* k,
+                        const tq_packed_kv* v, const int32_t* ctx_lens, float scale, float* out,
+                        float* scores_dbg, void* workspace, hipStream_t stream,
+                        const AppendLaunch* app = nullptr);
 
 }  // namespace tq

@@ -42,7 +42,7 @@ def parse():
                     help="counter summary with the measured HBM bytes per decode launch (default: profiles/)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device to device 3 times (scale reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["quantize", "decode"], default=None,
+    ap.add_argument("--only", choices=["quantize", "decode", "append"], default=None,
                     help="profiling runs: build the headline workload, then run only this stage "
                          "warmup + steps times and print its mean time (no JSON line)")
     return ap.parse_args()
@@ -404,8 +404,17 @@ def main():
         tq.decode_attention(w["q"], w["kcache"], w["vcache"], w["lens"], 1 / math.sqrt(w["d"]), max_ctx=w["T3"],
                             out=w["out"], workspace=w["ws"])
 
+    if args.only == "append":
+        knew = torch.zeros((w["B"], w["Hkv"], w["d"]), dtype=torch.bfloat16, device=dev)
+        knew.normal_()
+        vnew = torch.randn_like(knew)
+        lens_app = torch.full((w["B"],), w["T3"] - 1, dtype=torch.int32, device=dev)
+
+        def append_step():
+            tq.decode_append_attention(w["q"], knew, vnew, w["kcache"], w["vcache"], lens_app,
+                                       1 / math.sqrt(w["d"]), max_ctx=w["T3"], out=w["out"], workspace=w["ws"])
     if args.only:
-        stage = quantize_layer if args.only == "quantize" else decode
+        stage = quantize_layer if args.only == "quantize" else decode if args.only == "decode" else append_step
         for _ in range(args.warmup):
             stage()
         torch.cuda.synchronize()

@@ -358,20 +358,34 @@ tq_status tq_decode_attention(const tq_attn_shape* shape, const void* q, const t
  *                   (the caller adds 1 after the call). A sequence with
  *                   ctx_lens[b] >= max_ctx is not appended and attends max_ctx
  *                   tokens.
- *   workspace     : device, at least tq_decode_append_workspace_size() bytes.
+ *   dbg           : NULL, or device buffers (each may be NULL) that receive what
+ *                   the new records were decided on: rot [B][Hkv][2][d] float32,
+ *                   the rotated unit vectors Pi x/|x| of the key (index 0) and
+ *                   the value (index 1) exactly as compared with the
+ *                   thresholds; proj [B][Hkv][d] float32, S r of the key (prod)
+ *                   whose signs were stored. Entries of sequences that are not
+ *                   appended are left untouched.
+ *   workspace     : device, at least tq_decode_append_workspace_size() bytes
+ *                   (the same size as tq_decode_workspace_size()).
  * Same validation and errors as tq_decode_attention, plus TQ_ERR_INVALID_ARG
- * for NULL k_new / v_new or an unknown kv_dtype. Two steps on `stream` (one
- * workgroup per (b, h) quantizes and writes both records, then the attention);
- * no host synchronization. Records equal those of tq_quantize except where a
- * rotated coordinate lies within rounding of a decision threshold (the append
- * rotates in fp32 instead of split-bf16 matrix cores).
+ * for NULL k_new / v_new or an unknown kv_dtype. The new tokens are quantized by
+ * the launch that prepares the queries (one block per (b, h) and tensor, fp32
+ * rotation, fp64 norm), before the attention reads the cache; no host
+ * synchronization. Records equal those of tq_quantize except where a rotated
+ * coordinate lies within rounding of a decision threshold (tq_quantize rotates
+ * with split-bf16 matrix cores).
  */
+typedef struct {
+  float* rot;
+  float* proj;
+} tq_append_debug;
 tq_status tq_decode_append_workspace_size(const tq_attn_shape* shape, const tq_packed_kv* k,
                                           const tq_packed_kv* v, size_t* bytes);
 tq_status tq_decode_append_attention(const tq_attn_shape* shape, const void* q, const void* k_new,
                                      const void* v_new, tq_dtype kv_dtype, const tq_packed_kv* k,
                                      const tq_packed_kv* v, const int32_t* ctx_lens, float scale,
-                                     float* out, void* workspace, size_t ws_bytes, void* stream);
+                                     float* out, const tq_append_debug* dbg, void* workspace,
+                                     size_t ws_bytes, void* stream);
 
 /*
  * Decode attention over KV caches quantized with an outlier-channel split

@@ -134,7 +134,7 @@ def test_wht_argument_errors(lib):
 
 def test_append_argument_errors(lib):
     assert lib.tq_decode_append_attention(None, None, None, None, 1, None, None, None, ctypes.c_float(1.0), None,
-                                          None, 0, None) == tq.TQ_ERR_INVALID_ARG
+                                          None, None, 0, None) == tq.TQ_ERR_INVALID_ARG
     nb = ctypes.c_size_t(0)
     shape = tq.AttnShape(1, 8, 1, 128, 100)
     kv = tq.PackedKV(None, None, None, None, None)
