@@ -434,6 +434,13 @@ __device__ __forceinline__ unsigned split_pair(float x0, float x1, float nsel) {
   return r;
 }
 
+// RNE fp16 of x0 (low half) and x1 (high half): the hi parts of split_pair
+__device__ __forceinline__ unsigned f16_pair_rne(float x0, float x1) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f2){x0, x1}, h2));
+}
+
 // max of three floats as one v_max3_f32 (fmaxf chains pick up NaN
 // canonicalisations in IEEE mode); the inputs are ordinary VALU results
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -507,12 +514,12 @@ constexpr int kEvUnset = 40;
 // cache block layout puts token 16t + 4g + k in slot k; its bit reads as
 // 2^(k - 16), and the leftover 2^-2 is removed after the loop). The factor is
 // folded into the exp2 argument. The weights reach the A-operand lanes through
-// a per-wave LDS transpose (each token lane writes its two heads, each row lane
-// reads eight tokens of its head). The value subsets accumulate in NSET sets
-// (see value_sets); each set's lead coefficient and the 0/1-to-sign
-// correction are applied once, after the loop.
-//
-constexpr int kWRow = 40;  // floats per head row of the weight transpose (bank-disjoint writes)
+// a per-wave LDS transpose: each token lane splits its two heads' weights of
+// both tiles into fp16 hi and lo pairs (for the lead subsets and, scaled by
+// a_s / a_lead, for every other subset: see value_sets) and writes them into
+// the rows the value lanes read as whole operands. Each set's lead coefficient
+// and the 0/1-to-sign correction are applied once, after the loop.
+constexpr int kWRow = 40;  // dwords per (version, head) row: hi pairs [0,16), lo pairs [16,32), padding
 
 template <int D, int PK, bool QJL, int VB, int NSET>
 __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams prm) {
@@ -536,7 +543,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   const int bh = bhc / prm.n_chunks;
   const int b = bh / prm.Hkv, hkv = bh % prm.Hkv;
   __shared__ u32x4 kf_lds[KF_REG ? 1 : KW::NF * 64];
-  __shared__ float wt_lds[kThreads / 64][8][kWRow];
+  constexpr int NVER = 1 + (WV - NSET);  // weight versions: the leads, then one per other subset
+  __shared__ unsigned wt_lds[kThreads / 64][NVER][8][kWRow];
   const u32x4* fsrc = prm.frag + (int64_t)bhc * KW::NF * 64;
   u32x4 kf[KF_REG ? KW::NF : 1];
   if constexpr (KF_REG) {
@@ -583,8 +591,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   const unsigned s_off = (unsigned)(r16 * SREC + g * (D / 32));
   const unsigned v_off = (unsigned)((g * (D / 4) + VWL * r16) * 4);
   const unsigned n_off = (unsigned)r16 * 4;
-  const bool lo_row = r16 & 1;
-  const float nsel = lo_row ? -1.0f : -0.0f;  // x + nsel * hi(x): the lo part on odd rows
   // value slot of this lane's tokens (16 t + r16 sits in slot r16 % 4 of its block group)
   const float e_slot = (float)vslot_exp(r16 & 3);
 
@@ -658,7 +664,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   const unsigned n_rel = (unsigned)(t1 > t0 ? t1 - t0 : 0);
   int pend = 0;                       // 1: raise the running max; 2: lower the value exponent
   float pend_val[2] = {0.f, 0.f};     // lane values per head that triggered it
-  float (*wrow)[kWRow] = wt_lds[wave];
+  unsigned (*wrow)[8][kWRow] = wt_lds[wave];
 
   // One chunk: 0 = accumulated, otherwise the pend code (nothing accumulated).
   auto step = [&](unsigned rel, const Chunk& cur, auto mask_c) -> int {
@@ -699,21 +705,30 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
         }
       }
     };
+    unsigned kw[KW::NW][2];
 #pragma unroll
-    for (int W = 0; W < KW::NW; ++W) {
-      unsigned word[2];
-      key_words(W, word);
+    for (int W = 0; W < KW::NW; ++W) key_words(W, kw[W]);
+    // fragment f = 4 W + r scores both tiles: word W, nibble r. The two bit operands
+    // of fragment f + 1 are built while fragment f's MFMAs run, so no MFMA waits on
+    // the VALU that wrote its operand
+    u32x4 kop_next[2] = {bit_operand(kw[0][0], 0), bit_operand(kw[0][1], 0)};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const u32x4 bf = kfrag(4 * W + r);
-#pragma unroll
-        for (int tile = 0; tile < 2; ++tile) {
-          if (W < KW::NWM) cm[tile] = mfma16(bf, bit_operand(word[tile], r), cm[tile]);
-          else cq[tile] = mfma16(bf, bit_operand(word[tile], r), cq[tile]);
-        }
-        // keep each operand next to its MFMA (hoisting them all costs registers)
-        __builtin_amdgcn_sched_barrier(0);
+    for (int f = 0; f < KW::NF; ++f) {
+      const u32x4 op0 = kop_next[0], op1 = kop_next[1];
+      if (f + 1 < KW::NF) {
+        kop_next[0] = bit_operand(kw[(f + 1) / 4][0], (f + 1) % 4);
+        kop_next[1] = bit_operand(kw[(f + 1) / 4][1], (f + 1) % 4);
       }
+      const u32x4 bf = kfrag(f);
+      if (f / 4 < KW::NWM) {
+        cm[0] = mfma16(bf, op0, cm[0]);
+        cm[1] = mfma16(bf, op1, cm[1]);
+      } else {
+        cq[0] = mfma16(bf, op0, cq[0]);
+        cq[1] = mfma16(bf, op1, cq[1]);
+      }
+      // keep the operand construction next to its MFMAs (hoisting it all costs registers)
+      __builtin_amdgcn_sched_barrier(0);
     }
     // this lane: token 16 t + r16 of the chunk, heads 2g (rows 4g, 4g+1) and 2g + 1 (rows 4g+2, 4g+3);
     // raw scores sr = score 2^E (the operand exponent is applied in the exp2 argument)
@@ -773,45 +788,66 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
       }
     }
     // ---------------- weights: token lanes -> row lanes through LDS ----------------
+    // dword r16 of row (version, head) holds (tile 0, tile 1) of token r16 as fp16 hi
+    // parts, dword 16 + r16 the lo parts: K elements 2k, 2k + 1 of value lane group
+    // g' are tokens 4g' + k and 16 + 4g' + k, so a value lane reads 4 whole dwords
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      wrow[2 * g + hh][r16] = wv[0][hh];
-      wrow[2 * g + hh][16 + r16] = wv[1][hh];
+    for (int v = 0; v < NVER; ++v) {
+      float rho = 1.0f;
+#pragma unroll
+      for (int s = 0, n = 0; s < WV; ++s)
+        if (!walsh_is_lead(VB, NSET, s)) {
+          if (++n == v) rho = prm.vrho[s];
+        }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float x0 = v ? wv[0][hh] * rho : wv[0][hh], x1 = v ? wv[1][hh] * rho : wv[1][hh];
+        unsigned* row = wrow[v][2 * g + hh];
+        row[r16] = f16_pair_rne(x0, x1);
+        row[16 + r16] = split_pair(x0, x1, -1.0f);
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const float4 wa = *(const float4*)&wrow[r16 >> 1][4 * g];
-    const float4 wb = *(const float4*)&wrow[r16 >> 1][16 + 4 * g];
-    const float w0[4] = {wa.x, wa.y, wa.z, wa.w};  // tokens 4g + k (slot k)
-    const float w1[4] = {wb.x, wb.y, wb.z, wb.w};  // tokens 16 + 4g + k
     // ---------------- values ----------------
-    // A operand for weights x: the hi (even rows) or lo (odd rows) fp16 part
-    auto a_operand = [&](float rho, bool scaled) -> u32x4 {
-      unsigned d4[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) d4[k] = split_pair(scaled ? w0[k] * rho : w0[k], scaled ? w1[k] * rho : w1[k], nsel);
-      return u32x4{d4[0], d4[1], d4[2], d4[3]};
+    // A operand of version v: the hi (even rows) or lo (odd rows) parts of head r16 / 2
+    auto a_operand = [&](int v) -> u32x4 {
+      return *(const u32x4*)&wrow[v][r16 >> 1][16 * (r16 & 1) + 4 * g];
     };
-    const u32x4 a_lead = a_operand(1.0f, false);
+    const u32x4 a_lead = a_operand(0);
+    u32x4 af[NVER];
+    af[0] = a_lead;
 #pragma unroll
-    for (int s = 0; s < WV; ++s) {
-      const int mask = walsh_mask(VB, s);
-      const bool lead = walsh_is_lead(VB, NSET, s);
-      const int set = walsh_set(VB, NSET, s);
-      const u32x4 af = lead ? a_lead : a_operand(prm.vrho[s], true);
+    for (int v = 1; v < NVER; ++v) af[v] = a_operand(v);
+    // value words of every subset (XORs of the planes), then MFMA i: subset i / (4 VWL),
+    // word (i / 4) % VWL, nibble i % 4, operands built one MFMA ahead
+    unsigned vw[WV][VWL];
+#pragma unroll
+    for (int s = 0; s < WV; ++s)
 #pragma unroll
       for (int w = 0; w < VWL; ++w) {
         unsigned word = 0u;
 #pragma unroll
         for (int p = 0; p < VB; ++p)
-          if (mask >> p & 1) word ^= cur.vp[p][w];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = 4 * w + r;
-          acc[set][q] = mfma16(af, bit_operand(word, r), acc[set][q]);
-          if (r & 1) __builtin_amdgcn_sched_barrier(0);
-        }
+          if (walsh_mask(VB, s) >> p & 1) word ^= cur.vp[p][w];
+        vw[s][w] = word;
       }
+    constexpr int NVI = 4 * VWL * WV;
+    auto vop = [&](int i) { return bit_operand(vw[i / (4 * VWL)][(i / 4) % VWL], i % 4); };
+    u32x4 vop_next[2] = {vop(0), vop(1)};  // operands two MFMAs ahead
+#pragma unroll
+    for (int i = 0; i < NVI; ++i) {
+      const int s = i / (4 * VWL), q = i % (4 * VWL);
+      const u32x4 op = vop_next[i % 2];
+      if (i + 2 < NVI) vop_next[i % 2] = vop(i + 2);
+      int ver = 0;  // weight version of subset s: 0 for a lead, else its rank among the others
+#pragma unroll
+      for (int t = 0; t <= s; ++t)
+        if (!walsh_is_lead(VB, NSET, t)) ++ver;
+      if (walsh_is_lead(VB, NSET, s)) ver = 0;
+      const int set = walsh_set(VB, NSET, s);
+      acc[set][q] = mfma16(af[ver], op, acc[set][q]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     wacc = mfma16(a_lead, ones, wacc);
     return 0;
@@ -1065,8 +1101,8 @@ tq_status plan_decode(const tq_attn_shape* s, const tq_quantizer* k0, const tq_q
   const int nwq = p->k_qjl ? (d >= 128 ? d / 128 : 1) : 0;
   p->k_words = nwm + nwq;
   const int64_t units = (int64_t)p->batch * p->n_kv_heads * p->n_chunks;
-  // aim for about 16 waves per CU in total, splits of at least 256 tokens
-  const int64_t target = (int64_t)16 * device_cus();
+  // one round of waves (the main kernel holds 8 per CU), splits of at least 256 tokens
+  const int64_t target = (int64_t)8 * device_cus();
   int64_t ns = (target + units - 1) / units;
   const int64_t max_splits = (p->max_ctx + 255) / 256;
   if (ns > max_splits) ns = max_splits;
