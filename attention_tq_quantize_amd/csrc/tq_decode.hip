@@ -521,6 +521,33 @@ constexpr int kEvUnset = 40;
 // and the 0/1-to-sign correction are applied once, after the loop.
 constexpr int kWRow = 40;  // dwords per (version, head) row: hi pairs [0,16), lo pairs [16,32), padding
 
+// Raw cache bytes of one 32-token chunk of one (batch, kv head) as the main loop
+// stages them in LDS: key codes, QJL signs, key norms, residual norms, value
+// norms (128 bytes each) and the 32-token value block, each contiguous in HBM.
+// DEPTH chunks per wave are in flight (buffer-to-LDS loads, no registers held);
+// the depth is the largest of 3, 2, 1 that leaves room for two workgroups per
+// CU next to the score fragments and the weight transpose, else 0 (registers,
+// one chunk ahead).
+template <int D, int PK, bool QJL, int VB, int NSET>
+struct DecRing {
+  static constexpr int KREC = PK * D / 8, SREC = D / 8;
+  static constexpr int OFF_S = 32 * KREC;
+  static constexpr int OFF_NK = OFF_S + (QJL ? 32 * SREC : 0);
+  static constexpr int OFF_GM = OFF_NK + 128;
+  static constexpr int OFF_NV = OFF_GM + (QJL ? 128 : 0);
+  static constexpr int OFF_V = OFF_NV + 128;
+  static constexpr int BYTES = OFF_V + 4 * VB * D;
+  static constexpr int WAVES = kThreads / 64;
+  static constexpr int FIXED =
+      KWords<D, PK, QJL>::NF * 64 * 16 + WAVES * (1 + n_walsh(VB) - NSET) * 8 * kWRow * 4;
+  static constexpr int kBudget = 80 * 1024;  // bytes per workgroup: two per CU
+  static constexpr int fits(int r) { return FIXED + r * WAVES * BYTES <= kBudget; }
+  static constexpr int DEPTH = fits(3) ? 3 : fits(2) ? 2 : fits(1) ? 1 : 0;
+  // 16-byte buffer-to-LDS loads per chunk (each segment a multiple of 128 bytes)
+  static constexpr int segs(int bytes) { return (bytes + 1023) / 1024; }
+  static constexpr int LOADS = (PK > 0 ? segs(32 * KREC) : 0) + (QJL ? segs(32 * SREC) + 1 : 0) + 2 + segs(4 * VB * D);
+};
+
 template <int D, int PK, bool QJL, int VB, int NSET>
 __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams prm) {
   using KW = KWords<D, PK, QJL>;
@@ -615,6 +642,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
     unsigned ksg[2][KW::NWQ > 0 ? KW::NWQ : 1];
     unsigned vp[VB][VWL];
     float nk[2], gm[2], nv[2];
+    // an empty asm per register: a chunk that runs again after a rescale is
+    // not loop-invariant to the compiler, which would otherwise hoist every
+    // value derived from it out of the rerun loop (and spill them)
+    __device__ void opaque() {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int p = 0; p < (PK > 0 ? PK : 1); ++p)
+#pragma unroll
+          for (int w = 0; w < WPP; ++w) asm volatile("" : "+v"(kpl[t][p][w]));
+#pragma unroll
+        for (int w = 0; w < (KW::NWQ > 0 ? KW::NWQ : 1); ++w) asm volatile("" : "+v"(ksg[t][w]));
+        asm volatile("" : "+v"(nk[t]), "+v"(gm[t]), "+v"(nv[t]));
+      }
+#pragma unroll
+      for (int p = 0; p < VB; ++p)
+#pragma unroll
+        for (int w = 0; w < VWL; ++w) asm volatile("" : "+v"(vp[p][w]));
+    }
   };
   auto load_chunk = [&](unsigned rel, Chunk& c) {  // rel = chunk start - t0 (multiple of 32)
 #pragma unroll
@@ -662,13 +708,90 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   };
 
   const unsigned n_rel = (unsigned)(t1 > t0 ? t1 - t0 : 0);
+
+  using RG = DecRing<D, PK, QJL, VB, NSET>;
+  constexpr int DEPTH = RG::DEPTH;
+  // the wave's ring of DEPTH staged chunks
+  __shared__ __attribute__((aligned(16))) uint8_t ring[RG::WAVES][DEPTH > 0 ? DEPTH : 1][DEPTH > 0 ? RG::BYTES : 16];
+  // ring loads: byte ranges of each cache array over this split
+  const i32x4 qk = make_rsrc4(prm.kcodes + tok0 * KREC, span * KREC);
+  const i32x4 qs = make_rsrc4(QJL ? prm.ksigns + tok0 * SREC : prm.kcodes, QJL ? span * SREC : 0u);
+  const i32x4 qn = make_rsrc4(prm.knorms + tok0, span * 4);
+  const i32x4 qr = make_rsrc4(QJL ? prm.krnorms + tok0 : prm.knorms, QJL ? span * 4 : 0u);
+  const i32x4 qvn = make_rsrc4(prm.vnorms + tok0, span * 4);
+  const i32x4 qv = make_rsrc4(prm.vcodes + (grp * (prm.max_ctx / 32) + t0 / 32) * (int64_t)VBLK, (span / 32) * VBLK);
+  // bytes [off, off + n) of r into dst, 16 bytes per lane per load; lane 0 is
+  // active in every load, so each counts once in vmcnt (RG::LOADS per chunk)
+  auto dma = [&](const i32x4& r, unsigned off, uint8_t* dst, auto NC) {
+    constexpr int n = decltype(NC)::value;
+    const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_ptr)dst);
+#pragma unroll
+    for (int i = 0; i < n; i += 1024) {
+      if (n - i >= 1024 || lane < (n - i) / 16) lds_load16(r, off + (unsigned)(i + 16 * lane), lds + i);
+    }
+  };
+  auto issue_chunk = [&](unsigned rel, uint8_t* dst) {
+    if constexpr (PK > 0) dma(qk, rel * KREC, dst, std::integral_constant<int, 32 * KREC>{});
+    if constexpr (QJL) dma(qs, rel * SREC, dst + RG::OFF_S, std::integral_constant<int, 32 * SREC>{});
+    dma(qn, rel * 4, dst + RG::OFF_NK, std::integral_constant<int, 128>{});
+    if constexpr (QJL) dma(qr, rel * 4, dst + RG::OFF_GM, std::integral_constant<int, 128>{});
+    dma(qvn, rel * 4, dst + RG::OFF_NV, std::integral_constant<int, 128>{});
+    dma(qv, (rel / 32) * VBLK, dst + RG::OFF_V, std::integral_constant<int, VBLK>{});
+  };
+  // this lane's words of a staged chunk (the same offsets load_chunk reads in HBM)
+  auto read_chunk = [&](const uint8_t* src, Chunk& c) {
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      if constexpr (PK > 0) {
+#pragma unroll
+        for (int p = 0; p < PK; ++p)
+#pragma unroll
+          for (int w = 0; w < WPP; ++w) {
+            const unsigned o = k_off + 16 * tile * KREC + p * (D / 8) + 4 * w;
+            const unsigned x = *(const unsigned*)(src + (o & ~3u));
+            c.kpl[tile][p][w] = (D >= 128) ? x : ((o & 2u) ? (x >> 16) : (x & 0xFFFFu));
+          }
+      }
+      if constexpr (QJL) {
+#pragma unroll
+        for (int Wq = 0; Wq < KW::NWQ; ++Wq) {
+          const unsigned o = s_off + 16 * tile * SREC + 4 * Wq;
+          const unsigned x = *(const unsigned*)(src + RG::OFF_S + (o & ~3u));
+          c.ksg[tile][Wq] = (D >= 128) ? x : ((o & 2u) ? (x >> 16) : (x & 0xFFFFu));
+        }
+      }
+      c.nk[tile] = *(const float*)(src + RG::OFF_NK + n_off + 64 * tile);
+      c.gm[tile] = QJL ? *(const float*)(src + RG::OFF_GM + n_off + 64 * tile) : 0.f;
+      c.nv[tile] = *(const float*)(src + RG::OFF_NV + n_off + 64 * tile);
+    }
+#pragma unroll
+    for (int p = 0; p < VB; ++p) {
+      const uint8_t* vsrc = src + RG::OFF_V + p * (4 * D) + v_off;
+      if constexpr (VWL == 1) {
+        c.vp[p][0] = *(const unsigned*)vsrc;
+      } else if constexpr (VWL == 2) {
+        const uint2 t = *(const uint2*)vsrc;
+        c.vp[p][0] = t.x;
+        c.vp[p][1] = t.y;
+      } else {
+        const uint4 t = *(const uint4*)vsrc;
+        c.vp[p][0] = t.x;
+        c.vp[p][1] = t.y;
+        c.vp[p][2] = t.z;
+        c.vp[p][3] = t.w;
+      }
+    }
+  };
+
   int pend = 0;                       // 1: raise the running max; 2: lower the value exponent
   float pend_val[2] = {0.f, 0.f};     // lane values per head that triggered it
   unsigned (*wrow)[8][kWRow] = wt_lds[wave];
 
   // One chunk: 0 = accumulated, otherwise the pend code (nothing accumulated).
-  auto step = [&](unsigned rel, const Chunk& cur, auto mask_c) -> int {
-    constexpr bool MASK = decltype(mask_c)::value;  // the chunk runs past the context
+  // mask: the chunk runs past the context; mid() runs once per chunk (first
+  // pass), after the key phase has consumed the chunk's key words
+  auto step = [&](unsigned rel, Chunk& cur, bool mask, bool first, auto&& mid) -> int {
+    cur.opaque();
     // ---------------- scores: two tiles of 16 tokens ----------------
     f32x4 cm[2], cq[2];
 #pragma unroll
@@ -730,6 +853,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
       // keep the operand construction next to its MFMAs (hoisting it all costs registers)
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (first) mid();
     // this lane: token 16 t + r16 of the chunk, heads 2g (rows 4g, 4g+1) and 2g + 1 (rows 4g+2, 4g+3);
     // raw scores sr = score 2^E (the operand exponent is applied in the exp2 argument)
     float sr[2][2];
@@ -742,7 +866,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
         float sc = cmv[2 * hh] + cmv[2 * hh + 1];
         if constexpr (QJL) sc = fmaf(cur.gm[tile], cqv[2 * hh] + cqv[2 * hh + 1], sc);
         sr[tile][hh] = cur.nk[tile] * sc;
-        if constexpr (MASK) {
+        if (mask) {
           if (rel + 16 * tile + r16 >= n_rel) sr[tile][hh] = -INFINITY;
         }
       }
@@ -761,7 +885,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
       for (int hh = 0; hh < 2; ++hh) {
         pk[tile][hh] = __builtin_amdgcn_exp2f(fmaf(sr[tile][hh], isc[hh], -mk[hh]));  // p 2^(ev - e_slot)
         float w = pk[tile][hh] * cur.nv[tile];
-        if constexpr (MASK) w = pk[tile][hh] > 0.f ? w : 0.f;  // masked tokens may hold garbage norms
+        if (mask) w = pk[tile][hh] > 0.f ? w : 0.f;  // masked tokens may hold garbage norms
         wv[tile][hh] = w;
       }
     const float wm0 = fmaxf(wv[0][0], wv[1][0]), wm1 = fmaxf(wv[0][1], wv[1][1]);
@@ -856,70 +980,88 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   // The hot loop touches the accumulators only with MFMAs. When a chunk needs
   // the running max raised or the value exponent lowered, it is not
   // accumulated: the state is rescaled here and the chunk runs again.
-  unsigned rel = 0;
-  while (true) {
-    if (pend) {
-      // group-wide maxima over the 16 token lanes of this lane group (heads 2g, 2g + 1)
-      float f[2];
+  auto rescale = [&]() {
+    // group-wide maxima over the 16 token lanes of this lane group (heads 2g, 2g + 1)
+    float f[2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float v = pend_val[hh];
+    for (int hh = 0; hh < 2; ++hh) {
+      float v = pend_val[hh];
 #pragma unroll
-        for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-        f[hh] = 1.0f;
-        if (pend == 1) {
-          const float m_new = fmaxf(m_run[hh], v);
-          // 0 on the first chunk (m_run = -inf); the state is still zero then
-          if (m_new > -INFINITY) f[hh] = exp2f(m_run[hh] - m_new);
-          m_run[hh] = m_new;
-        } else {
-          const int e_need = range_exp(v);  // v: the head's largest weight in this chunk
-          const int ev_new = e_need < ev[hh] ? e_need : ev[hh];
-          f[hh] = ldexpf(1.0f, ev_new - ev[hh]);
-          ev[hh] = ev_new;
-        }
-        m_thr[hh] = (m_run[hh] + kRescaleSlack) / isc[hh];
-        mk[hh] = m_run[hh] - ((float)ev[hh] - e_slot);
-        lsum[hh] *= f[hh];
+      for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+      f[hh] = 1.0f;
+      if (pend == 1) {
+        const float m_new = fmaxf(m_run[hh], v);
+        // 0 on the first chunk (m_run = -inf); the state is still zero then
+        if (m_new > -INFINITY) f[hh] = exp2f(m_run[hh] - m_new);
+        m_run[hh] = m_new;
+      } else {
+        const int e_need = range_exp(v);  // v: the head's largest weight in this chunk
+        const int ev_new = e_need < ev[hh] ? e_need : ev[hh];
+        f[hh] = ldexpf(1.0f, ev_new - ev[hh]);
+        ev[hh] = ev_new;
       }
-      // value rows 4g .. 4g+3 of every lane in this group are heads 2g (x, y) and 2g + 1 (z, w)
-#pragma unroll
-      for (int a = 0; a < NACC; ++a)
-#pragma unroll
-        for (int q = 0; q < NT; ++q) {
-          acc[a][q].x *= f[0];
-          acc[a][q].y *= f[0];
-          acc[a][q].z *= f[1];
-          acc[a][q].w *= f[1];
-        }
-      wacc.x *= f[0];
-      wacc.y *= f[0];
-      wacc.z *= f[1];
-      wacc.w *= f[1];
-      pend = 0;
+      m_thr[hh] = (m_run[hh] + kRescaleSlack) / isc[hh];
+      mk[hh] = m_run[hh] - ((float)ev[hh] - e_slot);
+      lsum[hh] *= f[hh];
     }
-    if (rel >= n_rel) break;
-    // ping-pong buffers: the next chunk loads while this one computes
-    const unsigned n_full = n_rel & ~31u;  // chunks that lie inside the context
+    // value rows 4g .. 4g+3 of every lane in this group are heads 2g (x, y) and 2g + 1 (z, w)
+#pragma unroll
+    for (int a = 0; a < NACC; ++a)
+#pragma unroll
+      for (int q = 0; q < NT; ++q) {
+        acc[a][q].x *= f[0];
+        acc[a][q].y *= f[0];
+        acc[a][q].z *= f[1];
+        acc[a][q].w *= f[1];
+      }
+    wacc.x *= f[0];
+    wacc.y *= f[0];
+    wacc.z *= f[1];
+    wacc.w *= f[1];
+  };
+  auto run = [&](unsigned rel, Chunk& cur, auto&& mid) {
+    const bool mask = rel + 32 > n_rel;
+    bool first = true;
+    while ((pend = step(rel, cur, mask, first, mid)) != 0) {
+      rescale();
+      first = false;
+    }
+  };
+  if constexpr (DEPTH == 0) {
+    // registers, ping-pong: the next chunk loads while this one computes
     Chunk ca, cb;
-    load_chunk(rel, ca);
-    while (rel < n_full) {
+    if (n_rel > 0) load_chunk(0, ca);
+    for (unsigned rel = 0; rel < n_rel; rel += 64) {
       if (rel + 32 < n_rel) load_chunk(rel + 32, cb);
-      pend = step(rel, ca, std::false_type{});
-      if (pend) break;
-      rel += 32;
-      if (rel >= n_full) {
-        ca = cb;  // the tail chunk, if any
-        break;
-      }
-      if (rel + 32 < n_rel) load_chunk(rel + 32, ca);
-      pend = step(rel, cb, std::false_type{});
-      if (pend) break;
-      rel += 32;
+      run(rel, ca, [] {});
+      if (rel + 32 >= n_rel) break;
+      if (rel + 64 < n_rel) load_chunk(rel + 64, ca);
+      run(rel + 32, cb, [] {});
     }
-    if (!pend && rel < n_rel) {
-      pend = step(rel, ca, std::true_type{});
-      if (!pend) rel += 32;
+  } else {
+    // LDS ring: chunk c sits in slot c % DEPTH. Before a chunk is read, the
+    // loads of the (up to DEPTH - 1) chunks issued after it may stay in
+    // flight; once its key phase has run, its slot is refilled with chunk
+    // c + DEPTH. One chunk per loop iteration keeps the register allocation
+    // of a single step.
+    for (int j = 0; j < DEPTH; ++j)
+      if (32u * j < n_rel) issue_chunk(32u * j, ring[wave][j]);
+    const unsigned last = (n_rel - 1) / 32;  // index of the split's last chunk
+    int slot = 0;
+    for (unsigned rel = 0; rel < n_rel; rel += 32) {
+      uint8_t* sb = ring[wave][slot];
+      // the debug score stores also count in vmcnt, so that mode waits for all
+      const unsigned ahead = min(last - rel / 32, (unsigned)(DEPTH - 1));
+      if (prm.scores_dbg || ahead == 0) wait_vmcnt<0>();
+      else if (ahead == 1) wait_vmcnt<RG::LOADS>();
+      else wait_vmcnt<(DEPTH > 2 ? 2 : 1) * RG::LOADS>();
+      Chunk cur;
+      read_chunk(sb, cur);
+      run(rel, cur, [&] {
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot's reads have landed
+        if (rel + 32u * DEPTH < n_rel) issue_chunk(rel + 32u * DEPTH, sb);
+      });
+      slot = slot + 1 == DEPTH ? 0 : slot + 1;
     }
   }
 

@@ -161,6 +161,39 @@ __device__ __forceinline__ float swap_pair(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
 }
 
+// s_waitcnt immediate (gfx9 encoding) that waits for lgkmcnt(0) only
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// an LDS address as the buffer/global-to-LDS load builtins take it
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// A raw buffer resource as four SGPRs (48-bit base, 32-bit byte range, no
+// stride) for the LDS loads below, which are written in assembly.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc4(const void* base, unsigned bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return i32x4{(int)(unsigned)a, (int)((a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+// 16 bytes per lane from byte voff of r straight into LDS at lds + 16 lane
+// (lanes past the range load zeros). Written in assembly so that the compiler
+// does not make every later LDS read wait for it: the caller waits with
+// wait_vmcnt before it reads the bytes, and must not overwrite the
+// destination's earlier reads before they have returned. m0 is restored.
+__device__ __forceinline__ void lds_load16(i32x4 r, unsigned voff, unsigned lds) {
+  unsigned save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds), "v"(voff), "s"(r)
+      : "memory");
+}
+// wait until at most N vector memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Buffer resources: a wave-uniform base in SGPRs plus a 32-bit lane offset keeps
 // the hot loop free of 64-bit VGPR address arithmetic (raw buffer, 32-bit data).
 typedef __amdgpu_buffer_rsrc_t buf_t;

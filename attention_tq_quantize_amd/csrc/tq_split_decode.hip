@@ -85,7 +85,6 @@ struct SmParams {
   SmSeg seg[kSmMaxSeg];
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
 
 __device__ __forceinline__ unsigned lds_u32(const uint8_t* p) { return *(const unsigned*)p; }
 
