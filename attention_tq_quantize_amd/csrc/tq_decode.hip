@@ -528,6 +528,13 @@ constexpr int kWRow = 40;  // dwords per (version, head) row: hi pairs [0,16), l
 // the depth is the largest of 3, 2, 1 that leaves room for two workgroups per
 // CU next to the score fragments and the weight transpose, else 0 (registers,
 // one chunk ahead).
+// Score fragments held in registers for the whole split instead of re-read
+// from LDS every chunk: chosen for the shapes where that still compiles
+// without spills at two waves per SIMD.
+__host__ __device__ constexpr bool frag_in_regs(int D, int PK, bool QJL, int VB) {
+  return D == 128 && PK <= 2 && (VB == 3 || (VB == 4 && (QJL || PK < 2)));
+}
+
 template <int D, int PK, bool QJL, int VB, int NSET>
 struct DecRing {
   static constexpr int KREC = PK * D / 8, SREC = D / 8;
@@ -538,8 +545,8 @@ struct DecRing {
   static constexpr int OFF_V = OFF_NV + 128;
   static constexpr int BYTES = OFF_V + 4 * VB * D;
   static constexpr int WAVES = kThreads / 64;
-  static constexpr int FIXED =
-      KWords<D, PK, QJL>::NF * 64 * 16 + WAVES * (1 + n_walsh(VB) - NSET) * 8 * kWRow * 4;
+  static constexpr int FIXED = (frag_in_regs(D, PK, QJL, VB) ? 0 : KWords<D, PK, QJL>::NF * 64 * 16) +
+                               WAVES * (1 + n_walsh(VB) - NSET) * 8 * kWRow * 4;
   static constexpr int kBudget = 80 * 1024;  // bytes per workgroup: two per CU
   static constexpr int fits(int r) { return FIXED + r * WAVES * BYTES <= kBudget; }
   static constexpr int DEPTH = fits(3) ? 3 : fits(2) ? 2 : fits(1) ? 1 : 0;
@@ -560,7 +567,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   constexpr int SREC = D / 8;
   constexpr int VBLK = 4 * VB * D;  // bytes of one 32-token value block
   constexpr int WPP = D >= 128 ? D / 128 : 1;
-  constexpr bool KF_REG = false;  // score fragments in registers (else LDS)
+  constexpr bool KF_REG = frag_in_regs(D, PK, QJL, VB);  // score fragments in registers (else LDS)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
