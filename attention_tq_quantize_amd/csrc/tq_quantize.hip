@@ -85,8 +85,37 @@ __device__ __forceinline__ void load_tile(const uint8_t* base, unsigned rel, int
   for (int i = 0; i < XTile<D, XF32>::NR; ++i) t.raw[i] = src[i];
 }
 
+// This lane's part of |x|^2 for bf16 input, exactly in fp64 (the fallback of
+// tile_operands for tiny or huge vectors).
+template <int D>
+__device__ __forceinline__ double sumsq_bf16_exact(const XTile<D, false>& t) {
+  double acc = 0.0;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    const u32x4 v = t.raw[ks];
+    const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = bf16_val(w[e] & 0xFFFFu), b = bf16_val(w[e] >> 16);
+      acc = fma((double)a, (double)a, acc);
+      acc = fma((double)b, (double)b, acc);
+    }
+  }
+  return acc;
+}
+
+// |x|^2 of bf16 input from the fast part sums is used when it lies in
+// [2^-90, 2^100]: there no square is subnormal or infinite in fp32 enough to
+// matter (the ones below 2^-126 add at most 2^-119 in all), and the result
+// keeps the bound of tile_operands.
+constexpr double kSumsqFastLo = 0x1p-90, kSumsqFastHi = 0x1p100;
+
 // MFMA operands of a tile (K index 8g + e of k-step ks <-> coordinate
-// g D/4 + 8 ks + e) and this lane's part of |x|^2 in fp64.
+// g D/4 + 8 ks + e) and this lane's part of |x|^2. fp32 input: fp64 fma per
+// coordinate. bf16 input: the two squares of a dword are exact in fp32 and
+// v_dot2 adds them to its accumulator with one rounding; a chain of two covers
+// four coordinates and the partials are added in fp64, so the relative error
+// is at most about 2^-23 (the norm's about 2^-24, within one fp32 ulp).
 template <int D, bool XF32>
 __device__ __forceinline__ double tile_operands(const XTile<D, XF32>& t, u32x4* xh, u32x4* xl) {
   constexpr int NK = D / 32;
@@ -94,15 +123,18 @@ __device__ __forceinline__ double tile_operands(const XTile<D, XF32>& t, u32x4* 
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) {
     if constexpr (!XF32) {
+      typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
       const u32x4 v = t.raw[ks];
       xh[ks] = v;
       const unsigned w[4] = {v.x, v.y, v.z, v.w};
+      float q[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float a = bf16_val(w[e] & 0xFFFFu), b = bf16_val(w[e] >> 16);
-        acc = fma((double)a, (double)a, acc);
-        acc = fma((double)b, (double)b, acc);
+      for (int e = 0; e < 2; ++e) {
+        const bf2 h0 = __builtin_bit_cast(bf2, w[2 * e]), h1 = __builtin_bit_cast(bf2, w[2 * e + 1]);
+        q[e] = __builtin_amdgcn_fdot2_f32_bf16(h1, h1, __builtin_amdgcn_fdot2_f32_bf16(h0, h0, 0.0f, false), false);
       }
+      acc += (double)q[0];
+      acc += (double)q[1];
     } else {
       const u32x4 u0 = t.raw[2 * ks], u1 = t.raw[2 * ks + 1];
       const float f[8] = {__uint_as_float(u0.x), __uint_as_float(u0.y), __uint_as_float(u0.z), __uint_as_float(u0.w),
@@ -305,6 +337,14 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD)) void quantize
       ss[t] = tile_operands<D, XF32>(cur[t], xh[t], xl[t]);
       ss[t] += __shfl_xor(ss[t], 16);
       ss[t] += __shfl_xor(ss[t], 32);
+      if constexpr (!XF32) {
+        // the four lanes of a vector share ss, so they take this branch together
+        if (!(ss[t] >= kSumsqFastLo && ss[t] <= kSumsqFastHi)) {
+          ss[t] = sumsq_bf16_exact<D>(cur[t]);
+          ss[t] += __shfl_xor(ss[t], 16);
+          ss[t] += __shfl_xor(ss[t], 32);
+        }
+      }
     }
     const int64_t v0 = step * 16 * T;  // first vector of this step
 
