@@ -30,6 +30,7 @@ EXPORTS = [
     "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_append_workspace_size",
     "tq_decode_append_attention", "tq_search_workspace_size", "tq_search_scores", "tq_quantize_split",
     "tq_inner_products_split", "tq_decode_split_workspace_size", "tq_decode_attention_split",
+    "tq_decode_attention_noalloc",
 ]
 
 
@@ -105,6 +106,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                              ctypes.POINTER(PackedKV), ctypes.POINTER(ctypes.c_size_t)]
     lib.tq_decode_attention.argtypes = [ctypes.POINTER(AttnShape), _VP, ctypes.POINTER(PackedKV),
                                         ctypes.POINTER(PackedKV), _VP, _F, _VP, _VP, _VP, ctypes.c_size_t, _VP]
+    lib.tq_decode_attention_noalloc.argtypes = [ctypes.POINTER(AttnShape), _VP, ctypes.POINTER(PackedKV),
+                                                ctypes.POINTER(PackedKV), _VP, _F, _VP, _VP, _VP]
     lib.tq_decode_append_workspace_size.argtypes = [ctypes.POINTER(AttnShape), ctypes.POINTER(PackedKV),
                                                     ctypes.POINTER(PackedKV), ctypes.POINTER(ctypes.c_size_t)]
     lib.tq_decode_append_attention.argtypes = [ctypes.POINTER(AttnShape), _VP, _VP, _VP, _I,
@@ -548,6 +551,36 @@ def decode_attention(q, kcache: KVCache, vcache: KVCache, ctx_lens, scale: Optio
     _check(lib.tq_decode_attention(ctypes.byref(shape), _ptr(q), ctypes.byref(kp), ctypes.byref(vp),
                                    _ptr(ctx_lens), float(scale), _ptr(out), _ptr(scores), _ptr(workspace),
                                    workspace.numel(), _stream(stream)), "tq_decode_attention")
+    return out
+
+
+def decode_attention_noalloc(q, kcache: KVCache, vcache: KVCache, ctx_lens, out, scale: Optional[float] = None,
+                             max_ctx: Optional[int] = None, scores=None, stream=None):
+    """decode_attention through tq_decode_attention_noalloc: the library's static
+    per-GPU scratch instead of a workspace, and a caller-provided out [B, Hq, d]
+    float32, so the call allocates nothing. Calls that overlap on one GPU race."""
+    import torch
+    lib = load()
+    B, Hq, d = q.shape
+    Hkv = len(kcache.qz)
+    T = int(max_ctx if max_ctx is not None else kcache.norms.shape[-1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check_decode_args(q, ctx_lens, B, Hkv, d, T, kcache, vcache)
+    _need_dtype(out, torch.float32, "out")
+    _need_cuda(out, "out")
+    _need_bytes(out, B * Hq * d * 4, "out")
+    if not q.is_contiguous() or not out.is_contiguous():
+        raise ValueError("decode_attention_noalloc: q and out must be contiguous")
+    if scores is not None:
+        _need_dtype(scores, torch.float32, "scores")
+        _need_bytes(scores, B * Hq * T * 4, "scores")
+    shape = AttnShape(B, Hq, Hkv, d, T)
+    kp, ka = kcache.packed()
+    vp, va = vcache.packed()
+    _check(lib.tq_decode_attention_noalloc(ctypes.byref(shape), _ptr(q), ctypes.byref(kp), ctypes.byref(vp),
+                                           _ptr(ctx_lens), float(scale), _ptr(out), _ptr(scores), _stream(stream)),
+           "tq_decode_attention_noalloc")
     return out
 
 

@@ -712,6 +712,24 @@ tq_status tq_decode_attention(const tq_attn_shape* shape, const void* q, const t
   return launch_decode(p, q, k, v, ctx_lens, scale, out, scores_dbg, workspace, (hipStream_t)stream);
 }
 
+tq_status tq_decode_attention_noalloc(const tq_attn_shape* shape, const void* q, const tq_packed_kv* k,
+                                      const tq_packed_kv* v, const int32_t* ctx_lens, float scale,
+                                      float* out, float* scores_dbg, void* stream) {
+  DecodePlan p;
+  tq_status st = check_decode(shape, k, v, &p);
+  if (st != TQ_OK) return st;
+  if (!q || !ctx_lens || !out) return set_error(TQ_ERR_INVALID_ARG, "decode_noalloc: q, ctx_lens or out is NULL");
+  if (!std::isfinite(scale)) return set_error(TQ_ERR_INVALID_ARG, "decode_noalloc: scale is not finite");
+  if (p.total_bytes > kNoAllocScratchBytes)
+    return set_error(TQ_ERR_WORKSPACE, fmt("decode_noalloc: the call needs %zu bytes of scratch, the static scratch "
+                                           "holds %zu; use tq_decode_attention with a workspace",
+                                           p.total_bytes, kNoAllocScratchBytes));
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != TQ_OK) return st;
+  return launch_decode(p, q, k, v, ctx_lens, scale, out, scores_dbg, ws, (hipStream_t)stream);
+}
+
 // Append workspace: the same as the plain decode's (the new records go straight
 // into the caches; the attended length is formed in the main kernel)
 static size_t append_workspace(const DecodePlan& p) { return p.total_bytes; }

@@ -34,6 +34,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 
 #include "tq_device.h"
@@ -1419,5 +1420,39 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
   });
 }
 
+
+// ---------------------------------------------------------------------------
+// Scratch of tq_decode_attention_noalloc: the decode workspace (score
+// fragments, constants and split partials) as a file-scope device array, for
+// callers that cannot allocate. Each GPU the library runs on holds its own
+// copy until the process ends. In host code "scratch" names a host-side
+// stand-in; the device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current, and only that address is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+tq_status noalloc_scratch(void** ptr) {
+  int dev = -1;
+  tq_status st = check_hip(hipGetDevice(&dev), "noalloc: hipGetDevice");
+  if (st != TQ_OK) return st;
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return set_error(TQ_ERR_UNSUPPORTED, "noalloc: device index " + std::to_string(dev) + " out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    st = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "noalloc: hipGetSymbolAddress(scratch)");
+    if (st != TQ_OK) return st;
+    if (!p) return set_error(TQ_ERR_DEVICE, "noalloc: scratch has no device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return TQ_OK;
+}
 
 }  // namespace tq

@@ -174,4 +174,9 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
                         float* scores_dbg, void* workspace, hipStream_t stream,
                         const AppendLaunch* app = nullptr);
 
+// Device address of the no-alloc decode scratch on the current device
+// (kNoAllocScratchBytes bytes; looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+tq_status noalloc_scratch(void** ptr);
+
 }  // namespace tq

@@ -341,6 +341,24 @@ tq_status tq_decode_attention(const tq_attn_shape* shape, const void* q, const t
                               void* stream);
 
 /*
+ * Decode attention that allocates nothing: tq_decode_attention with the
+ * workspace taken from a static device array of the library (32 MiB per GPU,
+ * held by each GPU the library runs on until the process ends). For callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. It calls no allocating
+ * routine. Arguments, layouts and results are those of tq_decode_attention
+ * (same kernels, same split schedule, so the same output bits).
+ * Every call on one GPU shares that GPU's array (it keeps the last call's
+ * partials; nothing in it needs to start at zero): calls that overlap on one
+ * GPU, on any streams, race and must be serialized by the caller.
+ * Errors: as tq_decode_attention, and TQ_ERR_WORKSPACE when the shape needs
+ * more than 32 MiB of scratch (tq_decode_workspace_size() tells how much).
+ */
+tq_status tq_decode_attention_noalloc(const tq_attn_shape* shape, const void* q, const tq_packed_kv* k,
+                                      const tq_packed_kv* v, const int32_t* ctx_lens, float scale,
+                                      float* out, float* scores_dbg, void* stream);
+
+/*
  * Decode step with append: the online use of the quantizer ([NIK] "Step 0" to
  * "Step 2": vector in, code out, nothing to train; for prod keys also "TurboQuant
  * proper") followed by the attention step that reads the cache ([NAH]: the prod
