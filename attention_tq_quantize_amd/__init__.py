@@ -587,19 +587,31 @@ def decode_attention_noalloc(q, kcache: KVCache, vcache: KVCache, ctx_lens, out,
 @dataclass
 class SplitKV:
     """One side (keys or values) of a split cache: parts[p] = (quantizers per KV head,
-    channel list, records dict of device tensors [B, Hkv, T, ...] / [B, Hkv, T])."""
+    channels, records dict of device tensors [B, Hkv, T, ...] / [B, Hkv, T]).
+    channels: [Hkv][d_p] (each KV head's own list) or [d_p] (the same list for
+    every head)."""
     parts: Sequence[tuple]
 
     def packed(self, n_kv_heads):
         import numpy as np
         P = len(self.parts)
         qz = (ctypes.c_void_p * (P * n_kv_heads))()
-        for p, (qs, _, _) in enumerate(self.parts):
-            assert len(qs) == n_kv_heads
+        lists = []
+        for p, (qs, c, _) in enumerate(self.parts):
+            if len(qs) != n_kv_heads:
+                raise ValueError(f"split part {p}: {len(qs)} quantizers for {n_kv_heads} KV heads")
             for g, q in enumerate(qs):
                 qz[p * n_kv_heads + g] = q.handle.value
-        ch = np.ascontiguousarray(np.concatenate([np.asarray(c, dtype=np.int32).ravel() for _, c, _ in self.parts]),
-                                  dtype=np.int32)
+            c = np.asarray(c, dtype=np.int32)
+            d_p = qs[0].d
+            if c.ndim == 1:
+                c = np.broadcast_to(c, (n_kv_heads, c.shape[0]))
+            if c.shape != (n_kv_heads, d_p):
+                raise ValueError(f"split part {p}: channels must be [{n_kv_heads}][{d_p}] or [{d_p}], "
+                                 f"got {list(c.shape)}")
+            lists.append(c.reshape(-1))
+        # [n_parts][n_kv_heads][d_p], as tq_split_cache.channels
+        ch = np.ascontiguousarray(np.concatenate(lists), dtype=np.int32)
         recs = _records([r for _, _, r in self.parts])
         sc = SplitCache(P, qz, ch.ctypes.data, ctypes.cast(recs, ctypes.c_void_p))
         return sc, (qz, ch, recs)  # keep the arrays alive for the call

@@ -576,12 +576,25 @@ static tq_status check_split_side(const tq_split_cache* c, const tq_attn_shape* 
     off += q0->d;
   }
   if (off > s->head_dim) return set_error(TQ_ERR_INVALID_ARG, fmt("%s: parts cover %d channels of %d", what, off, s->head_dim));
-  std::vector<char> seen(s->head_dim, 0);
-  for (int j = 0; j < off; ++j) {
-    const int ch = c->channels[j];
-    if (ch < 0 || ch >= s->head_dim) return set_error(TQ_ERR_INVALID_ARG, fmt("%s: channels[%d]=%d out of range", what, j, ch));
-    if (seen[ch]) return set_error(TQ_ERR_INVALID_ARG, fmt("%s: channel %d listed twice", what, ch));
-    seen[ch] = 1;
+  // channels [n_parts][n_kv_heads][d_p]: every KV head's lists over the parts
+  // are in range and repeat no channel
+  for (int g = 0; g < s->n_kv_heads; ++g) {
+    std::vector<char> seen(s->head_dim, 0);
+    int po = 0;
+    for (int p = 0; p < c->n_parts; ++p) {
+      const int dp = c->qz[p * s->n_kv_heads]->d;
+      for (int j = 0; j < dp; ++j) {
+        const int64_t at = (int64_t)s->n_kv_heads * po + (int64_t)g * dp + j;
+        const int ch = c->channels[at];
+        if (ch < 0 || ch >= s->head_dim)
+          return set_error(TQ_ERR_INVALID_ARG, fmt("%s: channels[%lld]=%d (part %d, KV head %d) out of range", what,
+                                                   (long long)at, ch, p, g));
+        if (seen[ch])
+          return set_error(TQ_ERR_INVALID_ARG, fmt("%s: KV head %d lists channel %d twice", what, g, ch));
+        seen[ch] = 1;
+      }
+      po += dp;
+    }
   }
   *total = off;
   return TQ_OK;

@@ -79,7 +79,7 @@ struct SmParams {
   int* qexp;     // [B * Hkv][2][8]: their power-of-two scales per (kind, head)
   int stage_bytes, tab_off, wave_off, wave_bytes;  // LDS layout (bytes); fragments at 0
   int prep_rows;  // matrix rows the prep kernel stages per block
-  uint8_t kchan[kSplitMaxDecodeDim], vchan[kSplitMaxDecodeDim];
+  uint8_t kchan[kSplitMaxKv][kSplitMaxDecodeDim], vchan[kSplitMaxKv][kSplitMaxDecodeDim];  // per KV head
   uint8_t vword_part[kSplitMaxDecodeDim / 32];  // value part of each 32-coordinate word
   SmPart kp[kSplitMaxParts], vp[kSplitMaxParts];
   SmSeg seg[kSmMaxSeg];
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kSmThreads) void split_prep_kernel(SmParams prm) {
   float* mat = qs + G * prm.dk;         // [2][prep_rows][d + 1] rows of Pi and S
   for (int e = tid; e < G * prm.dk; e += kSmThreads) {
     const int h = e / prm.dk, j = e % prm.dk;
-    qraw[e] = __uint_as_float((unsigned)prm.q[((int64_t)b * prm.Hq + g * G + h) * prm.dim + prm.kchan[j]] << 16);
+    qraw[e] = __uint_as_float((unsigned)prm.q[((int64_t)b * prm.Hq + g * G + h) * prm.dim + prm.kchan[g][j]] << 16);
   }
   for (int p = 0; p < prm.nk; ++p) {
     const SmPart& P = prm.kp[p];
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(kSmThreads) void split_combine_kernel(SmParams prm)
       const float* pc = P.pi[g] + j;
 #pragma unroll 8
       for (int i = 0; i < P.d; ++i) v = fmaf(pc[(int64_t)i * P.d], a[P.off + i], v);
-      o[prm.vchan[P.off + j]] = v;
+      o[prm.vchan[g][P.off + j]] = v;
     }
   }
 }
@@ -636,7 +636,7 @@ static void build_split_params(const SplitDecodeLaunch& L, SmParams& prm, size_t
   for (int side = 0; side < 2; ++side) {
     const SplitSide& S = side == 0 ? L.k : L.v;
     SmPart* dst = side == 0 ? prm.kp : prm.vp;
-    uint8_t* chan = side == 0 ? prm.kchan : prm.vchan;
+    uint8_t (*chan)[kSplitMaxDecodeDim] = side == 0 ? prm.kchan : prm.vchan;
     int off = 0;
     for (int p = 0; p < S.n_parts; ++p) {
       const tq_quantizer* q0 = S.qz[p * L.Hkv];
@@ -662,7 +662,9 @@ static void build_split_params(const SplitDecodeLaunch& L, SmParams& prm, size_t
         P.pi[g] = S.qz[p * L.Hkv + g]->pi32;
         P.s[g] = S.qz[p * L.Hkv + g]->s32;
       }
-      for (int j = 0; j < P.d; ++j) chan[off + j] = (uint8_t)S.channels[off + j];
+      // channels [n_parts][n_kv_heads][d_p]: part p of head g starts at Hkv off + g d_p
+      for (int g = 0; g < L.Hkv; ++g)
+        for (int j = 0; j < P.d; ++j) chan[g][off + j] = (uint8_t)S.channels[(int64_t)L.Hkv * off + g * P.d + j];
       if (side == 1)
         for (int w = off / 32; w < (off + P.d) / 32; ++w) prm.vword_part[w] = (uint8_t)p;
       off += P.d;

@@ -271,8 +271,8 @@ def decode_1m(tq, syn, torch, dev, reps=20):
 
 def outlier_split_decode(tq, syn, torch, dev, reps=10, bits=(3, 2)):
     """Decode attention over an outlier-split cache at the 128K batch shape (B=8,
-    64/8 heads, d=128, ctx 131072): keys TurboQuant_prod with the 32 largest-RMS
-    channels at bits[0] and the other 96 at bits[1], values TurboQuant_mse with the
+    64/8 heads, d=128, ctx 131072): keys TurboQuant_prod with each KV head's 32
+    largest-RMS channels at bits[0] and the other 96 at bits[1], values TurboQuant_mse with the
     same bit split (3 + 2 bits: 96 B per (token, KV head) against 108 B for the
     uniform 3-bit cache; 4 + 3 bits: 128 B); tq_decode_attention_split (matrix-core
     split kernels)."""
@@ -280,10 +280,11 @@ def outlier_split_decode(tq, syn, torch, dev, reps=10, bits=(3, 2)):
     sides = []
     for tensor, var in ((syn.T_K, "prod"), (syn.T_V, "mse")):
         qs_p = [[], []]
-        chans_p = [None, None]
+        # every KV head keeps its own 32 largest-RMS channels (batch-0 sample of that head)
         sample = syn.kv_vectors_device(Hkv, 4096, d, syn.CFG_DECODE_128K, tensor, dev, seed_offset=0)
-        order = torch.argsort(sample[0].float().pow(2).mean(dim=0), descending=True, stable=True).cpu().numpy()
-        chans_p = [order[:32], order[32:]]
+        order = torch.argsort(sample.float().pow(2).mean(dim=1), dim=1, descending=True, stable=True).cpu().numpy()
+        chans_p = [order[:, :32], order[:, 32:]]  # [Hkv][d_p] per part
+        del sample
         for p, pbits in enumerate(bits):
             dp = len(chans_p[p])
             for g in range(Hkv):
@@ -301,7 +302,7 @@ def outlier_split_decode(tq, syn, torch, dev, reps=10, bits=(3, 2)):
         for b in range(B):
             x = syn.kv_vectors_device(Hkv, T, d, syn.CFG_DECODE_128K, tensor, dev, seed_offset=b)
             for g in range(Hkv):
-                got = tq.quantize_split([qs_p[0][g], qs_p[1][g]], chans_p, x[g])
+                got = tq.quantize_split([qs_p[0][g], qs_p[1][g]], [chans_p[0][g], chans_p[1][g]], x[g])
                 for p in range(2):
                     for key, val in got[p].items():
                         recs[p][key][b, g].copy_(val.view(recs[p][key][b, g].shape))

@@ -420,8 +420,12 @@ tq_status tq_decode_append_attention(const tq_attn_shape* shape, const void* q, 
  *              qz[p * n_kv_heads + g]; the handles of one part share (d, bits,
  *              variant); d a multiple of 32; keys mse or prod, values mse;
  *              codes and signs 4-byte aligned.
- *   channels : host int32, the parts' channel lists concatenated (entries in
- *              [0, head_dim), none repeated).
+ *   channels : host int32 [n_parts][n_kv_heads][d_p]: part p of KV head g
+ *              keeps the channels channels[n_kv_heads * off_p + g * d_p + j],
+ *              j < d_p, off_p = d_0 + .. + d_{p-1} (coordinate j of that
+ *              part; the order tq_quantize_split was given for that head).
+ *              Heads may pick different channels; within a head every entry
+ *              lies in [0, head_dim) and none repeats. Copied.
  *   rec      : host [n_parts]; rec[p] holds part p's device arrays.
  * head_dim = the full channel count (at most 256), at most 8 KV heads and 8
  * query heads per KV head. q: device bf16 [B][n_q_heads][head_dim];

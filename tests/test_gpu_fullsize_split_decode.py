@@ -1,7 +1,8 @@
 """GPU parity of decode attention over an outlier-split cache at the full
 benchmark size (batch 8, 64/8 heads, head_dim 128, context 131072; keys
-TurboQuant_prod with 32 channels at 3 bits and 96 at 2, values TurboQuant_mse
-with the same split; [NIK] "Experiments", KV cache), in the launch
+TurboQuant_prod with 32 channels at 3 bits and 96 at 2, each KV head with its
+own channel lists, values TurboQuant_mse with the same split; [NIK]
+"Experiments", KV cache), in the launch
 configuration the benchmark times. Two sampled (batch, KV head) groups are
 quantized and packed by the fp64 oracle from seeded vectors with per-token
 LogNormal(0, 0.5) scales; every other group holds seeded random bits and
@@ -45,7 +46,7 @@ def _side(tq, spec, tensor, chans, seed):
             Pi = syn.rotation(n, syn.CFG_DECODE_128K, tensor, 300 + 10 * p + g)
             S = syn.gaussian_matrix(n, syn.CFG_DECODE_128K, tensor, 300 + 10 * p + g) if var == "prod" else None
             qg.append(tq.Quantizer(n, bits, var, Pi, S))
-            part = {"channels": chans[p], "variant": var, "Pi": Pi, "centroids": O.codebook(n, planes)}
+            part = {"channels": chans[p][g], "variant": var, "Pi": Pi, "centroids": O.codebook(n, planes)}
             if S is not None:
                 part["S"] = S
             pg.append(part)
@@ -76,9 +77,12 @@ def _pack_group(x, spec, parts_g, recs, b, g):
 def test_split_decode_full_size(gpu_lib):
     tq = gpu_lib
     print(f"split decode full size B={B} Hq={HQ} Hkv={HKV} d={D} T={T}", flush=True)
-    sample = syn.kv_vectors(4096, D, syn.CFG_DECODE_128K, syn.T_K, 0, 1)
-    order = np.argsort(-np.sqrt(np.mean(sample.astype(np.float64) ** 2, axis=0)), kind="stable")
-    chans = [order[:32], order[32:]]
+    # every KV head keeps its own 32 largest-RMS channels (from a sample of that head)
+    order = np.stack([np.argsort(-np.sqrt(np.mean(syn.kv_vectors(4096, D, syn.CFG_DECODE_128K, syn.T_K, 0, 40 + g)
+                                                  .astype(np.float64) ** 2, axis=0)), kind="stable")
+                      for g in range(HKV)])
+    chans = [order[:, :32], order[:, 32:]]  # per part: [HKV][d_p]
+    assert any(set(chans[0][g]) != set(chans[0][0]) for g in range(1, HKV))
     kq, kparts, krecs = _side(tq, KSPEC, syn.T_K, chans, 4101)
     vq, vparts, vrecs = _side(tq, VSPEC, syn.T_V, chans, 4102)
     oracle = {}

@@ -3,7 +3,8 @@
 more bits) against the oracle's decode_attention_split on oracle-packed
 records: outputs within rtol 1e-3 / atol 1e-4. Cases: the pages' split of a
 128-channel head (32 channels at 3 bits, 96 at 2; prod keys, mse values) with
-GQA 8 and ragged lengths; parts that drop channels, with different channel
+GQA 8 and ragged lengths; every KV head with its own channel lists (its
+largest-RMS channels); parts that drop channels, with different channel
 lists for keys and values, and an empty context; GQA 1 at head_dim 64; every
 plane count of key and value parts; head_dim 256; splits of several chunks."""
 import math
@@ -26,14 +27,16 @@ def _order(x):
 
 
 def _build_side(tq, B, Hkv, T, dim, spec, tensor, seed):
-    """spec: [(n_channels, variant, bits)]; channels picked per side from the RMS
-    order of the first (batch, head) sample (largest first), parts in order."""
-    sample = syn.kv_vectors(T, dim, syn.CFG_TEST, tensor, 0, seed)
-    order = _order(sample)
-    chans, off = [], 0
-    for n, _, _ in spec:
-        chans.append(order[off:off + n])
-        off += n
+    """spec: [(n_channels, variant, bits)]; each KV head picks its own channels
+    from the RMS order of its batch-0 vectors (largest first), parts in order,
+    so heads whose outliers sit elsewhere get different lists."""
+    chans = [np.zeros((Hkv, n), np.int64) for n, _, _ in spec]  # per part: [Hkv][n]
+    for g in range(Hkv):
+        order = _order(syn.kv_vectors(T, dim, syn.CFG_TEST, tensor, 0, seed + g, lognormal_sigma=0.5))
+        off = 0
+        for p, (n, _, _) in enumerate(spec):
+            chans[p][g] = order[off:off + n]
+            off += n
     parts_g, qs = [], []  # per part: list over g of oracle parts / quantizers
     for p, (n, var, bits) in enumerate(spec):
         planes = bits - 1 if var == "prod" else bits
@@ -41,7 +44,7 @@ def _build_side(tq, B, Hkv, T, dim, spec, tensor, seed):
         for g in range(Hkv):
             Pi = syn.rotation(n, syn.CFG_TEST, tensor, 200 + 10 * p + g)
             S = syn.gaussian_matrix(n, syn.CFG_TEST, tensor, 200 + 10 * p + g) if var == "prod" else None
-            part = {"channels": chans[p], "variant": var, "Pi": Pi, "centroids": O.codebook(n, planes)}
+            part = {"channels": chans[p][g], "variant": var, "Pi": Pi, "centroids": O.codebook(n, planes)}
             if S is not None:
                 part["S"] = S
             pg.append(part)
@@ -127,7 +130,12 @@ def test_split_decode_parity(gpu_lib, case):
     for b in range(B):
         if lens[b] == 0:
             assert np.all(got[b] == 0)
-    kept = np.zeros(dim, bool)
-    for _, c, _ in v.parts:
-        kept[np.asarray(c)] = True
-    assert np.all(got[:, :, ~kept] == 0)
+    G = Hq // Hkv
+    for g in range(Hkv):
+        kept = np.zeros(dim, bool)
+        for _, c, _ in v.parts:
+            kept[np.asarray(c)[g]] = True
+        assert np.all(got[:, g * G:(g + 1) * G, ~kept] == 0)
+    if Hkv > 1 and sum(n for n, _, _ in kspec) < dim:
+        # the heads really do keep different channels in this case
+        assert any(not np.array_equal(np.sort(k.parts[0][1][0]), np.sort(k.parts[0][1][g])) for g in range(1, Hkv))
