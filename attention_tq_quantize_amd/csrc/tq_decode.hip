@@ -796,9 +796,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
   unsigned (*wrow)[8][kWRow] = wt_lds[wave];
 
   // One chunk: 0 = accumulated, otherwise the pend code (nothing accumulated).
-  // mask: the chunk runs past the context; mid() runs once per chunk (first
-  // pass), after the key phase has consumed the chunk's key words
-  auto step = [&](unsigned rel, Chunk& cur, bool mask, bool first, auto&& mid) -> int {
+  // mask_c: the chunk runs past the context (only a split's last chunk can);
+  // mid() runs once per chunk (first pass), after the key phase has consumed
+  // the chunk's key words
+  auto step = [&](unsigned rel, Chunk& cur, auto mask_c, bool first, auto&& mid) -> int {
+    constexpr bool MASK = decltype(mask_c)::value;
     cur.opaque();
     // ---------------- scores: two tiles of 16 tokens ----------------
     f32x4 cm[2], cq[2];
@@ -874,14 +876,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
         float sc = cmv[2 * hh] + cmv[2 * hh + 1];
         if constexpr (QJL) sc = fmaf(cur.gm[tile], cqv[2 * hh] + cqv[2 * hh + 1], sc);
         sr[tile][hh] = cur.nk[tile] * sc;
-        if (mask) {
+        if constexpr (MASK) {
           if (rel + 16 * tile + r16 >= n_rel) sr[tile][hh] = -INFINITY;
         }
       }
     }
     // ---------------- online softmax: lane-local checks, no cross-lane work ----------------
     const float mx0 = fmaxf(sr[0][0], sr[1][0]), mx1 = fmaxf(sr[0][1], sr[1][1]);
-    if (__builtin_expect(__any(mx0 > m_thr[0] || mx1 > m_thr[1]), 0)) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx0 > m_thr[0] || mx1 > m_thr[1]) != 0, 0)) {
       pend_val[0] = mx0 * isc[0];
       pend_val[1] = mx1 * isc[1];
       return 1;
@@ -893,11 +895,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
       for (int hh = 0; hh < 2; ++hh) {
         pk[tile][hh] = __builtin_amdgcn_exp2f(fmaf(sr[tile][hh], isc[hh], -mk[hh]));  // p 2^(ev - e_slot)
         float w = pk[tile][hh] * cur.nv[tile];
-        if (mask) w = pk[tile][hh] > 0.f ? w : 0.f;  // masked tokens may hold garbage norms
+        if constexpr (MASK) w = pk[tile][hh] > 0.f ? w : 0.f;  // masked tokens may hold garbage norms
         wv[tile][hh] = w;
       }
     const float wm0 = fmaxf(wv[0][0], wv[1][0]), wm1 = fmaxf(wv[0][1], wv[1][1]);
-    if (__builtin_expect(__any(fmaxf(wm0, wm1) >= kWeightOperandMax), 0)) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(fmaxf(wm0, wm1) >= kWeightOperandMax) != 0, 0)) {
       // largest unscaled weight of this lane per head: w 2^(e_slot - ev); nothing accumulated
       pend_val[0] = wm0 * exp2f(e_slot - (float)ev[0]);
       pend_val[1] = wm1 * exp2f(e_slot - (float)ev[1]);
@@ -1027,25 +1029,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
     wacc.z *= f[1];
     wacc.w *= f[1];
   };
-  auto run = [&](unsigned rel, Chunk& cur, auto&& mid) {
-    const bool mask = rel + 32 > n_rel;
+  auto run = [&](unsigned rel, Chunk& cur, auto mask_c, auto&& mid) {
     bool first = true;
-    while ((pend = step(rel, cur, mask, first, mid)) != 0) {
+    while ((pend = step(rel, cur, mask_c, first, mid)) != 0) {
       rescale();
       first = false;
     }
   };
+  // chunks [0, n_full) lie inside the context; a last partial chunk runs masked
+  const unsigned n_full = n_rel & ~31u;
   if constexpr (DEPTH == 0) {
-    // registers, ping-pong: the next chunk loads while this one computes
-    Chunk ca, cb;
-    if (n_rel > 0) load_chunk(0, ca);
-    for (unsigned rel = 0; rel < n_rel; rel += 64) {
-      if (rel + 32 < n_rel) load_chunk(rel + 32, cb);
-      run(rel, ca, [] {});
-      if (rel + 32 >= n_rel) break;
-      if (rel + 64 < n_rel) load_chunk(rel + 64, ca);
-      run(rel + 32, cb, [] {});
+    // registers: the next chunk loads while this one computes, then moves in
+    Chunk cur, nxt;
+    if (n_rel > 0) load_chunk(0, cur);
+    unsigned rel = 0;
+    for (; rel < n_full; rel += 32) {
+      if (rel + 32 < n_rel) load_chunk(rel + 32, nxt);
+      run(rel, cur, std::false_type{}, [] {});
+      cur = nxt;
     }
+    if (rel < n_rel) run(rel, cur, std::true_type{}, [] {});
   } else {
     // LDS ring: chunk c sits in slot c % DEPTH. Before a chunk is read, the
     // loads of the (up to DEPTH - 1) chunks issued after it may stay in
@@ -1056,7 +1059,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
       if (32u * j < n_rel) issue_chunk(32u * j, ring[wave][j]);
     const unsigned last = (n_rel - 1) / 32;  // index of the split's last chunk
     int slot = 0;
-    for (unsigned rel = 0; rel < n_rel; rel += 32) {
+    auto body = [&](unsigned rel, auto mask_c) {
       uint8_t* sb = ring[wave][slot];
       // the debug score stores also count in vmcnt, so that mode waits for all
       const unsigned ahead = min(last - rel / 32, (unsigned)(DEPTH - 1));
@@ -1065,12 +1068,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_main_kernel(DecMainParams 
       else wait_vmcnt<(DEPTH > 2 ? 2 : 1) * RG::LOADS>();
       Chunk cur;
       read_chunk(sb, cur);
-      run(rel, cur, [&] {
+      run(rel, cur, mask_c, [&] {
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot's reads have landed
         if (rel + 32u * DEPTH < n_rel) issue_chunk(rel + 32u * DEPTH, sb);
       });
       slot = slot + 1 == DEPTH ? 0 : slot + 1;
-    }
+    };
+    unsigned rel = 0;
+    for (; rel < n_full; rel += 32) body(rel, std::false_type{});
+    if (rel < n_rel) body(rel, std::true_type{});
   }
 
   // ---------------- write this split's partial state ----------------
