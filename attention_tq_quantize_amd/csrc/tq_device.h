@@ -208,6 +208,9 @@ __device__ __forceinline__ uint2 ld64(buf_t r, unsigned voff, unsigned soff) {
   const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
   return uint2{v.x, v.y};
 }
+__device__ __forceinline__ void st32(buf_t r, unsigned v, unsigned voff, unsigned soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0);
+}
 __device__ __forceinline__ uint4 ld128(buf_t r, unsigned voff, unsigned soff) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return uint4{v.x, v.y, v.z, v.w};

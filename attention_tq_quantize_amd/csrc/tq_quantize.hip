@@ -62,7 +62,8 @@ struct QuantParams {
 __host__ __device__ constexpr int q_tiles(int D, bool prod, bool xf32, bool blk) {
   return (D == 256 && (prod || xf32) && !blk) ? 1 : 2;
 }
-__host__ __device__ constexpr int q_waves_per_simd(int D, bool prod) { return (D <= 128 && !prod) ? 4 : 2; }
+// waves per SIMD: 4 where the registers allow (bf16 mse up to d = 128), else 2
+__host__ __device__ constexpr int q_waves_per_simd(int D, bool prod, bool xf32) { return (D <= 128 && !prod && !xf32) ? 4 : 2; }
 __host__ __device__ constexpr bool q_prefetch(int D, bool xf32) { return !(D == 256 && xf32); }
 
 // Raw input of one 16-vector tile for lane (r, g): vector r, coordinates
@@ -263,7 +264,7 @@ __device__ __forceinline__ unsigned quad_or(unsigned w) {
 }
 
 template <int D, int P, bool PROD, bool XF32, bool BLK, bool DBG>
-__global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD)) void quantize_kernel(QuantParams prm) {
+__global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void quantize_kernel(QuantParams prm) {
   constexpr int NQ = D / 16, NK = D / 32, Q4 = D / 4;
   constexpr int T = q_tiles(D, PROD, XF32, BLK);
   constexpr bool PREF = q_prefetch(D, XF32);
@@ -322,10 +323,24 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD)) void quantize
   }
   // fragment (hilo, q, ks) of this lane
   auto frag = [&](const u32x4* base, int hl, int q, int ks) -> u32x4 {
-    return base[((hl * NQ + q) * NK + ks) * 64 + lane];
+    if constexpr (LDS_FRAG) {
+      return base[((hl * NQ + q) * NK + ks) * 64 + lane];
+    } else {
+      // global: wave-uniform base and fragment offset in SGPRs, one lane offset
+      // register for every fragment
+      const buf_t r = make_buf(base, FRAG_VECS * 16u);
+      const uint4 v = ld128(r, 16u * lane, (unsigned)(((hl * NQ + q) * NK + ks) * 64 * 16));
+      return u32x4{v.x, v.y, v.z, v.w};
+    }
   };
 
   for (; step < steps; step += stride) {
+    // d = 256: the fragments stay in global memory. Opaque copies of their
+    // addresses keep the compiler from hoisting every step-invariant fragment
+    // load out of this loop (about a thousand registers, all spilled).
+    const u32x4* fpi_l = fpi;
+    const u32x4* fsp_l = fsp;
+    if constexpr (!LDS_FRAG) asm volatile("" : "+s"(fpi_l), "+s"(fsp_l));
     const int64_t nstep = step + stride;
     if constexpr (PREF) {
       if (nstep < steps) load_step(nstep, nxt);
@@ -380,7 +395,7 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD)) void quantize
         for (int t = 0; t < T; ++t) C[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NK; ++ks) {
-          const u32x4 ph = frag(fpi, 0, q, ks), pl = frag(fpi, 1, q, ks);
+          const u32x4 ph = frag(fpi_l, 0, q, ks), pl = frag(fpi_l, 1, q, ks);
 #pragma unroll
           for (int t = 0; t < T; ++t) {
             C[t] = mfma(ph, xh[t][ks], C[t]);
@@ -476,7 +491,7 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD)) void quantize
           for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < NK; ++ks) {
-            const u32x4 sh = frag(fsp, 0, q, ks), sl = frag(fsp, 1, q, ks);
+            const u32x4 sh = frag(fsp_l, 0, q, ks), sl = frag(fsp_l, 1, q, ks);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
               acc[t] = mfma(sh, eh[t][ks], acc[t]);
@@ -539,7 +554,9 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD)) void quantize
         if (g == 0 && v < n) prm.norms[gbase + v] = (float)nu_own;
       }
       const int slot = r16 & 3;
-      uint8_t* blk = prm.codes + ((gbase + v0) / 32) * (int64_t)(4 * P * D);
+      // this step's 32-vector block; 32-bit lane offset of word (p = 0, q = 0)
+      const buf_t blk = make_buf(prm.codes + ((gbase + v0) / 32) * (int64_t)(4 * P * D), (unsigned)(4 * P * D));
+      const unsigned blk_lane = (unsigned)((g * (D / 4) + (D / 16) * (r16 >> 2)) * 4);
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         f32x4 C[T];
@@ -547,7 +564,7 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD)) void quantize
         for (int t = 0; t < T; ++t) C[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NK; ++ks) {
-          const u32x4 ph = frag(fpi, 0, q, ks), pl = frag(fpi, 1, q, ks);
+          const u32x4 ph = frag(fpi_l, 0, q, ks), pl = frag(fpi_l, 1, q, ks);
 #pragma unroll
           for (int t = 0; t < T; ++t) {
             C[t] = mfma(xh[t][ks], ph, C[t]);
@@ -577,13 +594,13 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD)) void quantize
             }
           }
         }
-        const int w = (D / 16) * (r16 >> 2) + q;
+        // word ((p, g), (D/16)(r16/4) + q) of the block
 #pragma unroll
         for (int p = 0; p < P; ++p) {
           unsigned word = (nib[0][p] & vmask[0]) << (4 * slot);
           if constexpr (T > 1) word |= (nib[1][p] & vmask[1]) << (16 + 4 * slot);
           word = quad_or(word);
-          if (slot == 0) *(unsigned*)(blk + ((p * 4 + g) * (D / 4) + w) * 4) = word;
+          if (slot == 0) st32(blk, word, blk_lane + (unsigned)(p * 4 * D), (unsigned)(4 * q));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -652,7 +669,7 @@ tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream) {
                   }
                   // persistent workgroups: as many as fit on the device at once, split over the groups
                   constexpr int T = q_tiles(D, PROD, XF32, BLK);
-                  const int by_waves = q_waves_per_simd(D, PROD) * 4 / kQWaves;
+                  const int by_waves = q_waves_per_simd(D, PROD, XF32) * 4 / kQWaves;
                   const int by_lds = lds ? (int)((160 * 1024) / lds) : by_waves;
                   const int per_cu = by_waves < by_lds ? by_waves : by_lds;
                   const int64_t steps = (a.n_per_group + 16 * T - 1) / (16 * T);

@@ -286,7 +286,7 @@ def outlier_split_decode(tq, syn, torch, dev, reps=10, bits=(3, 2)):
         chans_p = [order[:, :32], order[:, 32:]]  # [Hkv][d_p] per part
         del sample
         for p, pbits in enumerate(bits):
-            dp = len(chans_p[p])
+            dp = chans_p[p].shape[-1]
             for g in range(Hkv):
                 S = syn.gaussian_matrix(dp, syn.CFG_DECODE_128K, tensor, 300 + 10 * p + g) if var == "prod" else None
                 qs_p[p].append(tq.Quantizer(dp, pbits, var, syn.rotation(dp, syn.CFG_DECODE_128K, tensor, 300 + 10 * p + g), S))
