@@ -12,9 +12,14 @@ The decode streams 906 MB, more than the 256 MB Infinity Cache, so each step's
 quantize inputs are not cache-resident when it starts.
 
 Printed: one JSON line. `value` is the step's algorithmic HBM bytes (quantize
-in + codes + norms; decode 108 B per token and KV head) per second. Per-stage
-throughput, the decode kernel's roofline and the fp64 oracle's CPU rate on a
-bounded sample are attached.
+in + codes + norms; decode 108 B per token and KV head) per second over the
+timed steps (50 by default); per-stage means, medians and p10/p90 come from HIP
+events around each stage. Components timed on their own (the prod quantize, the
+bit-width / head-dim sweep, vector-search scoring) run each call after writing a
+512 MB buffer, so their inputs come from HBM and not the 256 MB Infinity Cache,
+and report the median. Also attached: the decode kernel's roofline, the
+quantize's bf16 MFMA use as a fraction of the 2.5 PFLOP/s dense peak, and the
+fp64 oracle's CPU rate on a bounded sample (all host threads, and one core).
 """
 from __future__ import annotations
 
@@ -29,13 +34,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
+FLUSH_BYTES = 512 << 20  # written before a timed call so its inputs are not cache-resident (256 MB MALL)
 METRIC = "quantize Mvec/s (d=128,b=3) + decode-attention GB/s over packed KV, % roofline"
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle CPU timing")
     ap.add_argument("--traffic", type=str, default=None,
@@ -119,6 +126,118 @@ def decode_traffic(path=None):
     return int(fields["decode_bytes_per_launch"])
 
 
+def make_flush(torch, dev):
+    """A 512 MB buffer; writing it evicts the 256 MB Infinity Cache, so the next
+    call reads its inputs from HBM."""
+    buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    state = {"k": 0}
+
+    def flush():
+        state["k"] = (state["k"] + 1) & 0xFF
+        buf.fill_(state["k"])
+    return flush
+
+
+def timed_flushed(torch, fn, flush, reps):
+    """reps calls of fn, each after a cache flush, each timed alone with HIP
+    events on the current stream: (median, p10, p90) in ms."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        flush()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return ms[reps // 2], ms[reps // 10], ms[min(reps - 1, (9 * reps) // 10)]
+
+
+def quantize_mfma_flops(d, variant):
+    """MFMA floating-point operations the quantize kernel executes per bf16 vector:
+    the rotation as bf16 hi and lo passes (2 x 2 d^2) and, for prod, the S' = S Pi^T
+    projection of the residual as three bf16 passes (hi*hi, lo*hi, hi*lo)."""
+    return 4 * d * d + (6 * d * d if variant == "prod" else 0)
+
+
+def c4_sweep(tq, syn, torch, dev, flush, reps=20):
+    """Bit-width and head-dim sweep: b in {1, 2, 4} x {mse, prod} keys (values mse b)
+    x d in {64, 256}; B = 4, 64 query / 8 KV heads, 16384 tokens per sequence, bf16
+    KV with the headline's outlier channels and per-token LogNormal(0, 0.5) scale.
+    Per row: layer quantize of keys and values (two launches, 2 x 524,288 vectors)
+    and decode attention over the packed caches, each timed after a 512 MB cache
+    flush, median of reps calls; quantize MFMA use as executed bf16 MFMA FLOPs over
+    the 2.5 PFLOP/s dense peak."""
+    B, Hq, Hkv, T = 4, 64, 8, 16384
+    G = B * Hkv
+    rows = []
+    for d in (64, 256):
+        xk = syn.kv_vectors_device(G, T, d, syn.CFG_SWEEP, syn.T_K, dev, lognormal_sigma=0.5)
+        xv = syn.kv_vectors_device(G, T, d, syn.CFG_SWEEP, syn.T_V, dev, lognormal_sigma=0.5)
+        q = torch.from_numpy(syn.decode_queries(B, Hq, d, syn.CFG_SWEEP)).to(dev).to(torch.bfloat16)
+        lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+        for bits in (1, 2, 4):
+            for var in ("mse", "prod"):
+                kq = [tq.Quantizer(d, bits, var, syn.rotation(d, syn.CFG_SWEEP, syn.T_K, 700 + h),
+                                   syn.gaussian_matrix(d, syn.CFG_SWEEP, syn.T_K, 700 + h) if var == "prod" else None)
+                      for h in range(Hkv)]
+                vq = [tq.Quantizer(d, bits, "mse", syn.rotation(d, syn.CFG_SWEEP, syn.T_V, 700 + h)) for h in range(Hkv)]
+                kp = kq[0].planes
+                kcodes = torch.empty((B, Hkv, T, kq[0].code_bytes), dtype=torch.uint8, device=dev) if kp > 0 else None
+                ksigns = torch.empty((B, Hkv, T, d // 8), dtype=torch.uint8, device=dev) if var == "prod" else None
+                knorms = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+                krn = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev) if var == "prod" else None
+                vcodes = torch.empty((B, Hkv, T // 32, 4 * bits * d), dtype=torch.uint8, device=dev)
+                vnorms = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+                kout = {"norms": knorms.view(G, T)}
+                if kp > 0:
+                    kout["codes"] = kcodes.view(G, -1)
+                if var == "prod":
+                    kout["signs"] = ksigns.view(G, T, -1)
+                    kout["rnorms"] = krn.view(G, T)
+                vout = {"codes": vcodes.view(G, -1), "norms": vnorms.view(G, T)}
+                kq_g = [kq[g % Hkv] for g in range(G)]
+                vq_g = [vq[g % Hkv] for g in range(G)]
+
+                def quant():
+                    tq.quantize(kq_g, xk, layout="vector", out=kout)
+                    tq.quantize(vq_g, xv, layout="block32", out=vout)
+                quant()
+                torch.cuda.synchronize()
+                kcache = tq.KVCache(kq, knorms, kcodes, ksigns, krn)
+                vcache = tq.KVCache(vq, vnorms, vcodes)
+                ws = torch.empty(tq.decode_workspace_size(B, Hq, Hkv, d, T, kcache, vcache), dtype=torch.uint8,
+                                 device=dev)
+                out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+
+                def dec():
+                    tq.decode_attention(q, kcache, vcache, lens, 1 / math.sqrt(d), max_ctx=T, out=out, workspace=ws)
+                dec()
+                qmed, q10, q90 = timed_flushed(torch, quant, flush, reps)
+                dmed, d10, d90 = timed_flushed(torch, dec, flush, reps)
+                n = G * T
+                krec = kq[0].code_bytes + 4 + ((d // 8 + 4) if var == "prod" else 0)
+                vrec = bits * d // 8 + 4
+                qbytes = n * (2 * d * 2 + krec + vrec)
+                dbytes = n * (krec + vrec)
+                mflops = n * (quantize_mfma_flops(d, var) + quantize_mfma_flops(d, "mse"))
+                rows.append({
+                    "d": d, "bits": bits, "keys": var, "values": "mse",
+                    "quantize_ms": round(qmed, 4), "quantize_ms_p10_p90": [round(q10, 4), round(q90, 4)],
+                    "quantize_mvec_s": round(2 * n / (qmed * 1e-3) / 1e6, 1),
+                    "quantize_gb_s": round(qbytes / (qmed * 1e-3) / 1e9, 1),
+                    "quantize_frac_hbm": round(qbytes / (qmed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "quantize_frac_mfma": round(mflops / (qmed * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                    "decode_ms": round(dmed, 4), "decode_ms_p10_p90": [round(d10, 4), round(d90, 4)],
+                    "decode_gb_s": round(dbytes / (dmed * 1e-3) / 1e9, 1),
+                    "decode_frac_hbm": round(dbytes / (dmed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "bytes_per_token_head": krec + vrec})
+                del kcache, vcache, ws, kcodes, ksigns, knorms, krn, vcodes, vnorms, kout, vout
+        del xk, xv
+        torch.cuda.empty_cache()
+    return {"workload": "B=4, 64/8 heads, ctx 16384; keys mse|prod b, values mse b; flushed, median of "
+                        f"{reps}", "rows": rows}
+
+
 def cpu_baseline(syn):
     """The fp64 oracle on a bounded sample of the same workload, host cores."""
     import numpy as np
@@ -159,21 +278,48 @@ def cpu_baseline(syn):
         t0 = time.perf_counter()
         O.decode_attention(q, kc, vc, np.array([T]), 1 / math.sqrt(d))
         td_s += time.perf_counter() - t0
+        if h == 0:
+            first = (q, kc, vc)
     qbytes = nq * (256 + 48 + 4)
     dbytes = n_groups * T * 108
+    # the same oracle on one host core (BLAS held to one thread): a smaller sample
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        n1 = 1 << 17
+        x1 = syn.kv_vectors(n1, d, syn.CFG_LAYER_QUANT, syn.T_K, 0, 1)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            r1 = O.quantize_mse(x1, Pi, cb)
+            O.pack_vector_layout(r1["idx"], 3)
+            tq1 = time.perf_counter() - t0
+            q, kc, vc = first
+            t0 = time.perf_counter()
+            O.decode_attention(q, kc, vc, np.array([T]), 1 / math.sqrt(d))
+            td1 = time.perf_counter() - t0
+        b1 = n1 * (256 + 48 + 4) + T * 108
+        single = {"value": round(b1 / (tq1 + td1) / 1e9, 5), "unit": "GB/s", "cores": 1,
+                  "sample": (f"quantize_mse of {n1} vectors ({tq1:.2f} s) + decode attention of one (batch, kv "
+                             f"head) group over {T} tokens ({td1:.2f} s), BLAS limited to one thread"),
+                  "quantize_mvec_s": round(n1 / tq1 / 1e6, 5), "decode_gb_s": round(T * 108 / td1 / 1e9, 5)}
+    except ImportError:
+        pass
     return {"value": round((qbytes + dbytes) / (tq_s + td_s) / 1e9, 4), "unit": "GB/s", "cores": int(cores),
             "kind": "oracle",
             "sample": (f"fp64 oracle: quantize_mse of {nq} bf16 vectors (d=128, b=3; {tq_s:.2f} s) + decode "
                        f"attention of {n_groups} (batch, kv head) groups, 8 query heads each over {T} tokens "
                        f"(prod-3 keys, mse-3 values; {td_s:.2f} s); same algorithmic-byte accounting"),
-            "quantize_mvec_s": round(nq / tq_s / 1e6, 5), "decode_gb_s": round(dbytes / td_s / 1e9, 5)}
+            "quantize_mvec_s": round(nq / tq_s / 1e6, 5), "decode_gb_s": round(dbytes / td_s / 1e9, 5),
+            "single_core": single}
 
 
-def vector_search(tq, syn, torch, dev, n=100000, m=16, bits=3):
+def vector_search(tq, syn, torch, dev, flush, n=100000, m=16, bits=3, reps=10):
     """Vector-search workload: index n synthetic Gaussian embeddings with
     TurboQuant_prod (b = 3) at d = 1536 and 3072, then score m queries against
     the packed database with tq_inner_products (fp32 vector units) and with
-    tq_search_scores (matrix cores)."""
+    tq_search_scores (matrix cores). Scoring calls are timed after a 512 MB cache
+    flush each (the database would otherwise stay in the Infinity Cache), median
+    of reps."""
     import numpy as np
     out = {}
     for d in (1536, 3072):
@@ -195,23 +341,11 @@ def vector_search(tq, syn, torch, dev, n=100000, m=16, bits=3):
         args = (qz, y, rec["codes"], rec["norms"], rec["signs"], rec["rnorms"])
         for _ in range(3):
             tq.inner_products(*args)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(10):
-            tq.inner_products(*args)
-        e1.record()
-        torch.cuda.synchronize()
-        score_ms = e0.elapsed_time(e1) / 10
+        score_ms, _, _ = timed_flushed(torch, lambda: tq.inner_products(*args), flush, reps)
         ws = torch.empty(tq.search_workspace_size(qz, m), dtype=torch.uint8, device=dev)
         for _ in range(3):
             tq.search_scores(*args, workspace=ws)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(10):
-            tq.search_scores(*args, workspace=ws)
-        e1.record()
-        torch.cuda.synchronize()
-        mfma_ms = e0.elapsed_time(e1) / 10
+        mfma_ms, _, _ = timed_flushed(torch, lambda: tq.search_scores(*args, workspace=ws), flush, reps)
         rec_bytes = (bits - 1) * d // 8 + d // 8 + 8
         out[f"d{d}"] = {"database": n, "queries": m, "variant": f"prod b={bits}",
                         "index_ms": round(index_ms, 3), "index_mvec_s": round(n / (index_ms * 1e-3) / 1e6, 2),
@@ -460,18 +594,14 @@ def main():
     ms_per_step = total_ms / K
     value = (q_bytes + d_bytes) / (ms_per_step * 1e-3) / 1e9
 
-    # residual + QJL stage on its own: prod quantize of the layer's keys
+    flush = make_flush(torch, dev)
+    # residual + QJL stage on its own: prod quantize of the layer's keys (flushed, median)
+    pq = lambda: tq.quantize(w["qp2"], w["xk2"], layout="vector", out=w["out_p2"])
     for _ in range(3):
-        tq.quantize(w["qp2"], w["xk2"], layout="vector", out=w["out_p2"])
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(10):
-        tq.quantize(w["qp2"], w["xk2"], layout="vector", out=w["out_p2"])
-    e1.record()
-    torch.cuda.synchronize()
-    p_ms = e0.elapsed_time(e1) / 10
+        pq()
+    p_ms, _, _ = timed_flushed(torch, pq, flush, 20)
     p_vec = w["H"] * w["T2"]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     # decode step with append: the new token's key and value are quantized into the
     # caches at position ctx - 1 of every sequence, then ctx tokens are attended
@@ -497,7 +627,8 @@ def main():
     torch.cuda.synchronize()
     a_ms = e0.elapsed_time(e1) / 10
 
-    vsearch = vector_search(tq, syn, torch, dev)
+    vsearch = vector_search(tq, syn, torch, dev, flush)
+    c4 = c4_sweep(tq, syn, torch, dev, flush)
     split = outlier_split(tq, syn, torch, dev, w)
     split_35 = outlier_split(tq, syn, torch, dev, w, bits=(4, 3))
     dec1m = decode_1m(tq, syn, torch, dev)
@@ -530,10 +661,19 @@ def main():
             "decode_gb_s": round(d_gbs, 1),
             "decode_ms": round(d_avg, 4),
             "decode_ms_p10_p90": [round(d_ms[K // 10], 4), round(d_ms[(9 * K) // 10 - 1 if K >= 10 else -1], 4)],
+            "quantize_ms_median": round(q_ms[K // 2], 4),
+            "quantize_ms_p10_p90": [round(q_ms[K // 10], 4), round(q_ms[(9 * K) // 10 - 1 if K >= 10 else -1], 4)],
+            "decode_ms_median": round(d_ms[K // 2], 4),
+            "quantize_frac_mfma": round(n_vec * quantize_mfma_flops(w["d"], "mse") / (q_avg * 1e-3) / 1e12
+                                        / BF16_MFMA_PEAK_TFLOPS, 4),
             "quantize_prod_mvec_s": round(p_vec / (p_ms * 1e-3) / 1e6, 1),
             "quantize_prod_gb_s": round(p_vec * (256 + 32 + 16 + 8) / (p_ms * 1e-3) / 1e9, 1),
+            "quantize_prod_ms_median_flushed": round(p_ms, 4),
+            "quantize_prod_frac_mfma": round(p_vec * quantize_mfma_flops(w["d"], "prod") / (p_ms * 1e-3) / 1e12
+                                             / BF16_MFMA_PEAK_TFLOPS, 4),
             "decode_append_ms": round(a_ms, 4),
             "vector_search": vsearch,
+            "c4_sweep": c4,
             "outlier_split": split,
             "decode_1m": dec1m,
             "outlier_split_decode": split_dec,
