@@ -175,14 +175,15 @@ __device__ __forceinline__ i32x4 make_rsrc4(const void* base, unsigned bytes) {
   return i32x4{(int)(unsigned)a, (int)((a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
 }
 // 16 bytes per lane from byte voff of r straight into LDS at lds + 16 lane
-// (lanes past the range load zeros). Written in assembly so that the compiler
+// (lanes past the range load zeros), with the non-temporal hint: the bytes are
+// streamed once. Written in assembly so that the compiler
 // does not make every later LDS read wait for it: the caller waits with
 // wait_vmcnt before it reads the bytes, and must not overwrite the
 // destination's earlier reads before they have returned. m0 is restored.
 __device__ __forceinline__ void lds_load16(i32x4 r, unsigned voff, unsigned lds) {
   unsigned save;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
       : "=&s"(save)
       : "s"(lds), "v"(voff), "s"(r)
       : "memory");

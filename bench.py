@@ -106,21 +106,25 @@ def build_workloads(tq, syn, torch, dev):
                 qp2=qp2, out_p2=out_p2)
 
 
+# the sources of the decode kernels (their hash keys the committed traffic counters)
+DECODE_SOURCES = ("tq_decode.hip", "tq_device.h", "tq_internal.h")
+
+
 def decode_traffic(path=None):
     """HBM bytes per decode main-kernel launch measured with rocprofv3 FETCH_SIZE /
     WRITE_SIZE (scaled by a 1 GiB copy), read from the committed counter summary.
     None when the decode source changed since the counters were taken."""
     import hashlib
     path = path or os.path.join(ROOT, "profiles", "decode_attention_b8_ctx128k_hbm_counters.md")
-    src = os.path.join(ROOT, "attention_tq_quantize_amd", "csrc", "tq_decode.hip")
-    if not (os.path.exists(path) and os.path.exists(src)):
+    srcs = [os.path.join(ROOT, "attention_tq_quantize_amd", "csrc", f) for f in DECODE_SOURCES]
+    if not (os.path.exists(path) and all(os.path.exists(f) for f in srcs)):
         return None
     fields = {}
     for line in open(path):
         if ":" in line and line.split(":", 1)[0].strip() in ("decode_bytes_per_launch", "decode_source_sha256_16"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    now = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    now = hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()[:16]
     if fields.get("decode_source_sha256_16") != now or "decode_bytes_per_launch" not in fields:
         return None
     return int(fields["decode_bytes_per_launch"])
