@@ -93,6 +93,7 @@ struct DecPrepParams {
   u32x4* frag;
   float* consts;
   int Hq, Hkv, group, chunk_heads, n_chunks, n_units;
+  int head_split;  // workgroups per unit, each for a slice of its query heads
   float scale_log2e;
   float kappa;
   float kcoef[kMaxWalsh];
@@ -250,57 +251,69 @@ template <int D, int PK, bool QJL>
 __global__ __launch_bounds__(4 * D) void decode_prep_kernel(DecPrepParams prm) {
   using KW = KWords<D, PK, QJL>;
   constexpr int NTH = 4 * D;
-  if ((int)blockIdx.x >= prm.n_units) {
-    const int a = blockIdx.x - prm.n_units;
+  if ((int)blockIdx.x >= prm.n_units * prm.head_split) {
+    const int a = blockIdx.x - prm.n_units * prm.head_split;
     append_one<D, NTH>(prm.app, a >> 1, a & 1, prm.Hkv);
     return;
   }
   __shared__ float qs[8][D], qp[8][D], qq[8][D];
   __shared__ float stats[8][4];  // per head: sum q', sum q'', max |q'|, max |q''|
-  const int unit = blockIdx.x;
+  const int unit = blockIdx.x / prm.head_split, slice = blockIdx.x % prm.head_split;
   const int chunk = unit % prm.n_chunks, bh = unit / prm.n_chunks;
   const int b = bh / prm.Hkv, hkv = bh % prm.Hkv;
   const int nh = prm.chunk_heads;
   const int hq0 = hkv * prm.group + chunk * nh;
+  // this workgroup's heads [h0, h1) of the unit; slice 0 also writes the unused rows h >= nh
+  const int hps = (nh + prm.head_split - 1) / prm.head_split;
+  const int h0 = slice * hps, h1 = min(h0 + hps, nh);
+  auto mine = [&](int h) { return h < nh ? (h >= h0 && h < h1) : slice == 0; };
   const int t = threadIdx.x;
-  for (int i = t; i < nh * D; i += NTH) qs[i / D][i % D] = bf16_val(prm.q[((int64_t)b * prm.Hq + hq0 + i / D) * D + i % D]);
+  const int mrow = t >> 1, half = t & 1;  // matrix row (Pi_K rows, then S_K rows), half of it
+  const bool s_row = mrow >= D;
+  const int row = mrow % D;
+  const bool m_active = !s_row || QJL;
+  constexpr int NV = D / 8;              // float4 loads per half row
+  constexpr int NB = NV < 16 ? NV : 16;  // loads in flight per batch (64 VGPRs)
+  const float4* m4 = (const float4*)((s_row ? prm.sk[hkv] : prm.pk[hkv]) + (int64_t)row * D) + half * NV;
+  // the first batch of matrix rows is in flight while the query is staged
+  float4 mv0[NB];
+  if (m_active) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) mv0[k] = m4[k];
+  }
+  for (int i = t; i < (h1 - h0) * D; i += NTH)
+    qs[h0 + i / D][i % D] = bf16_val(prm.q[((int64_t)b * prm.Hq + hq0 + h0 + i / D) * D + i % D]);
   __syncthreads();
   {
-    const int mrow = t >> 1, half = t & 1;  // matrix row (Pi_K rows, then S_K rows), half of it
-    const bool s_row = mrow >= D;
-    const int row = mrow % D;
-    constexpr int NV = D / 8;           // float4 loads per half row
-    constexpr int NB = NV < 16 ? NV : 16;  // loads in flight per batch (64 VGPRs)
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (!s_row || QJL) {
-      const float4* m4 = (const float4*)((s_row ? prm.sk[hkv] : prm.pk[hkv]) + (int64_t)row * D) + half * NV;
+    if (m_active) {
 #pragma unroll
       for (int k0 = 0; k0 < NV; k0 += NB) {
         float4 mv[NB];
 #pragma unroll
-        for (int k = 0; k < NB; ++k) mv[k] = m4[k0 + k];
+        for (int k = 0; k < NB; ++k) mv[k] = k0 == 0 ? mv0[k] : m4[k0 + k];
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
           const int c = 4 * (half * NV + k0 + k);
 #pragma unroll
           for (int h = 0; h < 8; ++h)
-            if (h < nh) a[h] = fmaf(mv[k].x, qs[h][c], fmaf(mv[k].y, qs[h][c + 1], fmaf(mv[k].z, qs[h][c + 2], fmaf(mv[k].w, qs[h][c + 3], a[h]))));
+            if (h >= h0 && h < h1) a[h] = fmaf(mv[k].x, qs[h][c], fmaf(mv[k].y, qs[h][c + 1], fmaf(mv[k].z, qs[h][c + 2], fmaf(mv[k].w, qs[h][c + 3], a[h]))));
         }
       }
     }
 #pragma unroll
     for (int h = 0; h < 8; ++h) a[h] += __shfl_xor(a[h], 1);
-    if (half == 0 && (!s_row || QJL)) {
+    if (half == 0 && m_active) {
       float(*dst)[D] = s_row ? qq : qp;
 #pragma unroll
       for (int h = 0; h < 8; ++h)
-        if (h < nh) dst[h][row] = a[h];
+        if (h >= h0 && h < h1) dst[h][row] = a[h];
     }
   }
   __syncthreads();
   {
     const int wave = t >> 6, lane = t & 63;
-    for (int h = wave; h < nh; h += NTH / 64) {
+    for (int h = h0 + wave; h < h1; h += NTH / 64) {
       float s_p = 0.f, s_q = 0.f, m_p = 0.f, m_q = 0.f;
       for (int j = lane; j < D; j += 64) {
         s_p += qp[h][j];
@@ -331,33 +344,38 @@ __global__ __launch_bounds__(4 * D) void decode_prep_kernel(DecPrepParams prm) {
     amax = fmaxf(amax, fabsf(prm.kcoef[s]));
     asum += prm.kcoef[s];
   }
-  // one exponent per head for both score parts: the main loop scales their sum once
-  auto head_exp = [&](int h) {
-    return range_exp(fmaxf(2.f * amax * stats[h][2], QJL ? 2.f * prm.kappa * stats[h][3] : 0.f) * prm.scale_log2e);
-  };
+  // one exponent per head for both score parts (the main loop scales their sum
+  // once), and each head's operand scale per slot k: scale log2 e 2^(E + 14 - pos(k))
+  __shared__ float opscale[8][4];
   float* cst = prm.consts + (int64_t)unit * kConstsPerUnit;
-  if (t < 16) {
+  if (t < 16 && mine(t >> 1)) {
     const int h = t >> 1, lo = t & 1;
     if (h < nh) {
-      const int em = head_exp(h);
+      const int em = range_exp(fmaxf(2.f * amax * stats[h][2], QJL ? 2.f * prm.kappa * stats[h][3] : 0.f) *
+                               prm.scale_log2e);
       cst[t] = lo ? 0.f : -asum * stats[h][0] * prm.scale_log2e * ldexpf(1.0f, em - 10);
       cst[16 + t] = lo ? 0.f : (QJL ? -prm.kappa * stats[h][1] * prm.scale_log2e * ldexpf(1.0f, em - 10) : 0.f);
       cst[32 + t] = ldexpf(1.0f, 10 - em);
       cst[48 + t] = ldexpf(1.0f, 10 - em);
+      if (!lo)
+        for (int k = 0; k < 4; ++k) opscale[h][k] = prm.scale_log2e * ldexpf(1.0f, em + 14 - operand_pos(k));
     } else {
       cst[t] = 0.f;
       cst[16 + t] = 0.f;
       cst[32 + t] = 1.f;
       cst[48 + t] = 1.f;
+      if (!lo)
+        for (int k = 0; k < 4; ++k) opscale[h][k] = 0.f;
     }
   }
+  __syncthreads();
   // fragment (f, lane): row r16 = 2 h + lo of the MFMA, K elements 8 g .. 8 g + 7
   for (int e = t; e < KW::NF * 64; e += NTH) {
     const int f = e / 64, lane = e % 64;
     const int g = lane >> 4, r16 = lane & 15, h = r16 >> 1, lo = r16 & 1;
+    if (!mine(h)) continue;
     const int W = f / 4, r = f % 4;
     unsigned hv[8];
-    const int E = h < nh ? head_exp(h) : 0;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int k = it / 2, half = it % 2;
@@ -383,7 +401,7 @@ __global__ __launch_bounds__(4 * D) void decode_prep_kernel(DecPrepParams prm) {
           }
         }
         // the lane's bit reads as 2^(operand_pos(k) - 24); raw scores come out x 2^(E - 10)
-        val *= prm.scale_log2e * ldexpf(1.0f, E + 14 - operand_pos(k));
+        val *= opscale[h][k];
       }
       hv[it] = f16_part(val, lo);
     }
@@ -1304,6 +1322,8 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
   pp.chunk_heads = p.chunk_heads;
   pp.n_chunks = p.n_chunks;
   pp.n_units = units;
+  // two query heads per prep workgroup: four times the workgroups of one per unit
+  pp.head_split = p.chunk_heads > 2 ? (p.chunk_heads + 1) / 2 : 1;
   pp.scale_log2e = scale * kLog2e;
   pp.kappa = (float)(std::sqrt(M_PI / 2.0) / p.d);
   for (int s = 0; s < k0->cb.n_walsh; ++s) pp.kcoef[s] = k0->cb.walsh_coef[s];
@@ -1341,7 +1361,7 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
     a.rot_dbg = app->rot_dbg;
     a.proj_dbg = app->proj_dbg;
   }
-  const int prep_blocks = units + (app ? 2 * p.batch * p.n_kv_heads : 0);
+  const int prep_blocks = units * pp.head_split + (app ? 2 * p.batch * p.n_kv_heads : 0);
 
   DecMainParams mp{};
   mp.frag = frag;
