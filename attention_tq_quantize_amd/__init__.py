@@ -94,7 +94,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tq_quantizer_sizes.argtypes = [_VP, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
     lib.tq_dequantize.argtypes = [_VP, _I, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
     lib.tq_inner_products.argtypes = [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
-    lib.tq_quantize_split.argtypes = [_VP, _I, _VP, _I, _VP, _I, _I64, ctypes.POINTER(Records), _VP]
+    lib.tq_quantize_split.argtypes = [_VP, _I, _I, _VP, _I, _VP, _I, _I64, ctypes.POINTER(Records), _VP]
     lib.tq_inner_products_split.argtypes = [_VP, _I, _VP, _I, _VP, _I64, ctypes.POINTER(Records), _I64, _VP, _VP]
     lib.tq_decode_split_workspace_size.argtypes = [ctypes.POINTER(AttnShape), ctypes.POINTER(SplitCache),
                                                    ctypes.POINTER(SplitCache), ctypes.POINTER(ctypes.c_size_t)]
@@ -422,36 +422,77 @@ def _records(rs):
     return arr
 
 
-def quantize_split(qs: Sequence[Quantizer], channels, x, rot_dbg: bool = False, proj_dbg: bool = False,
-                   stream=None) -> list:
-    """Outlier-channel split (tq_quantize_split): part p quantizes x[:, channels[p]] with qs[p].
-    x: [n, dim] float32 or bfloat16 CUDA tensor; returns one record dict per part."""
-    import torch
-    lib = load()
-    dt = _float_dtype(x, "x")
-    if x.dim() != 2:
-        raise ValueError("x must be [n, dim]")
-    _need_cuda(x, "x")
-    n, dim = x.shape
-    ch = _split_args(qs, channels)
-    outs = []
-    with _on(stream):
-        x = x.contiguous()
-        for q in qs:
-            o = {"norms": torch.empty(n, dtype=torch.float32, device=x.device)}
-            if q.planes > 0:
-                o["codes"] = torch.empty((n, q.code_bytes), dtype=torch.uint8, device=x.device)
-            if q.variant == "prod":
-                o["signs"] = torch.empty((n, q.d // 8), dtype=torch.uint8, device=x.device)
-                o["rnorms"] = torch.empty(n, dtype=torch.float32, device=x.device)
-                if proj_dbg:
-                    o["proj"] = torch.empty((n, q.d), dtype=torch.float32, device=x.device)
-            if rot_dbg:
-                o["rot"] = torch.empty((n, q.d), dtype=torch.float32, device=x.device)
-            outs.append(o)
-    _check(lib.tq_quantize_split(_handles(qs), len(qs), ch.ctypes.data, dim, _ptr(x), dt, n, _records(outs),
-                                 _stream(stream)), "tq_quantize_split")
-    return outs
+class SplitQuantize:
+    """A prepared tq_quantize_split call: the handles and channel lists are
+    marshalled once. Single group (grouped=False): qs[p] a Quantizer, channels[p]
+    its list, x [n, dim]. Grouped: qs[p][g], channels[p][g] per group g (e.g. per
+    KV head), x [G, n, dim]."""
+
+    def __init__(self, qs, channels, grouped: bool = False):
+        import numpy as np
+        qg = qs if grouped else [[q] for q in qs]
+        cg = channels if grouped else [[c] for c in channels]
+        if len(qg) != len(cg) or not qg:
+            raise ValueError("one channel list (per group) for every part")
+        G = len(qg[0])
+        lists = []
+        for p, (qp, cp) in enumerate(zip(qg, cg)):
+            if len(qp) != G or len(cp) != G:
+                raise ValueError(f"split part {p}: {G} quantizers and channel lists expected")
+            for q, c in zip(qp, cp):
+                if q.d != qp[0].d or q.bits != qp[0].bits or q.variant != qp[0].variant:
+                    raise ValueError(f"split part {p}: quantizers differ across groups")
+                if len(c) != q.d:
+                    raise ValueError("each part's channel list must have its quantizer's d entries")
+                lists.append(np.asarray(c, dtype=np.int32).ravel())
+        self.grouped, self.G, self.parts = grouped, G, [qp[0] for qp in qg]
+        self._qs = qg  # keeps the handles alive
+        self._ch = np.ascontiguousarray(np.concatenate(lists), dtype=np.int32)
+        self._handles = (ctypes.c_void_p * (len(qg) * G))(*[q.handle.value for qp in qg for q in qp])
+
+    def __call__(self, x, out: Optional[list] = None, rot_dbg: bool = False, proj_dbg: bool = False,
+                 stream=None) -> list:
+        import torch
+        lib = load()
+        dt = _float_dtype(x, "x")
+        _need_cuda(x, "x")
+        if x.dim() != (3 if self.grouped else 2) or (self.grouped and x.shape[0] != self.G):
+            raise ValueError(f"x must be [{self.G}, n, dim]" if self.grouped else "x must be [n, dim]")
+        n, dim = x.shape[-2], x.shape[-1]
+        lead = (self.G, n) if self.grouped else (n,)
+        with _on(stream):
+            x = x.contiguous()
+            if out is None:
+                out = []
+                for q in self.parts:
+                    o = {"norms": torch.empty(lead, dtype=torch.float32, device=x.device)}
+                    if q.planes > 0:
+                        o["codes"] = torch.empty(lead + (q.code_bytes,), dtype=torch.uint8, device=x.device)
+                    if q.variant == "prod":
+                        o["signs"] = torch.empty(lead + (q.d // 8,), dtype=torch.uint8, device=x.device)
+                        o["rnorms"] = torch.empty(lead, dtype=torch.float32, device=x.device)
+                        if proj_dbg:
+                            o["proj"] = torch.empty(lead + (q.d,), dtype=torch.float32, device=x.device)
+                    if rot_dbg:
+                        o["rot"] = torch.empty(lead + (q.d,), dtype=torch.float32, device=x.device)
+                    out.append(o)
+            elif len(out) != len(self.parts):
+                raise ValueError("out: one record dict per part")
+        _check(lib.tq_quantize_split(self._handles, len(self.parts), self.G, self._ch.ctypes.data, dim, _ptr(x), dt, n,
+                                     _records(out), _stream(stream)), "tq_quantize_split")
+        return out
+
+
+def quantize_split(qs, channels, x, rot_dbg: bool = False, proj_dbg: bool = False, stream=None) -> list:
+    """Outlier-channel split (tq_quantize_split). Single group: x [n, dim], qs[p] a
+    Quantizer and channels[p] its list; part p quantizes x[:, channels[p]] with qs[p].
+    Grouped: x [G, n, dim], qs[p][g] and channels[p][g] per group g (e.g. per KV
+    head). x is float32 or bfloat16 (CUDA); returns one record dict per part, with
+    a leading G axis in the grouped form."""
+    _float_dtype(x, "x")
+    if x.dim() not in (2, 3):
+        raise ValueError("x must be [n, dim] or [G, n, dim]")
+    return SplitQuantize(qs, channels, grouped=x.dim() == 3)(x, rot_dbg=rot_dbg, proj_dbg=proj_dbg, stream=stream)
 
 
 def inner_products_split(qs: Sequence[Quantizer], channels, y, recs, stream=None):

@@ -196,11 +196,13 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
   }
 
   const size_t dd = (size_t)d * d;
-  // large d: fp32 Pi and S only (the MFMA fragments and S' = S Pi^T serve the
-  // d <= 256 kernels; the O(d^3) fold would dominate creation time)
+  // large d: fp32 Pi and S only (the MFMA fragments serve the d = 64, 128, 256
+  // kernels). S' = S Pi^T is folded up to d = 256 (it also serves channel-split
+  // parts of such sizes); beyond, the O(d^3) fold would dominate creation time.
   const size_t frag_bytes = large ? 0 : 2 * dd * sizeof(uint16_t);  // hi + lo
   const bool prod = variant == TQ_PROD;
-  const size_t total = frag_bytes * (prod ? 2 : 1) + dd * sizeof(float) * (prod ? (large ? 2 : 3) : 1);
+  const bool fold = prod && d <= 256;
+  const size_t total = frag_bytes * (prod ? 2 : 1) + dd * sizeof(float) * (prod ? (fold ? 3 : 2) : 1);
   std::vector<unsigned char> host(total);
   size_t off = 0;
   if (!large) build_fragments(d, pi, (uint16_t*)(host.data() + off));
@@ -208,7 +210,7 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
   off += frag_bytes;
   size_t off_sp_frag = 0;
   std::vector<double> sp;
-  if (prod && !large) {
+  if (fold) {
     // S' = S Pi^T, folded in fp64, so that S r = S' (Pi u - y~): the residual never
     // leaves the rotated space.
     sp.assign(dd, 0.0);
@@ -218,6 +220,8 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
         for (int k = 0; k < d; ++k) acc += s[(size_t)i * d + k] * pi[(size_t)j * d + k];
         sp[(size_t)i * d + j] = acc;
       }
+  }
+  if (prod && !large) {
     build_fragments(d, sp.data(), (uint16_t*)(host.data() + off));
     off_sp_frag = off;
     off += frag_bytes;
@@ -230,7 +234,7 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
     off_s32 = off;
     for (size_t i = 0; i < dd; ++i) ((float*)(host.data() + off))[i] = (float)s[i];
     off += dd * sizeof(float);
-    if (!large) {
+    if (fold) {
       off_sp32 = off;
       for (size_t i = 0; i < dd; ++i) ((float*)(host.data() + off))[i] = (float)sp[i];
       off += dd * sizeof(float);
@@ -252,7 +256,7 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
   q->sp_frag = prod && !large ? (const uint16_t*)(base + off_sp_frag) : nullptr;
   q->pi32 = (const float*)(base + off_pi32);
   q->s32 = prod ? (const float*)(base + off_s32) : nullptr;
-  q->sp32 = prod && !large ? (const float*)(base + off_sp32) : nullptr;
+  q->sp32 = fold ? (const float*)(base + off_sp32) : nullptr;
   if (large) {
     hs = build_large_tables(q);
     if (hs != TQ_OK) {
@@ -452,58 +456,95 @@ tq_status tq_search_scores(const tq_quantizer* q, const float* y, int64_t m, con
 }
 
 // ---- outlier-channel split ([NIK] "Experiments": separate quantizers for outlier and ordinary channels) ----
-static tq_status check_split(const tq_quantizer* const* qz, int n_parts, const int32_t* channels, int dim,
-                             std::vector<uint16_t>* chan, std::vector<int>* off) {
+// qz [n_parts][n_groups], channels [n_parts][n_groups][d_p]: the handles of a
+// part share d, bits and variant; every group's lists are in range and repeat
+// no channel. chan receives the lists, off[p] the start of part p's block.
+static tq_status check_split(const tq_quantizer* const* qz, int n_parts, int n_groups, const int32_t* channels,
+                             int dim, std::vector<uint16_t>* chan, std::vector<int64_t>* off) {
   if (!qz || !channels) return set_error(TQ_ERR_INVALID_ARG, "split: qz or channels is NULL");
   if (n_parts < 1 || n_parts > 8) return set_error(TQ_ERR_INVALID_ARG, "split: n_parts outside [1, 8]");
+  if (n_groups < 1) return set_error(TQ_ERR_INVALID_ARG, "split: n_groups < 1");
   if (dim < 1 || dim > kSplitMaxDim) return set_error(TQ_ERR_UNSUPPORTED, fmt("split: dim=%d outside [1, %d]", dim, kSplitMaxDim));
   int total = 0;
   off->assign(n_parts + 1, 0);
   for (int p = 0; p < n_parts; ++p) {
-    if (!qz[p]) return set_error(TQ_ERR_INVALID_ARG, fmt("split: part %d handle is NULL", p));
-    if (qz[p]->planes > 4) return set_error(TQ_ERR_UNSUPPORTED, "split: planes");
-    total += qz[p]->d;
-    (*off)[p + 1] = total;
+    const tq_quantizer* q0 = qz[(size_t)p * n_groups];
+    if (!q0) return set_error(TQ_ERR_INVALID_ARG, fmt("split: part %d handle is NULL", p));
+    if (q0->planes > 4) return set_error(TQ_ERR_UNSUPPORTED, "split: planes");
+    for (int g = 1; g < n_groups; ++g) {
+      const tq_quantizer* qg = qz[(size_t)p * n_groups + g];
+      if (!qg || qg->d != q0->d || qg->bits != q0->bits || qg->variant != q0->variant)
+        return set_error(TQ_ERR_INVALID_ARG, fmt("split: part %d handles differ across groups", p));
+    }
+    total += q0->d;
+    (*off)[p + 1] = (int64_t)n_groups * total;
   }
   if (total > dim) return set_error(TQ_ERR_INVALID_ARG, fmt("split: parts cover %d channels, the rows have %d", total, dim));
-  std::vector<char> seen(dim, 0);
-  chan->resize(total);
-  for (int j = 0; j < total; ++j) {
-    const int c = channels[j];
-    if (c < 0 || c >= dim) return set_error(TQ_ERR_INVALID_ARG, fmt("split: channels[%d]=%d outside [0, %d)", j, c, dim));
-    if (seen[c]) return set_error(TQ_ERR_INVALID_ARG, fmt("split: channel %d listed twice", c));
-    seen[c] = 1;
-    (*chan)[j] = (uint16_t)c;
+  chan->resize((size_t)n_groups * total);
+  for (int g = 0; g < n_groups; ++g) {
+    std::vector<char> seen(dim, 0);
+    for (int p = 0; p < n_parts; ++p) {
+      const int dp = qz[(size_t)p * n_groups]->d;
+      for (int j = 0; j < dp; ++j) {
+        const int64_t at = (*off)[p] + (int64_t)g * dp + j;
+        const int c = channels[at];
+        if (c < 0 || c >= dim)
+          return set_error(TQ_ERR_INVALID_ARG, fmt("split: channels[%lld]=%d (part %d, group %d) outside [0, %d)",
+                                                   (long long)at, c, p, g, dim));
+        if (seen[c]) return set_error(TQ_ERR_INVALID_ARG, fmt("split: group %d lists channel %d twice", g, c));
+        seen[c] = 1;
+        (*chan)[at] = (uint16_t)c;
+      }
+    }
   }
   return TQ_OK;
 }
 
-tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, const int32_t* channels, int dim,
-                            const void* x, tq_dtype x_dtype, int64_t n, const tq_records* out, void* stream) {
+tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, int n_groups, const int32_t* channels, int dim,
+                            const void* x, tq_dtype x_dtype, int64_t n_per_group, const tq_records* out,
+                            void* stream) {
   std::vector<uint16_t> chan;
-  std::vector<int> off;
-  tq_status st = check_split(qz, n_parts, channels, dim, &chan, &off);
+  std::vector<int64_t> off;
+  tq_status st = check_split(qz, n_parts, n_groups, channels, dim, &chan, &off);
   if (st != TQ_OK) return st;
   if (!out) return set_error(TQ_ERR_INVALID_ARG, "split: out is NULL");
-  if (n < 0) return set_error(TQ_ERR_INVALID_ARG, "split: negative n");
+  if (n_per_group < 0) return set_error(TQ_ERR_INVALID_ARG, "split: negative n_per_group");
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return set_error(TQ_ERR_INVALID_ARG, "split: x_dtype");
-  if (n == 0) return TQ_OK;
+  if (n_per_group == 0) return TQ_OK;
   if (!x) return set_error(TQ_ERR_INVALID_ARG, "split: x is NULL");
-  if (n > (int64_t)1 << 31) return set_error(TQ_ERR_UNSUPPORTED, "split: n > 2^31");
+  if ((int64_t)n_groups * n_per_group > (int64_t)1 << 31)
+    return set_error(TQ_ERR_UNSUPPORTED, "split: n_groups * n_per_group > 2^31");
   for (int p = 0; p < n_parts; ++p) {
     const tq_records& r = out[p];
-    const bool prod = qz[p]->variant == TQ_PROD;
-    if (!r.norms || (qz[p]->planes > 0 && !r.codes) || (prod && (!r.signs || !r.rnorms)))
+    const tq_quantizer* q0 = qz[(size_t)p * n_groups];
+    const bool prod = q0->variant == TQ_PROD;
+    if (!r.norms || (q0->planes > 0 && !r.codes) || (prod && (!r.signs || !r.rnorms)))
       return set_error(TQ_ERR_INVALID_ARG, fmt("split: part %d output buffer is NULL", p));
     if (misaligned(r.codes, 4) || misaligned(r.signs, 4))
       return set_error(TQ_ERR_INVALID_ARG, fmt("split: part %d codes and signs must be 4-byte aligned", p));
   }
+  const size_t esize = x_dtype == TQ_F32 ? 4 : 2;
   for (int p = 0; p < n_parts; ++p) {
     const tq_records& r = out[p];
-    const tq_quantizer* one[1] = {qz[p]};
-    QuantizeLaunch a{one, 1, n, x, dim, x_dtype, TQ_LAYOUT_VECTOR, r.codes, r.signs, r.norms, r.rnorms, r.rot_dbg, r.proj_dbg};
-    st = launch_quantize_fp32(a, chan.data() + off[p], dim, (hipStream_t)stream);
-    if (st != TQ_OK) return st;
+    const tq_quantizer* const* qp = qz + (size_t)p * n_groups;
+    const int dp = qp[0]->d;
+    if (quantize_split_fast(dim, qp[0])) {
+      st = launch_quantize_split(qp, n_groups, n_per_group, chan.data() + off[p], x, x_dtype, r, (hipStream_t)stream);
+      if (st != TQ_OK) return st;
+      continue;
+    }
+    // generic fp32 kernels: one launch per group
+    const int64_t cb = (int64_t)qp[0]->planes * dp / 8;
+    for (int g = 0; g < n_groups; ++g) {
+      const int64_t v0 = (int64_t)g * n_per_group;
+      const tq_quantizer* one[1] = {qp[g]};
+      auto at = [&](auto* base, int64_t per) { return base ? base + v0 * per : base; };
+      QuantizeLaunch a{one, 1, n_per_group, (const char*)x + v0 * dim * esize, dim, x_dtype, TQ_LAYOUT_VECTOR,
+                       at(r.codes, cb), at(r.signs, (int64_t)dp / 8), at(r.norms, 1), at(r.rnorms, 1),
+                       at(r.rot_dbg, dp), at(r.proj_dbg, dp)};
+      st = launch_quantize_fp32(a, chan.data() + off[p] + (size_t)g * dp, dim, (hipStream_t)stream);
+      if (st != TQ_OK) return st;
+    }
   }
   return TQ_OK;
 }
@@ -512,8 +553,8 @@ tq_status tq_inner_products_split(const tq_quantizer* const* qz, int n_parts, co
                                   const float* y, int64_t m, const tq_records* recs, int64_t n, float* out,
                                   void* stream) {
   std::vector<uint16_t> chan;
-  std::vector<int> off;
-  tq_status st = check_split(qz, n_parts, channels, dim, &chan, &off);
+  std::vector<int64_t> off;
+  tq_status st = check_split(qz, n_parts, 1, channels, dim, &chan, &off);
   if (st != TQ_OK) return st;
   if (m < 0 || n < 0) return set_error(TQ_ERR_INVALID_ARG, "split inner products: negative size");
   if (m == 0 || n == 0) return TQ_OK;

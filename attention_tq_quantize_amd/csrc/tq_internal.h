@@ -42,6 +42,7 @@ struct tq_quantizer {
   //   pi_frag / sp_frag: bf16 hi/lo MFMA fragments of Pi and S' = S Pi^T,
   //                      ordered [hilo][mtile][kstep][lane][8]
   //   pi32 / s32 / sp32: float32 row-major copies of Pi, S and S' = S Pi^T
+  //                      (sp32: prod with d <= 256, else NULL)
   void* dev_block = nullptr;
   const uint16_t* pi_frag = nullptr;
   const uint16_t* sp_frag = nullptr;
@@ -85,6 +86,11 @@ tq_status launch_quantize_large(const QuantizeLaunch& a, hipStream_t stream);
 // fp32 kernels for any d (multiple of 32): optional channel map (quantized
 // coordinate j reads input channel chan[j] of a row of x_stride elements)
 tq_status launch_quantize_fp32(const QuantizeLaunch& a, const uint16_t* chan, int64_t x_stride, hipStream_t stream);
+// One part of a channel split over n_groups groups of d = 128 rows on the
+// matrix cores (tq_quantize.hip); chan: [n_groups][d_p] channel lists.
+bool quantize_split_fast(int dim, const tq_quantizer* q);
+tq_status launch_quantize_split(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group, const uint16_t* chan,
+                                const void* x, tq_dtype x_dtype, const tq_records& out, hipStream_t stream);
 tq_status launch_inner_products_fp32(const tq_quantizer* q, const float* y, int64_t y_stride, const uint16_t* chan,
                                      bool accumulate, int64_t m, const uint8_t* codes, const uint8_t* signs,
                                      const float* norms, const float* rnorms, int64_t n, float* out,

@@ -24,6 +24,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <type_traits>
 
 #include "tq_device.h"
 
@@ -57,6 +58,22 @@ struct QuantParams {
   const uint16_t* pi_frag[kMaxGroupsPerLaunch];
   const uint16_t* sp_frag[kMaxGroupsPerLaunch];
 };
+
+// One part of an outlier-channel split ([NIK] "Experiments", KV cache) over up
+// to kQSplitGroups groups, for d = 128 heads: the part's d_p x d_p rotation is
+// laid into a 128 x 128 matrix M with M[o][c] = Pi_p[o][j] where channel c is
+// coordinate j of the part (o < d_p), zero elsewhere; likewise S' = S Pi^T on
+// the first d_p rotated coordinates. Lane groups g < d_p / 32 then hold the
+// part's rotated coordinates and write its records.
+constexpr int kQSplitGroups = 16;
+struct QuantSplitParams {
+  int dp;                                // d_p, a multiple of 32 up to 128
+  unsigned chan_mask[kQSplitGroups][4];  // bit b of word w: channel 32 w + b is in the part
+  int8_t inv[kQSplitGroups][128];        // channel -> coordinate of the part, -1 if absent
+  const float* pi[kQSplitGroups];        // Pi_p, fp32 [d_p][d_p]
+  const float* sp[kQSplitGroups];        // prod: S' = S_p Pi_p^T, fp32 [d_p][d_p]
+};
+struct QuantNoSplit {};
 
 // 16-vector tiles per wave step (the block layout needs two: a block is 32 vectors)
 __host__ __device__ constexpr int q_tiles(int D, bool prod, bool xf32, bool blk) {
@@ -103,6 +120,25 @@ __device__ __forceinline__ double sumsq_bf16_exact(const XTile<D, false>& t) {
     }
   }
   return acc;
+}
+
+// Channels outside a split part read as zero: lane group g's bit b of cm is
+// channel 32 g + b (d = 128; bf16 words hold two channels, fp32 words one).
+template <int D, bool XF32>
+__device__ __forceinline__ void mask_tile(XTile<D, XF32>& t, unsigned cm) {
+  auto bit = [&](int pos) -> unsigned { return (unsigned)(((int)(cm << (31 - pos))) >> 31); };
+#pragma unroll
+  for (int i = 0; i < XTile<D, XF32>::NR; ++i) {
+    unsigned w[4] = {t.raw[i].x, t.raw[i].y, t.raw[i].z, t.raw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (XF32)
+        w[j] &= bit(4 * i + j);
+      else
+        w[j] &= (bit(8 * i + 2 * j) & 0xFFFFu) | (bit(8 * i + 2 * j + 1) << 16);
+    }
+    t.raw[i] = u32x4{w[0], w[1], w[2], w[3]};
+  }
 }
 
 // |x|^2 of bf16 input from the fast part sums is used when it lies in
@@ -263,11 +299,14 @@ __device__ __forceinline__ unsigned quad_or(unsigned w) {
   return w;
 }
 
-template <int D, int P, bool PROD, bool XF32, bool BLK, bool DBG>
-__global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void quantize_kernel(QuantParams prm) {
+template <int D, int P, bool PROD, bool XF32, bool BLK, bool DBG, bool SPLIT = false>
+__global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void quantize_kernel(
+    QuantParams prm, std::conditional_t<SPLIT, QuantSplitParams, QuantNoSplit> sx) {
+  static_assert(!SPLIT || (D == 128 && !BLK), "split parts: d = 128 heads, vector layout");
   constexpr int NQ = D / 16, NK = D / 32, Q4 = D / 4;
   constexpr int T = q_tiles(D, PROD, XF32, BLK);
-  constexpr bool PREF = q_prefetch(D, XF32);
+  // split mse at four waves per SIMD has no registers for the next step's tiles
+  constexpr bool PREF = q_prefetch(D, XF32) && !(SPLIT && !PROD && !XF32);
   constexpr int WPL = Q4 >= 32 ? Q4 / 32 : 1;  // 32-bit words per plane per lane (vector layout)
   constexpr int PP = P > 0 ? P : 1;
   constexpr bool LDS_FRAG = D <= 128;
@@ -278,6 +317,16 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int grp = blockIdx.y;
+  // record width (d_p of a split part), whether this lane group holds record
+  // coordinates, and its channel mask
+  int RD = D;
+  bool gv = true;
+  unsigned cm = ~0u;
+  if constexpr (SPLIT) {
+    RD = sx.dp;
+    gv = g < sx.dp / Q4;
+    cm = sx.chan_mask[grp][g];
+  }
   const int64_t n = prm.n_per_group;
   const int64_t gbase = (prm.group_base + grp) * n;
   const int64_t steps = (n + 16 * T - 1) / (16 * T);
@@ -307,7 +356,38 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
 
   const u32x4* fpi;
   const u32x4* fsp;
-  if constexpr (LDS_FRAG) {
+  if constexpr (SPLIT) {
+    // fragments of the part's matrices laid over the head's channels, built here
+    // from the fp32 tables (hi = bf16(v), lo = bf16(v - hi), as on the host)
+    constexpr int HALF = FRAG_VECS / 2;
+    const int dp = sx.dp;
+    const int8_t* inv = sx.inv[grp];
+    for (int w = 0; w < (PROD ? 2 : 1); ++w) {
+      const float* M = w ? sx.sp[grp] : sx.pi[grp];
+      for (int i = threadIdx.x; i < HALF; i += kQThreads) {
+        const int l = i & 63, ks = (i >> 6) % NK, q = (i >> 6) / NK;
+        const int m = l & 15;
+        const int row = Q4 * (m >> 2) + 4 * q + (m & 3);
+        const int col = Q4 * (l >> 4) + 8 * ks;
+        unsigned h[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // Pi_p: input channel col + e is coordinate inv of the part; S': the
+          // residual's coordinate is col + e itself
+          const int j = w ? (col + e < dp ? col + e : -1) : (int)inv[col + e];
+          const float v = (row < dp && j >= 0) ? M[row * dp + j] : 0.0f;
+          h[e] = bf16_part(v, false);
+          lo[e] = bf16_part(v, true);
+        }
+        smem_frag[w * FRAG_VECS + i] = u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+        smem_frag[w * FRAG_VECS + HALF + i] =
+            u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])};
+      }
+    }
+    __syncthreads();
+    fpi = smem_frag;
+    fsp = smem_frag + FRAG_VECS;
+  } else if constexpr (LDS_FRAG) {
     const u32x4* src = (const u32x4*)prm.pi_frag[grp];
     for (int i = threadIdx.x; i < FRAG_VECS; i += kQThreads) smem_frag[i] = src[i];
     if constexpr (PROD) {
@@ -347,8 +427,13 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
     }
     u32x4 xh[T][NK], xl[T][XF32 ? NK : 1];
     double ss[T];
+    // split: an opaque copy of the channel mask per step keeps the compiler from
+    // holding every expanded word mask across the loop (register spills)
+    unsigned cm_l = cm;
+    if constexpr (SPLIT) asm volatile("" : "+v"(cm_l));
 #pragma unroll
     for (int t = 0; t < T; ++t) {
+      if constexpr (SPLIT) mask_tile<D, XF32>(cur[t], cm_l);
       ss[t] = tile_operands<D, XF32>(cur[t], xh[t], xl[t]);
       ss[t] += __shfl_xor(ss[t], 16);
       ss[t] += __shfl_xor(ss[t], 32);
@@ -408,8 +493,8 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
           const float y[4] = {C[t].x * inv[t], C[t].y * inv[t], C[t].z * inv[t], C[t].w * inv[t]};
           if constexpr (DBG) {
             const int64_t v = v0 + 16 * t + r16;
-            if (prm.rot_dbg && v < n)
-              *(float4*)(prm.rot_dbg + (gbase + v) * D + Q4 * g + 4 * q) = float4{y[0], y[1], y[2], y[3]};
+            if (prm.rot_dbg && v < n && gv)
+              *(float4*)(prm.rot_dbg + (gbase + v) * RD + Q4 * g + 4 * q) = float4{y[0], y[1], y[2], y[3]};
           }
           float e4[4];
           PlaneMasks<P> pm[4];
@@ -426,7 +511,7 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
 #pragma unroll
           for (int i = 3; i >= 0; --i) {
             if constexpr (PROD) {
-              const float ej = valid[t] ? y[i] - plane_centroid<P>(pm[i], cen) : 0.0f;
+              const float ej = (valid[t] && gv) ? y[i] - plane_centroid<P>(pm[i], cen) : 0.0f;
               e4[i] = ej;
               esq[t] = fmaf(ej, ej, esq[t]);
             }
@@ -453,22 +538,25 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
       }
       // wave-uniform bases of this step, 32-bit lane offsets
       float* nbase = prm.norms + gbase + v0;
-      uint8_t* cbase = prm.codes + (gbase + v0) * (P * D / 8);
+      uint8_t* cbase = prm.codes + (gbase + v0) * (P * RD / 8);
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const int rel = 16 * t + r16;
         if (v0 + rel < n) {
           if (g == 0) nbase[rel] = (float)nu[t];
-          if constexpr (P > 0) {
-            uint8_t* dst = cbase + (unsigned)rel * (P * D / 8);
+          if (P > 0 && gv) {
+            // 32-bit lane offset; opaque for a runtime record width, which keeps
+            // the compiler from holding 64-bit addresses across the loop
+            unsigned lo = (unsigned)rel * (unsigned)(P * RD / 8) + (unsigned)(g * (Q4 / 8));
+            if constexpr (SPLIT) asm volatile("" : "+v"(lo));
 #pragma unroll
             for (int p = 0; p < P; ++p) {
               if constexpr (Q4 >= 32) {
 #pragma unroll
                 for (int w = 0; w < WPL; ++w)
-                  *(unsigned*)(dst + p * D / 8 + g * (Q4 / 8) + 4 * w) = valid[t] ? pw[t][p][w] : 0u;
+                  *(unsigned*)(cbase + lo + p * RD / 8 + 4 * w) = valid[t] ? pw[t][p][w] : 0u;
               } else {
-                *(unsigned short*)(dst + p * D / 8 + g * (Q4 / 8)) = (unsigned short)(valid[t] ? pw[t][p][0] : 0u);
+                *(unsigned short*)(cbase + lo + p * RD / 8) = (unsigned short)(valid[t] ? pw[t][p][0] : 0u);
               }
             }
           }
@@ -511,23 +599,27 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
             }
             if constexpr (DBG) {
               const int64_t v = v0 + 16 * t + r16;
-              if (prm.proj_dbg && v < n)
-                *(float4*)(prm.proj_dbg + (gbase + v) * D + Q4 * g + 4 * q) = float4{pv[0], pv[1], pv[2], pv[3]};
+              if (prm.proj_dbg && v < n && gv)
+                *(float4*)(prm.proj_dbg + (gbase + v) * RD + Q4 * g + 4 * q) = float4{pv[0], pv[1], pv[2], pv[3]};
             }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
         float* rbase = prm.rnorms + gbase + v0;
-        uint8_t* sbase = prm.signs + (gbase + v0) * (D / 8);
+        uint8_t* sbase = prm.signs + (gbase + v0) * (RD / 8);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           const int rel = 16 * t + r16;
           if (v0 + rel < n) {
             if (g == 0) rbase[rel] = valid[t] ? sqrtf(esq[t]) : 0.0f;
-            uint8_t* dst = sbase + (unsigned)rel * (D / 8);
+            uint8_t* dst = sbase + (unsigned)rel * (RD / 8);
             if constexpr (Q4 >= 32) {
+              if (gv) {
+                unsigned lo = (unsigned)rel * (unsigned)(RD / 8) + (unsigned)(g * (Q4 / 8));
+                if constexpr (SPLIT) asm volatile("" : "+v"(lo));
 #pragma unroll
-              for (int w = 0; w < WPL; ++w) *(unsigned*)(dst + g * (Q4 / 8) + 4 * w) = valid[t] ? sw[t][w] : 0u;
+                for (int w = 0; w < WPL; ++w) *(unsigned*)(sbase + lo + 4 * w) = valid[t] ? sw[t][w] : 0u;
+              }
             } else {
               *(unsigned short*)(dst + g * (Q4 / 8)) = (unsigned short)(valid[t] ? sw[t][0] : 0u);
             }
@@ -677,7 +769,8 @@ tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream) {
                   const int64_t cap = (steps + kQWaves - 1) / kQWaves;
                   if (want > cap) want = cap;
                   if (want < 1) want = 1;
-                  hipLaunchKernelGGL(kern, dim3((unsigned)want, (unsigned)ng), dim3(kQThreads), lds, stream, prm);
+                  hipLaunchKernelGGL(kern, dim3((unsigned)want, (unsigned)ng), dim3(kQThreads), lds, stream, prm,
+                                     QuantNoSplit{});
                   return launch_check("quantize: launch");
                 });
               }
@@ -691,5 +784,85 @@ tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream) {
   return TQ_OK;
 }
 
+bool quantize_split_fast(int dim, const tq_quantizer* q) {
+  const bool prod = q->variant == TQ_PROD;
+  // the kernel builds its fragments from pi32 and, for prod, sp32
+  return dim == 128 && q->d % 32 == 0 && q->d <= 128 && q->pi32 != nullptr &&
+         (prod ? q->planes <= 3 && q->sp32 != nullptr : q->planes >= 1);
+}
+
+tq_status launch_quantize_split(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group, const uint16_t* chan,
+                                const void* x, tq_dtype x_dtype, const tq_records& out, hipStream_t stream) {
+  constexpr int D = 128;
+  const tq_quantizer* q0 = qz[0];
+  const int dp = q0->d;
+  const bool prod = q0->variant == TQ_PROD;
+  const bool xf32 = x_dtype == TQ_F32;
+  const bool dbg = out.rot_dbg != nullptr || out.proj_dbg != nullptr;
+  const int P = q0->planes;
+  const size_t lds = (size_t)2 * D * D * 2 * (prod ? 2 : 1);
+  for (int g0 = 0; g0 < n_groups; g0 += kQSplitGroups) {
+    const int ng = n_groups - g0 < kQSplitGroups ? n_groups - g0 : kQSplitGroups;
+    QuantParams prm{};
+    prm.x = x;
+    prm.x_row_bytes = (int64_t)D * (xf32 ? 4 : 2);
+    prm.n_per_group = n_per_group;
+    prm.n_groups = ng;
+    prm.group_base = g0;
+    prm.codes = out.codes;
+    prm.signs = out.signs;
+    prm.norms = out.norms;
+    prm.rnorms = out.rnorms;
+    prm.rot_dbg = out.rot_dbg;
+    prm.proj_dbg = out.proj_dbg;
+    const int K = 1 << P;
+    for (int i = 0; i + 1 < K; ++i) prm.thr[i] = q0->cb.thresholds[i];
+    for (int i = 0; i < K; ++i) prm.cen[i] = q0->cb.centroids[i];
+    QuantSplitParams sx{};
+    sx.dp = dp;
+    for (int g = 0; g < ng; ++g) {
+      const uint16_t* c = chan + (size_t)(g0 + g) * dp;
+      for (int k = 0; k < D; ++k) sx.inv[g][k] = -1;
+      for (int j = 0; j < dp; ++j) {
+        sx.inv[g][c[j]] = (int8_t)j;
+        sx.chan_mask[g][c[j] / 32] |= 1u << (c[j] % 32);
+      }
+      sx.pi[g] = qz[g0 + g]->pi32;
+      sx.sp[g] = qz[g0 + g]->sp32;
+    }
+    tq_status st = dispatch_planes(P, [&](auto PC) -> tq_status {
+      constexpr int PP = decltype(PC)::value;
+      return dispatch_bool(prod, [&](auto PR) -> tq_status {
+        constexpr bool PROD = decltype(PR)::value;
+        if constexpr ((!PROD && PP == 0) || (PROD && PP > 3)) {
+          return set_error(TQ_ERR_UNSUPPORTED, "split quantize: unsupported (variant, planes)");
+        } else {
+          return dispatch_bool(xf32, [&](auto XF) -> tq_status {
+            constexpr bool XF32 = decltype(XF)::value;
+            return dispatch_bool(dbg, [&](auto DB) -> tq_status {
+              constexpr bool DBG = decltype(DB)::value;
+              auto kern = quantize_kernel<D, PP, PROD, XF32, false, DBG, true>;
+              hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+              if (e != hipSuccess) return check_hip(e, "split quantize: set LDS size");
+              constexpr int T = q_tiles(D, PROD, XF32, false);
+              const int by_waves = q_waves_per_simd(D, PROD, XF32) * 4 / kQWaves;
+              const int by_lds = (int)((160 * 1024) / lds);
+              const int per_cu = by_waves < by_lds ? by_waves : by_lds;
+              const int64_t steps = (n_per_group + 16 * T - 1) / (16 * T);
+              int64_t want = ((int64_t)(per_cu > 0 ? per_cu : 1) * device_cus() + ng - 1) / ng;
+              const int64_t cap = (steps + kQWaves - 1) / kQWaves;
+              if (want > cap) want = cap;
+              if (want < 1) want = 1;
+              hipLaunchKernelGGL(kern, dim3((unsigned)want, (unsigned)ng), dim3(kQThreads), lds, stream, prm, sx);
+              return launch_check("split quantize: launch");
+            });
+          });
+        }
+      });
+    });
+    if (st != TQ_OK) return st;
+  }
+  return TQ_OK;
+}
 
 }  // namespace tq

@@ -438,13 +438,13 @@ def outlier_split_decode(tq, syn, torch, dev, reps=10, bits=(3, 2)):
                 r["rnorms"] = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
             recs.append(r)
         for b in range(B):
+            # one grouped call per batch row: the KV heads are the groups
             x = syn.kv_vectors_device(Hkv, T, d, syn.CFG_DECODE_128K, tensor, dev, seed_offset=b)
-            for g in range(Hkv):
-                got = tq.quantize_split([qs_p[0][g], qs_p[1][g]], [chans_p[0][g], chans_p[1][g]], x[g])
-                for p in range(2):
-                    for key, val in got[p].items():
-                        recs[p][key][b, g].copy_(val.view(recs[p][key][b, g].shape))
-            del x
+            got = tq.quantize_split(qs_p, chans_p, x)
+            for p in range(2):
+                for key, val in got[p].items():
+                    recs[p][key][b].copy_(val.view(recs[p][key][b].shape))
+            del x, got
         sides.append(tq.SplitKV([(qs_p[p], chans_p[p], recs[p]) for p in range(2)]))
     k, v = sides
     q = torch.from_numpy(syn.decode_queries(B, Hq, d, syn.CFG_DECODE_128K)).to(dev).to(torch.bfloat16)
@@ -473,41 +473,35 @@ def outlier_split_decode(tq, syn, torch, dev, reps=10, bits=(3, 2)):
             "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def outlier_split(tq, syn, torch, dev, w, bits=(3, 2)):
+def outlier_split(tq, syn, torch, dev, w, flush, bits=(3, 2)):
     """Outlier-channel mixed precision on the layer's KV (8 heads x 32768 tokens,
     d = 128): per head, the 32 channels of largest RMS at bits[0] and the other 96
     at bits[1] (3 + 2: 2.25 bits per channel; 4 + 3: 3.25), keys TurboQuant_prod,
-    values TurboQuant_mse, through tq_quantize_split (two parts per call, one call
-    per head and tensor)."""
+    values TurboQuant_mse, through tq_quantize_split: one grouped call per tensor
+    (the heads are the groups, each with its own channels and quantizers; one
+    matrix-core launch per part)."""
     H, T2, d = w["H"], w["T2"], w["d"]
     calls = []
     for t, xs, var in ((syn.T_K, w["xk2"], "prod"), (syn.T_V, w["xv2"], "mse")):
+        qs, chans = [[], []], [[], []]
         for h in range(H):
-            x = xs[h]
-            rms = x.float().pow(2).mean(dim=0)
+            rms = xs[h].float().pow(2).mean(dim=0)
             order = torch.argsort(rms, descending=True, stable=True).cpu().numpy()
-            chans = [order[:32], order[32:]]
-            qs = []
-            for i, (c, pbits) in enumerate(zip(chans, bits)):
+            for i, (c, pbits) in enumerate(zip((order[:32], order[32:]), bits)):
                 dp = len(c)
                 S = syn.gaussian_matrix(dp, syn.CFG_LAYER_QUANT, t, 100 + 2 * h + i) if var == "prod" else None
-                qs.append(tq.Quantizer(dp, pbits, var, syn.rotation(dp, syn.CFG_LAYER_QUANT, t, 100 + 2 * h + i), S))
-            calls.append((qs, chans, x))
-    run = lambda: [tq.quantize_split(qs, chans, x) for qs, chans, x in calls]
+                qs[i].append(tq.Quantizer(dp, pbits, var, syn.rotation(dp, syn.CFG_LAYER_QUANT, t, 100 + 2 * h + i), S))
+                chans[i].append(c)
+        sq = tq.SplitQuantize(qs, chans, grouped=True)
+        calls.append((sq, xs, sq(xs)))
+    run = lambda: [sq(x, out=o) for sq, x, o in calls]
     run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(3):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 3
+    ms, ms10, ms90 = timed_flushed(torch, run, flush, 20)
     nvec = 2 * H * T2
     per_ch = (32 * bits[0] + 96 * bits[1]) / 128
     return {"split": f"32 ch x {bits[0]} b + 96 ch x {bits[1]} b ({per_ch} bits/channel), keys prod, values mse",
-            "vectors": nvec,
-            "ms": round(ms, 3), "mvec_s": round(nvec / (ms * 1e-3) / 1e6, 1),
+            "vectors": nvec, "launches": 4,
+            "ms": round(ms, 4), "ms_p10_p90": [round(ms10, 4), round(ms90, 4)], "mvec_s": round(nvec / (ms * 1e-3) / 1e6, 1),
             "input_gb_s": round(nvec * d * 2 / (ms * 1e-3) / 1e9, 1)}
 
 
@@ -640,8 +634,8 @@ def main():
 
     vsearch = vector_search(tq, syn, torch, dev, flush)
     c4 = c4_sweep(tq, syn, torch, dev, flush)
-    split = outlier_split(tq, syn, torch, dev, w)
-    split_35 = outlier_split(tq, syn, torch, dev, w, bits=(4, 3))
+    split = outlier_split(tq, syn, torch, dev, w, flush)
+    split_35 = outlier_split(tq, syn, torch, dev, w, flush, bits=(4, 3))
     dec1m = decode_1m(tq, syn, torch, dev)
     split_dec = outlier_split_decode(tq, syn, torch, dev)
     split_dec_35 = outlier_split_decode(tq, syn, torch, dev, bits=(4, 3))

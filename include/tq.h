@@ -215,27 +215,36 @@ tq_status tq_inner_products(const tq_quantizer* q, const float* y, int64_t m,
  * Outlier-channel mixed precision ([NIK] "Experiments", KV cache: outlier
  * channels get more bits than the others, e.g. 32 channels at 3 bits and 96
  * at 2 bits of a 128-channel head): the channels of each input row are split
- * into parts and part p is quantized by its own quantizer qz[p] (its own
- * rotation, norm, codebook and, for prod, QJL matrix) in the VECTOR layout.
- * The rule that picks the outlier channels is not given by the pages; the
- * caller passes the channel lists.
- *   qz       : host array [n_parts] of handles, 1 <= n_parts <= 8, any
- *              variant and bit width each (d_p = the handle's d, at most 4
- *              MSE-stage planes).
- *   channels : host int32 [d_0 + ... + d_{P-1}]: part p takes the input
- *              channels channels[off_p .. off_p + d_p), off_p = d_0 + .. +
- *              d_{p-1}, in that order (coordinate j of the part is channel
- *              channels[off_p + j]). Every entry in [0, dim), none repeated;
- *              channels left out are dropped. Copied.
+ * into parts and part p is quantized by its own quantizer (its own rotation,
+ * norm, codebook and, for prod, QJL matrix) in the VECTOR layout. The rule
+ * that picks the outlier channels is not given by the pages; the caller
+ * passes the channel lists. Grouped as tq_quantize: row i of group g
+ * (i < n_per_group) is x[g*n_per_group + i] and uses group g's handles and
+ * channel lists (e.g. one group per KV head, each head with its own outlier
+ * channels).
+ *   qz       : host array [n_parts][n_groups] of handles (part p, group g at
+ *              qz[p*n_groups + g]), 1 <= n_parts <= 8; the handles of one
+ *              part share d, bits and variant (d_p = that d, at most 4
+ *              MSE-stage planes); parts may differ in all three.
+ *   n_groups : >= 1.
+ *   channels : host int32 [n_parts][n_groups][d_p]: group g's part p takes the
+ *              input channels channels[off_p + g*d_p .. + d_p), off_p =
+ *              n_groups*(d_0 + .. + d_{p-1}), in that order (coordinate j of
+ *              the part is that list's entry j). Every entry in [0, dim), none
+ *              repeated within a group; channels left out are dropped. Copied.
  *   dim      : channels per input row, at most 512.
- *   x        : device [n][dim], float32 or bfloat16.
- *   out      : host array [n_parts] of device record buffers, as for
- *              tq_quantize with d = d_p (rot_dbg / proj_dbg may be NULL;
- *              codes and signs 4-byte aligned).
- * One launch per part on the caller's stream; the kernels are the generic
- * fp32 ones (any d_p a multiple of 32). Allocates nothing.
- * Errors: TQ_ERR_INVALID_ARG (NULL pointers, a channel out of range or
- * repeated, more channels than dim), TQ_ERR_UNSUPPORTED (dim > 512, n > 2^31).
+ *   x        : device [n_groups*n_per_group][dim], float32 or bfloat16.
+ *   out      : host array [n_parts] of device record buffers for all
+ *              n_groups*n_per_group rows, as for tq_quantize with d = d_p
+ *              (rot_dbg / proj_dbg may be NULL; codes and signs 4-byte aligned).
+ * On the caller's stream. dim = 128 with d_p a multiple of 32 (mse, or prod of
+ * at most 4 bits): one matrix-core launch per part and 16 groups, the part's
+ * matrices laid over the head's channels. Otherwise the generic fp32 kernels,
+ * one launch per part and group. Allocates nothing.
+ * Errors: TQ_ERR_INVALID_ARG (NULL pointers, n_groups < 1, handles of a part
+ * that differ, a channel out of range or repeated within a group, more
+ * channels than dim), TQ_ERR_UNSUPPORTED (dim > 512, n_groups*n_per_group >
+ * 2^31).
  */
 typedef struct {
   uint8_t* codes;   /* code_planes*d/8 bytes per vector (NULL when code_planes == 0) */
@@ -245,14 +254,15 @@ typedef struct {
   float* rot_dbg;   /* optional [n][d] */
   float* proj_dbg;  /* optional [n][d] (prod) */
 } tq_records;
-tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, const int32_t* channels, int dim,
-                            const void* x, tq_dtype x_dtype, int64_t n, const tq_records* out,
+tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, int n_groups, const int32_t* channels,
+                            int dim, const void* x, tq_dtype x_dtype, int64_t n_per_group, const tq_records* out,
                             void* stream);
 /*
  * Inner products of m float32 queries y [m][dim] with n split records:
  *   out[i][j] = sum_p <y_i restricted to part p's channels, x~_p,j>
  * the estimate of <y_i, x_j> over the kept channels (each part as in
- * tq_inner_products). recs is read only; out: device float32 [m][n].
+ * tq_inner_products). qz and channels as for tq_quantize_split with
+ * n_groups = 1. recs is read only; out: device float32 [m][n].
  * Errors as for tq_quantize_split, plus m > 65535.
  */
 tq_status tq_inner_products_split(const tq_quantizer* const* qz, int n_parts, const int32_t* channels,

@@ -150,7 +150,7 @@ def test_search_argument_errors(lib):
 
 def test_split_argument_errors(lib):
     ch = (ctypes.c_int32 * 4)(0, 1, 2, 3)
-    assert lib.tq_quantize_split(None, 1, ch, 4, None, 0, 1, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_quantize_split(None, 1, 1, ch, 4, None, 0, 1, None, None) == tq.TQ_ERR_INVALID_ARG
     assert lib.tq_inner_products_split(None, 1, ch, 4, None, 1, None, 1, None, None) == tq.TQ_ERR_INVALID_ARG
 
 

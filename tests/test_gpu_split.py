@@ -49,29 +49,78 @@ def _parts(tq, specs, seed0):
 
 
 CASES = [
-    # name, dim, n, dtype, [(n_channels or "rest", variant, bits)], dropped channels
+    # name, dim, n, dtype, [(n_channels or "rest", variant, bits)]; channels not
+    # listed are dropped. d = 128 rows with parts of a multiple of 32 channels run
+    # on the matrix-core kernel, the others on the generic fp32 kernels.
     ("kv_mse_32x3_96x2", 128, 700, "bf16", [(32, "mse", 3), ("rest", "mse", 2)]),
     ("kv_prod_32x3_96x2", 128, 500, "f32", [(32, "prod", 3), ("rest", "prod", 2)]),
+    ("kv_prod_bf16_32x4_96x3", 128, 333, "bf16", [(32, "prod", 4), ("rest", "prod", 3)]),
     ("mixed_drop", 128, 300, "f32", [(32, "mse", 4), (64, "prod", 1)]),
+    ("mixed_drop_bf16", 128, 290, "bf16", [(64, "mse", 1), (32, "prod", 2)]),
+    ("generic_dim192", 192, 200, "bf16", [(64, "mse", 3), ("rest", "prod", 2)]),
     ("d256_96_160", 256, 260, "bf16", [(96, "prod", 4), ("rest", "mse", 3)]),
 ]
+
+
+def _split_specs(x, spec):
+    first, rest = _outlier_first(x, spec[0][0])
+    specs, used = [], 0
+    order = np.concatenate([first, rest])
+    for k, var, bits in spec:
+        cnt = x.shape[1] - used if k == "rest" else k
+        specs.append((order[used:used + cnt], var, bits))
+        used += cnt
+    return specs, order[used:]
 
 
 def _build_case(tq, dim, n, dt, spec, seed):
     x = syn.kv_vectors(n, dim, syn.CFG_TEST, syn.T_K, 0, seed, lognormal_sigma=0.5)
     x[3] = 0.0
-    first, rest = _outlier_first(x, spec[0][0])
-    specs, used = [], 0
-    order = np.concatenate([first, rest])
-    for k, var, bits in spec:
-        cnt = dim - used if k == "rest" else k
-        specs.append((order[used:used + cnt], var, bits))
-        used += cnt
+    specs, dropped = _split_specs(x, spec)
+    if len(dropped):
+        # a dropped channel is never read: not even a NaN there reaches the records
+        x[5, dropped[0]] = np.nan
+        x[6, dropped[-1]] = np.inf
     parts, qs = _parts(tq, specs, 40 + seed)
     xd = torch.from_numpy(x).to(DEV)
     if dt == "bf16":
         xd = xd.to(torch.bfloat16)
+        x = xd.float().cpu().numpy()
     return x, parts, qs, xd
+
+
+def _check_part(p, q, g, r):
+    """One part's device records g against the oracle's r (tolerances in the module docstring)."""
+    d = len(p["channels"])
+    valid = r["nu"] > 0
+    assert ulp_diff_f32(g["norms"].cpu().numpy(), r["nu"].astype(np.float32)).max() <= 2
+    rot = g["rot"].cpu().numpy()
+    assert np.abs(rot[valid] - r["y"][valid]).max() < 2e-5
+    cb = p["centroids"]
+    if q.planes > 0:
+        codes = g["codes"].cpu().numpy()
+        fed = O.nearest_index(rot.astype(np.float64), cb)
+        fed[~valid] = 0
+        assert np.array_equal(codes, O.pack_vector_layout(fed, q.planes))
+        idx = O.unpack_vector_layout(codes, q.planes, d)
+        flips = idx[valid] != r["idx"][valid]
+        assert flips.mean() < MAX_FLIP_RATE
+        if flips.any():
+            assert np.all(near_threshold(r["y"][valid][flips], cb, TIE_BAND))
+    if p["variant"] == "prod":
+        proj = g["proj"].cpu().numpy()
+        fz = proj >= 0
+        fz[~valid] = False
+        assert np.array_equal(g["signs"].cpu().numpy(), O.pack_bits(fz))
+        same = valid.copy()
+        if q.planes > 0:
+            same &= np.all(O.unpack_vector_layout(g["codes"].cpu().numpy(), q.planes, d) == r["idx"], axis=1)
+        assert same.sum() > 0.9 * valid.sum()
+        rn = g["rnorms"].cpu().numpy()
+        assert np.all(rn[~valid] == 0)
+        assert np.allclose(rn[same], r["gamma"][same], rtol=2e-5, atol=2e-7)
+        perr = np.abs(proj[same] - r["p"][same]).max(axis=1)
+        assert np.all(perr <= 5e-4 * r["gamma"][same])
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
@@ -83,37 +132,42 @@ def test_split_quantize_parity(gpu_lib, case):
     got = tq.quantize_split(qs, [p["channels"] for p in parts], xd, rot_dbg=True, proj_dbg=True)
     torch.cuda.synchronize()
     ref = O.quantize_split(x, parts)
+    assert ref[0]["nu"][3] == 0
     for p, q, g, r in zip(parts, qs, got, ref):
-        d = len(p["channels"])
-        valid = r["nu"] > 0
-        assert ulp_diff_f32(g["norms"].cpu().numpy(), r["nu"].astype(np.float32)).max() <= 2
-        rot = g["rot"].cpu().numpy()
-        assert np.abs(rot[valid] - r["y"][valid]).max() < 2e-5
-        cb = p["centroids"]
-        if q.planes > 0:
-            codes = g["codes"].cpu().numpy()
-            fed = O.nearest_index(rot.astype(np.float64), cb)
-            fed[~valid] = 0
-            assert np.array_equal(codes, O.pack_vector_layout(fed, q.planes))
-            idx = O.unpack_vector_layout(codes, q.planes, d)
-            flips = idx[valid] != r["idx"][valid]
-            assert flips.mean() < MAX_FLIP_RATE
-            if flips.any():
-                assert np.all(near_threshold(r["y"][valid][flips], cb, TIE_BAND))
-        if p["variant"] == "prod":
-            proj = g["proj"].cpu().numpy()
-            fz = proj >= 0
-            fz[~valid] = False
-            assert np.array_equal(g["signs"].cpu().numpy(), O.pack_bits(fz))
-            same = valid.copy()
-            if q.planes > 0:
-                same &= np.all(O.unpack_vector_layout(g["codes"].cpu().numpy(), q.planes, d) == r["idx"], axis=1)
-            assert same.sum() > 0.9 * valid.sum()
-            rn = g["rnorms"].cpu().numpy()
-            assert rn[3] == 0
-            assert np.allclose(rn[same], r["gamma"][same], rtol=2e-5, atol=2e-7)
-            perr = np.abs(proj[same] - r["p"][same]).max(axis=1)
-            assert np.all(perr <= 5e-4 * r["gamma"][same])
+        _check_part(p, q, g, r)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_split_quantize_grouped_parity(gpu_lib, dt):
+    """Grouped split (one call over G groups, e.g. the KV heads of a layer): every
+    group has its own outlier channels and quantizers; 32 + 96 channels (the
+    matrix-core kernel) for keys (prod) and values (mse), and a ragged n."""
+    tq = gpu_lib
+    G, n, dim = 3, 333, 128
+    print(f"split quantize grouped {dt}", flush=True)
+    for var, bits in (("prod", (3, 2)), ("mse", (3, 2)), ("mse", (4, 1))):
+        xs, parts_g, qs_g = [], [], []
+        for g in range(G):
+            x = syn.kv_vectors(n, dim, syn.CFG_TEST, syn.T_V, g, 7, lognormal_sigma=0.5)
+            x[g] = 0.0
+            specs, _ = _split_specs(x, [(32, var, bits[0]), ("rest", var, bits[1])])
+            parts, qs = _parts(tq, specs, 70 + 5 * g)
+            xs.append(x)
+            parts_g.append(parts)
+            qs_g.append(qs)
+        xd = torch.from_numpy(np.stack(xs)).to(DEV)
+        if dt == "bf16":
+            xd = xd.to(torch.bfloat16)
+        xr = xd.float().cpu().numpy()
+        got = tq.quantize_split([[qs_g[g][p] for g in range(G)] for p in range(2)],
+                                [[parts_g[g][p]["channels"] for g in range(G)] for p in range(2)], xd,
+                                rot_dbg=True, proj_dbg=True)
+        torch.cuda.synchronize()
+        for g in range(G):
+            ref = O.quantize_split(xr[g], parts_g[g])
+            assert ref[0]["nu"][g] == 0
+            for p in range(2):
+                _check_part(parts_g[g][p], qs_g[g][p], {k: v[g] for k, v in got[p].items()}, ref[p])
 
 
 def _pack(parts, qs, ref):
@@ -188,18 +242,28 @@ def test_split_rejects_bad_channel_lists(gpu_lib):
     recs = [{"norms": torch.empty(4, device=DEV), "codes": torch.empty((4, q.code_bytes), dtype=torch.uint8, device=DEV)}
             for q in (qa, qb)]
     ok = np.arange(64, dtype=np.int32)
-    assert lib.tq_quantize_split(hs, 2, ok.ctypes.data, 64, x.data_ptr(), tq.TQ_F32, 4, tq._records(recs), None) == tq.TQ_OK
+    call = lambda h, ng, ch, dim, n=4: lib.tq_quantize_split(h, 2, ng, ch.ctypes.data, dim, x.data_ptr(), tq.TQ_F32, n,
+                                                             tq._records(recs), None)
+    assert call(hs, 1, ok, 64) == tq.TQ_OK
     rep = ok.copy()
     rep[40] = 5
-    assert lib.tq_quantize_split(hs, 2, rep.ctypes.data, 64, x.data_ptr(), tq.TQ_F32, 4, tq._records(recs), None) == \
-        tq.TQ_ERR_INVALID_ARG
+    assert call(hs, 1, rep, 64) == tq.TQ_ERR_INVALID_ARG
     assert b"twice" in lib.tq_last_error_message()
     far = ok.copy()
     far[0] = 64
-    assert lib.tq_quantize_split(hs, 2, far.ctypes.data, 64, x.data_ptr(), tq.TQ_F32, 4, tq._records(recs), None) == \
-        tq.TQ_ERR_INVALID_ARG
-    assert lib.tq_quantize_split(hs, 2, ok.ctypes.data, 48, x.data_ptr(), tq.TQ_F32, 4, tq._records(recs), None) == \
-        tq.TQ_ERR_INVALID_ARG
-    assert lib.tq_quantize_split(hs, 2, ok.ctypes.data, 600, x.data_ptr(), tq.TQ_F32, 4, tq._records(recs), None) == \
-        tq.TQ_ERR_UNSUPPORTED
+    assert call(hs, 1, far, 64) == tq.TQ_ERR_INVALID_ARG
+    assert call(hs, 1, ok, 48) == tq.TQ_ERR_INVALID_ARG
+    assert call(hs, 1, ok, 600) == tq.TQ_ERR_UNSUPPORTED
+    assert call(hs, 0, ok, 64) == tq.TQ_ERR_INVALID_ARG
+    # two groups of two rows: part 0's handles must agree across the groups
+    qc = tq.Quantizer(32, 4, "mse", syn.rotation(32, syn.CFG_TEST, syn.T_K, 92))
+    two = np.concatenate([ok[:32], ok[:32], ok[32:], ok[32:]]).astype(np.int32)
+    assert call(tq._handles([qa, qa, qb, qb]), 2, two, 64, 2) == tq.TQ_OK
+    assert call(tq._handles([qa, qc, qb, qb]), 2, two, 64, 2) == tq.TQ_ERR_INVALID_ARG
+    assert b"differ across groups" in lib.tq_last_error_message()
+    # group 1 repeats a channel of its own
+    bad = two.copy()
+    bad[64 + 32] = bad[32]
+    assert call(tq._handles([qa, qa, qb, qb]), 2, bad, 64, 2) == tq.TQ_ERR_INVALID_ARG
+    assert b"group 1" in lib.tq_last_error_message()
     torch.cuda.synchronize()
