@@ -49,7 +49,7 @@ def parse():
                     help="counter summary with the measured HBM bytes per decode launch (default: profiles/)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy 1 GiB device to device 3 times (scale reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["quantize", "decode", "append"], default=None,
+    ap.add_argument("--only", choices=["quantize", "decode", "append", "split_decode"], default=None,
                     help="profiling runs: build the headline workload, then run only this stage "
                          "warmup + steps times and print its mean time (no JSON line)")
     return ap.parse_args()
@@ -526,6 +526,9 @@ def main():
     tq.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only == "split_decode":
+        print(json.dumps(outlier_split_decode(tq, syn, torch, dev, reps=max(args.steps, 1))), flush=True)
+        return 0
     print("building workloads", file=sys.stderr, flush=True)
     w = build_workloads(tq, syn, torch, dev)
 

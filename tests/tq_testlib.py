@@ -52,6 +52,27 @@ def allclose_report(got, want, rtol=RTOL, atol=ATOL):
     return int(bad.sum()), float(err.max()) if err.size else 0.0
 
 
+def assert_scores_close(got, want, y, xt, rtol=RTOL, atol=ATOL):
+    """Inner products against the oracle, element by element:
+        |got_ij - want_ij| <= atol * sigma_ij + rtol * |want_ij|,
+    sigma_ij = |y_i| |xt_j| / sqrt(d), the spread of <y_i, x> over directions of
+    x. The score tolerance (rel 1e-3 / abs 1e-4) is stated for attention scores,
+    which the 1/sqrt(d) scaling of unit-variance vectors brings to unit spread;
+    for raw inner products of any scale its absolute part is read in those units
+    (fp32 rounding grows with |y| |x|, so no fixed absolute bar fits every scale)."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    xt = np.asarray(xt, dtype=np.float64)
+    sigma = np.linalg.norm(y, axis=1)[:, None] * np.linalg.norm(xt, axis=1)[None, :] / math.sqrt(y.shape[1])
+    err = np.abs(got - want)
+    bar = atol * sigma + rtol * np.abs(want)
+    bad = err > bar
+    worst = float(np.max(err / np.where(bar > 0, bar, 1.0))) if err.size else 0.0
+    assert not bad.any(), f"{int(bad.sum())} of {err.size} scores outside the bar (worst err/bar {worst:.3g})"
+    return worst
+
+
 def near_threshold(y, centroids, band=TIE_BAND):
     mids = (centroids[:-1] + centroids[1:]) / 2
     if mids.size == 0:
