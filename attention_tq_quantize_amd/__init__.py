@@ -94,7 +94,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tq_quantizer_sizes.argtypes = [_VP, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
     lib.tq_dequantize.argtypes = [_VP, _I, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
     lib.tq_inner_products.argtypes = [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP, _VP]
-    lib.tq_quantize_split.argtypes = [_VP, _I, _I, _VP, _I, _VP, _I, _I64, ctypes.POINTER(Records), _VP]
+    lib.tq_quantize_split.argtypes = [_VP, _I, _I, _VP, _I, _VP, _I, _I64, _I, ctypes.POINTER(Records), _VP]
     lib.tq_inner_products_split.argtypes = [_VP, _I, _VP, _I, _VP, _I64, ctypes.POINTER(Records), _I64, _VP, _VP]
     lib.tq_decode_split_workspace_size.argtypes = [ctypes.POINTER(AttnShape), ctypes.POINTER(SplitCache),
                                                    ctypes.POINTER(SplitCache), ctypes.POINTER(ctypes.c_size_t)]
@@ -426,9 +426,10 @@ class SplitQuantize:
     """A prepared tq_quantize_split call: the handles and channel lists are
     marshalled once. Single group (grouped=False): qs[p] a Quantizer, channels[p]
     its list, x [n, dim]. Grouped: qs[p][g], channels[p][g] per group g (e.g. per
-    KV head), x [G, n, dim]."""
+    KV head), x [G, n, dim]. layout "block32" (mse parts, n % 32 == 0) writes
+    the codes in blocks of 32 rows, the value layout of a split cache."""
 
-    def __init__(self, qs, channels, grouped: bool = False):
+    def __init__(self, qs, channels, grouped: bool = False, layout: str = "vector"):
         import numpy as np
         qg = qs if grouped else [[q] for q in qs]
         cg = channels if grouped else [[c] for c in channels]
@@ -446,6 +447,9 @@ class SplitQuantize:
                     raise ValueError("each part's channel list must have its quantizer's d entries")
                 lists.append(np.asarray(c, dtype=np.int32).ravel())
         self.grouped, self.G, self.parts = grouped, G, [qp[0] for qp in qg]
+        if layout not in ("vector", "block32"):
+            raise ValueError("layout must be 'vector' or 'block32'")
+        self.layout = TQ_LAYOUT_BLOCK32 if layout == "block32" else TQ_LAYOUT_VECTOR
         self._qs = qg  # keeps the handles alive
         self._ch = np.ascontiguousarray(np.concatenate(lists), dtype=np.int32)
         self._handles = (ctypes.c_void_p * (len(qg) * G))(*[q.handle.value for qp in qg for q in qp])
@@ -479,20 +483,23 @@ class SplitQuantize:
             elif len(out) != len(self.parts):
                 raise ValueError("out: one record dict per part")
         _check(lib.tq_quantize_split(self._handles, len(self.parts), self.G, self._ch.ctypes.data, dim, _ptr(x), dt, n,
-                                     _records(out), _stream(stream)), "tq_quantize_split")
+                                     self.layout, _records(out), _stream(stream)), "tq_quantize_split")
         return out
 
 
-def quantize_split(qs, channels, x, rot_dbg: bool = False, proj_dbg: bool = False, stream=None) -> list:
+def quantize_split(qs, channels, x, rot_dbg: bool = False, proj_dbg: bool = False, layout: str = "vector",
+                   stream=None) -> list:
     """Outlier-channel split (tq_quantize_split). Single group: x [n, dim], qs[p] a
     Quantizer and channels[p] its list; part p quantizes x[:, channels[p]] with qs[p].
     Grouped: x [G, n, dim], qs[p][g] and channels[p][g] per group g (e.g. per KV
     head). x is float32 or bfloat16 (CUDA); returns one record dict per part, with
-    a leading G axis in the grouped form."""
+    a leading G axis in the grouped form. layout "block32": codes of mse parts in
+    blocks of 32 rows (a split cache's values)."""
     _float_dtype(x, "x")
     if x.dim() not in (2, 3):
         raise ValueError("x must be [n, dim] or [G, n, dim]")
-    return SplitQuantize(qs, channels, grouped=x.dim() == 3)(x, rot_dbg=rot_dbg, proj_dbg=proj_dbg, stream=stream)
+    return SplitQuantize(qs, channels, grouped=x.dim() == 3, layout=layout)(x, rot_dbg=rot_dbg, proj_dbg=proj_dbg,
+                                                                            stream=stream)
 
 
 def inner_products_split(qs: Sequence[Quantizer], channels, y, recs, stream=None):
@@ -628,7 +635,8 @@ def decode_attention_noalloc(q, kcache: KVCache, vcache: KVCache, ctx_lens, out,
 @dataclass
 class SplitKV:
     """One side (keys or values) of a split cache: parts[p] = (quantizers per KV head,
-    channels, records dict of device tensors [B, Hkv, T, ...] / [B, Hkv, T]).
+    channels, records dict of device tensors [B, Hkv, T, ...] / [B, Hkv, T]); value
+    parts keep their codes in the block32 layout (quantize_split(..., layout="block32")).
     channels: [Hkv][d_p] (each KV head's own list) or [d_p] (the same list for
     every head)."""
     parts: Sequence[tuple]

@@ -501,8 +501,8 @@ static tq_status check_split(const tq_quantizer* const* qz, int n_parts, int n_g
 }
 
 tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, int n_groups, const int32_t* channels, int dim,
-                            const void* x, tq_dtype x_dtype, int64_t n_per_group, const tq_records* out,
-                            void* stream) {
+                            const void* x, tq_dtype x_dtype, int64_t n_per_group, tq_layout layout,
+                            const tq_records* out, void* stream) {
   std::vector<uint16_t> chan;
   std::vector<int64_t> off;
   tq_status st = check_split(qz, n_parts, n_groups, channels, dim, &chan, &off);
@@ -510,6 +510,13 @@ tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, int n_gr
   if (!out) return set_error(TQ_ERR_INVALID_ARG, "split: out is NULL");
   if (n_per_group < 0) return set_error(TQ_ERR_INVALID_ARG, "split: negative n_per_group");
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return set_error(TQ_ERR_INVALID_ARG, "split: x_dtype");
+  if (layout != TQ_LAYOUT_VECTOR && layout != TQ_LAYOUT_BLOCK32) return set_error(TQ_ERR_INVALID_ARG, "split: layout");
+  if (layout == TQ_LAYOUT_BLOCK32) {
+    if (n_per_group % 32) return set_error(TQ_ERR_INVALID_ARG, "split: BLOCK32 needs n_per_group % 32 == 0");
+    for (int p = 0; p < n_parts; ++p)
+      if (qz[(size_t)p * n_groups]->variant != TQ_MSE)
+        return set_error(TQ_ERR_UNSUPPORTED, fmt("split: BLOCK32 is for mse parts (part %d is prod)", p));
+  }
   if (n_per_group == 0) return TQ_OK;
   if (!x) return set_error(TQ_ERR_INVALID_ARG, "split: x is NULL");
   if ((int64_t)n_groups * n_per_group > (int64_t)1 << 31)
@@ -528,13 +535,20 @@ tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, int n_gr
     const tq_records& r = out[p];
     const tq_quantizer* const* qp = qz + (size_t)p * n_groups;
     const int dp = qp[0]->d;
+    const int64_t cb = (int64_t)qp[0]->planes * dp / 8;
+    // the kernels write the VECTOR layout; BLOCK32 repacks each 32-record block in place
+    auto finish = [&]() -> tq_status {
+      if (layout != TQ_LAYOUT_BLOCK32) return TQ_OK;
+      return launch_repack_block32(r.codes, (int64_t)n_groups * n_per_group / 32, qp[0]->planes, dp,
+                                   (hipStream_t)stream);
+    };
     if (quantize_split_fast(dim, qp[0])) {
       st = launch_quantize_split(qp, n_groups, n_per_group, chan.data() + off[p], x, x_dtype, r, (hipStream_t)stream);
+      if (st == TQ_OK) st = finish();
       if (st != TQ_OK) return st;
       continue;
     }
     // generic fp32 kernels: one launch per group
-    const int64_t cb = (int64_t)qp[0]->planes * dp / 8;
     for (int g = 0; g < n_groups; ++g) {
       const int64_t v0 = (int64_t)g * n_per_group;
       const tq_quantizer* one[1] = {qp[g]};
@@ -545,6 +559,8 @@ tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, int n_gr
       st = launch_quantize_fp32(a, chan.data() + off[p] + (size_t)g * dp, dim, (hipStream_t)stream);
       if (st != TQ_OK) return st;
     }
+    st = finish();
+    if (st != TQ_OK) return st;
   }
   return TQ_OK;
 }
@@ -652,6 +668,8 @@ static tq_status plan_split_decode(const tq_attn_shape* s, const tq_split_cache*
   if (s->head_dim < 16 || s->head_dim > kSplitMaxDecodeDim)
     return set_error(TQ_ERR_UNSUPPORTED, fmt("split decode: head_dim outside [16, %d]", kSplitMaxDecodeDim));
   if (s->max_ctx > ((int64_t)1 << 31)) return set_error(TQ_ERR_UNSUPPORTED, "split decode: max_ctx > 2^31");
+  if (s->max_ctx % 32)
+    return set_error(TQ_ERR_INVALID_ARG, "split decode: max_ctx % 32 != 0 (value codes are in blocks of 32 tokens)");
   tq_status st = check_split_side(k, s, false, &L->k, &plan->dk);
   if (st != TQ_OK) return st;
   st = check_split_side(v, s, true, &L->v, &plan->dv);

@@ -89,6 +89,9 @@ tq_status launch_quantize_fp32(const QuantizeLaunch& a, const uint16_t* chan, in
 // One part of a channel split over n_groups groups of d = 128 rows on the
 // matrix cores (tq_quantize.hip); chan: [n_groups][d_p] channel lists.
 bool quantize_split_fast(int dim, const tq_quantizer* q);
+// in-place VECTOR -> BLOCK32 repack of n_blocks blocks of 32 records (d a
+// multiple of 32, 4 planes d <= 8 KiB)
+tq_status launch_repack_block32(uint8_t* codes, int64_t n_blocks, int planes, int d, hipStream_t stream);
 tq_status launch_quantize_split(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group, const uint16_t* chan,
                                 const void* x, tq_dtype x_dtype, const tq_records& out, hipStream_t stream);
 tq_status launch_inner_products_fp32(const tq_quantizer* q, const float* y, int64_t y_stride, const uint16_t* chan,

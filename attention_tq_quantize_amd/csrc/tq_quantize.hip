@@ -784,6 +784,47 @@ tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream) {
   return TQ_OK;
 }
 
+// In-place VECTOR -> BLOCK32 repack of the codes of 32-vector blocks (one
+// workgroup per block): the block's 32 records, 4 planes d bytes together, are
+// read into LDS, then every 32-bit block word is assembled from its 32 bits
+// (word (p, g, w): bit 4r+k = plane p of coordinate 4w+r of block vector 4g+k,
+// bit 16+4r+k the same for vector 16+4g+k) and written over the block.
+constexpr int kRepackThreads = 256;
+constexpr int kRepackMaxBytes = 4 * 4 * 512;  // 4 planes, d <= 512
+__global__ __launch_bounds__(kRepackThreads) void repack_block32_kernel(uint8_t* codes, int planes, int d) {
+  __shared__ unsigned rec[kRepackMaxBytes / 4];
+  const int words = planes * d;  // 32-bit words per block (= 32 records of planes d / 8 bytes)
+  unsigned* blk = (unsigned*)(codes + (int64_t)blockIdx.x * 4 * words);
+  for (int i = threadIdx.x; i < words; i += kRepackThreads) rec[i] = blk[i];
+  __syncthreads();
+  const uint8_t* rb = (const uint8_t*)rec;
+  const int rbytes = planes * d / 8;  // one record
+  for (int i = threadIdx.x; i < words; i += kRepackThreads) {
+    const int w = i % (d / 4), pg = i / (d / 4);
+    const int g = pg & 3, p = pg >> 2;
+    unsigned word = 0u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int v = 16 * h + 4 * g + k, j = 4 * w + r;
+          const unsigned bit = (rb[v * rbytes + p * (d / 8) + j / 8] >> (j % 8)) & 1u;
+          word |= bit << (16 * h + 4 * r + k);
+        }
+    blk[i] = word;  // every read of the block happened before the barrier
+  }
+}
+
+tq_status launch_repack_block32(uint8_t* codes, int64_t n_blocks, int planes, int d, hipStream_t stream) {
+  if (n_blocks <= 0 || planes <= 0) return TQ_OK;
+  if (d % 32 || 4 * planes * d > kRepackMaxBytes || n_blocks > 0x7FFFFFFF)
+    return set_error(TQ_ERR_UNSUPPORTED, "block repack: d, planes or size out of range");
+  hipLaunchKernelGGL(repack_block32_kernel, dim3((unsigned)n_blocks), dim3(kRepackThreads), 0, stream, codes, planes, d);
+  return launch_check("block repack: launch");
+}
+
 bool quantize_split_fast(int dim, const tq_quantizer* q) {
   const bool prod = q->variant == TQ_PROD;
   // the kernel builds its fragments from pi32 and, for prod, sp32

@@ -25,11 +25,14 @@
 //        <q', c~> and <q'', z> for 16 tokens x 8 heads per instruction;
 //      * an online softmax per head over the chunk (16-lane reductions);
 //      * values: the probabilities times each value part's norms become the
-//        fp16 hi/lo weight operand (rows = 8 heads x {hi, lo}, K = 32 tokens),
-//        each lane turns one coordinate of two tokens at a time into the
-//        centroid operand, and the matrix cores accumulate 16 coordinates x 8
-//        heads per instruction in the part's rotated basis (a running
-//        power-of-two exponent per part keeps the weights in fp16 range);
+//        fp16 hi/lo weight operand (rows = 8 heads x {hi, lo}, K = 32 tokens in
+//        the BLOCK32 token order); the value codes are BLOCK32, so one word per
+//        plane holds a lane's coordinate for all eight of its tokens, and each
+//        lane turns two tokens at a time into the centroid operand with one
+//        bit-field extract per plane and one pair-table read; the matrix cores
+//        accumulate 16 coordinates x 8 heads per instruction in the part's
+//        rotated basis (a running power-of-two exponent per part keeps the
+//        weights in fp16 range);
 //  3. combine, one workgroup per (batch, query head): log-sum-exp merge of the
 //     splits, each value part rotated back (Pi_p^T) and scattered to its
 //     channels (deterministic, no atomics).
@@ -65,6 +68,7 @@ struct SmPart {
 struct SmSeg {  // one per-token array of one part: elem bytes per token, [B * Hkv][T][elem]
   const uint8_t* base;
   int elem, lds;
+  int blocked;  // BLOCK32 codes: a chunk is one whole block (no per-token clamp)
 };
 
 struct SmParams {
@@ -294,7 +298,9 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
     for (int si = 0; si < prm.n_seg; ++si) {
       const SmSeg S = prm.seg[si];
       const int wpt = S.elem >> 2;
-      const int nd = kSmChunk * wpt, nvd = nvalid * wpt;
+      // per-token arrays: tokens at or beyond t1 read copies of the last valid
+      // dword; a BLOCK32 chunk is read whole (its block lies inside max_ctx)
+      const int nd = kSmChunk * wpt, nvd = S.blocked ? nd : nvalid * wpt;
       const unsigned* src = (const unsigned*)(S.base + ((int64_t)bgi * prm.T + c0) * S.elem);
       for (int e0 = 0; e0 < nd; e0 += 64) {
         const int e = e0 + lane;
@@ -454,36 +460,40 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
         if (wd == 0) {  // first word of this part: its weight operand
           const int ev = evs[p];
           const float wsc = ev == kSmEvUnset ? 0.f : ldexpf(1.f, -ev);
-          const float4* wr = (const float4*)(wts + (r16 >> 1) * kSmChunk + 8 * g4);
-          const float4* nr = (const float4*)(sb + P.st_norms + 4 * 8 * g4);
-          const float4 wa = wr[0], wb = wr[1], na = nr[0], nb = nr[1];
+          // K slots 0-3 of lane group g4 are tokens 4 g4 + k, slots 4-7 tokens
+          // 16 + 4 g4 + k: the token order of a BLOCK32 word's two halves
+          const float* wr = wts + (r16 >> 1) * kSmChunk + 4 * g4;
+          const float* nr = (const float*)(sb + P.st_norms) + 4 * g4;
+          const float4 wa = *(const float4*)wr, wb = *(const float4*)(wr + 16);
+          const float4 na = *(const float4*)nr, nb = *(const float4*)(nr + 16);
           const float x[8] = {wa.x * na.x * wsc, wa.y * na.y * wsc, wa.z * na.z * wsc, wa.w * na.w * wsc,
                               wb.x * nb.x * wsc, wb.y * nb.y * wsc, wb.z * nb.z * wsc, wb.w * nb.w * wsc};
           const bool lo = r16 & 1;
 #pragma unroll
           for (int v = 0; v < 4; ++v) aw[v] = f16_part(x[2 * v], lo) | (f16_part(x[2 * v + 1], lo) << 16);
         }
-        // one 32-coordinate word of a value part with PL planes: two tiles of 16 coordinates
+        // one 32-coordinate word of a value part with PL planes: two tiles of 16
+        // coordinates. BLOCK32 codes: block word (pl, g4, c / 4) holds plane pl of
+        // coordinate c for this lane's eight tokens, nibble c % 4 of each half.
         auto value_word = [&](auto PLc) {
           constexpr int PL = decltype(PLc)::value;
-          const int dq = P.d >> 3, rec = P.rec;
-          const uint8_t* vc = sb + P.st_codes + 4 * wd;
+          const int d4 = P.d >> 2;
+          const uint8_t* vc = sb + P.st_codes;
           const uint2* tv = (const uint2*)(lds + prm.tab_off + P.ptab);
-          unsigned w[8][PL];
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int pl = 0; pl < PL; ++pl) w[e][pl] = lds_u32(vc + (8 * g4 + e) * rec + pl * dq);
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            const unsigned bit = 16 * hf + r16;
+            const int c = 32 * wd + 16 * hf + r16;  // coordinate within the part
+            const unsigned nib = 4u * (unsigned)(c & 3);
+            unsigned w[PL];
+#pragma unroll
+            for (int pl = 0; pl < PL; ++pl) w[pl] = lds_u32(vc + 4 * ((pl * 4 + g4) * d4 + (c >> 2)));
             u32x4 bh, bl;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {  // tokens 8 g4 + 2v, + 1
-              unsigned pi = bfe<1>(w[2 * v][0], bit) | (bfe<1>(w[2 * v + 1][0], bit) << 1);
+            for (int v = 0; v < 4; ++v) {  // K slots 2v, 2v + 1: two tokens of one half
+              const unsigned at = nib + 16u * (unsigned)(v >> 1) + 2u * (unsigned)(v & 1);
+              unsigned pi = bfe<2>(w[0], at);
 #pragma unroll
-              for (int pl = 1; pl < PL; ++pl)
-                pi |= (bfe<1>(w[2 * v][pl], bit) | (bfe<1>(w[2 * v + 1][pl], bit) << 1)) << (2 * pl);
+              for (int pl = 1; pl < PL; ++pl) pi |= bfe<2>(w[pl], at) << (2 * pl);
               const uint2 en = tv[pi];
               bh[v] = en.x;
               bl[v] = en.y;
@@ -627,9 +637,9 @@ static void build_split_params(const SplitDecodeLaunch& L, SmParams& prm, size_t
   prm.split_tokens = L.split_tokens;
   // staging buffer of one wave: every part's per-token arrays for 32 tokens, 16-byte aligned
   int st = 0;
-  auto add_seg = [&](const void* base, int elem) -> int {
+  auto add_seg = [&](const void* base, int elem, bool blocked = false) -> int {
     const int at = st;
-    prm.seg[prm.n_seg++] = SmSeg{(const uint8_t*)base, elem, at};
+    prm.seg[prm.n_seg++] = SmSeg{(const uint8_t*)base, elem, at, blocked ? 1 : 0};
     st += (kSmChunk * elem + 15) / 16 * 16;
     return at;
   };
@@ -646,7 +656,8 @@ static void build_split_params(const SplitDecodeLaunch& L, SmParams& prm, size_t
       P.off = off;
       P.qjl = side == 0 && q0->variant == TQ_PROD;
       P.rec = P.planes * P.d / 8;
-      if (P.planes > 0) P.st_codes = add_seg(S.codes[p], P.rec);
+      // value codes in BLOCK32: a 32-token block is 32 rec bytes, like 32 records
+      if (P.planes > 0) P.st_codes = add_seg(S.codes[p], P.rec, side == 1);
       if (P.qjl) P.st_signs = add_seg(S.signs[p], P.d / 8);
       P.st_norms = add_seg(S.norms[p], 4);
       if (P.qjl) P.st_rnorms = add_seg(S.rnorms[p], 4);

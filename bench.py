@@ -440,7 +440,7 @@ def outlier_split_decode(tq, syn, torch, dev, reps=10, bits=(3, 2)):
         for b in range(B):
             # one grouped call per batch row: the KV heads are the groups
             x = syn.kv_vectors_device(Hkv, T, d, syn.CFG_DECODE_128K, tensor, dev, seed_offset=b)
-            got = tq.quantize_split(qs_p, chans_p, x)
+            got = tq.quantize_split(qs_p, chans_p, x, layout="block32" if var == "mse" else "vector")
             for p in range(2):
                 for key, val in got[p].items():
                     recs[p][key][b].copy_(val.view(recs[p][key][b].shape))
@@ -479,7 +479,8 @@ def outlier_split(tq, syn, torch, dev, w, flush, bits=(3, 2)):
     at bits[1] (3 + 2: 2.25 bits per channel; 4 + 3: 3.25), keys TurboQuant_prod,
     values TurboQuant_mse, through tq_quantize_split: one grouped call per tensor
     (the heads are the groups, each with its own channels and quantizers; one
-    matrix-core launch per part)."""
+    matrix-core launch per part; the values' codes in the BLOCK32 layout the
+    split decode reads, one in-place repack launch per value part)."""
     H, T2, d = w["H"], w["T2"], w["d"]
     calls = []
     for t, xs, var in ((syn.T_K, w["xk2"], "prod"), (syn.T_V, w["xv2"], "mse")):
@@ -492,7 +493,7 @@ def outlier_split(tq, syn, torch, dev, w, flush, bits=(3, 2)):
                 S = syn.gaussian_matrix(dp, syn.CFG_LAYER_QUANT, t, 100 + 2 * h + i) if var == "prod" else None
                 qs[i].append(tq.Quantizer(dp, pbits, var, syn.rotation(dp, syn.CFG_LAYER_QUANT, t, 100 + 2 * h + i), S))
                 chans[i].append(c)
-        sq = tq.SplitQuantize(qs, chans, grouped=True)
+        sq = tq.SplitQuantize(qs, chans, grouped=True, layout="block32" if var == "mse" else "vector")
         calls.append((sq, xs, sq(xs)))
     run = lambda: [sq(x, out=o) for sq, x, o in calls]
     run()
@@ -500,7 +501,7 @@ def outlier_split(tq, syn, torch, dev, w, flush, bits=(3, 2)):
     nvec = 2 * H * T2
     per_ch = (32 * bits[0] + 96 * bits[1]) / 128
     return {"split": f"32 ch x {bits[0]} b + 96 ch x {bits[1]} b ({per_ch} bits/channel), keys prod, values mse",
-            "vectors": nvec, "launches": 4,
+            "vectors": nvec, "launches": 6,
             "ms": round(ms, 4), "ms_p10_p90": [round(ms10, 4), round(ms90, 4)], "mvec_s": round(nvec / (ms * 1e-3) / 1e6, 1),
             "input_gb_s": round(nvec * d * 2 / (ms * 1e-3) / 1e9, 1)}
 

@@ -234,17 +234,21 @@ tq_status tq_inner_products(const tq_quantizer* q, const float* y, int64_t m,
  *              repeated within a group; channels left out are dropped. Copied.
  *   dim      : channels per input row, at most 512.
  *   x        : device [n_groups*n_per_group][dim], float32 or bfloat16.
+ *   layout   : TQ_LAYOUT_VECTOR, or TQ_LAYOUT_BLOCK32 (every part mse,
+ *              n_per_group % 32 == 0): each part's codes in blocks of 32 rows,
+ *              the value-cache layout tq_decode_attention_split reads.
  *   out      : host array [n_parts] of device record buffers for all
  *              n_groups*n_per_group rows, as for tq_quantize with d = d_p
  *              (rot_dbg / proj_dbg may be NULL; codes and signs 4-byte aligned).
  * On the caller's stream. dim = 128 with d_p a multiple of 32 (mse, or prod of
  * at most 4 bits): one matrix-core launch per part and 16 groups, the part's
  * matrices laid over the head's channels. Otherwise the generic fp32 kernels,
- * one launch per part and group. Allocates nothing.
+ * one launch per part and group. BLOCK32 adds one in-place repack launch per
+ * part. Allocates nothing.
  * Errors: TQ_ERR_INVALID_ARG (NULL pointers, n_groups < 1, handles of a part
  * that differ, a channel out of range or repeated within a group, more
- * channels than dim), TQ_ERR_UNSUPPORTED (dim > 512, n_groups*n_per_group >
- * 2^31).
+ * channels than dim, BLOCK32 with n_per_group % 32 != 0), TQ_ERR_UNSUPPORTED
+ * (dim > 512, n_groups*n_per_group > 2^31, BLOCK32 with a prod part).
  */
 typedef struct {
   uint8_t* codes;   /* code_planes*d/8 bytes per vector (NULL when code_planes == 0) */
@@ -255,8 +259,8 @@ typedef struct {
   float* proj_dbg;  /* optional [n][d] (prod) */
 } tq_records;
 tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, int n_groups, const int32_t* channels,
-                            int dim, const void* x, tq_dtype x_dtype, int64_t n_per_group, const tq_records* out,
-                            void* stream);
+                            int dim, const void* x, tq_dtype x_dtype, int64_t n_per_group, tq_layout layout,
+                            const tq_records* out, void* stream);
 /*
  * Inner products of m float32 queries y [m][dim] with n split records:
  *   out[i][j] = sum_p <y_i restricted to part p's channels, x~_p,j>
@@ -420,8 +424,10 @@ tq_status tq_decode_append_attention(const tq_attn_shape* shape, const void* q, 
  * ([NIK] "Experiments", KV cache: outlier channels at more bits; the same
  * attention as tq_decode_attention, scores and outputs over the channels the
  * parts keep). Each side (keys, values) is a split of the head's channels into
- * parts, part p quantized per KV head in the VECTOR layout (records
- * [B][n_kv_heads][max_ctx], as tq_quantize_split writes them per head):
+ * parts, part p quantized per KV head (records [B][n_kv_heads][max_ctx], as
+ * tq_quantize_split writes them with the KV heads as groups): key parts in the
+ * VECTOR layout, value parts in the BLOCK32 layout (codes
+ * [B][n_kv_heads][max_ctx/32][4*planes*d_p]; max_ctx % 32 == 0):
  *   s_t = scale * sum_p <q restricted to key part p's channels, k~_{p,t}>
  *   out[b,h] = sum_{t < ctx_lens[b]} softmax(s)_t v~_t, each value part written
  *   to its channels (channels no value part keeps are 0; ctx_lens[b] <= 0 gives
@@ -444,8 +450,8 @@ tq_status tq_decode_append_attention(const tq_attn_shape* shape, const void* q, 
  * rotated query operands; the size depends on the device, which sets the number
  * of context splits). Scores and value sums run on the matrix cores as exact
  * fp16 hi/lo products, split context with a log-sum-exp combine
- * (deterministic). Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED (limits
- * above), TQ_ERR_WORKSPACE.
+ * (deterministic). Errors: TQ_ERR_INVALID_ARG (also max_ctx % 32 != 0),
+ * TQ_ERR_UNSUPPORTED (limits above), TQ_ERR_WORKSPACE.
  */
 typedef struct {
   int n_parts;

@@ -150,7 +150,7 @@ def test_search_argument_errors(lib):
 
 def test_split_argument_errors(lib):
     ch = (ctypes.c_int32 * 4)(0, 1, 2, 3)
-    assert lib.tq_quantize_split(None, 1, 1, ch, 4, None, 0, 1, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_quantize_split(None, 1, 1, ch, 4, None, 0, 1, 0, None, None) == tq.TQ_ERR_INVALID_ARG
     assert lib.tq_inner_products_split(None, 1, ch, 4, None, 1, None, 1, None, None) == tq.TQ_ERR_INVALID_ARG
 
 
@@ -170,6 +170,7 @@ def test_split_decode_argument_errors(lib):
                        (tq.AttnShape(1, 12, 8, 128, 64), tq.TQ_ERR_UNSUPPORTED),    # heads do not divide
                        (tq.AttnShape(1, 8, 1, 512, 64), tq.TQ_ERR_UNSUPPORTED),     # head_dim above 256
                        (tq.AttnShape(1, 8, 1, 128, 1 << 32), tq.TQ_ERR_UNSUPPORTED),
+                       (tq.AttnShape(1, 8, 1, 128, 100), tq.TQ_ERR_INVALID_ARG),    # value blocks need max_ctx % 32 == 0
                        (ok_shape, tq.TQ_ERR_INVALID_ARG)):                          # NULL cache description
         assert lib.tq_decode_split_workspace_size(ctypes.byref(shape), ctypes.byref(empty), ctypes.byref(empty),
                                                   ctypes.byref(nb)) == err, (shape.n_q_heads, shape.n_kv_heads)

@@ -1,7 +1,8 @@
 """GPU parity of decode attention over an outlier-split cache at the full
 benchmark size (batch 8, 64/8 heads, head_dim 128, context 131072; keys
 TurboQuant_prod with 32 channels at 3 bits and 96 at 2, each KV head with its
-own channel lists, values TurboQuant_mse with the same split; [NIK]
+own channel lists, values TurboQuant_mse with the same split, codes in the
+BLOCK32 layout; [NIK]
 "Experiments", KV cache), in the launch
 configuration the benchmark times. Two sampled (batch, KV head) groups are
 quantized and packed by the fp64 oracle from seeded vectors with per-token
@@ -67,7 +68,10 @@ def _pack_group(x, spec, parts_g, recs, b, g):
     for p, (n, var, bits) in enumerate(spec):
         planes = _planes(bits, var)
         recs[p]["norms"][b, g] = torch.from_numpy(res[p]["norms"].astype(np.float32)).to(DEV)
-        recs[p]["codes"][b, g] = torch.from_numpy(O.pack_vector_layout(res[p]["idx"], planes)).to(DEV)
+        # keys VECTOR, values (mse) BLOCK32, the layouts of a split cache
+        pack = O.pack_vector_layout if var == "prod" else O.pack_block_layout
+        codes = pack(res[p]["idx"], planes).reshape(T, planes * n // 8)
+        recs[p]["codes"][b, g] = torch.from_numpy(codes).to(DEV)
         if var == "prod":
             recs[p]["signs"][b, g] = torch.from_numpy(O.pack_bits(res[p]["signs"])).to(DEV)
             recs[p]["rnorms"][b, g] = torch.from_numpy(res[p]["rnorms"].astype(np.float32)).to(DEV)

@@ -171,6 +171,46 @@ def test_split_quantize_grouped_parity(gpu_lib, dt):
                 _check_part(parts_g[g][p], qs_g[g][p], {k: v[g] for k, v in got[p].items()}, ref[p])
 
 
+@pytest.mark.parametrize("dim,spec", [(128, [(32, 3), ("rest", 2)]), (192, [(64, 4), ("rest", 1)])],
+                         ids=["matrix_cores_32x3_96x2", "generic_64x4_128x1"])
+def test_split_quantize_block32(gpu_lib, dim, spec):
+    """layout="block32" (the value layout of a split cache): every part's codes
+    equal the oracle's BLOCK32 packing of the indices the kernel's own rotated
+    coordinates give, over two groups of 96 rows; norms as in the VECTOR layout."""
+    tq = gpu_lib
+    G, n = 2, 96
+    print(f"split quantize block32 dim={dim}", flush=True)
+    xs, parts_g, qs_g = [], [], []
+    for g in range(G):
+        x = syn.kv_vectors(n, dim, syn.CFG_TEST, syn.T_V, g, 9, lognormal_sigma=0.5)
+        x[5 + g] = 0.0
+        specs, _ = _split_specs(x, [(k, "mse", b) for k, b in spec])
+        parts, qs = _parts(tq, specs, 80 + 5 * g)
+        xs.append(x)
+        parts_g.append(parts)
+        qs_g.append(qs)
+    xd = torch.from_numpy(np.stack(xs)).to(DEV).to(torch.bfloat16)
+    xr = xd.float().cpu().numpy()
+    args = ([[qs_g[g][p] for g in range(G)] for p in range(2)], [[parts_g[g][p]["channels"] for g in range(G)]
+                                                                   for p in range(2)], xd)
+    vec = tq.quantize_split(*args, rot_dbg=True)
+    blk = tq.quantize_split(*args, rot_dbg=True, layout="block32")
+    torch.cuda.synchronize()
+    for g in range(G):
+        ref = O.quantize_split(xr[g], parts_g[g])
+        for p in range(2):
+            q = qs_g[g][p]
+            assert torch.equal(blk[p]["norms"][g], vec[p]["norms"][g])
+            assert torch.equal(blk[p]["rot"][g], vec[p]["rot"][g])
+            rot = blk[p]["rot"][g].cpu().numpy().astype(np.float64)
+            fed = O.nearest_index(rot, parts_g[g][p]["centroids"])
+            fed[~(ref[p]["nu"] > 0)] = 0
+            want = O.pack_block_layout(fed, q.planes).reshape(n, -1)
+            assert np.array_equal(blk[p]["codes"][g].cpu().numpy(), want), (g, p)
+    with pytest.raises(RuntimeError):
+        tq.quantize_split(args[0], args[1], xd[:, :80], layout="block32")  # 80 rows: not whole blocks
+
+
 def _pack(parts, qs, ref):
     recs = []
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
@@ -242,8 +282,8 @@ def test_split_rejects_bad_channel_lists(gpu_lib):
     recs = [{"norms": torch.empty(4, device=DEV), "codes": torch.empty((4, q.code_bytes), dtype=torch.uint8, device=DEV)}
             for q in (qa, qb)]
     ok = np.arange(64, dtype=np.int32)
-    call = lambda h, ng, ch, dim, n=4: lib.tq_quantize_split(h, 2, ng, ch.ctypes.data, dim, x.data_ptr(), tq.TQ_F32, n,
-                                                             tq._records(recs), None)
+    call = lambda h, ng, ch, dim, n=4, lay=tq.TQ_LAYOUT_VECTOR: lib.tq_quantize_split(
+        h, 2, ng, ch.ctypes.data, dim, x.data_ptr(), tq.TQ_F32, n, lay, tq._records(recs), None)
     assert call(hs, 1, ok, 64) == tq.TQ_OK
     rep = ok.copy()
     rep[40] = 5
@@ -255,6 +295,12 @@ def test_split_rejects_bad_channel_lists(gpu_lib):
     assert call(hs, 1, ok, 48) == tq.TQ_ERR_INVALID_ARG
     assert call(hs, 1, ok, 600) == tq.TQ_ERR_UNSUPPORTED
     assert call(hs, 0, ok, 64) == tq.TQ_ERR_INVALID_ARG
+    assert call(hs, 1, ok, 64, lay=7) == tq.TQ_ERR_INVALID_ARG
+    assert call(hs, 1, ok, 64, lay=tq.TQ_LAYOUT_BLOCK32) == tq.TQ_ERR_INVALID_ARG  # 4 rows: not whole blocks
+    qp = tq.Quantizer(32, 2, "prod", syn.rotation(32, syn.CFG_TEST, syn.T_K, 93),
+                      syn.gaussian_matrix(32, syn.CFG_TEST, syn.T_K, 93))
+    assert call(tq._handles([qp, qb]), 1, ok, 64, 32, tq.TQ_LAYOUT_BLOCK32) == tq.TQ_ERR_UNSUPPORTED
+    assert b"mse parts" in lib.tq_last_error_message()
     # two groups of two rows: part 0's handles must agree across the groups
     qc = tq.Quantizer(32, 4, "mse", syn.rotation(32, syn.CFG_TEST, syn.T_K, 92))
     two = np.concatenate([ok[:32], ok[:32], ok[32:], ok[32:]]).astype(np.int32)

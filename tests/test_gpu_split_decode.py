@@ -1,7 +1,8 @@
 """GPU parity of decode attention over outlier-split caches
 (tq_decode_attention_split; [NIK] "Experiments", KV cache: outlier channels at
 more bits) against the oracle's decode_attention_split on oracle-packed
-records: outputs within rtol 1e-3 / atol 1e-4. Cases: the pages' split of a
+records (keys VECTOR, values BLOCK32): outputs within rtol 1e-3 / atol 1e-4.
+Cases: the pages' split of a
 128-channel head (32 channels at 3 bits, 96 at 2; prod keys, mse values) with
 GQA 8 and ragged lengths; every KV head with its own channel lists (its
 largest-RMS channels); parts that drop channels, with different channel
@@ -72,7 +73,11 @@ def _build_side(tq, B, Hkv, T, dim, spec, tensor, seed):
                 planes = bits - 1 if var == "prod" else bits
                 recs[p]["norms"][b, g] = res[p]["norms"]
                 if planes:
-                    recs[p]["codes"][b, g] = O.pack_vector_layout(res[p]["idx"], planes)
+                    # keys VECTOR, values (mse) BLOCK32, the layouts of a split cache
+                    if tensor == syn.T_K:
+                        recs[p]["codes"][b, g] = O.pack_vector_layout(res[p]["idx"], planes)
+                    else:
+                        recs[p]["codes"][b, g] = O.pack_block_layout(res[p]["idx"], planes).reshape(T, -1)
                 if var == "prod":
                     recs[p]["signs"][b, g] = O.pack_bits(res[p]["signs"])
                     recs[p]["rnorms"][b, g] = res[p]["rnorms"]
@@ -117,6 +122,7 @@ def test_split_decode_parity(gpu_lib, case):
     tq = gpu_lib
     name, B, Hq, Hkv, dim, T, lens, kspec, vspec = case
     print(f"split decode {name}", flush=True)
+    T = -(-T // 32) * 32  # the value blocks need a context of whole 32-token blocks
     k, ok = _build_side(tq, B, Hkv, T, dim, kspec, syn.T_K, 11)
     v, ov = _build_side(tq, B, Hkv, T, dim, vspec, syn.T_V, 21)
     q = syn.decode_queries(B, Hq, dim, syn.CFG_TEST)
