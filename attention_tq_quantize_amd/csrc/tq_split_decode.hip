@@ -225,8 +225,48 @@ __global__ __launch_bounds__(kSmThreads) void split_prep_kernel(SmParams prm) {
   }
 }
 
-template <int NW>  // 32-coordinate words of the value vector, at most
-__global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3))) void split_main_kernel(SmParams prm) {
+// Part configurations of the main kernel. SmDyn reads every part's shape from
+// the kernel arguments at run time; SmPages fixes the pages' split of a
+// 128-channel head (32 outlier channels, then 96; keys prod, values mse, each
+// part with its own plane count) at compile time, so the part loops, the
+// staging copies and every record offset fold into constants.
+struct SmDyn {
+  static constexpr bool fixed = false;
+  static constexpr int nk = 0, nv = 0, dv = 0, nseg = 0;
+  static constexpr int kd[1] = {0}, kpl[1] = {0}, vd[1] = {0}, vpl[1] = {0};
+  __host__ __device__ static constexpr int koff(int) { return 0; }
+  __host__ __device__ static constexpr int voff(int) { return 0; }
+  __host__ __device__ static constexpr int vpart(int) { return 0; }
+  __host__ __device__ static constexpr int seg_elem(int) { return 0; }
+  __host__ __device__ static constexpr bool seg_blocked(int) { return false; }
+};
+template <int KP0, int KP1, int VP0, int VP1>
+struct SmPages {
+  static_assert(KP0 > 0 && KP1 > 0 && VP0 > 0 && VP1 > 0, "every part has code planes");
+  static constexpr bool fixed = true;
+  static constexpr int nk = 2, nv = 2, dv = 128, nseg = 12;
+  static constexpr int kd[2] = {32, 96}, kpl[2] = {KP0, KP1}, vd[2] = {32, 96}, vpl[2] = {VP0, VP1};
+  __host__ __device__ static constexpr int koff(int p) { return p ? 32 : 0; }
+  __host__ __device__ static constexpr int voff(int p) { return p ? 32 : 0; }
+  __host__ __device__ static constexpr int vpart(int np) { return np ? 1 : 0; }
+  // staging segments, in the order the host adds them: per key part its codes,
+  // signs, norms and residual norms; per value part its codes (BLOCK32) and norms
+  __host__ __device__ static constexpr int seg_elem(int si) {
+    return si == 0 ? 4 * KP0 : si == 4 ? 12 * KP1 : si == 8 ? 4 * VP0 : si == 10 ? 12 * VP1 : si == 5 ? 12 : 4;
+  }
+  __host__ __device__ static constexpr bool seg_blocked(int si) { return si == 8 || si == 10; }
+};
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int NW, class C>  // NW: 32-coordinate words of the value vector, at most
+__global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(C::fixed ? 3 : (NW == 4 ? 4 : 3)))) void split_main_kernel(SmParams prm) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int sexp[2][kSplitMaxGroup];
   __shared__ __align__(16) float wts_s[kSmWaves][kSplitMaxGroup * kSmChunk];
@@ -291,10 +331,35 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
 #pragma unroll
   for (int t = 0; t < 2 * NW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // fixed parts: each staging segment's source pointer, advanced one chunk per
+  // copy (the chunks are copied in order from t0)
+  const unsigned* segp[C::fixed ? C::nseg : 1];
+  if constexpr (C::fixed) {
+    static_for<0, C::nseg>([&](auto SI) {
+      constexpr int si = decltype(SI)::value;
+      segp[si] = (const unsigned*)(prm.seg[si].base + ((int64_t)bgi * prm.T + t0) * C::seg_elem(si));
+    });
+  }
   // copy the records of tokens [c0, c0 + 32) into a staging buffer; tokens at or
   // beyond t1 read copies of the last valid dword (finite, masked later)
   auto issue = [&](int64_t c0, uint8_t* dst) {
     const int nvalid = (int)min((int64_t)kSmChunk, t1 - c0);
+    if constexpr (C::fixed) {
+      static_for<0, C::nseg>([&](auto SI) {
+        constexpr int si = decltype(SI)::value;
+        constexpr int wpt = C::seg_elem(si) / 4, nd = kSmChunk * wpt;
+        const int nvd = C::seg_blocked(si) ? nd : nvalid * wpt;
+        const unsigned* src = segp[si];
+        uint8_t* to = dst + prm.seg[si].lds;
+#pragma unroll
+        for (int e0 = 0; e0 < nd; e0 += 64) {
+          const int e = e0 + lane;
+          if (e < nd) __builtin_amdgcn_global_load_lds((void*)(src + min(e, nvd - 1)), (lds_ptr)(to + 4 * e0), 4, 0, 0);
+        }
+        segp[si] = src + nd;
+      });
+      return;
+    }
     for (int si = 0; si < prm.n_seg; ++si) {
       const SmSeg S = prm.seg[si];
       const int wpt = S.elem >> 2;
@@ -322,16 +387,19 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
     // ---------------- scores: 2 tiles of 16 tokens x this lane's 2 heads ----------------
     float sv[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
     // one key part with PL planes (QJ: QJL signs); am / aq: <q', c~> and <q'', z> per tile
-    auto key_part = [&](auto PLc, auto QJc, const SmPart& P) {
+    // (DC, OC: the part's dimension and channel offset when fixed at compile time, else 0)
+    auto key_part = [&](auto PLc, auto QJc, const SmPart& P, auto DC, auto OC) {
       constexpr int PL = decltype(PLc)::value;
       constexpr bool QJ = decltype(QJc)::value;
-      const int dq = P.d >> 3, rec = P.rec, kg0 = P.off >> 5, nks = P.d >> 5;
+      constexpr int DF = decltype(DC)::value, OF = decltype(OC)::value;
+      const int d = DF ? DF : P.d;
+      const int dq = d >> 3, rec = PL * dq, kg0 = (DF ? OF : P.off) >> 5, nks = d >> 5;
       const uint8_t* kc = sb + P.st_codes;
       const uint8_t* ksg = sb + P.st_signs;
       const uint2* tk = (const uint2*)(lds + prm.tab_off + P.ptab);
       f32x4 am[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       f32x4 aq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      for (int ks = 0; ks < nks; ++ks) {
+      auto step = [&](int ks) {
         const u32x4 fm = frag[(2 * (kg0 + ks)) * 64 + lane];
         const u32x4 fq = frag[(2 * (kg0 + ks) + 1) * 64 + lane];
 #pragma unroll
@@ -362,6 +430,12 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
             aq[tile] = mfma16(fq, bz, aq[tile]);
           }
         }
+      };
+      if constexpr (DF != 0) {
+#pragma unroll
+        for (int ks = 0; ks < DF / 32; ++ks) step(ks);
+      } else {
+        for (int ks = 0; ks < nks; ++ks) step(ks);
       }
       const float* kn = (const float*)(sb + P.st_norms);
       const float* kr = (const float*)(sb + P.st_rnorms);
@@ -374,25 +448,33 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
         sv[tile][1] += nu * fmaf(ga * iqB, aq[tile][2] + aq[tile][3], imB * (am[tile][2] + am[tile][3]));
       }
     };
-    for (int p = 0; p < prm.nk; ++p) {
-      const SmPart& P = prm.kp[p];
-      using I0 = std::integral_constant<int, 0>;
-      using I1 = std::integral_constant<int, 1>;
-      using I2 = std::integral_constant<int, 2>;
-      using I3 = std::integral_constant<int, 3>;
-      using I4 = std::integral_constant<int, 4>;
-      using T_ = std::true_type;
-      using F_ = std::false_type;
-      switch (P.planes * 2 + (P.qjl ? 1 : 0)) {
-        case 1: key_part(I0{}, T_{}, P); break;
-        case 2: key_part(I1{}, F_{}, P); break;
-        case 3: key_part(I1{}, T_{}, P); break;
-        case 4: key_part(I2{}, F_{}, P); break;
-        case 5: key_part(I2{}, T_{}, P); break;
-        case 6: key_part(I3{}, F_{}, P); break;
-        case 7: key_part(I3{}, T_{}, P); break;
-        case 8: key_part(I4{}, F_{}, P); break;
-        default: break;
+    using I0 = std::integral_constant<int, 0>;
+    if constexpr (C::fixed) {
+      static_for<0, C::nk>([&](auto PI) {
+        constexpr int p = decltype(PI)::value;
+        key_part(std::integral_constant<int, C::kpl[p]>{}, std::true_type{}, prm.kp[p],
+                 std::integral_constant<int, C::kd[p]>{}, std::integral_constant<int, C::koff(p)>{});
+      });
+    } else {
+      for (int p = 0; p < prm.nk; ++p) {
+        const SmPart& P = prm.kp[p];
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        using I4 = std::integral_constant<int, 4>;
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        switch (P.planes * 2 + (P.qjl ? 1 : 0)) {
+          case 1: key_part(I0{}, T_{}, P, I0{}, I0{}); break;
+          case 2: key_part(I1{}, F_{}, P, I0{}, I0{}); break;
+          case 3: key_part(I1{}, T_{}, P, I0{}, I0{}); break;
+          case 4: key_part(I2{}, F_{}, P, I0{}, I0{}); break;
+          case 5: key_part(I2{}, T_{}, P, I0{}, I0{}); break;
+          case 6: key_part(I3{}, F_{}, P, I0{}, I0{}); break;
+          case 7: key_part(I3{}, T_{}, P, I0{}, I0{}); break;
+          case 8: key_part(I4{}, F_{}, P, I0{}, I0{}); break;
+          default: break;
+        }
       }
     }
 
@@ -412,7 +494,9 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
     }
     // value weight exponents: weights p |v| 2^-ev stay below 2^14
     bool refit = false;
-    for (int p = 0; p < prm.nv; ++p) {
+    const int nvp = C::fixed ? C::nv : prm.nv;
+#pragma unroll
+    for (int p = 0; p < nvp; ++p) {
       const SmPart& P = prm.vp[p];
       float nmx = lane < kSmChunk ? ((const float*)(sb + P.st_norms))[lane] : 0.f;
 #pragma unroll
@@ -435,8 +519,8 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
     if (refit || __ballot(alpha[0] != 1.f || alpha[1] != 1.f)) {
 #pragma unroll
       for (int np = 0; np < NW; ++np) {
-        if (32 * np < prm.dv) {
-          const float f = fix[prm.vword_part[np]];
+        if (32 * np < (C::fixed ? C::dv : prm.dv)) {
+          const float f = fix[C::fixed ? C::vpart(np) : prm.vword_part[np]];
           const float fa = alpha[0] * f, fb = alpha[1] * f;
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
@@ -451,12 +535,9 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
 
     // ---------------- values: 16 coordinates x 8 heads per instruction ----------------
     u32x4 aw = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int np = 0; np < NW; ++np) {
-      if (32 * np < prm.dv) {
-        const int p = prm.vword_part[np];
-        const SmPart& P = prm.vp[p];
-        const int wd = np - (P.off >> 5);
+    // word np of the value vector: word wd of value part p (PLc planes; DC its
+    // dimension when fixed at compile time, else 0)
+    auto value_np = [&](const int np, const int p, const int wd, const SmPart& P, auto PLc, auto DC) {
         if (wd == 0) {  // first word of this part: its weight operand
           const int ev = evs[p];
           const float wsc = ev == kSmEvUnset ? 0.f : ldexpf(1.f, -ev);
@@ -475,9 +556,10 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
         // one 32-coordinate word of a value part with PL planes: two tiles of 16
         // coordinates. BLOCK32 codes: block word (pl, g4, c / 4) holds plane pl of
         // coordinate c for this lane's eight tokens, nibble c % 4 of each half.
-        auto value_word = [&](auto PLc) {
+        {
           constexpr int PL = decltype(PLc)::value;
-          const int d4 = P.d >> 2;
+          constexpr int DF = decltype(DC)::value;
+          const int d4 = (DF ? DF : P.d) >> 2;
           const uint8_t* vc = sb + P.st_codes;
           const uint2* tv = (const uint2*)(lds + prm.tab_off + P.ptab);
 #pragma unroll
@@ -501,13 +583,28 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(3)))
             acc[2 * np + hf] = mfma16(aw, bh, acc[2 * np + hf]);
             acc[2 * np + hf] = mfma16(aw, bl, acc[2 * np + hf]);
           }
-        };
-        switch (P.planes) {
-          case 1: value_word(std::integral_constant<int, 1>{}); break;
-          case 2: value_word(std::integral_constant<int, 2>{}); break;
-          case 3: value_word(std::integral_constant<int, 3>{}); break;
-          case 4: value_word(std::integral_constant<int, 4>{}); break;
-          default: break;
+        }
+    };
+    if constexpr (C::fixed) {
+      static_for<0, C::dv / 32>([&](auto NP) {
+        constexpr int np = decltype(NP)::value, p = C::vpart(np);
+        value_np(np, p, np - C::voff(p) / 32, prm.vp[p], std::integral_constant<int, C::vpl[p]>{},
+                 std::integral_constant<int, C::vd[p]>{});
+      });
+    } else {
+#pragma unroll
+      for (int np = 0; np < NW; ++np) {
+        if (32 * np < prm.dv) {
+          const int p = prm.vword_part[np];
+          const SmPart& P = prm.vp[p];
+          const int wd = np - (P.off >> 5);
+          switch (P.planes) {
+            case 1: value_np(np, p, wd, P, std::integral_constant<int, 1>{}, I0{}); break;
+            case 2: value_np(np, p, wd, P, std::integral_constant<int, 2>{}, I0{}); break;
+            case 3: value_np(np, p, wd, P, std::integral_constant<int, 3>{}, I0{}); break;
+            case 4: value_np(np, p, wd, P, std::integral_constant<int, 4>{}, I0{}); break;
+            default: break;
+          }
         }
       }
     }
@@ -710,7 +807,26 @@ static void build_split_params(const SplitDecodeLaunch& L, SmParams& prm, size_t
   prm.qexp = ws ? (int*)(ws + part_bytes + (size_t)L.B * L.Hkv * (prm.dk / 32) * 2 * 64 * 16) : nullptr;
 }
 
-static void (*split_kernel(int dv))(SmParams) { return dv <= 128 ? split_main_kernel<4> : split_main_kernel<8>; }
+// the main kernel for these parts: the compile-time pages' split where the
+// parts and their staging segments match it exactly, else the run-time one
+template <class C>
+static bool matches(const SmParams& prm) {
+  if (prm.nk != C::nk || prm.nv != C::nv || prm.n_seg != C::nseg) return false;
+  for (int p = 0; p < C::nk; ++p)
+    if (prm.kp[p].d != C::kd[p] || prm.kp[p].planes != C::kpl[p] || !prm.kp[p].qjl || prm.kp[p].off != C::koff(p))
+      return false;
+  for (int p = 0; p < C::nv; ++p)
+    if (prm.vp[p].d != C::vd[p] || prm.vp[p].planes != C::vpl[p] || prm.vp[p].off != C::voff(p)) return false;
+  for (int si = 0; si < C::nseg; ++si)
+    if (prm.seg[si].elem != C::seg_elem(si) || (prm.seg[si].blocked != 0) != C::seg_blocked(si)) return false;
+  return true;
+}
+static void (*split_kernel(const SmParams& prm))(SmParams) {
+  // 32 channels at 3 bits and 96 at 2 (prod keys: 2 and 1 MSE-stage planes), and 4 + 3 bits
+  if (matches<SmPages<2, 1, 3, 2>>(prm)) return split_main_kernel<4, SmPages<2, 1, 3, 2>>;
+  if (matches<SmPages<3, 2, 4, 3>>(prm)) return split_main_kernel<4, SmPages<3, 2, 4, 3>>;
+  return prm.dv <= 128 ? split_main_kernel<4, SmDyn> : split_main_kernel<8, SmDyn>;
+}
 
 }  // namespace
 
@@ -725,7 +841,7 @@ int split_decode_resident_waves(const SplitDecodeLaunch& L) {
   build_split_params(L, prm, &lds);
   int fallback = 3 * 4 * 256;  // 3 waves per SIMD on 256 CUs
   if (lds == 0) return fallback;
-  auto kern = split_kernel(prm.dv);
+  auto kern = split_kernel(prm);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
@@ -765,7 +881,7 @@ tq_status launch_split_decode(const SplitDecodeLaunch& L, hipStream_t stream) {
   build_split_params(L, prm, &lds);
   if (lds == 0) return set_error(TQ_ERR_UNSUPPORTED, "split decode: parts need more LDS than a workgroup has");
   const dim3 grid((unsigned)((L.n_splits + kSmWaves - 1) / kSmWaves), (unsigned)(L.B * L.Hkv));
-  auto kern = split_kernel(prm.dv);
+  auto kern = split_kernel(prm);
   int dmax = 0;
   for (int p = 0; p < prm.nk; ++p) dmax = prm.kp[p].d > dmax ? prm.kp[p].d : dmax;
   // prep LDS: q, q', q'' [G][dk] each, then as many rows of Pi and S as fit (at most 128)
