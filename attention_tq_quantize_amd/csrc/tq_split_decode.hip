@@ -107,15 +107,34 @@ __device__ __forceinline__ unsigned bfe(unsigned w, unsigned off) {
 // planes: bits 2 pl and 2 pl + 1 are plane pl of a and of b.
 __device__ __forceinline__ unsigned pair_entries(int PL) { return 1u << (2 * PL); }
 
+// Reductions over each row of 16 lanes with DPP permutations (no LDS round
+// trip): swap neighbours, then pairs of a quad, then mirror the half rows and
+// the row; every step combines two partials that the partner lane combines in
+// the other order, so all 16 lanes end with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_perm(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_perm<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_perm<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_perm<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dpp_perm<0x140>(v));  // row_mirror
 }
 __device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_perm<0xB1>(v);
+  v += dpp_perm<0x4E>(v);
+  v += dpp_perm<0x141>(v);
+  return v + dpp_perm<0x140>(v);
+}
+// maximum over the wave: the rows' maxima, then the four rows' through readlane
+__device__ __forceinline__ float wave_max(float v) {
+  v = group16_max(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // One workgroup per (batch, KV head): the query parts rotated into each key
@@ -320,6 +339,13 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(C::f
   int* evs = evs_s[wave];    // per value part: weight exponent
   float* fix = fix_s[wave];  // per value part: accumulator rescale
   if (lane < kSplitMaxParts) evs[lane] = kSmEvUnset;
+  int evr[C::fixed ? C::nv : 1];  // fixed parts: weight exponents and rescales in registers
+  float fxr[C::fixed ? C::nv : 1];
+#pragma unroll
+  for (int p = 0; p < (C::fixed ? C::nv : 1); ++p) {
+    evr[p] = kSmEvUnset;
+    fxr[p] = 1.f;
+  }
   const int hA = 2 * g4, hB = 2 * g4 + 1;  // this lane's heads in every C tile
   const float imA = hA < G ? ldexpf(1.f, -sexp[0][hA]) : 0.f, imB = hB < G ? ldexpf(1.f, -sexp[0][hB]) : 0.f;
   const float iqA = hA < G ? ldexpf(1.f, -sexp[1][hA]) : 0.f, iqB = hB < G ? ldexpf(1.f, -sexp[1][hB]) : 0.f;
@@ -494,33 +520,48 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(C::f
     }
     // value weight exponents: weights p |v| 2^-ev stay below 2^14
     bool refit = false;
-    const int nvp = C::fixed ? C::nv : prm.nv;
-#pragma unroll
-    for (int p = 0; p < nvp; ++p) {
-      const SmPart& P = prm.vp[p];
-      float nmx = lane < kSmChunk ? ((const float*)(sb + P.st_norms))[lane] : 0.f;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) nmx = fmaxf(nmx, __shfl_xor(nmx, o));
+    // (wave-uniform: fixed parts keep them in registers, others in LDS)
+    auto exponent = [&](const SmPart& P, int ev, int* ev_out, float* fix_out) {
+      const float nmx = wave_max(lane < kSmChunk ? ((const float*)(sb + P.st_norms))[lane] : 0.f);
       int e = 0;
       frexpf(nmx, &e);
       const int need = nmx > 0.f ? max(e - 14, -100) : kSmEvUnset;
-      const int ev = evs[p];
-      float f = 1.f;
+      *fix_out = 1.f;
+      *ev_out = ev;
       if (need > ev) {
-        if (ev != kSmEvUnset) f = ldexpf(1.f, ev - need);
+        if (ev != kSmEvUnset) *fix_out = ldexpf(1.f, ev - need);
         refit = true;
-        __builtin_amdgcn_wave_barrier();
-        if (lane == 0) evs[p] = need;
+        *ev_out = need;
       }
-      if (lane == 0) fix[p] = f;
+    };
+    if constexpr (C::fixed) {
+      static_for<0, C::nv>([&](auto PI) {
+        constexpr int p = decltype(PI)::value;
+        exponent(prm.vp[p], evr[p], &evr[p], &fxr[p]);
+      });
+    } else {
+      for (int p = 0; p < prm.nv; ++p) {
+        int ev_new;
+        float f;
+        exponent(prm.vp[p], evs[p], &ev_new, &f);
+        __builtin_amdgcn_wave_barrier();
+        if (lane == 0) {
+          evs[p] = ev_new;
+          fix[p] = f;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
     }
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("" ::: "memory");
     if (refit || __ballot(alpha[0] != 1.f || alpha[1] != 1.f)) {
 #pragma unroll
       for (int np = 0; np < NW; ++np) {
         if (32 * np < (C::fixed ? C::dv : prm.dv)) {
-          const float f = fix[C::fixed ? C::vpart(np) : prm.vword_part[np]];
+          float f;
+          if constexpr (C::fixed)
+            f = fxr[C::vpart(np)];
+          else
+            f = fix[prm.vword_part[np]];
           const float fa = alpha[0] * f, fb = alpha[1] * f;
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
@@ -539,7 +580,11 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(C::f
     // dimension when fixed at compile time, else 0)
     auto value_np = [&](const int np, const int p, const int wd, const SmPart& P, auto PLc, auto DC) {
         if (wd == 0) {  // first word of this part: its weight operand
-          const int ev = evs[p];
+          int ev;
+          if constexpr (C::fixed)
+            ev = evr[p];
+          else
+            ev = evs[p];
           const float wsc = ev == kSmEvUnset ? 0.f : ldexpf(1.f, -ev);
           // K slots 0-3 of lane group g4 are tokens 4 g4 + k, slots 4-7 tokens
           // 16 + 4 g4 + k: the token order of a BLOCK32 word's two halves
@@ -617,7 +662,11 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(C::f
 #pragma unroll
   for (int np = 0; np < NW; ++np) {
     if (32 * np < prm.dv) {
-      const int ev = evs[prm.vword_part[np]];
+      int ev;
+      if constexpr (C::fixed)
+        ev = evr[C::vpart(np)];
+      else
+        ev = evs[prm.vword_part[np]];
       const float sc = ev == kSmEvUnset ? 0.f : ldexpf(1.f, ev);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
