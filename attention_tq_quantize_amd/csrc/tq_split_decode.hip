@@ -18,18 +18,20 @@
 //     device at once). Each wave walks its split in chunks of 32 tokens:
 //      * the chunk's records of every part are copied straight from HBM into
 //        the wave's LDS staging buffer (global_load_lds, double-buffered);
-//      * scores: per key part and 32-coordinate step, each lane turns two
-//        coordinates of one token at a time into exact fp16 hi/lo centroid
-//        operands with one bit-field extract per plane and one read of a pair
-//        table (the QJL signs into +-1 likewise), and the matrix cores form
-//        <q', c~> and <q'', z> for 16 tokens x 8 heads per instruction;
-//      * an online softmax per head over the chunk (16-lane reductions);
+//      * scores: per key part and 32-coordinate step, each lane turns the
+//        coordinates of one token into exact fp16 hi/lo centroid operands with
+//        one bit-field extract per plane and one table read per four
+//        coordinates (parts of one or two planes: quad tables) or per two
+//        (pair tables), the QJL signs into +-1 per four from a nibble table,
+//        and the matrix cores form <q', c~> and <q'', z> for 16 tokens x 8
+//        heads per instruction;
+//      * an online softmax per head over the chunk (16-lane DPP reductions);
 //      * values: the probabilities times each value part's norms become the
 //        fp16 hi/lo weight operand (rows = 8 heads x {hi, lo}, K = 32 tokens in
 //        the BLOCK32 token order); the value codes are BLOCK32, so one word per
 //        plane holds a lane's coordinate for all eight of its tokens, and each
-//        lane turns two tokens at a time into the centroid operand with one
-//        bit-field extract per plane and one pair-table read; the matrix cores
+//        lane turns four (quad tables) or two (pair tables) tokens at a time
+//        into the centroid operand; the matrix cores
 //        accumulate 16 coordinates x 8 heads per instruction in the part's
 //        rotated basis (a running power-of-two exponent per part keeps the
 //        weights in fp16 range);
@@ -58,7 +60,7 @@ struct SmPart {
   int d, planes, off, qjl;
   int rec;                                   // code bytes per token: planes * d / 8
   int st_codes, st_signs, st_norms, st_rnorms;  // byte offsets in a staging buffer
-  int ptab;                                  // byte offset of its pair table from the tables' start
+  int ptab;                                  // byte offset of its quad or pair table from the tables' start
   float kappa;                               // sqrt(pi/2) / d
   unsigned tab[16];                          // centroid i as fp16 hi | lo << 16
   const float* pi[kSplitMaxKv];
@@ -105,7 +107,18 @@ __device__ __forceinline__ unsigned bfe(unsigned w, unsigned off) {
 // two coordinates, holds their centroids as fp16 (hi_a | hi_b << 16, lo_a | lo_b
 // << 16), i.e. one dword of each MFMA operand. The entry index interleaves the
 // planes: bits 2 pl and 2 pl + 1 are plane pl of a and of b.
-__device__ __forceinline__ unsigned pair_entries(int PL) { return 1u << (2 * PL); }
+// Parts with one or two planes use quad tables instead: entry e of a part with
+// PL planes holds four coordinates' centroids (hi_0 | hi_1 << 16, hi_2 | hi_3 <<
+// 16, lo_0 | lo_1 << 16, lo_2 | lo_3 << 16), two dwords of each operand from
+// one 16-byte read; bits 4 pl .. 4 pl + 3 of e are plane pl of the four. Both
+// kinds sit in LDS, 16-byte aligned, at the part's table offset.
+__host__ __device__ constexpr bool quad_table(int PL) { return PL == 1 || PL == 2; }
+__host__ __device__ constexpr int table_entries(int PL) { return quad_table(PL) ? 1 << (4 * PL) : 1 << (2 * PL); }
+__host__ __device__ constexpr int table_bytes(int PL) {
+  return PL == 0 ? 0 : quad_table(PL) ? 16 * table_entries(PL) : (8 * table_entries(PL) + 15) / 16 * 16;
+}
+// QJL sign nibbles: entry e holds four fp16 +-1 (bit set: +1), two dwords
+constexpr int kSignTableBytes = 16 * 8;
 
 // Reductions over each row of 16 lanes with DPP permutations (no LDS round
 // trip): swap neighbours, then pairs of a quad, then mirror the half rows and
@@ -299,21 +312,39 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(C::f
   u32x4* frag = (u32x4*)lds;  // [dk / 32][{mse, qjl}][64 lanes]
   unsigned* tabs = (unsigned*)(lds + prm.tab_off);
 
-  // ---- tables: QJL sign pairs (+-1 fp16), then a pair table per key and value part ----
-  if (tid < 4) tabs[tid] = ((tid & 1) ? 0x3C00u : 0xBC00u) | (((tid & 2) ? 0x3C00u : 0xBC00u) << 16);
+  // ---- tables: QJL sign nibbles (+-1 fp16), then a quad or pair table per key and value part ----
+  if (tid < 32) {
+    const int e = tid >> 1, h = tid & 1;  // dword h of entry e: signs of bits 2h, 2h + 1
+    const unsigned s0 = (e >> (2 * h)) & 1 ? 0x3C00u : 0xBC00u, s1 = (e >> (2 * h + 1)) & 1 ? 0x3C00u : 0xBC00u;
+    tabs[tid] = s0 | (s1 << 16);
+  }
   for (int side = 0; side < 2; ++side) {
     const int np = side ? prm.nv : prm.nk;
     for (int p = 0; p < np; ++p) {
       const SmPart& P = side ? prm.vp[p] : prm.kp[p];
-      uint2* pt = (uint2*)(lds + prm.tab_off + P.ptab);
-      for (int e = tid; e < (int)pair_entries(P.planes); e += kSmThreads) {
-        unsigned ia = 0, ib = 0;
-        for (int pl = 0; pl < P.planes; ++pl) {
-          ia |= ((e >> (2 * pl)) & 1) << pl;
-          ib |= ((e >> (2 * pl + 1)) & 1) << pl;
+      if (quad_table(P.planes)) {
+        u32x4* qt = (u32x4*)(lds + prm.tab_off + P.ptab);
+        for (int e = tid; e < table_entries(P.planes); e += kSmThreads) {
+          unsigned t[4];
+          for (int i = 0; i < 4; ++i) {
+            unsigned c = 0;
+            for (int pl = 0; pl < P.planes; ++pl) c |= ((e >> (4 * pl + i)) & 1) << pl;
+            t[i] = P.tab[c];
+          }
+          qt[e] = u32x4{(t[0] & 0xFFFFu) | (t[1] << 16), (t[2] & 0xFFFFu) | (t[3] << 16),
+                        (t[0] >> 16) | (t[1] & 0xFFFF0000u), (t[2] >> 16) | (t[3] & 0xFFFF0000u)};
         }
-        const unsigned ta = P.tab[ia], tb = P.tab[ib];
-        pt[e] = uint2{(ta & 0xFFFFu) | (tb << 16), (ta >> 16) | (tb & 0xFFFF0000u)};
+      } else if (P.planes > 0) {
+        uint2* pt = (uint2*)(lds + prm.tab_off + P.ptab);
+        for (int e = tid; e < table_entries(P.planes); e += kSmThreads) {
+          unsigned ia = 0, ib = 0;
+          for (int pl = 0; pl < P.planes; ++pl) {
+            ia |= ((e >> (2 * pl)) & 1) << pl;
+            ib |= ((e >> (2 * pl + 1)) & 1) << pl;
+          }
+          const unsigned ta = P.tab[ia], tb = P.tab[ib];
+          pt[e] = uint2{(ta & 0xFFFFu) | (tb << 16), (ta >> 16) | (tb & 0xFFFF0000u)};
+        }
       }
     }
   }
@@ -349,7 +380,7 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(C::f
   const int hA = 2 * g4, hB = 2 * g4 + 1;  // this lane's heads in every C tile
   const float imA = hA < G ? ldexpf(1.f, -sexp[0][hA]) : 0.f, imB = hB < G ? ldexpf(1.f, -sexp[0][hB]) : 0.f;
   const float iqA = hA < G ? ldexpf(1.f, -sexp[1][hA]) : 0.f, iqB = hB < G ? ldexpf(1.f, -sexp[1][hB]) : 0.f;
-  const unsigned* ztab = tabs;
+  const uint2* ztab = (const uint2*)tabs;
   const unsigned offv[4] = {8u * g4, 8u * g4 + 2, 8u * g4 + 4, 8u * g4 + 6};  // bit offsets of this lane's coordinate pairs
 
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
@@ -436,14 +467,27 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(C::f
 #pragma unroll
             for (int pl = 0; pl < PL; ++pl) w[pl] = lds_u32(kc + tok * rec + pl * dq + 4 * ks);
             u32x4 bh, bl;
+            if constexpr (quad_table(PL)) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {  // coordinates 8 g4 + 2v, + 1 of this step
-              unsigned pi = bfe<2>(w[0], offv[v]);
+              for (int h = 0; h < 2; ++h) {  // coordinates 8 g4 + 4h .. + 3 of this step
+                unsigned qi = bfe<4>(w[0], offv[2 * h]);
+                if constexpr (PL == 2) qi |= bfe<4>(w[1], offv[2 * h]) << 4;
+                const u32x4 en = ((const u32x4*)tk)[qi];
+                bh[2 * h] = en.x;
+                bh[2 * h + 1] = en.y;
+                bl[2 * h] = en.z;
+                bl[2 * h + 1] = en.w;
+              }
+            } else {
 #pragma unroll
-              for (int pl = 1; pl < PL; ++pl) pi |= bfe<2>(w[pl], offv[v]) << (2 * pl);
-              const uint2 en = tk[pi];
-              bh[v] = en.x;
-              bl[v] = en.y;
+              for (int v = 0; v < 4; ++v) {  // coordinates 8 g4 + 2v, + 1 of this step
+                unsigned pi = bfe<2>(w[0], offv[v]);
+#pragma unroll
+                for (int pl = 1; pl < PL; ++pl) pi |= bfe<2>(w[pl], offv[v]) << (2 * pl);
+                const uint2 en = tk[pi];
+                bh[v] = en.x;
+                bl[v] = en.y;
+              }
             }
             am[tile] = mfma16(fm, bh, am[tile]);
             am[tile] = mfma16(fm, bl, am[tile]);
@@ -452,7 +496,11 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(C::f
             const unsigned z = lds_u32(ksg + tok * dq + 4 * ks);
             u32x4 bz;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) bz[v] = ztab[bfe<2>(z, offv[v])];
+            for (int h = 0; h < 2; ++h) {
+              const uint2 en = ztab[bfe<4>(z, offv[2 * h])];
+              bz[2 * h] = en.x;
+              bz[2 * h + 1] = en.y;
+            }
             aq[tile] = mfma16(fq, bz, aq[tile]);
           }
         }
@@ -615,15 +663,29 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(C::f
 #pragma unroll
             for (int pl = 0; pl < PL; ++pl) w[pl] = lds_u32(vc + 4 * ((pl * 4 + g4) * d4 + (c >> 2)));
             u32x4 bh, bl;
+            if constexpr (quad_table(PL)) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {  // K slots 2v, 2v + 1: two tokens of one half
-              const unsigned at = nib + 16u * (unsigned)(v >> 1) + 2u * (unsigned)(v & 1);
-              unsigned pi = bfe<2>(w[0], at);
+              for (int h = 0; h < 2; ++h) {  // K slots 4h .. 4h + 3: the four tokens of one half
+                const unsigned at = nib + 16u * (unsigned)h;
+                unsigned qi = bfe<4>(w[0], at);
+                if constexpr (PL == 2) qi |= bfe<4>(w[1], at) << 4;
+                const u32x4 en = ((const u32x4*)tv)[qi];
+                bh[2 * h] = en.x;
+                bh[2 * h + 1] = en.y;
+                bl[2 * h] = en.z;
+                bl[2 * h + 1] = en.w;
+              }
+            } else {
 #pragma unroll
-              for (int pl = 1; pl < PL; ++pl) pi |= bfe<2>(w[pl], at) << (2 * pl);
-              const uint2 en = tv[pi];
-              bh[v] = en.x;
-              bl[v] = en.y;
+              for (int v = 0; v < 4; ++v) {  // K slots 2v, 2v + 1: two tokens of one half
+                const unsigned at = nib + 16u * (unsigned)(v >> 1) + 2u * (unsigned)(v & 1);
+                unsigned pi = bfe<2>(w[0], at);
+#pragma unroll
+                for (int pl = 1; pl < PL; ++pl) pi |= bfe<2>(w[pl], at) << (2 * pl);
+                const uint2 en = tv[pi];
+                bh[v] = en.x;
+                bl[v] = en.y;
+              }
             }
             acc[2 * np + hf] = mfma16(aw, bh, acc[2 * np + hf]);
             acc[2 * np + hf] = mfma16(aw, bl, acc[2 * np + hf]);
@@ -836,14 +898,14 @@ static void build_split_params(const SplitDecodeLaunch& L, SmParams& prm, size_t
   }
   prm.stage_bytes = st;
   prm.tab_off = (prm.dk / 32) * 2 * 64 * 16;
-  int tb = 16;  // QJL sign pairs first
+  int tb = kSignTableBytes;  // QJL sign nibbles first
   for (int p = 0; p < prm.nk; ++p) {
     prm.kp[p].ptab = tb;
-    tb += 8 << (2 * prm.kp[p].planes);
+    tb += table_bytes(prm.kp[p].planes);
   }
   for (int p = 0; p < prm.nv; ++p) {
     prm.vp[p].ptab = tb;
-    tb += 8 << (2 * prm.vp[p].planes);
+    tb += table_bytes(prm.vp[p].planes);
   }
   prm.wave_off = prm.tab_off + (tb + 15) / 16 * 16;
   prm.wave_bytes = 2 * st;  // per wave: two staging buffers
