@@ -271,6 +271,9 @@ struct SmDyn {
   __host__ __device__ static constexpr int vpart(int) { return 0; }
   __host__ __device__ static constexpr int seg_elem(int) { return 0; }
   __host__ __device__ static constexpr bool seg_blocked(int) { return false; }
+  __host__ __device__ static constexpr int seg_lds(int) { return 0; }
+  static constexpr int stage_bytes = 0, dma_rounds = 0;
+  static constexpr int vnorm_seg[1] = {0};
 };
 template <int KP0, int KP1, int VP0, int VP1>
 struct SmPages {
@@ -287,6 +290,15 @@ struct SmPages {
     return si == 0 ? 4 * KP0 : si == 4 ? 12 * KP1 : si == 8 ? 4 * VP0 : si == 10 ? 12 * VP1 : si == 5 ? 12 : 4;
   }
   __host__ __device__ static constexpr bool seg_blocked(int si) { return si == 8 || si == 10; }
+  // staging offset of segment si (each 32-token segment padded to 16 bytes, as the host lays them)
+  __host__ __device__ static constexpr int seg_lds(int si) {
+    int at = 0;
+    for (int i = 0; i < si; ++i) at += (kSmChunk * seg_elem(i) + 15) / 16 * 16;
+    return at;
+  }
+  static constexpr int stage_bytes = seg_lds(nseg);
+  static constexpr int dma_rounds = (stage_bytes + 1023) / 1024;  // 16 bytes x 64 lanes per copy
+  static constexpr int vnorm_seg[2] = {9, 11};                     // value parts' norm segments
 };
 
 template <int I, int N, class F>
@@ -388,33 +400,40 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(C::f
 #pragma unroll
   for (int t = 0; t < 2 * NW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fixed parts: each staging segment's source pointer, advanced one chunk per
-  // copy (the chunks are copied in order from t0)
-  const unsigned* segp[C::fixed ? C::nseg : 1];
+  // fixed parts: a chunk's staging buffer is copied by dma_rounds 16-byte DMA
+  // copies per lane; lane l of copy k fills staging bytes [1024 k + 16 l, + 16),
+  // which lie in one segment: its source pointer (advanced one chunk per copy,
+  // the chunks being copied in order from t0) and step are set up once here
+  const uint8_t* dsrc[C::fixed ? C::dma_rounds : 1];
+  unsigned dstep[C::fixed ? C::dma_rounds : 1];
   if constexpr (C::fixed) {
-    static_for<0, C::nseg>([&](auto SI) {
-      constexpr int si = decltype(SI)::value;
-      segp[si] = (const unsigned*)(prm.seg[si].base + ((int64_t)bgi * prm.T + t0) * C::seg_elem(si));
-    });
+#pragma unroll
+    for (int k = 0; k < C::dma_rounds; ++k) {
+      const int pos = 1024 * k + 16 * lane;
+      dsrc[k] = nullptr;
+      dstep[k] = 0;
+      static_for<0, C::nseg>([&](auto SI) {
+        constexpr int si = decltype(SI)::value, elem = C::seg_elem(si), at = C::seg_lds(si);
+        if (pos >= at && pos < at + kSmChunk * elem) {
+          dsrc[k] = prm.seg[si].base + ((int64_t)bgi * prm.T + t0) * elem + (pos - at);
+          dstep[k] = kSmChunk * elem;
+        }
+      });
+    }
   }
   // copy the records of tokens [c0, c0 + 32) into a staging buffer; tokens at or
   // beyond t1 read copies of the last valid dword (finite, masked later)
   auto issue = [&](int64_t c0, uint8_t* dst) {
     const int nvalid = (int)min((int64_t)kSmChunk, t1 - c0);
     if constexpr (C::fixed) {
-      static_for<0, C::nseg>([&](auto SI) {
-        constexpr int si = decltype(SI)::value;
-        constexpr int wpt = C::seg_elem(si) / 4, nd = kSmChunk * wpt;
-        const int nvd = C::seg_blocked(si) ? nd : nvalid * wpt;
-        const unsigned* src = segp[si];
-        uint8_t* to = dst + prm.seg[si].lds;
+      // whole chunks: records of tokens at or beyond t1 (inside max_ctx) are
+      // copied too; the tail chunk's value norms are zeroed before use
 #pragma unroll
-        for (int e0 = 0; e0 < nd; e0 += 64) {
-          const int e = e0 + lane;
-          if (e < nd) __builtin_amdgcn_global_load_lds((void*)(src + min(e, nvd - 1)), (lds_ptr)(to + 4 * e0), 4, 0, 0);
-        }
-        segp[si] = src + nd;
-      });
+      for (int k = 0; k < C::dma_rounds; ++k) {
+        if (dstep[k]) __builtin_amdgcn_global_load_lds((void*)dsrc[k], (lds_ptr)(dst + 1024 * k), 16, 0, 0);
+        dsrc[k] += dstep[k];
+      }
+      (void)nvalid;
       return;
     }
     for (int si = 0; si < prm.n_seg; ++si) {
@@ -440,6 +459,14 @@ __global__ __launch_bounds__(kSmThreads) __attribute__((amdgpu_waves_per_eu(C::f
     const uint8_t* sb = wbase + (it & 1) * prm.stage_bytes;
     if (c0 + kSmChunk < t1) issue(c0 + kSmChunk, wbase + ((it + 1) & 1) * prm.stage_bytes);
     const int nvalid = (int)min((int64_t)kSmChunk, t1 - c0);
+    if constexpr (C::fixed) {
+      if (nvalid < kSmChunk) {  // tail chunk: tokens past the context weigh nothing
+#pragma unroll
+        for (int p = 0; p < C::nv; ++p)
+          if (lane >= nvalid && lane < kSmChunk) ((float*)(sb + C::seg_lds(C::vnorm_seg[p])))[lane] = 0.f;
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
 
     // ---------------- scores: 2 tiles of 16 tokens x this lane's 2 heads ----------------
     float sv[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
@@ -929,8 +956,12 @@ static bool matches(const SmParams& prm) {
   for (int p = 0; p < C::nv; ++p)
     if (prm.vp[p].d != C::vd[p] || prm.vp[p].planes != C::vpl[p] || prm.vp[p].off != C::voff(p)) return false;
   for (int si = 0; si < C::nseg; ++si)
-    if (prm.seg[si].elem != C::seg_elem(si) || (prm.seg[si].blocked != 0) != C::seg_blocked(si)) return false;
-  return true;
+    if (prm.seg[si].elem != C::seg_elem(si) || (prm.seg[si].blocked != 0) != C::seg_blocked(si) ||
+        prm.seg[si].lds != C::seg_lds(si) || ((uintptr_t)prm.seg[si].base & 15))  // 16-byte copies
+      return false;
+  for (int p = 0; p < C::nv; ++p)
+    if (prm.vp[p].st_norms != C::seg_lds(C::vnorm_seg[p])) return false;
+  return prm.stage_bytes == C::stage_bytes;
 }
 static void (*split_kernel(const SmParams& prm))(SmParams) {
   // 32 channels at 3 bits and 96 at 2 (prod keys: 2 and 1 MSE-stage planes), and 4 + 3 bits

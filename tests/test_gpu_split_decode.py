@@ -1,7 +1,8 @@
 """GPU parity of decode attention over outlier-split caches
 (tq_decode_attention_split; [NIK] "Experiments", KV cache: outlier channels at
 more bits) against the oracle's decode_attention_split on oracle-packed
-records (keys VECTOR, values BLOCK32): outputs within rtol 1e-3 / atol 1e-4.
+records (keys VECTOR, values BLOCK32): outputs within rtol 1e-3 / atol 1e-4,
+with NaN norms in every record past a sequence's length.
 Cases: the pages' split of a
 128-channel head (32 channels at 3 bits, 96 at 2; prod keys, mse values) with
 GQA 8 and ragged lengths; every KV head with its own channel lists (its
@@ -128,6 +129,13 @@ def test_split_decode_parity(gpu_lib, case):
     q = syn.decode_queries(B, Hq, dim, syn.CFG_TEST)
     lens = np.array(lens, np.int32)
     scale = 1 / math.sqrt(dim)
+    # records past each sequence's length are never used: NaN norms there must not leak
+    for side in (k, v):
+        for _, _, r in side.parts:
+            for b in range(B):
+                for key in ("norms", "rnorms"):
+                    if key in r:
+                        r[key][b, :, int(lens[b]):] = float("nan")
     got = tq.decode_attention_split(torch.from_numpy(q).to(DEV).to(torch.bfloat16), k, v,
                                     torch.from_numpy(lens).to(DEV), scale).cpu().numpy()
     want = O.decode_attention_split(q, ok, ov, lens, scale, dim)
