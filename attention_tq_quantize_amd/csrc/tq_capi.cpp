@@ -536,15 +536,15 @@ tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, int n_gr
     const tq_quantizer* const* qp = qz + (size_t)p * n_groups;
     const int dp = qp[0]->d;
     const int64_t cb = (int64_t)qp[0]->planes * dp / 8;
-    // the kernels write the VECTOR layout; BLOCK32 repacks each 32-record block in place
+    // the generic kernels write the VECTOR layout; BLOCK32 repacks each 32-record block in place
     auto finish = [&]() -> tq_status {
       if (layout != TQ_LAYOUT_BLOCK32) return TQ_OK;
       return launch_repack_block32(r.codes, (int64_t)n_groups * n_per_group / 32, qp[0]->planes, dp,
                                    (hipStream_t)stream);
     };
-    if (quantize_split_fast(dim, qp[0])) {
-      st = launch_quantize_split(qp, n_groups, n_per_group, chan.data() + off[p], x, x_dtype, r, (hipStream_t)stream);
-      if (st == TQ_OK) st = finish();
+    if (quantize_split_fast(dim, qp[0])) {  // writes either layout itself
+      st = launch_quantize_split(qp, n_groups, n_per_group, chan.data() + off[p], x, x_dtype,
+                                 layout == TQ_LAYOUT_BLOCK32, r, (hipStream_t)stream);
       if (st != TQ_OK) return st;
       continue;
     }

@@ -302,7 +302,7 @@ __device__ __forceinline__ unsigned quad_or(unsigned w) {
 template <int D, int P, bool PROD, bool XF32, bool BLK, bool DBG, bool SPLIT = false>
 __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void quantize_kernel(
     QuantParams prm, std::conditional_t<SPLIT, QuantSplitParams, QuantNoSplit> sx) {
-  static_assert(!SPLIT || (D == 128 && !BLK), "split parts: d = 128 heads, vector layout");
+  static_assert(!SPLIT || D == 128, "split parts: d = 128 heads");
   constexpr int NQ = D / 16, NK = D / 32, Q4 = D / 4;
   constexpr int T = q_tiles(D, PROD, XF32, BLK);
   // split mse at four waves per SIMD has no registers for the next step's tiles
@@ -647,8 +647,11 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
       }
       const int slot = r16 & 3;
       // this step's 32-vector block; 32-bit lane offset of word (p = 0, q = 0)
-      const buf_t blk = make_buf(prm.codes + ((gbase + v0) / 32) * (int64_t)(4 * P * D), (unsigned)(4 * P * D));
-      const unsigned blk_lane = (unsigned)((g * (D / 4) + (D / 16) * (r16 >> 2)) * 4);
+      // (split: a block of the part's records is 4 P d_p bytes, and lanes whose
+      // coordinates lie beyond d_p store nothing)
+      const buf_t blk = make_buf(prm.codes + ((gbase + v0) / 32) * (int64_t)(4 * P * RD), (unsigned)(4 * P * RD));
+      const unsigned blk_lane = (unsigned)((g * (RD / 4) + (D / 16) * (r16 >> 2)) * 4);
+      const bool bv = !SPLIT || (r16 >> 2) < RD / Q4;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         f32x4 C[T];
@@ -682,7 +685,7 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
             for (int k = 0; k < 4; ++k) {
               const int64_t v = v0 + 16 * t + 4 * g + k;
               const int o = Q4 * (r16 >> 2) + 4 * q + slot;
-              if (prm.rot_dbg && v < n) prm.rot_dbg[(gbase + v) * D + o] = y[k];
+              if (prm.rot_dbg && v < n && bv) prm.rot_dbg[(gbase + v) * RD + o] = y[k];
             }
           }
         }
@@ -692,7 +695,7 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
           unsigned word = (nib[0][p] & vmask[0]) << (4 * slot);
           if constexpr (T > 1) word |= (nib[1][p] & vmask[1]) << (16 + 4 * slot);
           word = quad_or(word);
-          if (slot == 0) st32(blk, word, blk_lane + (unsigned)(p * 4 * D), (unsigned)(4 * q));
+          if (slot == 0 && bv) st32(blk, word, blk_lane + (unsigned)(p * 4 * RD), (unsigned)(4 * q));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -833,7 +836,7 @@ bool quantize_split_fast(int dim, const tq_quantizer* q) {
 }
 
 tq_status launch_quantize_split(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group, const uint16_t* chan,
-                                const void* x, tq_dtype x_dtype, const tq_records& out, hipStream_t stream) {
+                                const void* x, tq_dtype x_dtype, bool blk, const tq_records& out, hipStream_t stream) {
   constexpr int D = 128;
   const tq_quantizer* q0 = qz[0];
   const int dp = q0->d;
@@ -882,10 +885,13 @@ tq_status launch_quantize_split(const tq_quantizer* const* qz, int n_groups, int
             constexpr bool XF32 = decltype(XF)::value;
             return dispatch_bool(dbg, [&](auto DB) -> tq_status {
               constexpr bool DBG = decltype(DB)::value;
-              auto kern = quantize_kernel<D, PP, PROD, XF32, false, DBG, true>;
+              return dispatch_bool(blk, [&](auto BL) -> tq_status {
+              constexpr bool BLK = decltype(BL)::value && !PROD;
+              if (blk && !BLK) return set_error(TQ_ERR_UNSUPPORTED, "split quantize: BLOCK32 is for mse parts");
+              auto kern = quantize_kernel<D, PP, PROD, XF32, BLK, DBG, true>;
               hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
               if (e != hipSuccess) return check_hip(e, "split quantize: set LDS size");
-              constexpr int T = q_tiles(D, PROD, XF32, false);
+              constexpr int T = q_tiles(D, PROD, XF32, BLK);
               const int by_waves = q_waves_per_simd(D, PROD, XF32) * 4 / kQWaves;
               const int by_lds = (int)((160 * 1024) / lds);
               const int per_cu = by_waves < by_lds ? by_waves : by_lds;
@@ -896,6 +902,7 @@ tq_status launch_quantize_split(const tq_quantizer* const* qz, int n_groups, int
               if (want < 1) want = 1;
               hipLaunchKernelGGL(kern, dim3((unsigned)want, (unsigned)ng), dim3(kQThreads), lds, stream, prm, sx);
               return launch_check("split quantize: launch");
+              });
             });
           });
         }
