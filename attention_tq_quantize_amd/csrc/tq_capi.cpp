@@ -531,6 +531,11 @@ tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, int n_gr
       return set_error(TQ_ERR_INVALID_ARG, fmt("split: part %d codes and signs must be 4-byte aligned", p));
   }
   const size_t esize = x_dtype == TQ_F32 ? 4 : 2;
+  if (n_parts == 2 && quantize_split_fusable(dim, qz[0], qz[n_groups])) {
+    // both parts of a 128-channel head in one pass over the rows
+    return launch_quantize_split(qz, qz + n_groups, n_groups, n_per_group, chan.data() + off[0], chan.data() + off[1],
+                                 x, x_dtype, layout == TQ_LAYOUT_BLOCK32, out[0], &out[1], (hipStream_t)stream);
+  }
   for (int p = 0; p < n_parts; ++p) {
     const tq_records& r = out[p];
     const tq_quantizer* const* qp = qz + (size_t)p * n_groups;
@@ -543,8 +548,8 @@ tq_status tq_quantize_split(const tq_quantizer* const* qz, int n_parts, int n_gr
                                    (hipStream_t)stream);
     };
     if (quantize_split_fast(dim, qp[0])) {  // writes either layout itself
-      st = launch_quantize_split(qp, n_groups, n_per_group, chan.data() + off[p], x, x_dtype,
-                                 layout == TQ_LAYOUT_BLOCK32, r, (hipStream_t)stream);
+      st = launch_quantize_split(qp, nullptr, n_groups, n_per_group, chan.data() + off[p], nullptr, x, x_dtype,
+                                 layout == TQ_LAYOUT_BLOCK32, r, nullptr, (hipStream_t)stream);
       if (st != TQ_OK) return st;
       continue;
     }

@@ -92,9 +92,14 @@ bool quantize_split_fast(int dim, const tq_quantizer* q);
 // in-place VECTOR -> BLOCK32 repack of n_blocks blocks of 32 records (d a
 // multiple of 32, 4 planes d <= 8 KiB)
 tq_status launch_repack_block32(uint8_t* codes, int64_t n_blocks, int planes, int d, hipStream_t stream);
-// blk: codes in the BLOCK32 layout (mse parts, n_per_group % 32 == 0)
-tq_status launch_quantize_split(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group, const uint16_t* chan,
-                                const void* x, tq_dtype x_dtype, bool blk, const tq_records& out, hipStream_t stream);
+// blk: codes in the BLOCK32 layout (mse parts, n_per_group % 32 == 0).
+// qz1 / chan1 / out1 non-NULL: the fused two-part split (both parts in one pass;
+// quantize_split_fusable says when).
+bool quantize_split_fusable(int dim, const tq_quantizer* q0, const tq_quantizer* q1);
+tq_status launch_quantize_split(const tq_quantizer* const* qz, const tq_quantizer* const* qz1, int n_groups,
+                                int64_t n_per_group, const uint16_t* chan, const uint16_t* chan1, const void* x,
+                                tq_dtype x_dtype, bool blk, const tq_records& out, const tq_records* out1,
+                                hipStream_t stream);
 tq_status launch_inner_products_fp32(const tq_quantizer* q, const float* y, int64_t y_stride, const uint16_t* chan,
                                      bool accumulate, int64_t m, const uint8_t* codes, const uint8_t* signs,
                                      const float* norms, const float* rnorms, int64_t n, float* out,

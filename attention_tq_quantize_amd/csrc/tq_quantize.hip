@@ -65,13 +65,35 @@ struct QuantParams {
 // coordinate j of the part (o < d_p), zero elsewhere; likewise S' = S Pi^T on
 // the first d_p rotated coordinates. Lane groups g < d_p / 32 then hold the
 // part's rotated coordinates and write its records.
+//
+// Fused two-part split (both parts of a 128-channel head whose dimensions are
+// multiples of 32 and add up to 128, same variant): one pass over the row. The
+// two rotations form one block-diagonal 128 x 128 matrix (part 0 on output
+// coordinates [0, d_0), part 1 on [d_0, 128)), so each lane group's 32 output
+// coordinates belong to one part; the part with fewer planes runs the same
+// P-plane search on its thresholds with +inf above them (its top planes come out
+// 0 and are not stored).
 constexpr int kQSplitGroups = 16;
+constexpr uint8_t kNoChannel = 0xFF;
 struct QuantSplitParams {
-  int dp;                                // d_p, a multiple of 32 up to 128
-  unsigned chan_mask[kQSplitGroups][4];  // bit b of word w: channel 32 w + b is in the part
-  int8_t inv[kQSplitGroups][128];        // channel -> coordinate of the part, -1 if absent
+  int dp;                                // d_p (fused: d_0), a multiple of 32 up to 128
+  unsigned chan_mask[kQSplitGroups][4];  // bit b of word w: channel 32 w + b is in the part (fused: part 0)
+  uint8_t inv[kQSplitGroups][128];       // channel -> (part << 7) | its coordinate in the part; kNoChannel: none
   const float* pi[kQSplitGroups];        // Pi_p, fp32 [d_p][d_p]
   const float* sp[kQSplitGroups];        // prod: S' = S_p Pi_p^T, fp32 [d_p][d_p]
+  // fused only: part 1's dimension and tables, both parts' plane counts, their
+  // thresholds and centroids laid on the P-plane search, part 1's records
+  int dp1, planes0, planes1;
+  unsigned chan_mask1[kQSplitGroups][4];
+  const float* pi1[kQSplitGroups];
+  const float* sp1[kQSplitGroups];
+  float thr_e[2][15], cen_e[2][16];
+  uint8_t* codes1;
+  uint8_t* signs1;
+  float* norms1;
+  float* rnorms1;
+  float* rot1;
+  float* proj1;
 };
 struct QuantNoSplit {};
 
@@ -79,8 +101,11 @@ struct QuantNoSplit {};
 __host__ __device__ constexpr int q_tiles(int D, bool prod, bool xf32, bool blk) {
   return (D == 256 && (prod || xf32) && !blk) ? 1 : 2;
 }
-// waves per SIMD: 4 where the registers allow (bf16 mse up to d = 128), else 2
-__host__ __device__ constexpr int q_waves_per_simd(int D, bool prod, bool xf32) { return (D <= 128 && !prod && !xf32) ? 4 : 2; }
+// waves per SIMD: 4 where the registers allow (bf16 mse up to d = 128, not the
+// fused two-part split, which keeps both parts' norms), else 2
+__host__ __device__ constexpr int q_waves_per_simd(int D, bool prod, bool xf32, bool fused = false) {
+  return (D <= 128 && !prod && !xf32 && !fused) ? 4 : 2;
+}
 __host__ __device__ constexpr bool q_prefetch(int D, bool xf32) { return !(D == 256 && xf32); }
 
 // Raw input of one 16-vector tile for lane (r, g): vector r, coordinates
@@ -139,6 +164,46 @@ __device__ __forceinline__ void mask_tile(XTile<D, XF32>& t, unsigned cm) {
     }
     t.raw[i] = u32x4{w[0], w[1], w[2], w[3]};
   }
+}
+
+// This lane's part of |x|^2 over the channels of cm (split parts): as
+// tile_operands (v_dot2 pairs for bf16, fp64 fma for fp32) on the masked words,
+// and the exact fp64 sum for bf16 (the fallback for tiny or huge vectors).
+template <int D, bool XF32>
+__device__ __forceinline__ double sumsq_masked(const XTile<D, XF32>& t, unsigned cm, bool exact) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  auto bit = [&](int pos) -> unsigned { return (unsigned)(((int)(cm << (31 - pos))) >> 31); };
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < XTile<D, XF32>::NR; ++i) {
+    unsigned w[4] = {t.raw[i].x, t.raw[i].y, t.raw[i].z, t.raw[i].w};
+    if constexpr (XF32) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float f = __uint_as_float(w[j] & bit(4 * i + j));
+        acc = fma((double)f, (double)f, acc);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] &= (bit(8 * i + 2 * j) & 0xFFFFu) | (bit(8 * i + 2 * j + 1) << 16);
+      if (exact) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float a = bf16_val(w[j] & 0xFFFFu), b = bf16_val(w[j] >> 16);
+          acc = fma((double)a, (double)a, acc);
+          acc = fma((double)b, (double)b, acc);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const bf2 h0 = __builtin_bit_cast(bf2, w[2 * e]), h1 = __builtin_bit_cast(bf2, w[2 * e + 1]);
+          acc += (double)__builtin_amdgcn_fdot2_f32_bf16(h1, h1, __builtin_amdgcn_fdot2_f32_bf16(h0, h0, 0.0f, false),
+                                                         false);
+        }
+      }
+    }
+  }
+  return acc;
 }
 
 // |x|^2 of bf16 input from the fast part sums is used when it lies in
@@ -299,14 +364,16 @@ __device__ __forceinline__ unsigned quad_or(unsigned w) {
   return w;
 }
 
-template <int D, int P, bool PROD, bool XF32, bool BLK, bool DBG, bool SPLIT = false>
-__global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void quantize_kernel(
-    QuantParams prm, std::conditional_t<SPLIT, QuantSplitParams, QuantNoSplit> sx) {
+// SPLIT: 0 whole vectors, 1 one part of a channel split, 2 the fused two-part split
+template <int D, int P, bool PROD, bool XF32, bool BLK, bool DBG, int SPLIT = 0>
+__global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT == 2)) void quantize_kernel(
+    QuantParams prm, std::conditional_t<SPLIT != 0, QuantSplitParams, QuantNoSplit> sx) {
   static_assert(!SPLIT || D == 128, "split parts: d = 128 heads");
+  constexpr bool FUSED = SPLIT == 2;
   constexpr int NQ = D / 16, NK = D / 32, Q4 = D / 4;
   constexpr int T = q_tiles(D, PROD, XF32, BLK);
   // split mse at four waves per SIMD has no registers for the next step's tiles
-  constexpr bool PREF = q_prefetch(D, XF32) && !(SPLIT && !PROD && !XF32);
+  constexpr bool PREF = q_prefetch(D, XF32) && !(SPLIT == 1 && !PROD && !XF32);
   constexpr int WPL = Q4 >= 32 ? Q4 / 32 : 1;  // 32-bit words per plane per lane (vector layout)
   constexpr int PP = P > 0 ? P : 1;
   constexpr bool LDS_FRAG = D <= 128;
@@ -318,14 +385,36 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
   const int r16 = lane & 15, g = lane >> 4;
   const int grp = blockIdx.y;
   // record width (d_p of a split part), whether this lane group holds record
-  // coordinates, and its channel mask
+  // coordinates, and its channel mask. Fused split: this lane's part (by lane
+  // group for vectors, by coordinate group r16 / 4 for blocks), its plane count,
+  // its lane group within the part and its record arrays.
   int RD = D;
   bool gv = true;
-  unsigned cm = ~0u;
+  unsigned cm = ~0u, cm0 = 0u, cm1 = 0u;
+  int part = 0, RP = P, gl = g, G0 = 4;
+  uint8_t* r_codes = prm.codes;
+  uint8_t* r_signs = prm.signs;
+  float* r_rot = prm.rot_dbg;
+  float* r_proj = prm.proj_dbg;
   if constexpr (SPLIT) {
     RD = sx.dp;
     gv = g < sx.dp / Q4;
     cm = sx.chan_mask[grp][g];
+  }
+  if constexpr (FUSED) {
+    G0 = sx.dp / Q4;
+    cm0 = sx.chan_mask[grp][g];
+    cm1 = sx.chan_mask1[grp][g];
+    cm = cm0 | cm1;
+    gv = true;
+    part = (BLK ? (r16 >> 2) : g) >= G0 ? 1 : 0;
+    RD = part ? sx.dp1 : sx.dp;
+    RP = part ? sx.planes1 : sx.planes0;
+    gl = g - (part ? G0 : 0);
+    r_codes = part ? sx.codes1 : prm.codes;
+    r_signs = part ? sx.signs1 : prm.signs;
+    r_rot = part ? sx.rot1 : prm.rot_dbg;
+    r_proj = part ? sx.proj1 : prm.proj_dbg;
   }
   const int64_t n = prm.n_per_group;
   const int64_t gbase = (prm.group_base + grp) * n;
@@ -334,9 +423,19 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
   constexpr int NCEN = 1 << (P > 0 ? P : 0);
   float thr[NTHR], cen[NCEN];
 #pragma unroll
-  for (int i = 0; i < NTHR; ++i) thr[i] = opaque_vgpr(prm.thr[i]);
+  for (int i = 0; i < NTHR; ++i) {
+    if constexpr (FUSED)
+      thr[i] = opaque_vgpr(part ? sx.thr_e[1][i] : sx.thr_e[0][i]);
+    else
+      thr[i] = opaque_vgpr(prm.thr[i]);
+  }
 #pragma unroll
-  for (int i = 0; i < NCEN; ++i) cen[i] = PROD ? opaque_vgpr(prm.cen[i]) : 0.0f;
+  for (int i = 0; i < NCEN; ++i) {
+    if constexpr (FUSED)
+      cen[i] = PROD ? opaque_vgpr(part ? sx.cen_e[1][i] : sx.cen_e[0][i]) : 0.0f;
+    else
+      cen[i] = PROD ? opaque_vgpr(prm.cen[i]) : 0.0f;
+  }
   const int64_t stride = (int64_t)gridDim.x * kQWaves;
   int64_t step = (int64_t)blockIdx.x * kQWaves + wave;
 
@@ -359,23 +458,33 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
   if constexpr (SPLIT) {
     // fragments of the part's matrices laid over the head's channels, built here
     // from the fp32 tables (hi = bf16(v), lo = bf16(v - hi), as on the host)
+    // (fused: block-diagonal, part 0 on output rows [0, d_0), part 1 below)
     constexpr int HALF = FRAG_VECS / 2;
-    const int dp = sx.dp;
-    const int8_t* inv = sx.inv[grp];
+    const int dp0 = sx.dp;
+    const uint8_t* inv = sx.inv[grp];
     for (int w = 0; w < (PROD ? 2 : 1); ++w) {
-      const float* M = w ? sx.sp[grp] : sx.pi[grp];
       for (int i = threadIdx.x; i < HALF; i += kQThreads) {
         const int l = i & 63, ks = (i >> 6) % NK, q = (i >> 6) / NK;
         const int m = l & 15;
         const int row = Q4 * (m >> 2) + 4 * q + (m & 3);
         const int col = Q4 * (l >> 4) + 8 * ks;
+        const int prow = (FUSED && row >= dp0) ? 1 : 0;  // the part of this output row
+        const int r = row - (prow ? dp0 : 0), dpr = prow ? sx.dp1 : dp0;
+        const float* M = w ? (prow ? sx.sp1[grp] : sx.sp[grp]) : (prow ? sx.pi1[grp] : sx.pi[grp]);
         unsigned h[8], lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          // Pi_p: input channel col + e is coordinate inv of the part; S': the
-          // residual's coordinate is col + e itself
-          const int j = w ? (col + e < dp ? col + e : -1) : (int)inv[col + e];
-          const float v = (row < dp && j >= 0) ? M[row * dp + j] : 0.0f;
+          // Pi_p: input channel col + e is coordinate inv of its part; S': the
+          // residual's coordinate is col + e itself (minus d_0 in part 1)
+          int j;
+          if (w) {
+            const int c = col + e, pc = (FUSED && c >= dp0) ? 1 : 0;
+            j = pc == prow ? c - (pc ? dp0 : 0) : -1;
+          } else {
+            const unsigned iv = inv[col + e];
+            j = (iv != kNoChannel && (int)(iv >> 7) == prow) ? (int)(iv & 0x7Fu) : -1;
+          }
+          const float v = (r < dpr && j >= 0 && j < dpr) ? M[r * dpr + j] : 0.0f;
           h[e] = bf16_part(v, false);
           lo[e] = bf16_part(v, true);
         }
@@ -427,14 +536,35 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
     }
     u32x4 xh[T][NK], xl[T][XF32 ? NK : 1];
     double ss[T];
+    double ssp[FUSED ? T : 1][2];  // fused: |x|^2 over each part's channels
     // split: an opaque copy of the channel mask per step keeps the compiler from
     // holding every expanded word mask across the loop (register spills)
-    unsigned cm_l = cm;
+    unsigned cm_l = cm, cm0_l = cm0, cm1_l = cm1;
     if constexpr (SPLIT) asm volatile("" : "+v"(cm_l));
+    if constexpr (FUSED) asm volatile("" : "+v"(cm0_l), "+v"(cm1_l));
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if constexpr (SPLIT) mask_tile<D, XF32>(cur[t], cm_l);
       ss[t] = tile_operands<D, XF32>(cur[t], xh[t], xl[t]);
+      if constexpr (FUSED) {
+        // both parts' sums; the lanes' own part's goes on in ss
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          double a = sumsq_masked<D, XF32>(cur[t], k ? cm1_l : cm0_l, false);
+          a += __shfl_xor(a, 16);
+          a += __shfl_xor(a, 32);
+          if constexpr (!XF32) {
+            if (!(a >= kSumsqFastLo && a <= kSumsqFastHi)) {  // the vector's four lanes together
+              a = sumsq_masked<D, XF32>(cur[t], k ? cm1_l : cm0_l, true);
+              a += __shfl_xor(a, 16);
+              a += __shfl_xor(a, 32);
+            }
+          }
+          ssp[t][k] = a;
+        }
+        ss[t] = part ? ssp[t][1] : ssp[t][0];
+        continue;
+      }
       ss[t] += __shfl_xor(ss[t], 16);
       ss[t] += __shfl_xor(ss[t], 32);
       if constexpr (!XF32) {
@@ -493,8 +623,8 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
           const float y[4] = {C[t].x * inv[t], C[t].y * inv[t], C[t].z * inv[t], C[t].w * inv[t]};
           if constexpr (DBG) {
             const int64_t v = v0 + 16 * t + r16;
-            if (prm.rot_dbg && v < n && gv)
-              *(float4*)(prm.rot_dbg + (gbase + v) * RD + Q4 * g + 4 * q) = float4{y[0], y[1], y[2], y[3]};
+            if (r_rot && v < n && gv)
+              *(float4*)(r_rot + (gbase + v) * RD + Q4 * gl + 4 * q) = float4{y[0], y[1], y[2], y[3]};
           }
           float e4[4];
           PlaneMasks<P> pm[4];
@@ -536,21 +666,25 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
         // keep the scheduler from hoisting every block's fragment reads (register spills)
         __builtin_amdgcn_sched_barrier(0);
       }
-      // wave-uniform bases of this step, 32-bit lane offsets
+      // bases of this step (wave-uniform unless fused), 32-bit lane offsets
       float* nbase = prm.norms + gbase + v0;
-      uint8_t* cbase = prm.codes + (gbase + v0) * (P * RD / 8);
+      uint8_t* cbase = r_codes + (gbase + v0) * (RP * RD / 8);
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const int rel = 16 * t + r16;
         if (v0 + rel < n) {
           if (g == 0) nbase[rel] = (float)nu[t];
+          if constexpr (FUSED) {
+            if (g == G0) sx.norms1[gbase + v0 + rel] = (float)nu[t];
+          }
           if (P > 0 && gv) {
             // 32-bit lane offset; opaque for a runtime record width, which keeps
             // the compiler from holding 64-bit addresses across the loop
-            unsigned lo = (unsigned)rel * (unsigned)(P * RD / 8) + (unsigned)(g * (Q4 / 8));
+            unsigned lo = (unsigned)rel * (unsigned)(RP * RD / 8) + (unsigned)(gl * (Q4 / 8));
             if constexpr (SPLIT) asm volatile("" : "+v"(lo));
 #pragma unroll
             for (int p = 0; p < P; ++p) {
+              if (FUSED && p >= RP) continue;  // the part's top planes (all zero) are not stored
               if constexpr (Q4 >= 32) {
 #pragma unroll
                 for (int w = 0; w < WPL; ++w)
@@ -567,8 +701,17 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
         unsigned sw[T][WPL];
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          esq[t] += __shfl_xor(esq[t], 16);
-          esq[t] += __shfl_xor(esq[t], 32);
+          if constexpr (FUSED) {  // each part's residual over its own lane groups
+            float e0 = part ? 0.0f : esq[t], e1 = part ? esq[t] : 0.0f;
+            e0 += __shfl_xor(e0, 16);
+            e1 += __shfl_xor(e1, 16);
+            e0 += __shfl_xor(e0, 32);
+            e1 += __shfl_xor(e1, 32);
+            esq[t] = part ? e1 : e0;
+          } else {
+            esq[t] += __shfl_xor(esq[t], 16);
+            esq[t] += __shfl_xor(esq[t], 32);
+          }
 #pragma unroll
           for (int w = 0; w < WPL; ++w) sw[t][w] = 0u;
         }
@@ -599,23 +742,26 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
             }
             if constexpr (DBG) {
               const int64_t v = v0 + 16 * t + r16;
-              if (prm.proj_dbg && v < n && gv)
-                *(float4*)(prm.proj_dbg + (gbase + v) * RD + Q4 * g + 4 * q) = float4{pv[0], pv[1], pv[2], pv[3]};
+              if (r_proj && v < n && gv)
+                *(float4*)(r_proj + (gbase + v) * RD + Q4 * gl + 4 * q) = float4{pv[0], pv[1], pv[2], pv[3]};
             }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
         float* rbase = prm.rnorms + gbase + v0;
-        uint8_t* sbase = prm.signs + (gbase + v0) * (RD / 8);
+        uint8_t* sbase = r_signs + (gbase + v0) * (RD / 8);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           const int rel = 16 * t + r16;
           if (v0 + rel < n) {
             if (g == 0) rbase[rel] = valid[t] ? sqrtf(esq[t]) : 0.0f;
+            if constexpr (FUSED) {
+              if (g == G0) sx.rnorms1[gbase + v0 + rel] = valid[t] ? sqrtf(esq[t]) : 0.0f;
+            }
             uint8_t* dst = sbase + (unsigned)rel * (RD / 8);
             if constexpr (Q4 >= 32) {
               if (gv) {
-                unsigned lo = (unsigned)rel * (unsigned)(RD / 8) + (unsigned)(g * (Q4 / 8));
+                unsigned lo = (unsigned)rel * (unsigned)(RD / 8) + (unsigned)(gl * (Q4 / 8));
                 if constexpr (SPLIT) asm volatile("" : "+v"(lo));
 #pragma unroll
                 for (int w = 0; w < WPL; ++w) *(unsigned*)(sbase + lo + 4 * w) = valid[t] ? sw[t][w] : 0u;
@@ -634,24 +780,46 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
       unsigned vmask[T];  // bit k: vector 16t + 4g + k has a nonzero norm
 #pragma unroll
       for (int t = 0; t < T; ++t) {
+        const int64_t v = v0 + 16 * t + r16;
+        vmask[t] = 0u;
+        if constexpr (FUSED) {
+          // vector 16t + r16's norm over each part; this lane takes its part's
+          const double nu0 = sqrt(ssp[t][0]), nu1 = sqrt(ssp[t][1]);
+          const float i0 = nu0 > 0.0 ? (float)(1.0 / nu0) : 0.0f, i1 = nu1 > 0.0 ? (float)(1.0 / nu1) : 0.0f;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float a = __shfl(i0, 4 * g + k), b = __shfl(i1, 4 * g + k);
+            inv[t][k] = part ? b : a;
+            vmask[t] |= (inv[t][k] > 0.0f ? 1u : 0u) << k;
+          }
+          if (g == 0 && v < n) prm.norms[gbase + v] = (float)nu0;
+          if (g == 1 && v < n) sx.norms1[gbase + v] = (float)nu1;
+          continue;
+        }
         const double nu_own = sqrt(ss[t]);  // vector 16t + r16
         const float inv_own = nu_own > 0.0 ? (float)(1.0 / nu_own) : 0.0f;
-        vmask[t] = 0u;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           inv[t][k] = __shfl(inv_own, 4 * g + k);
           vmask[t] |= (inv[t][k] > 0.0f ? 1u : 0u) << k;
         }
-        const int64_t v = v0 + 16 * t + r16;
         if (g == 0 && v < n) prm.norms[gbase + v] = (float)nu_own;
       }
       const int slot = r16 & 3;
       // this step's 32-vector block; 32-bit lane offset of word (p = 0, q = 0)
       // (split: a block of the part's records is 4 P d_p bytes, and lanes whose
       // coordinates lie beyond d_p store nothing)
+      // (fused: each part's blocks in its own array, 4 P_p d_p bytes each; this
+      // lane's coordinate group counted within its part)
       const buf_t blk = make_buf(prm.codes + ((gbase + v0) / 32) * (int64_t)(4 * P * RD), (unsigned)(4 * P * RD));
-      const unsigned blk_lane = (unsigned)((g * (RD / 4) + (D / 16) * (r16 >> 2)) * 4);
-      const bool bv = !SPLIT || (r16 >> 2) < RD / Q4;
+      buf_t blk0 = blk, blk1 = blk;
+      if constexpr (FUSED) {
+        const int b0 = 4 * sx.planes0 * sx.dp, b1 = 4 * sx.planes1 * sx.dp1;
+        blk0 = make_buf(prm.codes + ((gbase + v0) / 32) * (int64_t)b0, (unsigned)b0);
+        blk1 = make_buf(sx.codes1 + ((gbase + v0) / 32) * (int64_t)b1, (unsigned)b1);
+      }
+      const unsigned blk_lane = (unsigned)((g * (RD / 4) + (D / 16) * ((r16 >> 2) - (part ? G0 : 0))) * 4);
+      const bool bv = FUSED || !SPLIT || (r16 >> 2) < RD / Q4;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         f32x4 C[T];
@@ -684,8 +852,8 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               const int64_t v = v0 + 16 * t + 4 * g + k;
-              const int o = Q4 * (r16 >> 2) + 4 * q + slot;
-              if (prm.rot_dbg && v < n && bv) prm.rot_dbg[(gbase + v) * RD + o] = y[k];
+              const int o = Q4 * ((r16 >> 2) - (part ? G0 : 0)) + 4 * q + slot;  // within the lane's part
+              if (r_rot && v < n && bv) r_rot[(gbase + v) * RD + o] = y[k];
             }
           }
         }
@@ -695,7 +863,16 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32)) void qu
           unsigned word = (nib[0][p] & vmask[0]) << (4 * slot);
           if constexpr (T > 1) word |= (nib[1][p] & vmask[1]) << (16 + 4 * slot);
           word = quad_or(word);
-          if (slot == 0 && bv) st32(blk, word, blk_lane + (unsigned)(p * 4 * RD), (unsigned)(4 * q));
+          if constexpr (FUSED) {
+            if (slot == 0 && p < RP) {
+              if (part)
+                st32(blk1, word, blk_lane + (unsigned)(p * 4 * RD), (unsigned)(4 * q));
+              else
+                st32(blk0, word, blk_lane + (unsigned)(p * 4 * RD), (unsigned)(4 * q));
+            }
+          } else {
+            if (slot == 0 && bv) st32(blk, word, blk_lane + (unsigned)(p * 4 * RD), (unsigned)(4 * q));
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -835,15 +1012,25 @@ bool quantize_split_fast(int dim, const tq_quantizer* q) {
          (prod ? q->planes <= 3 && q->sp32 != nullptr : q->planes >= 1);
 }
 
-tq_status launch_quantize_split(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group, const uint16_t* chan,
-                                const void* x, tq_dtype x_dtype, bool blk, const tq_records& out, hipStream_t stream) {
+bool quantize_split_fusable(int dim, const tq_quantizer* q0, const tq_quantizer* q1) {
+  return quantize_split_fast(dim, q0) && quantize_split_fast(dim, q1) && q0->variant == q1->variant &&
+         q0->d + q1->d == dim;
+}
+
+tq_status launch_quantize_split(const tq_quantizer* const* qz, const tq_quantizer* const* qz1, int n_groups,
+                                int64_t n_per_group, const uint16_t* chan, const uint16_t* chan1, const void* x,
+                                tq_dtype x_dtype, bool blk, const tq_records& out, const tq_records* out1,
+                                hipStream_t stream) {
   constexpr int D = 128;
+  const bool fused = qz1 != nullptr;
   const tq_quantizer* q0 = qz[0];
+  const tq_quantizer* q1 = fused ? qz1[0] : nullptr;
   const int dp = q0->d;
   const bool prod = q0->variant == TQ_PROD;
   const bool xf32 = x_dtype == TQ_F32;
-  const bool dbg = out.rot_dbg != nullptr || out.proj_dbg != nullptr;
-  const int P = q0->planes;
+  const bool dbg = out.rot_dbg != nullptr || out.proj_dbg != nullptr ||
+                   (fused && (out1->rot_dbg != nullptr || out1->proj_dbg != nullptr));
+  const int P = fused && q1->planes > q0->planes ? q1->planes : q0->planes;
   const size_t lds = (size_t)2 * D * D * 2 * (prod ? 2 : 1);
   for (int g0 = 0; g0 < n_groups; g0 += kQSplitGroups) {
     const int ng = n_groups - g0 < kQSplitGroups ? n_groups - g0 : kQSplitGroups;
@@ -859,20 +1046,46 @@ tq_status launch_quantize_split(const tq_quantizer* const* qz, int n_groups, int
     prm.rnorms = out.rnorms;
     prm.rot_dbg = out.rot_dbg;
     prm.proj_dbg = out.proj_dbg;
-    const int K = 1 << P;
-    for (int i = 0; i + 1 < K; ++i) prm.thr[i] = q0->cb.thresholds[i];
-    for (int i = 0; i < K; ++i) prm.cen[i] = q0->cb.centroids[i];
+    for (int i = 0; i + 1 < (1 << q0->planes); ++i) prm.thr[i] = q0->cb.thresholds[i];
+    for (int i = 0; i < (1 << q0->planes); ++i) prm.cen[i] = q0->cb.centroids[i];
     QuantSplitParams sx{};
     sx.dp = dp;
     for (int g = 0; g < ng; ++g) {
-      const uint16_t* c = chan + (size_t)(g0 + g) * dp;
-      for (int k = 0; k < D; ++k) sx.inv[g][k] = -1;
-      for (int j = 0; j < dp; ++j) {
-        sx.inv[g][c[j]] = (int8_t)j;
-        sx.chan_mask[g][c[j] / 32] |= 1u << (c[j] % 32);
+      for (int k = 0; k < D; ++k) sx.inv[g][k] = kNoChannel;
+      for (int part = 0; part < (fused ? 2 : 1); ++part) {
+        const int d = part ? q1->d : dp;
+        const uint16_t* c = (part ? chan1 : chan) + (size_t)(g0 + g) * d;
+        unsigned(*mask)[4] = part ? sx.chan_mask1 : sx.chan_mask;
+        for (int j = 0; j < d; ++j) {
+          sx.inv[g][c[j]] = (uint8_t)((part << 7) | j);
+          mask[g][c[j] / 32] |= 1u << (c[j] % 32);
+        }
       }
       sx.pi[g] = qz[g0 + g]->pi32;
       sx.sp[g] = qz[g0 + g]->sp32;
+      if (fused) {
+        sx.pi1[g] = qz1[g0 + g]->pi32;
+        sx.sp1[g] = qz1[g0 + g]->sp32;
+      }
+    }
+    if (fused) {
+      sx.dp1 = q1->d;
+      sx.planes0 = q0->planes;
+      sx.planes1 = q1->planes;
+      // each part's thresholds and centroids on the P-plane search: a part with
+      // fewer planes keeps its own below +inf, so its top planes come out 0
+      for (int part = 0; part < 2; ++part) {
+        const tq_quantizer* q = part ? q1 : q0;
+        for (int i = 0; i < 15; ++i)
+          sx.thr_e[part][i] = i + 1 < (1 << q->planes) ? q->cb.thresholds[i] : INFINITY;
+        for (int i = 0; i < 16; ++i) sx.cen_e[part][i] = i < (1 << q->planes) ? q->cb.centroids[i] : 0.0f;
+      }
+      sx.codes1 = out1->codes;
+      sx.signs1 = out1->signs;
+      sx.norms1 = out1->norms;
+      sx.rnorms1 = out1->rnorms;
+      sx.rot1 = out1->rot_dbg;
+      sx.proj1 = out1->proj_dbg;
     }
     tq_status st = dispatch_planes(P, [&](auto PC) -> tq_status {
       constexpr int PP = decltype(PC)::value;
@@ -886,22 +1099,26 @@ tq_status launch_quantize_split(const tq_quantizer* const* qz, int n_groups, int
             return dispatch_bool(dbg, [&](auto DB) -> tq_status {
               constexpr bool DBG = decltype(DB)::value;
               return dispatch_bool(blk, [&](auto BL) -> tq_status {
-              constexpr bool BLK = decltype(BL)::value && !PROD;
-              if (blk && !BLK) return set_error(TQ_ERR_UNSUPPORTED, "split quantize: BLOCK32 is for mse parts");
-              auto kern = quantize_kernel<D, PP, PROD, XF32, BLK, DBG, true>;
-              hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-              if (e != hipSuccess) return check_hip(e, "split quantize: set LDS size");
-              constexpr int T = q_tiles(D, PROD, XF32, BLK);
-              const int by_waves = q_waves_per_simd(D, PROD, XF32) * 4 / kQWaves;
-              const int by_lds = (int)((160 * 1024) / lds);
-              const int per_cu = by_waves < by_lds ? by_waves : by_lds;
-              const int64_t steps = (n_per_group + 16 * T - 1) / (16 * T);
-              int64_t want = ((int64_t)(per_cu > 0 ? per_cu : 1) * device_cus() + ng - 1) / ng;
-              const int64_t cap = (steps + kQWaves - 1) / kQWaves;
-              if (want > cap) want = cap;
-              if (want < 1) want = 1;
-              hipLaunchKernelGGL(kern, dim3((unsigned)want, (unsigned)ng), dim3(kQThreads), lds, stream, prm, sx);
-              return launch_check("split quantize: launch");
+                constexpr bool BLK = decltype(BL)::value && !PROD;
+                if (blk && !BLK) return set_error(TQ_ERR_UNSUPPORTED, "split quantize: BLOCK32 is for mse parts");
+                return dispatch_bool(fused, [&](auto FU) -> tq_status {
+                  constexpr int SPLIT = decltype(FU)::value ? 2 : 1;
+                  auto kern = quantize_kernel<D, PP, PROD, XF32, BLK, DBG, SPLIT>;
+                  hipError_t e =
+                      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                  if (e != hipSuccess) return check_hip(e, "split quantize: set LDS size");
+                  constexpr int T = q_tiles(D, PROD, XF32, BLK);
+                  const int by_waves = q_waves_per_simd(D, PROD, XF32, SPLIT == 2) * 4 / kQWaves;
+                  const int by_lds = (int)((160 * 1024) / lds);
+                  const int per_cu = by_waves < by_lds ? by_waves : by_lds;
+                  const int64_t steps = (n_per_group + 16 * T - 1) / (16 * T);
+                  int64_t want = ((int64_t)(per_cu > 0 ? per_cu : 1) * device_cus() + ng - 1) / ng;
+                  const int64_t cap = (steps + kQWaves - 1) / kQWaves;
+                  if (want > cap) want = cap;
+                  if (want < 1) want = 1;
+                  hipLaunchKernelGGL(kern, dim3((unsigned)want, (unsigned)ng), dim3(kQThreads), lds, stream, prm, sx);
+                  return launch_check("split quantize: launch");
+                });
               });
             });
           });
