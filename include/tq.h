@@ -241,10 +241,11 @@ tq_status tq_inner_products(const tq_quantizer* q, const float* y, int64_t m,
  *              n_groups*n_per_group rows, as for tq_quantize with d = d_p
  *              (rot_dbg / proj_dbg may be NULL; codes and signs 4-byte aligned).
  * On the caller's stream. dim = 128 with d_p a multiple of 32 (mse, or prod of
- * at most 4 bits): one matrix-core launch per part and 16 groups, the part's
- * matrices laid over the head's channels. Otherwise the generic fp32 kernels,
- * one launch per part and group, where BLOCK32 adds one in-place repack
- * launch per part. Allocates nothing.
+ * at most 4 bits): matrix-core launches of 16 groups with the parts' matrices
+ * laid over the head's channels, both parts in one pass when two parts of one
+ * variant cover all 128 channels, else one launch per part. Otherwise the
+ * generic fp32 kernels, one launch per part and group, where BLOCK32 adds one
+ * in-place repack launch per part. Allocates nothing.
  * Errors: TQ_ERR_INVALID_ARG (NULL pointers, n_groups < 1, handles of a part
  * that differ, a channel out of range or repeated within a group, more
  * channels than dim, BLOCK32 with n_per_group % 32 != 0), TQ_ERR_UNSUPPORTED
