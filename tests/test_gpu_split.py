@@ -56,6 +56,10 @@ CASES = [
     ("kv_mse_32x3_96x2", 128, 700, "bf16", [(32, "mse", 3), ("rest", "mse", 2)]),
     ("kv_prod_32x3_96x2", 128, 500, "f32", [(32, "prod", 3), ("rest", "prod", 2)]),
     ("kv_prod_bf16_32x4_96x3", 128, 333, "bf16", [(32, "prod", 4), ("rest", "prod", 3)]),
+    # the fused two-part kernel with the wider part first, and with a 1-bit prod
+    # part (no code planes) beside a 2-bit one
+    ("fused_mse_96x1_32x4", 128, 300, "f32", [(96, "mse", 1), ("rest", "mse", 4)]),
+    ("fused_prod_64x2_64x1", 128, 257, "bf16", [(64, "prod", 2), ("rest", "prod", 1)]),
     ("mixed_drop", 128, 300, "f32", [(32, "mse", 4), (64, "prod", 1)]),
     ("mixed_drop_bf16", 128, 290, "bf16", [(64, "mse", 1), (32, "prod", 2)]),
     ("generic_dim192", 192, 200, "bf16", [(64, "mse", 3), ("rest", "prod", 2)]),
@@ -171,8 +175,9 @@ def test_split_quantize_grouped_parity(gpu_lib, dt):
                 _check_part(parts_g[g][p], qs_g[g][p], {k: v[g] for k, v in got[p].items()}, ref[p])
 
 
-@pytest.mark.parametrize("dim,spec", [(128, [(32, 3), ("rest", 2)]), (192, [(64, 4), ("rest", 1)])],
-                         ids=["matrix_cores_32x3_96x2", "generic_64x4_128x1"])
+@pytest.mark.parametrize("dim,spec", [(128, [(32, 3), ("rest", 2)]), (128, [(64, 1), ("rest", 4)]),
+                                      (128, [(32, 4), (32, 2)]), (192, [(64, 4), ("rest", 1)])],
+                         ids=["fused_32x3_96x2", "fused_64x1_64x4", "per_part_32x4_32x2", "generic_64x4_128x1"])
 def test_split_quantize_block32(gpu_lib, dim, spec):
     """layout="block32" (the value layout of a split cache): every part's codes
     equal the oracle's BLOCK32 packing of the indices the kernel's own rotated
