@@ -376,14 +376,21 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
   constexpr bool PREF = q_prefetch(D, XF32) && !(SPLIT == 1 && !PROD && !XF32);
   constexpr int WPL = Q4 >= 32 ? Q4 / 32 : 1;  // 32-bit words per plane per lane (vector layout)
   constexpr int PP = P > 0 ? P : 1;
-  constexpr bool LDS_FRAG = D <= 128;
-  constexpr int FRAG_VECS = 2 * NQ * NK * 64;  // u32x4 per matrix (hi + lo)
+  // d = 256 mse: two workgroup sets, each for half of the output rows (16-row
+  // blocks [QH h, QH h + QH) and 32-bit words h of the vector layout), whose
+  // fragments (128 KB) fit in LDS; every vector is read by both
+  constexpr bool HALF = D == 256 && !PROD && SPLIT == 0;
+  constexpr int QH = HALF ? NQ / 2 : NQ;  // 16-row blocks per workgroup
+  constexpr bool LDS_FRAG = D <= 128 || HALF;
+  constexpr int FRAG_VECS = 2 * QH * NK * 64;  // u32x4 of this workgroup's fragments per matrix (hi + lo)
   extern __shared__ u32x4 smem_frag[];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const int grp = blockIdx.y;
+  const int grp = HALF ? (int)(blockIdx.y >> 1) : (int)blockIdx.y;
+  const int hq = HALF ? (int)(blockIdx.y & 1) : 0;  // this workgroup's half of the output rows
+  const int q0 = hq * QH;
   // record width (d_p of a split part), whether this lane group holds record
   // coordinates, and its channel mask. Fused split: this lane's part (by lane
   // group for vectors, by coordinate group r16 / 4 for blocks), its plane count,
@@ -498,7 +505,15 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
     fsp = smem_frag + FRAG_VECS;
   } else if constexpr (LDS_FRAG) {
     const u32x4* src = (const u32x4*)prm.pi_frag[grp];
-    for (int i = threadIdx.x; i < FRAG_VECS; i += kQThreads) smem_frag[i] = src[i];
+    if constexpr (HALF) {
+      // blocks [q0, q0 + QH) of the hi and of the lo fragments ([hilo][q][ks][lane] in memory)
+      for (int i = threadIdx.x; i < FRAG_VECS; i += kQThreads) {
+        const int hl = i / (QH * NK * 64), rest = i % (QH * NK * 64);
+        smem_frag[i] = src[(hl * NQ + q0) * NK * 64 + rest];
+      }
+    } else {
+      for (int i = threadIdx.x; i < FRAG_VECS; i += kQThreads) smem_frag[i] = src[i];
+    }
     if constexpr (PROD) {
       const u32x4* s2 = (const u32x4*)prm.sp_frag[grp];
       for (int i = threadIdx.x; i < FRAG_VECS; i += kQThreads) smem_frag[FRAG_VECS + i] = s2[i];
@@ -513,7 +528,7 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
   // fragment (hilo, q, ks) of this lane
   auto frag = [&](const u32x4* base, int hl, int q, int ks) -> u32x4 {
     if constexpr (LDS_FRAG) {
-      return base[((hl * NQ + q) * NK + ks) * 64 + lane];
+      return base[((hl * QH + (q - q0)) * NK + ks) * 64 + lane];
     } else {
       // global: wave-uniform base and fragment offset in SGPRs, one lane offset
       // register for every fragment
@@ -589,13 +604,14 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
         valid[t] = nu[t] > 0.0;
         inv[t] = valid[t] ? (float)(1.0 / nu[t]) : 0.0f;
       }
-      unsigned pw[T][PP][WPL];
+      constexpr int WPLR = HALF ? 1 : WPL;  // plane words held per lane (a half holds word hq)
+      unsigned pw[T][PP][WPLR];
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
         for (int p = 0; p < PP; ++p)
 #pragma unroll
-          for (int w = 0; w < WPL; ++w) pw[t][p][w] = 0u;
+          for (int w = 0; w < WPLR; ++w) pw[t][p][w] = 0u;
       // prod: residual operands for the second contraction, K order = this lane's coords
       u32x4 eh[PROD ? T : 1][PROD ? NK : 1], el[PROD ? T : 1][PROD ? NK : 1];
       float eodd[PROD ? T : 1][4];
@@ -604,7 +620,8 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
       for (int t = 0; t < T; ++t) esq[t] = 0.0f;
 
 #pragma unroll
-      for (int q = NQ - 1; q >= 0; --q) {
+      for (int qq = QH - 1; qq >= 0; --qq) {
+        const int q = q0 + qq;
         f32x4 C[T];
 #pragma unroll
         for (int t = 0; t < T; ++t) C[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -634,7 +651,7 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
             for (int p = 0; p < P; ++p)
 #pragma unroll
               for (int i = 3; i >= 0; --i) {
-                unsigned& w = pw[t][p][(4 * q + i) / 32];
+                unsigned& w = pw[t][p][HALF ? 0 : (4 * qq + i) / 32];
                 w = shift_in(w, pm[i].m[p]);
               }
           }
@@ -673,7 +690,7 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
       for (int t = 0; t < T; ++t) {
         const int rel = 16 * t + r16;
         if (v0 + rel < n) {
-          if (g == 0) nbase[rel] = (float)nu[t];
+          if (g == 0 && hq == 0) nbase[rel] = (float)nu[t];
           if constexpr (FUSED) {
             if (g == G0) sx.norms1[gbase + v0 + rel] = (float)nu[t];
           }
@@ -687,8 +704,8 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
               if (FUSED && p >= RP) continue;  // the part's top planes (all zero) are not stored
               if constexpr (Q4 >= 32) {
 #pragma unroll
-                for (int w = 0; w < WPL; ++w)
-                  *(unsigned*)(cbase + lo + p * RD / 8 + 4 * w) = valid[t] ? pw[t][p][w] : 0u;
+                for (int w = 0; w < WPLR; ++w)
+                  *(unsigned*)(cbase + lo + p * RD / 8 + 4 * (HALF ? hq : w)) = valid[t] ? pw[t][p][w] : 0u;
               } else {
                 *(unsigned short*)(cbase + lo + p * RD / 8) = (unsigned short)(valid[t] ? pw[t][p][0] : 0u);
               }
@@ -803,7 +820,7 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
           inv[t][k] = __shfl(inv_own, 4 * g + k);
           vmask[t] |= (inv[t][k] > 0.0f ? 1u : 0u) << k;
         }
-        if (g == 0 && v < n) prm.norms[gbase + v] = (float)nu_own;
+        if (g == 0 && hq == 0 && v < n) prm.norms[gbase + v] = (float)nu_own;
       }
       const int slot = r16 & 3;
       // this step's 32-vector block; 32-bit lane offset of word (p = 0, q = 0)
@@ -821,7 +838,8 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
       const unsigned blk_lane = (unsigned)((g * (RD / 4) + (D / 16) * ((r16 >> 2) - (part ? G0 : 0))) * 4);
       const bool bv = FUSED || !SPLIT || (r16 >> 2) < RD / Q4;
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
+      for (int qq = 0; qq < QH; ++qq) {
+        const int q = q0 + qq;
         f32x4 C[T];
 #pragma unroll
         for (int t = 0; t < T; ++t) C[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -920,7 +938,9 @@ tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream) {
     const bool dbg = a.rot_dbg != nullptr || a.proj_dbg != nullptr;
     tq_status st = dispatch_dim(q0->d, [&](auto DC) -> tq_status {
       constexpr int D = decltype(DC)::value;
-      const size_t lds = D <= 128 ? (size_t)2 * D * D * 2 * (prod ? 2 : 1) : 0;
+      // fragments in LDS: d <= 128 both matrices; d = 256 mse half of Pi per workgroup
+      const bool half = D == 256 && !prod;
+      const size_t lds = D <= 128 ? (size_t)2 * D * D * 2 * (prod ? 2 : 1) : half ? (size_t)D * D * 2 : 0;
       return dispatch_planes(P, [&](auto PC) -> tq_status {
         constexpr int PP = decltype(PC)::value;
         return dispatch_bool(prod, [&](auto PR) -> tq_status {
@@ -945,11 +965,12 @@ tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream) {
                   const int by_lds = lds ? (int)((160 * 1024) / lds) : by_waves;
                   const int per_cu = by_waves < by_lds ? by_waves : by_lds;
                   const int64_t steps = (a.n_per_group + 16 * T - 1) / (16 * T);
-                  int64_t want = ((int64_t)(per_cu > 0 ? per_cu : 1) * device_cus() + ng - 1) / ng;
+                  const int sets = half ? 2 * ng : ng;  // workgroup sets: (group, half of the rows) at d = 256 mse
+                  int64_t want = ((int64_t)(per_cu > 0 ? per_cu : 1) * device_cus() + sets - 1) / sets;
                   const int64_t cap = (steps + kQWaves - 1) / kQWaves;
                   if (want > cap) want = cap;
                   if (want < 1) want = 1;
-                  hipLaunchKernelGGL(kern, dim3((unsigned)want, (unsigned)ng), dim3(kQThreads), lds, stream, prm,
+                  hipLaunchKernelGGL(kern, dim3((unsigned)want, (unsigned)sets), dim3(kQThreads), lds, stream, prm,
                                      QuantNoSplit{});
                   return launch_check("quantize: launch");
                 });
