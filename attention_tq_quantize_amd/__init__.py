@@ -25,7 +25,7 @@ TQ_LAYOUT_VECTOR, TQ_LAYOUT_BLOCK32 = 0, 1
 EXPORTS = [
     "tq_status_string", "tq_last_error_message", "tq_version", "tq_codebook_build",
     "tq_quantizer_create", "tq_quantizer_create_wht", "tq_quantizer_destroy", "tq_quantizer_info",
-    "tq_quantizer_sizes", "tq_quantize",
+    "tq_quantizer_sizes", "tq_quantize", "tq_quantize_kv",
     "tq_quantize_mse", "tq_quantize_prod", "tq_dequantize", "tq_inner_products",
     "tq_decode_workspace_size", "tq_decode_attention", "tq_decode_append_workspace_size",
     "tq_decode_append_attention", "tq_search_workspace_size", "tq_search_scores", "tq_quantize_split",
@@ -89,6 +89,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tq_quantizer_destroy.argtypes = [_VP]
     lib.tq_quantizer_info.argtypes = [_VP, _VP, _VP, _VP, _VP]
     lib.tq_quantize.argtypes = [_VP, _I, _I64, _VP, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
+    lib.tq_quantize_kv.argtypes = [_VP, _VP, _I, _I64, _VP, _VP, _I, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
     lib.tq_quantize_mse.argtypes = [_VP, _VP, _I, _I64, _I64, _VP, _VP, _VP, _VP]
     lib.tq_quantize_prod.argtypes = [_VP, _VP, _I, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
     lib.tq_quantizer_sizes.argtypes = [_VP, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
@@ -317,6 +318,38 @@ def quantize(qs: Sequence[Quantizer], x, layout: str = "vector", rot_dbg: bool =
                            _ptr(o["norms"]), _ptr(o.get("rnorms")), _ptr(o.get("rot")), _ptr(o.get("proj")),
                            _stream(stream)), "tq_quantize")
     return o
+
+
+def quantize_kv(kqs: Sequence[Quantizer], vqs: Sequence[Quantizer], xk, xv, kout: Optional[dict] = None,
+                vout: Optional[dict] = None, stream=None):
+    """A layer's keys (qs kqs, VECTOR layout) and values (vqs, mse, BLOCK32 layout) in one call:
+    xk, xv are [G, n, d] (the same float dtype); returns (key records, value records)."""
+    lib = load()
+    G = len(kqs)
+    if len(vqs) != G:
+        raise ValueError("kqs and vqs must have one quantizer per group each")
+    dt = _float_dtype(xk, "xk")
+    if _float_dtype(xv, "xv") != dt:
+        raise TypeError("xk and xv must have the same dtype")
+    for x, q0, name in ((xk, kqs[0], "xk"), (xv, vqs[0], "xv")):
+        if not (x.dim() == 3 and x.shape[0] == G and x.shape[2] == q0.d):
+            raise ValueError(f"{name} must be [n_groups, n, d]")
+        _need_cuda(x, name)
+    if xk.shape[1] != xv.shape[1]:
+        raise ValueError("xk and xv must hold the same number of vectors per group")
+    with _on(stream):
+        xk = xk.contiguous()
+        xv = xv.contiguous()
+    n = xk.shape[1]
+    ko = kout if kout is not None else {}
+    vo = vout if vout is not None else {}
+    with _on(stream):
+        _alloc_quantize_out(ko, kqs[0], G, n, xk.device, False, False)
+        _alloc_quantize_out(vo, vqs[0], G, n, xv.device, False, False)
+    _check(lib.tq_quantize_kv(_handles(kqs), _handles(vqs), G, n, _ptr(xk), _ptr(xv), dt, _ptr(ko.get("codes")),
+                              _ptr(ko.get("signs")), _ptr(ko["norms"]), _ptr(ko.get("rnorms")), _ptr(vo.get("codes")),
+                              _ptr(vo["norms"]), _stream(stream)), "tq_quantize_kv")
+    return ko, vo
 
 
 def _rows(x):

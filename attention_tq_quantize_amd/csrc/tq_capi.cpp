@@ -327,10 +327,12 @@ tq_status tq_quantizer_info(const tq_quantizer* q, int* d, int* bits, tq_variant
   return TQ_OK;
 }
 
-static tq_status quantize_impl(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group,
-                               const void* x, int64_t x_stride, tq_dtype x_dtype, tq_layout layout,
-                               uint8_t* codes, uint8_t* signs, float* norms, float* rnorms, float* rot_dbg,
-                               float* proj_dbg, void* stream) {
+// Argument checks of a quantize call; on TQ_OK *a describes the launch
+// (n_per_group == 0 passes with nothing to launch).
+static tq_status quantize_check(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group,
+                                const void* x, int64_t x_stride, tq_dtype x_dtype, tq_layout layout,
+                                uint8_t* codes, uint8_t* signs, float* norms, float* rnorms, float* rot_dbg,
+                                float* proj_dbg, QuantizeLaunch* a) {
   if (!qz) return set_error(TQ_ERR_INVALID_ARG, "quantize: qz is NULL");
   if (n_groups < 1) return set_error(TQ_ERR_INVALID_ARG, fmt("quantize: n_groups=%d < 1", n_groups));
   if (n_per_group < 0) return set_error(TQ_ERR_INVALID_ARG, "quantize: n_per_group < 0");
@@ -351,7 +353,10 @@ static tq_status quantize_impl(const tq_quantizer* const* qz, int n_groups, int6
     if (n_per_group % kBlock) return set_error(TQ_ERR_INVALID_ARG, "quantize: BLOCK32 needs n_per_group % 32 == 0");
   }
   const bool prod = q0->variant == TQ_PROD;
-  if (n_per_group == 0) return TQ_OK;
+  if (n_per_group == 0) {
+    *a = QuantizeLaunch{qz, n_groups, 0, x, x_stride, x_dtype, layout, codes, signs, norms, rnorms, rot_dbg, proj_dbg};
+    return TQ_OK;
+  }
   if (!x) return set_error(TQ_ERR_INVALID_ARG, "quantize: x is NULL");
   if (q0->planes > 0 && !codes) return set_error(TQ_ERR_INVALID_ARG, "quantize: codes is NULL");
   if (!norms) return set_error(TQ_ERR_INVALID_ARG, "quantize: norms is NULL");
@@ -362,9 +367,45 @@ static tq_status quantize_impl(const tq_quantizer* const* qz, int n_groups, int6
   if (misaligned(x, 16) || misaligned(codes, 4) || misaligned(signs, 4) || misaligned(rot_dbg, 16) ||
       misaligned(proj_dbg, 16))
     return set_error(TQ_ERR_INVALID_ARG, "quantize: x, rot_dbg and proj_dbg must be 16-byte aligned, codes and signs 4-byte aligned");
-  QuantizeLaunch a{qz, n_groups, n_per_group, x, x_stride, x_dtype, layout, codes, signs, norms, rnorms, rot_dbg, proj_dbg};
-  if (large_dim(q0->d)) return launch_quantize_large(a, (hipStream_t)stream);
+  *a = QuantizeLaunch{qz, n_groups, n_per_group, x, x_stride, x_dtype, layout, codes, signs, norms, rnorms, rot_dbg, proj_dbg};
+  return TQ_OK;
+}
+
+static tq_status quantize_run(const QuantizeLaunch& a, void* stream) {
+  if (a.n_per_group == 0) return TQ_OK;
+  if (large_dim(a.qz[0]->d)) return launch_quantize_large(a, (hipStream_t)stream);
   return launch_quantize(a, (hipStream_t)stream);
+}
+
+static tq_status quantize_impl(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group,
+                               const void* x, int64_t x_stride, tq_dtype x_dtype, tq_layout layout,
+                               uint8_t* codes, uint8_t* signs, float* norms, float* rnorms, float* rot_dbg,
+                               float* proj_dbg, void* stream) {
+  QuantizeLaunch a{};
+  tq_status st = quantize_check(qz, n_groups, n_per_group, x, x_stride, x_dtype, layout, codes, signs, norms, rnorms,
+                                rot_dbg, proj_dbg, &a);
+  if (st != TQ_OK) return st;
+  return quantize_run(a, stream);
+}
+
+tq_status tq_quantize_kv(const tq_quantizer* const* kqz, const tq_quantizer* const* vqz, int n_groups,
+                         int64_t n_per_group, const void* xk, const void* xv, tq_dtype x_dtype, uint8_t* kcodes,
+                         uint8_t* ksigns, float* knorms, float* krnorms, uint8_t* vcodes, float* vnorms,
+                         void* stream) {
+  if (!kqz || !kqz[0] || !vqz || !vqz[0]) return set_error(TQ_ERR_INVALID_ARG, "quantize_kv: kqz or vqz is NULL");
+  if (vqz[0]->variant != TQ_MSE) return set_error(TQ_ERR_INVALID_ARG, "quantize_kv: value quantizers must be TQ_MSE");
+  QuantizeLaunch k{}, v{};
+  tq_status st = quantize_check(kqz, n_groups, n_per_group, xk, kqz[0]->d, x_dtype, TQ_LAYOUT_VECTOR, kcodes, ksigns,
+                                knorms, krnorms, nullptr, nullptr, &k);
+  if (st != TQ_OK) return st;
+  st = quantize_check(vqz, n_groups, n_per_group, xv, vqz[0]->d, x_dtype, TQ_LAYOUT_BLOCK32, vcodes, nullptr, vnorms,
+                      nullptr, nullptr, nullptr, &v);
+  if (st != TQ_OK) return st;
+  if (n_per_group == 0) return TQ_OK;
+  if (quantize_kv_fusable(k, v)) return launch_quantize_kv(k, v, (hipStream_t)stream);
+  st = quantize_run(k, stream);
+  if (st != TQ_OK) return st;
+  return quantize_run(v, stream);
 }
 
 tq_status tq_quantize(const tq_quantizer* const* qz, int n_groups, int64_t n_per_group,

@@ -81,6 +81,10 @@ struct QuantizeLaunch {
   float* proj_dbg;
 };
 tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream);
+// keys (VECTOR) and values (BLOCK32) of one layer in one launch, when both are
+// mse with the same (d <= 256, bits), dtype and groups, packed rows, no debug outputs
+bool quantize_kv_fusable(const QuantizeLaunch& k, const QuantizeLaunch& v);
+tq_status launch_quantize_kv(const QuantizeLaunch& k, const QuantizeLaunch& v, hipStream_t stream);
 // d > 256 (tq_large.hip): vector layout only
 tq_status launch_quantize_large(const QuantizeLaunch& a, hipStream_t stream);
 // fp32 kernels for any d (multiple of 32): optional channel map (quantized

@@ -24,6 +24,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 #include <type_traits>
 
 #include "tq_device.h"
@@ -55,6 +56,7 @@ struct QuantParams {
   float* proj_dbg;
   float thr[15];
   float cen[16];
+  unsigned thr_key[8];  // magnitude-search keys of the upper thresholds (P >= 3)
   const uint16_t* pi_frag[kMaxGroupsPerLaunch];
   const uint16_t* sp_frag[kMaxGroupsPerLaunch];
 };
@@ -338,6 +340,68 @@ __device__ __forceinline__ void nearest_planes(const float* y, const float* T, P
     for (int i = 0; i < N; ++i) r[i].m[0] = cmp_gt(y[i], sel(r[i].m[2], a[i], b[i]));
   }
 }
+// Nearest centroid of a symmetric codebook (C[K-1-i] = -C[i], so the middle
+// threshold is 0) from the magnitude, for P >= 3. With neg = [y <= 0] and
+// key = 2 bits(|y|) + neg (bits(y) + bits(y) + carry: the add drops the sign
+// bit), one unsigned compare key > TK[j] against
+//   TK[j] = 2 bits(t_u) + (1 if the midpoint behind t_u is not a float32)
+// for the upper thresholds t_u (u = K/2 + j) decides both sides: y > 0 is past
+// the midpoint when |y| > t_u; y <= 0 is below its mirror when |y| >= the
+// midpoint (the tie goes to the lower index, which on the negative side is the
+// one farther from zero), i.e. |y| > t_u unless the midpoint is a float32 and
+// equals t_u. J = the number of upper midpoints passed is found by a binary
+// search over TK; then idx = neg ? K/2 - 1 - J : K/2 + J, so the top plane is
+// !neg and the lower planes are J's bits flipped when neg (mask XORs on the
+// scalar unit). Per value 2 + (P - 1) compares, 2^(P-2) - 1 selects and the
+// key add, against P compares and 2^(P-1) - 1 selects of the plain search.
+__device__ __forceinline__ lanemask cmp_le0(float a) {  // lanes with a <= 0
+  lanemask m;
+  asm("v_cmp_ge_f32_e64 %0, 0, %1" : "=s"(m) : "v"(a));
+  return m;
+}
+__device__ __forceinline__ lanemask cmp_gt_u(unsigned a, unsigned b) {  // lanes with a > b (unsigned)
+  lanemask m;
+  asm("v_cmp_gt_u32_e64 %0, %1, %2" : "=s"(m) : "v"(a), "v"(b));
+  return m;
+}
+__device__ __forceinline__ unsigned sel_u(lanemask m, unsigned a, unsigned b) {  // lane-wise m ? b : a
+  unsigned r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(m));
+  return r;
+}
+template <int P, int N>
+__device__ __forceinline__ void nearest_planes_sym(const float* y, const unsigned* TK, PlaneMasks<P>* r) {
+  static_assert(P == 3 || P == 4, "magnitude search: 3 or 4 planes");
+  lanemask neg[N];
+  unsigned key[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) neg[i] = cmp_le0(y[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) key[i] = shift_in(__float_as_uint(y[i]), neg[i]);
+  if constexpr (P == 3) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) r[i].m[1] = cmp_gt_u(key[i], TK[1]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) r[i].m[0] = cmp_gt_u(key[i], sel_u(r[i].m[1], TK[0], TK[2]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) r[i].m[2] = cmp_gt_u(key[i], TK[3]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) r[i].m[1] = cmp_gt_u(key[i], sel_u(r[i].m[2], TK[1], TK[5]));
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const unsigned a = sel_u(r[i].m[2], TK[0], TK[4]), b = sel_u(r[i].m[2], TK[2], TK[6]);
+      r[i].m[0] = cmp_gt_u(key[i], sel_u(r[i].m[1], a, b));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+#pragma unroll
+    for (int p = 0; p < P - 1; ++p) r[i].m[p] ^= neg[i];
+    r[i].m[P - 1] = ~neg[i];
+  }
+}
+
 // centroid C[idx] of the index whose plane masks are r
 template <int P>
 __device__ __forceinline__ float plane_centroid(const PlaneMasks<P>& r, const float* C) {
@@ -365,9 +429,13 @@ __device__ __forceinline__ unsigned quad_or(unsigned w) {
 }
 
 // SPLIT: 0 whole vectors, 1 one part of a channel split, 2 the fused two-part split
+// The work of one workgroup: by is its row of the grid (the group, and at
+// d = 256 mse the half of the rotation's output rows), blockIdx.x / gridDim.x
+// its place among the persistent workgroups of that row.
 template <int D, int P, bool PROD, bool XF32, bool BLK, bool DBG, int SPLIT = 0>
-__global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT == 2)) void quantize_kernel(
-    QuantParams prm, std::conditional_t<SPLIT != 0, QuantSplitParams, QuantNoSplit> sx) {
+__device__ __forceinline__ void quantize_body(const QuantParams& prm,
+                                              const std::conditional_t<SPLIT != 0, QuantSplitParams, QuantNoSplit>& sx,
+                                              const int by) {
   static_assert(!SPLIT || D == 128, "split parts: d = 128 heads");
   constexpr bool FUSED = SPLIT == 2;
   constexpr int NQ = D / 16, NK = D / 32, Q4 = D / 4;
@@ -388,8 +456,8 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const int grp = HALF ? (int)(blockIdx.y >> 1) : (int)blockIdx.y;
-  const int hq = HALF ? (int)(blockIdx.y & 1) : 0;  // this workgroup's half of the output rows
+  const int grp = HALF ? (by >> 1) : by;
+  const int hq = HALF ? (by & 1) : 0;  // this workgroup's half of the output rows
   const int q0 = hq * QH;
   // record width (d_p of a split part), whether this lane group holds record
   // coordinates, and its channel mask. Fused split: this lane's part (by lane
@@ -429,6 +497,12 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
   constexpr int NTHR = P > 0 ? (1 << P) - 1 : 1;
   constexpr int NCEN = 1 << (P > 0 ? P : 0);
   float thr[NTHR], cen[NCEN];
+  // the magnitude search (whole vectors, 3 or 4 planes)
+  constexpr bool SYM = SPLIT == 0 && P >= 3;
+  constexpr int NTK = SYM ? (1 << (P - 1)) - 1 : 1;
+  unsigned tkey[NTK];
+#pragma unroll
+  for (int i = 0; i < NTK; ++i) tkey[i] = SYM ? __float_as_uint(opaque_vgpr(__uint_as_float(prm.thr_key[i]))) : 0u;
 #pragma unroll
   for (int i = 0; i < NTHR; ++i) {
     if constexpr (FUSED)
@@ -646,7 +720,10 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
           float e4[4];
           PlaneMasks<P> pm[4];
           if constexpr (P > 0) {
-            nearest_planes<P, 4>(y, thr, pm);
+            if constexpr (SYM)
+              nearest_planes_sym<P, 4>(y, tkey, pm);
+            else
+              nearest_planes<P, 4>(y, thr, pm);
 #pragma unroll
             for (int p = 0; p < P; ++p)
 #pragma unroll
@@ -861,7 +938,10 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
           for (int p = 0; p < PP; ++p) nib[t][p] = 0u;
           const float y[4] = {cv[0] * inv[t][0], cv[1] * inv[t][1], cv[2] * inv[t][2], cv[3] * inv[t][3]};
           PlaneMasks<P> pm[4];
-          nearest_planes<P, 4>(y, thr, pm);
+          if constexpr (SYM)
+            nearest_planes_sym<P, 4>(y, tkey, pm);
+          else
+            nearest_planes<P, 4>(y, thr, pm);
 #pragma unroll
           for (int p = 0; p < P; ++p)
 #pragma unroll
@@ -906,6 +986,46 @@ __global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT ==
   }
 }
 
+template <int D, int P, bool PROD, bool XF32, bool BLK, bool DBG, int SPLIT = 0>
+__global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, PROD, XF32, SPLIT == 2)) void quantize_kernel(
+    QuantParams prm, std::conditional_t<SPLIT != 0, QuantSplitParams, QuantNoSplit> sx) {
+  quantize_body<D, P, PROD, XF32, BLK, DBG, SPLIT>(prm, sx, (int)blockIdx.y);
+}
+
+// A layer's keys (VECTOR layout) and values (BLOCK32 layout) in one launch,
+// both TurboQuant_mse with the same (d, bits): grid rows [0, rows_k) run the
+// keys, the rest the values, so the two tensors share one launch's set-up and
+// tail instead of paying each twice.
+template <int D, int P, bool XF32>
+__global__ __launch_bounds__(kQThreads, q_waves_per_simd(D, false, XF32)) void quantize_kv_kernel(
+    QuantParams pk, QuantParams pv, int rows_k) {
+  if ((int)blockIdx.y < rows_k)
+    quantize_body<D, P, false, XF32, false, false>(pk, QuantNoSplit{}, (int)blockIdx.y);
+  else
+    quantize_body<D, P, false, XF32, true, false>(pv, QuantNoSplit{}, (int)blockIdx.y - rows_k);
+}
+
+// Keys of the magnitude search (nearest_planes_sym) for a codebook of P >= 3
+// planes: TK[j] = 2 bits(t_u) + (1 unless the midpoint of centroids u and u+1
+// is a float32), u = K/2 + j. The codebook is symmetric by construction
+// (centroids rounded from a symmetric fp64 solution, middle midpoint 0); a
+// codebook that is not is refused.
+bool threshold_keys(const Codebook& cb, unsigned* tk) {
+  const int K = 1 << cb.planes;
+  if (cb.planes < 3) return true;
+  for (int i = 0; i < K; ++i)
+    if (cb.centroids[K - 1 - i] != -cb.centroids[i]) return false;
+  if (cb.thresholds[K / 2 - 1] != 0.0f) return false;
+  for (int j = 0; j < K / 2 - 1; ++j) {
+    const int u = K / 2 + j;
+    const double mid = ((double)cb.centroids[u] + (double)cb.centroids[u + 1]) / 2.0;  // exact in fp64
+    unsigned b;
+    std::memcpy(&b, &cb.thresholds[u], 4);
+    tk[j] = 2u * b + ((double)(float)mid == mid ? 0u : 1u);
+  }
+  return true;
+}
+
 }  // namespace
 
 tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream) {
@@ -931,6 +1051,7 @@ tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream) {
     const int K = 1 << P;
     for (int i = 0; i + 1 < K; ++i) prm.thr[i] = q0->cb.thresholds[i];
     for (int i = 0; i < K; ++i) prm.cen[i] = q0->cb.centroids[i];
+    if (!threshold_keys(q0->cb, prm.thr_key)) return set_error(TQ_ERR_UNSUPPORTED, "quantize: codebook is not symmetric");
     for (int g = 0; g < ng; ++g) {
       prm.pi_frag[g] = a.qz[g0 + g]->pi_frag;
       prm.sp_frag[g] = a.qz[g0 + g]->sp_frag;
@@ -983,6 +1104,75 @@ tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream) {
     if (st != TQ_OK) return st;
   }
   return TQ_OK;
+}
+
+bool quantize_kv_fusable(const QuantizeLaunch& k, const QuantizeLaunch& v) {
+  const tq_quantizer* a = k.qz[0];
+  const tq_quantizer* b = v.qz[0];
+  return a->variant == TQ_MSE && b->variant == TQ_MSE && a->d == b->d && a->bits == b->bits && a->d <= 256 &&
+         k.layout == TQ_LAYOUT_VECTOR && v.layout == TQ_LAYOUT_BLOCK32 && k.x_dtype == v.x_dtype &&
+         k.x_stride == a->d && v.x_stride == b->d && k.n_groups == v.n_groups && k.n_groups <= kMaxGroupsPerLaunch &&
+         !k.rot_dbg && !v.rot_dbg && !k.proj_dbg && !v.proj_dbg;
+}
+
+tq_status launch_quantize_kv(const QuantizeLaunch& k, const QuantizeLaunch& v, hipStream_t stream) {
+  const bool xf32 = k.x_dtype == TQ_F32;
+  const int P = k.qz[0]->planes;
+  const int ng = k.n_groups;
+  auto params = [&](const QuantizeLaunch& a) {
+    QuantParams prm{};
+    prm.x = a.x;
+    prm.x_row_bytes = a.x_stride * (xf32 ? 4 : 2);
+    prm.n_per_group = a.n_per_group;
+    prm.n_groups = ng;
+    prm.group_base = 0;
+    prm.codes = a.codes;
+    prm.norms = a.norms;
+    const tq_quantizer* q0 = a.qz[0];
+    for (int i = 0; i + 1 < (1 << P); ++i) prm.thr[i] = q0->cb.thresholds[i];
+    for (int i = 0; i < (1 << P); ++i) prm.cen[i] = q0->cb.centroids[i];
+    for (int g = 0; g < ng; ++g) prm.pi_frag[g] = a.qz[g]->pi_frag;
+    return prm;
+  };
+  QuantParams pk = params(k), pv = params(v);
+  if (!threshold_keys(k.qz[0]->cb, pk.thr_key) || !threshold_keys(v.qz[0]->cb, pv.thr_key))
+    return set_error(TQ_ERR_UNSUPPORTED, "quantize_kv: codebook is not symmetric");
+  return dispatch_dim(k.qz[0]->d, [&](auto DC) -> tq_status {
+    constexpr int D = decltype(DC)::value;
+    constexpr bool HALF = D == 256;  // d = 256 mse: two workgroup rows per group, each half of Pi in LDS
+    const size_t lds = D <= 128 ? (size_t)2 * D * D * 2 : (size_t)D * D * 2;
+    return dispatch_planes(P, [&](auto PC) -> tq_status {
+      constexpr int PP = decltype(PC)::value;
+      if constexpr (PP == 0) {
+        return set_error(TQ_ERR_UNSUPPORTED, "quantize_kv: mse needs code planes");
+      } else {
+        return dispatch_bool(xf32, [&](auto XF) -> tq_status {
+          constexpr bool XF32 = decltype(XF)::value;
+          auto kern = quantize_kv_kernel<D, PP, XF32>;
+          if (lds > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return check_hip(e, "quantize_kv: set LDS size");
+          }
+          // persistent workgroups: as many as fit on the device at once, split over
+          // the grid rows (each row walks the steps of one group, or half of one)
+          constexpr int T = q_tiles(D, false, XF32, false);
+          const int by_waves = q_waves_per_simd(D, false, XF32) * 4 / kQWaves;
+          const int by_lds = (int)((160 * 1024) / lds);
+          const int per_cu = by_waves < by_lds ? by_waves : by_lds;
+          const int rows_k = HALF ? 2 * ng : ng;
+          const int rows = 2 * rows_k;
+          const int64_t n_max = k.n_per_group > v.n_per_group ? k.n_per_group : v.n_per_group;
+          const int64_t steps = (n_max + 16 * T - 1) / (16 * T);
+          int64_t want = ((int64_t)(per_cu > 0 ? per_cu : 1) * device_cus() + rows - 1) / rows;
+          const int64_t cap = (steps + kQWaves - 1) / kQWaves;
+          if (want > cap) want = cap;
+          if (want < 1) want = 1;
+          hipLaunchKernelGGL(kern, dim3((unsigned)want, (unsigned)rows), dim3(kQThreads), lds, stream, pk, pv, rows_k);
+          return launch_check("quantize_kv: launch");
+        });
+      }
+    });
+  });
 }
 
 // In-place VECTOR -> BLOCK32 repack of the codes of 32-vector blocks (one

@@ -4,7 +4,7 @@
 One step = one pass over every stage of the path on synthetic inputs:
   1. quantize one layer's KV: 8 KV heads x 32768 tokens, head_dim 128, bf16,
      TurboQuant_mse b=3 (keys -> vector layout, values -> 32-vector block
-     layout), 524,288 vectors;
+     layout), 524,288 vectors, in one tq_quantize_kv call (one launch);
   2. decode attention over a resident packed cache: batch 8, 64 query / 8 KV
      heads, head_dim 128, context 131072, keys TurboQuant_prod b=3, values
      TurboQuant_mse b=3, one query token per sequence.
@@ -167,7 +167,8 @@ def c4_sweep(tq, syn, torch, dev, flush, reps=20):
     """Bit-width and head-dim sweep: b in {1, 2, 4} x {mse, prod} keys (values mse b)
     x d in {64, 256}; B = 4, 64 query / 8 KV heads, 16384 tokens per sequence, bf16
     KV with the headline's outlier channels and per-token LogNormal(0, 0.5) scale.
-    Per row: layer quantize of keys and values (two launches, 2 x 524,288 vectors)
+    Per row: layer quantize of keys and values (one tq_quantize_kv call, 2 x 524,288
+    vectors: one launch for mse keys, two for prod keys)
     and decode attention over the packed caches, each timed after a 512 MB cache
     flush, median of reps calls; quantize MFMA use as executed bf16 MFMA FLOPs over
     the 2.5 PFLOP/s dense peak."""
@@ -203,8 +204,7 @@ def c4_sweep(tq, syn, torch, dev, flush, reps=20):
                 vq_g = [vq[g % Hkv] for g in range(G)]
 
                 def quant():
-                    tq.quantize(kq_g, xk, layout="vector", out=kout)
-                    tq.quantize(vq_g, xv, layout="block32", out=vout)
+                    tq.quantize_kv(kq_g, vq_g, xk, xv, kout=kout, vout=vout)
                 quant()
                 torch.cuda.synchronize()
                 kcache = tq.KVCache(kq, knorms, kcodes, ksigns, krn)
@@ -534,8 +534,7 @@ def main():
     w = build_workloads(tq, syn, torch, dev)
 
     def quantize_layer():
-        tq.quantize(w["qk2"], w["xk2"], layout="vector", out=w["out_k2"])
-        tq.quantize(w["qv2"], w["xv2"], layout="block32", out=w["out_v2"])
+        tq.quantize_kv(w["qk2"], w["qv2"], w["xk2"], w["xv2"], kout=w["out_k2"], vout=w["out_v2"])
 
     def decode():
         tq.decode_attention(w["q"], w["kcache"], w["vcache"], w["lens"], 1 / math.sqrt(w["d"]), max_ctx=w["T3"],

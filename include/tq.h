@@ -173,6 +173,29 @@ tq_status tq_quantize(const tq_quantizer* const* qz, int n_groups, int64_t n_per
                       uint8_t* signs, float* norms, float* rnorms, float* rot_dbg,
                       float* proj_dbg, void* stream);
 
+/*
+ * One layer's new keys and values in one call: the online quantization of
+ * [NIK] "Step 0" to "Step 2" applied to both tensors of a layer, keys with
+ * kqz[g] (TurboQuant_mse or TurboQuant_prod) into the VECTOR layout, values
+ * with vqz[g] (TurboQuant_mse) into the BLOCK32 layout, as the decode cache
+ * keeps them.
+ *   kqz, vqz    : host arrays [n_groups] of handles (each array one (d, bits,
+ *                 variant), as for tq_quantize).
+ *   xk, xv      : device [n_groups*n_per_group][d] each, x_dtype for both.
+ *   kcodes, ksigns, knorms, krnorms : key records as tq_quantize writes them
+ *                 (ksigns / krnorms NULL for mse keys).
+ *   vcodes, vnorms : value records, BLOCK32 codes; n_per_group % 32 == 0.
+ * When keys and values are both TurboQuant_mse with the same (d <= 256, bits),
+ * the two tensors run in one launch; otherwise the call makes the two
+ * launches that tq_quantize would. Records are identical to those of two
+ * tq_quantize calls. Errors as for tq_quantize, checked for both tensors
+ * before anything is launched.
+ */
+tq_status tq_quantize_kv(const tq_quantizer* const* kqz, const tq_quantizer* const* vqz, int n_groups,
+                         int64_t n_per_group, const void* xk, const void* xv, tq_dtype x_dtype,
+                         uint8_t* kcodes, uint8_t* ksigns, float* knorms, float* krnorms,
+                         uint8_t* vcodes, float* vnorms, void* stream);
+
 /* Q_mse for n vectors with one quantizer, VECTOR layout ([NIK] Theorem 1's map
  * Q_mse : R^d -> {0,1}^(b d)). Same argument meanings as tq_quantize, except:
  *   x_stride : elements from one input vector to the next (>= d; x_stride

@@ -176,3 +176,46 @@ def test_split_decode_argument_errors(lib):
                                                   ctypes.byref(nb)) == err, (shape.n_q_heads, shape.n_kv_heads)
         assert lib.tq_decode_attention_split(ctypes.byref(shape), None, ctypes.byref(empty), ctypes.byref(empty),
                                              None, ctypes.c_float(1.0), None, None, 0, None) == err
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bits", [3, 4])
+def test_magnitude_search_rule(lib, d, bits):
+    # The quantize kernels find the nearest centroid of 3- and 4-plane codebooks
+    # from the magnitude (the codebook is symmetric, its middle threshold 0):
+    # key(y) = 2 bits(|y|) + [y <= 0] as uint32 against TK_j = 2 bits(t_u) + [the
+    # midpoint of centroids u, u + 1 is not a float32] for the upper thresholds
+    # u = K/2 + j; with J the number of keys passed, idx = K/2 - 1 - J for y <= 0
+    # and K/2 + J otherwise. That rule must be the argmin with ties low for every
+    # float32, in particular on and next to each threshold, on both sides, and on
+    # midpoints that are float32 (d = 128, b = 3 has one).
+    c, t, _ = tq.codebook_build(d, bits)
+    K = 1 << bits
+    assert np.array_equal(c[::-1], -c) and t[K // 2 - 1] == 0.0
+    up = np.arange(K // 2, K - 1)
+    mids = (c[up].astype(np.float64) + c[up + 1].astype(np.float64)) / 2
+    exact = mids.astype(np.float32).astype(np.float64) == mids
+    tk = 2 * t[up].view(np.uint32).astype(np.uint64) + (~exact).astype(np.uint64)
+    near = [t, mids.astype(np.float32)]
+    above, below = t.copy(), t.copy()
+    for _ in range(3):  # one to three float32 steps either side of every threshold
+        above = np.nextafter(above, np.float32(np.inf))
+        below = np.nextafter(below, np.float32(-np.inf))
+        near += [above, below]
+    g = np.random.Generator(np.random.PCG64(3))
+    y = np.concatenate(near + [(g.standard_normal(100000) / math.sqrt(d)).astype(np.float32),
+                               np.array([0.0, -0.0, 1e-30, -1e-30, 2.0, -2.0], np.float32)])
+    y = np.concatenate([y, -y]).astype(np.float32)
+    neg = y <= 0
+    key = (2 * y.view(np.uint32).astype(np.uint64)) % (1 << 32) + neg
+    J = np.sum(key[:, None] > tk[None, :], axis=1)
+    idx = np.where(neg, K // 2 - 1 - J, K // 2 + J)
+    assert np.array_equal(idx, O.nearest_index(y.astype(np.float64), c.astype(np.float64)))
+
+
+def test_quantize_kv_argument_errors(lib):
+    arr = (ctypes.c_void_p * 1)(None)
+    assert lib.tq_quantize_kv(None, None, 1, 32, None, None, tq.TQ_BF16, None, None, None, None, None, None,
+                              None) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_quantize_kv(arr, arr, 1, 32, None, None, tq.TQ_BF16, None, None, None, None, None, None,
+                              None) == tq.TQ_ERR_INVALID_ARG

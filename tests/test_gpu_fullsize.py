@@ -36,13 +36,18 @@ def test_layer_quantize_full_size(gpu_lib):
     print(f"layer quantize H={H} T={T} d={D} mse b=3", flush=True)
     cb = O.codebook(D, 3)
     g = np.random.default_rng(20260401)
+    # the benchmark's call: keys and values of the layer in one tq_quantize_kv launch
+    qs_kv = {t: [tq.Quantizer(D, 3, "mse", syn.rotation(D, syn.CFG_LAYER_QUANT, t, h)) for h in range(H)]
+             for t in (syn.T_K, syn.T_V)}
+    xs_kv = {t: syn.kv_vectors_device(H, T, D, syn.CFG_LAYER_QUANT, t, DEV) for t in (syn.T_K, syn.T_V)}
+    outs = {t: {"codes": torch.empty((H, T * 48), dtype=torch.uint8, device=DEV),
+                "norms": torch.empty((H, T), dtype=torch.float32, device=DEV)} for t in (syn.T_K, syn.T_V)}
+    tq.quantize_kv(qs_kv[syn.T_K], qs_kv[syn.T_V], xs_kv[syn.T_K], xs_kv[syn.T_V], kout=outs[syn.T_K],
+                   vout=outs[syn.T_V])
+    torch.cuda.synchronize()
     for tensor, layout in ((syn.T_K, "vector"), (syn.T_V, "block32")):
-        qs = [tq.Quantizer(D, 3, "mse", syn.rotation(D, syn.CFG_LAYER_QUANT, tensor, h)) for h in range(H)]
-        x = syn.kv_vectors_device(H, T, D, syn.CFG_LAYER_QUANT, tensor, DEV)
-        out = {"codes": torch.empty((H, T * 48), dtype=torch.uint8, device=DEV),
-               "norms": torch.empty((H, T), dtype=torch.float32, device=DEV)}
-        tq.quantize(qs, x, layout=layout, out=out)
-        torch.cuda.synchronize()
+        x = xs_kv[tensor]
+        out = outs[tensor]
         codes = out["codes"].cpu().numpy()
         norms = out["norms"].cpu().numpy()
         n_flip = n_coord = 0
@@ -62,7 +67,7 @@ def test_layer_quantize_full_size(gpu_lib):
             n_flip += int(flips.sum())
             n_coord += flips.size
         assert n_flip / n_coord < MAX_FLIP_RATE, (tensor, n_flip, n_coord)
-        del x, out
+    del xs_kv, outs
 
 
 def _planes(bits, variant):
