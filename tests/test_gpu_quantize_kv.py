@@ -44,7 +44,8 @@ def _quantizers(tq, d, bits, variant, tensor, G):
 
 def _vectors(G, n, d, tensor, dtype):
     x = np.stack([syn.kv_vectors(n, d, syn.CFG_TEST, tensor, 0, 300 + h, lognormal_sigma=0.5) for h in range(G)])
-    x[0, 5] = 0.0  # a zero vector
+    if n > 5:
+        x[0, 5] = 0.0  # a zero vector
     t = torch.from_numpy(x).to(DEV)
     return (t.to(torch.bfloat16) if dtype == "bf16" else t), x
 
@@ -106,3 +107,44 @@ def test_quantize_kv_parity(gpu_lib, d, bits, kvar, dtype, G, n):
             n_coord += flips.size
         if n_coord:
             assert n_flip / n_coord < MAX_FLIP_RATE, (tensor, n_flip, n_coord)
+
+
+def _kv_pair(tq, G, n, d, kbits, vbits, dtype="bf16"):
+    kqs, _ = _quantizers(tq, d, kbits, "mse", syn.T_K, G)
+    vqs, _ = _quantizers(tq, d, vbits, "mse", syn.T_V, G)
+    xk, _ = _vectors(G, n, d, syn.T_K, dtype)
+    xv, _ = _vectors(G, n, d, syn.T_V, dtype)
+    return kqs, vqs, xk, xv
+
+
+@pytest.mark.parametrize("case", ["bits_differ", "many_groups"])
+def test_quantize_kv_two_launch_forms(gpu_lib, case):
+    # keys and values of different bit widths, and more groups than one launch
+    # takes (65), go through two tq_quantize launches: records as those calls write them
+    tq = gpu_lib
+    G, n, kb, vb = (3, 256, 3, 2) if case == "bits_differ" else (65, 64, 3, 3)
+    print(f"case quantize_kv {case} G={G} n={n} kbits={kb} vbits={vb}", flush=True)
+    kqs, vqs, xk, xv = _kv_pair(tq, G, n, 128, kb, vb)
+    ko, vo = tq.quantize_kv(kqs, vqs, xk, xv)
+    kr = tq.quantize(kqs, xk, layout="vector")
+    vr = tq.quantize(vqs, xv, layout="block32")
+    torch.cuda.synchronize()
+    for name in ko:
+        assert torch.equal(ko[name], kr[name]), ("keys", name)
+    for name in vo:
+        assert torch.equal(vo[name], vr[name]), ("values", name)
+
+
+def test_quantize_kv_empty_and_errors(gpu_lib):
+    tq = gpu_lib
+    kqs, vqs, xk, xv = _kv_pair(tq, 2, 0, 128, 3, 3)
+    ko, vo = tq.quantize_kv(kqs, vqs, xk, xv)  # no vectors: nothing to do, no error
+    torch.cuda.synchronize()
+    assert ko["norms"].numel() == 0 and vo["norms"].numel() == 0
+    kqs, vqs, xk, xv = _kv_pair(tq, 2, 64, 128, 3, 3)
+    pq = [tq.Quantizer(128, 3, "prod", syn.rotation(128, syn.CFG_TEST, syn.T_V, 9),
+                       syn.gaussian_matrix(128, syn.CFG_TEST, syn.T_V, 9)) for _ in range(2)]
+    with pytest.raises(tq.TQError):
+        tq.quantize_kv(kqs, pq, xk, xv)  # values must be mse (block layout)
+    with pytest.raises(tq.TQError):
+        tq.quantize_kv(kqs, vqs, xk[:, :48].contiguous(), xv[:, :48].contiguous())  # n % 32 != 0
