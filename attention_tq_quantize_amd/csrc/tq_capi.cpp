@@ -202,7 +202,13 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
   const size_t frag_bytes = large ? 0 : 2 * dd * sizeof(uint16_t);  // hi + lo
   const bool prod = variant == TQ_PROD;
   const bool fold = prod && d <= 256;
-  const size_t total = frag_bytes * (prod ? 2 : 1) + dd * sizeof(float) * (prod ? (fold ? 3 : 2) : 1);
+  // fp32 Pi is followed by its column sums (Pi^T 1, d floats); fp32 S by its
+  // column sums (S^T 1) and its largest row norm (rounded up), 4 floats: the
+  // decode query prep takes sum_j (Pi q)_j = (Pi^T 1) q, sum_j (S q)_j = (S^T 1) q,
+  // max_j |(Pi q)_j| <= |q| and max_j |(S q)_j| <= |q| max_i |S_i| from them
+  const size_t pi_tail = (size_t)d * sizeof(float), s_tail = ((size_t)d + 4) * sizeof(float);
+  const size_t total = frag_bytes * (prod ? 2 : 1) + dd * sizeof(float) * (prod ? (fold ? 3 : 2) : 1) + pi_tail +
+                       (prod ? s_tail : 0);
   std::vector<unsigned char> host(total);
   size_t off = 0;
   if (!large) build_fragments(d, pi, (uint16_t*)(host.data() + off));
@@ -229,11 +235,31 @@ tq_status tq_quantizer_create(int d, int bits, tq_variant variant, const double*
   const size_t off_pi32 = off;
   for (size_t i = 0; i < dd; ++i) ((float*)(host.data() + off))[i] = (float)pi[i];
   off += dd * sizeof(float);
+  for (int j = 0; j < d; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < d; ++i) acc += pi[(size_t)i * d + j];
+    ((float*)(host.data() + off))[j] = (float)acc;
+  }
+  off += pi_tail;
   size_t off_s32 = 0, off_sp32 = 0;
   if (prod) {
     off_s32 = off;
     for (size_t i = 0; i < dd; ++i) ((float*)(host.data() + off))[i] = (float)s[i];
     off += dd * sizeof(float);
+    float* tail = (float*)(host.data() + off);
+    double rmax = 0.0;
+    for (int j = 0; j < d; ++j) {
+      double acc = 0.0, rn = 0.0;
+      for (int i = 0; i < d; ++i) {
+        acc += s[(size_t)i * d + j];
+        rn += s[(size_t)j * d + i] * s[(size_t)j * d + i];
+      }
+      tail[j] = (float)acc;
+      rmax = std::fmax(rmax, std::sqrt(rn));
+    }
+    tail[d] = (float)(rmax * (1.0 + 0x1p-20));
+    tail[d + 1] = tail[d + 2] = tail[d + 3] = 0.0f;
+    off += s_tail;
     if (fold) {
       off_sp32 = off;
       for (size_t i = 0; i < dd; ++i) ((float*)(host.data() + off))[i] = (float)sp[i];

@@ -93,7 +93,6 @@ struct DecPrepParams {
   u32x4* frag;
   float* consts;
   int Hq, Hkv, group, chunk_heads, n_chunks, n_units;
-  int head_split;  // workgroups per unit, each for a slice of its query heads
   float scale_log2e;
   float kappa;
   float kcoef[kMaxWalsh];
@@ -247,94 +246,108 @@ __device__ void append_one(const AppendArgs& p, int grp, bool value, int Hkv) {
 // (fp16 hi/lo of 2 a_s (Pi_K q)_j and 2 kappa (S_K q)_j with the bit-position
 // powers of two) and the per-row constants. Blocks past n_units (decode with
 // append): the new token's key and value records.
+// Query prep of one (batch, KV head, head chunk) unit, in kPrepSlices
+// workgroups: slice s owns coordinates [s D/4, (s+1) D/4) of q' = Pi_K q and
+// q'' = S_K q, which are exactly the K elements of lane group s in every score
+// fragment, so a workgroup reads only its D/4 rows of each matrix and writes
+// the fragment lanes of its group. The per-head operand exponent comes from
+// bounds that every slice has at hand: |q'_j| <= |q| (Pi's rows are unit
+// vectors) and |q''_j| <= |q| max_i |S_i|; the constant parts of the scores
+// use sum_j q'_j = (Pi^T 1) q and sum_j q''_j = (S^T 1) q (slice 0).
+constexpr int kPrepSlices = 4;
+
 template <int D, int PK, bool QJL>
 __global__ __launch_bounds__(4 * D) void decode_prep_kernel(DecPrepParams prm) {
   using KW = KWords<D, PK, QJL>;
   constexpr int NTH = 4 * D;
-  if ((int)blockIdx.x >= prm.n_units * prm.head_split) {
-    const int a = blockIdx.x - prm.n_units * prm.head_split;
+  constexpr int RS = D / kPrepSlices;  // rows of each matrix per slice
+  if ((int)blockIdx.x >= prm.n_units * kPrepSlices) {
+    const int a = blockIdx.x - prm.n_units * kPrepSlices;
     append_one<D, NTH>(prm.app, a >> 1, a & 1, prm.Hkv);
     return;
   }
-  __shared__ float qs[8][D], qp[8][D], qq[8][D];
-  __shared__ float stats[8][4];  // per head: sum q', sum q'', max |q'|, max |q''|
-  const int unit = blockIdx.x / prm.head_split, slice = blockIdx.x % prm.head_split;
+  __shared__ float qs[8][D];            // the unit's queries
+  __shared__ float qp[8][RS], qq[8][RS];  // this slice's coordinates of Pi_K q and S_K q
+  __shared__ float qn[8], qsp[8], qsq[8];  // |q|, (Pi^T 1) q, (S^T 1) q per head
+  __shared__ float opscale[8][4];
+  const int unit = blockIdx.x / kPrepSlices, slice = blockIdx.x % kPrepSlices;
   const int chunk = unit % prm.n_chunks, bh = unit / prm.n_chunks;
   const int b = bh / prm.Hkv, hkv = bh % prm.Hkv;
   const int nh = prm.chunk_heads;
   const int hq0 = hkv * prm.group + chunk * nh;
-  // this workgroup's heads [h0, h1) of the unit; slice 0 also writes the unused rows h >= nh
-  const int hps = (nh + prm.head_split - 1) / prm.head_split;
-  const int h0 = slice * hps, h1 = min(h0 + hps, nh);
-  auto mine = [&](int h) { return h < nh ? (h >= h0 && h < h1) : slice == 0; };
   const int t = threadIdx.x;
-  const int mrow = t >> 1, half = t & 1;  // matrix row (Pi_K rows, then S_K rows), half of it
-  const bool s_row = mrow >= D;
-  const int row = mrow % D;
+  // thread t: eighth (t % 8) of row pair t / 8; pairs [0, RS) are rows of Pi_K,
+  // [RS, 2 RS) rows of S_K, both within this slice
+  const int pair = t >> 3, part = t & 7;
+  const bool s_row = pair >= RS;
+  const int row = slice * RS + pair % RS;
   const bool m_active = !s_row || QJL;
-  constexpr int NV = D / 8;              // float4 loads per half row
-  constexpr int NB = NV < 16 ? NV : 16;  // loads in flight per batch (64 VGPRs)
-  const float4* m4 = (const float4*)((s_row ? prm.sk[hkv] : prm.pk[hkv]) + (int64_t)row * D) + half * NV;
-  // the first batch of matrix rows is in flight while the query is staged
-  float4 mv0[NB];
+  constexpr int NE = D / 8;  // row elements per thread
+  constexpr int NV = NE / 4;
+  const float* mrow = (s_row ? prm.sk[hkv] : prm.pk[hkv]) + (int64_t)row * D + part * NE;
+  float4 mv[NV];
   if (m_active) {
 #pragma unroll
-    for (int k = 0; k < NB; ++k) mv0[k] = m4[k];
+    for (int k = 0; k < NV; ++k) mv[k] = ((const float4*)mrow)[k];
   }
-  for (int i = t; i < (h1 - h0) * D; i += NTH)
-    qs[h0 + i / D][i % D] = bf16_val(prm.q[((int64_t)b * prm.Hq + hq0 + h0 + i / D) * D + i % D]);
+  for (int i = t; i < nh * D; i += NTH)
+    qs[i / D][i % D] = bf16_val(prm.q[((int64_t)b * prm.Hq + hq0 + i / D) * D + i % D]);
+  // slice 0: the column sums Pi^T 1 and S^T 1 (stored after each matrix), and S's row-norm bound
+  __shared__ float colsum[2][D + 1];
+  if (slice == 0)
+    for (int i = t; i < 2 * D; i += NTH) {
+      const int m = i / D, j = i % D;
+      if (m == 0 || QJL) colsum[m][j] = (m ? prm.sk[hkv] : prm.pk[hkv])[D * D + j];
+    }
+  if (QJL && t == 0) colsum[1][D] = prm.sk[hkv][D * D + D];
   __syncthreads();
   {
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (m_active) {
 #pragma unroll
-      for (int k0 = 0; k0 < NV; k0 += NB) {
-        float4 mv[NB];
+      for (int k = 0; k < NV; ++k) {
+        const int c = part * NE + 4 * k;
 #pragma unroll
-        for (int k = 0; k < NB; ++k) mv[k] = k0 == 0 ? mv0[k] : m4[k0 + k];
-#pragma unroll
-        for (int k = 0; k < NB; ++k) {
-          const int c = 4 * (half * NV + k0 + k);
-#pragma unroll
-          for (int h = 0; h < 8; ++h)
-            if (h >= h0 && h < h1) a[h] = fmaf(mv[k].x, qs[h][c], fmaf(mv[k].y, qs[h][c + 1], fmaf(mv[k].z, qs[h][c + 2], fmaf(mv[k].w, qs[h][c + 3], a[h]))));
-        }
+        for (int h = 0; h < 8; ++h)
+          if (h < nh)
+            a[h] = fmaf(mv[k].x, qs[h][c], fmaf(mv[k].y, qs[h][c + 1], fmaf(mv[k].z, qs[h][c + 2], fmaf(mv[k].w, qs[h][c + 3], a[h]))));
       }
     }
 #pragma unroll
-    for (int h = 0; h < 8; ++h) a[h] += __shfl_xor(a[h], 1);
-    if (half == 0 && m_active) {
-      float(*dst)[D] = s_row ? qq : qp;
+    for (int h = 0; h < 8; ++h) {
+      a[h] += __shfl_xor(a[h], 1);
+      a[h] += __shfl_xor(a[h], 2);
+      a[h] += __shfl_xor(a[h], 4);
+    }
+    if (part == 0 && m_active) {
+      float(*dst)[RS] = s_row ? qq : qp;
 #pragma unroll
       for (int h = 0; h < 8; ++h)
-        if (h >= h0 && h < h1) dst[h][row] = a[h];
+        if (h < nh) dst[h][pair % RS] = a[h];
     }
   }
-  __syncthreads();
+  // |q| per head, and on slice 0 the sums of q' and q'' (one wave per head)
   {
     const int wave = t >> 6, lane = t & 63;
-    for (int h = h0 + wave; h < h1; h += NTH / 64) {
-      float s_p = 0.f, s_q = 0.f, m_p = 0.f, m_q = 0.f;
+    for (int h = wave; h < nh; h += NTH / 64) {
+      float s2 = 0.f, s_p = 0.f, s_q = 0.f;
       for (int j = lane; j < D; j += 64) {
-        s_p += qp[h][j];
-        m_p = fmaxf(m_p, fabsf(qp[h][j]));
-        if (QJL) {
-          s_q += qq[h][j];
-          m_q = fmaxf(m_q, fabsf(qq[h][j]));
+        s2 = fmaf(qs[h][j], qs[h][j], s2);
+        if (slice == 0) {
+          s_p = fmaf(colsum[0][j], qs[h][j], s_p);
+          if (QJL) s_q = fmaf(colsum[1][j], qs[h][j], s_q);
         }
       }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
+        s2 += __shfl_xor(s2, o);
         s_p += __shfl_xor(s_p, o);
         s_q += __shfl_xor(s_q, o);
-        m_p = fmaxf(m_p, __shfl_xor(m_p, o));
-        m_q = fmaxf(m_q, __shfl_xor(m_q, o));
       }
       if (lane == 0) {
-        stats[h][0] = s_p;
-        stats[h][1] = s_q;
-        stats[h][2] = m_p;
-        stats[h][3] = m_q;
+        qn[h] = sqrtf(s2);
+        qsp[h] = s_p;
+        qsq[h] = s_q;
       }
     }
   }
@@ -344,36 +357,44 @@ __global__ __launch_bounds__(4 * D) void decode_prep_kernel(DecPrepParams prm) {
     amax = fmaxf(amax, fabsf(prm.kcoef[s]));
     asum += prm.kcoef[s];
   }
+  const float smax = QJL ? colsum[1][D] : 0.f;
   // one exponent per head for both score parts (the main loop scales their sum
-  // once), and each head's operand scale per slot k: scale log2 e 2^(E + 14 - pos(k))
-  __shared__ float opscale[8][4];
+  // once), and each head's operand scale per slot k: scale log2 e 2^(E + 14 - pos(k));
+  // slice 0 writes the unit's constants
   float* cst = prm.consts + (int64_t)unit * kConstsPerUnit;
-  if (t < 16 && mine(t >> 1)) {
+  if (t < 16) {
     const int h = t >> 1, lo = t & 1;
     if (h < nh) {
-      const int em = range_exp(fmaxf(2.f * amax * stats[h][2], QJL ? 2.f * prm.kappa * stats[h][3] : 0.f) *
+      // the bound on |q|: the rounding of the fp32 products and sums stays far
+      // below the factor 2 of headroom range_exp leaves
+      const int em = range_exp(fmaxf(2.f * amax * qn[h], QJL ? 2.f * prm.kappa * qn[h] * smax : 0.f) *
                                prm.scale_log2e);
-      cst[t] = lo ? 0.f : -asum * stats[h][0] * prm.scale_log2e * ldexpf(1.0f, em - 10);
-      cst[16 + t] = lo ? 0.f : (QJL ? -prm.kappa * stats[h][1] * prm.scale_log2e * ldexpf(1.0f, em - 10) : 0.f);
-      cst[32 + t] = ldexpf(1.0f, 10 - em);
-      cst[48 + t] = ldexpf(1.0f, 10 - em);
+      if (slice == 0) {
+        cst[t] = lo ? 0.f : -asum * qsp[h] * prm.scale_log2e * ldexpf(1.0f, em - 10);
+        cst[16 + t] = lo ? 0.f : (QJL ? -prm.kappa * qsq[h] * prm.scale_log2e * ldexpf(1.0f, em - 10) : 0.f);
+        cst[32 + t] = ldexpf(1.0f, 10 - em);
+        cst[48 + t] = ldexpf(1.0f, 10 - em);
+      }
       if (!lo)
         for (int k = 0; k < 4; ++k) opscale[h][k] = prm.scale_log2e * ldexpf(1.0f, em + 14 - operand_pos(k));
     } else {
-      cst[t] = 0.f;
-      cst[16 + t] = 0.f;
-      cst[32 + t] = 1.f;
-      cst[48 + t] = 1.f;
+      if (slice == 0) {
+        cst[t] = 0.f;
+        cst[16 + t] = 0.f;
+        cst[32 + t] = 1.f;
+        cst[48 + t] = 1.f;
+      }
       if (!lo)
         for (int k = 0; k < 4; ++k) opscale[h][k] = 0.f;
     }
   }
   __syncthreads();
-  // fragment (f, lane): row r16 = 2 h + lo of the MFMA, K elements 8 g .. 8 g + 7
-  for (int e = t; e < KW::NF * 64; e += NTH) {
-    const int f = e / 64, lane = e % 64;
-    const int g = lane >> 4, r16 = lane & 15, h = r16 >> 1, lo = r16 & 1;
-    if (!mine(h)) continue;
+  // fragment (f, lane) of lane group g = slice: row r16 = 2 h + lo of the MFMA,
+  // K elements 8 g .. 8 g + 7
+  const int g = slice;
+  for (int e = t; e < KW::NF * 16; e += NTH) {
+    const int f = e / 16, r16 = e % 16;
+    const int h = r16 >> 1, lo = r16 & 1;
     const int W = f / 4, r = f % 4;
     unsigned hv[8];
 #pragma unroll
@@ -383,21 +404,21 @@ __global__ __launch_bounds__(4 * D) void decode_prep_kernel(DecPrepParams prm) {
       float val = 0.f;
       if (h < nh) {
         if (W < KW::NWM) {
-          int s, jj;
+          int s, jl;  // Walsh subset and the coordinate within this slice
           if constexpr (D >= 128) {
             s = W / (D / 128);
-            jj = g * (D / 4) + 32 * (W % (D / 128)) + beta;
+            jl = 32 * (W % (D / 128)) + beta;
           } else {
             s = 2 * W + half;
-            jj = g * (D / 4) + (beta % 16);
+            jl = beta % 16;
           }
-          if (s < KW::WK) val = 2.f * prm.kcoef[s] * qp[h][jj];
+          if (s < KW::WK) val = 2.f * prm.kcoef[s] * qp[h][jl];
         } else {
           const int Wq = W - KW::NWM;
           if constexpr (D >= 128) {
-            val = 2.f * prm.kappa * qq[h][g * (D / 4) + 32 * Wq + beta];
+            val = 2.f * prm.kappa * qq[h][32 * Wq + beta];
           } else {
-            if (half == 0) val = 2.f * prm.kappa * qq[h][g * (D / 4) + beta];
+            if (half == 0) val = 2.f * prm.kappa * qq[h][beta];
           }
         }
         // the lane's bit reads as 2^(operand_pos(k) - 24); raw scores come out x 2^(E - 10)
@@ -405,7 +426,7 @@ __global__ __launch_bounds__(4 * D) void decode_prep_kernel(DecPrepParams prm) {
       }
       hv[it] = f16_part(val, lo);
     }
-    prm.frag[((int64_t)unit * KW::NF + f) * 64 + lane] =
+    prm.frag[((int64_t)unit * KW::NF + f) * 64 + 16 * g + r16] =
         u32x4{pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]), pack2(hv[6], hv[7])};
   }
 }
@@ -1322,8 +1343,7 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
   pp.chunk_heads = p.chunk_heads;
   pp.n_chunks = p.n_chunks;
   pp.n_units = units;
-  // two query heads per prep workgroup: four times the workgroups of one per unit
-  pp.head_split = p.chunk_heads > 2 ? (p.chunk_heads + 1) / 2 : 1;
+
   pp.scale_log2e = scale * kLog2e;
   pp.kappa = (float)(std::sqrt(M_PI / 2.0) / p.d);
   for (int s = 0; s < k0->cb.n_walsh; ++s) pp.kcoef[s] = k0->cb.walsh_coef[s];
@@ -1361,7 +1381,7 @@ tq_status launch_decode(const DecodePlan& p, const void* q, const tq_packed_kv* 
     a.rot_dbg = app->rot_dbg;
     a.proj_dbg = app->proj_dbg;
   }
-  const int prep_blocks = units * pp.head_split + (app ? 2 * p.batch * p.n_kv_heads : 0);
+  const int prep_blocks = units * kPrepSlices + (app ? 2 * p.batch * p.n_kv_heads : 0);
 
   DecMainParams mp{};
   mp.frag = frag;

@@ -42,7 +42,9 @@ struct tq_quantizer {
   //   pi_frag / sp_frag: bf16 hi/lo MFMA fragments of Pi and S' = S Pi^T,
   //                      ordered [hilo][mtile][kstep][lane][8]
   //   pi32 / s32 / sp32: float32 row-major copies of Pi, S and S' = S Pi^T
-  //                      (sp32: prod with d <= 256, else NULL)
+  //                      (sp32: prod with d <= 256, else NULL); pi32 is followed
+  //                      by Pi^T 1 (d floats), s32 by S^T 1 (d floats) and an
+  //                      upper bound of S's row norms (then 3 zero floats)
   void* dev_block = nullptr;
   const uint16_t* pi_frag = nullptr;
   const uint16_t* sp_frag = nullptr;
