@@ -1194,6 +1194,16 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecComb
   const int ns = prm.n_splits;
   const float* ml = prm.part_ml + bhq * ns * 2;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // this thread's column entries of Pi_V for the final out = Pi_V^T acc, in
+  // flight while the splits are merged: thread (i, phase) holds rows phase,
+  // phase + R, ... of column i
+  constexpr int R = kCombineThreads / D;
+  constexpr int NJ = D / R;
+  const float* Pv = prm.pv[hkv];
+  const int i = t % D, pr = t / D;
+  float pvv[NJ];
+#pragma unroll
+  for (int u = 0; u < NJ; ++u) pvv[u] = Pv[(int64_t)(pr + u * R) * D + i];
   float mx = -INFINITY;
   for (int s = t; s < ns; s += kCombineThreads)
     if (ml[2 * s + 1] > 0.f) mx = fmaxf(mx, ml[2 * s]);
@@ -1253,13 +1263,6 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecComb
   }
   __syncthreads();
   // out[i] = sum_j Pi_V[j][i] o[j]: thread (i, phase) sums rows phase, phase + R, ...
-  constexpr int R = kCombineThreads / D;
-  const float* Pv = prm.pv[hkv];
-  const int i = t % D, pr = t / D;
-  constexpr int NJ = D / R;  // rows per thread, every load in flight at once
-  float pvv[NJ];
-#pragma unroll
-  for (int u = 0; u < NJ; ++u) pvv[u] = Pv[(int64_t)(pr + u * R) * D + i];
   float b4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < NJ; ++u) b4[u & 3] = fmaf(pvv[u], o[pr + u * R], b4[u & 3]);
