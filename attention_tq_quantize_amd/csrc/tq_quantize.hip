@@ -352,8 +352,9 @@ __device__ __forceinline__ void nearest_planes(const float* y, const float* T, P
 // equals t_u. J = the number of upper midpoints passed is found by a binary
 // search over TK; then idx = neg ? K/2 - 1 - J : K/2 + J, so the top plane is
 // !neg and the lower planes are J's bits flipped when neg (mask XORs on the
-// scalar unit). Per value 2 + (P - 1) compares, 2^(P-2) - 1 selects and the
-// key add, against P compares and 2^(P-1) - 1 selects of the plain search.
+// scalar unit). Per value one float compare, the key add, P - 1 integer
+// compares and 2^(P-2) - 1 selects, against P compares and 2^(P-1) - 1 selects
+// of the plain search.
 __device__ __forceinline__ lanemask cmp_le0(float a) {  // lanes with a <= 0
   lanemask m;
   asm("v_cmp_ge_f32_e64 %0, 0, %1" : "=s"(m) : "v"(a));
