@@ -442,7 +442,12 @@ __device__ __forceinline__ void quantize_body(const QuantParams& prm,
   constexpr int NQ = D / 16, NK = D / 32, Q4 = D / 4;
   constexpr int T = q_tiles(D, PROD, XF32, BLK);
   // split mse at four waves per SIMD has no registers for the next step's tiles
-  constexpr bool PREF = q_prefetch(D, XF32) && !(SPLIT == 1 && !PROD && !XF32);
+  // d = 256 prod (bf16 input): the 16-row fragment blocks of Pi and S' stream
+  // through a double-buffered LDS slot shared by the workgroup's waves, one
+  // block per barrier, in the order the rotation (blocks 15..0 of Pi) and the
+  // projection (blocks 15..0 of S') use them
+  constexpr bool STREAM = D == 256 && PROD && !XF32 && SPLIT == 0;
+  constexpr bool PREF = q_prefetch(D, XF32) && !(SPLIT == 1 && !PROD && !XF32) && !STREAM;
   constexpr int WPL = Q4 >= 32 ? Q4 / 32 : 1;  // 32-bit words per plane per lane (vector layout)
   constexpr int PP = P > 0 ? P : 1;
   // d = 256 mse: two workgroup sets, each for half of the output rows (16-row
@@ -533,7 +538,13 @@ __device__ __forceinline__ void quantize_body(const QuantParams& prm,
       load_tile<D, XF32>(base, (unsigned)(rel < left ? rel : left), xrow, g, dst[t]);
     }
   };
-  if (step < steps) load_step(step, cur);  // in flight while the fragments are staged
+  // streamed kernels run every step of the workgroup in every wave (the barriers
+  // need all of them): a wave past the end works on a clamped step and stores nothing
+  if constexpr (STREAM) {
+    load_step(step < steps ? step : steps - 1, cur);
+  } else {
+    if (step < steps) load_step(step, cur);  // in flight while the fragments are staged
+  }
 
   const u32x4* fpi;
   const u32x4* fsp;
@@ -600,9 +611,45 @@ __device__ __forceinline__ void quantize_body(const QuantParams& prm,
     fpi = (const u32x4*)prm.pi_frag[grp];
     fsp = (const u32x4*)prm.sp_frag[grp];
   }
+  // streamed blocks: sequence index b = 0..15 is block 15 - b of Pi, 16..31
+  // block 31 - b of S'; thread t holds element t of the block's hi and lo parts
+  // (NK * 64 = the workgroup's thread count) from its load to its LDS store.
+  // Loads run two blocks ahead (register slots b & 1), so a block's wait at the
+  // end of the one before it leaves the next block's loads in flight.
+  constexpr int SBLK = 2 * NK * 64;  // u32x4 per streamed block
+  u32x4 pend_h[2] = {}, pend_l[2] = {};
+  auto stream_issue = [&](int bseq, int slot) {
+    if constexpr (STREAM) {
+      static_assert(NK * 64 == kQThreads, "one element of each part per thread");
+      // buffer loads: one lane offset register for every block, the block's
+      // offset in an SGPR (per-block 64-bit addresses would be hoisted and spilled)
+      const buf_t r = make_buf(bseq < NQ ? fpi : fsp, FRAG_VECS * 16u);
+      const int qb = bseq < NQ ? NQ - 1 - bseq : 2 * NQ - 1 - bseq;
+      const uint4 h = ld128(r, 16u * threadIdx.x, (unsigned)((0 * NQ + qb) * NK * 64 * 16));
+      const uint4 l = ld128(r, 16u * threadIdx.x, (unsigned)((1 * NQ + qb) * NK * 64 * 16));
+      pend_h[slot] = u32x4{h.x, h.y, h.z, h.w};
+      pend_l[slot] = u32x4{l.x, l.y, l.z, l.w};
+    }
+  };
+  auto stream_store = [&](int buf) {  // block in register slot buf into LDS buffer buf
+    if constexpr (STREAM) {
+      smem_frag[buf * SBLK + threadIdx.x] = pend_h[buf];
+      smem_frag[buf * SBLK + NK * 64 + threadIdx.x] = pend_l[buf];
+      __syncthreads();
+    }
+  };
+  if constexpr (STREAM) {
+    stream_issue(0, 0);
+    stream_issue(1, 1);
+    stream_store(0);
+  }
   // fragment (hilo, q, ks) of this lane
   auto frag = [&](const u32x4* base, int hl, int q, int ks) -> u32x4 {
-    if constexpr (LDS_FRAG) {
+    if constexpr (STREAM) {
+      // the buffer of q's block: rotation block q is sequence 15 - q, projection
+      // block q is 31 - q; both have the parity of q + 1
+      return smem_frag[((q + 1) & 1) * SBLK + (hl * NK + ks) * 64 + lane];
+    } else if constexpr (LDS_FRAG) {
       return base[((hl * QH + (q - q0)) * NK + ks) * 64 + lane];
     } else {
       // global: wave-uniform base and fragment offset in SGPRs, one lane offset
@@ -613,7 +660,7 @@ __device__ __forceinline__ void quantize_body(const QuantParams& prm,
     }
   };
 
-  for (; step < steps; step += stride) {
+  for (; STREAM ? step - wave < steps : step < steps; step += stride) {
     // d = 256: the fragments stay in global memory. Opaque copies of their
     // addresses keep the compiler from hoisting every step-invariant fragment
     // load out of this loop (about a thousand registers, all spilled).
@@ -697,6 +744,7 @@ __device__ __forceinline__ void quantize_body(const QuantParams& prm,
 #pragma unroll
       for (int qq = QH - 1; qq >= 0; --qq) {
         const int q = q0 + qq;
+        if constexpr (STREAM) stream_issue(NQ + 1 - q, (NQ - 1 - q) & 1);  // two blocks ahead
         f32x4 C[T];
 #pragma unroll
         for (int t = 0; t < T; ++t) C[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -760,6 +808,7 @@ __device__ __forceinline__ void quantize_body(const QuantParams& prm,
         }
         // keep the scheduler from hoisting every block's fragment reads (register spills)
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (STREAM) stream_store((NQ - q) & 1);
       }
       // bases of this step (wave-uniform unless fused), 32-bit lane offsets
       float* nbase = prm.norms + gbase + v0;
@@ -812,6 +861,7 @@ __device__ __forceinline__ void quantize_body(const QuantParams& prm,
         }
 #pragma unroll
         for (int q = NQ - 1; q >= 0; --q) {
+          if constexpr (STREAM) stream_issue((2 * NQ + 1 - q) % (2 * NQ), (2 * NQ - 1 - q) & 1);  // two blocks ahead (wraps to the next step's first two)
           f32x4 acc[T];
 #pragma unroll
           for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -842,6 +892,7 @@ __device__ __forceinline__ void quantize_body(const QuantParams& prm,
             }
           }
           __builtin_amdgcn_sched_barrier(0);
+          if constexpr (STREAM) stream_store((2 * NQ - q) & 1);
         }
         float* rbase = prm.rnorms + gbase + v0;
         uint8_t* sbase = r_signs + (gbase + v0) * (RD / 8);
@@ -981,6 +1032,8 @@ __device__ __forceinline__ void quantize_body(const QuantParams& prm,
 #pragma unroll
         for (int t = 0; t < T; ++t) cur[t] = nxt[t];
       }
+    } else if constexpr (STREAM) {
+      load_step(nstep < steps ? nstep : steps - 1, cur);
     } else {
       if (nstep < steps) load_step(nstep, cur);
     }
@@ -1062,7 +1115,12 @@ tq_status launch_quantize(const QuantizeLaunch& a, hipStream_t stream) {
       constexpr int D = decltype(DC)::value;
       // fragments in LDS: d <= 128 both matrices; d = 256 mse half of Pi per workgroup
       const bool half = D == 256 && !prod;
-      const size_t lds = D <= 128 ? (size_t)2 * D * D * 2 * (prod ? 2 : 1) : half ? (size_t)D * D * 2 : 0;
+      // (d = 256 prod with bf16 input: two streamed 16-row blocks, hi and lo, 32 KB)
+      const bool streamed = D == 256 && prod && !xf32;
+      const size_t lds = D <= 128 ? (size_t)2 * D * D * 2 * (prod ? 2 : 1)
+                         : half   ? (size_t)D * D * 2
+                         : streamed ? (size_t)2 * 2 * (D / 32) * 64 * 16
+                                  : 0;
       return dispatch_planes(P, [&](auto PC) -> tq_status {
         constexpr int PP = decltype(PC)::value;
         return dispatch_bool(prod, [&](auto PR) -> tq_status {
